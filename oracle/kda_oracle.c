@@ -1,0 +1,192 @@
+/*
+ * kda_oracle.c -- plain, slow, fp64 CPU oracle for the Kimi Delta Attention
+ * (KDA) operator.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, calls or
+ * loads this file; it is compiled into its own shared object (liboracle_kda.so)
+ * and used only by the tests, by the smoke check and by the benchmark's
+ * cpu_baseline leg.  It shares no code, header, table or helper with the HIP
+ * path.
+ *
+ * What it computes (Kimi Linear summary page, "De la atencion lineal a Gated
+ * DeltaNet" and "Control fino de memoria en Kimi Delta Attention"): per head a
+ * matrix-valued fast-weight state S (dk x dv; row = key channel, column = value
+ * channel) updated token by token with the gated delta rule whose forget gate
+ * is a per-key-channel diagonal,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t          (output read AFTER the update),
+ *
+ * with alpha_t = exp(g_t) (g is the natural log of the gate, passed in).
+ * The step is evaluated in its delta-rule form -- decay first, then one online
+ * gradient step on the reconstruction loss 1/2 ||S^T k - v||^2 with step size
+ * beta -- which expands to exactly the product above:
+ *
+ *     S <- Diag(exp(g_t)) S
+ *     u  = S^T k_t                     (what the state recalls for k_t)
+ *     S <- S + beta_t k_t (v_t - u)^T  (write the correction)
+ *     o_t = scale * S^T q_t
+ *
+ * No chunking, no reordering: the exact result, one token at a time, in fp64
+ * on the exact input values (fp32 arrays; bf16 inputs are upcast exactly by
+ * the caller).  Independent (sequence, head) chains run in parallel with
+ * OpenMP, each chain strictly in token order.
+ *
+ * Layouts (all contiguous, row-major):
+ *   q, k  [B, T, H, dk]   v [B, T, H, dv]   g [B, T, H, dk]   beta [B, T, H]
+ *   o     [B, T, H, dv]   (fp64)
+ *   S0, S_final  [N, H, dk, dv] (fp64); S0 may be NULL (= zero state)
+ *   cu_seqlens   int32 [N + 1] or NULL.  Non-NULL requires B == 1: sequence n
+ *                occupies tokens [cu[n], cu[n+1]) and starts from S0[n].
+ *                NULL means N == B and sequence n is batch row n.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One token of the recurrence on state S (dk x dv, fp64).
+ * drop_erase != 0 removes the k k^T (erase) term, leaving the plain additive
+ * write S <- Diag(alpha) S + beta k v^T; it exists only so the tests can
+ * reduce the oracle to textbook linear attention and is never used for
+ * parity against the GPU path. */
+static void kda_token(int dk, int dv, double scale, const float *q,
+                      const float *k, const float *v, const float *g,
+                      double beta, double *S, double *u, double *o,
+                      int drop_erase)
+{
+    for (int i = 0; i < dk; ++i) {
+        const double a = exp((double)g[i]);
+        double *row = S + (size_t)i * dv;
+        for (int j = 0; j < dv; ++j) row[j] *= a;
+    }
+    for (int j = 0; j < dv; ++j) u[j] = 0.0;
+    if (!drop_erase) {
+        for (int i = 0; i < dk; ++i) {
+            const double ki = (double)k[i];
+            const double *row = S + (size_t)i * dv;
+            for (int j = 0; j < dv; ++j) u[j] += row[j] * ki;
+        }
+    }
+    for (int j = 0; j < dv; ++j) u[j] = beta * ((double)v[j] - u[j]);
+    for (int i = 0; i < dk; ++i) {
+        const double ki = (double)k[i];
+        double *row = S + (size_t)i * dv;
+        for (int j = 0; j < dv; ++j) row[j] += ki * u[j];
+    }
+    if (o) {
+        for (int j = 0; j < dv; ++j) o[j] = 0.0;
+        for (int i = 0; i < dk; ++i) {
+            const double qi = (double)q[i];
+            const double *row = S + (size_t)i * dv;
+            for (int j = 0; j < dv; ++j) o[j] += row[j] * qi;
+        }
+        for (int j = 0; j < dv; ++j) o[j] *= scale;
+    }
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Full forward over B rows (or N packed sequences).  Returns 0 on success,
+ * nonzero on a malformed argument. */
+int oracle_kda_fwd(int B, int T, int H, int dk, int dv, double scale,
+                   const float *q, const float *k, const float *v,
+                   const float *g, const float *beta, const double *S0,
+                   const int32_t *cu_seqlens, int N, int drop_erase,
+                   double *o, double *S_final)
+{
+    if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return 1;
+    if (cu_seqlens) {
+        if (B != 1 || N <= 0) return 2;
+        if (cu_seqlens[0] != 0 || cu_seqlens[N] != T) return 3;
+        for (int n = 0; n < N; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return 4;
+    } else {
+        N = B;
+    }
+    const size_t tok_k = (size_t)H * dk, tok_v = (size_t)H * dv;
+    const long chains = (long)N * H;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *S = (double *)malloc(sizeof(double) * (size_t)dk * dv);
+        double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !u) {
+#pragma omp atomic write
+            err = 5;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long c = 0; c < chains; ++c) {
+                const int n = (int)(c / H), h = (int)(c % H);
+                long t0, t1, base;
+                if (cu_seqlens) { t0 = cu_seqlens[n]; t1 = cu_seqlens[n + 1]; base = 0; }
+                else { t0 = 0; t1 = T; base = (long)n * T; }
+                const size_t sidx = ((size_t)n * H + h) * (size_t)dk * dv;
+                if (S0) memcpy(S, S0 + sidx, sizeof(double) * (size_t)dk * dv);
+                else memset(S, 0, sizeof(double) * (size_t)dk * dv);
+                for (long t = t0; t < t1; ++t) {
+                    const size_t tok = (size_t)(base + t);
+                    kda_token(dk, dv, scale,
+                              q + tok * tok_k + (size_t)h * dk,
+                              k + tok * tok_k + (size_t)h * dk,
+                              v + tok * tok_v + (size_t)h * dv,
+                              g + tok * tok_k + (size_t)h * dk,
+                              (double)beta[tok * H + h], S, u,
+                              o ? o + tok * tok_v + (size_t)h * dv : NULL,
+                              drop_erase);
+                }
+                if (S_final) memcpy(S_final + sidx, S, sizeof(double) * (size_t)dk * dv);
+            }
+        }
+        free(S);
+        free(u);
+    }
+    return err;
+}
+
+/* One decode step: the same token update applied once to each sequence's
+ * cached state.  state is [num_slots, H, dk, dv] fp64, updated in place;
+ * sequence n uses slot slot_idx[n] (or n when slot_idx is NULL).  Sequences
+ * whose slot is out of range are skipped and their output row is left as is.
+ * q, k, g [N, H, dk]; v [N, H, dv]; beta [N, H]; o [N, H, dv] (fp64). */
+int oracle_kda_decode_step(int N, int H, int dk, int dv, double scale,
+                           const float *q, const float *k, const float *v,
+                           const float *g, const float *beta, double *state,
+                           int num_slots, const int32_t *slot_idx, double *o)
+{
+    if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || num_slots < 0) return 1;
+    if (!slot_idx && N > num_slots) return 2;
+    const long chains = (long)N * H;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!u) {
+#pragma omp atomic write
+            err = 5;
+        } else {
+#pragma omp for schedule(static)
+            for (long c = 0; c < chains; ++c) {
+                const int n = (int)(c / H), h = (int)(c % H);
+                const int slot = slot_idx ? slot_idx[n] : n;
+                if (slot < 0 || slot >= num_slots) continue;
+                double *S = state + ((size_t)slot * H + h) * (size_t)dk * dv;
+                const size_t r = (size_t)n * H + h;
+                kda_token(dk, dv, scale, q + r * dk, k + r * dk, v + r * dv,
+                          g + r * dk, (double)beta[r], S, u, o + r * dv, 0);
+            }
+        }
+        free(u);
+    }
+    return err;
+}
