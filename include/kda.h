@@ -1,0 +1,149 @@
+/*
+ * kda.h -- C ABI of libkda.so: the Kimi Delta Attention (KDA) operator on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operator (GeekNews summary of Kimi Linear, es.news.hada.io topic 31936,
+ * sections "De la atencion lineal a Gated DeltaNet" and "Control fino de
+ * memoria en Kimi Delta Attention"): per head a matrix-valued state S
+ * (dk x dv; row = key channel, column = value channel) follows the gated delta
+ * rule with a per-key-channel forget gate,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,        alpha_t = exp(g_t),
+ *
+ * i.e. the state is first decayed channel by channel, then the rank-1 delta
+ * rule erases what it recalls for k_t and writes v_t, and the output reads the
+ * updated state.
+ *
+ * kda_chunk_fwd evaluates a whole prompt with the chunkwise-parallel form
+ * (same page, "Algoritmo paralelo por chunks": fixed-length chunks that hand
+ * their final state to the next chunk; inside a chunk the rank-1 updates are
+ * packed by the WY representation, the UT transform (I + A)^-1 is obtained by
+ * forward substitution, and the output joins the inter-chunk recurrent part
+ * with the intra-chunk parallel part).  kda_decode_step is the same
+ * recurrence applied once per sequence to a state cache, the constant-size
+ * per-sequence memory the page credits for the low time per output token
+ * ("Uso de NoPE y resultados de evaluacion").
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller, contiguous and
+ *     row-major, 16-byte aligned.  The library allocates no device memory,
+ *     keeps no global mutable state and is safe to call from several threads.
+ *   - Calls are asynchronous and ordered on `stream` (NULL = the default
+ *     stream).  KDA_OK means "validated and launched"; a fault inside a
+ *     kernel surfaces at the caller's next synchronisation.
+ *   - All arguments are validated on the host before anything is launched; on
+ *     an error nothing is written and the specific code is returned.  A launch
+ *     failure reported by the runtime maps to KDA_ERR_HIP.
+ *   - Numerics: q, k, v are bf16 or fp32; g (log of the gate), beta, states
+ *     and o are fp32.  The bf16 path feeds the matrix cores with fp16 operands
+ *     (exact for bf16 inputs of magnitude >= 2^-14) and accumulates in fp32;
+ *     the fp32 path uses fp32 matrix-core products throughout.
+ *   - Domain of the fast path (not checked): finite inputs; g <= 0; q and k
+ *     L2-normalised (|entries| <= 1); |v| and the state entries < 6e4; within
+ *     any 16-token block of a chunk the per-channel sum of -g stays below 10
+ *     (per-token gates down to about -0.6 on average).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_ARG = 1,     /* a required pointer is NULL or misaligned   */
+    KDA_ERR_BAD_SHAPE = 2,    /* a size is negative/zero where it may not be,
+                                 or sizes are inconsistent                   */
+    KDA_ERR_UNSUPPORTED = 3,  /* dk, dv, chunk or dtype outside the built set */
+    KDA_ERR_BAD_DTYPE = 4,    /* dtype code not in kda_dtype                 */
+    KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required     */
+    KDA_ERR_HIP = 6           /* the HIP runtime reported an error           */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kda_status_string(kda_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int kda_version(void);
+
+/* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if the
+ * sizes are invalid or unsupported).  num_seqs: the number of packed
+ * sequences when cu_seqlens will be passed (then B must be 1), or 0 for
+ * B equal-length rows.  The size grows with T and num_seqs only, so a
+ * workspace sized for the largest call serves all smaller ones. */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv,
+                                     int chunk, int num_seqs,
+                                     kda_dtype qkv_dtype);
+
+/* Chunkwise-parallel KDA prefill.
+ *
+ *   B, T, H      batch rows, tokens per row, heads.  B*T may be 0.
+ *   dk, dv       head dims; dk == dv in {32, 64, 128}.
+ *   chunk        chunk length in {16, 32, 64}.  The result does not depend on
+ *                it beyond rounding.
+ *   scale        output scale (usually dk^-0.5).
+ *   qkv_dtype    KDA_BF16 or KDA_F32 for q, k, v.
+ *   q, k         [B, T, H, dk]            (qkv_dtype)
+ *   v            [B, T, H, dv]            (qkv_dtype)
+ *   g            [B, T, H, dk] fp32       natural log of the forget gate
+ *   beta         [B, T, H]     fp32       delta-rule write strength
+ *   initial_state [N, H, dk, dv] fp32 or NULL (zero state)
+ *   cu_seqlens   int32 [N+1] or NULL.  Non-NULL packs N = num_seqs sequences
+ *                along T (B must be 1): sequence n is tokens
+ *                [cu_seqlens[n], cu_seqlens[n+1]) and starts from
+ *                initial_state[n].  Must be non-decreasing with cu[0] = 0 and
+ *                cu[N] = T (device data, not checked).  NULL means N = B.
+ *   num_seqs     N when cu_seqlens is given (>= 1); ignored otherwise.
+ *   o            [B, T, H, dv] fp32 output.
+ *   final_state  [N, H, dk, dv] fp32 or NULL.  May alias initial_state
+ *                (in-place state hand-off); no other aliasing is allowed.
+ *   workspace    device scratch of at least kda_chunk_fwd_workspace_bytes(...)
+ *                bytes, 256-byte aligned; contents on entry are ignored.
+ */
+kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk,
+                         float scale, kda_dtype qkv_dtype,
+                         const void *q, const void *k, const void *v,
+                         const float *g, const float *beta,
+                         const float *initial_state,
+                         const int32_t *cu_seqlens, int num_seqs,
+                         float *o, float *final_state,
+                         void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* One recurrent decode step for N sequences against a state cache.
+ *
+ *   N            sequences in this step (N may be 0).
+ *   H, dk, dv    heads and head dims; dk == dv in {32, 64, 128}.
+ *   scale        output scale.
+ *   qkv_dtype    KDA_BF16 or KDA_F32 for q, k, v.
+ *   q, k         [N, H, dk];  v [N, H, dv]  (qkv_dtype)
+ *   g            [N, H, dk] fp32 (log gate);  beta [N, H] fp32
+ *   state_cache  [num_slots, H, dk, dv] fp32, updated IN PLACE: sequence n
+ *                reads and writes slot slot_idx[n].
+ *   slot_idx     int32 [N] or NULL (= identity; then N <= num_slots).  Slots
+ *                must be distinct within a call; a slot outside
+ *                [0, num_slots) makes that sequence a no-op (its o row is
+ *                left untouched).
+ *   o            [N, H, dv] fp32 output.
+ */
+kda_status kda_decode_step(int N, int H, int dk, int dv, float scale,
+                           kda_dtype qkv_dtype,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           float *state_cache, int num_slots,
+                           const int32_t *slot_idx, float *o,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,168 @@
+"""Python binding of libkda.so -- the KDA operator on MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/kda.h``.  PyTorch provides
+device memory and streams.  If the library is not built, importing works but
+every call raises ``RuntimeError`` -- there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_F32 = 0
+KDA_BF16 = 1
+KDA_OK = 0
+STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL_ARG", 2: "KDA_ERR_BAD_SHAPE",
+                3: "KDA_ERR_UNSUPPORTED", 4: "KDA_ERR_BAD_DTYPE", 5: "KDA_ERR_WORKSPACE",
+                6: "KDA_ERR_HIP"}
+
+# name -> (restype, argtypes), mirroring include/kda.h
+_P, _I, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "kda_status_string": (ctypes.c_char_p, [_I]),
+    "kda_version": (_I, []),
+    "kda_chunk_fwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "kda_chunk_fwd": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
+                           _P, _P, _P, _SZ, _P]),
+    "kda_decode_step": (_I, [_I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P]),
+}
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__("%s failed: %s" % (fn, kda_status_string(code)))
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so (raises if it is missing: the HIP path is the only path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError("libkda.so is not built (%s); run "
+                               "`python -m linear_attention_sequence_chunkwise_amd.build`" % path)
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def kda_status_string(code: int) -> str:
+    try:
+        return load_library().kda_status_string(int(code)).decode()
+    except RuntimeError:
+        return STATUS_NAMES.get(int(code), "KDA_ERR_UNKNOWN")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+
+
+def kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torch.bfloat16):
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load_library().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs,
+                                                             code))
+
+
+def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu_seqlens=None,
+                  output_final_state=True, o=None, final_state=None, workspace=None,
+                  stream=None):
+    """Chunkwise KDA prefill.
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32); g: [B, T, H, dk] fp32
+    (log gate); beta: [B, T, H] fp32; initial_state: [N, H, dk, dv] fp32 or
+    None; cu_seqlens: int32 [N + 1] (B must be 1) or None.  Returns
+    (o [B, T, H, dv] fp32, final_state [N, H, dk, dv] fp32 or None).
+    """
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    _check(g, "g", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(initial_state, "initial_state", torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if scale is None:
+        scale = dk ** -0.5
+    if o is None:
+        o = torch.empty(B, T, H, dv, dtype=torch.float32, device=dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    code = _dtype_code(q)
+    need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk,
+                                             N if cu_seqlens is not None else 0, code)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_fwd(B, T, H, dk, dv, chunk, float(scale), code, _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+                           N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state),
+                           _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != KDA_OK:
+        raise KDAError("kda_chunk_fwd", rc)
+    return o, final_state
+
+
+def kda_decode_step(q, k, v, g, beta, state_cache, scale=None, slot_idx=None, o=None,
+                    stream=None):
+    """One decode step.  q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H];
+    state_cache: [num_slots, H, dk, dv] fp32, updated in place; slot_idx:
+    int32 [N] or None.  Returns o [N, H, dv] fp32."""
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    _check(g, "g", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(state_cache, "state_cache", torch.float32, dev)
+    _check(slot_idx, "slot_idx", torch.int32, dev)
+    if scale is None:
+        scale = dk ** -0.5
+    if o is None:
+        o = torch.empty(N, H, dv, dtype=torch.float32, device=dev)
+    rc = lib.kda_decode_step(N, H, dk, dv, float(scale), _dtype_code(q), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(g), _ptr(beta), _ptr(state_cache),
+                             state_cache.shape[0], _ptr(slot_idx), _ptr(o), _stream(stream))
+    if rc != KDA_OK:
+        raise KDAError("kda_decode_step", rc)
+    return o

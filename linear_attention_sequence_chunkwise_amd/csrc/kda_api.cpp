@@ -1,0 +1,120 @@
+// kda_api.cpp -- the C ABI of libkda.so: host-side validation, workspace
+// sizing and dispatch to the HIP launchers.  Every argument check runs before
+// the first HIP call, so a rejected call touches neither the device nor the
+// caller's buffers.
+#include "kda.h"
+
+#include <stdint.h>
+
+#include "kda_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
+
+kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL_ARG: return "KDA_ERR_NULL_ARG: required pointer is NULL or not 16-byte aligned";
+        case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE: invalid or inconsistent sizes";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: dk/dv/chunk outside the built set";
+        case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE: unknown dtype code";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+int kda_version(void) { return 100; }
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                     int num_seqs, kda_dtype qkv_dtype) {
+    if (B < 1 || T < 0 || H < 1 || num_seqs < 0) return 0;
+    if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return 0;
+    if (dk != dv || !kda::prefill_supported(dk, chunk, qkv_dtype == KDA_BF16)) return 0;
+    const bool varlen = num_seqs > 0;
+    if (varlen && B != 1) return 0;
+    kda::PrefillPlan plan;
+    if (!kda::prefill_plan(B, T, H, dk, chunk, varlen ? num_seqs : B, varlen,
+                           qkv_dtype == KDA_BF16, &plan))
+        return 0;
+    return plan.total;
+}
+
+kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk, float scale,
+                         kda_dtype qkv_dtype, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* initial_state,
+                         const int32_t* cu_seqlens, int num_seqs, float* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_BAD_SHAPE;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen && (B != 1 || num_seqs < 1)) return KDA_ERR_BAD_SHAPE;
+    const int N = varlen ? num_seqs : B;
+    if ((long long)B * T * H * (long long)(dk > dv ? dk : dv) >= (1LL << 40)) return KDA_ERR_BAD_SHAPE;
+    if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+    if (dk != dv || !kda::prefill_supported(dk, chunk, qkv_dtype == KDA_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    const bool has_tokens = (long long)B * T > 0;
+    if (has_tokens) {
+        if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o))
+            return KDA_ERR_NULL_ARG;
+    }
+    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+        return KDA_ERR_NULL_ARG;
+    if (varlen && !cu_seqlens) return KDA_ERR_NULL_ARG;
+
+    kda::PrefillPlan plan;
+    if (!kda::prefill_plan(B, T, H, dk, chunk, N, varlen, qkv_dtype == KDA_BF16, &plan))
+        return KDA_ERR_BAD_SHAPE;
+    if (plan.total > 0 && (!workspace || workspace_bytes < plan.total || ((uintptr_t)workspace & 255u)))
+        return KDA_ERR_WORKSPACE;
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+
+    kda::PrefillArgs a;
+    a.B = B; a.T = T; a.H = H; a.D = dk; a.C = chunk; a.scale = scale;
+    a.bf16 = qkv_dtype == KDA_BF16;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s0 = initial_state; a.cu_seqlens = cu_seqlens; a.N = N;
+    a.o = o; a.sT = final_state;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.stream = stream;
+    return from_hip(kda::launch_prefill(a, plan));
+}
+
+kda_status kda_decode_step(int N, int H, int dk, int dv, float scale, kda_dtype qkv_dtype,
+                           const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state_cache, int num_slots,
+                           const int32_t* slot_idx, float* o, hipStream_t stream) {
+    if (N < 0 || H < 1 || dk < 1 || dv < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
+    if (!slot_idx && N > num_slots) return KDA_ERR_BAD_SHAPE;
+    if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+    if (dk != dv || !supported_dim(dk)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state_cache || !o) return KDA_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
+        !aligned16(state_cache) || !aligned16(o))
+        return KDA_ERR_NULL_ARG;
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+
+    kda::DecodeArgs a;
+    a.N = N; a.H = H; a.D = dk; a.scale = scale; a.bf16 = qkv_dtype == KDA_BF16;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.state = state_cache; a.num_slots = num_slots; a.slot_idx = slot_idx; a.o = o;
+    a.stream = stream;
+    return from_hip(kda::launch_decode(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// kda_common.h -- small device helpers shared by the KDA kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// bf16 is carried as its raw 16-bit pattern.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+    return __builtin_bit_cast(float, (uint32_t)x.bits << 16);
+}
+
+// Natural exponent through the hardware base-2 exponential.
+__device__ __forceinline__ float exp_e(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// Load 4 consecutive input elements (bf16 or fp32) as floats.
+__device__ __forceinline__ float4v load4(const float* p) {
+    return *reinterpret_cast<const float4v*>(p);
+}
+__device__ __forceinline__ float4v load4(const bf16_t* p) {
+    uint2 u = *reinterpret_cast<const uint2*>(p);
+    float4v r;
+    r[0] = __builtin_bit_cast(float, u.x << 16);
+    r[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+    r[2] = __builtin_bit_cast(float, u.y << 16);
+    r[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+    return r;
+}
+
+}  // namespace kda

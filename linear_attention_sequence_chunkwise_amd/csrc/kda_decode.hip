@@ -1,0 +1,135 @@
+// kda_decode.hip -- single-token KDA decode step over an in-place fp32 state
+// cache (gfx950).
+//
+// One recurrence step per (sequence, head) (GeekNews summary of Kimi Linear,
+// "Control fino de memoria en Kimi Delta Attention"; the constant-size state is
+// what keeps time per output token flat, "Uso de NoPE y resultados"):
+//     S'  = Diag(exp(g)) S            per-key-channel decay (rows)
+//     u   = S'^T k,  p = S'^T q        both reductions from one read of S'
+//     e   = beta (v - u)               delta-rule correction
+//     S   = S' + k e^T                 written back in place
+//     o   = scale (p + (k.q) e)        = scale S^T q with the updated S
+//
+// The step is bound by HBM: each (sequence, head) reads and writes its
+// dk x dv fp32 state exactly once (2 * 64 KB at d = 128) and touches a few
+// hundred bytes of token data.  No matrix cores.  One 256-thread workgroup per
+// (sequence, head); each thread owns 4 adjacent columns (one float4) of
+// D/ (256 / (D/4)) rows, rows interleaved so that a wavefront's load covers
+// whole consecutive rows.  The state stays in registers between the read and
+// the write.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int D, typename IT>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    int H, float scale, const IT* __restrict__ q, const IT* __restrict__ k,
+    const IT* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
+    float* __restrict__ state, int num_slots, const int32_t* __restrict__ slot_idx,
+    float* __restrict__ o) {
+    constexpr int CG = D / 4;        // float4 column groups
+    constexpr int RG = 256 / CG;     // row groups
+    constexpr int RPT = D / RG;      // rows per thread
+    static_assert(RPT >= 1 && RG * RPT == D, "bad decode tiling");
+
+    const int nh = blockIdx.x;       // sequence * H + head
+    const int n = nh / H;
+    const int h = nh - n * H;
+    const int slot = slot_idx ? slot_idx[n] : n;
+    if (slot < 0 || slot >= num_slots) return;   // whole workgroup leaves together
+
+    __shared__ float s_k[D], s_q[D], s_a[D], s_e[D];
+    __shared__ float s_red[2][RG][D];
+    __shared__ float s_kq[4];
+
+    const int tid = threadIdx.x;
+    const size_t tok = (size_t)nh;
+    if (tid < D) {
+        s_k[tid] = to_f32(k[tok * D + tid]);
+        s_q[tid] = to_f32(q[tok * D + tid]);
+        s_a[tid] = exp_e(g[tok * D + tid]);
+    }
+
+    const int cg = tid % CG;
+    const int rg = tid / CG;
+    float* S = state + ((size_t)slot * H + h) * (size_t)D * D;
+
+    // Issue every state load before the first barrier so the reads are in
+    // flight while the token vectors arrive.
+    float4v s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        s[i] = *reinterpret_cast<const float4v*>(S + (size_t)(i * RG + rg) * D + 4 * cg);
+
+    __syncthreads();
+
+    // k.q by wavefront 0
+    if (tid < 64) {
+        float t = 0.f;
+        for (int i = tid; i < D; i += 64) t += s_k[i] * s_q[i];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+        if (tid == 0) s_kq[0] = t;
+    }
+
+    float4v pu = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = i * RG + rg;
+        const float a = s_a[r];
+        s[i] *= a;
+        pu += s[i] * s_k[r];
+        pp += s[i] * s_q[r];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        s_red[0][rg][4 * cg + j] = pu[j];
+        s_red[1][rg][4 * cg + j] = pp[j];
+    }
+    __syncthreads();
+
+    if (tid < D) {
+        float u = 0.f, p = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < RG; ++r) {
+            u += s_red[0][r][tid];
+            p += s_red[1][r][tid];
+        }
+        const float vv = to_f32(v[tok * D + tid]);
+        const float e = beta[tok] * (vv - u);
+        s_e[tid] = e;
+        o[tok * D + tid] = scale * (p + s_kq[0] * e);
+    }
+    __syncthreads();
+
+    const float4v e4 = *reinterpret_cast<const float4v*>(&s_e[4 * cg]);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = i * RG + rg;
+        s[i] += s_k[r] * e4;
+        *reinterpret_cast<float4v*>(S + (size_t)r * D + 4 * cg) = s[i];
+    }
+}
+
+template <int D, typename IT>
+static hipError_t launch_decode_t(const DecodeArgs& a) {
+    if (a.N == 0) return hipSuccess;
+    dim3 grid((unsigned)(a.N * a.H)), block(256);
+    hipLaunchKernelGGL((decode_step_kernel<D, IT>), grid, block, 0, a.stream, a.H, a.scale,
+                       (const IT*)a.q, (const IT*)a.k, (const IT*)a.v, a.g, a.beta,
+                       a.state, a.num_slots, a.slot_idx, a.o);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+    const bool bf = a.bf16;
+    switch (a.D) {
+        case 32: return bf ? launch_decode_t<32, bf16_t>(a) : launch_decode_t<32, float>(a);
+        case 64: return bf ? launch_decode_t<64, bf16_t>(a) : launch_decode_t<64, float>(a);
+        case 128: return bf ? launch_decode_t<128, bf16_t>(a) : launch_decode_t<128, float>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kda

@@ -1,0 +1,56 @@
+// kda_internal.h -- launch descriptors passed from the C-ABI layer to the
+// kernel launchers.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    int N, H, D;
+    float scale;
+    bool bf16;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float* state;
+    int num_slots;
+    const int32_t* slot_idx;
+    float* o;
+    hipStream_t stream;
+};
+
+struct PrefillArgs {
+    int B, T, H, D, C;
+    float scale;
+    bool bf16;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const float* s0;
+    const int32_t* cu_seqlens;
+    int N;                 // sequences (B, or num_seqs with cu_seqlens)
+    float* o;
+    float* sT;
+    void* workspace;
+    size_t workspace_bytes;
+    hipStream_t stream;
+};
+
+// Workspace layout of the prefill (all offsets 256-byte aligned).
+struct PrefillPlan {
+    int nchunk_max;        // upper bound on chunks over all sequences
+    size_t chunk_rec_bytes;    // bytes of one chunk-head record
+    size_t off_table;      // chunk table (varlen only)
+    size_t off_records;    // chunk-head records
+    size_t total;
+};
+
+// True when (D, C, dtype) has a built prefill kernel that fits in LDS.
+bool prefill_supported(int D, int C, bool bf16);
+bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf16,
+                  PrefillPlan* plan);
+hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan);
+hipError_t launch_decode(const DecodeArgs& a);
+
+}  // namespace kda

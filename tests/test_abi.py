@@ -1,0 +1,98 @@
+"""CPU tests of the C-ABI library: it loads without a GPU, exports every
+symbol include/kda.h declares, and rejects bad arguments on the host before
+any HIP call (these calls never reach the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_chunkwise_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.fail("libkda.so not built; run python -m linear_attention_sequence_chunkwise_amd.build")
+    return kda.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == {"kda_status_string", "kda_version", "kda_chunk_fwd_workspace_bytes",
+                          "kda_chunk_fwd", "kda_decode_step"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in kda.SIGNATURES, n
+
+
+def test_status_strings(lib):
+    for code, name in kda.STATUS_NAMES.items():
+        assert kda.kda_status_string(code).startswith(name)
+    assert lib.kda_version() == 100
+
+
+def test_workspace_size(lib):
+    ws = lib.kda_chunk_fwd_workspace_bytes
+    # B=1 T=32768 H=32 d=128 C=64 bf16: 512 chunks x 32 heads x record
+    rec = (3 * 64 * 128 + 2 * 64 * 64) * 2 + 4 * 128
+    rec = (rec + 255) // 256 * 256
+    assert ws(1, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 512 * 32 * rec
+    assert ws(1, 100, 2, 64, 64, 16, 0, kda.KDA_F32) > ws(1, 100, 2, 64, 64, 16, 0, kda.KDA_BF16)
+    # packed sequences add a chunk table and one partial chunk per sequence
+    assert ws(1, 1000, 2, 64, 64, 64, 5, kda.KDA_BF16) > ws(1, 1000, 2, 64, 64, 64, 0, kda.KDA_BF16)
+    assert ws(1, 100, 2, 64, 32, 64, 0, kda.KDA_BF16) == 0      # dk != dv
+    assert ws(1, 100, 2, 96, 96, 64, 0, kda.KDA_BF16) == 0      # unsupported d
+    assert ws(1, 100, 2, 64, 64, 48, 0, kda.KDA_BF16) == 0      # unsupported chunk
+    assert ws(2, 100, 2, 64, 64, 64, 3, kda.KDA_BF16) == 0      # packed needs B == 1
+    assert ws(1, 100, 2, 64, 64, 64, 0, 7) == 0                 # bad dtype
+
+
+def _fwd(lib, B=1, T=64, H=2, dk=64, dv=64, chunk=64, dtype=kda.KDA_BF16, ptr=4096, cu=None,
+         nseq=0, ws=None, wsb=1 << 30, o=None):
+    p = ctypes.c_void_p(ptr)
+    return lib.kda_chunk_fwd(B, T, H, dk, dv, chunk, 1.0, dtype, p, p, p, p, p, None, cu, nseq,
+                             p if o is None else o, None, p if ws is None else ws, wsb, None)
+
+
+def test_prefill_validation(lib):
+    E = {v: k for k, v in kda.STATUS_NAMES.items()}
+    assert _fwd(lib, B=0) == E["KDA_ERR_BAD_SHAPE"]
+    assert _fwd(lib, T=-1) == E["KDA_ERR_BAD_SHAPE"]
+    assert _fwd(lib, H=0) == E["KDA_ERR_BAD_SHAPE"]
+    assert _fwd(lib, dtype=9) == E["KDA_ERR_BAD_DTYPE"]
+    assert _fwd(lib, dk=64, dv=32) == E["KDA_ERR_UNSUPPORTED"]
+    assert _fwd(lib, dk=48, dv=48) == E["KDA_ERR_UNSUPPORTED"]
+    assert _fwd(lib, chunk=128) == E["KDA_ERR_UNSUPPORTED"]
+    assert _fwd(lib, ptr=0) == E["KDA_ERR_NULL_ARG"]
+    assert _fwd(lib, ptr=4098) == E["KDA_ERR_NULL_ARG"]          # misaligned
+    assert _fwd(lib, B=2, cu=ctypes.c_void_p(4096), nseq=2) == E["KDA_ERR_BAD_SHAPE"]
+    assert _fwd(lib, cu=ctypes.c_void_p(4096), nseq=0) == E["KDA_ERR_BAD_SHAPE"]
+    assert _fwd(lib, wsb=16) == E["KDA_ERR_WORKSPACE"]
+    assert _fwd(lib, ws=ctypes.c_void_p(4096 + 16)) == E["KDA_ERR_WORKSPACE"]  # not 256-aligned
+
+
+def test_decode_validation(lib):
+    E = {v: k for k, v in kda.STATUS_NAMES.items()}
+    p = ctypes.c_void_p(4096)
+
+    def dec(N=2, H=2, dk=64, dv=64, dtype=kda.KDA_BF16, ptr=p, slots=4, idx=None):
+        return lib.kda_decode_step(N, H, dk, dv, 1.0, dtype, ptr, ptr, ptr, ptr, ptr, ptr, slots,
+                                   idx, ptr, None)
+    assert dec(N=-1) == E["KDA_ERR_BAD_SHAPE"]
+    assert dec(N=5, slots=4) == E["KDA_ERR_BAD_SHAPE"]          # identity slots need N <= slots
+    assert dec(dtype=3) == E["KDA_ERR_BAD_DTYPE"]
+    assert dec(dk=64, dv=128) == E["KDA_ERR_UNSUPPORTED"]
+    assert dec(dk=256, dv=256) == E["KDA_ERR_UNSUPPORTED"]
+    assert dec(ptr=None) == E["KDA_ERR_NULL_ARG"]
+    assert dec(ptr=ctypes.c_void_p(4100)) == E["KDA_ERR_NULL_ARG"]
+    assert dec(N=0) == E["KDA_OK"]                              # nothing to do, nothing launched

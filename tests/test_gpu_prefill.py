@@ -1,0 +1,133 @@
+"""GPU parity of kda_chunk_fwd (through the C ABI) against the fp64 oracle.
+
+Small shapes span several chunks and a ragged tail and are compared element by
+element in full; the benchmark-sized configurations are compared on sampled
+heads (every output and final state of those heads)."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import linear_attention_sequence_chunkwise_amd as kda
+import oracle
+from kda_testlib import TOL, make_prefill, np32, oracle_prefill, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run(d, chunk, cu=None, scale=None):
+    D = d["q"].shape[-1]
+    scale = D ** -0.5 if scale is None else scale
+    o, S = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=scale, chunk=chunk,
+                             initial_state=d.get("S0"), cu_seqlens=cu)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def check(d, chunk, cu=None, heads=None, tol=None):
+    D = d["q"].shape[-1]
+    o, S = run(d, chunk, cu)
+    o_ref, S_ref = oracle_prefill(d, D ** -0.5, heads=heads, cu=cu)
+    if heads is not None:
+        o, S = o[:, :, heads], S[:, heads]
+    tol = TOL[d["q"].dtype] if tol is None else tol
+    eo, es = rel_err(o.cpu().numpy(), o_ref), rel_err(S.cpu().numpy(), S_ref)
+    print("err_o %.3e err_S %.3e (tol %.0e)" % (eo, es, tol), flush=True)
+    assert eo < tol and es < tol
+    return eo, es
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_small_ragged(dtype, D, chunk):
+    for T, s0 in ((1, None), (chunk - 1, 0.1), (3 * chunk + 5, 0.05), (200, None)):
+        d = make_prefill(T * 31 + D + chunk, 2, T, 3, D, dtype, s0_std=s0)
+        check(d, chunk)
+
+
+def test_config0_fp32():
+    d = kda_inputs.config_inputs(0, "cuda")
+    check(d, 16)
+
+
+def test_config1_bf16_initial_state():
+    d = kda_inputs.config_inputs(1, "cuda")
+    check(d, 64)
+
+
+def test_config2_sampled_heads():
+    d = kda_inputs.config_inputs(2, "cuda")
+    check(d, 64, heads=[0, 13, 31])
+
+
+def test_config3_varlen_sampled_heads():
+    d = kda_inputs.config_inputs(3, "cuda")
+    check(d, 64, cu=d["cu_seqlens"], heads=[2, 29])
+
+
+def test_varlen_edge_lengths():
+    lens = [0, 1, 63, 64, 65, 0, 130, 2]
+    cu = kda_inputs.cu_seqlens_of(lens).cuda()
+    d = make_prefill(5, 1, sum(lens), 4, 64, torch.bfloat16, s0_std=0.1, n_states=len(lens))
+    check(d, 64, cu=cu)
+    d32 = make_prefill(6, 1, sum(lens), 2, 32, torch.float32, s0_std=0.1, n_states=len(lens))
+    check(d32, 16, cu=cu)
+
+
+def test_varlen_equals_separate_calls():
+    lens = [70, 5, 128, 33]
+    cu = kda_inputs.cu_seqlens_of(lens).cuda()
+    d = make_prefill(8, 1, sum(lens), 4, 128, torch.bfloat16, s0_std=0.05, n_states=len(lens))
+    o, S = run(d, 64, cu)
+    for n, (a, b) in enumerate(zip(cu[:-1].tolist(), cu[1:].tolist())):
+        dn = {k: d[k][:, a:b].contiguous() for k in ("q", "k", "v", "g", "beta")}
+        dn["S0"] = d["S0"][n:n + 1].contiguous()
+        on, Sn = run(dn, 64)
+        assert torch.equal(on, o[:, a:b]) and torch.equal(Sn[0], S[n])
+
+
+def test_split_and_resume():
+    B, T, H, D = 2, 300, 4, 128
+    d = make_prefill(9, B, T, H, D, torch.bfloat16, s0_std=0.1)
+    o, S = run(d, 64)
+    m = 130
+    d1 = {k: d[k][:, :m].contiguous() for k in ("q", "k", "v", "g", "beta")}
+    d1["S0"] = d["S0"]
+    o1, S1 = run(d1, 64)
+    d2 = {k: d[k][:, m:].contiguous() for k in ("q", "k", "v", "g", "beta")}
+    d2["S0"] = S1
+    o2, S2 = run(d2, 64)
+    o_ref, S_ref = oracle_prefill(d, D ** -0.5)
+    assert rel_err(torch.cat([o1, o2], 1).cpu().numpy(), o_ref) < TOL[torch.bfloat16]
+    assert rel_err(S2.cpu().numpy(), S_ref) < TOL[torch.bfloat16]
+
+
+def test_in_place_state_and_determinism():
+    B, T, H, D = 2, 257, 8, 64
+    d = make_prefill(10, B, T, H, D, torch.bfloat16, s0_std=0.1)
+    o1, S1 = run(d, 64)
+    st = d["S0"].clone()
+    o2, S2 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64,
+                               initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, st)
+
+
+def test_strong_decay():
+    """Per-token log gates down to -0.6: each 16-token sub-block decays by up
+    to exp(-9.6), the documented edge of the fast path."""
+    d = make_prefill(12, 1, 512, 4, 128, torch.bfloat16, s0_std=0.1, g_range=(0.05, 0.6))
+    check(d, 64)
+
+
+def test_empty_input_copies_state():
+    d = make_prefill(13, 2, 0, 2, 64, torch.bfloat16, s0_std=0.1)
+    o, S = run(d, 64)
+    assert o.numel() == 0 and torch.equal(S, d["S0"])
