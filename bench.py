@@ -1,0 +1,237 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+Prints one JSON line.  `value` is prefill throughput (tokens/s) of one
+Kimi-Linear-width layer: B=1, H=32, T=32768, dk=dv=128, chunk 64, bf16 q/k/v,
+fp32 gates, zero initial state.  The decode leg (reported under "decode") is
+256 sequences x 32 heads x d=128 with an fp32 state cache initialised by a
+4096-token prefill per sequence (untimed), then 512 timed decode steps with
+fresh inputs per step.  All inputs are synthetic (seeded) and resident in HBM
+before timing starts.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2500.0      # dense fp16/bf16 matrix cores, TFLOP/s
+PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4   # q,k,v bf16; g; beta; o fp32
+DECODE_BYTES_PER_TOKEN_HEAD = 2 * 128 * 128 * 4 + 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4
+
+
+def prefill_flops_per_token_head(dk=128, dv=128, C=64):
+    return 6 * dk * dv + (C + 1) * (3 * dk + 2 * dv) + C * C / 3.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=512)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class StreamTimer:
+    """HIP events recorded on the stream the kernels run on."""
+
+    def __init__(self, stream):
+        self.stream = stream
+        self.t0 = torch.cuda.Event(enable_timing=True)
+        self.t1 = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.t0.record(self.stream)
+
+    def stop(self):
+        self.t1.record(self.stream)
+        self.t1.synchronize()
+        return self.t0.elapsed_time(self.t1)
+
+
+def bench_prefill(kda, kda_inputs, steps, warmup, stream):
+    c = kda_inputs.CONFIGS[2]
+    B, T, H, D, C = c["B"], c["T"], c["H"], c["dk"], c["chunk"]
+    d = kda_inputs.config_inputs(2, "cuda")
+    o = torch.empty(B, T, H, D, device="cuda")
+    S = torch.empty(B, H, D, D, device="cuda")
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(B, T, H, D, D, C), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+
+    def call():
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=C, o=o,
+                          final_state=S, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    tm = StreamTimer(stream)
+    tm.start()
+    for _ in range(steps):
+        call()
+    ms = tm.stop() / steps
+    torch.cuda.synchronize()
+    return dict(ms=ms, tokens=B * T, token_heads=B * T * H, inputs=d)
+
+
+def bench_decode(kda, kda_inputs, n_steps, warmup, stream):
+    c = kda_inputs.CONFIGS[4]
+    N, H, D, C, T0 = c["N"], c["H"], c["dk"], c["chunk"], c["init_T"]
+    seed = kda_inputs.CFG_SEED[4]
+    cache = torch.empty(N, H, D, D, device="cuda")
+    # state initialisation: 4096-token prefill per sequence, 32 sequences per call
+    nb = 32
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(nb, T0, H, D, D, C), dtype=torch.uint8,
+                     device="cuda")
+    for b0 in range(0, N, nb):
+        d = kda_inputs.prefill_inputs(seed * 1000 + b0, nb, T0, H, D, D, torch.bfloat16, "cuda")
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=C,
+                          final_state=cache[b0:b0 + nb], workspace=ws, stream=stream)
+        del d
+    torch.cuda.synchronize()
+    del ws
+    steps = [kda_inputs.decode_inputs(seed, s, N, H, D, D, torch.bfloat16, "cuda")
+             for s in range(n_steps)]
+    o = torch.empty(n_steps, N, H, D, device="cuda")
+    scratch = cache.clone()
+    for s in range(warmup):
+        x = steps[s % n_steps]
+        kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], scratch, o=o[0],
+                            stream=stream)
+    del scratch
+    torch.cuda.synchronize()
+    tm = StreamTimer(stream)
+    tm.start()
+    for s in range(n_steps):
+        x = steps[s]
+        kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], cache, o=o[s],
+                            stream=stream)
+    ms = tm.stop() / n_steps
+    torch.cuda.synchronize()
+    return dict(ms=ms, N=N, token_heads=N * H)
+
+
+def cpu_baseline_prefill(d, target_s=8.0):
+    """The fp64 oracle on a bounded sample of the prefill workload: all 32
+    heads of the first T_s tokens (T_s grown until the run takes a few
+    seconds).  Reported as tokens/s of the same layer."""
+    import numpy as np
+    import oracle
+    H = d["q"].shape[2]
+    Ts = 256
+    while True:
+        sl = lambda t: t[:, :Ts].float().cpu().numpy()
+        q, k, v, g, b = (sl(d[n]) for n in ("q", "k", "v", "g", "beta"))
+        t0 = time.perf_counter()
+        oracle.kda_fwd(q, k, v, g, b, 128 ** -0.5)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or Ts >= d["q"].shape[1]:
+            break
+        Ts = min(d["q"].shape[1], Ts * 4)
+    del np
+    return dict(value=Ts / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample="prefill B1 H32 d128: all 32 heads of the first %d of 32768 tokens, %.2f s"
+                % (Ts, dt))
+
+
+def cpu_baseline_decode(kda_inputs, n_steps=4):
+    import numpy as np
+    import oracle
+    c = kda_inputs.CONFIGS[4]
+    N, H, D = c["N"], c["H"], c["dk"]
+    rng = np.random.default_rng(0)
+    state = rng.standard_normal((N, H, D, D)) * 0.1
+    xs = [kda_inputs.decode_inputs(kda_inputs.CFG_SEED[4], s, N, H, D, D, torch.bfloat16, "cpu")
+          for s in range(n_steps)]
+    xs = [{k: v.float().numpy() for k, v in x.items()} for x in xs]
+    t0 = time.perf_counter()
+    for x in xs:
+        oracle.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], D ** -0.5, state)
+    dt = time.perf_counter() - t0
+    return dict(value=N * n_steps / dt, unit="tokens/s", cores=oracle.num_threads(),
+                kind="oracle", sample="decode N256 H32 d128: %d steps, %.2f s" % (n_steps, dt))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the KDA operator is benchmarked on a single "
+              "MI355X (every (sequence, head) chain is independent, so more GPUs would shard "
+              "sequences/heads with no exchange). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import kda_inputs
+    import linear_attention_sequence_chunkwise_amd as kda
+    kda.load_library()
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+
+    pf = bench_prefill(kda, kda_inputs, args.steps, args.warmup, stream)
+    print("prefill %.4f ms/call" % pf["ms"], file=sys.stderr, flush=True)
+    th = pf["token_heads"]
+    pf_bytes = PREFILL_BYTES_PER_TOKEN_HEAD * th
+    pf_flops = prefill_flops_per_token_head() * th
+    tok_s = pf["tokens"] / (pf["ms"] / 1e3)
+    roof = dict(bound="hbm", achieved=pf_bytes / (pf["ms"] / 1e3) / 1e9, peak=HBM_PEAK_GBS,
+                unit="GB/s", traffic=None, kernel="kda_chunk_fwd (all kernels of one call)",
+                algorithmic_bytes=pf_bytes,
+                mfma_tflops=pf_flops / (pf["ms"] / 1e3) / 1e12)
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["mfma_frac"] = roof["mfma_tflops"] / MFMA_PEAK_TFLOPS
+
+    dec = None
+    if not args.no_decode:
+        dc = bench_decode(kda, kda_inputs, args.decode_steps, args.warmup, stream)
+        print("decode %.4f ms/step" % dc["ms"], file=sys.stderr, flush=True)
+        db = DECODE_BYTES_PER_TOKEN_HEAD * dc["token_heads"]
+        dec = dict(metric="KDA decode tokens/s", value=dc["N"] / (dc["ms"] / 1e3),
+                   unit="tokens/s", ms_per_step=dc["ms"], steps=args.decode_steps,
+                   config=dict(workload="decode N256 H32 dk=dv=128 fp32 cache, 4096-token "
+                               "prefill init, 512 steps, bf16 q/k/v"),
+                   roofline=dict(bound="hbm", achieved=db / (dc["ms"] / 1e3) / 1e9,
+                                 peak=HBM_PEAK_GBS, unit="GB/s", traffic=None,
+                                 kernel="decode_step_kernel<128, bf16>",
+                                 algorithmic_bytes=db))
+        dec["roofline"]["frac"] = dec["roofline"]["achieved"] / HBM_PEAK_GBS
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_prefill(pf["inputs"])
+        if dec is not None:
+            dec["cpu_baseline"] = cpu_baseline_decode(kda_inputs)
+
+    out = {
+        "metric": "KDA prefill tokens/s (H=32, d=128)",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 inputs, fp16 matrix-core operands, fp32 accumulate/state",
+        "data": "synthetic (seeded), resident in HBM",
+        "config": {"workload": "prefill B=1 H=32 T=32768 dk=dv=128 chunk=64 bf16 q/k/v, fp32 "
+                               "gates, zero initial state", "global_batch": 1, "seq_len": 32768,
+                   "heads": 32, "head_dim": 128, "chunk": 64, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "decode": dec,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -10,6 +10,9 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+// 16-byte move unit.  A native vector type (unlike HIP's uint4 struct) keeps
+// register arrays of it in VGPRs.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 is carried as its raw 16-bit pattern.
 struct bf16_t {
@@ -19,6 +22,15 @@ struct bf16_t {
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) {
     return __builtin_bit_cast(float, (uint32_t)x.bits << 16);
+}
+
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also
+// waits for every outstanding global load and store of the wave
+// (vmcnt(0)), which would drain the prefetch queue and stall on store
+// completion at every barrier.  No kernel here reads global data written by
+// another thread of its workgroup, so waiting for LDS is sufficient.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Natural exponent through the hardware base-2 exponential.

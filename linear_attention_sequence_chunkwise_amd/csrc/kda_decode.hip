@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int i = 0; i < RPT; ++i)
         s[i] = *reinterpret_cast<const float4v*>(S + (size_t)(i * RG + rg) * D + 4 * cg);
 
-    __syncthreads();
+    lds_barrier();
 
     // k.q by wavefront 0
     if (tid < 64) {
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         s_red[0][rg][4 * cg + j] = pu[j];
         s_red[1][rg][4 * cg + j] = pp[j];
     }
-    __syncthreads();
+    lds_barrier();
 
     if (tid < D) {
         float u = 0.f, p = 0.f;
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         s_e[tid] = e;
         o[tok * D + tid] = scale * (p + s_kq[0] * e);
     }
-    __syncthreads();
+    lds_barrier();
 
     const float4v e4 = *reinterpret_cast<const float4v*>(&s_e[4 * cg]);
 #pragma unroll

@@ -41,6 +41,9 @@
 //   F_IJ = exp(Gs_I - Ge_J) <= 1 for J < I, = exp(Gs_I - Ge_I) >= 1 for J = I,
 // where Gs_I is G just before sub-block I and Ge_J is G at the last token of
 // sub-block J.  The only factor above one spans a single 16-token sub-block.
+#include <stdlib.h>
+#include <string.h>
+
 #include <type_traits>
 
 #include "kda_common.h"
@@ -86,35 +89,91 @@ struct MM<float> {
 template <typename OT>
 __device__ __forceinline__ OT to_ot(float x) { return (OT)x; }
 
+// 16 bytes of inputs -> floats (8 bf16 or 4 fp32), without taking addresses
+// (keeps the prefetch buffers in registers).
+// Two consecutive inputs as floats (bf16 pair from one 32-bit load).
+__device__ __forceinline__ float2 load2(const float* p) {
+    return *reinterpret_cast<const float2*>(p);
+}
+__device__ __forceinline__ float2 load2(const bf16_t* p) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    return float2{__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u)};
+}
+__device__ __forceinline__ void unpack16(const u32x4& w, float (&e)[8]) {
+    const uint32_t u[4] = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        e[2 * i] = __builtin_bit_cast(float, u[i] << 16);
+        e[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xffff0000u);
+    }
+}
+// floats -> 16 bytes of OT (8 fp16 or 4 fp32), rounded once, built without
+// type punning through memory.
+__device__ __forceinline__ u32x4 pack16(const float (&x)[8]) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)x[2 * i]);
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)x[2 * i + 1]);
+        w[i] = lo | (hi << 16);
+    }
+    return w;
+}
+__device__ __forceinline__ u32x4 pack16(const float (&x)[4]) {
+    return __builtin_bit_cast(u32x4, float4v{x[0], x[1], x[2], x[3]});
+}
+__device__ __forceinline__ void unpack16(const u32x4& w, float (&e)[4]) {
+    const float4v f = __builtin_bit_cast(float4v, w);
+    e[0] = f[0];
+    e[1] = f[1];
+    e[2] = f[2];
+    e[3] = f[3];
+}
+
 // Padded leading dimension: +16 bytes per row spreads the rows of a 16-row
 // fragment over distinct LDS banks.
 template <typename OT>
 constexpr int padded(int k) { return k + 16 / (int)sizeof(OT); }
 
+// k extent of the chunk-indexed operands: at least one instruction's k (the
+// columns beyond C are kept at zero).
+template <int C, typename OT>
+constexpr int chunk_k() { return C > MM<OT>::KS ? C : MM<OT>::KS; }
+
 // ---------------------------------------------------------------------------
-// Workspace record of one (chunk, head), in OT elements unless noted:
-//   KG  [C][D]   k_r * exp(G_r)
-//   QG  [C][D]   q_r * exp(G_r)
-//   KPt [D][C]   k_i * exp(G_n - G_i), transposed
-//   Tb  [C][C]   T diag(beta), T = (I + A)^-1
-//   M   [C][C]   lower-triangular q.k^T Gram (zero above the diagonal)
-//   Gn  [D]      exp(G_n) in fp32
+// Workspace record of one (chunk, head).  It is stored as the exact LDS image
+// the inter-chunk kernel works on (padded rows, zero k-padding), so that
+// kernel moves it with linear 16-byte copies (or direct global-to-LDS loads).
+// Offsets in OT elements unless noted:
+//   KG  [C][LDK]   k_r * exp(G_r)
+//   QG  [C][LDK]   q_r * exp(G_r)
+//   KPt [D][LDC]   k_i * exp(G_n - G_i), transposed
+//   Tb  [C][LDC]   T diag(beta), T = (I + A)^-1
+//   M   [C][LDC]   lower-triangular q.k^T Gram (zero above the diagonal)
+//   Gn  [D]        exp(G_n), fp32, at byte gn_byte
+// with LDK = D + pad, LDC = max(C, one instruction's k) + pad; the record is
+// rounded up to whole KiB.
 // ---------------------------------------------------------------------------
 template <int D, int C, typename OT>
 struct Rec {
+    static constexpr int LDK = padded<OT>(D);
+    static constexpr int CK = chunk_k<C, OT>();
+    static constexpr int LDC = padded<OT>(CK);
     static constexpr size_t KG = 0;
-    static constexpr size_t QG = (size_t)C * D;
-    static constexpr size_t KPt = 2 * (size_t)C * D;
-    static constexpr size_t Tb = 3 * (size_t)C * D;
-    static constexpr size_t M = 3 * (size_t)C * D + (size_t)C * C;
-    static constexpr size_t gn_byte = (3 * (size_t)C * D + 2 * (size_t)C * C) * sizeof(OT);
-    static constexpr size_t bytes = ((gn_byte + 4 * (size_t)D) + 255) / 256 * 256;
+    static constexpr size_t QG = (size_t)C * LDK;
+    static constexpr size_t KPt = 2 * (size_t)C * LDK;
+    static constexpr size_t Tb = KPt + (size_t)D * LDC;
+    static constexpr size_t M = Tb + (size_t)C * LDC;
+    static constexpr size_t gn_byte = (M + (size_t)C * LDC) * sizeof(OT);
+    static constexpr size_t bytes = (gn_byte + 4 * (size_t)D + 1023) / 1024 * 1024;
 };
 
 static size_t rec_bytes(int D, int C, bool bf16) {
     const size_t es = bf16 ? 2 : 4;
-    const size_t gn = (3 * (size_t)C * D + 2 * (size_t)C * C) * es;
-    return (gn + 4 * (size_t)D + 255) / 256 * 256;
+    const size_t ks = bf16 ? 32 : 4;
+    const size_t ldk = D + 16 / es, ck = (size_t)C > ks ? C : ks, ldc = ck + 16 / es;
+    const size_t gn = (2 * (size_t)C * ldk + (size_t)D * ldc + 2 * (size_t)C * ldc) * es;
+    return (gn + 4 * (size_t)D + 1023) / 1024 * 1024;
 }
 
 struct ChunkInfo {
@@ -188,20 +247,65 @@ __global__ __launch_bounds__(256) void kda_chunk_table(const int32_t* __restrict
 
 // ---------------------------------------------------------------------------
 // K1: intra-chunk work for one (chunk, head).  256 threads.
+//
+// Task = (channel c, 16-token sub-block I): a wavefront holds 64 consecutive
+// channels of one sub-block, so its loads of g, k, q rows are contiguous.
+// Record tiles leave the workgroup through LDS as 16-byte coalesced stores.
 // ---------------------------------------------------------------------------
 template <int D, int C, typename OT>
 struct IntraSmem {
     static constexpr int NB = C / 16;
     static constexpr int LDK = padded<OT>(D);
-    static constexpr int LDA = C + 4;
-    OT kl[C * LDK];            // k_r a_r       (Gram left, k)
-    OT ql[C * LDK];            // q_r a_r       (Gram left, q)
-    OT kr[C * LDK];            // k_i b_i       (Gram right)
+    static constexpr int LDA = padded<OT>(C);
+    static constexpr int LDT = C + 4;
+    // Gram operands while the Gram runs; afterwards the same bytes hold the
+    // triangular solve's fp32 T, the staged M tile and per-wave scratch.
+    struct Gram {
+        OT kl[C * LDK];        // k_r a_r       (Gram left, k)
+        OT ql[C * LDK];        // q_r a_r       (Gram left, q)
+        OT kr[C * LDK];        // k_i b_i       (Gram right)
+    };
+    struct Solve {
+        float T[C * LDT];      // (I + A)^-1, fp32
+        OT M[C * LDA];         // q.k^T Gram, staged for the record
+        float Y[4][256];       // one 16x16 scratch tile per wavefront
+    };
+    union {
+        Gram g;
+        Solve s;
+    } u;
+    OT A[C * LDA];             // beta-scaled strict-lower k.k^T Gram
     OT F[NB * NB * D];         // F_IJ per channel
     float sig[NB * D];         // per sub-block sum of g
-    float A[C * LDA];          // beta-scaled strict-lower k.k^T Gram, fp32
+    float egs[NB * D];         // exp(Gs_I): block start relative to the chunk start
+    float egn[NB * D];         // exp(G_n - Ge_I)
     float beta[C];
 };
+
+// acc += X (16x16 at x, row-major ld ldx) * Y (16x16 at y, row-major [k][n]
+// ld ldy), operands rounded to OT: one fp16 16x16x16 instruction, or four
+// fp32 16x16x4 instructions.
+template <typename OT, typename XT, typename YT>
+__device__ __forceinline__ float4v mma16(float4v acc, const XT* x, int ldx, const YT* y, int ldy,
+                                         int lane) {
+    const int l16 = lane & 15, lq = lane >> 4;
+    if constexpr (sizeof(OT) == 2) {
+        half4 a, b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[j] = (_Float16)(float)x[l16 * ldx + 4 * lq + j];
+            b[j] = (_Float16)(float)y[(4 * lq + j) * ldy + l16];
+        }
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, acc, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32((float)x[l16 * ldx + 4 * s4 + lq],
+                                                       (float)y[(4 * s4 + lq) * ldy + l16], acc,
+                                                       0, 0, 0);
+        return acc;
+    }
+}
 
 template <int D, int C, typename OT, typename IT>
 __global__ __launch_bounds__(256) void kda_intra(
@@ -210,9 +314,11 @@ __global__ __launch_bounds__(256) void kda_intra(
     const float* __restrict__ g, const float* __restrict__ beta, char* __restrict__ records) {
     constexpr int NB = C / 16;
     constexpr int LDK = padded<OT>(D);
-    constexpr int LDA = C + 4;
+    constexpr int LDA = padded<OT>(C);
+    constexpr int EPV = 16 / (int)sizeof(OT);       // OT elements per 16 bytes
     typedef MM<OT> mm;
     typedef Rec<D, C, OT> R;
+    typedef u32x4 vec;
     extern __shared__ __align__(16) char smem_raw[];
     IntraSmem<D, C, OT>& sm = *reinterpret_cast<IntraSmem<D, C, OT>*>(smem_raw);
 
@@ -229,57 +335,64 @@ __global__ __launch_bounds__(256) void kda_intra(
         tok0 = b * T + c * C;
         len = min(C, T - c * C);
     }
-    OT* rec = reinterpret_cast<OT*>(records + ((size_t)ch * H + h) * R::bytes);
-    float* gn_out = reinterpret_cast<float*>(records + ((size_t)ch * H + h) * R::bytes + R::gn_byte);
+    char* recb = records + ((size_t)ch * H + h) * R::bytes;
+    OT* rec = reinterpret_cast<OT*>(recb);
+    float* gn_out = reinterpret_cast<float*>(recb + R::gn_byte);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    if (tid < C) sm.beta[tid] = tid < len ? beta[(size_t)(tok0 + tid) * H + h] : 0.f;
+    if (tid < C) {
+        const float bt = beta[(size_t)(tok0 + min(tid, len - 1)) * H + h];
+        sm.beta[tid] = tid < len ? bt : 0.f;
+    }
 
-    // ---- phase 1: per (channel pair, sub-block) task: prefix sums of g ----
+    // ---- phase 1: per task (channel pair, 16-token sub-block): load the
+    // sub-block's two columns of g, k, q and the sub-block gate sums ----
+    // Branch-free: every row is loaded (rows past the chunk end re-read its
+    // last row) and masked afterwards, so all loads issue before the first
+    // one is waited on.
     constexpr int NP = D / 2;
     const int cp = tid % NP;
     const int I = tid / NP;
     const bool task = I < NB;
     const int c0 = 2 * cp;
-    float P0[16], P1[16], k0v[16], k1v[16], q0v[16], q1v[16];
+    float g0[16], g1[16], k0v[16], k1v[16], q0v[16], q1v[16];
     if (task) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int r = min(16 * I + j, len - 1);
+            const size_t off = ((size_t)(tok0 + r) * H + h) * D + c0;
+            const float2 gg = *reinterpret_cast<const float2*>(g + off);
+            const float2 kk = load2(k + off);
+            const float2 qq = load2(q + off);
+            g0[j] = gg.x; g1[j] = gg.y;
+            k0v[j] = kk.x; k1v[j] = kk.y;
+            q0v[j] = qq.x; q1v[j] = qq.y;
+        }
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const int r = 16 * I + j;
-            float gx = 0.f, gy = 0.f, kx = 0.f, ky = 0.f, qx = 0.f, qy = 0.f;
-            if (r < len) {
-                const size_t base = ((size_t)(tok0 + r) * H + h) * D + c0;
-                const float2 g2 = *reinterpret_cast<const float2*>(g + base);
-                gx = g2.x;
-                gy = g2.y;
-                kx = to_f32(k[base]);
-                ky = to_f32(k[base + 1]);
-                qx = to_f32(q[base]);
-                qy = to_f32(q[base + 1]);
+            if (16 * I + j >= len) {
+                g0[j] = g1[j] = k0v[j] = k1v[j] = q0v[j] = q1v[j] = 0.f;
             }
-            s0 += gx;
-            s1 += gy;
-            P0[j] = s0;
-            P1[j] = s1;
-            k0v[j] = kx;
-            k1v[j] = ky;
-            q0v[j] = qx;
-            q1v[j] = qy;
+            s0 += g0[j];
+            s1 += g1[j];
         }
         sm.sig[I * D + c0] = s0;
         sm.sig[I * D + c0 + 1] = s1;
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- phase 2: decay factors and operand tiles ----
+    // ---- phase 2: decay factors (one exp per element) and Gram operands ----
     if (task) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int c = c0 + e;
+            float* gv = e ? g1 : g0;
+            const float* kv = e ? k1v : k0v;
+            const float* qv = e ? q1v : q0v;
             float Gs = 0.f, Gn = 0.f;
 #pragma unroll
             for (int m = 0; m < NB; ++m) {
@@ -287,10 +400,9 @@ __global__ __launch_bounds__(256) void kda_intra(
                 if (m < I) Gs += sg;
                 Gn += sg;
             }
-            const float sigI = e ? P1[15] : P0[15];
-            const float eGs = exp_e(Gs);                 // exp(G at block start) <= 1
-            const float eGnGe = exp_e(Gn - Gs - sigI);   // exp(G_n - Ge_I) <= 1
-            // F_IJ for J <= I
+            const float sigI = sm.sig[I * D + c];
+            sm.egs[I * D + c] = exp_e(Gs);                // exp(G before block I) <= 1
+            sm.egn[I * D + c] = exp_e(Gn - Gs - sigI);    // exp(G_n - Ge_I) <= 1
             float GsJ = 0.f;
             for (int J = 0; J <= I; ++J) {
                 const float sgJ = sm.sig[J * D + c];
@@ -299,183 +411,407 @@ __global__ __launch_bounds__(256) void kda_intra(
                 GsJ += sgJ;
             }
             if (I == 0) gn_out[c] = exp_e(Gn);
-            OT kpt[16];
+            // alpha_j = exp(g_j); a_j = prod_{j'<=j} alpha, b_j = prod_{j'>j} alpha
+#pragma unroll
+            for (int j = 0; j < 16; ++j) gv[j] = exp_e(gv[j]);
+            float a = 1.f;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
+                a *= gv[j];
                 const int r = 16 * I + j;
-                const float P = e ? P1[j] : P0[j];
-                const float kv = e ? k1v[j] : k0v[j];
-                const float qv = e ? q1v[j] : q0v[j];
-                const float a = exp_e(P);            // exp(G_r - Gs_I)
-                const float b = exp_e(sigI - P);     // exp(Ge_I - G_r)
-                sm.kl[r * LDK + c] = to_ot<OT>(kv * a);
-                sm.ql[r * LDK + c] = to_ot<OT>(qv * a);
-                sm.kr[r * LDK + c] = to_ot<OT>(kv * b);
-                rec[R::KG + (size_t)r * D + c] = to_ot<OT>(kv * a * eGs);
-                rec[R::QG + (size_t)r * D + c] = to_ot<OT>(qv * a * eGs);
-                kpt[j] = to_ot<OT>(kv * b * eGnGe);
+                sm.u.g.kl[r * LDK + c] = to_ot<OT>(kv[j] * a);
+                sm.u.g.ql[r * LDK + c] = to_ot<OT>(qv[j] * a);
             }
-            OT* dst = rec + R::KPt + (size_t)c * C + 16 * I;
+            float bb = 1.f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) dst[j] = kpt[j];
+            for (int j = 15; j >= 0; --j) {
+                const int r = 16 * I + j;
+                sm.u.g.kr[r * LDK + c] = to_ot<OT>(kv[j] * bb);
+                bb *= gv[j];
+            }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- phase 3: Gram blocks on the matrix cores ----
-    // tiles: t in [0, NB(NB+1)) ; first half A (k.k^T), second half M (q.k^T)
+    // ---- phase 3a: record tiles KG, QG, KPt from the LDS operands ----
+    // KG_r = (k_r a_r) exp(Gs_I), QG_r = (q_r a_r) exp(Gs_I) : rows of 16 bytes
+    for (int idx = tid; idx < C * D / EPV; idx += 256) {
+        const int r = idx / (D / EPV), c0 = (idx % (D / EPV)) * EPV;
+        const float* eg = &sm.egs[(r >> 4) * D + c0];
+        float kk[EPV], qq[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            kk[e] = (float)sm.u.g.kl[r * LDK + c0 + e] * eg[e];
+            qq[e] = (float)sm.u.g.ql[r * LDK + c0 + e] * eg[e];
+        }
+        *reinterpret_cast<vec*>(rec + R::KG + (size_t)r * R::LDK + c0) = pack16(kk);
+        *reinterpret_cast<vec*>(rec + R::QG + (size_t)r * R::LDK + c0) = pack16(qq);
+    }
+    // KPt[c][i] = (k_i b_i) exp(G_n - Ge_J), transposed: 16 bytes of one channel row
+    for (int idx = tid; idx < D * C / EPV; idx += 256) {
+        const int c = idx / (C / EPV), i0 = (idx % (C / EPV)) * EPV;
+        const float f = sm.egn[(i0 >> 4) * D + c];
+        float kk[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) kk[e] = (float)sm.u.g.kr[(i0 + e) * LDK + c] * f;
+        *reinterpret_cast<vec*>(rec + R::KPt + (size_t)c * R::LDC + i0) = pack16(kk);
+    }
+
+    // ---- phase 3b: Gram blocks on the matrix cores ----
+    // tiles t in [0, 2 NT): first NT are A (k.k^T), the rest M (q.k^T).  A goes
+    // to LDS now; M stays in registers until the Gram operands are dead.
     constexpr int NT = NB * (NB + 1) / 2;
+    constexpr int TPW = (2 * NT + 3) / 4;
     const int l16 = lane & 15;
     const int lq = lane >> 4;
-    for (int t = wave; t < 2 * NT; t += 4) {
-        const bool isM = t >= NT;
-        int tt = isM ? t - NT : t;
-        int Ib = 0;
-        while (tt > Ib) { tt -= Ib + 1; ++Ib; }
-        const int Jb = tt;
-        const OT* left = isM ? sm.ql : sm.kl;
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
+    float4v macc[TPW];
 #pragma unroll
-        for (int ks = 0; ks < D; ks += mm::KS) {
-            const int kk = ks + lq * mm::KPL;
-            typename mm::frag af = mm::load(left, LDK, 16 * Ib + l16, kk);
-            typename mm::frag bf = mm::load(sm.kr, LDK, 16 * Jb + l16, kk);
-            const typename mm::frag ff = mm::load(sm.F + (Ib * NB + Jb) * D, 0, 0, kk);
-            bf = bf * ff;
-            acc = mm::mma(af, bf, acc);
-        }
-        const int col = 16 * Jb + l16;
+    for (int i = 0; i < TPW; ++i) {
+        const int t = wave + 4 * i;
+        macc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+        if (t < 2 * NT) {
+            const bool isM = t >= NT;
+            int tt = isM ? t - NT : t;
+            int Ib = 0;
+            while (tt > Ib) { tt -= Ib + 1; ++Ib; }
+            const int Jb = tt;
+            const OT* left = isM ? sm.u.g.ql : sm.u.g.kl;
+            float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * Ib + 4 * lq + j;
-            if (!isM) {
-                sm.A[row * LDA + col] = col < row ? sm.beta[row] * acc[j] : 0.f;
-            } else {
-                rec[R::M + (size_t)row * C + col] = to_ot<OT>(col <= row ? acc[j] : 0.f);
+            for (int ks = 0; ks < D; ks += mm::KS) {
+                const int kk = ks + lq * mm::KPL;
+                typename mm::frag af = mm::load(left, LDK, 16 * Ib + l16, kk);
+                typename mm::frag bf = mm::load(sm.u.g.kr, LDK, 16 * Jb + l16, kk);
+                const typename mm::frag ff = mm::load(sm.F + (Ib * NB + Jb) * D, 0, 0, kk);
+                bf = bf * ff;
+                acc = mm::mma(af, bf, acc);
+            }
+            const int col = 16 * Jb + l16;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * Ib + 4 * lq + j;
+                if (!isM) sm.A[row * LDA + col] = to_ot<OT>(col < row ? sm.beta[row] * acc[j] : 0.f);
+                else macc[i][j] = col <= row ? acc[j] : 0.f;
             }
         }
     }
-    // upper off-diagonal tiles of M are never read by K2; A's upper part is
-    // never read by the solve.
-    __syncthreads();
+    // zero A above the diagonal blocks
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int r = idx / C, col = idx - r * C;
+        if ((col >> 4) > (r >> 4)) sm.A[r * LDA + col] = to_ot<OT>(0.f);
+    }
+    lds_barrier();   // Gram operands dead from here on
 
-    // ---- phase 4: T = (I + A)^-1 by forward substitution, column per lane ----
-    if (wave != 0) {   // zero M above the diagonal blocks (read as padding by K2)
-        for (int idx = tid - 64; idx < C * C; idx += 192) {
-            const int r = idx / C, col = idx - r * C;
-            if ((col >> 4) > (r >> 4)) rec[R::M + idx] = to_ot<OT>(0.f);
+    // ---- phase 4a: stage M; invert the diagonal 16x16 blocks of I + A ----
+    constexpr int LDT = C + 4;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int t = wave + 4 * i;
+        if (t >= NT && t < 2 * NT) {
+            int tt = t - NT;
+            int Ib = 0;
+            while (tt > Ib) { tt -= Ib + 1; ++Ib; }
+            const int Jb = tt;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sm.u.s.M[(16 * Ib + 4 * lq + j) * LDA + 16 * Jb + l16] = to_ot<OT>(macc[i][j]);
         }
     }
-    if (wave == 0 && lane < C) {
-        const int c = lane;
-        float x[C];
+    for (int idx = tid; idx < C * C; idx += 256) {   // zero the upper blocks of M and T
+        const int r = idx / C, col = idx - r * C;
+        if ((col >> 4) > (r >> 4)) {
+            sm.u.s.M[r * LDA + col] = to_ot<OT>(0.f);
+            sm.u.s.T[r * LDT + col] = 0.f;
+        }
+    }
+    if (wave < NB && lane < 16) {
+        // column `lane` of (I + A_II)^-1 by forward substitution (4 partial sums)
+        const int I = wave, jc = lane;
+        const OT* Ab = &sm.A[(16 * I) * LDA + 16 * I];
+        float x[16];
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
-            float s = 0.f;
+        for (int r = 0; r < 16; ++r) {
+            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
             for (int m = 0; m < r; m += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(&sm.A[r * LDA + m]);
-                s += a4.x * x[m];
-                if (m + 1 < r) s += a4.y * x[m + 1];
-                if (m + 2 < r) s += a4.z * x[m + 2];
-                if (m + 3 < r) s += a4.w * x[m + 3];
+                const OT* ar = Ab + r * LDA + m;
+                s0 += (float)ar[0] * x[m];
+                if (m + 1 < r) s1 += (float)ar[1] * x[m + 1];
+                if (m + 2 < r) s2 += (float)ar[2] * x[m + 2];
+                if (m + 3 < r) s3 += (float)ar[3] * x[m + 3];
             }
-            x[r] = (r == c) ? 1.f : ((r < c) ? 0.f : -s);
+            x[r] = (r == jc) ? 1.f : ((r < jc) ? 0.f : -((s0 + s1) + (s2 + s3)));
         }
-        const float bc = sm.beta[c];
 #pragma unroll
-        for (int r = 0; r < C; ++r) rec[R::Tb + (size_t)r * C + c] = to_ot<OT>(x[r] * bc);
+        for (int r = 0; r < 16; ++r) sm.u.s.T[(16 * I + r) * LDT + 16 * I + jc] = x[r];
+    }
+    lds_barrier();
+
+    // ---- phase 4b: store M; off-diagonal blocks of T level by level:
+    //      T_IJ = -T_II * sum_{m=J}^{I-1} A_Im T_mJ ----
+    for (int idx = tid; idx < C * C / EPV; idx += 256) {
+        const int r = idx / (C / EPV), c0 = (idx % (C / EPV)) * EPV;
+        *reinterpret_cast<vec*>(rec + R::M + (size_t)r * R::LDC + c0) =
+            *reinterpret_cast<const vec*>(&sm.u.s.M[r * LDA + c0]);
+    }
+    for (int d = 1; d < NB; ++d) {
+        if (wave < NB - d) {
+            const int J = wave, I = wave + d;
+            float4v y = {0.f, 0.f, 0.f, 0.f};
+            for (int m = J; m < I; ++m)
+                y = mma16<OT>(y, &sm.A[(16 * I) * LDA + 16 * m], LDA,
+                              &sm.u.s.T[(16 * m) * LDT + 16 * J], LDT, lane);
+            float* Y = sm.u.s.Y[wave];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Y[(4 * lq + j) * 16 + l16] = y[j];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            float4v t = {0.f, 0.f, 0.f, 0.f};
+            t = mma16<OT>(t, &sm.u.s.T[(16 * I) * LDT + 16 * I], LDT, Y, 16, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sm.u.s.T[(16 * I + 4 * lq + j) * LDT + 16 * J + l16] = -t[j];
+        }
+        lds_barrier();
+    }
+
+    // ---- phase 5: Tb = T diag(beta) into the record (16-byte rows) ----
+    for (int idx = tid; idx < C * C / EPV; idx += 256) {
+        const int r = idx / (C / EPV), c0 = (idx % (C / EPV)) * EPV;
+        float tv[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) tv[e] = sm.u.s.T[r * LDT + c0 + e] * sm.beta[c0 + e];
+        *reinterpret_cast<vec*>(rec + R::Tb + (size_t)r * R::LDC + c0) = pack16(tv);
+    }
+    if constexpr (R::CK > C) {   // zero k-padding of the chunk-indexed tiles
+        constexpr int PV = (R::CK - C) / EPV;
+        for (int idx = tid; idx < (D + 2 * C) * PV; idx += 256) {
+            const int row = idx / PV, c0 = C + (idx % PV) * EPV;
+            const size_t off = row < D ? R::KPt + (size_t)row * R::LDC
+                             : row < D + C ? R::Tb + (size_t)(row - D) * R::LDC
+                                           : R::M + (size_t)(row - D - C) * R::LDC;
+            *reinterpret_cast<vec*>(rec + off + c0) = vec{0u, 0u, 0u, 0u};
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // K2: inter-chunk recurrence + output for one (sequence, head, dv-slice).
+//
+// Workgroups are mapped so that all dv-slices of one (sequence, head) run on
+// the same XCD (dispatch is round-robin over the 8 XCDs), where they share
+// each chunk record through that XCD's L2.
 // ---------------------------------------------------------------------------
-// k extent of the chunk-indexed operands: at least one instruction's k (the
-// columns beyond C are kept at zero).
-template <int C, typename OT>
-constexpr int chunk_k() { return C > MM<OT>::KS ? C : MM<OT>::KS; }
+// Views of one chunk's tiles in LDS (same layout as the workspace record) and
+// of the value slice [C][BV] (raw input dtype).
+template <int D, int C, typename OT, typename IT>
+struct ChunkTiles {
+    const OT* kg;
+    const OT* qg;
+    const OT* kpt;
+    const OT* tb;
+    const OT* m;
+    const float* gn;
+    const IT* v;
+    __device__ ChunkTiles(const char* img, const IT* vraw) {
+        typedef Rec<D, C, OT> R;
+        const OT* base = reinterpret_cast<const OT*>(img);
+        kg = base + R::KG;
+        qg = base + R::QG;
+        kpt = base + R::KPt;
+        tb = base + R::Tb;
+        m = base + R::M;
+        gn = reinterpret_cast<const float*>(img + R::gn_byte);
+        v = vraw;
+    }
+};
 
+// Per-workgroup state operand and scratch of the chain.
 template <int D, int C, int BV, typename OT>
-struct InterSmem {
+struct ChainScratch {
     static constexpr int LDK = padded<OT>(D);
     static constexpr int LDC = padded<OT>(chunk_k<C, OT>());
-    OT kg[C * LDK];
-    OT qg[C * LDK];
-    OT kpt[D * LDC];
-    OT tb[C * LDC];
-    OT m[C * LDC];
     OT s[BV * LDK];      // state operand, [v][c]
     OT x[BV * LDC];      // V - KG S, [v][i]
     OT u[BV * LDC];      // U, [v][i]
-    float v[C * BV];     // value slice, [i][v]
-    float gn[D];
 };
 
-template <int D, int C, int BV, typename OT>
-constexpr size_t inter_smem_bytes() { return sizeof(InterSmem<D, C, BV, OT>); }
-template <int D, int C, typename OT>
-constexpr size_t intra_smem_bytes() { return sizeof(IntraSmem<D, C, OT>); }
-
+// One chunk of the chain: X = V - KG S, QS = QG S, U = Tb X,
+// O = scale (QS + M U), S <- Diag(Gamma_n) S + KPt U.  Ends with the new
+// state published to LDS; a barrier separates the last reads of the chunk
+// tiles and of the old state from that write, so on return the chunk's tiles
+// may be overwritten.
 template <int D, int C, int BV, typename OT, typename IT>
-__global__ __launch_bounds__(256) void kda_inter(
-    int T, int H, int N_seq, int nch_seq, const int32_t* __restrict__ cu,
-    const int* __restrict__ chunk_off, float scale, const IT* __restrict__ v, const float* __restrict__ s0,
-    const char* __restrict__ records, float* __restrict__ o, float* __restrict__ sT) {
-    constexpr int P = D / BV;
+__device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
+                                            ChainScratch<D, C, BV, OT>& cs,
+                                            float4v (&st)[((D / 16) * (BV / 16) + 3) / 4],
+                                            int tok0, int len, int H, int h, int v0,
+                                            float scale, float* __restrict__ o) {
     constexpr int LDK = padded<OT>(D);
     constexpr int CK = chunk_k<C, OT>();
     constexpr int LDC = padded<OT>(CK);
-    constexpr int RT = C / 16;          // row tiles of a chunk
-    constexpr int VT = BV / 16;         // column tiles of the slice
-    constexpr int ST = (D / 16) * VT;   // state tiles
-    constexpr int SPW = (ST + 3) / 4;   // state tiles per wave
+    constexpr int RT = C / 16;
+    constexpr int VT = BV / 16;
+    constexpr int ST = (D / 16) * VT;
+    constexpr int SPW = (ST + 3) / 4;
+    constexpr int OTILES = RT * VT;
+    constexpr int OPW = (OTILES + 3) / 4;
     typedef MM<OT> mm;
-    typedef Rec<D, C, OT> R;
-    extern __shared__ __align__(16) char smem_raw[];
-    InterSmem<D, C, BV, OT>& sm = *reinterpret_cast<InterSmem<D, C, BV, OT>*>(smem_raw);
-
-    const int id = blockIdx.x;
-    const int p = id % P;
-    const int nh = id / P;
-    const int h = nh % H;
-    const int n = nh / H;
-    const int v0 = p * BV;
-
-    int first, nch, seq_tok0, seq_len;
-    if (cu) {
-        first = chunk_off[n];
-        nch = min(chunk_off[n + 1], chunk_off[N_seq]) - first;
-        if (nch < 0) nch = 0;
-        seq_tok0 = cu[n];
-        seq_len = cu[n + 1] - seq_tok0;
-    } else {
-        first = n * nch_seq;
-        nch = nch_seq;
-        seq_tok0 = n * T;
-        seq_len = T;
-    }
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int l16 = lane & 15;
     const int lq = lane >> 4;
 
-    if constexpr (CK > C) {   // zero the k padding of the chunk-indexed tiles once
-        for (int r = tid; r < D + 2 * C + 2 * BV; r += 256) {
-            OT* row = r < D ? sm.kpt + r * LDC
-                    : r < D + C ? sm.tb + (r - D) * LDC
-                    : r < D + 2 * C ? sm.m + (r - D - C) * LDC
-                    : r < D + 2 * C + BV ? sm.x + (r - D - 2 * C) * LDC
-                    : sm.u + (r - D - 2 * C - BV) * LDC;
-            for (int c = C; c < CK; ++c) row[c] = to_ot<OT>(0.f);
+    // ---- X = V - KG S and QS = QG S (shared state fragments) ----
+    float4v qs[OPW];
+#pragma unroll
+    for (int i = 0; i < OPW; ++i) {
+        const int tt = wave + 4 * i;
+        qs[i] = float4v{0.f, 0.f, 0.f, 0.f};
+        if (tt < OTILES) {
+            const int rt = tt / VT, vt = tt % VT;
+            float4v xk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < D; ks += mm::KS) {
+                const int kk = ks + lq * mm::KPL;
+                const typename mm::frag bs = mm::load(cs.s, LDK, 16 * vt + l16, kk);
+                xk = mm::mma(mm::load(t.kg, LDK, 16 * rt + l16, kk), bs, xk);
+                qs[i] = mm::mma(mm::load(t.qg, LDK, 16 * rt + l16, kk), bs, qs[i]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * rt + 4 * lq + j;
+                const float vv = r < len ? to_f32(t.v[r * BV + 16 * vt + l16]) : 0.f;
+                cs.x[(16 * vt + l16) * LDC + r] = to_ot<OT>(vv - xk[j]);
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- U = Tb X (Tb lower triangular: k only up to the diagonal block) ----
+#pragma unroll
+    for (int i = 0; i < OPW; ++i) {
+        const int tt = wave + 4 * i;
+        if (tt < OTILES) {
+            const int rt = tt / VT, vt = tt % VT;
+            float4v uacc = {0.f, 0.f, 0.f, 0.f};
+            const int kend = 16 * (rt + 1);
+            for (int ks = 0; ks < kend; ks += mm::KS) {
+                const int kk = ks + lq * mm::KPL;
+                uacc = mm::mma(mm::load(t.tb, LDC, 16 * rt + l16, kk),
+                               mm::load(cs.x, LDC, 16 * vt + l16, kk), uacc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                cs.u[(16 * vt + l16) * LDC + 16 * rt + 4 * lq + j] = to_ot<OT>(uacc[j]);
+        }
+    }
+    lds_barrier();
+
+    // ---- O = scale (QS + M U) ----
+#pragma unroll
+    for (int i = 0; i < OPW; ++i) {
+        const int tt = wave + 4 * i;
+        if (tt < OTILES) {
+            const int rt = tt / VT, vt = tt % VT;
+            float4v acc = qs[i];
+            const int kend = 16 * (rt + 1);
+            for (int ks = 0; ks < kend; ks += mm::KS) {
+                const int kk = ks + lq * mm::KPL;
+                acc = mm::mma(mm::load(t.m, LDC, 16 * rt + l16, kk),
+                              mm::load(cs.u, LDC, 16 * vt + l16, kk), acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * rt + 4 * lq + j;
+                if (r < len)
+                    o[((size_t)(tok0 + r) * H + h) * D + v0 + 16 * vt + l16] = scale * acc[j];
+            }
         }
     }
 
-    // ---- state tiles owned by this wave: fp32 in registers ----
-    float4v st[SPW];
-    const size_t sbase = ((size_t)n * H + h) * (size_t)D * D;
+    // ---- S <- Diag(Gamma_n) S + KPt U ----
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int s = wave + 4 * i;
+        if (s < ST) {
+            const int ct = s / VT, vt = s % VT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st[i][j] *= t.gn[16 * ct + 4 * lq + j];
+#pragma unroll
+            for (int ks = 0; ks < CK; ks += mm::KS) {
+                const int kk = ks + lq * mm::KPL;
+                st[i] = mm::mma(mm::load(t.kpt, LDC, 16 * ct + l16, kk),
+                                mm::load(cs.u, LDC, 16 * vt + l16, kk), st[i]);
+            }
+        }
+    }
+    lds_barrier();   // all reads of the chunk tiles and of the old state are done
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int s = wave + 4 * i;
+        if (s < ST) {
+            const int ct = s / VT, vt = s % VT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                cs.s[(16 * vt + l16) * LDK + 16 * ct + 4 * lq + j] = to_ot<OT>(st[i][j]);
+        }
+    }
+}
+
+// Chain bounds of workgroup `L` (logical index after the XCD remap).
+struct ChainPos {
+    int n, h, v0, first, nch, seq_tok0, seq_len;
+    bool valid;
+};
+template <int D, int BV>
+__device__ __forceinline__ ChainPos chain_pos(int T, int H, int N_seq, int nch_seq, int G8,
+                                              const int32_t* __restrict__ cu,
+                                              const int* __restrict__ chunk_off) {
+    constexpr int P = D / BV;
+    ChainPos c;
+    const int b = blockIdx.x;
+    const int L = (b & 7) * G8 + (b >> 3);
+    const int p = L % P;
+    const int nh = L / P;
+    c.valid = nh < N_seq * H;
+    if (!c.valid) return c;
+    c.h = nh % H;
+    c.n = nh / H;
+    c.v0 = p * BV;
+    if (cu) {
+        c.first = chunk_off[c.n];
+        c.nch = min(chunk_off[c.n + 1], chunk_off[N_seq]) - c.first;
+        if (c.nch < 0) c.nch = 0;
+        c.seq_tok0 = cu[c.n];
+        c.seq_len = cu[c.n + 1] - c.seq_tok0;
+    } else {
+        c.first = c.n * nch_seq;
+        c.nch = nch_seq;
+        c.seq_tok0 = c.n * T;
+        c.seq_len = T;
+    }
+    return c;
+}
+
+// State tiles owned by this wave (fp32, MFMA output layout) from s0 or zero,
+// and the fp16/fp32 state operand in LDS.
+template <int D, int C, int BV, typename OT>
+__device__ __forceinline__ void chain_load_state(float4v (&st)[((D / 16) * (BV / 16) + 3) / 4],
+                                                 ChainScratch<D, C, BV, OT>& cs,
+                                                 const float* __restrict__ s0, size_t sbase,
+                                                 int v0) {
+    constexpr int VT = BV / 16, ST = (D / 16) * VT, SPW = (ST + 3) / 4;
+    constexpr int LDK = padded<OT>(D);
+    constexpr int CK = chunk_k<C, OT>();
+    constexpr int LDC = padded<OT>(CK);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lq = lane >> 4;
+    if constexpr (CK > C) {   // k-padding of X and U stays zero for the whole chain
+        for (int idx = threadIdx.x; idx < 2 * BV * (CK - C); idx += 256) {
+            const int row = idx / (CK - C), col = C + idx % (CK - C);
+            (row < BV ? cs.x : cs.u)[(row % BV) * LDC + col] = to_ot<OT>(0.f);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
         const int s = wave + 4 * i;
@@ -487,7 +823,6 @@ __global__ __launch_bounds__(256) void kda_inter(
                 st[i][j] = s0[sbase + (size_t)(16 * ct + 4 * lq + j) * D + v0 + 16 * vt + l16];
         }
     }
-    // publish the state operand
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
         const int s = wave + 4 * i;
@@ -495,163 +830,182 @@ __global__ __launch_bounds__(256) void kda_inter(
             const int ct = s / VT, vt = s % VT;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                sm.s[(16 * vt + l16) * LDK + 16 * ct + 4 * lq + j] = to_ot<OT>(st[i][j]);
+                cs.s[(16 * vt + l16) * LDK + 16 * ct + 4 * lq + j] = to_ot<OT>(st[i][j]);
         }
     }
+}
 
-    for (int c = 0; c < nch; ++c) {
-        const int ch = first + c;
-        const int tok0 = seq_tok0 + c * C;
-        const int len = min(C, seq_len - c * C);
-        const OT* rec = reinterpret_cast<const OT*>(records + ((size_t)ch * H + h) * R::bytes);
-        const float* gn = reinterpret_cast<const float*>(records + ((size_t)ch * H + h) * R::bytes + R::gn_byte);
-
-        // ---- stage the chunk record into LDS (16-byte moves) ----
-        constexpr int EPV = 16 / sizeof(OT);   // elements per 16 bytes
-        {
-            typedef uint4 vec;
-            // KG, QG: [C][D] -> [C][LDK]
-            for (int idx = tid; idx < C * D / EPV; idx += 256) {
-                const int r = idx / (D / EPV), cc = (idx % (D / EPV)) * EPV;
-                *reinterpret_cast<vec*>(&sm.kg[r * LDK + cc]) =
-                    *reinterpret_cast<const vec*>(rec + R::KG + (size_t)r * D + cc);
-                *reinterpret_cast<vec*>(&sm.qg[r * LDK + cc]) =
-                    *reinterpret_cast<const vec*>(rec + R::QG + (size_t)r * D + cc);
-            }
-            // KPt: [D][C] -> [D][LDC]
-            for (int idx = tid; idx < D * C / EPV; idx += 256) {
-                const int r = idx / (C / EPV), cc = (idx % (C / EPV)) * EPV;
-                *reinterpret_cast<vec*>(&sm.kpt[r * LDC + cc]) =
-                    *reinterpret_cast<const vec*>(rec + R::KPt + (size_t)r * C + cc);
-            }
-            // Tb, M: [C][C] -> [C][LDC]
-            for (int idx = tid; idx < C * C / EPV; idx += 256) {
-                const int r = idx / (C / EPV), cc = (idx % (C / EPV)) * EPV;
-                *reinterpret_cast<vec*>(&sm.tb[r * LDC + cc]) =
-                    *reinterpret_cast<const vec*>(rec + R::Tb + (size_t)r * C + cc);
-                *reinterpret_cast<vec*>(&sm.m[r * LDC + cc]) =
-                    *reinterpret_cast<const vec*>(rec + R::M + (size_t)r * C + cc);
-            }
-            for (int idx = tid; idx < D; idx += 256) sm.gn[idx] = gn[idx];
-            for (int idx = tid; idx < C * BV; idx += 256) {
-                const int r = idx / BV, vv = idx % BV;
-                sm.v[idx] = r < len ? to_f32(v[((size_t)(tok0 + r) * H + h) * D + v0 + vv]) : 0.f;
-            }
-        }
-        __syncthreads();
-
-        // ---- X = V - KG S and QS = QG S (shared state fragments) ----
-        constexpr int OTILES = RT * VT;
-        constexpr int OPW = (OTILES + 3) / 4;
-        float4v qs[OPW];
+template <int D, int BV>
+__device__ __forceinline__ void chain_store_state(
+    const float4v (&st)[((D / 16) * (BV / 16) + 3) / 4], float* __restrict__ sT, size_t sbase,
+    int v0) {
+    constexpr int VT = BV / 16, ST = (D / 16) * VT, SPW = (ST + 3) / 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
-        for (int i = 0; i < OPW; ++i) {
-            const int t = wave + 4 * i;
-            qs[i] = float4v{0.f, 0.f, 0.f, 0.f};
-            if (t < OTILES) {
-                const int rt = t / VT, vt = t % VT;
-                float4v xk = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < SPW; ++i) {
+        const int s = wave + 4 * i;
+        if (s < ST) {
+            const int ct = s / VT, vt = s % VT;
 #pragma unroll
-                for (int ks = 0; ks < D; ks += mm::KS) {
-                    const int kk = ks + lq * mm::KPL;
-                    const typename mm::frag bs = mm::load(sm.s, LDK, 16 * vt + l16, kk);
-                    xk = mm::mma(mm::load(sm.kg, LDK, 16 * rt + l16, kk), bs, xk);
-                    qs[i] = mm::mma(mm::load(sm.qg, LDK, 16 * rt + l16, kk), bs, qs[i]);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * rt + 4 * lq + j;
-                    const float xv = sm.v[r * BV + 16 * vt + l16] - xk[j];
-                    sm.x[(16 * vt + l16) * LDC + r] = to_ot<OT>(xv);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- U = Tb X (Tb lower triangular: k only up to the diagonal block) ----
-#pragma unroll
-        for (int i = 0; i < OPW; ++i) {
-            const int t = wave + 4 * i;
-            if (t < OTILES) {
-                const int rt = t / VT, vt = t % VT;
-                float4v uacc = {0.f, 0.f, 0.f, 0.f};
-                const int kend = 16 * (rt + 1);
-                for (int ks = 0; ks < kend; ks += mm::KS) {
-                    const int kk = ks + lq * mm::KPL;
-                    uacc = mm::mma(mm::load(sm.tb, LDC, 16 * rt + l16, kk),
-                                   mm::load(sm.x, LDC, 16 * vt + l16, kk), uacc);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    sm.u[(16 * vt + l16) * LDC + 16 * rt + 4 * lq + j] = to_ot<OT>(uacc[j]);
-            }
-        }
-        __syncthreads();
-
-        // ---- O = scale (QS + M U) ----
-#pragma unroll
-        for (int i = 0; i < OPW; ++i) {
-            const int t = wave + 4 * i;
-            if (t < OTILES) {
-                const int rt = t / VT, vt = t % VT;
-                float4v acc = qs[i];
-                const int kend = 16 * (rt + 1);
-                for (int ks = 0; ks < kend; ks += mm::KS) {
-                    const int kk = ks + lq * mm::KPL;
-                    acc = mm::mma(mm::load(sm.m, LDC, 16 * rt + l16, kk),
-                                  mm::load(sm.u, LDC, 16 * vt + l16, kk), acc);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * rt + 4 * lq + j;
-                    if (r < len)
-                        o[((size_t)(tok0 + r) * H + h) * D + v0 + 16 * vt + l16] = scale * acc[j];
-                }
-            }
-        }
-
-        // ---- S <- Diag(Gamma_n) S + KPt U ----
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int s = wave + 4 * i;
-            if (s < ST) {
-                const int ct = s / VT, vt = s % VT;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) st[i][j] *= sm.gn[16 * ct + 4 * lq + j];
-#pragma unroll
-                for (int ks = 0; ks < CK; ks += mm::KS) {
-                    const int kk = ks + lq * mm::KPL;
-                    st[i] = mm::mma(mm::load(sm.kpt, LDC, 16 * ct + l16, kk),
-                                    mm::load(sm.u, LDC, 16 * vt + l16, kk), st[i]);
-                }
-            }
-        }
-        __syncthreads();   // all reads of sm.s / record tiles done
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int s = wave + 4 * i;
-            if (s < ST) {
-                const int ct = s / VT, vt = s % VT;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    sm.s[(16 * vt + l16) * LDK + 16 * ct + 4 * lq + j] = to_ot<OT>(st[i][j]);
-            }
-        }
-        // the next iteration's first barrier orders these writes before use
-    }
-
-    if (sT) {
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int s = wave + 4 * i;
-            if (s < ST) {
-                const int ct = s / VT, vt = s % VT;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    sT[sbase + (size_t)(16 * ct + 4 * lq + j) * D + v0 + 16 * vt + l16] = st[i][j];
-            }
+            for (int j = 0; j < 4; ++j)
+                sT[sbase + (size_t)(16 * ct + 4 * lq + j) * D + v0 + 16 * vt + l16] = st[i][j];
         }
     }
+}
+
+// ---- K2a: register-staged variant (any dtype / slice width) ----
+template <int D, int C, int BV, typename OT, typename IT>
+struct InterSmem {
+    typedef Rec<D, C, OT> R;
+    alignas(16) char img[R::bytes];
+    alignas(16) IT vraw[C * BV];
+    ChainScratch<D, C, BV, OT> cs;
+};
+
+template <int D, int C, int BV, typename OT, typename IT>
+__global__ __launch_bounds__(256) void kda_inter(
+    int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
+    const int* __restrict__ chunk_off, float scale, const IT* __restrict__ v,
+    const float* __restrict__ s0, const char* __restrict__ records, float* __restrict__ o,
+    float* __restrict__ sT) {
+    constexpr int ST = (D / 16) * (BV / 16);
+    constexpr int SPW = (ST + 3) / 4;
+    typedef Rec<D, C, OT> R;
+    typedef u32x4 vec;
+    constexpr int NREC = (int)(R::bytes / 16);
+    constexpr int RPT = (NREC + 255) / 256;
+    constexpr int VPR = BV * (int)sizeof(IT) / 16;   // value vectors per row
+    constexpr int NVV = C * VPR;
+    constexpr int VPT = (NVV + 255) / 256;
+    extern __shared__ __align__(16) char smem_raw[];
+    InterSmem<D, C, BV, OT, IT>& sm = *reinterpret_cast<InterSmem<D, C, BV, OT, IT>*>(smem_raw);
+
+    const ChainPos cp = chain_pos<D, BV>(T, H, N_seq, nch_seq, G8, cu, chunk_off);
+    if (!cp.valid) return;
+    const int tid = threadIdx.x;
+    const size_t sbase = ((size_t)cp.n * H + cp.h) * (size_t)D * D;
+    float4v st[SPW];
+    chain_load_state<D, C, BV, OT>(st, sm.cs, s0, sbase, cp.v0);
+    const ChunkTiles<D, C, OT, IT> tiles(sm.img, sm.vraw);
+
+    vec rb[RPT], vb[VPT];
+    for (int c = 0; c < cp.nch; ++c) {
+        const int tok0 = cp.seq_tok0 + c * C;
+        const int len = min(C, cp.seq_len - c * C);
+        const vec* rec = reinterpret_cast<const vec*>(records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) rb[i] = rec[min(tid + 256 * i, NREC - 1)];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int idx = min(tid + 256 * i, NVV - 1);
+            const int r = min(idx / VPR, len - 1), cv = (idx % VPR) * (16 / (int)sizeof(IT));
+            vb[i] = *reinterpret_cast<const vec*>(v + ((size_t)(tok0 + r) * H + cp.h) * D + cp.v0 + cv);
+        }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            if (tid + 256 * i < NREC) reinterpret_cast<vec*>(sm.img)[tid + 256 * i] = rb[i];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+            if (tid + 256 * i < NVV) reinterpret_cast<vec*>(sm.vraw)[tid + 256 * i] = vb[i];
+        lds_barrier();
+        inter_chunk<D, C, BV, OT, IT>(tiles, sm.cs, st, tok0, len, H, cp.h, cp.v0, scale, o);
+    }
+    if (sT) chain_store_state<D, BV>(st, sT, sbase, cp.v0);
+}
+
+// ---- K2b: double-buffered direct global-to-LDS variant ----
+//
+// The chunk records (already in LDS-image form) and value rows are moved by
+// global_load_lds_dwordx4: every lane's 16 bytes land at consecutive LDS
+// addresses from a wave-uniform base held in M0, with no register
+// destination.  Chunk c+1's copies are in flight while chunk c computes.  The
+// copies are issued from inline assembly, so the compiler does not track
+// them; each wavefront waits for its own copies with an explicit
+// s_waitcnt vmcnt(N) (counter completion is in order, so "at most N newer
+// operations outstanding" implies this buffer is complete) and a barrier
+// then publishes them to the workgroup.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+template <int D, int C, int BV, typename OT, typename IT>
+struct InterDmaSmem {
+    typedef Rec<D, C, OT> R;
+    static constexpr int VBYTES = (C * BV * (int)sizeof(IT) + 1023) / 1024 * 1024;
+    alignas(1024) char img[2][R::bytes];
+    alignas(1024) char vraw[2][VBYTES];
+    ChainScratch<D, C, BV, OT> cs;
+};
+
+template <int D, int C, int BV, typename OT, typename IT>
+__global__ __launch_bounds__(256) void kda_inter_dma(
+    int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
+    const int* __restrict__ chunk_off, float scale, const IT* __restrict__ v,
+    const float* __restrict__ s0, const char* __restrict__ records, float* __restrict__ o,
+    float* __restrict__ sT) {
+    constexpr int ST = (D / 16) * (BV / 16);
+    constexpr int SPW = (ST + 3) / 4;
+    typedef Rec<D, C, OT> R;
+    typedef InterDmaSmem<D, C, BV, OT, IT> SM;
+    constexpr int NI = (int)(R::bytes / 1024);     // 1 KiB copies per record
+    constexpr int RB = BV * (int)sizeof(IT);       // bytes per value row
+    constexpr int LPR = RB / 16;                   // lanes per value row
+    constexpr int NVI = (C * LPR + 63) / 64;       // value-row copies
+    constexpr int NMIN = NI / 4;                   // copies issued by every wave
+    static_assert(RB % 16 == 0 && 64 % LPR == 0, "value rows must be whole 16-byte lanes");
+    extern __shared__ __align__(1024) char smem_raw[];
+    SM& sm = *reinterpret_cast<SM*>(smem_raw);
+
+    const ChainPos cp = chain_pos<D, BV>(T, H, N_seq, nch_seq, G8, cu, chunk_off);
+    if (!cp.valid) return;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const size_t sbase = ((size_t)cp.n * H + cp.h) * (size_t)D * D;
+    float4v st[SPW];
+    chain_load_state<D, C, BV, OT>(st, sm.cs, s0, sbase, cp.v0);
+    // Compiler-visible vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at
+    // their maxima): the initial-state loads are complete, so the compiler's
+    // own wait-count bookkeeping carries nothing pending into the loop and
+    // never inserts a wait that would drain the copies in flight.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
+    // issue every copy of chunk `c` into buffer `b` (wave-uniform arguments)
+    auto issue = [&](int c, int b) {
+        const char* rec = records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes;
+        const uint32_t ib = lds_addr(sm.img[b]);
+        for (int i = wave; i < NI; i += 4) dma16(rec + (size_t)i * 1024 + lane * 16, ib + i * 1024);
+        const int tok0 = cp.seq_tok0 + c * C;
+        const int len = min(C, cp.seq_len - c * C);
+        const uint32_t vb = lds_addr(sm.vraw[b]);
+        for (int i = wave; i < NVI; i += 4) {
+            const int r = min((i * 64 + lane) / LPR, len - 1);
+            const int part = (i * 64 + lane) % LPR;
+            dma16(reinterpret_cast<const char*>(v + ((size_t)(tok0 + r) * H + cp.h) * D + cp.v0) + part * 16,
+                  vb + i * 1024);
+        }
+    };
+
+    if (cp.nch > 0) issue(0, 0);
+    if (cp.nch > 1) issue(1, 1);
+    for (int c = 0; c < cp.nch; ++c) {
+        const int b = c & 1;
+        // chunk c's copies are complete once at most the next chunk's are in flight
+        if (c + 1 < cp.nch) asm volatile("s_waitcnt vmcnt(%0)" : : "n"(NMIN) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+        lds_barrier();
+        const ChunkTiles<D, C, OT, IT> tiles(sm.img[b], reinterpret_cast<const IT*>(sm.vraw[b]));
+        inter_chunk<D, C, BV, OT, IT>(tiles, sm.cs, st, cp.seq_tok0 + c * C,
+                                      min(C, cp.seq_len - c * C), H, cp.h, cp.v0, scale, o);
+        if (c + 2 < cp.nch) issue(c + 2, b);   // buffer b is free again
+    }
+    if (sT) chain_store_state<D, BV>(st, sT, sbase, cp.v0);
 }
 
 // ---------------------------------------------------------------------------
@@ -660,9 +1014,19 @@ __global__ __launch_bounds__(256) void kda_inter(
 constexpr size_t kLdsLimit = 160 * 1024;
 
 template <int D, int C, typename OT>
+constexpr size_t intra_smem_bytes() { return sizeof(IntraSmem<D, C, OT>); }
+template <int D, int C, int BV, typename OT, typename IT>
+constexpr size_t inter_smem_bytes() { return sizeof(InterSmem<D, C, BV, OT, IT>); }
+template <int D, int C, int BV, typename OT, typename IT>
+constexpr size_t inter_dma_smem_bytes() { return sizeof(InterDmaSmem<D, C, BV, OT, IT>); }
+
+template <typename OT>
+using InputOf = typename std::conditional<sizeof(OT) == 2, bf16_t, float>::type;
+
+template <int D, int C, typename OT>
 constexpr bool fits() {
     return intra_smem_bytes<D, C, OT>() <= kLdsLimit &&
-           inter_smem_bytes<D, C, 16, OT>() <= kLdsLimit;
+           inter_smem_bytes<D, C, 16, OT, InputOf<OT>>() <= kLdsLimit;
 }
 
 bool prefill_supported(int D, int C, bool bf16) {
@@ -698,27 +1062,39 @@ bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf
     return true;
 }
 
-// Columns per workgroup of K2: split dv until there are enough workgroups to
-// cover the chip (at least 512), but never below 16 columns.
-static int choose_bv(int D, int chains, bool bf16) {
-    if (!bf16) return 16;
-    int bv = D > 64 ? 64 : D;
-    while (bv > 16 && (long long)chains * (D / bv) < 512) bv /= 2;
-    return bv;
+// Chain-kernel choice.  Few chains (each must cover many CUs): 16-column
+// slices with double-buffered direct-to-LDS copies.  Many chains: wider
+// slices (less redundant record traffic), register-staged.  KDA_INTER_VARIANT
+// = "dma" / "reg16" / "reg32" / "reg64" overrides the choice (benchmarking).
+enum class InterVariant { Dma16, Reg16, Reg32, Reg64 };
+static InterVariant choose_inter(int D, long long chains, bool bf16, bool dma_ok) {
+    if (const char* e = getenv("KDA_INTER_VARIANT")) {
+        if (!strcmp(e, "dma") && dma_ok) return InterVariant::Dma16;
+        if (!strcmp(e, "reg16")) return InterVariant::Reg16;
+        if (!strcmp(e, "reg32") && bf16 && D >= 32) return InterVariant::Reg32;
+        if (!strcmp(e, "reg64") && bf16 && D >= 64) return InterVariant::Reg64;
+    }
+    if (!bf16) return InterVariant::Reg16;
+    if (dma_ok && chains * (D / 16) <= 2048) return InterVariant::Dma16;
+    if (D >= 64 && chains * (D / 64) >= 512) return InterVariant::Reg64;
+    if (D >= 32 && chains * (D / 32) >= 512) return InterVariant::Reg32;
+    return dma_ok ? InterVariant::Dma16 : InterVariant::Reg16;
 }
 
-template <int D, int C, int BV, typename OT, typename IT>
+template <int D, int C, int BV, typename OT, typename IT, bool DMA>
 static hipError_t launch_inter(const PrefillArgs& a, const PrefillPlan& plan, int nch_seq,
                                const int* chunk_off) {
-    const size_t smem = inter_smem_bytes<D, C, BV, OT>();
-    auto kern = kda_inter<D, C, BV, OT, IT>;
+    const size_t smem = DMA ? inter_dma_smem_bytes<D, C, BV, OT, IT>()
+                            : inter_smem_bytes<D, C, BV, OT, IT>();
+    auto kern = DMA ? kda_inter_dma<D, C, BV, OT, IT> : kda_inter<D, C, BV, OT, IT>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    const long long nblk = (long long)a.N * a.H * (D / BV);
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(256), smem, a.stream, a.T, a.H,
-                       a.N, nch_seq, a.cu_seqlens, chunk_off, a.scale, (const IT*)a.v, a.s0,
-                       (const char*)a.workspace + plan.off_records, a.o, a.sT);
+    const long long chains = (long long)a.N * a.H;
+    const long long G8 = (chains + 7) / 8 * (D / BV);   // blocks per XCD
+    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(256), smem, a.stream, a.T, a.H,
+                       a.N, nch_seq, (int)G8, a.cu_seqlens, chunk_off, a.scale, (const IT*)a.v,
+                       a.s0, (const char*)a.workspace + plan.off_records, a.o, a.sT);
     return hipGetLastError();
 }
 
@@ -754,12 +1130,22 @@ static hipError_t launch_dc(const PrefillArgs& a, const PrefillPlan& plan) {
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        const int bv = choose_bv(D, a.N * a.H, std::is_same<OT, _Float16>::value);
-        if constexpr (std::is_same<OT, _Float16>::value) {
-            if (bv == 64 && D >= 64) return launch_inter<D, C, (D >= 64 ? 64 : 16), OT, IT>(a, plan, nch_seq, chunk_off);
-            if (bv == 32 && D >= 32) return launch_inter<D, C, 32, OT, IT>(a, plan, nch_seq, chunk_off);
+        constexpr bool kBf = sizeof(OT) == 2;
+        constexpr bool kDmaOk = kBf && inter_dma_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
+        switch (choose_inter(D, (long long)a.N * a.H, kBf, kDmaOk)) {
+            case InterVariant::Dma16:
+                if constexpr (kDmaOk) return launch_inter<D, C, 16, OT, IT, true>(a, plan, nch_seq, chunk_off);
+                break;
+            case InterVariant::Reg64:
+                if constexpr (kBf && D >= 64) return launch_inter<D, C, 64, OT, IT, false>(a, plan, nch_seq, chunk_off);
+                break;
+            case InterVariant::Reg32:
+                if constexpr (kBf && D >= 32) return launch_inter<D, C, 32, OT, IT, false>(a, plan, nch_seq, chunk_off);
+                break;
+            default:
+                break;
         }
-        return launch_inter<D, C, 16, OT, IT>(a, plan, nch_seq, chunk_off);
+        return launch_inter<D, C, 16, OT, IT, false>(a, plan, nch_seq, chunk_off);
     }
 }
 
