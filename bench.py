@@ -38,7 +38,66 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-target", choices=["prefill", "decode", "copy"],
+                    help="run only this workload a few times (target for rocprofv3) and exit")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "linear_attention_sequence_chunkwise_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(leg):
+    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when the kernel sources changed since it was taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[leg]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash(rec["sources"]):
+        return None
+    return rec["bytes_per_call"]
+
+
+def profile_target(kind):
+    """Minimal workload for counter collection: 3 calls, nothing else timed."""
+    import kda_inputs
+    import linear_attention_sequence_chunkwise_amd as kda
+    kda.load_library()
+    if kind == "copy":
+        x = torch.empty(256 << 20, dtype=torch.float32, device="cuda")   # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+    elif kind == "prefill":
+        d = kda_inputs.config_inputs(2, "cuda")
+        B, T, H, D = d["q"].shape
+        ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(B, T, H, D, D, 64), dtype=torch.uint8,
+                         device="cuda")
+        o = torch.empty(B, T, H, D, device="cuda")
+        S = torch.empty(B, H, D, D, device="cuda")
+        for _ in range(3):
+            kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64, o=o,
+                              final_state=S, workspace=ws)
+    else:
+        c = kda_inputs.CONFIGS[4]
+        N, H, D = c["N"], c["H"], c["dk"]
+        gen = torch.Generator(device="cuda").manual_seed(3)
+        cache = 0.1 * torch.randn(N, H, D, D, device="cuda", generator=gen)
+        x = kda_inputs.decode_inputs(kda_inputs.CFG_SEED[4], 0, N, H, D, D, torch.bfloat16, "cuda")
+        for _ in range(3):
+            kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], cache)
+    torch.cuda.synchronize()
+    print("profile target %s done" % kind)
 
 
 class StreamTimer:
@@ -144,7 +203,7 @@ def cpu_baseline_prefill(d, target_s=8.0):
                 % (Ts, dt))
 
 
-def cpu_baseline_decode(kda_inputs, n_steps=4):
+def cpu_baseline_decode(kda_inputs, target_s=4.0):
     import numpy as np
     import oracle
     c = kda_inputs.CONFIGS[4]
@@ -152,11 +211,14 @@ def cpu_baseline_decode(kda_inputs, n_steps=4):
     rng = np.random.default_rng(0)
     state = rng.standard_normal((N, H, D, D)) * 0.1
     xs = [kda_inputs.decode_inputs(kda_inputs.CFG_SEED[4], s, N, H, D, D, torch.bfloat16, "cpu")
-          for s in range(n_steps)]
+          for s in range(8)]
     xs = [{k: v.float().numpy() for k, v in x.items()} for x in xs]
     t0 = time.perf_counter()
-    for x in xs:
+    n_steps = 0
+    while time.perf_counter() - t0 < target_s:
+        x = xs[n_steps % len(xs)]
         oracle.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], D ** -0.5, state)
+        n_steps += 1
     dt = time.perf_counter() - t0
     return dict(value=N * n_steps / dt, unit="tokens/s", cores=oracle.num_threads(),
                 kind="oracle", sample="decode N256 H32 d128: %d steps, %.2f s" % (n_steps, dt))
@@ -170,6 +232,9 @@ def main():
               "MI355X (every (sequence, head) chain is independent, so more GPUs would shard "
               "sequences/heads with no exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.profile_target:
+        profile_target(args.profile_target)
+        return
     import kda_inputs
     import linear_attention_sequence_chunkwise_amd as kda
     kda.load_library()
@@ -183,7 +248,8 @@ def main():
     pf_flops = prefill_flops_per_token_head() * th
     tok_s = pf["tokens"] / (pf["ms"] / 1e3)
     roof = dict(bound="hbm", achieved=pf_bytes / (pf["ms"] / 1e3) / 1e9, peak=HBM_PEAK_GBS,
-                unit="GB/s", traffic=None, kernel="kda_chunk_fwd (all kernels of one call)",
+                unit="GB/s", traffic=measured_traffic("prefill"),
+                kernel="kda_chunk_fwd call (kda_intra + kda_inter_dma)",
                 algorithmic_bytes=pf_bytes,
                 mfma_tflops=pf_flops / (pf["ms"] / 1e3) / 1e12)
     roof["frac"] = roof["achieved"] / roof["peak"]
@@ -199,7 +265,8 @@ def main():
                    config=dict(workload="decode N256 H32 dk=dv=128 fp32 cache, 4096-token "
                                "prefill init, 512 steps, bf16 q/k/v"),
                    roofline=dict(bound="hbm", achieved=db / (dc["ms"] / 1e3) / 1e9,
-                                 peak=HBM_PEAK_GBS, unit="GB/s", traffic=None,
+                                 peak=HBM_PEAK_GBS, unit="GB/s",
+                                 traffic=measured_traffic("decode"),
                                  kernel="decode_step_kernel<128, bf16>",
                                  algorithmic_bytes=db))
         dec["roofline"]["frac"] = dec["roofline"]["achieved"] / HBM_PEAK_GBS
@@ -221,7 +288,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 inputs, fp16 matrix-core operands, fp32 accumulate/state",
+        "dtype": "f16/f32",
+        "dtype_detail": "bf16 q/k/v in; fp16 matrix-core operands, fp32 accumulation, state, "
+                        "gates and output",
         "data": "synthetic (seeded), resident in HBM",
         "config": {"workload": "prefill B=1 H=32 T=32768 dk=dv=128 chunk=64 bf16 q/k/v, fp32 "
                                "gates, zero initial state", "global_batch": 1, "seq_len": 32768,

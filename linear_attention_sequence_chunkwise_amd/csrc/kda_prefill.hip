@@ -142,37 +142,50 @@ constexpr int chunk_k() { return C > MM<OT>::KS ? C : MM<OT>::KS; }
 
 // ---------------------------------------------------------------------------
 // Workspace record of one (chunk, head).  It is stored as the exact LDS image
-// the inter-chunk kernel works on (padded rows, zero k-padding), so that
-// kernel moves it with linear 16-byte copies (or direct global-to-LDS loads).
-// Offsets in OT elements unless noted:
-//   KG  [C][LDK]   k_r * exp(G_r)
-//   QG  [C][LDK]   q_r * exp(G_r)
-//   KPt [D][LDC]   k_i * exp(G_n - G_i), transposed
-//   Tb  [C][LDC]   T diag(beta), T = (I + A)^-1
-//   M   [C][LDC]   lower-triangular q.k^T Gram (zero above the diagonal)
+// the inter-chunk kernel works on, so that kernel moves it with linear
+// 16-byte copies (direct global-to-LDS loads).  Tiles are row-major without
+// padding; instead the 16-byte column groups of row r are XOR-permuted with
+// r (swz), so the 16 rows a matrix-core fragment reads at once fall in
+// different LDS banks.  Offsets in OT elements unless noted:
+//   KG  [C][D]     k_r * exp(G_r)
+//   QG  [C][D]     q_r * exp(G_r)
+//   KPt [D][CK]    k_i * exp(G_n - G_i), transposed
+//   Tb  [C][CK]    T diag(beta), T = (I + A)^-1
+//   M   [C][CK]    lower-triangular q.k^T Gram (zero above the diagonal)
 //   Gn  [D]        exp(G_n), fp32, at byte gn_byte
-// with LDK = D + pad, LDC = max(C, one instruction's k) + pad; the record is
+// CK = max(C, one instruction's k); columns C..CK-1 are zero.  The record is
 // rounded up to whole KiB.
 // ---------------------------------------------------------------------------
 template <int D, int C, typename OT>
 struct Rec {
-    static constexpr int LDK = padded<OT>(D);
     static constexpr int CK = chunk_k<C, OT>();
-    static constexpr int LDC = padded<OT>(CK);
     static constexpr size_t KG = 0;
-    static constexpr size_t QG = (size_t)C * LDK;
-    static constexpr size_t KPt = 2 * (size_t)C * LDK;
-    static constexpr size_t Tb = KPt + (size_t)D * LDC;
-    static constexpr size_t M = Tb + (size_t)C * LDC;
-    static constexpr size_t gn_byte = (M + (size_t)C * LDC) * sizeof(OT);
+    static constexpr size_t QG = (size_t)C * D;
+    static constexpr size_t KPt = 2 * (size_t)C * D;
+    static constexpr size_t Tb = KPt + (size_t)D * CK;
+    static constexpr size_t M = Tb + (size_t)C * CK;
+    static constexpr size_t gn_byte = (M + (size_t)C * CK) * sizeof(OT);
     static constexpr size_t bytes = (gn_byte + 4 * (size_t)D + 1023) / 1024 * 1024;
 };
+
+// Element offset of (row, k) in a swizzled [rows][LD] tile of OT.
+template <typename OT, int LD>
+__device__ __forceinline__ int swz(int row, int k) {
+    constexpr int EPV = 16 / (int)sizeof(OT);
+    constexpr int NG = LD / EPV;
+    static_assert((NG & (NG - 1)) == 0, "groups per row must be a power of two");
+    return row * LD + ((((k / EPV) ^ row) & (NG - 1)) * EPV) + (k % EPV);
+}
+template <typename OT, int LD>
+__device__ __forceinline__ typename MM<OT>::frag load_swz(const OT* tile, int row, int k) {
+    return MM<OT>::load(tile + swz<OT, LD>(row, k) - k, 0, 0, k);
+}
 
 static size_t rec_bytes(int D, int C, bool bf16) {
     const size_t es = bf16 ? 2 : 4;
     const size_t ks = bf16 ? 32 : 4;
-    const size_t ldk = D + 16 / es, ck = (size_t)C > ks ? C : ks, ldc = ck + 16 / es;
-    const size_t gn = (2 * (size_t)C * ldk + (size_t)D * ldc + 2 * (size_t)C * ldc) * es;
+    const size_t ck = (size_t)C > ks ? C : ks;
+    const size_t gn = (2 * (size_t)C * D + (size_t)D * ck + 2 * (size_t)C * ck) * es;
     return (gn + 4 * (size_t)D + 1023) / 1024 * 1024;
 }
 
@@ -444,8 +457,8 @@ __global__ __launch_bounds__(256) void kda_intra(
             kk[e] = (float)sm.u.g.kl[r * LDK + c0 + e] * eg[e];
             qq[e] = (float)sm.u.g.ql[r * LDK + c0 + e] * eg[e];
         }
-        *reinterpret_cast<vec*>(rec + R::KG + (size_t)r * R::LDK + c0) = pack16(kk);
-        *reinterpret_cast<vec*>(rec + R::QG + (size_t)r * R::LDK + c0) = pack16(qq);
+        *reinterpret_cast<vec*>(rec + R::KG + swz<OT, D>(r, c0)) = pack16(kk);
+        *reinterpret_cast<vec*>(rec + R::QG + swz<OT, D>(r, c0)) = pack16(qq);
     }
     // KPt[c][i] = (k_i b_i) exp(G_n - Ge_J), transposed: 16 bytes of one channel row
     for (int idx = tid; idx < D * C / EPV; idx += 256) {
@@ -454,7 +467,7 @@ __global__ __launch_bounds__(256) void kda_intra(
         float kk[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) kk[e] = (float)sm.u.g.kr[(i0 + e) * LDK + c] * f;
-        *reinterpret_cast<vec*>(rec + R::KPt + (size_t)c * R::LDC + i0) = pack16(kk);
+        *reinterpret_cast<vec*>(rec + R::KPt + swz<OT, R::CK>(c, i0)) = pack16(kk);
     }
 
     // ---- phase 3b: Gram blocks on the matrix cores ----
@@ -551,7 +564,7 @@ __global__ __launch_bounds__(256) void kda_intra(
     //      T_IJ = -T_II * sum_{m=J}^{I-1} A_Im T_mJ ----
     for (int idx = tid; idx < C * C / EPV; idx += 256) {
         const int r = idx / (C / EPV), c0 = (idx % (C / EPV)) * EPV;
-        *reinterpret_cast<vec*>(rec + R::M + (size_t)r * R::LDC + c0) =
+        *reinterpret_cast<vec*>(rec + R::M + swz<OT, R::CK>(r, c0)) =
             *reinterpret_cast<const vec*>(&sm.u.s.M[r * LDA + c0]);
     }
     for (int d = 1; d < NB; ++d) {
@@ -580,16 +593,16 @@ __global__ __launch_bounds__(256) void kda_intra(
         float tv[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) tv[e] = sm.u.s.T[r * LDT + c0 + e] * sm.beta[c0 + e];
-        *reinterpret_cast<vec*>(rec + R::Tb + (size_t)r * R::LDC + c0) = pack16(tv);
+        *reinterpret_cast<vec*>(rec + R::Tb + swz<OT, R::CK>(r, c0)) = pack16(tv);
     }
     if constexpr (R::CK > C) {   // zero k-padding of the chunk-indexed tiles
         constexpr int PV = (R::CK - C) / EPV;
         for (int idx = tid; idx < (D + 2 * C) * PV; idx += 256) {
             const int row = idx / PV, c0 = C + (idx % PV) * EPV;
-            const size_t off = row < D ? R::KPt + (size_t)row * R::LDC
-                             : row < D + C ? R::Tb + (size_t)(row - D) * R::LDC
-                                           : R::M + (size_t)(row - D - C) * R::LDC;
-            *reinterpret_cast<vec*>(rec + off + c0) = vec{0u, 0u, 0u, 0u};
+            const size_t off = row < D ? R::KPt + swz<OT, R::CK>(row, c0)
+                             : row < D + C ? R::Tb + swz<OT, R::CK>(row - D, c0)
+                                           : R::M + swz<OT, R::CK>(row - D - C, c0);
+            *reinterpret_cast<vec*>(rec + off) = vec{0u, 0u, 0u, 0u};
         }
     }
 }
@@ -640,10 +653,10 @@ struct ChainScratch {
 // state published to LDS; a barrier separates the last reads of the chunk
 // tiles and of the old state from that write, so on return the chunk's tiles
 // may be overwritten.
-template <int D, int C, int BV, typename OT, typename IT>
+template <int D, int C, int BV, typename OT, typename IT, int NWC = 4>
 __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
                                             ChainScratch<D, C, BV, OT>& cs,
-                                            float4v (&st)[((D / 16) * (BV / 16) + 3) / 4],
+                                            float4v (&st)[((D / 16) * (BV / 16) + NWC - 1) / NWC],
                                             int tok0, int len, int H, int h, int v0,
                                             float scale, float* __restrict__ o) {
     constexpr int LDK = padded<OT>(D);
@@ -652,9 +665,9 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
     constexpr int RT = C / 16;
     constexpr int VT = BV / 16;
     constexpr int ST = (D / 16) * VT;
-    constexpr int SPW = (ST + 3) / 4;
+    constexpr int SPW = (ST + NWC - 1) / NWC;
     constexpr int OTILES = RT * VT;
-    constexpr int OPW = (OTILES + 3) / 4;
+    constexpr int OPW = (OTILES + NWC - 1) / NWC;
     typedef MM<OT> mm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -666,7 +679,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
     float4v qs[OPW];
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
-        const int tt = wave + 4 * i;
+        const int tt = wave + NWC * i;
         qs[i] = float4v{0.f, 0.f, 0.f, 0.f};
         if (tt < OTILES) {
             const int rt = tt / VT, vt = tt % VT;
@@ -675,8 +688,8 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
             for (int ks = 0; ks < D; ks += mm::KS) {
                 const int kk = ks + lq * mm::KPL;
                 const typename mm::frag bs = mm::load(cs.s, LDK, 16 * vt + l16, kk);
-                xk = mm::mma(mm::load(t.kg, LDK, 16 * rt + l16, kk), bs, xk);
-                qs[i] = mm::mma(mm::load(t.qg, LDK, 16 * rt + l16, kk), bs, qs[i]);
+                xk = mm::mma(load_swz<OT, D>(t.kg, 16 * rt + l16, kk), bs, xk);
+                qs[i] = mm::mma(load_swz<OT, D>(t.qg, 16 * rt + l16, kk), bs, qs[i]);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -691,14 +704,14 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
     // ---- U = Tb X (Tb lower triangular: k only up to the diagonal block) ----
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
-        const int tt = wave + 4 * i;
+        const int tt = wave + NWC * i;
         if (tt < OTILES) {
             const int rt = tt / VT, vt = tt % VT;
             float4v uacc = {0.f, 0.f, 0.f, 0.f};
             const int kend = 16 * (rt + 1);
             for (int ks = 0; ks < kend; ks += mm::KS) {
                 const int kk = ks + lq * mm::KPL;
-                uacc = mm::mma(mm::load(t.tb, LDC, 16 * rt + l16, kk),
+                uacc = mm::mma(load_swz<OT, CK>(t.tb, 16 * rt + l16, kk),
                                mm::load(cs.x, LDC, 16 * vt + l16, kk), uacc);
             }
 #pragma unroll
@@ -711,14 +724,14 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
     // ---- O = scale (QS + M U) ----
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
-        const int tt = wave + 4 * i;
+        const int tt = wave + NWC * i;
         if (tt < OTILES) {
             const int rt = tt / VT, vt = tt % VT;
             float4v acc = qs[i];
             const int kend = 16 * (rt + 1);
             for (int ks = 0; ks < kend; ks += mm::KS) {
                 const int kk = ks + lq * mm::KPL;
-                acc = mm::mma(mm::load(t.m, LDC, 16 * rt + l16, kk),
+                acc = mm::mma(load_swz<OT, CK>(t.m, 16 * rt + l16, kk),
                               mm::load(cs.u, LDC, 16 * vt + l16, kk), acc);
             }
 #pragma unroll
@@ -733,7 +746,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
     // ---- S <- Diag(Gamma_n) S + KPt U ----
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-        const int s = wave + 4 * i;
+        const int s = wave + NWC * i;
         if (s < ST) {
             const int ct = s / VT, vt = s % VT;
 #pragma unroll
@@ -741,7 +754,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
 #pragma unroll
             for (int ks = 0; ks < CK; ks += mm::KS) {
                 const int kk = ks + lq * mm::KPL;
-                st[i] = mm::mma(mm::load(t.kpt, LDC, 16 * ct + l16, kk),
+                st[i] = mm::mma(load_swz<OT, CK>(t.kpt, 16 * ct + l16, kk),
                                 mm::load(cs.u, LDC, 16 * vt + l16, kk), st[i]);
             }
         }
@@ -749,7 +762,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
     lds_barrier();   // all reads of the chunk tiles and of the old state are done
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-        const int s = wave + 4 * i;
+        const int s = wave + NWC * i;
         if (s < ST) {
             const int ct = s / VT, vt = s % VT;
 #pragma unroll
@@ -796,25 +809,25 @@ __device__ __forceinline__ ChainPos chain_pos(int T, int H, int N_seq, int nch_s
 
 // State tiles owned by this wave (fp32, MFMA output layout) from s0 or zero,
 // and the fp16/fp32 state operand in LDS.
-template <int D, int C, int BV, typename OT>
-__device__ __forceinline__ void chain_load_state(float4v (&st)[((D / 16) * (BV / 16) + 3) / 4],
+template <int D, int C, int BV, typename OT, int NWC = 4>
+__device__ __forceinline__ void chain_load_state(float4v (&st)[((D / 16) * (BV / 16) + NWC - 1) / NWC],
                                                  ChainScratch<D, C, BV, OT>& cs,
                                                  const float* __restrict__ s0, size_t sbase,
                                                  int v0) {
-    constexpr int VT = BV / 16, ST = (D / 16) * VT, SPW = (ST + 3) / 4;
+    constexpr int VT = BV / 16, ST = (D / 16) * VT, SPW = (ST + NWC - 1) / NWC;
     constexpr int LDK = padded<OT>(D);
     constexpr int CK = chunk_k<C, OT>();
     constexpr int LDC = padded<OT>(CK);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lq = lane >> 4;
     if constexpr (CK > C) {   // k-padding of X and U stays zero for the whole chain
-        for (int idx = threadIdx.x; idx < 2 * BV * (CK - C); idx += 256) {
+        for (int idx = threadIdx.x; idx < 2 * BV * (CK - C); idx += 64 * NWC) {
             const int row = idx / (CK - C), col = C + idx % (CK - C);
             (row < BV ? cs.x : cs.u)[(row % BV) * LDC + col] = to_ot<OT>(0.f);
         }
     }
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-        const int s = wave + 4 * i;
+        const int s = wave + NWC * i;
         st[i] = float4v{0.f, 0.f, 0.f, 0.f};
         if (s < ST && s0) {
             const int ct = s / VT, vt = s % VT;
@@ -825,7 +838,7 @@ __device__ __forceinline__ void chain_load_state(float4v (&st)[((D / 16) * (BV /
     }
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-        const int s = wave + 4 * i;
+        const int s = wave + NWC * i;
         if (s < ST) {
             const int ct = s / VT, vt = s % VT;
 #pragma unroll
@@ -835,15 +848,15 @@ __device__ __forceinline__ void chain_load_state(float4v (&st)[((D / 16) * (BV /
     }
 }
 
-template <int D, int BV>
+template <int D, int BV, int NWC = 4>
 __device__ __forceinline__ void chain_store_state(
-    const float4v (&st)[((D / 16) * (BV / 16) + 3) / 4], float* __restrict__ sT, size_t sbase,
-    int v0) {
-    constexpr int VT = BV / 16, ST = (D / 16) * VT, SPW = (ST + 3) / 4;
+    const float4v (&st)[((D / 16) * (BV / 16) + NWC - 1) / NWC], float* __restrict__ sT,
+    size_t sbase, int v0) {
+    constexpr int VT = BV / 16, ST = (D / 16) * VT, SPW = (ST + NWC - 1) / NWC;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-        const int s = wave + 4 * i;
+        const int s = wave + NWC * i;
         if (s < ST) {
             const int ct = s / VT, vt = s % VT;
 #pragma unroll
@@ -918,12 +931,16 @@ __global__ __launch_bounds__(256) void kda_inter(
 // The chunk records (already in LDS-image form) and value rows are moved by
 // global_load_lds_dwordx4: every lane's 16 bytes land at consecutive LDS
 // addresses from a wave-uniform base held in M0, with no register
-// destination.  Chunk c+1's copies are in flight while chunk c computes.  The
-// copies are issued from inline assembly, so the compiler does not track
-// them; each wavefront waits for its own copies with an explicit
-// s_waitcnt vmcnt(N) (counter completion is in order, so "at most N newer
-// operations outstanding" implies this buffer is complete) and a barrier
-// then publishes them to the workgroup.
+// destination.  Four producer wavefronts issue all of these copies (one
+// wavefront alone cannot keep enough of them in flight); the four compute
+// wavefronts never touch the memory pipeline except for their output stores,
+// so a copy that waits for L2 never stalls the matrix work.
+// Chunk c+2's copies go into the buffer chunk c has just released and have
+// all of chunk c+1 to land.  The copies are issued from inline assembly (the
+// compiler does not track them); the producer waits for its own copies with
+// an explicit s_waitcnt vmcnt(N) -- the counter completes in order, so "at
+// most N newer operations outstanding" means the older buffer is complete --
+// and the next workgroup barrier publishes them.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -944,21 +961,26 @@ struct InterDmaSmem {
 };
 
 template <int D, int C, int BV, typename OT, typename IT>
-__global__ __launch_bounds__(256) void kda_inter_dma(
+__global__ __launch_bounds__(64 * (BV / 4 + 4)) void kda_inter_dma(
     int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
     const int* __restrict__ chunk_off, float scale, const IT* __restrict__ v,
     const float* __restrict__ s0, const char* __restrict__ records, float* __restrict__ o,
     float* __restrict__ sT) {
+    constexpr int NWC = BV / 4;                    // compute wavefronts (one tile each per phase)
+    static_assert(64 * (NWC + 4) <= 1024, "workgroup too large");
     constexpr int ST = (D / 16) * (BV / 16);
-    constexpr int SPW = (ST + 3) / 4;
+    constexpr int SPW = (ST + NWC - 1) / NWC;
     typedef Rec<D, C, OT> R;
     typedef InterDmaSmem<D, C, BV, OT, IT> SM;
     constexpr int NI = (int)(R::bytes / 1024);     // 1 KiB copies per record
     constexpr int RB = BV * (int)sizeof(IT);       // bytes per value row
     constexpr int LPR = RB / 16;                   // lanes per value row
     constexpr int NVI = (C * LPR + 63) / 64;       // value-row copies
-    constexpr int NMIN = NI / 4;                   // copies issued by every wave
+    constexpr int NB = (NI + NVI) / 4;             // copies per chunk issued by every producer
     static_assert(RB % 16 == 0 && 64 % LPR == 0, "value rows must be whole 16-byte lanes");
+    // vmcnt holds at most 63: waiting for "<= 63 outstanding" when a batch has
+    // more copies also completes the newest batch's first ones (stricter, safe)
+    constexpr int NWAIT = NB < 63 ? NB : 63;
     extern __shared__ __align__(1024) char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
@@ -966,46 +988,61 @@ __global__ __launch_bounds__(256) void kda_inter_dma(
     if (!cp.valid) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const bool producer = tid >= 64 * NWC;
     const size_t sbase = ((size_t)cp.n * H + cp.h) * (size_t)D * D;
+
+    if (producer) {
+        // all copies of chunk `c` into buffer `b`; the dv-slices of a head
+        // start at different offsets so their L2 requests spread out
+        const int pw = (tid - 64 * NWC) >> 6;        // producer wavefront 0..3
+        auto issue = [&](int c, int b) {
+            const char* rec = records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes;
+            const uint32_t ib = lds_addr(sm.img[b]);
+            const int rot = (cp.v0 / BV) * NI / (D / BV);
+            for (int i = pw; i < NI; i += 4) {
+                const int ii = i + rot < NI ? i + rot : i + rot - NI;
+                dma16(rec + (size_t)ii * 1024 + lane * 16, ib + ii * 1024);
+            }
+            const int tok0 = cp.seq_tok0 + c * C;
+            const int len = min(C, cp.seq_len - c * C);
+            const uint32_t vb = lds_addr(sm.vraw[b]);
+            for (int i = pw; i < NVI; i += 4) {
+                const int r = min((i * 64 + lane) / LPR, len - 1);
+                const int part = (i * 64 + lane) % LPR;
+                dma16(reinterpret_cast<const char*>(v + ((size_t)(tok0 + r) * H + cp.h) * D +
+                                                    cp.v0) + part * 16,
+                      vb + i * 1024);
+            }
+        };
+        if (cp.nch > 0) issue(0, 0);
+        if (cp.nch > 1) issue(1, 1);
+        for (int c = 0; c < cp.nch; ++c) {
+            // chunk c complete (at most chunk c+1's copies still in flight)
+            if (c + 1 < cp.nch) asm volatile("s_waitcnt vmcnt(%0)" : : "n"(NWAIT) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+            lds_barrier();                           // chunk c published
+            lds_barrier();                           // compute: X done
+            lds_barrier();                           // compute: U done
+            lds_barrier();                           // compute: chunk c's tiles released
+            if (c + 2 < cp.nch) issue(c + 2, c & 1);
+        }
+        return;
+    }
+
     float4v st[SPW];
-    chain_load_state<D, C, BV, OT>(st, sm.cs, s0, sbase, cp.v0);
+    chain_load_state<D, C, BV, OT, NWC>(st, sm.cs, s0, sbase, cp.v0);
     // Compiler-visible vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at
     // their maxima): the initial-state loads are complete, so the compiler's
-    // own wait-count bookkeeping carries nothing pending into the loop and
-    // never inserts a wait that would drain the copies in flight.
+    // wait-count bookkeeping carries nothing pending into the loop.
     __builtin_amdgcn_s_waitcnt(0x0F70);
-
-    // issue every copy of chunk `c` into buffer `b` (wave-uniform arguments)
-    auto issue = [&](int c, int b) {
-        const char* rec = records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes;
-        const uint32_t ib = lds_addr(sm.img[b]);
-        for (int i = wave; i < NI; i += 4) dma16(rec + (size_t)i * 1024 + lane * 16, ib + i * 1024);
-        const int tok0 = cp.seq_tok0 + c * C;
-        const int len = min(C, cp.seq_len - c * C);
-        const uint32_t vb = lds_addr(sm.vraw[b]);
-        for (int i = wave; i < NVI; i += 4) {
-            const int r = min((i * 64 + lane) / LPR, len - 1);
-            const int part = (i * 64 + lane) % LPR;
-            dma16(reinterpret_cast<const char*>(v + ((size_t)(tok0 + r) * H + cp.h) * D + cp.v0) + part * 16,
-                  vb + i * 1024);
-        }
-    };
-
-    if (cp.nch > 0) issue(0, 0);
-    if (cp.nch > 1) issue(1, 1);
     for (int c = 0; c < cp.nch; ++c) {
         const int b = c & 1;
-        // chunk c's copies are complete once at most the next chunk's are in flight
-        if (c + 1 < cp.nch) asm volatile("s_waitcnt vmcnt(%0)" : : "n"(NMIN) : "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-        lds_barrier();
+        lds_barrier();                               // chunk c published
         const ChunkTiles<D, C, OT, IT> tiles(sm.img[b], reinterpret_cast<const IT*>(sm.vraw[b]));
-        inter_chunk<D, C, BV, OT, IT>(tiles, sm.cs, st, cp.seq_tok0 + c * C,
+        inter_chunk<D, C, BV, OT, IT, NWC>(tiles, sm.cs, st, cp.seq_tok0 + c * C,
                                       min(C, cp.seq_len - c * C), H, cp.h, cp.v0, scale, o);
-        if (c + 2 < cp.nch) issue(c + 2, b);   // buffer b is free again
     }
-    if (sT) chain_store_state<D, BV>(st, sT, sbase, cp.v0);
+    if (sT) chain_store_state<D, BV, NWC>(st, sT, sbase, cp.v0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1062,37 +1099,48 @@ bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf
     return true;
 }
 
-// Chain-kernel choice.  Few chains (each must cover many CUs): 16-column
-// slices with double-buffered direct-to-LDS copies.  Many chains: wider
-// slices (less redundant record traffic), register-staged.  KDA_INTER_VARIANT
-// = "dma" / "reg16" / "reg32" / "reg64" overrides the choice (benchmarking).
-enum class InterVariant { Dma16, Reg16, Reg32, Reg64 };
-static InterVariant choose_inter(int D, long long chains, bool bf16, bool dma_ok) {
+// Chain-kernel choice.  Every dv-slice of a chain re-reads the whole chunk
+// record, so slices are made as wide as still covers the chip: few chains
+// (each must span many CUs) use 32- or 16-column slices with double-buffered
+// direct-to-LDS copies; many chains use 64-column slices, register-staged.
+// KDA_INTER_VARIANT = dma16 / dma32 / reg16 / reg32 / reg64 overrides the
+// choice (benchmarking).
+enum class InterVariant { Dma16, Dma32, Reg16, Reg32, Reg64 };
+static InterVariant choose_inter(int D, long long chains, bool bf16, bool dma16_ok,
+                                 bool dma32_ok) {
     if (const char* e = getenv("KDA_INTER_VARIANT")) {
-        if (!strcmp(e, "dma") && dma_ok) return InterVariant::Dma16;
+        if (!strcmp(e, "dma16") && dma16_ok) return InterVariant::Dma16;
+        if (!strcmp(e, "dma32") && dma32_ok) return InterVariant::Dma32;
         if (!strcmp(e, "reg16")) return InterVariant::Reg16;
         if (!strcmp(e, "reg32") && bf16 && D >= 32) return InterVariant::Reg32;
         if (!strcmp(e, "reg64") && bf16 && D >= 64) return InterVariant::Reg64;
     }
     if (!bf16) return InterVariant::Reg16;
-    if (dma_ok && chains * (D / 16) <= 2048) return InterVariant::Dma16;
     if (D >= 64 && chains * (D / 64) >= 512) return InterVariant::Reg64;
-    if (D >= 32 && chains * (D / 32) >= 512) return InterVariant::Reg32;
-    return dma_ok ? InterVariant::Dma16 : InterVariant::Reg16;
+    if (dma32_ok && chains * (D / 32) >= 256) return InterVariant::Dma32;
+    if (dma16_ok) return InterVariant::Dma16;
+    return InterVariant::Reg16;
 }
 
 template <int D, int C, int BV, typename OT, typename IT, bool DMA>
 static hipError_t launch_inter(const PrefillArgs& a, const PrefillPlan& plan, int nch_seq,
                                const int* chunk_off) {
-    const size_t smem = DMA ? inter_dma_smem_bytes<D, C, BV, OT, IT>()
-                            : inter_smem_bytes<D, C, BV, OT, IT>();
-    auto kern = DMA ? kda_inter_dma<D, C, BV, OT, IT> : kda_inter<D, C, BV, OT, IT>;
+    size_t smem;
+    void (*kern)(int, int, int, int, int, const int*, const int*, float, const IT*, const float*,
+                 const char*, float*, float*);
+    if constexpr (DMA) {
+        smem = inter_dma_smem_bytes<D, C, BV, OT, IT>();
+        kern = kda_inter_dma<D, C, BV, OT, IT>;
+    } else {
+        smem = inter_smem_bytes<D, C, BV, OT, IT>();
+        kern = kda_inter<D, C, BV, OT, IT>;
+    }
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     const long long chains = (long long)a.N * a.H;
     const long long G8 = (chains + 7) / 8 * (D / BV);   // blocks per XCD
-    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(256), smem, a.stream, a.T, a.H,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(DMA ? 64 * (BV / 4 + 4) : 256), smem, a.stream, a.T, a.H,
                        a.N, nch_seq, (int)G8, a.cu_seqlens, chunk_off, a.scale, (const IT*)a.v,
                        a.s0, (const char*)a.workspace + plan.off_records, a.o, a.sT);
     return hipGetLastError();
@@ -1131,10 +1179,14 @@ static hipError_t launch_dc(const PrefillArgs& a, const PrefillPlan& plan) {
             if (e != hipSuccess) return e;
         }
         constexpr bool kBf = sizeof(OT) == 2;
-        constexpr bool kDmaOk = kBf && inter_dma_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
-        switch (choose_inter(D, (long long)a.N * a.H, kBf, kDmaOk)) {
+        constexpr bool kDma16 = kBf && inter_dma_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
+        constexpr bool kDma32 = kBf && D >= 32 && inter_dma_smem_bytes<D, C, 32, OT, IT>() <= kLdsLimit;
+        switch (choose_inter(D, (long long)a.N * a.H, kBf, kDma16, kDma32)) {
             case InterVariant::Dma16:
-                if constexpr (kDmaOk) return launch_inter<D, C, 16, OT, IT, true>(a, plan, nch_seq, chunk_off);
+                if constexpr (kDma16) return launch_inter<D, C, 16, OT, IT, true>(a, plan, nch_seq, chunk_off);
+                break;
+            case InterVariant::Dma32:
+                if constexpr (kDma32) return launch_inter<D, C, 32, OT, IT, true>(a, plan, nch_seq, chunk_off);
                 break;
             case InterVariant::Reg64:
                 if constexpr (kBf && D >= 64) return launch_inter<D, C, 64, OT, IT, false>(a, plan, nch_seq, chunk_off);
