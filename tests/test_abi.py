@@ -43,9 +43,10 @@ def test_status_strings(lib):
 
 def test_workspace_size(lib):
     ws = lib.kda_chunk_fwd_workspace_bytes
-    # B=1 T=32768 H=32 d=128 C=64 bf16: 512 chunks x 32 heads x record
+    # B=1 T=32768 H=32 d=128 C=64 bf16: 512 chunks x 32 heads x record; a record
+    # holds three C x d and two C x C fp16 tiles plus d fp32 decays, in whole KiB
     rec = (3 * 64 * 128 + 2 * 64 * 64) * 2 + 4 * 128
-    rec = (rec + 255) // 256 * 256
+    rec = (rec + 1023) // 1024 * 1024
     assert ws(1, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 512 * 32 * rec
     assert ws(1, 100, 2, 64, 64, 16, 0, kda.KDA_F32) > ws(1, 100, 2, 64, 64, 16, 0, kda.KDA_BF16)
     # packed sequences add a chunk table and one partial chunk per sequence
