@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-target", choices=["prefill", "decode", "copy"],
                     help="run only this workload a few times (target for rocprofv3) and exit")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="read rocprofv3 FETCH_SIZE/WRITE_SIZE runs of the three profile "
+                         "targets from DIR/<target>_<counter>/ and write profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -68,6 +71,67 @@ def measured_traffic(leg):
     return rec["bytes_per_call"]
 
 
+LEG_SOURCES = {"prefill": ["kda_prefill.hip", "kda_common.h", "kda_internal.h"],
+               "decode": ["kda_decode.hip", "kda_common.h", "kda_internal.h"]}
+LEG_KERNELS = {"prefill": ("kda_intra", "kda_inter"), "decode": ("decode_step_kernel",)}
+COPY_BYTES = 1 << 30   # the copy target reads and writes 1 GiB per dispatch
+
+
+def _counter_means(path, counter):
+    """Mean per-dispatch value of one counter, per kernel name, from a rocprofv3
+    counter_collection.csv tree."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % path)
+    acc = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                a = acc.setdefault(row["Kernel_Name"], [0.0, 0])
+                a[0] += float(row["Counter_Value"])
+                a[1] += 1
+    return {k: v[0] / v[1] for k, v in acc.items()}
+
+
+def traffic_from(d):
+    """HBM bytes per call for each leg.  FETCH_SIZE and WRITE_SIZE come in KiB
+    per dispatch; each is divided by what the same counter reads for a plain
+    1 GiB elementwise copy (torch.mul(x, 1.0, out=y)), so that 1.0 means the
+    bytes actually moved."""
+    out = {"method": "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE in separate runs of "
+                     "python bench.py --profile-target {copy,prefill,decode}; per-dispatch "
+                     "means, scaled by the copy kernel's reading of a 1 GiB read + 1 GiB write"}
+    scale = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        m = _counter_means(os.path.join(d, "copy_" + ctr), ctr)
+        copy_k = [k for k in m if "mul" in k.lower() or "elementwise" in k.lower()]
+        if not copy_k:
+            raise SystemExit("copy kernel not found in %s counters" % ctr)
+        scale[ctr] = max(m[k] for k in copy_k) * 1024.0 / COPY_BYTES
+    out["scale"] = scale
+    for leg, kern in LEG_KERNELS.items():
+        per_kernel = {}
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            m = _counter_means(os.path.join(d, leg + "_" + ctr), ctr)
+            for k, v in m.items():
+                short = next((x for x in kern if x in k), None)
+                if short is None:
+                    continue
+                per_kernel.setdefault(short, {})[ctr] = v * 1024.0 / scale[ctr]
+        total = sum(v.get("FETCH_SIZE", 0.0) + v.get("WRITE_SIZE", 0.0)
+                    for v in per_kernel.values())
+        out[leg] = dict(bytes_per_call=total, per_kernel_bytes=per_kernel,
+                        sources=LEG_SOURCES[leg], source_hash=source_hash(LEG_SOURCES[leg]))
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def profile_target(kind):
     """Minimal workload for counter collection: 3 calls, nothing else timed."""
     import kda_inputs
@@ -77,7 +141,7 @@ def profile_target(kind):
         x = torch.empty(256 << 20, dtype=torch.float32, device="cuda")   # 1 GiB
         y = torch.empty_like(x)
         for _ in range(3):
-            y.copy_(x)
+            torch.mul(x, 1.0, out=y)
     elif kind == "prefill":
         d = kda_inputs.config_inputs(2, "cuda")
         B, T, H, D = d["q"].shape
@@ -143,25 +207,49 @@ def bench_prefill(kda, kda_inputs, steps, warmup, stream):
     return dict(ms=ms, tokens=B * T, token_heads=B * T * H, inputs=d)
 
 
-def bench_decode(kda, kda_inputs, n_steps, warmup, stream):
+def decode_setup(kda, kda_inputs, n_steps, stream):
+    """The decode workload: a 256 x 32 x 128 x 128 fp32 state cache filled by a
+    4096-token prefill per sequence (32 sequences per call), and the seeded
+    inputs of n_steps decode steps, all on the device."""
     c = kda_inputs.CONFIGS[4]
     N, H, D, C, T0 = c["N"], c["H"], c["dk"], c["chunk"], c["init_T"]
     seed = kda_inputs.CFG_SEED[4]
     cache = torch.empty(N, H, D, D, device="cuda")
-    # state initialisation: 4096-token prefill per sequence, 32 sequences per call
-    nb = 32
-    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(nb, T0, H, D, D, C), dtype=torch.uint8,
-                     device="cuda")
-    for b0 in range(0, N, nb):
-        d = kda_inputs.prefill_inputs(seed * 1000 + b0, nb, T0, H, D, D, torch.bfloat16, "cuda")
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(DECODE_INIT_BATCH, T0, H, D, D, C),
+                     dtype=torch.uint8, device="cuda")
+    for b0 in range(0, N, DECODE_INIT_BATCH):
+        d = decode_init_inputs(kda_inputs, b0, "cuda")
         kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=C,
-                          final_state=cache[b0:b0 + nb], workspace=ws, stream=stream)
+                          final_state=cache[b0:b0 + DECODE_INIT_BATCH], workspace=ws,
+                          stream=stream)
         del d
     torch.cuda.synchronize()
     del ws
     steps = [kda_inputs.decode_inputs(seed, s, N, H, D, D, torch.bfloat16, "cuda")
              for s in range(n_steps)]
     o = torch.empty(n_steps, N, H, D, device="cuda")
+    return cache, steps, o
+
+
+DECODE_INIT_BATCH = 32
+
+
+def decode_init_inputs(kda_inputs, b0, device):
+    """Prefill inputs that initialise sequences b0 .. b0+31 of the decode cache."""
+    c = kda_inputs.CONFIGS[4]
+    return kda_inputs.prefill_inputs(kda_inputs.CFG_SEED[4] * 1000 + b0, DECODE_INIT_BATCH,
+                                     c["init_T"], c["H"], c["dk"], c["dv"], torch.bfloat16,
+                                     device)
+
+
+def decode_run(kda, cache, steps, o, stream):
+    for s, x in enumerate(steps):
+        kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], cache, o=o[s],
+                            stream=stream)
+
+
+def bench_decode(kda, kda_inputs, n_steps, warmup, stream):
+    cache, steps, o = decode_setup(kda, kda_inputs, n_steps, stream)
     scratch = cache.clone()
     for s in range(warmup):
         x = steps[s % n_steps]
@@ -171,22 +259,19 @@ def bench_decode(kda, kda_inputs, n_steps, warmup, stream):
     torch.cuda.synchronize()
     tm = StreamTimer(stream)
     tm.start()
-    for s in range(n_steps):
-        x = steps[s]
-        kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], cache, o=o[s],
-                            stream=stream)
+    decode_run(kda, cache, steps, o, stream)
     ms = tm.stop() / n_steps
     torch.cuda.synchronize()
-    return dict(ms=ms, N=N, token_heads=N * H)
+    return dict(ms=ms, N=cache.shape[0], token_heads=cache.shape[0] * cache.shape[1])
 
 
-def cpu_baseline_prefill(d, target_s=8.0):
+def cpu_baseline_prefill(d, target_s=10.0):
     """The fp64 oracle on a bounded sample of the prefill workload: all 32
-    heads of the first T_s tokens (T_s grown until the run takes a few
-    seconds).  Reported as tokens/s of the same layer."""
-    import numpy as np
+    heads of the first T_s tokens (T_s grown until one run takes a quarter of
+    the budget, or the whole layer), repeated until about target_s seconds
+    have run.  Reported as tokens/s of the same layer."""
     import oracle
-    H = d["q"].shape[2]
+    T = d["q"].shape[1]
     Ts = 256
     while True:
         sl = lambda t: t[:, :Ts].float().cpu().numpy()
@@ -194,16 +279,21 @@ def cpu_baseline_prefill(d, target_s=8.0):
         t0 = time.perf_counter()
         oracle.kda_fwd(q, k, v, g, b, 128 ** -0.5)
         dt = time.perf_counter() - t0
-        if dt >= target_s / 4 or Ts >= d["q"].shape[1]:
+        if dt >= target_s / 4 or Ts >= T:
             break
-        Ts = min(d["q"].shape[1], Ts * 4)
-    del np
-    return dict(value=Ts / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                sample="prefill B1 H32 d128: all 32 heads of the first %d of 32768 tokens, %.2f s"
-                % (Ts, dt))
+        Ts = min(T, Ts * 4)
+    reps = 1
+    while dt < target_s:
+        t0 = time.perf_counter()
+        oracle.kda_fwd(q, k, v, g, b, 128 ** -0.5)
+        dt += time.perf_counter() - t0
+        reps += 1
+    return dict(value=Ts * reps / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample="prefill B1 H32 d128: all 32 heads of the first %d of %d tokens, %d run(s), "
+                       "%.2f s" % (Ts, T, reps, dt))
 
 
-def cpu_baseline_decode(kda_inputs, target_s=4.0):
+def cpu_baseline_decode(kda_inputs, target_s=6.0):
     import numpy as np
     import oracle
     c = kda_inputs.CONFIGS[4]
@@ -232,6 +322,9 @@ def main():
               "MI355X (every (sequence, head) chain is independent, so more GPUs would shard "
               "sequences/heads with no exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_from:
+        traffic_from(args.traffic_from)
+        return
     if args.profile_target:
         profile_target(args.profile_target)
         return

@@ -86,3 +86,42 @@ def test_decode_matches_prefill_and_is_deterministic():
     assert rel_err(outs[0][1].cpu().numpy(), S_ref) < 1e-5
     assert rel_err(o_p.cpu().numpy(), o_ref) < TOL[torch.bfloat16]
     assert rel_err(S_p.cpu().numpy(), S_ref) < TOL[torch.bfloat16]
+
+
+def test_config4_decode_workload_sampled_chains():
+    """The decode benchmark's workload exactly as bench.py times it: a 256 x 32
+    x 128 x 128 cache filled by a 4096-token prefill per sequence (32 per call),
+    then 512 decode steps with fresh inputs.  Eight (sequence, head) chains are
+    recomputed by the oracle one by one (prefill over the same 4096 tokens,
+    then the 512 steps); their outputs at every step and their final states
+    are compared."""
+    import bench
+    stream = torch.cuda.current_stream()
+    n_steps = 512
+    cache, steps, o = bench.decode_setup(kda, kda_inputs, n_steps, stream)
+    bench.decode_run(kda, cache, steps, o, stream)
+    torch.cuda.synchronize()
+    D = cache.shape[-1]
+    sample = [(0, 0), (5, 31), (31, 7), (32, 1), (100, 16), (200, 30), (255, 2), (255, 31)]
+    ns = torch.tensor([n for n, _ in sample], device="cuda")
+    hs = torch.tensor([h for _, h in sample], device="cuda")
+    # per-step inputs of the sampled chains: [chain, step, ...]
+    seq = {name: np32(torch.stack([x[name][ns, hs] for x in steps], dim=1))
+           for name in ("q", "k", "v", "g", "beta")}
+    for i, (n, h) in enumerate(sample):
+        b0 = n - n % bench.DECODE_INIT_BATCH
+        d = bench.decode_init_inputs(kda_inputs, b0, "cuda")
+        j = n - b0
+        pick = lambda t: np32(t[j:j + 1, :, h:h + 1])
+        _, S = oracle.kda_fwd(pick(d["q"]), pick(d["k"]), pick(d["v"]), pick(d["g"]),
+                              pick(d["beta"]), D ** -0.5)
+        del d
+        state = S[:, :1].copy()           # [1, 1, D, D] fp64
+        o_ref = np.empty((n_steps, D))
+        for s in range(n_steps):
+            sl = lambda name: seq[name][i, s].reshape((1, 1) + seq[name].shape[2:])
+            o_ref[s] = oracle.kda_decode_step(sl("q"), sl("k"), sl("v"), sl("g"), sl("beta"),
+                                              D ** -0.5, state)[0, 0]
+        o_gpu = o[:, n, h].cpu().numpy()
+        assert rel_err(o_gpu, o_ref) < TOL[torch.bfloat16], (n, h)
+        assert rel_err(cache[n, h].cpu().numpy(), state[0, 0]) < TOL[torch.bfloat16], (n, h)
