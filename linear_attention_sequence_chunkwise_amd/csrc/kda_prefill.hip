@@ -931,16 +931,27 @@ __global__ __launch_bounds__(256) void kda_inter(
 // The chunk records (already in LDS-image form) and value rows are moved by
 // global_load_lds_dwordx4: every lane's 16 bytes land at consecutive LDS
 // addresses from a wave-uniform base held in M0, with no register
-// destination.  Four producer wavefronts issue all of these copies (one
-// wavefront alone cannot keep enough of them in flight); the four compute
-// wavefronts never touch the memory pipeline except for their output stores,
-// so a copy that waits for L2 never stalls the matrix work.
-// Chunk c+2's copies go into the buffer chunk c has just released and have
-// all of chunk c+1 to land.  The copies are issued from inline assembly (the
-// compiler does not track them); the producer waits for its own copies with
-// an explicit s_waitcnt vmcnt(N) -- the counter completes in order, so "at
-// most N newer operations outstanding" means the older buffer is complete --
-// and the next workgroup barrier publishes them.
+// destination.  NP producer wavefronts issue all of these copies; the compute
+// wavefronts never touch the memory pipeline except for their output stores.
+//
+// A CU only keeps a limited number of cache-line misses in flight, so issuing
+// a whole 65 KiB chunk stalls the issuing wavefront for about as long as the
+// chunk's compute takes.  The producers take part in every workgroup barrier,
+// so one long burst would hold the compute wavefronts at the next barrier.
+// Instead each region of the two buffers is refilled as soon as the phase
+// that reads it has released it, and the copies of chunk c+2 are spread over
+// the four barrier intervals:
+//   copy order: KG, QG, V (read by the X/QS phase, free after barrier 2),
+//               Tb (U phase, free after barrier 3),
+//               KPt, M, Gamma_n (O/S phase, free after barrier 4);
+//   interval after barrier 2 of chunk c:   positions [0, P1)   of chunk c+2
+//   interval after barrier 3 of chunk c:   positions [P1, P2)  of chunk c+2
+//   interval after barrier 4 of chunk c:   positions [P2, P3)  of chunk c+2
+//   interval after barrier 1 of chunk c+1: positions [P3, NPOS) of chunk c+2
+// (the last part goes in while chunk c+1 runs, into regions chunk c left).
+// Every copy has at least one chunk of compute to land.  Before barrier 1 of
+// chunk c+1 a producer waits until at most its own count of chunk c+2 copies
+// is outstanding: the counter completes in order, so chunk c+1 is complete.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -960,27 +971,47 @@ struct InterDmaSmem {
     ChainScratch<D, C, BV, OT> cs;
 };
 
-template <int D, int C, int BV, typename OT, typename IT>
-__global__ __launch_bounds__(64 * (BV / 4 + 4)) void kda_inter_dma(
+// Copy schedule of one chunk (positions in 1 KiB copies, see above).
+template <int D, int C, int BV, typename OT, typename IT, int NP>
+struct DmaPlan {
+    typedef Rec<D, C, OT> R;
+    static constexpr int NI = (int)(R::bytes / 1024);                    // record copies
+    static constexpr int U_KPT = (int)(R::KPt * sizeof(OT) / 1024);      // = KG + QG
+    static constexpr int U_TB = (int)(R::Tb * sizeof(OT) / 1024);
+    static constexpr int U_M = (int)(R::M * sizeof(OT) / 1024);
+    static constexpr int LPR = BV * (int)sizeof(IT) / 16;                // lanes per value row
+    static constexpr int NVI = (C * LPR + 63) / 64;                      // value copies
+    static constexpr int NPOS = NI + NVI;
+    static constexpr int N01 = U_KPT + NVI;                              // free after barrier 2
+    static constexpr int N012 = N01 + (U_M - U_TB);                      // free after barrier 3
+    static constexpr int cap(int x, int hi) { return x < hi ? x : hi; }
+    static constexpr int P1 = cap(NPOS * 18 / 100, N01);
+    static constexpr int P2 = cap(NPOS * 54 / 100, N012);
+    static constexpr int P3 = NPOS * 64 / 100 > P2 ? NPOS * 64 / 100 : P2;
+    // copies producer wavefront w issues for positions [0, x) and [a, b)
+    static constexpr int upto(int x, int w) { return x > w ? (x - w - 1) / NP + 1 : 0; }
+    static constexpr int count(int a, int b, int w) { return b <= a ? 0 : upto(b, w) - upto(a, w); }
+    static_assert(R::bytes % 1024 == 0 && (R::KPt * sizeof(OT)) % 1024 == 0 &&
+                      (R::Tb * sizeof(OT)) % 1024 == 0 && (R::M * sizeof(OT)) % 1024 == 0,
+                  "record regions must be whole KiB");
+    static_assert(0 <= P1 && P1 <= P2 && P2 <= P3 && P3 <= NPOS, "bad copy schedule");
+};
+
+template <int D, int C, int BV, typename OT, typename IT, int NP>
+__global__ __launch_bounds__(64 * (BV / 4 + NP)) void kda_inter_dma(
     int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
     const int* __restrict__ chunk_off, float scale, const IT* __restrict__ v,
     const float* __restrict__ s0, const char* __restrict__ records, float* __restrict__ o,
     float* __restrict__ sT) {
     constexpr int NWC = BV / 4;                    // compute wavefronts (one tile each per phase)
-    static_assert(64 * (NWC + 4) <= 1024, "workgroup too large");
+    static_assert(64 * (NWC + NP) <= 1024, "workgroup too large");
     constexpr int ST = (D / 16) * (BV / 16);
     constexpr int SPW = (ST + NWC - 1) / NWC;
     typedef Rec<D, C, OT> R;
     typedef InterDmaSmem<D, C, BV, OT, IT> SM;
-    constexpr int NI = (int)(R::bytes / 1024);     // 1 KiB copies per record
-    constexpr int RB = BV * (int)sizeof(IT);       // bytes per value row
-    constexpr int LPR = RB / 16;                   // lanes per value row
-    constexpr int NVI = (C * LPR + 63) / 64;       // value-row copies
-    constexpr int NB = (NI + NVI) / 4;             // copies per chunk issued by every producer
-    static_assert(RB % 16 == 0 && 64 % LPR == 0, "value rows must be whole 16-byte lanes");
-    // vmcnt holds at most 63: waiting for "<= 63 outstanding" when a batch has
-    // more copies also completes the newest batch's first ones (stricter, safe)
-    constexpr int NWAIT = NB < 63 ? NB : 63;
+    typedef DmaPlan<D, C, BV, OT, IT, NP> PL;
+    static_assert(64 % PL::LPR == 0 && BV * (int)sizeof(IT) % 16 == 0,
+                  "value rows must be whole 16-byte lanes");
     extern __shared__ __align__(1024) char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
@@ -988,43 +1019,81 @@ __global__ __launch_bounds__(64 * (BV / 4 + 4)) void kda_inter_dma(
     if (!cp.valid) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const bool producer = tid >= 64 * NWC;
     const size_t sbase = ((size_t)cp.n * H + cp.h) * (size_t)D * D;
 
-    if (producer) {
-        // all copies of chunk `c` into buffer `b`; the dv-slices of a head
-        // start at different offsets so their L2 requests spread out
-        const int pw = (tid - 64 * NWC) >> 6;        // producer wavefront 0..3
-        auto issue = [&](int c, int b) {
+    if (tid >= 64 * NWC) {
+        const int pw = (tid - 64 * NWC) >> 6;        // producer wavefront 0..NP-1
+        // copies of chunk c into buffer b for schedule positions [a, e)
+        auto issue = [&](int c, int b, int a, int e) {
             const char* rec = records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes;
             const uint32_t ib = lds_addr(sm.img[b]);
-            const int rot = (cp.v0 / BV) * NI / (D / BV);
-            for (int i = pw; i < NI; i += 4) {
-                const int ii = i + rot < NI ? i + rot : i + rot - NI;
-                dma16(rec + (size_t)ii * 1024 + lane * 16, ib + ii * 1024);
-            }
+            const uint32_t vb = lds_addr(sm.vraw[b]);
             const int tok0 = cp.seq_tok0 + c * C;
             const int len = min(C, cp.seq_len - c * C);
-            const uint32_t vb = lds_addr(sm.vraw[b]);
-            for (int i = pw; i < NVI; i += 4) {
-                const int r = min((i * 64 + lane) / LPR, len - 1);
-                const int part = (i * 64 + lane) % LPR;
-                dma16(reinterpret_cast<const char*>(v + ((size_t)(tok0 + r) * H + cp.h) * D +
-                                                    cp.v0) + part * 16,
-                      vb + i * 1024);
+            for (int p = a + ((pw - a) % NP + NP) % NP; p < e; p += NP) {
+                if (p >= PL::U_KPT && p < PL::N01) {          // value rows
+                    const int i = p - PL::U_KPT;
+                    const int r = min((i * 64 + lane) / PL::LPR, len - 1);
+                    const int part = (i * 64 + lane) % PL::LPR;
+                    dma16(reinterpret_cast<const char*>(v + ((size_t)(tok0 + r) * H + cp.h) * D +
+                                                        cp.v0) + part * 16,
+                          vb + i * 1024);
+                } else {
+                    // record unit: KG, QG | Tb | KPt | M, Gamma_n
+                    int u;
+                    if (p < PL::U_KPT) u = p;
+                    else if (p < PL::N012) u = PL::U_TB + (p - PL::N01);
+                    else if (p < PL::N012 + (PL::U_TB - PL::U_KPT)) u = PL::U_KPT + (p - PL::N012);
+                    else u = PL::U_M + (p - PL::N012 - (PL::U_TB - PL::U_KPT));
+                    dma16(rec + (size_t)u * 1024 + lane * 16, ib + u * 1024);
+                }
             }
         };
-        if (cp.nch > 0) issue(0, 0);
-        if (cp.nch > 1) issue(1, 1);
+        // Chunk complete: at most this wavefront's own copies of the newer
+        // chunk's first three parts are outstanding (vmcnt holds at most 63;
+        // a smaller immediate only makes the wait stricter).
+        auto wait_prev = [&](bool newer) {
+            if (!newer) {
+                asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+                return;
+            }
+#define KDA_WAIT_CASE(w)                                                              \
+    case w:                                                                           \
+        asm volatile("s_waitcnt vmcnt(%0)"                                            \
+                     :                                                                \
+                     : "n"(PL::count(0, PL::P3, w) < 63 ? PL::count(0, PL::P3, w) : 63) \
+                     : "memory");                                                     \
+        break;
+            switch (pw) {
+                KDA_WAIT_CASE(0)
+                KDA_WAIT_CASE(1)
+                KDA_WAIT_CASE(2)
+                KDA_WAIT_CASE(3)
+                KDA_WAIT_CASE(4)
+                KDA_WAIT_CASE(5)
+                KDA_WAIT_CASE(6)
+                default:
+                    asm volatile("s_waitcnt vmcnt(%0)"
+                                 :
+                                 : "n"(PL::count(0, PL::P3, 7) < 63 ? PL::count(0, PL::P3, 7) : 63)
+                                 : "memory");
+            }
+#undef KDA_WAIT_CASE
+        };
+        static_assert(NP <= 8, "wait table covers eight producer wavefronts");
+        if (cp.nch > 0) issue(0, 0, 0, PL::NPOS);
+        if (cp.nch > 1) issue(1, 1, 0, PL::P3);
+        wait_prev(cp.nch > 1);
         for (int c = 0; c < cp.nch; ++c) {
-            // chunk c complete (at most chunk c+1's copies still in flight)
-            if (c + 1 < cp.nch) asm volatile("s_waitcnt vmcnt(%0)" : : "n"(NWAIT) : "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
             lds_barrier();                           // chunk c published
-            lds_barrier();                           // compute: X done
-            lds_barrier();                           // compute: U done
+            if (c + 1 < cp.nch) issue(c + 1, (c + 1) & 1, PL::P3, PL::NPOS);
+            lds_barrier();                           // compute: X done (KG, QG, V free)
+            if (c + 2 < cp.nch) issue(c + 2, c & 1, 0, PL::P1);
+            lds_barrier();                           // compute: U done (Tb free)
+            if (c + 2 < cp.nch) issue(c + 2, c & 1, PL::P1, PL::P2);
             lds_barrier();                           // compute: chunk c's tiles released
-            if (c + 2 < cp.nch) issue(c + 2, c & 1);
+            if (c + 2 < cp.nch) issue(c + 2, c & 1, PL::P2, PL::P3);
+            if (c + 1 < cp.nch) wait_prev(c + 2 < cp.nch);
         }
         return;
     }
@@ -1040,7 +1109,7 @@ __global__ __launch_bounds__(64 * (BV / 4 + 4)) void kda_inter_dma(
         lds_barrier();                               // chunk c published
         const ChunkTiles<D, C, OT, IT> tiles(sm.img[b], reinterpret_cast<const IT*>(sm.vraw[b]));
         inter_chunk<D, C, BV, OT, IT, NWC>(tiles, sm.cs, st, cp.seq_tok0 + c * C,
-                                      min(C, cp.seq_len - c * C), H, cp.h, cp.v0, scale, o);
+                                           min(C, cp.seq_len - c * C), H, cp.h, cp.v0, scale, o);
     }
     if (sT) chain_store_state<D, BV, NWC>(st, sT, sbase, cp.v0);
 }
@@ -1049,6 +1118,7 @@ __global__ __launch_bounds__(64 * (BV / 4 + 4)) void kda_inter_dma(
 // Host side: planning and dispatch.
 // ---------------------------------------------------------------------------
 constexpr size_t kLdsLimit = 160 * 1024;
+constexpr int kProducers = 8;   // producer wavefronts of the direct-copy chain kernel
 
 template <int D, int C, typename OT>
 constexpr size_t intra_smem_bytes() { return sizeof(IntraSmem<D, C, OT>); }
@@ -1122,15 +1192,16 @@ static InterVariant choose_inter(int D, long long chains, bool bf16, bool dma16_
     return InterVariant::Reg16;
 }
 
-template <int D, int C, int BV, typename OT, typename IT, bool DMA>
+// KIND: 0 register-staged (kda_inter), 1 direct-to-LDS copies (kda_inter_dma).
+template <int D, int C, int BV, typename OT, typename IT, int KIND>
 static hipError_t launch_inter(const PrefillArgs& a, const PrefillPlan& plan, int nch_seq,
                                const int* chunk_off) {
     size_t smem;
     void (*kern)(int, int, int, int, int, const int*, const int*, float, const IT*, const float*,
                  const char*, float*, float*);
-    if constexpr (DMA) {
+    if constexpr (KIND == 1) {
         smem = inter_dma_smem_bytes<D, C, BV, OT, IT>();
-        kern = kda_inter_dma<D, C, BV, OT, IT>;
+        kern = kda_inter_dma<D, C, BV, OT, IT, kProducers>;
     } else {
         smem = inter_smem_bytes<D, C, BV, OT, IT>();
         kern = kda_inter<D, C, BV, OT, IT>;
@@ -1140,7 +1211,8 @@ static hipError_t launch_inter(const PrefillArgs& a, const PrefillPlan& plan, in
     if (e != hipSuccess) return e;
     const long long chains = (long long)a.N * a.H;
     const long long G8 = (chains + 7) / 8 * (D / BV);   // blocks per XCD
-    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(DMA ? 64 * (BV / 4 + 4) : 256), smem, a.stream, a.T, a.H,
+    const int threads = KIND == 0 ? 256 : 64 * (BV / 4 + kProducers);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(threads), smem, a.stream, a.T, a.H,
                        a.N, nch_seq, (int)G8, a.cu_seqlens, chunk_off, a.scale, (const IT*)a.v,
                        a.s0, (const char*)a.workspace + plan.off_records, a.o, a.sT);
     return hipGetLastError();
@@ -1183,21 +1255,21 @@ static hipError_t launch_dc(const PrefillArgs& a, const PrefillPlan& plan) {
         constexpr bool kDma32 = kBf && D >= 32 && inter_dma_smem_bytes<D, C, 32, OT, IT>() <= kLdsLimit;
         switch (choose_inter(D, (long long)a.N * a.H, kBf, kDma16, kDma32)) {
             case InterVariant::Dma16:
-                if constexpr (kDma16) return launch_inter<D, C, 16, OT, IT, true>(a, plan, nch_seq, chunk_off);
+                if constexpr (kDma16) return launch_inter<D, C, 16, OT, IT, 1>(a, plan, nch_seq, chunk_off);
                 break;
             case InterVariant::Dma32:
-                if constexpr (kDma32) return launch_inter<D, C, 32, OT, IT, true>(a, plan, nch_seq, chunk_off);
+                if constexpr (kDma32) return launch_inter<D, C, 32, OT, IT, 1>(a, plan, nch_seq, chunk_off);
                 break;
             case InterVariant::Reg64:
-                if constexpr (kBf && D >= 64) return launch_inter<D, C, 64, OT, IT, false>(a, plan, nch_seq, chunk_off);
+                if constexpr (kBf && D >= 64) return launch_inter<D, C, 64, OT, IT, 0>(a, plan, nch_seq, chunk_off);
                 break;
             case InterVariant::Reg32:
-                if constexpr (kBf && D >= 32) return launch_inter<D, C, 32, OT, IT, false>(a, plan, nch_seq, chunk_off);
+                if constexpr (kBf && D >= 32) return launch_inter<D, C, 32, OT, IT, 0>(a, plan, nch_seq, chunk_off);
                 break;
             default:
                 break;
         }
-        return launch_inter<D, C, 16, OT, IT, false>(a, plan, nch_seq, chunk_off);
+        return launch_inter<D, C, 16, OT, IT, 0>(a, plan, nch_seq, chunk_off);
     }
 }
 
