@@ -12,26 +12,40 @@
 //
 // The step is bound by HBM: each (sequence, head) reads and writes its
 // dk x dv fp32 state exactly once (2 * 64 KB at d = 128) and touches a few
-// hundred bytes of token data.  No matrix cores.  One 256-thread workgroup per
-// (sequence, head); each thread owns 4 adjacent columns (one float4) of
-// D/ (256 / (D/4)) rows, rows interleaved so that a wavefront's load covers
-// whole consecutive rows.  The state stays in registers between the read and
-// the write.
+// hundred bytes of token data.  No matrix cores.  One workgroup per
+// (sequence, head) with as many threads as the tiling allows (1024 at
+// d = 64 and 128); each thread owns 4 adjacent columns (one float4) of
+// D / (threads / (D/4)) rows, rows interleaved so that a wavefront's load
+// covers whole consecutive rows.  The state stays in registers between the
+// read and the write, and both go through nontemporal (streaming) accesses:
+// every state byte is touched once per step, so caching it would only evict
+// the token vectors.
 #include "kda_common.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-template <int D, typename IT>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+template <bool NT>
+__device__ __forceinline__ float4v ld_state(const float* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const float4v*>(p));
+    else return *reinterpret_cast<const float4v*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st_state(float* p, float4v x) {
+    if constexpr (NT) __builtin_nontemporal_store(x, reinterpret_cast<float4v*>(p));
+    else *reinterpret_cast<float4v*>(p) = x;
+}
+
+template <int D, typename IT, int NTH, bool NT>
+__global__ __launch_bounds__(NTH) void decode_step_kernel(
     int H, float scale, const IT* __restrict__ q, const IT* __restrict__ k,
     const IT* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
     float* __restrict__ state, int num_slots, const int32_t* __restrict__ slot_idx,
     float* __restrict__ o) {
     constexpr int CG = D / 4;        // float4 column groups
-    constexpr int RG = 256 / CG;     // row groups
+    constexpr int RG = NTH / CG;     // row groups
     constexpr int RPT = D / RG;      // rows per thread
-    static_assert(RPT >= 1 && RG * RPT == D, "bad decode tiling");
+    static_assert(RPT >= 1 && RG * RPT == D && NTH >= D, "bad decode tiling");
 
     const int nh = blockIdx.x;       // sequence * H + head
     const int n = nh / H;
@@ -60,7 +74,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     float4v s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-        s[i] = *reinterpret_cast<const float4v*>(S + (size_t)(i * RG + rg) * D + 4 * cg);
+        s[i] = ld_state<NT>(S + (size_t)(i * RG + rg) * D + 4 * cg);
 
     lds_barrier();
 
@@ -108,18 +122,28 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int i = 0; i < RPT; ++i) {
         const int r = i * RG + rg;
         s[i] += s_k[r] * e4;
-        *reinterpret_cast<float4v*>(S + (size_t)r * D + 4 * cg) = s[i];
+        st_state<NT>(S + (size_t)r * D + 4 * cg, s[i]);
     }
 }
+
+template <int D, typename IT, int NTH, bool NT>
+static hipError_t launch_decode_v(const DecodeArgs& a) {
+    dim3 grid((unsigned)(a.N * a.H)), block(NTH);
+    hipLaunchKernelGGL((decode_step_kernel<D, IT, NTH, NT>), grid, block, 0, a.stream, a.H,
+                       a.scale, (const IT*)a.q, (const IT*)a.k, (const IT*)a.v, a.g, a.beta,
+                       a.state, a.num_slots, a.slot_idx, a.o);
+    return hipGetLastError();
+}
+
+// Largest workgroup the tiling allows (up to 1024 threads): fewer rows per
+// thread means more independent 16-byte state streams in flight per CU.
+template <int D>
+constexpr int decode_threads() { return D * D / 4 >= 1024 ? 1024 : D * D / 4; }
 
 template <int D, typename IT>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
     if (a.N == 0) return hipSuccess;
-    dim3 grid((unsigned)(a.N * a.H)), block(256);
-    hipLaunchKernelGGL((decode_step_kernel<D, IT>), grid, block, 0, a.stream, a.H, a.scale,
-                       (const IT*)a.q, (const IT*)a.k, (const IT*)a.v, a.g, a.beta,
-                       a.state, a.num_slots, a.slot_idx, a.o);
-    return hipGetLastError();
+    return launch_decode_v<D, IT, decode_threads<D>(), true>(a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {
