@@ -360,7 +360,7 @@ def main():
                    roofline=dict(bound="hbm", achieved=db / (dc["ms"] / 1e3) / 1e9,
                                  peak=HBM_PEAK_GBS, unit="GB/s",
                                  traffic=measured_traffic("decode"),
-                                 kernel="decode_step_kernel<128, bf16>",
+                                 kernel="decode_step_kernel<128, bf16, 1024 threads, streaming>",
                                  algorithmic_bytes=db))
         dec["roofline"]["frac"] = dec["roofline"]["achieved"] / HBM_PEAK_GBS
 
