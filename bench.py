@@ -207,6 +207,36 @@ def bench_prefill(kda, kda_inputs, steps, warmup, stream):
     return dict(ms=ms, tokens=B * T, token_heads=B * T * H, inputs=d)
 
 
+def bench_prefill_prep(kda, kda_inputs, steps, warmup, stream):
+    """The prefill layer on raw inputs with the in-kernel preparation (q/k L2
+    normalisation, beta from logits, gate activation) -- kda_chunk_fwd_prep."""
+    c = kda_inputs.CONFIGS[2]
+    B, T, H, D, C = c["B"], c["T"], c["H"], c["dk"], c["chunk"]
+    d = kda_inputs.raw_layer_inputs(kda_inputs.CFG_SEED[2] + 50, B, T, H, D, D, torch.bfloat16,
+                                    "cuda")
+    prep = dict(normalize_qk=True, eps=1e-6, beta_logit=True, A_log=d["A_log"],
+                dt_bias=d["dt_bias"])
+    o = torch.empty(B, T, H, D, device="cuda")
+    S = torch.empty(B, H, D, D, device="cuda")
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(B, T, H, D, D, C), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=C, o=o,
+                          final_state=S, workspace=ws, stream=stream, prep=prep)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    tm = StreamTimer(stream)
+    tm.start()
+    for _ in range(steps):
+        call()
+    ms = tm.stop() / steps
+    torch.cuda.synchronize()
+    return ms
+
+
 def decode_setup(kda, kda_inputs, n_steps, stream):
     """The decode workload: a 256 x 32 x 128 x 128 fp32 state cache filled by a
     4096-token prefill per sequence (32 sequences per call), and the seeded
@@ -248,6 +278,33 @@ def decode_run(kda, cache, steps, o, stream):
                             stream=stream)
 
 
+def bench_decode_prep(kda, kda_inputs, cache, n_steps, stream):
+    """Decode steps on raw inputs with the in-kernel preparation, continuing
+    from the benchmark's cache."""
+    N, H, D = cache.shape[0], cache.shape[1], cache.shape[2]
+    xs = [kda_inputs.raw_layer_inputs(kda_inputs.CFG_SEED[4] * 7 + s, 1, N, H, D, D,
+                                      torch.bfloat16, "cuda") for s in range(16)]
+    xs = [{k: (v[0].contiguous() if v.dim() >= 3 else v) for k, v in x.items()} for x in xs]
+    o = torch.empty(N, H, D, device="cuda")
+
+    def step(x):
+        kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], cache, o=o,
+                            stream=stream, prep=dict(normalize_qk=True, eps=1e-6,
+                                                     beta_logit=True, A_log=x["A_log"],
+                                                     dt_bias=x["dt_bias"]))
+
+    for s in range(4):
+        step(xs[s])
+    torch.cuda.synchronize()
+    tm = StreamTimer(stream)
+    tm.start()
+    for s in range(n_steps):
+        step(xs[s % 16])
+    ms = tm.stop() / n_steps
+    torch.cuda.synchronize()
+    return ms
+
+
 def bench_decode(kda, kda_inputs, n_steps, warmup, stream):
     cache, steps, o = decode_setup(kda, kda_inputs, n_steps, stream)
     scratch = cache.clone()
@@ -262,7 +319,10 @@ def bench_decode(kda, kda_inputs, n_steps, warmup, stream):
     decode_run(kda, cache, steps, o, stream)
     ms = tm.stop() / n_steps
     torch.cuda.synchronize()
-    return dict(ms=ms, N=cache.shape[0], token_heads=cache.shape[0] * cache.shape[1])
+    del steps, o
+    ms_prep = bench_decode_prep(kda, kda_inputs, cache, 128, stream)
+    return dict(ms=ms, ms_prep=ms_prep, N=cache.shape[0],
+                token_heads=cache.shape[0] * cache.shape[1])
 
 
 def cpu_baseline_prefill(d, target_s=10.0):
@@ -336,6 +396,8 @@ def main():
 
     pf = bench_prefill(kda, kda_inputs, args.steps, args.warmup, stream)
     print("prefill %.4f ms/call" % pf["ms"], file=sys.stderr, flush=True)
+    pf_prep_ms = bench_prefill_prep(kda, kda_inputs, args.steps, args.warmup, stream)
+    print("prefill with preparation %.4f ms/call" % pf_prep_ms, file=sys.stderr, flush=True)
     th = pf["token_heads"]
     pf_bytes = PREFILL_BYTES_PER_TOKEN_HEAD * th
     pf_flops = prefill_flops_per_token_head() * th
@@ -363,6 +425,11 @@ def main():
                                  kernel="decode_step_kernel<128, bf16, 1024 threads, streaming>",
                                  algorithmic_bytes=db))
         dec["roofline"]["frac"] = dec["roofline"]["achieved"] / HBM_PEAK_GBS
+        dec["with_preparation"] = dict(
+            ms_per_step=dc["ms_prep"], value=dc["N"] / (dc["ms_prep"] / 1e3), unit="tokens/s",
+            steps=128, hbm_frac=db / (dc["ms_prep"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            workload="same cache; raw q/k, beta logits and gate pre-activations prepared "
+                     "in the kernel (kda_decode_step_prep)")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -389,6 +456,12 @@ def main():
                                "gates, zero initial state", "global_batch": 1, "seq_len": 32768,
                    "heads": 32, "head_dim": 128, "chunk": 64, "parallelism": "single GPU"},
         "roofline": roof,
+        "prefill_with_preparation": dict(
+            ms_per_step=pf_prep_ms, value=pf["tokens"] / (pf_prep_ms / 1e3), unit="tokens/s",
+            overhead=pf_prep_ms / pf["ms"] - 1.0,
+            hbm_frac=pf_bytes / (pf_prep_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            workload="same layer on raw inputs: q/k L2-normalised, beta from logits and the "
+                     "gate activated inside the kernels (kda_chunk_fwd_prep)"),
         "cpu_baseline": cpu,
         "decode": dec,
     }

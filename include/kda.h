@@ -68,6 +68,32 @@ typedef enum {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
+/* Optional input preparation done inside the kernels -- the per-token steps
+ * a Kimi Linear layer applies to the operator's inputs (GeekNews summary of
+ * Kimi Linear, "Configuracion del modelo Kimi Linear": L2 normalisation of
+ * queries and keys; a per-channel decay gate produced from a low-rank
+ * projection through a decay function of the GDN / Mamba family).  The page
+ * names that family only; the form implemented is the Mamba/GDN one applied
+ * per key channel:
+ *     log alpha_t[c] = -exp(A_log[h]) * softplus(g_t[c] + dt_bias[h, c]).
+ *
+ *   normalize_qk   nonzero: q_t, k_t <- x / sqrt(sum_c x_c^2 + qk_eps), per
+ *                  token and head, computed in fp32 from the stored inputs.
+ *   qk_eps         >= 0 (1e-6 is usual).
+ *   beta_is_logit  nonzero: beta_t <- 1 / (1 + exp(-beta_t)).
+ *   A_log          device pointer to [H] fp32, or NULL: g is already the log
+ *                  of the gate.  Non-NULL: g holds the gate pre-activation.
+ *   dt_bias        device pointer to [H, dk] fp32, or NULL (zero bias); only
+ *                  meaningful with A_log (non-NULL without A_log is an error).
+ * A NULL kda_prep* (or all fields zero/NULL) means no preparation. */
+typedef struct {
+    int normalize_qk;
+    float qk_eps;
+    int beta_is_logit;
+    const float *A_log;
+    const float *dt_bias;
+} kda_prep;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *kda_status_string(kda_status s);
 
@@ -118,6 +144,21 @@ kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk,
                          void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* kda_chunk_fwd with the optional input preparation above applied inside the
+ * kernels (prep may be NULL).  Same arguments, layouts, workspace and errors
+ * as kda_chunk_fwd; additionally KDA_ERR_NULL_ARG when prep->dt_bias is given
+ * without prep->A_log or a prep pointer is not 4-byte aligned, and
+ * KDA_ERR_BAD_SHAPE when prep->qk_eps is negative or not finite. */
+kda_status kda_chunk_fwd_prep(int B, int T, int H, int dk, int dv, int chunk,
+                              float scale, kda_dtype qkv_dtype,
+                              const void *q, const void *k, const void *v,
+                              const float *g, const float *beta,
+                              const float *initial_state,
+                              const int32_t *cu_seqlens, int num_seqs,
+                              float *o, float *final_state,
+                              void *workspace, size_t workspace_bytes,
+                              const kda_prep *prep, hipStream_t stream);
+
 /* One recurrent decode step for N sequences against a state cache.
  *
  *   N            sequences in this step (N may be 0).
@@ -141,6 +182,16 @@ kda_status kda_decode_step(int N, int H, int dk, int dv, float scale,
                            float *state_cache, int num_slots,
                            const int32_t *slot_idx, float *o,
                            hipStream_t stream);
+
+/* kda_decode_step with the optional input preparation above (prep may be
+ * NULL); errors as for kda_chunk_fwd_prep. */
+kda_status kda_decode_step_prep(int N, int H, int dk, int dv, float scale,
+                                kda_dtype qkv_dtype,
+                                const void *q, const void *k, const void *v,
+                                const float *g, const float *beta,
+                                float *state_cache, int num_slots,
+                                const int32_t *slot_idx, float *o,
+                                const kda_prep *prep, hipStream_t stream);
 
 #ifdef __cplusplus
 }

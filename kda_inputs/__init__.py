@@ -75,6 +75,26 @@ def prefill_inputs(seed, B, T, H, dk, dv, dtype=torch.bfloat16, device="cpu",
     return out
 
 
+def raw_layer_inputs(seed, B, T, H, dk, dv, dtype=torch.bfloat16, device="cpu"):
+    """Inputs as a model layer hands them over before its preparation step:
+    q, k un-normalised (each row N(0, 1) times a length in [0.3, 3.3]), beta
+    as a N(0, 1) logit, g as a 0.5 N(0, 1) gate pre-activation, plus per-head
+    A_log ~ U(-1, 0.5) and per-channel dt_bias ~ U(-5, -2) (so the prepared
+    log-gate stays in [-0.5, 0) like the configs' gates)."""
+    gen = _gen(seed, device)
+    f = dict(device=device, dtype=torch.float32, generator=gen)
+    q = torch.randn(B, T, H, dk, **f) * (0.3 + 3 * torch.rand(B, T, H, 1, **f))
+    k = torch.randn(B, T, H, dk, **f) * (0.3 + 3 * torch.rand(B, T, H, 1, **f))
+    v = torch.randn(B, T, H, dv, **f)
+    b = torch.randn(B, T, H, **f)
+    g = 0.5 * torch.randn(B, T, H, dk, **f)
+    A_log = -1.0 + 1.5 * torch.rand(H, **f)
+    dt_bias = -5.0 + 3.0 * torch.rand(H, dk, **f)
+    return dict(q=q.to(dtype).contiguous(), k=k.to(dtype).contiguous(),
+                v=v.to(dtype).contiguous(), beta=b.contiguous(), g=g.contiguous(),
+                A_log=A_log.contiguous(), dt_bias=dt_bias.contiguous())
+
+
 def varlen_lengths(seed, n, lo, hi):
     """n integer lengths, uniform on [lo, hi] inclusive (CPU generator, so the
     same on every machine)."""

@@ -24,13 +24,27 @@ STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL_ARG", 2: "KDA_ERR_BAD_SHAPE",
 
 # name -> (restype, argtypes), mirroring include/kda.h
 _P, _I, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+class KdaPrep(ctypes.Structure):
+    """kda_prep of include/kda.h."""
+    _fields_ = [("normalize_qk", ctypes.c_int), ("qk_eps", ctypes.c_float),
+                ("beta_is_logit", ctypes.c_int), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p)]
+
+
+_PREP = ctypes.POINTER(KdaPrep)
 SIGNATURES = {
     "kda_status_string": (ctypes.c_char_p, [_I]),
     "kda_version": (_I, []),
     "kda_chunk_fwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "kda_chunk_fwd": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                            _P, _P, _P, _SZ, _P]),
+    "kda_chunk_fwd_prep": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
+                                _P, _P, _P, _SZ, _PREP, _P]),
     "kda_decode_step": (_I, [_I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P]),
+    "kda_decode_step_prep": (_I, [_I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                  _PREP, _P]),
 }
 
 _lib = None
@@ -94,6 +108,26 @@ def _check(t, name, dtype=None, device=None):
         raise ValueError("%s must be on %s" % (name, device))
 
 
+def make_prep(prep, H, dk, device):
+    """kda_prep from a dict: normalize_qk (bool), eps (float, default 1e-6),
+    beta_logit (bool), A_log ([H] fp32 tensor or None), dt_bias ([H, dk] fp32
+    tensor or None).  Returns (struct or None, tensors to keep alive)."""
+    if prep is None:
+        return None, ()
+    a = prep.get("A_log")
+    b = prep.get("dt_bias")
+    _check(a, "A_log", torch.float32, device)
+    _check(b, "dt_bias", torch.float32, device)
+    if a is not None and a.numel() != H:
+        raise ValueError("A_log must hold H values")
+    if b is not None and b.numel() != H * dk:
+        raise ValueError("dt_bias must hold H * dk values")
+    st = KdaPrep(1 if prep.get("normalize_qk") else 0, float(prep.get("eps", 1e-6)),
+                 1 if prep.get("beta_logit") else 0,
+                 None if a is None else a.data_ptr(), None if b is None else b.data_ptr())
+    return st, (a, b)
+
+
 def kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torch.bfloat16):
     code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
     return int(load_library().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs,
@@ -102,13 +136,14 @@ def kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torc
 
 def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu_seqlens=None,
                   output_final_state=True, o=None, final_state=None, workspace=None,
-                  stream=None):
+                  stream=None, prep=None):
     """Chunkwise KDA prefill.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32); g: [B, T, H, dk] fp32
     (log gate); beta: [B, T, H] fp32; initial_state: [N, H, dk, dv] fp32 or
-    None; cu_seqlens: int32 [N + 1] (B must be 1) or None.  Returns
-    (o [B, T, H, dv] fp32, final_state [N, H, dk, dv] fp32 or None).
+    None; cu_seqlens: int32 [N + 1] (B must be 1) or None; prep: optional
+    in-kernel input preparation (see make_prep; calls kda_chunk_fwd_prep).
+    Returns (o [B, T, H, dv] fp32, final_state [N, H, dk, dv] fp32 or None).
     """
     lib = load_library()
     B, T, H, dk = q.shape
@@ -132,20 +167,27 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu
                                              N if cu_seqlens is not None else 0, code)
     if workspace is None:
         workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
-    rc = lib.kda_chunk_fwd(B, T, H, dk, dv, chunk, float(scale), code, _ptr(q), _ptr(k), _ptr(v),
-                           _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
-                           N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state),
-                           _ptr(workspace), workspace.numel(), _stream(stream))
+    args = (B, T, H, dk, dv, chunk, float(scale), code, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+            _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+            N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), _ptr(workspace),
+            workspace.numel())
+    if prep is None:
+        rc = lib.kda_chunk_fwd(*args, _stream(stream))
+        fn = "kda_chunk_fwd"
+    else:
+        st, _keep = make_prep(prep, H, dk, dev)
+        rc = lib.kda_chunk_fwd_prep(*args, ctypes.byref(st), _stream(stream))
+        fn = "kda_chunk_fwd_prep"
     if rc != KDA_OK:
-        raise KDAError("kda_chunk_fwd", rc)
+        raise KDAError(fn, rc)
     return o, final_state
 
 
 def kda_decode_step(q, k, v, g, beta, state_cache, scale=None, slot_idx=None, o=None,
-                    stream=None):
+                    stream=None, prep=None):
     """One decode step.  q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H];
     state_cache: [num_slots, H, dk, dv] fp32, updated in place; slot_idx:
-    int32 [N] or None.  Returns o [N, H, dv] fp32."""
+    int32 [N] or None; prep as in kda_chunk_fwd.  Returns o [N, H, dv] fp32."""
     lib = load_library()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -160,9 +202,15 @@ def kda_decode_step(q, k, v, g, beta, state_cache, scale=None, slot_idx=None, o=
         scale = dk ** -0.5
     if o is None:
         o = torch.empty(N, H, dv, dtype=torch.float32, device=dev)
-    rc = lib.kda_decode_step(N, H, dk, dv, float(scale), _dtype_code(q), _ptr(q), _ptr(k),
-                             _ptr(v), _ptr(g), _ptr(beta), _ptr(state_cache),
-                             state_cache.shape[0], _ptr(slot_idx), _ptr(o), _stream(stream))
+    args = (N, H, dk, dv, float(scale), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+            _ptr(beta), _ptr(state_cache), state_cache.shape[0], _ptr(slot_idx), _ptr(o))
+    if prep is None:
+        rc = lib.kda_decode_step(*args, _stream(stream))
+        fn = "kda_decode_step"
+    else:
+        st, _keep = make_prep(prep, H, dk, dev)
+        rc = lib.kda_decode_step_prep(*args, ctypes.byref(st), _stream(stream))
+        fn = "kda_decode_step_prep"
     if rc != KDA_OK:
-        raise KDAError("kda_decode_step", rc)
+        raise KDAError(fn, rc)
     return o

@@ -4,6 +4,7 @@
 // caller's buffers.
 #include "kda.h"
 
+#include <math.h>
 #include <stdint.h>
 
 #include "kda_internal.h"
@@ -15,6 +16,24 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Validates a kda_prep and converts it; NULL means no preparation.
+kda_status read_prep(const kda_prep* p, kda::Prep* out) {
+    *out = kda::Prep();
+    if (!p) return KDA_OK;
+    if (p->dt_bias && !p->A_log) return KDA_ERR_NULL_ARG;
+    if ((p->A_log && !aligned4(p->A_log)) || (p->dt_bias && !aligned4(p->dt_bias)))
+        return KDA_ERR_NULL_ARG;
+    if (!(p->qk_eps >= 0.f) || !isfinite(p->qk_eps)) return KDA_ERR_BAD_SHAPE;
+    out->normalize = p->normalize_qk != 0;
+    out->eps = p->qk_eps;
+    out->beta_logit = p->beta_is_logit != 0;
+    out->A_log = p->A_log;
+    out->dt_bias = p->dt_bias;
+    return KDA_OK;
+}
 
 }  // namespace
 
@@ -49,12 +68,16 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
     return plan.total;
 }
 
-kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk, float scale,
-                         kda_dtype qkv_dtype, const void* q, const void* k, const void* v,
-                         const float* g, const float* beta, const float* initial_state,
-                         const int32_t* cu_seqlens, int num_seqs, float* o, float* final_state,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+kda_status kda_chunk_fwd_prep(int B, int T, int H, int dk, int dv, int chunk, float scale,
+                              kda_dtype qkv_dtype, const void* q, const void* k,
+                              const void* v, const float* g, const float* beta,
+                              const float* initial_state, const int32_t* cu_seqlens,
+                              int num_seqs, float* o, float* final_state, void* workspace,
+                              size_t workspace_bytes, const kda_prep* prep,
+                              hipStream_t stream) {
     if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_BAD_SHAPE;
+    kda::Prep pr;
+    if (kda_status e = read_prep(prep, &pr)) return e;
     const bool varlen = cu_seqlens != nullptr;
     if (varlen && (B != 1 || num_seqs < 1)) return KDA_ERR_BAD_SHAPE;
     const int N = varlen ? num_seqs : B;
@@ -88,15 +111,29 @@ kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk, float s
     a.s0 = initial_state; a.cu_seqlens = cu_seqlens; a.N = N;
     a.o = o; a.sT = final_state;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.prep = pr;
     a.stream = stream;
     return from_hip(kda::launch_prefill(a, plan));
 }
 
-kda_status kda_decode_step(int N, int H, int dk, int dv, float scale, kda_dtype qkv_dtype,
-                           const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, float* state_cache, int num_slots,
-                           const int32_t* slot_idx, float* o, hipStream_t stream) {
+kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk, float scale,
+                         kda_dtype qkv_dtype, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* initial_state,
+                         const int32_t* cu_seqlens, int num_seqs, float* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return kda_chunk_fwd_prep(B, T, H, dk, dv, chunk, scale, qkv_dtype, q, k, v, g, beta,
+                              initial_state, cu_seqlens, num_seqs, o, final_state, workspace,
+                              workspace_bytes, nullptr, stream);
+}
+
+kda_status kda_decode_step_prep(int N, int H, int dk, int dv, float scale,
+                                kda_dtype qkv_dtype, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta,
+                                float* state_cache, int num_slots, const int32_t* slot_idx,
+                                float* o, const kda_prep* prep, hipStream_t stream) {
     if (N < 0 || H < 1 || dk < 1 || dv < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
+    kda::Prep pr;
+    if (kda_status e = read_prep(prep, &pr)) return e;
     if (!slot_idx && N > num_slots) return KDA_ERR_BAD_SHAPE;
     if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
     if (dk != dv || !supported_dim(dk)) return KDA_ERR_UNSUPPORTED;
@@ -113,8 +150,17 @@ kda_status kda_decode_step(int N, int H, int dk, int dv, float scale, kda_dtype 
     a.N = N; a.H = H; a.D = dk; a.scale = scale; a.bf16 = qkv_dtype == KDA_BF16;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.state = state_cache; a.num_slots = num_slots; a.slot_idx = slot_idx; a.o = o;
+    a.prep = pr;
     a.stream = stream;
     return from_hip(kda::launch_decode(a));
+}
+
+kda_status kda_decode_step(int N, int H, int dk, int dv, float scale, kda_dtype qkv_dtype,
+                           const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state_cache, int num_slots,
+                           const int32_t* slot_idx, float* o, hipStream_t stream) {
+    return kda_decode_step_prep(N, H, dk, dv, scale, qkv_dtype, q, k, v, g, beta, state_cache,
+                                num_slots, slot_idx, o, nullptr, stream);
 }
 
 }  // extern "C"

@@ -38,6 +38,17 @@ __device__ __forceinline__ float exp_e(float x) {
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
+// Input preparation helpers (see kda_prep in kda.h).
+// softplus(x) = max(x, 0) + ln(1 + e^-|x|), the logarithm through the hardware
+// base-2 log: 1 + e^-|x| lies in [1, 2], so the absolute error stays below
+// 1e-7 (for very negative x the true value e^x may be lost below that).
+__device__ __forceinline__ float softplus_f(float x) {
+    return fmaxf(x, 0.f) + 0.6931471805599453f * __builtin_amdgcn_logf(1.f + exp_e(-fabsf(x)));
+}
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + exp_e(-x)); }
+// 1 / sqrt(s) for s > 0 and 0 for s == 0, so that a zero vector stays zero.
+__device__ __forceinline__ float rnorm(float s) { return s > 0.f ? rsqrtf(s) : 0.f; }
+
 // Load 4 consecutive input elements (bf16 or fp32) as floats.
 __device__ __forceinline__ float4v load4(const float* p) {
     return *reinterpret_cast<const float4v*>(p);

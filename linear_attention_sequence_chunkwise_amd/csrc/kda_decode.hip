@@ -36,12 +36,15 @@ __device__ __forceinline__ void st_state(float* p, float4v x) {
     else *reinterpret_cast<float4v*>(p) = x;
 }
 
-template <int D, typename IT, int NTH, bool NT>
+// PREP: apply the optional input preparation (kda_prep).  The L2 norms of k
+// and q are folded in after the reductions: u = |k|^-1 S'^T k,
+// p = |q|^-1 S'^T q, and the rank-1 update uses |k|^-1 e.
+template <int D, typename IT, int NTH, bool NT, bool PREP>
 __global__ __launch_bounds__(NTH) void decode_step_kernel(
     int H, float scale, const IT* __restrict__ q, const IT* __restrict__ k,
     const IT* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
     float* __restrict__ state, int num_slots, const int32_t* __restrict__ slot_idx,
-    float* __restrict__ o) {
+    float* __restrict__ o, Prep prep) {
     constexpr int CG = D / 4;        // float4 column groups
     constexpr int RG = NTH / CG;     // row groups
     constexpr int RPT = D / RG;      // rows per thread
@@ -62,7 +65,13 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(
     if (tid < D) {
         s_k[tid] = to_f32(k[tok * D + tid]);
         s_q[tid] = to_f32(q[tok * D + tid]);
-        s_a[tid] = exp_e(g[tok * D + tid]);
+        float lg = g[tok * D + tid];
+        if constexpr (PREP) {
+            if (prep.A_log)
+                lg = -exp_e(prep.A_log[h]) *
+                     softplus_f(lg + (prep.dt_bias ? prep.dt_bias[h * D + tid] : 0.f));
+        }
+        s_a[tid] = exp_e(lg);
     }
 
     const int cg = tid % CG;
@@ -78,13 +87,36 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(
 
     lds_barrier();
 
-    // k.q by wavefront 0
+    // k.q (and, when normalising, |k|^-1 and |q|^-1) by wavefront 0
     if (tid < 64) {
-        float t = 0.f;
-        for (int i = tid; i < D; i += 64) t += s_k[i] * s_q[i];
+        float t = 0.f, sk = 0.f, sq = 0.f;
+        for (int i = tid; i < D; i += 64) {
+            t += s_k[i] * s_q[i];
+            if constexpr (PREP) {
+                sk += s_k[i] * s_k[i];
+                sq += s_q[i] * s_q[i];
+            }
+        }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
-        if (tid == 0) s_kq[0] = t;
+        for (int off = 32; off > 0; off >>= 1) {
+            t += __shfl_xor(t, off);
+            if constexpr (PREP) {
+                sk += __shfl_xor(sk, off);
+                sq += __shfl_xor(sq, off);
+            }
+        }
+        if (tid == 0) {
+            float nk = 1.f, nq = 1.f;
+            if constexpr (PREP) {
+                if (prep.normalize) {
+                    nk = rnorm(sk + prep.eps);
+                    nq = rnorm(sq + prep.eps);
+                }
+            }
+            s_kq[0] = t * nk * nq;
+            s_kq[1] = nk;
+            s_kq[2] = nq;
+        }
     }
 
     float4v pu = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
@@ -110,9 +142,16 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(
             u += s_red[0][r][tid];
             p += s_red[1][r][tid];
         }
+        float b = beta[tok];
+        if constexpr (PREP) {
+            u *= s_kq[1];
+            p *= s_kq[2];
+            if (prep.beta_logit) b = sigmoid_f(b);
+        }
         const float vv = to_f32(v[tok * D + tid]);
-        const float e = beta[tok] * (vv - u);
-        s_e[tid] = e;
+        const float e = b * (vv - u);
+        if constexpr (PREP) s_e[tid] = e * s_kq[1];
+        else s_e[tid] = e;
         o[tok * D + tid] = scale * (p + s_kq[0] * e);
     }
     lds_barrier();
@@ -129,9 +168,14 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(
 template <int D, typename IT, int NTH, bool NT>
 static hipError_t launch_decode_v(const DecodeArgs& a) {
     dim3 grid((unsigned)(a.N * a.H)), block(NTH);
-    hipLaunchKernelGGL((decode_step_kernel<D, IT, NTH, NT>), grid, block, 0, a.stream, a.H,
-                       a.scale, (const IT*)a.q, (const IT*)a.k, (const IT*)a.v, a.g, a.beta,
-                       a.state, a.num_slots, a.slot_idx, a.o);
+    if (a.prep.active())
+        hipLaunchKernelGGL((decode_step_kernel<D, IT, NTH, NT, true>), grid, block, 0, a.stream,
+                           a.H, a.scale, (const IT*)a.q, (const IT*)a.k, (const IT*)a.v, a.g,
+                           a.beta, a.state, a.num_slots, a.slot_idx, a.o, a.prep);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<D, IT, NTH, NT, false>), grid, block, 0, a.stream,
+                           a.H, a.scale, (const IT*)a.q, (const IT*)a.k, (const IT*)a.v, a.g,
+                           a.beta, a.state, a.num_slots, a.slot_idx, a.o, a.prep);
     return hipGetLastError();
 }
 

@@ -8,6 +8,17 @@
 
 namespace kda {
 
+// In-kernel input preparation (see kda_prep in kda.h).  active() is false
+// when every step is off, and the kernels then take their plain path.
+struct Prep {
+    bool normalize = false;
+    float eps = 0.f;
+    bool beta_logit = false;
+    const float* A_log = nullptr;
+    const float* dt_bias = nullptr;
+    bool active() const { return normalize || beta_logit || A_log != nullptr; }
+};
+
 struct DecodeArgs {
     int N, H, D;
     float scale;
@@ -18,6 +29,7 @@ struct DecodeArgs {
     int num_slots;
     const int32_t* slot_idx;
     float* o;
+    Prep prep;
     hipStream_t stream;
 };
 
@@ -34,6 +46,7 @@ struct PrefillArgs {
     float* sT;
     void* workspace;
     size_t workspace_bytes;
+    Prep prep;
     hipStream_t stream;
 };
 

@@ -320,11 +320,35 @@ __device__ __forceinline__ float4v mma16(float4v acc, const XT* x, int ldx, cons
     }
 }
 
-template <int D, int C, typename OT, typename IT>
+// Lane permute within rows of 16 lanes (DPP), every lane active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of W lanes (W a power of two, 2..64): pairs, quads,
+// half rows and rows through DPP (after the quad steps every lane of a quad
+// holds the quad sum, so the mirror permutes pair equal partial sums), then
+// cross-row steps through lane shuffles.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(W >= 2 && W <= 64 && (W & (W - 1)) == 0, "bad group");
+    x += dpp_f<0xB1>(x);                     // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (W >= 4) x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (W >= 8) x += dpp_f<0x141>(x);  // row_half_mirror
+    if constexpr (W >= 16) x += dpp_f<0x140>(x); // row_mirror
+    if constexpr (W >= 32) x += __shfl_xor(x, 16);
+    if constexpr (W >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+// PREP: apply the optional input preparation (kda_prep) while loading.
+template <int D, int C, typename OT, typename IT, bool PREP>
 __global__ __launch_bounds__(256) void kda_intra(
     int T, int H, int nch_seq, const ChunkInfo* __restrict__ table,
     const int* __restrict__ chunk_total, const IT* __restrict__ q, const IT* __restrict__ k,
-    const float* __restrict__ g, const float* __restrict__ beta, char* __restrict__ records) {
+    const float* __restrict__ g, const float* __restrict__ beta, char* __restrict__ records,
+    Prep pp) {
     constexpr int NB = C / 16;
     constexpr int LDK = padded<OT>(D);
     constexpr int LDA = padded<OT>(C);
@@ -357,7 +381,10 @@ __global__ __launch_bounds__(256) void kda_intra(
     const int wave = tid >> 6;
 
     if (tid < C) {
-        const float bt = beta[(size_t)(tok0 + min(tid, len - 1)) * H + h];
+        float bt = beta[(size_t)(tok0 + min(tid, len - 1)) * H + h];
+        if constexpr (PREP) {
+            if (pp.beta_logit) bt = sigmoid_f(bt);
+        }
         sm.beta[tid] = tid < len ? bt : 0.f;
     }
 
@@ -384,6 +411,19 @@ __global__ __launch_bounds__(256) void kda_intra(
             k0v[j] = kk.x; k1v[j] = kk.y;
             q0v[j] = qq.x; q1v[j] = qq.y;
         }
+        if constexpr (PREP) {
+            // gate pre-activation -> log alpha = -exp(A_log) softplus(x + dt_bias)
+            if (pp.A_log) {
+                const float rate = exp_e(pp.A_log[h]);
+                const float b0 = pp.dt_bias ? pp.dt_bias[h * D + c0] : 0.f;
+                const float b1 = pp.dt_bias ? pp.dt_bias[h * D + c0 + 1] : 0.f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    g0[j] = -rate * softplus_f(g0[j] + b0);
+                    g1[j] = -rate * softplus_f(g1[j] + b1);
+                }
+            }
+        }
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -392,6 +432,20 @@ __global__ __launch_bounds__(256) void kda_intra(
             }
             s0 += g0[j];
             s1 += g1[j];
+        }
+        if constexpr (PREP) {
+            // L2 norm of every row of q and k: the NP lanes of this sub-block
+            // (one per channel pair) hold the whole row
+            if (pp.normalize) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float sk = group_sum<NP>(k0v[j] * k0v[j] + k1v[j] * k1v[j]);
+                    const float sq = group_sum<NP>(q0v[j] * q0v[j] + q1v[j] * q1v[j]);
+                    const float nk = rnorm(sk + pp.eps), nq = rnorm(sq + pp.eps);
+                    k0v[j] *= nk; k1v[j] *= nk;
+                    q0v[j] *= nq; q1v[j] *= nq;
+                }
+            }
         }
         sm.sig[I * D + c0] = s0;
         sm.sig[I * D + c0 + 1] = s1;
@@ -1239,14 +1293,14 @@ static hipError_t launch_dc(const PrefillArgs& a, const PrefillPlan& plan) {
         }
         if (plan.nchunk_max > 0) {
             const size_t smem = intra_smem_bytes<D, C, OT>();
-            auto kern = kda_intra<D, C, OT, IT>;
+            auto kern = a.prep.active() ? kda_intra<D, C, OT, IT, true> : kda_intra<D, C, OT, IT, false>;
             hipError_t e = hipFuncSetAttribute(
                 (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL(kern, dim3((unsigned)plan.nchunk_max, (unsigned)a.H), dim3(256),
                                smem, a.stream, a.T, a.H, nch_seq, table,
                                varlen ? chunk_off + a.N : nullptr, (const IT*)a.q,
-                               (const IT*)a.k, a.g, a.beta, ws + plan.off_records);
+                               (const IT*)a.k, a.g, a.beta, ws + plan.off_records, a.prep);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

@@ -72,6 +72,12 @@ def _load():
         lib.oracle_kda_fwd.restype = I
         lib.oracle_kda_decode_step.argtypes = [I, I, I, I, D, P, P, P, P, P, P, I, P, P]
         lib.oracle_kda_decode_step.restype = I
+        lib.oracle_kda_fwd_prep.argtypes = [I, I, I, I, I, D, P, P, P, P, P, P, P, I, I, D, P, P,
+                                            P, P]
+        lib.oracle_kda_fwd_prep.restype = I
+        lib.oracle_kda_decode_step_prep.argtypes = [I, I, I, I, D, P, P, P, P, P, P, I, P, I, D,
+                                                    P, P, P]
+        lib.oracle_kda_decode_step_prep.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         _lib = lib
@@ -97,13 +103,27 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def kda_fwd(q, k, v, g, beta, scale, S0=None, cu_seqlens=None, drop_erase=False):
+def _prep_args(prep, H, dk):
+    """(flags, eps, A_log, dt_bias) for the C oracle from a prep dict:
+    normalize_qk (bool), eps (float), beta_logit (bool), A_log ([H] or None),
+    dt_bias ([H, dk] or None).  See prepare_token in kda_oracle.c."""
+    flags = (1 if prep.get("normalize_qk") else 0) | (2 if prep.get("beta_logit") else 0)
+    a = prep.get("A_log")
+    b = prep.get("dt_bias")
+    a = None if a is None else _f32(a).reshape(H)
+    b = None if b is None else _f32(b).reshape(H, dk)
+    return flags, float(prep.get("eps", 1e-6)), a, b
+
+
+def kda_fwd(q, k, v, g, beta, scale, S0=None, cu_seqlens=None, drop_erase=False, prep=None):
     """Exact KDA forward in fp64.
 
     q, k, g: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H] (float32 values,
     upcast to fp64 inside).  S0: [N, H, dk, dv] or None.  cu_seqlens: int32
-    [N + 1] or None (then N = B).  Returns (o [B, T, H, dv], S [N, H, dk, dv]),
-    both float64.
+    [N + 1] or None (then N = B).  prep: optional input preparation (see
+    _prep_args): L2 normalisation of q and k, beta given as logits, g given as
+    the gate pre-activation of the Mamba/GDN-style decay.  Returns
+    (o [B, T, H, dv], S [N, H, dk, dv]), both float64.
     """
     q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
     B, T, H, dk = q.shape
@@ -122,17 +142,25 @@ def kda_fwd(q, k, v, g, beta, scale, S0=None, cu_seqlens=None, drop_erase=False)
         assert s0.shape == (N, H, dk, dv)
     o = np.zeros((B, T, H, dv), dtype=np.float64)
     S = np.zeros((N, H, dk, dv), dtype=np.float64)
-    rc = _load().oracle_kda_fwd(B, T, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
-                                _ptr(g), _ptr(beta), _ptr(s0), _ptr(cu), N,
-                                1 if drop_erase else 0, _ptr(o), _ptr(S))
+    if prep is not None:
+        assert not drop_erase
+        flags, eps, a, b = _prep_args(prep, H, dk)
+        rc = _load().oracle_kda_fwd_prep(B, T, H, dk, dv, float(scale), _ptr(q), _ptr(k),
+                                         _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(cu), N,
+                                         flags, eps, _ptr(a), _ptr(b), _ptr(o), _ptr(S))
+    else:
+        rc = _load().oracle_kda_fwd(B, T, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(g), _ptr(beta), _ptr(s0), _ptr(cu), N,
+                                    1 if drop_erase else 0, _ptr(o), _ptr(S))
     if rc != 0:
         raise ValueError("oracle_kda_fwd rejected its arguments (code %d)" % rc)
     return o, S
 
 
-def kda_decode_step(q, k, v, g, beta, scale, state, slot_idx=None):
+def kda_decode_step(q, k, v, g, beta, scale, state, slot_idx=None, prep=None):
     """One exact decode step.  q, k, g [N, H, dk]; v [N, H, dv]; beta [N, H];
-    state: float64 [num_slots, H, dk, dv], updated IN PLACE.  Returns o [N, H, dv]."""
+    state: float64 [num_slots, H, dk, dv], updated IN PLACE; prep as in
+    kda_fwd.  Returns o [N, H, dv]."""
     q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -140,9 +168,16 @@ def kda_decode_step(q, k, v, g, beta, scale, state, slot_idx=None):
     num_slots = state.shape[0]
     si = None if slot_idx is None else np.ascontiguousarray(np.asarray(slot_idx, dtype=np.int32))
     o = np.zeros((N, H, dv), dtype=np.float64)
-    rc = _load().oracle_kda_decode_step(N, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
-                                        _ptr(g), _ptr(beta), _ptr(state), num_slots, _ptr(si),
-                                        _ptr(o))
+    if prep is not None:
+        flags, eps, a, b = _prep_args(prep, H, dk)
+        rc = _load().oracle_kda_decode_step_prep(N, H, dk, dv, float(scale), _ptr(q), _ptr(k),
+                                                 _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                                 num_slots, _ptr(si), flags, eps, _ptr(a),
+                                                 _ptr(b), _ptr(o))
+    else:
+        rc = _load().oracle_kda_decode_step(N, H, dk, dv, float(scale), _ptr(q), _ptr(k),
+                                            _ptr(v), _ptr(g), _ptr(beta), _ptr(state), num_slots,
+                                            _ptr(si), _ptr(o))
     if rc != 0:
         raise ValueError("oracle_kda_decode_step rejected its arguments (code %d)" % rc)
     return o

@@ -48,43 +48,101 @@
 #include <omp.h>
 #endif
 
-/* One token of the recurrence on state S (dk x dv, fp64).
+/* One token of the recurrence on state S (dk x dv, fp64), on fp64 token
+ * vectors q, k (dk), v (dv) and the log gate lg (dk).
  * drop_erase != 0 removes the k k^T (erase) term, leaving the plain additive
  * write S <- Diag(alpha) S + beta k v^T; it exists only so the tests can
  * reduce the oracle to textbook linear attention and is never used for
  * parity against the GPU path. */
-static void kda_token(int dk, int dv, double scale, const float *q,
-                      const float *k, const float *v, const float *g,
+static void kda_token(int dk, int dv, double scale, const double *q,
+                      const double *k, const float *v, const double *lg,
                       double beta, double *S, double *u, double *o,
                       int drop_erase)
 {
     for (int i = 0; i < dk; ++i) {
-        const double a = exp((double)g[i]);
+        const double a = exp(lg[i]);
         double *row = S + (size_t)i * dv;
         for (int j = 0; j < dv; ++j) row[j] *= a;
     }
     for (int j = 0; j < dv; ++j) u[j] = 0.0;
     if (!drop_erase) {
         for (int i = 0; i < dk; ++i) {
-            const double ki = (double)k[i];
+            const double ki = k[i];
             const double *row = S + (size_t)i * dv;
             for (int j = 0; j < dv; ++j) u[j] += row[j] * ki;
         }
     }
     for (int j = 0; j < dv; ++j) u[j] = beta * ((double)v[j] - u[j]);
     for (int i = 0; i < dk; ++i) {
-        const double ki = (double)k[i];
+        const double ki = k[i];
         double *row = S + (size_t)i * dv;
         for (int j = 0; j < dv; ++j) row[j] += ki * u[j];
     }
     if (o) {
         for (int j = 0; j < dv; ++j) o[j] = 0.0;
         for (int i = 0; i < dk; ++i) {
-            const double qi = (double)q[i];
+            const double qi = q[i];
             const double *row = S + (size_t)i * dv;
             for (int j = 0; j < dv; ++j) o[j] += row[j] * qi;
         }
         for (int j = 0; j < dv; ++j) o[j] *= scale;
+    }
+}
+
+/* Optional preparation of one token's inputs, as a model layer does before
+ * the operator (summary page, "Configuracion del modelo Kimi Linear": L2
+ * normalisation of queries and keys; a per-channel decay gate computed with a
+ * GDN/Mamba-style decay function).  The page names the decay function only
+ * by family; the form taken is the Mamba/GDN one, per key channel:
+ *     log alpha_c = -exp(A_log[h]) * softplus(g_c + dt_bias[h, c]).
+ * flags bit 0: q, k <- x / sqrt(sum x^2 + eps)      (L2 normalisation)
+ * flags bit 1: beta <- 1 / (1 + exp(-beta))         (beta given as a logit)
+ * A_log != NULL: g holds the gate pre-activation (dt_bias may be NULL = 0).
+ * Without any of these the values are passed through unchanged. */
+typedef struct {
+    int flags;
+    double eps;
+    const float *A_log;     /* [H] */
+    const float *dt_bias;   /* [H, dk] */
+} prep_t;
+
+static double softplus(double x)
+{
+    return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+}
+
+static void prepare_token(const prep_t *p, int h, int dk, const float *q,
+                          const float *k, const float *g, float beta,
+                          double *qd, double *kd, double *lg, double *bd)
+{
+    for (int i = 0; i < dk; ++i) {
+        qd[i] = (double)q[i];
+        kd[i] = (double)k[i];
+        lg[i] = (double)g[i];
+    }
+    *bd = (double)beta;
+    if (!p) return;
+    if (p->flags & 1) {
+        double sq = 0.0, sk = 0.0;
+        for (int i = 0; i < dk; ++i) {
+            sq += qd[i] * qd[i];
+            sk += kd[i] * kd[i];
+        }
+        /* a zero vector (with eps = 0) stays zero */
+        const double nq = sq + p->eps > 0.0 ? 1.0 / sqrt(sq + p->eps) : 0.0;
+        const double nk = sk + p->eps > 0.0 ? 1.0 / sqrt(sk + p->eps) : 0.0;
+        for (int i = 0; i < dk; ++i) {
+            qd[i] *= nq;
+            kd[i] *= nk;
+        }
+    }
+    if (p->flags & 2) *bd = 1.0 / (1.0 + exp(-*bd));
+    if (p->A_log) {
+        const double rate = exp((double)p->A_log[h]);
+        for (int i = 0; i < dk; ++i) {
+            const double bias = p->dt_bias ? (double)p->dt_bias[(size_t)h * dk + i] : 0.0;
+            lg[i] = -rate * softplus(lg[i] + bias);
+        }
     }
 }
 
@@ -97,13 +155,14 @@ int oracle_num_threads(void)
 #endif
 }
 
-/* Full forward over B rows (or N packed sequences).  Returns 0 on success,
- * nonzero on a malformed argument. */
-int oracle_kda_fwd(int B, int T, int H, int dk, int dv, double scale,
-                   const float *q, const float *k, const float *v,
-                   const float *g, const float *beta, const double *S0,
-                   const int32_t *cu_seqlens, int N, int drop_erase,
-                   double *o, double *S_final)
+/* Full forward over B rows (or N packed sequences), with optional input
+ * preparation (see prepare_token; prep == NULL passes inputs through).
+ * Returns 0 on success, nonzero on a malformed argument. */
+static int kda_fwd_impl(int B, int T, int H, int dk, int dv, double scale,
+                        const float *q, const float *k, const float *v,
+                        const float *g, const float *beta, const double *S0,
+                        const int32_t *cu_seqlens, int N, int drop_erase,
+                        const prep_t *prep, double *o, double *S_final)
 {
     if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return 1;
     if (cu_seqlens) {
@@ -121,7 +180,8 @@ int oracle_kda_fwd(int B, int T, int H, int dk, int dv, double scale,
     {
         double *S = (double *)malloc(sizeof(double) * (size_t)dk * dv);
         double *u = (double *)malloc(sizeof(double) * (size_t)dv);
-        if (!S || !u) {
+        double *tv = (double *)malloc(sizeof(double) * (size_t)dk * 3);
+        if (!S || !u || !tv) {
 #pragma omp atomic write
             err = 5;
         } else {
@@ -136,22 +196,47 @@ int oracle_kda_fwd(int B, int T, int H, int dk, int dv, double scale,
                 else memset(S, 0, sizeof(double) * (size_t)dk * dv);
                 for (long t = t0; t < t1; ++t) {
                     const size_t tok = (size_t)(base + t);
-                    kda_token(dk, dv, scale,
-                              q + tok * tok_k + (size_t)h * dk,
-                              k + tok * tok_k + (size_t)h * dk,
-                              v + tok * tok_v + (size_t)h * dv,
-                              g + tok * tok_k + (size_t)h * dk,
-                              (double)beta[tok * H + h], S, u,
-                              o ? o + tok * tok_v + (size_t)h * dv : NULL,
-                              drop_erase);
+                    double bd;
+                    prepare_token(prep, h, dk, q + tok * tok_k + (size_t)h * dk,
+                                  k + tok * tok_k + (size_t)h * dk,
+                                  g + tok * tok_k + (size_t)h * dk, beta[tok * H + h],
+                                  tv, tv + dk, tv + 2 * dk, &bd);
+                    kda_token(dk, dv, scale, tv, tv + dk, v + tok * tok_v + (size_t)h * dv,
+                              tv + 2 * dk, bd, S, u,
+                              o ? o + tok * tok_v + (size_t)h * dv : NULL, drop_erase);
                 }
                 if (S_final) memcpy(S_final + sidx, S, sizeof(double) * (size_t)dk * dv);
             }
         }
         free(S);
         free(u);
+        free(tv);
     }
     return err;
+}
+
+int oracle_kda_fwd(int B, int T, int H, int dk, int dv, double scale,
+                   const float *q, const float *k, const float *v,
+                   const float *g, const float *beta, const double *S0,
+                   const int32_t *cu_seqlens, int N, int drop_erase,
+                   double *o, double *S_final)
+{
+    return kda_fwd_impl(B, T, H, dk, dv, scale, q, k, v, g, beta, S0, cu_seqlens, N,
+                        drop_erase, NULL, o, S_final);
+}
+
+/* The forward with input preparation: flags, eps, A_log [H] or NULL,
+ * dt_bias [H, dk] or NULL (see prepare_token). */
+int oracle_kda_fwd_prep(int B, int T, int H, int dk, int dv, double scale,
+                        const float *q, const float *k, const float *v,
+                        const float *g, const float *beta, const double *S0,
+                        const int32_t *cu_seqlens, int N, int flags, double eps,
+                        const float *A_log, const float *dt_bias,
+                        double *o, double *S_final)
+{
+    prep_t p = {flags, eps, A_log, dt_bias};
+    return kda_fwd_impl(B, T, H, dk, dv, scale, q, k, v, g, beta, S0, cu_seqlens, N, 0,
+                        &p, o, S_final);
 }
 
 /* One decode step: the same token update applied once to each sequence's
@@ -159,10 +244,11 @@ int oracle_kda_fwd(int B, int T, int H, int dk, int dv, double scale,
  * sequence n uses slot slot_idx[n] (or n when slot_idx is NULL).  Sequences
  * whose slot is out of range are skipped and their output row is left as is.
  * q, k, g [N, H, dk]; v [N, H, dv]; beta [N, H]; o [N, H, dv] (fp64). */
-int oracle_kda_decode_step(int N, int H, int dk, int dv, double scale,
+static int kda_decode_impl(int N, int H, int dk, int dv, double scale,
                            const float *q, const float *k, const float *v,
                            const float *g, const float *beta, double *state,
-                           int num_slots, const int32_t *slot_idx, double *o)
+                           int num_slots, const int32_t *slot_idx,
+                           const prep_t *prep, double *o)
 {
     if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || num_slots < 0) return 1;
     if (!slot_idx && N > num_slots) return 2;
@@ -171,7 +257,8 @@ int oracle_kda_decode_step(int N, int H, int dk, int dv, double scale,
 #pragma omp parallel
     {
         double *u = (double *)malloc(sizeof(double) * (size_t)dv);
-        if (!u) {
+        double *tv = (double *)malloc(sizeof(double) * (size_t)dk * 3);
+        if (!u || !tv) {
 #pragma omp atomic write
             err = 5;
         } else {
@@ -182,11 +269,36 @@ int oracle_kda_decode_step(int N, int H, int dk, int dv, double scale,
                 if (slot < 0 || slot >= num_slots) continue;
                 double *S = state + ((size_t)slot * H + h) * (size_t)dk * dv;
                 const size_t r = (size_t)n * H + h;
-                kda_token(dk, dv, scale, q + r * dk, k + r * dk, v + r * dv,
-                          g + r * dk, (double)beta[r], S, u, o + r * dv, 0);
+                double bd;
+                prepare_token(prep, h, dk, q + r * dk, k + r * dk, g + r * dk, beta[r], tv,
+                              tv + dk, tv + 2 * dk, &bd);
+                kda_token(dk, dv, scale, tv, tv + dk, v + r * dv, tv + 2 * dk, bd, S, u,
+                          o + r * dv, 0);
             }
         }
         free(u);
+        free(tv);
     }
     return err;
+}
+
+int oracle_kda_decode_step(int N, int H, int dk, int dv, double scale,
+                           const float *q, const float *k, const float *v,
+                           const float *g, const float *beta, double *state,
+                           int num_slots, const int32_t *slot_idx, double *o)
+{
+    return kda_decode_impl(N, H, dk, dv, scale, q, k, v, g, beta, state, num_slots,
+                           slot_idx, NULL, o);
+}
+
+int oracle_kda_decode_step_prep(int N, int H, int dk, int dv, double scale,
+                                const float *q, const float *k, const float *v,
+                                const float *g, const float *beta, double *state,
+                                int num_slots, const int32_t *slot_idx, int flags,
+                                double eps, const float *A_log, const float *dt_bias,
+                                double *o)
+{
+    prep_t p = {flags, eps, A_log, dt_bias};
+    return kda_decode_impl(N, H, dk, dv, scale, q, k, v, g, beta, state, num_slots,
+                           slot_idx, &p, o);
 }
