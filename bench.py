@@ -207,15 +207,22 @@ def bench_prefill(kda, kda_inputs, steps, warmup, stream):
     return dict(ms=ms, tokens=B * T, token_heads=B * T * H, inputs=d)
 
 
-def bench_prefill_prep(kda, kda_inputs, steps, warmup, stream):
+def bench_prefill_prep(kda, kda_inputs, steps, warmup, stream, with_epilogue=False):
     """The prefill layer on raw inputs with the in-kernel preparation (q/k L2
-    normalisation, beta from logits, gate activation) -- kda_chunk_fwd_prep."""
+    normalisation, beta from logits, gate activation) and optionally the
+    output epilogue (per-head RMSNorm, weight, sigmoid gate) --
+    kda_chunk_fwd_ex."""
     c = kda_inputs.CONFIGS[2]
     B, T, H, D, C = c["B"], c["T"], c["H"], c["dk"], c["chunk"]
     d = kda_inputs.raw_layer_inputs(kda_inputs.CFG_SEED[2] + 50, B, T, H, D, D, torch.bfloat16,
                                     "cuda")
     prep = dict(normalize_qk=True, eps=1e-6, beta_logit=True, A_log=d["A_log"],
                 dt_bias=d["dt_bias"])
+    epi = None
+    if with_epilogue:
+        gen = torch.Generator(device="cuda").manual_seed(kda_inputs.CFG_SEED[2] + 51)
+        epi = dict(eps=1e-6, weight=0.5 + torch.rand(D, device="cuda", generator=gen),
+                   gate=torch.randn(B, T, H, D, device="cuda", generator=gen).to(torch.bfloat16))
     o = torch.empty(B, T, H, D, device="cuda")
     S = torch.empty(B, H, D, D, device="cuda")
     ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(B, T, H, D, D, C), dtype=torch.uint8,
@@ -223,7 +230,7 @@ def bench_prefill_prep(kda, kda_inputs, steps, warmup, stream):
 
     def call():
         kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=C, o=o,
-                          final_state=S, workspace=ws, stream=stream, prep=prep)
+                          final_state=S, workspace=ws, stream=stream, prep=prep, epilogue=epi)
 
     for _ in range(warmup):
         call()
@@ -279,27 +286,32 @@ def decode_run(kda, cache, steps, o, stream):
 
 
 def bench_decode_prep(kda, kda_inputs, cache, n_steps, stream):
-    """Decode steps on raw inputs with the in-kernel preparation, continuing
-    from the benchmark's cache."""
+    """Decode steps on raw inputs with the in-kernel preparation and the fused
+    output epilogue, continuing from the benchmark's cache."""
     N, H, D = cache.shape[0], cache.shape[1], cache.shape[2]
     xs = [kda_inputs.raw_layer_inputs(kda_inputs.CFG_SEED[4] * 7 + s, 1, N, H, D, D,
                                       torch.bfloat16, "cuda") for s in range(16)]
     xs = [{k: (v[0].contiguous() if v.dim() >= 3 else v) for k, v in x.items()} for x in xs]
     o = torch.empty(N, H, D, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(kda_inputs.CFG_SEED[4] * 7 + 99)
+    w = 0.5 + torch.rand(D, device="cuda", generator=gen)
+    zs = [torch.randn(N, H, D, device="cuda", generator=gen).to(torch.bfloat16)
+          for _ in range(16)]
 
-    def step(x):
+    def step(x, z):
         kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], cache, o=o,
                             stream=stream, prep=dict(normalize_qk=True, eps=1e-6,
                                                      beta_logit=True, A_log=x["A_log"],
-                                                     dt_bias=x["dt_bias"]))
+                                                     dt_bias=x["dt_bias"]),
+                            epilogue=dict(eps=1e-6, weight=w, gate=z))
 
     for s in range(4):
-        step(xs[s])
+        step(xs[s], zs[s])
     torch.cuda.synchronize()
     tm = StreamTimer(stream)
     tm.start()
     for s in range(n_steps):
-        step(xs[s % 16])
+        step(xs[s % 16], zs[s % 16])
     ms = tm.stop() / n_steps
     torch.cuda.synchronize()
     return ms
@@ -398,6 +410,9 @@ def main():
     print("prefill %.4f ms/call" % pf["ms"], file=sys.stderr, flush=True)
     pf_prep_ms = bench_prefill_prep(kda, kda_inputs, args.steps, args.warmup, stream)
     print("prefill with preparation %.4f ms/call" % pf_prep_ms, file=sys.stderr, flush=True)
+    pf_full_ms = bench_prefill_prep(kda, kda_inputs, args.steps, args.warmup, stream, True)
+    print("prefill with preparation and epilogue %.4f ms/call" % pf_full_ms, file=sys.stderr,
+          flush=True)
     th = pf["token_heads"]
     pf_bytes = PREFILL_BYTES_PER_TOKEN_HEAD * th
     pf_flops = prefill_flops_per_token_head() * th
@@ -429,7 +444,8 @@ def main():
             ms_per_step=dc["ms_prep"], value=dc["N"] / (dc["ms_prep"] / 1e3), unit="tokens/s",
             steps=128, hbm_frac=db / (dc["ms_prep"] / 1e3) / 1e9 / HBM_PEAK_GBS,
             workload="same cache; raw q/k, beta logits and gate pre-activations prepared "
-                     "in the kernel (kda_decode_step_prep)")
+                     "in the kernel, output RMSNorm + sigmoid gate fused "
+                     "(kda_decode_step_ex)")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -461,7 +477,12 @@ def main():
             overhead=pf_prep_ms / pf["ms"] - 1.0,
             hbm_frac=pf_bytes / (pf_prep_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
             workload="same layer on raw inputs: q/k L2-normalised, beta from logits and the "
-                     "gate activated inside the kernels (kda_chunk_fwd_prep)"),
+                     "gate activated inside the kernels (kda_chunk_fwd_ex)"),
+        "prefill_with_preparation_and_epilogue": dict(
+            ms_per_step=pf_full_ms, value=pf["tokens"] / (pf_full_ms / 1e3), unit="tokens/s",
+            overhead=pf_full_ms / pf["ms"] - 1.0,
+            workload="as above plus the output epilogue (per-head RMSNorm, weight, sigmoid "
+                     "gate; one extra pass over o inside the call)"),
         "cpu_baseline": cpu,
         "decode": dec,
     }

@@ -94,6 +94,28 @@ typedef struct {
     const float *dt_bias;
 } kda_prep;
 
+/* Optional output epilogue done inside the library -- what a Kimi Linear
+ * layer applies to the operator's output before its output projection (same
+ * page, "Configuracion del modelo Kimi Linear": per-head RMSNorm and a
+ * data-dependent output gate).  The page does not name the gate's activation;
+ * the sigmoid is used.  Every output row (one token, one head, dv values) is
+ * replaced by
+ *     y_j = o_j / sqrt(mean_j o_j^2 + eps) * weight_j * sigmoid(gate_j).
+ *
+ *   eps      >= 0.
+ *   weight   device pointer to [dv] fp32 shared by all heads, or NULL (= 1).
+ *   gate     device pointer to the gate logits, laid out like o ([B, T, H, dv]
+ *            for the prefill, [N, H, dv] for decode) in qkv_dtype, or NULL
+ *            (no gate).
+ * The decode step applies it in the same kernel; the prefill applies it in
+ * one extra pass over o inside the same call (an output row is spread over
+ * several workgroups of the chain kernel). */
+typedef struct {
+    float eps;
+    const float *weight;
+    const void *gate;
+} kda_epilogue;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *kda_status_string(kda_status s);
 
@@ -144,20 +166,22 @@ kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk,
                          void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
-/* kda_chunk_fwd with the optional input preparation above applied inside the
- * kernels (prep may be NULL).  Same arguments, layouts, workspace and errors
- * as kda_chunk_fwd; additionally KDA_ERR_NULL_ARG when prep->dt_bias is given
- * without prep->A_log or a prep pointer is not 4-byte aligned, and
- * KDA_ERR_BAD_SHAPE when prep->qk_eps is negative or not finite. */
-kda_status kda_chunk_fwd_prep(int B, int T, int H, int dk, int dv, int chunk,
-                              float scale, kda_dtype qkv_dtype,
-                              const void *q, const void *k, const void *v,
-                              const float *g, const float *beta,
-                              const float *initial_state,
-                              const int32_t *cu_seqlens, int num_seqs,
-                              float *o, float *final_state,
-                              void *workspace, size_t workspace_bytes,
-                              const kda_prep *prep, hipStream_t stream);
+/* kda_chunk_fwd with the optional input preparation and output epilogue
+ * above (either pointer may be NULL).  Same arguments, layouts, workspace and
+ * errors as kda_chunk_fwd; additionally KDA_ERR_NULL_ARG when prep->dt_bias is
+ * given without prep->A_log or a prep/epilogue pointer is misaligned (4 bytes
+ * for A_log, dt_bias, weight; 16 bytes for gate), and KDA_ERR_BAD_SHAPE when
+ * an eps is negative or not finite. */
+kda_status kda_chunk_fwd_ex(int B, int T, int H, int dk, int dv, int chunk,
+                            float scale, kda_dtype qkv_dtype,
+                            const void *q, const void *k, const void *v,
+                            const float *g, const float *beta,
+                            const float *initial_state,
+                            const int32_t *cu_seqlens, int num_seqs,
+                            float *o, float *final_state,
+                            void *workspace, size_t workspace_bytes,
+                            const kda_prep *prep, const kda_epilogue *epilogue,
+                            hipStream_t stream);
 
 /* One recurrent decode step for N sequences against a state cache.
  *
@@ -183,15 +207,16 @@ kda_status kda_decode_step(int N, int H, int dk, int dv, float scale,
                            const int32_t *slot_idx, float *o,
                            hipStream_t stream);
 
-/* kda_decode_step with the optional input preparation above (prep may be
- * NULL); errors as for kda_chunk_fwd_prep. */
-kda_status kda_decode_step_prep(int N, int H, int dk, int dv, float scale,
-                                kda_dtype qkv_dtype,
-                                const void *q, const void *k, const void *v,
-                                const float *g, const float *beta,
-                                float *state_cache, int num_slots,
-                                const int32_t *slot_idx, float *o,
-                                const kda_prep *prep, hipStream_t stream);
+/* kda_decode_step with the optional input preparation and output epilogue
+ * (either pointer may be NULL); errors as for kda_chunk_fwd_ex. */
+kda_status kda_decode_step_ex(int N, int H, int dk, int dv, float scale,
+                              kda_dtype qkv_dtype,
+                              const void *q, const void *k, const void *v,
+                              const float *g, const float *beta,
+                              float *state_cache, int num_slots,
+                              const int32_t *slot_idx, float *o,
+                              const kda_prep *prep, const kda_epilogue *epilogue,
+                              hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -33,18 +33,24 @@ class KdaPrep(ctypes.Structure):
                 ("dt_bias", ctypes.c_void_p)]
 
 
+class KdaEpilogue(ctypes.Structure):
+    """kda_epilogue of include/kda.h."""
+    _fields_ = [("eps", ctypes.c_float), ("weight", ctypes.c_void_p), ("gate", ctypes.c_void_p)]
+
+
 _PREP = ctypes.POINTER(KdaPrep)
+_EPI = ctypes.POINTER(KdaEpilogue)
 SIGNATURES = {
     "kda_status_string": (ctypes.c_char_p, [_I]),
     "kda_version": (_I, []),
     "kda_chunk_fwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "kda_chunk_fwd": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                            _P, _P, _P, _SZ, _P]),
-    "kda_chunk_fwd_prep": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
-                                _P, _P, _P, _SZ, _PREP, _P]),
+    "kda_chunk_fwd_ex": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
+                              _P, _P, _P, _SZ, _PREP, _EPI, _P]),
     "kda_decode_step": (_I, [_I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P]),
-    "kda_decode_step_prep": (_I, [_I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P,
-                                  _PREP, _P]),
+    "kda_decode_step_ex": (_I, [_I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                _PREP, _EPI, _P]),
 }
 
 _lib = None
@@ -128,6 +134,25 @@ def make_prep(prep, H, dk, device):
     return st, (a, b)
 
 
+def make_epilogue(epilogue, dv, o_shape, qkv_dtype, device):
+    """kda_epilogue from a dict: eps (float, default 1e-6), weight ([dv] fp32
+    tensor or None), gate (tensor shaped like o in the q/k/v dtype, or None).
+    Returns (struct or None, tensors to keep alive)."""
+    if epilogue is None:
+        return None, ()
+    w = epilogue.get("weight")
+    z = epilogue.get("gate")
+    _check(w, "weight", torch.float32, device)
+    _check(z, "gate", qkv_dtype, device)
+    if w is not None and w.numel() != dv:
+        raise ValueError("weight must hold dv values")
+    if z is not None and tuple(z.shape) != tuple(o_shape):
+        raise ValueError("gate must be shaped like o")
+    st = KdaEpilogue(float(epilogue.get("eps", 1e-6)), None if w is None else w.data_ptr(),
+                     None if z is None else z.data_ptr())
+    return st, (w, z)
+
+
 def kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torch.bfloat16):
     code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
     return int(load_library().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs,
@@ -136,14 +161,16 @@ def kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torc
 
 def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu_seqlens=None,
                   output_final_state=True, o=None, final_state=None, workspace=None,
-                  stream=None, prep=None):
+                  stream=None, prep=None, epilogue=None):
     """Chunkwise KDA prefill.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32); g: [B, T, H, dk] fp32
     (log gate); beta: [B, T, H] fp32; initial_state: [N, H, dk, dv] fp32 or
     None; cu_seqlens: int32 [N + 1] (B must be 1) or None; prep: optional
-    in-kernel input preparation (see make_prep; calls kda_chunk_fwd_prep).
-    Returns (o [B, T, H, dv] fp32, final_state [N, H, dk, dv] fp32 or None).
+    in-kernel input preparation (see make_prep); epilogue: optional output
+    RMSNorm + gate (see make_epilogue).  With either, kda_chunk_fwd_ex is
+    called.  Returns (o [B, T, H, dv] fp32, final_state [N, H, dk, dv] fp32 or
+    None).
     """
     lib = load_library()
     B, T, H, dk = q.shape
@@ -171,23 +198,26 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu
             _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
             N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), _ptr(workspace),
             workspace.numel())
-    if prep is None:
+    if prep is None and epilogue is None:
         rc = lib.kda_chunk_fwd(*args, _stream(stream))
         fn = "kda_chunk_fwd"
     else:
         st, _keep = make_prep(prep, H, dk, dev)
-        rc = lib.kda_chunk_fwd_prep(*args, ctypes.byref(st), _stream(stream))
-        fn = "kda_chunk_fwd_prep"
+        et, _keep2 = make_epilogue(epilogue, dv, (B, T, H, dv), q.dtype, dev)
+        rc = lib.kda_chunk_fwd_ex(*args, None if st is None else ctypes.byref(st),
+                                  None if et is None else ctypes.byref(et), _stream(stream))
+        fn = "kda_chunk_fwd_ex"
     if rc != KDA_OK:
         raise KDAError(fn, rc)
     return o, final_state
 
 
 def kda_decode_step(q, k, v, g, beta, state_cache, scale=None, slot_idx=None, o=None,
-                    stream=None, prep=None):
+                    stream=None, prep=None, epilogue=None):
     """One decode step.  q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H];
     state_cache: [num_slots, H, dk, dv] fp32, updated in place; slot_idx:
-    int32 [N] or None; prep as in kda_chunk_fwd.  Returns o [N, H, dv] fp32."""
+    int32 [N] or None; prep and epilogue as in kda_chunk_fwd.  Returns
+    o [N, H, dv] fp32."""
     lib = load_library()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -204,13 +234,15 @@ def kda_decode_step(q, k, v, g, beta, state_cache, scale=None, slot_idx=None, o=
         o = torch.empty(N, H, dv, dtype=torch.float32, device=dev)
     args = (N, H, dk, dv, float(scale), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
             _ptr(beta), _ptr(state_cache), state_cache.shape[0], _ptr(slot_idx), _ptr(o))
-    if prep is None:
+    if prep is None and epilogue is None:
         rc = lib.kda_decode_step(*args, _stream(stream))
         fn = "kda_decode_step"
     else:
         st, _keep = make_prep(prep, H, dk, dev)
-        rc = lib.kda_decode_step_prep(*args, ctypes.byref(st), _stream(stream))
-        fn = "kda_decode_step_prep"
+        et, _keep2 = make_epilogue(epilogue, dv, (N, H, dv), q.dtype, dev)
+        rc = lib.kda_decode_step_ex(*args, None if st is None else ctypes.byref(st),
+                                    None if et is None else ctypes.byref(et), _stream(stream))
+        fn = "kda_decode_step_ex"
     if rc != KDA_OK:
         raise KDAError(fn, rc)
     return o

@@ -35,6 +35,20 @@ kda_status read_prep(const kda_prep* p, kda::Prep* out) {
     return KDA_OK;
 }
 
+// Validates a kda_epilogue and converts it; NULL means none.
+kda_status read_epilogue(const kda_epilogue* e, kda::Epilogue* out) {
+    *out = kda::Epilogue();
+    if (!e) return KDA_OK;
+    if ((e->weight && !aligned4(e->weight)) || (e->gate && !aligned16(e->gate)))
+        return KDA_ERR_NULL_ARG;
+    if (!(e->eps >= 0.f) || !isfinite(e->eps)) return KDA_ERR_BAD_SHAPE;
+    out->on = true;
+    out->eps = e->eps;
+    out->weight = e->weight;
+    out->gate = e->gate;
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -68,16 +82,18 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
     return plan.total;
 }
 
-kda_status kda_chunk_fwd_prep(int B, int T, int H, int dk, int dv, int chunk, float scale,
-                              kda_dtype qkv_dtype, const void* q, const void* k,
-                              const void* v, const float* g, const float* beta,
-                              const float* initial_state, const int32_t* cu_seqlens,
-                              int num_seqs, float* o, float* final_state, void* workspace,
-                              size_t workspace_bytes, const kda_prep* prep,
-                              hipStream_t stream) {
+kda_status kda_chunk_fwd_ex(int B, int T, int H, int dk, int dv, int chunk, float scale,
+                            kda_dtype qkv_dtype, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, const float* initial_state,
+                            const int32_t* cu_seqlens, int num_seqs, float* o,
+                            float* final_state, void* workspace, size_t workspace_bytes,
+                            const kda_prep* prep, const kda_epilogue* epilogue,
+                            hipStream_t stream) {
     if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_BAD_SHAPE;
     kda::Prep pr;
     if (kda_status e = read_prep(prep, &pr)) return e;
+    kda::Epilogue ep;
+    if (kda_status e = read_epilogue(epilogue, &ep)) return e;
     const bool varlen = cu_seqlens != nullptr;
     if (varlen && (B != 1 || num_seqs < 1)) return KDA_ERR_BAD_SHAPE;
     const int N = varlen ? num_seqs : B;
@@ -112,6 +128,7 @@ kda_status kda_chunk_fwd_prep(int B, int T, int H, int dk, int dv, int chunk, fl
     a.o = o; a.sT = final_state;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.prep = pr;
+    a.epi = ep;
     a.stream = stream;
     return from_hip(kda::launch_prefill(a, plan));
 }
@@ -121,19 +138,21 @@ kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk, float s
                          const float* g, const float* beta, const float* initial_state,
                          const int32_t* cu_seqlens, int num_seqs, float* o, float* final_state,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return kda_chunk_fwd_prep(B, T, H, dk, dv, chunk, scale, qkv_dtype, q, k, v, g, beta,
-                              initial_state, cu_seqlens, num_seqs, o, final_state, workspace,
-                              workspace_bytes, nullptr, stream);
+    return kda_chunk_fwd_ex(B, T, H, dk, dv, chunk, scale, qkv_dtype, q, k, v, g, beta,
+                            initial_state, cu_seqlens, num_seqs, o, final_state, workspace,
+                            workspace_bytes, nullptr, nullptr, stream);
 }
 
-kda_status kda_decode_step_prep(int N, int H, int dk, int dv, float scale,
-                                kda_dtype qkv_dtype, const void* q, const void* k,
-                                const void* v, const float* g, const float* beta,
-                                float* state_cache, int num_slots, const int32_t* slot_idx,
-                                float* o, const kda_prep* prep, hipStream_t stream) {
+kda_status kda_decode_step_ex(int N, int H, int dk, int dv, float scale, kda_dtype qkv_dtype,
+                              const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, float* state_cache, int num_slots,
+                              const int32_t* slot_idx, float* o, const kda_prep* prep,
+                              const kda_epilogue* epilogue, hipStream_t stream) {
     if (N < 0 || H < 1 || dk < 1 || dv < 1 || num_slots < 0) return KDA_ERR_BAD_SHAPE;
     kda::Prep pr;
     if (kda_status e = read_prep(prep, &pr)) return e;
+    kda::Epilogue ep;
+    if (kda_status e = read_epilogue(epilogue, &ep)) return e;
     if (!slot_idx && N > num_slots) return KDA_ERR_BAD_SHAPE;
     if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
     if (dk != dv || !supported_dim(dk)) return KDA_ERR_UNSUPPORTED;
@@ -151,6 +170,7 @@ kda_status kda_decode_step_prep(int N, int H, int dk, int dv, float scale,
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.state = state_cache; a.num_slots = num_slots; a.slot_idx = slot_idx; a.o = o;
     a.prep = pr;
+    a.epi = ep;
     a.stream = stream;
     return from_hip(kda::launch_decode(a));
 }
@@ -159,8 +179,8 @@ kda_status kda_decode_step(int N, int H, int dk, int dv, float scale, kda_dtype 
                            const void* q, const void* k, const void* v, const float* g,
                            const float* beta, float* state_cache, int num_slots,
                            const int32_t* slot_idx, float* o, hipStream_t stream) {
-    return kda_decode_step_prep(N, H, dk, dv, scale, qkv_dtype, q, k, v, g, beta, state_cache,
-                                num_slots, slot_idx, o, nullptr, stream);
+    return kda_decode_step_ex(N, H, dk, dv, scale, qkv_dtype, q, k, v, g, beta, state_cache,
+                              num_slots, slot_idx, o, nullptr, nullptr, stream);
 }
 
 }  // extern "C"

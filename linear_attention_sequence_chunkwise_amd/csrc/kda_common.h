@@ -49,6 +49,28 @@ __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + exp_e(
 // 1 / sqrt(s) for s > 0 and 0 for s == 0, so that a zero vector stays zero.
 __device__ __forceinline__ float rnorm(float s) { return s > 0.f ? rsqrtf(s) : 0.f; }
 
+// Lane permute within rows of 16 lanes (DPP), every lane active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of W lanes (W a power of two, 2..64): pairs, quads,
+// half rows and rows through DPP (after the quad steps every lane of a quad
+// holds the quad sum, so the mirror permutes pair equal partial sums), then
+// cross-row steps through lane shuffles.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(W >= 2 && W <= 64 && (W & (W - 1)) == 0, "bad group");
+    x += dpp_f<0xB1>(x);                     // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (W >= 4) x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (W >= 8) x += dpp_f<0x141>(x);  // row_half_mirror
+    if constexpr (W >= 16) x += dpp_f<0x140>(x); // row_mirror
+    if constexpr (W >= 32) x += __shfl_xor(x, 16);
+    if constexpr (W >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
 // Load 4 consecutive input elements (bf16 or fp32) as floats.
 __device__ __forceinline__ float4v load4(const float* p) {
     return *reinterpret_cast<const float4v*>(p);

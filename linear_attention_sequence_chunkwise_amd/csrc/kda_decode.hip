@@ -39,12 +39,14 @@ __device__ __forceinline__ void st_state(float* p, float4v x) {
 // PREP: apply the optional input preparation (kda_prep).  The L2 norms of k
 // and q are folded in after the reductions: u = |k|^-1 S'^T k,
 // p = |q|^-1 S'^T q, and the rank-1 update uses |k|^-1 e.
-template <int D, typename IT, int NTH, bool NT, bool PREP>
+// EPI: replace the output row by the epilogue (kda_epilogue) of it: RMSNorm
+// over the row, weight, sigmoid gate.
+template <int D, typename IT, int NTH, bool NT, bool PREP, bool EPI>
 __global__ __launch_bounds__(NTH) void decode_step_kernel(
     int H, float scale, const IT* __restrict__ q, const IT* __restrict__ k,
     const IT* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
     float* __restrict__ state, int num_slots, const int32_t* __restrict__ slot_idx,
-    float* __restrict__ o, Prep prep) {
+    float* __restrict__ o, Prep prep, Epilogue epi) {
     constexpr int CG = D / 4;        // float4 column groups
     constexpr int RG = NTH / CG;     // row groups
     constexpr int RPT = D / RG;      // rows per thread
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(
     const int slot = slot_idx ? slot_idx[n] : n;
     if (slot < 0 || slot >= num_slots) return;   // whole workgroup leaves together
 
-    __shared__ float s_k[D], s_q[D], s_a[D], s_e[D];
+    __shared__ float s_k[D], s_q[D], s_a[D], s_e[D], s_o[EPI ? D : 1];
     __shared__ float s_red[2][RG][D];
     __shared__ float s_kq[4];
 
@@ -152,7 +154,8 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(
         const float e = b * (vv - u);
         if constexpr (PREP) s_e[tid] = e * s_kq[1];
         else s_e[tid] = e;
-        o[tok * D + tid] = scale * (p + s_kq[0] * e);
+        if constexpr (EPI) s_o[tid] = scale * (p + s_kq[0] * e);
+        else o[tok * D + tid] = scale * (p + s_kq[0] * e);
     }
     lds_barrier();
 
@@ -163,19 +166,37 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(
         s[i] += s_k[r] * e4;
         st_state<NT>(S + (size_t)r * D + 4 * cg, s[i]);
     }
+    if constexpr (EPI) {
+        // mean square of the output row by wavefront 0, then the row
+        if (tid < 64) {
+            float t = 0.f;
+            for (int i = tid; i < D; i += 64) t += s_o[i] * s_o[i];
+            t = group_sum<64>(t);
+            if (tid == 0) s_kq[3] = rnorm(t * (1.f / D) + epi.eps);
+        }
+        lds_barrier();
+        if (tid < D) {
+            float y = s_o[tid] * s_kq[3];
+            if (epi.weight) y *= epi.weight[tid];
+            if (epi.gate) y *= sigmoid_f(to_f32(reinterpret_cast<const IT*>(epi.gate)[tok * D + tid]));
+            o[tok * D + tid] = y;
+        }
+    }
 }
 
 template <int D, typename IT, int NTH, bool NT>
 static hipError_t launch_decode_v(const DecodeArgs& a) {
     dim3 grid((unsigned)(a.N * a.H)), block(NTH);
-    if (a.prep.active())
-        hipLaunchKernelGGL((decode_step_kernel<D, IT, NTH, NT, true>), grid, block, 0, a.stream,
-                           a.H, a.scale, (const IT*)a.q, (const IT*)a.k, (const IT*)a.v, a.g,
-                           a.beta, a.state, a.num_slots, a.slot_idx, a.o, a.prep);
-    else
-        hipLaunchKernelGGL((decode_step_kernel<D, IT, NTH, NT, false>), grid, block, 0, a.stream,
-                           a.H, a.scale, (const IT*)a.q, (const IT*)a.k, (const IT*)a.v, a.g,
-                           a.beta, a.state, a.num_slots, a.slot_idx, a.o, a.prep);
+#define KDA_DECODE_LAUNCH(P, E)                                                           \
+    hipLaunchKernelGGL((decode_step_kernel<D, IT, NTH, NT, P, E>), grid, block, 0, a.stream, \
+                       a.H, a.scale, (const IT*)a.q, (const IT*)a.k, (const IT*)a.v, a.g,   \
+                       a.beta, a.state, a.num_slots, a.slot_idx, a.o, a.prep, a.epi)
+    const bool p = a.prep.active(), e = a.epi.on;
+    if (p && e) KDA_DECODE_LAUNCH(true, true);
+    else if (p) KDA_DECODE_LAUNCH(true, false);
+    else if (e) KDA_DECODE_LAUNCH(false, true);
+    else KDA_DECODE_LAUNCH(false, false);
+#undef KDA_DECODE_LAUNCH
     return hipGetLastError();
 }
 

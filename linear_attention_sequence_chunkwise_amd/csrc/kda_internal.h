@@ -19,6 +19,14 @@ struct Prep {
     bool active() const { return normalize || beta_logit || A_log != nullptr; }
 };
 
+// Output epilogue (see kda_epilogue in kda.h).
+struct Epilogue {
+    bool on = false;
+    float eps = 0.f;
+    const float* weight = nullptr;
+    const void* gate = nullptr;
+};
+
 struct DecodeArgs {
     int N, H, D;
     float scale;
@@ -30,6 +38,7 @@ struct DecodeArgs {
     const int32_t* slot_idx;
     float* o;
     Prep prep;
+    Epilogue epi;
     hipStream_t stream;
 };
 
@@ -47,6 +56,7 @@ struct PrefillArgs {
     void* workspace;
     size_t workspace_bytes;
     Prep prep;
+    Epilogue epi;
     hipStream_t stream;
 };
 

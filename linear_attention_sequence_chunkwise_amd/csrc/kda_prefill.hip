@@ -320,28 +320,6 @@ __device__ __forceinline__ float4v mma16(float4v acc, const XT* x, int ldx, cons
     }
 }
 
-// Lane permute within rows of 16 lanes (DPP), every lane active.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-// Sum over aligned groups of W lanes (W a power of two, 2..64): pairs, quads,
-// half rows and rows through DPP (after the quad steps every lane of a quad
-// holds the quad sum, so the mirror permutes pair equal partial sums), then
-// cross-row steps through lane shuffles.
-template <int W>
-__device__ __forceinline__ float group_sum(float x) {
-    static_assert(W >= 2 && W <= 64 && (W & (W - 1)) == 0, "bad group");
-    x += dpp_f<0xB1>(x);                     // quad_perm [1,0,3,2]: lane ^ 1
-    if constexpr (W >= 4) x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
-    if constexpr (W >= 8) x += dpp_f<0x141>(x);  // row_half_mirror
-    if constexpr (W >= 16) x += dpp_f<0x140>(x); // row_mirror
-    if constexpr (W >= 32) x += __shfl_xor(x, 16);
-    if constexpr (W >= 64) x += __shfl_xor(x, 32);
-    return x;
-}
-
 // PREP: apply the optional input preparation (kda_prep) while loading.
 template <int D, int C, typename OT, typename IT, bool PREP>
 __global__ __launch_bounds__(256) void kda_intra(
@@ -1169,6 +1147,49 @@ __global__ __launch_bounds__(64 * (BV / 4 + NP)) void kda_inter_dma(
 }
 
 // ---------------------------------------------------------------------------
+// K4: output epilogue over finished output rows (per-head RMSNorm, weight,
+// sigmoid output gate), in place.  An output row is written in dv-slices by
+// several chain workgroups, so the row norm is taken in this one extra pass.
+// D/4 lanes hold one row (a float4 each); rows are grid-strided.
+// ---------------------------------------------------------------------------
+template <int D, typename IT>
+__global__ __launch_bounds__(256) void kda_epilogue_rows(long long rows, float* __restrict__ o,
+                                                         const IT* __restrict__ gate,
+                                                         const float* __restrict__ weight,
+                                                         float eps) {
+    constexpr int LPR = D / 4;                 // lanes per row
+    constexpr int RPB = 256 / LPR;             // rows per workgroup pass
+    const int lr = threadIdx.x / LPR, lc = threadIdx.x % LPR;
+    float4v w = {1.f, 1.f, 1.f, 1.f};
+    if (weight) w = *reinterpret_cast<const float4v*>(weight + 4 * lc);
+    for (long long r = (long long)blockIdx.x * RPB + lr; r < rows;
+         r += (long long)gridDim.x * RPB) {
+        float* row = o + r * D + 4 * lc;
+        float4v x = *reinterpret_cast<const float4v*>(row);
+        const float ms = group_sum<LPR>(x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]);
+        float4v y = x * (rnorm(ms * (1.f / D) + eps)) * w;
+        if (gate) {
+            const float4v z = load4(gate + r * D + 4 * lc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] *= sigmoid_f(z[j]);
+        }
+        *reinterpret_cast<float4v*>(row) = y;
+    }
+}
+
+template <int D, typename IT>
+static hipError_t launch_epilogue(const PrefillArgs& a) {
+    const long long rows = (long long)a.B * a.T * a.H;
+    if (rows == 0) return hipSuccess;
+    constexpr int RPB = 256 / (D / 4);
+    const long long need = (rows + RPB - 1) / RPB;
+    const unsigned grid = (unsigned)(need < 4096 ? need : 4096);
+    hipLaunchKernelGGL((kda_epilogue_rows<D, IT>), dim3(grid), dim3(256), 0, a.stream, rows, a.o,
+                       (const IT*)a.epi.gate, a.epi.weight, a.epi.eps);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Host side: planning and dispatch.
 // ---------------------------------------------------------------------------
 constexpr size_t kLdsLimit = 160 * 1024;
@@ -1329,12 +1350,15 @@ static hipError_t launch_dc(const PrefillArgs& a, const PrefillPlan& plan) {
 
 template <int D, typename OT, typename IT>
 static hipError_t launch_d(const PrefillArgs& a, const PrefillPlan& plan) {
+    hipError_t e;
     switch (a.C) {
-        case 16: return launch_dc<D, 16, OT, IT>(a, plan);
-        case 32: return launch_dc<D, 32, OT, IT>(a, plan);
-        case 64: return launch_dc<D, 64, OT, IT>(a, plan);
+        case 16: e = launch_dc<D, 16, OT, IT>(a, plan); break;
+        case 32: e = launch_dc<D, 32, OT, IT>(a, plan); break;
+        case 64: e = launch_dc<D, 64, OT, IT>(a, plan); break;
         default: return hipErrorInvalidValue;
     }
+    if (e != hipSuccess || !a.epi.on) return e;
+    return launch_epilogue<D, IT>(a);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan) {

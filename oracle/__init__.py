@@ -72,12 +72,12 @@ def _load():
         lib.oracle_kda_fwd.restype = I
         lib.oracle_kda_decode_step.argtypes = [I, I, I, I, D, P, P, P, P, P, P, I, P, P]
         lib.oracle_kda_decode_step.restype = I
-        lib.oracle_kda_fwd_prep.argtypes = [I, I, I, I, I, D, P, P, P, P, P, P, P, I, I, D, P, P,
-                                            P, P]
-        lib.oracle_kda_fwd_prep.restype = I
-        lib.oracle_kda_decode_step_prep.argtypes = [I, I, I, I, D, P, P, P, P, P, P, I, P, I, D,
-                                                    P, P, P]
-        lib.oracle_kda_decode_step_prep.restype = I
+        lib.oracle_kda_fwd_ex.argtypes = [I, I, I, I, I, D, P, P, P, P, P, P, P, I, I, D, P, P,
+                                          I, D, P, P, P, P]
+        lib.oracle_kda_fwd_ex.restype = I
+        lib.oracle_kda_decode_step_ex.argtypes = [I, I, I, I, D, P, P, P, P, P, P, I, P, I, D,
+                                                  P, P, I, D, P, P, P]
+        lib.oracle_kda_decode_step_ex.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         _lib = lib
@@ -115,15 +115,30 @@ def _prep_args(prep, H, dk):
     return flags, float(prep.get("eps", 1e-6)), a, b
 
 
-def kda_fwd(q, k, v, g, beta, scale, S0=None, cu_seqlens=None, drop_erase=False, prep=None):
+def _epi_args(epi, shape_o, dv):
+    """(on, eps, w, z) for the C oracle from an epilogue dict: eps (float),
+    weight ([dv] or None), gate ([..., dv] shaped like o, or None).  See
+    epilogue_row in kda_oracle.c."""
+    if epi is None:
+        return 0, 0.0, None, None
+    w = epi.get("weight")
+    z = epi.get("gate")
+    w = None if w is None else _f32(w).reshape(dv)
+    z = None if z is None else _f32(z).reshape(shape_o)
+    return 1, float(epi.get("eps", 1e-6)), w, z
+
+
+def kda_fwd(q, k, v, g, beta, scale, S0=None, cu_seqlens=None, drop_erase=False, prep=None,
+            epilogue=None):
     """Exact KDA forward in fp64.
 
     q, k, g: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H] (float32 values,
     upcast to fp64 inside).  S0: [N, H, dk, dv] or None.  cu_seqlens: int32
     [N + 1] or None (then N = B).  prep: optional input preparation (see
     _prep_args): L2 normalisation of q and k, beta given as logits, g given as
-    the gate pre-activation of the Mamba/GDN-style decay.  Returns
-    (o [B, T, H, dv], S [N, H, dk, dv]), both float64.
+    the gate pre-activation of the Mamba/GDN-style decay.  epilogue: optional
+    per-head RMSNorm + sigmoid output gate applied to every output row (see
+    _epi_args).  Returns (o [B, T, H, dv], S [N, H, dk, dv]), both float64.
     """
     q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
     B, T, H, dk = q.shape
@@ -142,12 +157,14 @@ def kda_fwd(q, k, v, g, beta, scale, S0=None, cu_seqlens=None, drop_erase=False,
         assert s0.shape == (N, H, dk, dv)
     o = np.zeros((B, T, H, dv), dtype=np.float64)
     S = np.zeros((N, H, dk, dv), dtype=np.float64)
-    if prep is not None:
+    if prep is not None or epilogue is not None:
         assert not drop_erase
-        flags, eps, a, b = _prep_args(prep, H, dk)
-        rc = _load().oracle_kda_fwd_prep(B, T, H, dk, dv, float(scale), _ptr(q), _ptr(k),
-                                         _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(cu), N,
-                                         flags, eps, _ptr(a), _ptr(b), _ptr(o), _ptr(S))
+        flags, eps, a, b = _prep_args(prep or {}, H, dk)
+        on, e_eps, w, z = _epi_args(epilogue, (B, T, H, dv), dv)
+        rc = _load().oracle_kda_fwd_ex(B, T, H, dk, dv, float(scale), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(cu), N,
+                                       flags, eps, _ptr(a), _ptr(b), on, e_eps, _ptr(w), _ptr(z),
+                                       _ptr(o), _ptr(S))
     else:
         rc = _load().oracle_kda_fwd(B, T, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(g), _ptr(beta), _ptr(s0), _ptr(cu), N,
@@ -157,10 +174,10 @@ def kda_fwd(q, k, v, g, beta, scale, S0=None, cu_seqlens=None, drop_erase=False,
     return o, S
 
 
-def kda_decode_step(q, k, v, g, beta, scale, state, slot_idx=None, prep=None):
+def kda_decode_step(q, k, v, g, beta, scale, state, slot_idx=None, prep=None, epilogue=None):
     """One exact decode step.  q, k, g [N, H, dk]; v [N, H, dv]; beta [N, H];
-    state: float64 [num_slots, H, dk, dv], updated IN PLACE; prep as in
-    kda_fwd.  Returns o [N, H, dv]."""
+    state: float64 [num_slots, H, dk, dv], updated IN PLACE; prep and epilogue
+    as in kda_fwd.  Returns o [N, H, dv]."""
     q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -168,12 +185,13 @@ def kda_decode_step(q, k, v, g, beta, scale, state, slot_idx=None, prep=None):
     num_slots = state.shape[0]
     si = None if slot_idx is None else np.ascontiguousarray(np.asarray(slot_idx, dtype=np.int32))
     o = np.zeros((N, H, dv), dtype=np.float64)
-    if prep is not None:
-        flags, eps, a, b = _prep_args(prep, H, dk)
-        rc = _load().oracle_kda_decode_step_prep(N, H, dk, dv, float(scale), _ptr(q), _ptr(k),
-                                                 _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                                 num_slots, _ptr(si), flags, eps, _ptr(a),
-                                                 _ptr(b), _ptr(o))
+    if prep is not None or epilogue is not None:
+        flags, eps, a, b = _prep_args(prep or {}, H, dk)
+        on, e_eps, w, z = _epi_args(epilogue, (N, H, dv), dv)
+        rc = _load().oracle_kda_decode_step_ex(N, H, dk, dv, float(scale), _ptr(q), _ptr(k),
+                                               _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                               num_slots, _ptr(si), flags, eps, _ptr(a),
+                                               _ptr(b), on, e_eps, _ptr(w), _ptr(z), _ptr(o))
     else:
         rc = _load().oracle_kda_decode_step(N, H, dk, dv, float(scale), _ptr(q), _ptr(k),
                                             _ptr(v), _ptr(g), _ptr(beta), _ptr(state), num_slots,

@@ -155,6 +155,33 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Optional output epilogue of a Kimi Linear layer (summary page,
+ * "Configuracion del modelo Kimi Linear": per-head RMSNorm and a
+ * data-dependent output gate before the output projection).  The gate's
+ * activation is not named on the page; the sigmoid is taken.  On one output
+ * row o (dv) of one head:
+ *     y_j = o_j / sqrt(mean_j o_j^2 + eps) * w_j * sigmoid(z_j)
+ * w: [dv] or NULL (= 1); z: the row's gate logits [dv] or NULL (no gate). */
+typedef struct {
+    double eps;
+    const float *w;       /* [dv] */
+    const float *z;       /* [.., H, dv] like o */
+} epi_t;
+
+static void epilogue_row(const epi_t *e, int dv, const float *z, double *o)
+{
+    double ms = 0.0;
+    for (int j = 0; j < dv; ++j) ms += o[j] * o[j];
+    ms /= dv;
+    const double r = ms + e->eps > 0.0 ? 1.0 / sqrt(ms + e->eps) : 0.0;
+    for (int j = 0; j < dv; ++j) {
+        double y = o[j] * r;
+        if (e->w) y *= (double)e->w[j];
+        if (z) y *= 1.0 / (1.0 + exp(-(double)z[j]));
+        o[j] = y;
+    }
+}
+
 /* Full forward over B rows (or N packed sequences), with optional input
  * preparation (see prepare_token; prep == NULL passes inputs through).
  * Returns 0 on success, nonzero on a malformed argument. */
@@ -162,7 +189,8 @@ static int kda_fwd_impl(int B, int T, int H, int dk, int dv, double scale,
                         const float *q, const float *k, const float *v,
                         const float *g, const float *beta, const double *S0,
                         const int32_t *cu_seqlens, int N, int drop_erase,
-                        const prep_t *prep, double *o, double *S_final)
+                        const prep_t *prep, const epi_t *epi, double *o,
+                        double *S_final)
 {
     if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return 1;
     if (cu_seqlens) {
@@ -201,9 +229,12 @@ static int kda_fwd_impl(int B, int T, int H, int dk, int dv, double scale,
                                   k + tok * tok_k + (size_t)h * dk,
                                   g + tok * tok_k + (size_t)h * dk, beta[tok * H + h],
                                   tv, tv + dk, tv + 2 * dk, &bd);
+                    double *orow = o ? o + tok * tok_v + (size_t)h * dv : NULL;
                     kda_token(dk, dv, scale, tv, tv + dk, v + tok * tok_v + (size_t)h * dv,
-                              tv + 2 * dk, bd, S, u,
-                              o ? o + tok * tok_v + (size_t)h * dv : NULL, drop_erase);
+                              tv + 2 * dk, bd, S, u, orow, drop_erase);
+                    if (epi && orow)
+                        epilogue_row(epi, dv, epi->z ? epi->z + tok * tok_v + (size_t)h * dv : NULL,
+                                     orow);
                 }
                 if (S_final) memcpy(S_final + sidx, S, sizeof(double) * (size_t)dk * dv);
             }
@@ -222,21 +253,24 @@ int oracle_kda_fwd(int B, int T, int H, int dk, int dv, double scale,
                    double *o, double *S_final)
 {
     return kda_fwd_impl(B, T, H, dk, dv, scale, q, k, v, g, beta, S0, cu_seqlens, N,
-                        drop_erase, NULL, o, S_final);
+                        drop_erase, NULL, NULL, o, S_final);
 }
 
-/* The forward with input preparation: flags, eps, A_log [H] or NULL,
- * dt_bias [H, dk] or NULL (see prepare_token). */
-int oracle_kda_fwd_prep(int B, int T, int H, int dk, int dv, double scale,
-                        const float *q, const float *k, const float *v,
-                        const float *g, const float *beta, const double *S0,
-                        const int32_t *cu_seqlens, int N, int flags, double eps,
-                        const float *A_log, const float *dt_bias,
-                        double *o, double *S_final)
+/* The forward with input preparation (flags, eps, A_log [H] or NULL,
+ * dt_bias [H, dk] or NULL; see prepare_token) and output epilogue (epi_on,
+ * epi_eps, w [dv] or NULL, z [B, T, H, dv] or NULL; see epilogue_row). */
+int oracle_kda_fwd_ex(int B, int T, int H, int dk, int dv, double scale,
+                      const float *q, const float *k, const float *v,
+                      const float *g, const float *beta, const double *S0,
+                      const int32_t *cu_seqlens, int N, int flags, double eps,
+                      const float *A_log, const float *dt_bias, int epi_on,
+                      double epi_eps, const float *w, const float *z,
+                      double *o, double *S_final)
 {
     prep_t p = {flags, eps, A_log, dt_bias};
+    epi_t e = {epi_eps, w, z};
     return kda_fwd_impl(B, T, H, dk, dv, scale, q, k, v, g, beta, S0, cu_seqlens, N, 0,
-                        &p, o, S_final);
+                        &p, epi_on ? &e : NULL, o, S_final);
 }
 
 /* One decode step: the same token update applied once to each sequence's
@@ -248,7 +282,7 @@ static int kda_decode_impl(int N, int H, int dk, int dv, double scale,
                            const float *q, const float *k, const float *v,
                            const float *g, const float *beta, double *state,
                            int num_slots, const int32_t *slot_idx,
-                           const prep_t *prep, double *o)
+                           const prep_t *prep, const epi_t *epi, double *o)
 {
     if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || num_slots < 0) return 1;
     if (!slot_idx && N > num_slots) return 2;
@@ -274,6 +308,7 @@ static int kda_decode_impl(int N, int H, int dk, int dv, double scale,
                               tv + dk, tv + 2 * dk, &bd);
                 kda_token(dk, dv, scale, tv, tv + dk, v + r * dv, tv + 2 * dk, bd, S, u,
                           o + r * dv, 0);
+                if (epi) epilogue_row(epi, dv, epi->z ? epi->z + r * dv : NULL, o + r * dv);
             }
         }
         free(u);
@@ -288,17 +323,19 @@ int oracle_kda_decode_step(int N, int H, int dk, int dv, double scale,
                            int num_slots, const int32_t *slot_idx, double *o)
 {
     return kda_decode_impl(N, H, dk, dv, scale, q, k, v, g, beta, state, num_slots,
-                           slot_idx, NULL, o);
+                           slot_idx, NULL, NULL, o);
 }
 
-int oracle_kda_decode_step_prep(int N, int H, int dk, int dv, double scale,
-                                const float *q, const float *k, const float *v,
-                                const float *g, const float *beta, double *state,
-                                int num_slots, const int32_t *slot_idx, int flags,
-                                double eps, const float *A_log, const float *dt_bias,
-                                double *o)
+int oracle_kda_decode_step_ex(int N, int H, int dk, int dv, double scale,
+                              const float *q, const float *k, const float *v,
+                              const float *g, const float *beta, double *state,
+                              int num_slots, const int32_t *slot_idx, int flags,
+                              double eps, const float *A_log, const float *dt_bias,
+                              int epi_on, double epi_eps, const float *w,
+                              const float *z, double *o)
 {
     prep_t p = {flags, eps, A_log, dt_bias};
+    epi_t e = {epi_eps, w, z};
     return kda_decode_impl(N, H, dk, dv, scale, q, k, v, g, beta, state, num_slots,
-                           slot_idx, &p, o);
+                           slot_idx, &p, epi_on ? &e : NULL, o);
 }

@@ -29,8 +29,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
     assert set(names) == {"kda_status_string", "kda_version", "kda_chunk_fwd_workspace_bytes",
-                          "kda_chunk_fwd", "kda_chunk_fwd_prep", "kda_decode_step",
-                          "kda_decode_step_prep"}
+                          "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_decode_step",
+                          "kda_decode_step_ex"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in kda.SIGNATURES, n
@@ -100,26 +100,37 @@ def test_decode_validation(lib):
     assert dec(N=0) == E["KDA_OK"]                              # nothing to do, nothing launched
 
 
-def test_prep_validation(lib):
-    """A malformed kda_prep is rejected on the host, before any HIP call."""
+def test_prep_and_epilogue_validation(lib):
+    """A malformed kda_prep or kda_epilogue is rejected on the host, before any
+    HIP call."""
     E = {v: k for k, v in kda.STATUS_NAMES.items()}
     p = ctypes.c_void_p(4096)
 
-    def fwd(prep):
-        return lib.kda_chunk_fwd_prep(1, 64, 2, 64, 64, 64, 1.0, kda.KDA_BF16, p, p, p, p, p,
-                                      None, None, 0, p, None, p, 1 << 30, ctypes.byref(prep),
-                                      None)
+    def fwd(prep=None, epi=None):
+        return lib.kda_chunk_fwd_ex(1, 64, 2, 64, 64, 64, 1.0, kda.KDA_BF16, p, p, p, p, p,
+                                    None, None, 0, p, None, p, 1 << 30,
+                                    None if prep is None else ctypes.byref(prep),
+                                    None if epi is None else ctypes.byref(epi), None)
 
-    def dec(prep):
-        return lib.kda_decode_step_prep(2, 2, 64, 64, 1.0, kda.KDA_BF16, p, p, p, p, p, p, 2,
-                                        None, p, ctypes.byref(prep), None)
+    def dec(prep=None, epi=None):
+        return lib.kda_decode_step_ex(2, 2, 64, 64, 1.0, kda.KDA_BF16, p, p, p, p, p, p, 2,
+                                      None, p, None if prep is None else ctypes.byref(prep),
+                                      None if epi is None else ctypes.byref(epi), None)
 
     bias_only = kda.KdaPrep(0, 1e-6, 0, None, 4096)
     bad_eps = kda.KdaPrep(1, -1.0, 0, None, None)
     nan_eps = kda.KdaPrep(1, float("nan"), 0, None, None)
     odd_ptr = kda.KdaPrep(0, 0.0, 0, 4098, None)
+    epi_bad_eps = kda.KdaEpilogue(-1e-3, None, None)
+    epi_inf_eps = kda.KdaEpilogue(float("inf"), None, None)
+    epi_odd_w = kda.KdaEpilogue(1e-6, 4098, None)
+    epi_odd_gate = kda.KdaEpilogue(1e-6, None, 4100)
     for call in (fwd, dec):
-        assert call(bias_only) == E["KDA_ERR_NULL_ARG"]
-        assert call(bad_eps) == E["KDA_ERR_BAD_SHAPE"]
-        assert call(nan_eps) == E["KDA_ERR_BAD_SHAPE"]
-        assert call(odd_ptr) == E["KDA_ERR_NULL_ARG"]
+        assert call(prep=bias_only) == E["KDA_ERR_NULL_ARG"]
+        assert call(prep=bad_eps) == E["KDA_ERR_BAD_SHAPE"]
+        assert call(prep=nan_eps) == E["KDA_ERR_BAD_SHAPE"]
+        assert call(prep=odd_ptr) == E["KDA_ERR_NULL_ARG"]
+        assert call(epi=epi_bad_eps) == E["KDA_ERR_BAD_SHAPE"]
+        assert call(epi=epi_inf_eps) == E["KDA_ERR_BAD_SHAPE"]
+        assert call(epi=epi_odd_w) == E["KDA_ERR_NULL_ARG"]
+        assert call(epi=epi_odd_gate) == E["KDA_ERR_NULL_ARG"]
