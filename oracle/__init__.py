@@ -78,6 +78,9 @@ def _load():
         lib.oracle_kda_decode_step_ex.argtypes = [I, I, I, I, D, P, P, P, P, P, P, I, P, I, D,
                                                   P, P, I, D, P, P, P]
         lib.oracle_kda_decode_step_ex.restype = I
+        lib.oracle_kda_bwd.argtypes = [I, I, I, I, I, D, P, P, P, P, P, P, P, I, P, P, P, P, P, P,
+                                       P, P]
+        lib.oracle_kda_bwd.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         _lib = lib
@@ -172,6 +175,38 @@ def kda_fwd(q, k, v, g, beta, scale, S0=None, cu_seqlens=None, drop_erase=False,
     if rc != 0:
         raise ValueError("oracle_kda_fwd rejected its arguments (code %d)" % rc)
     return o, S
+
+
+def kda_bwd(q, k, v, g, beta, scale, d_o, S0=None, cu_seqlens=None, d_S_final=None):
+    """Exact gradients of L = sum(o * d_o) + sum(S_final * d_S_final) in fp64
+    (reverse mode through the token recurrence).  Shapes as in kda_fwd; d_o
+    like o, d_S_final like the final state (None = 0).  Returns
+    (dq, dk, dv, dg, dbeta, dS0), float64; dS0 has the initial state's shape."""
+    q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.shape[0] - 1
+    else:
+        cu = None
+        N = B
+    s0 = None if S0 is None else np.ascontiguousarray(np.asarray(S0, dtype=np.float64))
+    do = np.ascontiguousarray(np.asarray(d_o, dtype=np.float64))
+    assert do.shape == (B, T, H, dv)
+    dsf = None if d_S_final is None else np.ascontiguousarray(np.asarray(d_S_final, np.float64))
+    dq = np.zeros((B, T, H, dk))
+    dkk = np.zeros((B, T, H, dk))
+    dvv = np.zeros((B, T, H, dv))
+    dg = np.zeros((B, T, H, dk))
+    db = np.zeros((B, T, H))
+    dS0 = np.zeros((N, H, dk, dv))
+    rc = _load().oracle_kda_bwd(B, T, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                _ptr(beta), _ptr(s0), _ptr(cu), N, _ptr(do), _ptr(dsf), _ptr(dq),
+                                _ptr(dkk), _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dS0))
+    if rc != 0:
+        raise ValueError("oracle_kda_bwd rejected its arguments (code %d)" % rc)
+    return dq, dkk, dvv, dg, db, dS0
 
 
 def kda_decode_step(q, k, v, g, beta, scale, state, slot_idx=None, prep=None, epilogue=None):

@@ -339,3 +339,161 @@ int oracle_kda_decode_step_ex(int N, int H, int dk, int dv, double scale,
     return kda_decode_impl(N, H, dk, dv, scale, q, k, v, g, beta, state, num_slots,
                            slot_idx, &p, epi_on ? &e : NULL, o);
 }
+
+/* ------------------------------------------------------------------------
+ * Gradients of the forward (reverse mode through the same token recurrence,
+ * in fp64).  For the loss L = sum(o * d_o) + sum(S_final * d_S_final), with
+ * each token step written as
+ *     a  = exp(g_t);  S1 = Diag(a) S_{t-1};  u = S1^T k;  e = beta (v - u);
+ *     S_t = S1 + k e^T;  o_t = scale S_t^T q,
+ * the adjoints, taken in reverse token order, are
+ *     dS_t += scale q do^T;        dq = scale S_t do
+ *     dk   = dS_t e;               de = dS_t^T k
+ *     dbeta = de . (v - u);        dv = beta de;       du = -beta de
+ *     dS1  = dS_t + k du^T;        dk += S1 du
+ *     dS_{t-1} = Diag(a) dS1;      dg = a * rowsum(dS1 * S_{t-1})
+ * The states of one chain are kept for the whole sequence (test sizes only).
+ * Outputs dq, dk, dg [B,T,H,dk], dv [B,T,H,dv], dbeta [B,T,H], and dS0
+ * [N,H,dk,dv] when non-NULL; d_S_final may be NULL (zero).
+ * ------------------------------------------------------------------------ */
+int oracle_kda_bwd(int B, int T, int H, int dk, int dv, double scale,
+                   const float *q, const float *k, const float *v,
+                   const float *g, const float *beta, const double *S0,
+                   const int32_t *cu_seqlens, int N, const double *d_o,
+                   const double *d_S_final, double *dq, double *dkk,
+                   double *dvv, double *dg, double *dbeta, double *dS0)
+{
+    if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return 1;
+    if (cu_seqlens) {
+        if (B != 1 || N <= 0) return 2;
+        if (cu_seqlens[0] != 0 || cu_seqlens[N] != T) return 3;
+        for (int n = 0; n < N; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return 4;
+    } else {
+        N = B;
+    }
+    const size_t tok_k = (size_t)H * dk, tok_v = (size_t)H * dv, SZ = (size_t)dk * dv;
+    const long chains = (long)N * H;
+    int err = 0;
+#pragma omp parallel
+    {
+        const long maxlen = cu_seqlens ? T : T;
+        double *hist = (double *)malloc(sizeof(double) * SZ * (size_t)(maxlen + 1));
+        double *dS = (double *)malloc(sizeof(double) * SZ);
+        double *S1 = (double *)malloc(sizeof(double) * SZ);
+        double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *e = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *de = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *du = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!hist || !dS || !S1 || !u || !e || !de || !du) {
+#pragma omp atomic write
+            err = 5;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long c = 0; c < chains; ++c) {
+                const int n = (int)(c / H), h = (int)(c % H);
+                long t0, t1, base;
+                if (cu_seqlens) { t0 = cu_seqlens[n]; t1 = cu_seqlens[n + 1]; base = 0; }
+                else { t0 = 0; t1 = T; base = (long)n * T; }
+                const size_t sidx = ((size_t)n * H + h) * SZ;
+                /* forward: hist[j] = state after j tokens of this chain */
+                if (S0) memcpy(hist, S0 + sidx, sizeof(double) * SZ);
+                else memset(hist, 0, sizeof(double) * SZ);
+                for (long t = t0; t < t1; ++t) {
+                    const size_t tok = (size_t)(base + t);
+                    const float *kt = k + tok * tok_k + (size_t)h * dk;
+                    const float *vt = v + tok * tok_v + (size_t)h * dv;
+                    const float *gt = g + tok * tok_k + (size_t)h * dk;
+                    const double bt = (double)beta[tok * H + h];
+                    const double *Sp = hist + (size_t)(t - t0) * SZ;
+                    double *Sn = hist + (size_t)(t - t0 + 1) * SZ;
+                    for (int i = 0; i < dk; ++i) {
+                        const double a = exp((double)gt[i]);
+                        for (int j = 0; j < dv; ++j) Sn[(size_t)i * dv + j] = a * Sp[(size_t)i * dv + j];
+                    }
+                    for (int j = 0; j < dv; ++j) u[j] = 0.0;
+                    for (int i = 0; i < dk; ++i)
+                        for (int j = 0; j < dv; ++j) u[j] += Sn[(size_t)i * dv + j] * (double)kt[i];
+                    for (int j = 0; j < dv; ++j) e[j] = bt * ((double)vt[j] - u[j]);
+                    for (int i = 0; i < dk; ++i)
+                        for (int j = 0; j < dv; ++j) Sn[(size_t)i * dv + j] += (double)kt[i] * e[j];
+                }
+                /* reverse */
+                if (d_S_final) memcpy(dS, d_S_final + sidx, sizeof(double) * SZ);
+                else memset(dS, 0, sizeof(double) * SZ);
+                for (long t = t1 - 1; t >= t0; --t) {
+                    const size_t tok = (size_t)(base + t);
+                    const float *qt = q + tok * tok_k + (size_t)h * dk;
+                    const float *kt = k + tok * tok_k + (size_t)h * dk;
+                    const float *vt = v + tok * tok_v + (size_t)h * dv;
+                    const float *gt = g + tok * tok_k + (size_t)h * dk;
+                    const double bt = (double)beta[tok * H + h];
+                    const double *Sp = hist + (size_t)(t - t0) * SZ;
+                    const double *St = hist + (size_t)(t - t0 + 1) * SZ;
+                    const double *dot = d_o + tok * tok_v + (size_t)h * dv;
+                    double *dqt = dq + tok * tok_k + (size_t)h * dk;
+                    double *dkt = dkk + tok * tok_k + (size_t)h * dk;
+                    double *dvt = dvv + tok * tok_v + (size_t)h * dv;
+                    double *dgt = dg + tok * tok_k + (size_t)h * dk;
+                    /* recompute S1, u, e of this token */
+                    for (int i = 0; i < dk; ++i) {
+                        const double a = exp((double)gt[i]);
+                        for (int j = 0; j < dv; ++j) S1[(size_t)i * dv + j] = a * Sp[(size_t)i * dv + j];
+                    }
+                    for (int j = 0; j < dv; ++j) u[j] = 0.0;
+                    for (int i = 0; i < dk; ++i)
+                        for (int j = 0; j < dv; ++j) u[j] += S1[(size_t)i * dv + j] * (double)kt[i];
+                    for (int j = 0; j < dv; ++j) e[j] = bt * ((double)vt[j] - u[j]);
+                    /* output */
+                    for (int i = 0; i < dk; ++i) {
+                        double acc = 0.0;
+                        for (int j = 0; j < dv; ++j) {
+                            dS[(size_t)i * dv + j] += scale * (double)qt[i] * dot[j];
+                            acc += St[(size_t)i * dv + j] * dot[j];
+                        }
+                        dqt[i] = scale * acc;
+                    }
+                    /* write */
+                    for (int j = 0; j < dv; ++j) de[j] = 0.0;
+                    for (int i = 0; i < dk; ++i) {
+                        double acc = 0.0;
+                        for (int j = 0; j < dv; ++j) {
+                            acc += dS[(size_t)i * dv + j] * e[j];
+                            de[j] += dS[(size_t)i * dv + j] * (double)kt[i];
+                        }
+                        dkt[i] = acc;
+                    }
+                    double db = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        db += de[j] * ((double)vt[j] - u[j]);
+                        dvt[j] = bt * de[j];
+                        du[j] = -bt * de[j];
+                    }
+                    dbeta[tok * H + h] = db;
+                    /* recall u = S1^T k */
+                    for (int i = 0; i < dk; ++i) {
+                        double acc = 0.0;
+                        for (int j = 0; j < dv; ++j) {
+                            dS[(size_t)i * dv + j] += (double)kt[i] * du[j];
+                            acc += S1[(size_t)i * dv + j] * du[j];
+                        }
+                        dkt[i] += acc;
+                    }
+                    /* decay */
+                    for (int i = 0; i < dk; ++i) {
+                        const double a = exp((double)gt[i]);
+                        double acc = 0.0;
+                        for (int j = 0; j < dv; ++j) {
+                            acc += dS[(size_t)i * dv + j] * Sp[(size_t)i * dv + j];
+                            dS[(size_t)i * dv + j] *= a;
+                        }
+                        dgt[i] = a * acc;
+                    }
+                }
+                if (dS0) memcpy(dS0 + sidx, dS, sizeof(double) * SZ);
+            }
+        }
+        free(hist); free(dS); free(S1); free(u); free(e); free(de); free(du);
+    }
+    return err;
+}
