@@ -24,6 +24,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2500.0      # dense fp16/bf16 matrix cores, TFLOP/s
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4   # q,k,v bf16; g; beta; o fp32
 DECODE_BYTES_PER_TOKEN_HEAD = 2 * 128 * 128 * 4 + 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4
+# backward: q,k,v bf16, g, beta, grad_o in; grad q,k,v,g fp32 and grad beta out
+BACKWARD_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4 + 4 * 128 * 4 + 4
 
 
 def prefill_flops_per_token_head(dk=128, dv=128, C=64):
@@ -38,7 +40,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-target", choices=["prefill", "decode", "copy"],
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--profile-target", choices=["prefill", "decode", "backward", "copy"],
                     help="run only this workload a few times (target for rocprofv3) and exit")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="read rocprofv3 FETCH_SIZE/WRITE_SIZE runs of the three profile "
@@ -72,8 +75,11 @@ def measured_traffic(leg):
 
 
 LEG_SOURCES = {"prefill": ["kda_prefill.hip", "kda_common.h", "kda_internal.h"],
-               "decode": ["kda_decode.hip", "kda_common.h", "kda_internal.h"]}
-LEG_KERNELS = {"prefill": ("kda_intra", "kda_inter"), "decode": ("decode_step_kernel",)}
+               "decode": ["kda_decode.hip", "kda_common.h", "kda_internal.h"],
+               "backward": ["kda_prefill.hip", "kda_common.h", "kda_internal.h"]}
+LEG_KERNELS = {"prefill": ("kda_intra", "kda_inter"), "decode": ("decode_step_kernel",),
+               "backward": ("kda_intra", "kda_inter", "kda_bwd_chain", "kda_bwd_dv",
+                            "kda_bwd_intra")}
 COPY_BYTES = 1 << 30   # the copy target reads and writes 1 GiB per dispatch
 
 
@@ -152,6 +158,15 @@ def profile_target(kind):
         for _ in range(3):
             kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64, o=o,
                               final_state=S, workspace=ws)
+    elif kind == "backward":
+        d = kda_inputs.config_inputs(2, "cuda")
+        B, T, H, D = d["q"].shape
+        ws = torch.empty(kda.kda_chunk_bwd_workspace_bytes(B, T, H, D, D, 64), dtype=torch.uint8,
+                         device="cuda")
+        do = torch.randn(B, T, H, D, device="cuda")
+        for _ in range(3):
+            kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, chunk=64,
+                              want_grad_initial_state=False, workspace=ws)
     else:
         c = kda_inputs.CONFIGS[4]
         N, H, D = c["N"], c["H"], c["dk"]
@@ -242,6 +257,35 @@ def bench_prefill_prep(kda, kda_inputs, steps, warmup, stream, with_epilogue=Fal
     ms = tm.stop() / steps
     torch.cuda.synchronize()
     return ms
+
+
+def bench_backward(kda, kda_inputs, d, steps, warmup, stream):
+    """Gradients of the same prefill layer (kda_chunk_bwd): random grad_o, no
+    final-state gradient, zero initial state."""
+    B, T, H, D = d["q"].shape
+    C = kda_inputs.CONFIGS[2]["chunk"]
+    gen = torch.Generator(device="cuda").manual_seed(kda_inputs.CFG_SEED[2] + 60)
+    do = torch.randn(B, T, H, D, device="cuda", generator=gen)
+    ws = torch.empty(kda.kda_chunk_bwd_workspace_bytes(B, T, H, D, D, C), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        return kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, chunk=C,
+                                 want_grad_initial_state=False, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    tm = StreamTimer(stream)
+    keep = []
+    tm.start()
+    for _ in range(steps):
+        keep.append(call())
+        if len(keep) > 2:
+            keep.pop(0)
+    ms = tm.stop() / steps
+    torch.cuda.synchronize()
+    return dict(ms=ms, workspace_bytes=ws.numel())
 
 
 def decode_setup(kda, kda_inputs, n_steps, stream):
@@ -425,6 +469,22 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["mfma_frac"] = roof["mfma_tflops"] / MFMA_PEAK_TFLOPS
 
+    bwd = None
+    if not args.no_backward:
+        bw = bench_backward(kda, kda_inputs, pf["inputs"], args.steps, args.warmup, stream)
+        print("backward %.4f ms/call" % bw["ms"], file=sys.stderr, flush=True)
+        bb = BACKWARD_BYTES_PER_TOKEN_HEAD * th
+        bwd = dict(ms_per_step=bw["ms"], value=pf["tokens"] / (bw["ms"] / 1e3), unit="tokens/s",
+                   workload="gradients of the same layer (kda_chunk_bwd): grad_o random, no "
+                            "final-state gradient, fp32 chunk records",
+                   workspace_bytes=bw["workspace_bytes"],
+                   roofline=dict(bound="hbm", achieved=bb / (bw["ms"] / 1e3) / 1e9,
+                                 peak=HBM_PEAK_GBS, unit="GB/s", algorithmic_bytes=bb,
+                                 traffic=measured_traffic("backward"),
+                                 kernel="kda_chunk_bwd call (kda_intra, kda_inter with state "
+                                        "history, kda_bwd_chain, kda_bwd_dv, kda_bwd_intra)"))
+        bwd["roofline"]["frac"] = bwd["roofline"]["achieved"] / HBM_PEAK_GBS
+
     dec = None
     if not args.no_decode:
         dc = bench_decode(kda, kda_inputs, args.decode_steps, args.warmup, stream)
@@ -484,6 +544,7 @@ def main():
             workload="as above plus the output epilogue (per-head RMSNorm, weight, sigmoid "
                      "gate; one extra pass over o inside the call)"),
         "cpu_baseline": cpu,
+        "backward": bwd,
         "decode": dec,
     }
     print(json.dumps(out))

@@ -218,6 +218,51 @@ kda_status kda_decode_step_ex(int N, int H, int dk, int dv, float scale,
                               const kda_prep *prep, const kda_epilogue *epilogue,
                               hipStream_t stream);
 
+/* Bytes of device workspace kda_chunk_bwd needs for these sizes (0 if the
+ * sizes are invalid or unsupported); arguments as for
+ * kda_chunk_fwd_workspace_bytes.  It holds the forward's chunk records plus
+ * the state at every chunk start, the state gradient after every chunk and a
+ * per-chunk gradient record, about (2 dk dv + 3 C dk + 2 C^2) * 4 bytes per
+ * (chunk, head) on top of the forward's. */
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv,
+                                     int chunk, int num_seqs,
+                                     kda_dtype qkv_dtype);
+
+/* Gradients of kda_chunk_fwd (no preparation, no epilogue) by reverse mode
+ * through the chunkwise form (same page, "Algoritmo paralelo por chunks";
+ * the page gives the forward only, the backward is its exact derivative).
+ * For the loss L = <o, grad_o> + <final_state, grad_final_state> it writes
+ * dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta and dL/d initial_state.
+ *
+ *   B .. num_seqs  exactly as passed to kda_chunk_fwd (the forward's inputs;
+ *                  o and final_state are not needed: the call recomputes
+ *                  what it needs).
+ *   grad_o           [B, T, H, dv] fp32, the gradient with respect to o.
+ *   grad_final_state [N, H, dk, dv] fp32 or NULL (zero).
+ *   grad_q, grad_k   [B, T, H, dk] fp32 outputs.
+ *   grad_v           [B, T, H, dv] fp32 output.
+ *   grad_g           [B, T, H, dk] fp32 output (with respect to log alpha).
+ *   grad_beta        [B, T, H] fp32 output (4-byte aligned).
+ *   grad_initial_state [N, H, dk, dv] fp32 output or NULL (not wanted).  May
+ *                  alias grad_final_state; no other aliasing is allowed.
+ *   workspace      at least kda_chunk_bwd_workspace_bytes(...) bytes,
+ *                  256-byte aligned; contents on entry are ignored.
+ * Errors as for kda_chunk_fwd.  Domain: that of kda_chunk_fwd, and within a
+ * chunk the per-channel sum of -g stays below 80 (the intra-chunk gradient is
+ * formed with exp(+-G) relative to the chunk start in fp32). */
+kda_status kda_chunk_bwd(int B, int T, int H, int dk, int dv, int chunk,
+                         float scale, kda_dtype qkv_dtype,
+                         const void *q, const void *k, const void *v,
+                         const float *g, const float *beta,
+                         const float *initial_state,
+                         const int32_t *cu_seqlens, int num_seqs,
+                         const float *grad_o, const float *grad_final_state,
+                         float *grad_q, float *grad_k, float *grad_v,
+                         float *grad_g, float *grad_beta,
+                         float *grad_initial_state,
+                         void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,6 +48,9 @@ SIGNATURES = {
                            _P, _P, _P, _SZ, _P]),
     "kda_chunk_fwd_ex": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                               _P, _P, _P, _SZ, _PREP, _EPI, _P]),
+    "kda_chunk_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "kda_chunk_bwd": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
+                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "kda_decode_step": (_I, [_I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P]),
     "kda_decode_step_ex": (_I, [_I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                 _PREP, _EPI, _P]),
@@ -210,6 +213,59 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu
     if rc != KDA_OK:
         raise KDAError(fn, rc)
     return o, final_state
+
+
+def kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torch.bfloat16):
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load_library().kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs,
+                                                             code))
+
+
+def kda_chunk_bwd(q, k, v, g, beta, grad_o, scale=None, chunk=64, initial_state=None,
+                  cu_seqlens=None, grad_final_state=None, want_grad_initial_state=True,
+                  workspace=None, stream=None):
+    """Gradients of kda_chunk_fwd (no preparation, no epilogue) for the loss
+    <o, grad_o> + <final_state, grad_final_state>.
+
+    Forward arguments as in kda_chunk_fwd; grad_o: [B, T, H, dv] fp32;
+    grad_final_state: [N, H, dk, dv] fp32 or None (zero).  Returns (dq, dk, dv,
+    dg, dbeta, d_initial_state), all fp32, the last None when not wanted.
+    """
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    _check(g, "g", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(initial_state, "initial_state", torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _check(grad_o, "grad_o", torch.float32, dev)
+    _check(grad_final_state, "grad_final_state", torch.float32, dev)
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if scale is None:
+        scale = dk ** -0.5
+    f = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty(B, T, H, dk, **f)
+    dk_ = torch.empty(B, T, H, dk, **f)
+    dv_ = torch.empty(B, T, H, dv, **f)
+    dg = torch.empty(B, T, H, dk, **f)
+    db = torch.empty(B, T, H, **f)
+    dS0 = torch.empty(N, H, dk, dv, **f) if want_grad_initial_state else None
+    code = _dtype_code(q)
+    nseq = N if cu_seqlens is not None else 0
+    need = lib.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk, nseq, code)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_bwd(B, T, H, dk, dv, chunk, float(scale), code, _ptr(q), _ptr(k),
+                           _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+                           nseq, _ptr(grad_o), _ptr(grad_final_state), _ptr(dq), _ptr(dk_),
+                           _ptr(dv_), _ptr(dg), _ptr(db), _ptr(dS0), _ptr(workspace),
+                           workspace.numel(), _stream(stream))
+    if rc != KDA_OK:
+        raise KDAError("kda_chunk_bwd", rc)
+    return dq, dk_, dv_, dg, db, dS0
 
 
 def kda_decode_step(q, k, v, g, beta, state_cache, scale=None, slot_idx=None, o=None,

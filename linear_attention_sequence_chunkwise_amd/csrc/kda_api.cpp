@@ -143,6 +143,76 @@ kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk, float s
                             workspace_bytes, nullptr, nullptr, stream);
 }
 
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                     int num_seqs, kda_dtype qkv_dtype) {
+    if (B < 1 || T < 0 || H < 1 || num_seqs < 0) return 0;
+    if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return 0;
+    if (dk != dv || !kda::backward_supported(dk, chunk, qkv_dtype == KDA_BF16)) return 0;
+    const bool varlen = num_seqs > 0;
+    if (varlen && B != 1) return 0;
+    kda::BackwardPlan plan;
+    if (!kda::backward_plan(B, T, H, dk, chunk, varlen ? num_seqs : B, varlen,
+                            qkv_dtype == KDA_BF16, &plan))
+        return 0;
+    return plan.total;
+}
+
+kda_status kda_chunk_bwd(int B, int T, int H, int dk, int dv, int chunk, float scale,
+                         kda_dtype qkv_dtype, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* initial_state,
+                         const int32_t* cu_seqlens, int num_seqs, const float* grad_o,
+                         const float* grad_final_state, float* grad_q, float* grad_k,
+                         float* grad_v, float* grad_g, float* grad_beta,
+                         float* grad_initial_state, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_BAD_SHAPE;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen && (B != 1 || num_seqs < 1)) return KDA_ERR_BAD_SHAPE;
+    const int N = varlen ? num_seqs : B;
+    if ((long long)B * T * H * (long long)(dk > dv ? dk : dv) >= (1LL << 40)) return KDA_ERR_BAD_SHAPE;
+    if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+    if (dk != dv || !kda::backward_supported(dk, chunk, qkv_dtype == KDA_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    const bool has_tokens = (long long)B * T > 0;
+    if (has_tokens) {
+        if (!q || !k || !v || !g || !beta || !grad_o || !grad_q || !grad_k || !grad_v ||
+            !grad_g || !grad_beta)
+            return KDA_ERR_NULL_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
+            !aligned16(grad_o) || !aligned16(grad_q) || !aligned16(grad_k) ||
+            !aligned16(grad_v) || !aligned16(grad_g) || !aligned4(grad_beta))
+            return KDA_ERR_NULL_ARG;
+    }
+    if ((initial_state && !aligned16(initial_state)) ||
+        (grad_final_state && !aligned16(grad_final_state)) ||
+        (grad_initial_state && !aligned16(grad_initial_state)))
+        return KDA_ERR_NULL_ARG;
+
+    kda::BackwardPlan plan;
+    if (!kda::backward_plan(B, T, H, dk, chunk, N, varlen, qkv_dtype == KDA_BF16, &plan))
+        return KDA_ERR_BAD_SHAPE;
+    if (plan.total > 0 && (!workspace || workspace_bytes < plan.total || ((uintptr_t)workspace & 255u)))
+        return KDA_ERR_WORKSPACE;
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+
+    kda::BackwardArgs b;
+    kda::PrefillArgs& a = b.f;
+    a.B = B; a.T = T; a.H = H; a.D = dk; a.C = chunk; a.scale = scale;
+    a.bf16 = qkv_dtype == KDA_BF16;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s0 = initial_state; a.cu_seqlens = cu_seqlens; a.N = N;
+    a.o = nullptr; a.sT = nullptr;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.stream = stream;
+    b.d_o = grad_o;
+    b.dS_final = grad_final_state;
+    b.dq = grad_q; b.dk = grad_k; b.dv = grad_v; b.dg = grad_g; b.dbeta = grad_beta;
+    b.dS0 = grad_initial_state;
+    return from_hip(kda::launch_backward(b, plan));
+}
+
 kda_status kda_decode_step_ex(int N, int H, int dk, int dv, float scale, kda_dtype qkv_dtype,
                               const void* q, const void* k, const void* v, const float* g,
                               const float* beta, float* state_cache, int num_slots,

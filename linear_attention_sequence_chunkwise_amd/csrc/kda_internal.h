@@ -69,11 +69,35 @@ struct PrefillPlan {
     size_t total;
 };
 
+// Gradients of the prefill (kda_chunk_bwd).  f: the forward's arguments
+// (o, sT and the epilogue unused).
+struct BackwardArgs {
+    PrefillArgs f;
+    const float* d_o;       // [B, T, H, dv]
+    const float* dS_final;  // [N, H, dk, dv] or null
+    float *dq, *dk, *dv, *dg, *dbeta;
+    float* dS0;             // [N, H, dk, dv] or null
+};
+
+// Workspace of the backward: the forward's table and records, then the state
+// at every chunk start, dS after every chunk, and per-chunk gradient records.
+struct BackwardPlan {
+    PrefillPlan f;
+    size_t off_shist, off_dshist, off_grec;
+    size_t grec_floats;
+    size_t total;
+};
+
 // True when (D, C, dtype) has a built prefill kernel that fits in LDS.
 bool prefill_supported(int D, int C, bool bf16);
 bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf16,
                   PrefillPlan* plan);
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan);
 hipError_t launch_decode(const DecodeArgs& a);
+// True when (D, C, dtype) has built backward kernels that fit in LDS.
+bool backward_supported(int D, int C, bool bf16);
+bool backward_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf16,
+                   BackwardPlan* plan);
+hipError_t launch_backward(const BackwardArgs& a, const BackwardPlan& plan);
 
 }  // namespace kda

@@ -769,7 +769,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * rt + 4 * lq + j;
-                if (r < len)
+                if (o && r < len)
                     o[((size_t)(tok0 + r) * H + h) * D + v0 + 16 * vt + l16] = scale * acc[j];
             }
         }
@@ -907,12 +907,14 @@ struct InterSmem {
     ChainScratch<D, C, BV, OT> cs;
 };
 
+// s_hist (optional): the state at the start of every chunk, [chunk][H][D][D]
+// fp32 (the backward pass reads it); o may then be NULL.
 template <int D, int C, int BV, typename OT, typename IT>
 __global__ __launch_bounds__(256) void kda_inter(
     int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
     const int* __restrict__ chunk_off, float scale, const IT* __restrict__ v,
     const float* __restrict__ s0, const char* __restrict__ records, float* __restrict__ o,
-    float* __restrict__ sT) {
+    float* __restrict__ sT, float* __restrict__ s_hist) {
     constexpr int ST = (D / 16) * (BV / 16);
     constexpr int SPW = (ST + 3) / 4;
     typedef Rec<D, C, OT> R;
@@ -953,6 +955,9 @@ __global__ __launch_bounds__(256) void kda_inter(
         for (int i = 0; i < VPT; ++i)
             if (tid + 256 * i < NVV) reinterpret_cast<vec*>(sm.vraw)[tid + 256 * i] = vb[i];
         lds_barrier();
+        if (s_hist)
+            chain_store_state<D, BV>(st, s_hist, ((size_t)(cp.first + c) * H + cp.h) * (size_t)D * D,
+                                     cp.v0);
         inter_chunk<D, C, BV, OT, IT>(tiles, sm.cs, st, tok0, len, H, cp.h, cp.v0, scale, o);
     }
     if (sT) chain_store_state<D, BV>(st, sT, sbase, cp.v0);
@@ -1034,7 +1039,7 @@ __global__ __launch_bounds__(64 * (BV / 4 + NP)) void kda_inter_dma(
     int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
     const int* __restrict__ chunk_off, float scale, const IT* __restrict__ v,
     const float* __restrict__ s0, const char* __restrict__ records, float* __restrict__ o,
-    float* __restrict__ sT) {
+    float* __restrict__ sT, float* __restrict__ /*s_hist: not supported here*/) {
     constexpr int NWC = BV / 4;                    // compute wavefronts (one tile each per phase)
     static_assert(64 * (NWC + NP) <= 1024, "workgroup too large");
     constexpr int ST = (D / 16) * (BV / 16);
@@ -1189,6 +1194,641 @@ static hipError_t launch_epilogue(const PrefillArgs& a) {
     return hipGetLastError();
 }
 
+// ===========================================================================
+// Backward: gradients of the chunkwise forward.
+//
+// Per chunk, with S the state at the chunk start and dSn the gradient with
+// respect to the state after it (G, Gamma, KG, QG, KE = K * exp(G_n - G),
+// KI = K / Gamma, A, M, T, Tb as in the forward):
+//   X  = V - KG S,  U = Tb X
+//   dU = scale M^T dO + KE dSn,   dX = Tb^T dU,   dV = dX
+//   dS = Gamma_n * dSn + scale QG^T dO - KG^T dX          (chain, reverse order)
+//   dQG = scale dO S^T,  dKG = -dX S^T,  dKE = U dSn^T,
+//   dM = scale dO U^T (lower),  dTb = dU X^T,  dGamma_n = rowsum(dSn * S)
+//   dT = dTb diag(beta);  dbeta += colsum(dTb * T);  dA = -T^T dT T^T (strict lower)
+//   dbeta += rowsum(dA * P) with P = KG KI^T;  dP = diag(beta) dA
+//   dKG += dP KI;  dKI = dP^T KG + dM^T QG;  dQG += dM KI
+//   dK = dKG Gamma + dKI / Gamma + dKE E;  dQ = dQG Gamma
+//   dG = dKG KG + dQG QG - dKI KI - dKE KE;  dG_n = colsum(dKE KE) + dGamma_n Gamma_n
+//   dg_r = sum_{r' >= r} dG_r' + dG_n
+// Kernels: the forward records (K0/K1) and a forward chain that keeps the
+// state at every chunk start; B3 the reverse chain per (sequence, head,
+// 16-column slice), keeping dSn of every chunk; B4a the products that
+// contract over dv, per (chunk, head), looping over 16-column blocks; B4b the
+// intra-chunk part per (chunk, head) in fp32, looping over 32-channel blocks.
+// All products use fp32 matrix-core tiles (v_mfma_f32_16x16x4f32), whose
+// one-element-per-lane operands make transposed reads plain element loads.
+// ===========================================================================
+
+// acc += sum_{k in [k0, k1)} A(m, k) B(k, n) for one 16x16 tile; a(m, k) and
+// b(k, n) take the row / column inside the tile.  Lane l supplies
+// A(l % 16, k + l / 16) and B(k + l / 16, l % 16); the result holds rows
+// 4 (l / 16) + j, column l % 16.  (k1 - k0) % 4 == 0.
+template <typename FA, typename FB>
+__device__ __forceinline__ float4v tile_mma(float4v acc, int k0, int k1, FA a, FB b) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
+    for (int k = k0; k < k1; k += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, k + lq), b(k + lq, l16), acc, 0, 0, 0);
+    return acc;
+}
+
+// Per-chunk gradient record that B4a hands to B4b (fp32).
+template <int D, int C>
+struct GradRec {
+    static constexpr size_t DQG = 0;                   // [C][D]  scale dO S^T
+    static constexpr size_t DKG = (size_t)C * D;       // [C][D]  -dX S^T
+    static constexpr size_t DKE = 2 * (size_t)C * D;   // [C][D]  U dSn^T
+    static constexpr size_t DM = 3 * (size_t)C * D;    // [C][C]  scale dO U^T (lower)
+    static constexpr size_t DTB = DM + (size_t)C * C;  // [C][C]  dU X^T
+    static constexpr size_t DGN = DTB + (size_t)C * C; // [D]     rowsum(dSn * S)
+    static constexpr size_t floats = (DGN + D + 63) / 64 * 64;
+};
+
+// ---- B3: reverse chain ----
+template <int D, int C, typename OT>
+struct BwdChainSmem {
+    static constexpr int LDV = 17;
+    alignas(16) char img[Rec<D, C, OT>::bytes];
+    float dO[C * LDV];
+    float dS[D * LDV];
+    float dU[C * LDV];
+    float dX[C * LDV];
+};
+
+template <int D, int C, typename OT>
+__global__ __launch_bounds__(256) void kda_bwd_chain(
+    int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
+    const int* __restrict__ chunk_off, float scale, const char* __restrict__ records,
+    const float* __restrict__ d_o, const float* __restrict__ dS_final,
+    float* __restrict__ ds_hist, float* __restrict__ dS0) {
+    constexpr int BV = 16, LDV = 17;
+    typedef Rec<D, C, OT> R;
+    constexpr int CK = R::CK;
+    constexpr int NREC = (int)(R::bytes / 16);
+    constexpr int RPT = (NREC + 255) / 256;
+    constexpr int NDO = (C * BV + 255) / 256;
+    constexpr int RT = C / 16, DT = D / 16, SPW = (DT + 3) / 4;
+    typedef u32x4 vec;
+    extern __shared__ __align__(16) char smem_raw[];
+    BwdChainSmem<D, C, OT>& sm = *reinterpret_cast<BwdChainSmem<D, C, OT>*>(smem_raw);
+
+    const ChainPos cp = chain_pos<D, BV>(T, H, N_seq, nch_seq, G8, cu, chunk_off);
+    if (!cp.valid) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const size_t sbase = ((size_t)cp.n * H + cp.h) * (size_t)D * D;
+    const OT* img = reinterpret_cast<const OT*>(sm.img);
+    const float* gn = reinterpret_cast<const float*>(sm.img + R::gn_byte);
+
+    float4v ds[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int s = wave + 4 * i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            ds[i][j] = (dS_final && s < DT)
+                           ? dS_final[sbase + (size_t)(16 * s + 4 * lq + j) * D + cp.v0 + l16]
+                           : 0.f;
+    }
+    for (int c = cp.nch - 1; c >= 0; --c) {
+        const int chunk = cp.first + c;
+        const int tok0 = cp.seq_tok0 + c * C;
+        const int len = min(C, cp.seq_len - c * C);
+        const vec* rec = reinterpret_cast<const vec*>(records + ((size_t)chunk * H + cp.h) * R::bytes);
+        vec rb[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) rb[i] = rec[min(tid + 256 * i, NREC - 1)];
+        float dov[NDO];
+#pragma unroll
+        for (int i = 0; i < NDO; ++i) {
+            const int idx = min(tid + 256 * i, C * BV - 1);
+            const int r = idx / BV, col = idx % BV;
+            const float x = d_o[((size_t)(tok0 + min(r, len - 1)) * H + cp.h) * D + cp.v0 + col];
+            dov[i] = r < len ? x : 0.f;
+        }
+        // dSn of this chunk, for B4a
+        float* dh = ds_hist + ((size_t)chunk * H + cp.h) * (size_t)D * D;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int s = wave + 4 * i;
+            if (s < DT) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dh[(size_t)(16 * s + 4 * lq + j) * D + cp.v0 + l16] = ds[i][j];
+            }
+        }
+        lds_barrier();   // the previous chunk's reads of LDS are complete
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            if (tid + 256 * i < NREC) reinterpret_cast<vec*>(sm.img)[tid + 256 * i] = rb[i];
+#pragma unroll
+        for (int i = 0; i < NDO; ++i) {
+            const int idx = tid + 256 * i;
+            if (idx < C * BV) sm.dO[(idx / BV) * LDV + idx % BV] = dov[i];
+        }
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int s = wave + 4 * i;
+            if (s < DT) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sm.dS[(16 * s + 4 * lq + j) * LDV + l16] = ds[i][j];
+            }
+        }
+        lds_barrier();
+        // dU = scale M^T dO + KE dSn   (M[i][r] and Tb[i][r] vanish for i < r)
+        for (int rt = wave; rt < RT; rt += 4) {
+            const float4v z = {0.f, 0.f, 0.f, 0.f};
+            const float4v a = tile_mma(
+                z, 16 * rt, C, [&](int m, int k) { return (float)img[R::M + swz<OT, CK>(k, 16 * rt + m)]; },
+                [&](int k, int n) { return sm.dO[k * LDV + n]; });
+            const float4v b = tile_mma(
+                z, 0, D, [&](int m, int k) { return (float)img[R::KPt + swz<OT, CK>(k, 16 * rt + m)]; },
+                [&](int k, int n) { return sm.dS[k * LDV + n]; });
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sm.dU[(16 * rt + 4 * lq + j) * LDV + l16] = scale * a[j] + b[j];
+        }
+        lds_barrier();
+        // dX = Tb^T dU
+        for (int rt = wave; rt < RT; rt += 4) {
+            const float4v z = {0.f, 0.f, 0.f, 0.f};
+            const float4v x = tile_mma(
+                z, 16 * rt, C, [&](int m, int k) { return (float)img[R::Tb + swz<OT, CK>(k, 16 * rt + m)]; },
+                [&](int k, int n) { return sm.dU[k * LDV + n]; });
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sm.dX[(16 * rt + 4 * lq + j) * LDV + l16] = x[j];
+        }
+        lds_barrier();
+        // dS = Gamma_n dSn + scale QG^T dO - KG^T dX
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int s = wave + 4 * i;
+            if (s < DT) {
+                const float4v z = {0.f, 0.f, 0.f, 0.f};
+                const float4v a = tile_mma(
+                    z, 0, C, [&](int m, int k) { return (float)img[R::QG + swz<OT, D>(k, 16 * s + m)]; },
+                    [&](int k, int n) { return sm.dO[k * LDV + n]; });
+                const float4v b = tile_mma(
+                    z, 0, C, [&](int m, int k) { return (float)img[R::KG + swz<OT, D>(k, 16 * s + m)]; },
+                    [&](int k, int n) { return sm.dX[k * LDV + n]; });
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    ds[i][j] = gn[16 * s + 4 * lq + j] * ds[i][j] + scale * a[j] - b[j];
+            }
+        }
+    }
+    if (dS0) {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int s = wave + 4 * i;
+            if (s < DT) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dS0[sbase + (size_t)(16 * s + 4 * lq + j) * D + cp.v0 + l16] = ds[i][j];
+            }
+        }
+    }
+}
+
+// ---- B4a: products over dv, per (chunk, head), 16-column value blocks ----
+template <int D, int C, typename OT>
+struct BwdDvSmem {
+    static constexpr int LDV = 17;
+    static constexpr int CK = chunk_k<C, OT>();
+    OT kg[C * D];                      // record KG (swizzled)
+    OT tail[D * CK + 2 * C * CK];      // record KPt, Tb, M (swizzled)
+    float S[D * LDV], dSn[D * LDV];
+    float dO[C * LDV], V[C * LDV], X[C * LDV], U[C * LDV], dU[C * LDV], dX[C * LDV];
+};
+
+template <int D, int C, typename OT, typename IT>
+__global__ __launch_bounds__(256) void kda_bwd_dv(
+    int T, int H, int nch_seq, const ChunkInfo* __restrict__ table,
+    const int* __restrict__ chunk_total, float scale, const IT* __restrict__ v,
+    const char* __restrict__ records, const float* __restrict__ s_hist,
+    const float* __restrict__ ds_hist, const float* __restrict__ d_o,
+    float* __restrict__ grec, float* __restrict__ dv_out) {
+    constexpr int BV = 16, LDV = 17;
+    typedef Rec<D, C, OT> R;
+    typedef GradRec<D, C> GR;
+    constexpr int CK = R::CK;
+    constexpr int RT = C / 16, DT = D / 16;
+    constexpr int NQ = RT * DT, QPW = (NQ + 3) / 4;     // C x D tiles per wavefront
+    constexpr int NM = RT * RT, MPW = (NM + 3) / 4;     // C x C tiles per wavefront
+    typedef u32x4 vec;
+    extern __shared__ __align__(16) char smem_raw[];
+    BwdDvSmem<D, C, OT>& sm = *reinterpret_cast<BwdDvSmem<D, C, OT>*>(smem_raw);
+
+    const int ch = blockIdx.x, h = blockIdx.y;
+    int tok0, len;
+    if (table) {
+        if (ch >= *chunk_total) return;
+        const ChunkInfo ci = table[ch];
+        tok0 = ci.tok0;
+        len = ci.len;
+    } else {
+        const int b = ch / nch_seq, c = ch - b * nch_seq;
+        tok0 = b * T + c * C;
+        len = min(C, T - c * C);
+    }
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const char* recb = records + ((size_t)ch * H + h) * R::bytes;
+    {   // stage KG and the KPt / Tb / M tail of the record
+        constexpr int NKG = (int)(C * D * sizeof(OT) / 16);
+        constexpr int NTL = (int)((D * CK + 2 * C * CK) * sizeof(OT) / 16);
+        const vec* a = reinterpret_cast<const vec*>(recb + R::KG * sizeof(OT));
+        const vec* b = reinterpret_cast<const vec*>(recb + R::KPt * sizeof(OT));
+        for (int i = tid; i < NKG; i += 256) reinterpret_cast<vec*>(sm.kg)[i] = a[i];
+        for (int i = tid; i < NTL; i += 256) reinterpret_cast<vec*>(sm.tail)[i] = b[i];
+    }
+    const OT* kpt = sm.tail;
+    const OT* tb = sm.tail + D * CK;
+    const OT* mm = sm.tail + D * CK + C * CK;
+    const float* Sh = s_hist + ((size_t)ch * H + h) * (size_t)D * D;
+    const float* dSh = ds_hist + ((size_t)ch * H + h) * (size_t)D * D;
+
+    float4v aq[QPW], ak[QPW], ae[QPW], am[MPW], at[MPW];
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) aq[i] = ak[i] = ae[i] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) am[i] = at[i] = float4v{0.f, 0.f, 0.f, 0.f};
+    float agn = 0.f;
+    const float4v z = {0.f, 0.f, 0.f, 0.f};
+
+    for (int vb = 0; vb < D; vb += BV) {
+        lds_barrier();   // previous block's reads complete (and, first time, staging visible)
+        for (int idx = tid; idx < D * BV; idx += 256) {
+            const int c = idx / BV, col = idx % BV;
+            sm.S[c * LDV + col] = Sh[(size_t)c * D + vb + col];
+            sm.dSn[c * LDV + col] = dSh[(size_t)c * D + vb + col];
+        }
+        for (int idx = tid; idx < C * BV; idx += 256) {
+            const int r = idx / BV, col = idx % BV;
+            const size_t off = ((size_t)(tok0 + min(r, len - 1)) * H + h) * D + vb + col;
+            sm.dO[r * LDV + col] = r < len ? d_o[off] : 0.f;
+            sm.V[r * LDV + col] = r < len ? to_f32(v[off]) : 0.f;
+        }
+        lds_barrier();
+        // X = V - KG S ; dU = scale M^T dO + KE dSn
+        for (int rt = wave; rt < RT; rt += 4) {
+            const float4v x = tile_mma(
+                z, 0, D, [&](int m, int k) { return (float)sm.kg[swz<OT, D>(16 * rt + m, k)]; },
+                [&](int k, int n) { return sm.S[k * LDV + n]; });
+            const float4v a = tile_mma(
+                z, 16 * rt, C, [&](int m, int k) { return (float)mm[swz<OT, CK>(k, 16 * rt + m)]; },
+                [&](int k, int n) { return sm.dO[k * LDV + n]; });
+            const float4v b = tile_mma(
+                z, 0, D, [&](int m, int k) { return (float)kpt[swz<OT, CK>(k, 16 * rt + m)]; },
+                [&](int k, int n) { return sm.dSn[k * LDV + n]; });
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * rt + 4 * lq + j;
+                sm.X[r * LDV + l16] = sm.V[r * LDV + l16] - x[j];
+                sm.dU[r * LDV + l16] = scale * a[j] + b[j];
+            }
+        }
+        lds_barrier();
+        // U = Tb X (Tb[r][i] = 0 for i > r) ; dX = Tb^T dU ; dV = dX
+        for (int rt = wave; rt < RT; rt += 4) {
+            const float4v u = tile_mma(
+                z, 0, 16 * (rt + 1), [&](int m, int k) { return (float)tb[swz<OT, CK>(16 * rt + m, k)]; },
+                [&](int k, int n) { return sm.X[k * LDV + n]; });
+            const float4v x = tile_mma(
+                z, 16 * rt, C, [&](int m, int k) { return (float)tb[swz<OT, CK>(k, 16 * rt + m)]; },
+                [&](int k, int n) { return sm.dU[k * LDV + n]; });
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * rt + 4 * lq + j;
+                sm.U[r * LDV + l16] = u[j];
+                sm.dX[r * LDV + l16] = x[j];
+                if (r < len) dv_out[((size_t)(tok0 + r) * H + h) * D + vb + l16] = x[j];
+            }
+        }
+        lds_barrier();
+        // accumulate the products over this block's dv columns
+#pragma unroll
+        for (int i = 0; i < QPW; ++i) {
+            const int t = wave + 4 * i;
+            if (t < NQ) {
+                const int rt = t / DT, ct = t % DT;
+                aq[i] = tile_mma(aq[i], 0, BV, [&](int m, int k) { return sm.dO[(16 * rt + m) * LDV + k]; },
+                                 [&](int k, int n) { return sm.S[(16 * ct + n) * LDV + k]; });
+                ak[i] = tile_mma(ak[i], 0, BV, [&](int m, int k) { return sm.dX[(16 * rt + m) * LDV + k]; },
+                                 [&](int k, int n) { return sm.S[(16 * ct + n) * LDV + k]; });
+                ae[i] = tile_mma(ae[i], 0, BV, [&](int m, int k) { return sm.U[(16 * rt + m) * LDV + k]; },
+                                 [&](int k, int n) { return sm.dSn[(16 * ct + n) * LDV + k]; });
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const int t = wave + 4 * i;
+            if (t < NM) {
+                const int rt = t / RT, ct = t % RT;
+                am[i] = tile_mma(am[i], 0, BV, [&](int m, int k) { return sm.dO[(16 * rt + m) * LDV + k]; },
+                                 [&](int k, int n) { return sm.U[(16 * ct + n) * LDV + k]; });
+                at[i] = tile_mma(at[i], 0, BV, [&](int m, int k) { return sm.dU[(16 * rt + m) * LDV + k]; },
+                                 [&](int k, int n) { return sm.X[(16 * ct + n) * LDV + k]; });
+            }
+        }
+        if (tid < D) {
+#pragma unroll
+            for (int col = 0; col < BV; ++col) agn += sm.dSn[tid * LDV + col] * sm.S[tid * LDV + col];
+        }
+    }
+    float* gr = grec + ((size_t)ch * H + h) * GR::floats;
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+        const int t = wave + 4 * i;
+        if (t < NQ) {
+            const int rt = t / DT, ct = t % DT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const size_t e = (size_t)(16 * rt + 4 * lq + j) * D + 16 * ct + l16;
+                gr[GR::DQG + e] = scale * aq[i][j];
+                gr[GR::DKG + e] = -ak[i][j];
+                gr[GR::DKE + e] = ae[i][j];
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+        const int t = wave + 4 * i;
+        if (t < NM) {
+            const int rt = t / RT, ct = t % RT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * rt + 4 * lq + j, c = 16 * ct + l16;
+                gr[GR::DM + (size_t)r * C + c] = c <= r ? scale * am[i][j] : 0.f;
+                gr[GR::DTB + (size_t)r * C + c] = at[i][j];
+            }
+        }
+    }
+    if (tid < D) gr[GR::DGN + tid] = agn;
+}
+
+// ---- B4b: intra-chunk backward, per (chunk, head), fp32 ----
+template <int C>
+struct BwdIntraSmem {
+    static constexpr int LDC = C + 1, CB = 32, LDB = CB + 1;
+    float P[C * LDC];      // KG KI^T
+    float Tm[C * LDC];     // T = (I + A)^-1
+    float dP[C * LDC];     // dTb, then dA / dP
+    float dM[C * LDC];
+    float Y[C * LDC];      // scratch product
+    float G[C * LDB], kg[C * LDB], ki[C * LDB], qg[C * LDB];
+    float x1[C * LDB], x2[C * LDB], x3[C * LDB];    // dKG, dKI, dQG of the channel block
+    float beta[C], dbeta[C];
+};
+
+template <int D, int C, typename IT>
+__global__ __launch_bounds__(256) void kda_bwd_intra(
+    int T, int H, int nch_seq, const ChunkInfo* __restrict__ table,
+    const int* __restrict__ chunk_total, const IT* __restrict__ q, const IT* __restrict__ k,
+    const float* __restrict__ g, const float* __restrict__ beta,
+    const float* __restrict__ grec, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dg, float* __restrict__ dbeta) {
+    typedef GradRec<D, C> GR;
+    typedef BwdIntraSmem<C> SM;
+    constexpr int LDC = SM::LDC, CB = SM::CB, LDB = SM::LDB;
+    constexpr int RT = C / 16, NM = RT * RT, MPW = (NM + 3) / 4;
+    constexpr int NBT = RT * (CB / 16), BPW = (NBT + 3) / 4;   // C x CB tiles per wavefront
+    extern __shared__ __align__(16) char smem_raw[];
+    SM& sm = *reinterpret_cast<SM*>(smem_raw);
+
+    const int ch = blockIdx.x, h = blockIdx.y;
+    int tok0, len;
+    if (table) {
+        if (ch >= *chunk_total) return;
+        const ChunkInfo ci = table[ch];
+        tok0 = ci.tok0;
+        len = ci.len;
+    } else {
+        const int b = ch / nch_seq, c = ch - b * nch_seq;
+        tok0 = b * T + c * C;
+        len = min(C, T - c * C);
+    }
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const float* gr = grec + ((size_t)ch * H + h) * GR::floats;
+    const float4v z = {0.f, 0.f, 0.f, 0.f};
+    auto tok = [&](int r) { return ((size_t)(tok0 + min(r, len - 1)) * H + h) * D; };
+
+    if (tid < C) {
+        sm.beta[tid] = tid < len ? beta[(size_t)(tok0 + min(tid, len - 1)) * H + h] : 0.f;
+        sm.dbeta[tid] = 0.f;
+    }
+    // G, KG = K Gamma, KI = K / Gamma (and QG) of one 32-channel block
+    auto load_block = [&](int c0, bool with_q) {
+        for (int idx = tid; idx < C * CB; idx += 256) {
+            const int r = idx / CB, c = idx % CB;
+            const float x = g[tok(r) + c0 + c];
+            sm.G[r * LDB + c] = r < len ? x : 0.f;
+        }
+        lds_barrier();
+        if (tid < CB) {   // running sum over the chunk, per channel
+            float acc = 0.f;
+            for (int r = 0; r < C; ++r) {
+                acc += sm.G[r * LDB + tid];
+                sm.G[r * LDB + tid] = acc;
+            }
+        }
+        lds_barrier();
+        for (int idx = tid; idx < C * CB; idx += 256) {
+            const int r = idx / CB, c = idx % CB;
+            const float G = sm.G[r * LDB + c];
+            const float kk = r < len ? to_f32(k[tok(r) + c0 + c]) : 0.f;
+            sm.kg[r * LDB + c] = kk * exp_e(G);
+            sm.ki[r * LDB + c] = kk * exp_e(-G);
+            if (with_q) sm.qg[r * LDB + c] = (r < len ? to_f32(q[tok(r) + c0 + c]) : 0.f) * exp_e(G);
+        }
+        lds_barrier();
+    };
+
+    // ---- pass 1: P = KG KI^T over the channel blocks ----
+    float4v ap[MPW];
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) ap[i] = z;
+    for (int c0 = 0; c0 < D; c0 += CB) {
+        load_block(c0, false);
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const int t = wave + 4 * i;
+            if (t < NM) {
+                const int rt = t / RT, ct = t % RT;
+                ap[i] = tile_mma(ap[i], 0, CB, [&](int m, int kk) { return sm.kg[(16 * rt + m) * LDB + kk]; },
+                                 [&](int kk, int n) { return sm.ki[(16 * ct + n) * LDB + kk]; });
+            }
+        }
+        lds_barrier();
+    }
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+        const int t = wave + 4 * i;
+        if (t < NM) {
+            const int rt = t / RT, ct = t % RT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sm.P[(16 * rt + 4 * lq + j) * LDC + 16 * ct + l16] = ap[i][j];
+        }
+    }
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int r = idx / C, c = idx % C;
+        sm.dP[r * LDC + c] = gr[GR::DTB + idx];
+        sm.dM[r * LDC + c] = gr[GR::DM + idx];
+    }
+    lds_barrier();
+    // ---- T = (I + A)^-1, A = diag(beta) strict_lower(P): one column per lane ----
+    if (wave == 0 && lane < C) {
+        for (int i = 0; i < C; ++i) {
+            float acc = 0.f;
+            for (int m = 0; m < i; ++m) acc += sm.P[i * LDC + m] * sm.Tm[m * LDC + lane];
+            sm.Tm[i * LDC + lane] = (i == lane ? 1.f : 0.f) - sm.beta[i] * acc;
+        }
+    }
+    lds_barrier();
+    // dbeta (from Tb = T diag beta) = colsum(dTb * T); dT = dTb diag(beta) -> Y
+    if (tid < C) {
+        float acc = 0.f;
+        for (int i = 0; i < C; ++i) acc += sm.dP[i * LDC + tid] * sm.Tm[i * LDC + tid];
+        sm.dbeta[tid] = acc;
+    }
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int r = idx / C, c = idx % C;
+        sm.Y[r * LDC + c] = sm.dP[r * LDC + c] * sm.beta[c];
+    }
+    lds_barrier();
+    // dP <- dT T^T
+    {
+        float4v a[MPW];
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const int t = wave + 4 * i;
+            a[i] = z;
+            if (t < NM) {
+                const int rt = t / RT, ct = t % RT;
+                a[i] = tile_mma(z, 0, C, [&](int m, int kk) { return sm.Y[(16 * rt + m) * LDC + kk]; },
+                                [&](int kk, int n) { return sm.Tm[(16 * ct + n) * LDC + kk]; });
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const int t = wave + 4 * i;
+            if (t < NM) {
+                const int rt = t / RT, ct = t % RT;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sm.dP[(16 * rt + 4 * lq + j) * LDC + 16 * ct + l16] = a[i][j];
+            }
+        }
+        lds_barrier();
+        // dA = -T^T (dT T^T), strict lower; dbeta += rowsum(dA * P); dP = diag(beta) dA
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const int t = wave + 4 * i;
+            a[i] = z;
+            if (t < NM) {
+                const int rt = t / RT, ct = t % RT;
+                a[i] = tile_mma(z, 0, C, [&](int m, int kk) { return sm.Tm[kk * LDC + 16 * rt + m]; },
+                                [&](int kk, int n) { return sm.dP[kk * LDC + 16 * ct + n]; });
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const int t = wave + 4 * i;
+            if (t < NM) {
+                const int rt = t / RT, ct = t % RT;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j, c = 16 * ct + l16;
+                    sm.Y[r * LDC + c] = c < r ? -a[i][j] : 0.f;     // dA
+                }
+            }
+        }
+        lds_barrier();
+    }
+    if (tid < C) {
+        float acc = 0.f;
+        for (int c = 0; c < tid; ++c) acc += sm.Y[tid * LDC + c] * sm.P[tid * LDC + c];
+        sm.dbeta[tid] += acc;
+    }
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int r = idx / C, c = idx % C;
+        sm.dP[r * LDC + c] = sm.beta[r] * sm.Y[r * LDC + c];
+    }
+    lds_barrier();
+    if (tid < len) dbeta[(size_t)(tok0 + tid) * H + h] = sm.dbeta[tid];
+
+    // ---- pass 2: per channel block, the K, Q and gate gradients ----
+    for (int c0 = 0; c0 < D; c0 += CB) {
+        load_block(c0, true);
+        // dKG += dP KI ; dKI = dP^T KG + dM^T QG ; dQG += dM KI  (C x CB tiles)
+        float4v b1[BPW], b2[BPW], b3[BPW];
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) {
+            const int t = wave + 4 * i;
+            b1[i] = b2[i] = b3[i] = z;
+            if (t < NBT) {
+                const int rt = t / (CB / 16), ct = t % (CB / 16);
+                b1[i] = tile_mma(z, 0, C, [&](int m, int kk) { return sm.dP[(16 * rt + m) * LDC + kk]; },
+                                 [&](int kk, int n) { return sm.ki[kk * LDB + 16 * ct + n]; });
+                b2[i] = tile_mma(z, 0, C, [&](int m, int kk) { return sm.dP[kk * LDC + 16 * rt + m]; },
+                                 [&](int kk, int n) { return sm.kg[kk * LDB + 16 * ct + n]; });
+                b2[i] = tile_mma(b2[i], 0, C, [&](int m, int kk) { return sm.dM[kk * LDC + 16 * rt + m]; },
+                                 [&](int kk, int n) { return sm.qg[kk * LDB + 16 * ct + n]; });
+                b3[i] = tile_mma(z, 0, C, [&](int m, int kk) { return sm.dM[(16 * rt + m) * LDC + kk]; },
+                                 [&](int kk, int n) { return sm.ki[kk * LDB + 16 * ct + n]; });
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) {
+            const int t = wave + 4 * i;
+            if (t < NBT) {
+                const int rt = t / (CB / 16), ct = t % (CB / 16);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j, c = 16 * ct + l16;
+                    sm.x1[r * LDB + c] = b1[i][j] + gr[GR::DKG + (size_t)r * D + c0 + c];
+                    sm.x2[r * LDB + c] = b2[i][j];
+                    sm.x3[r * LDB + c] = b3[i][j] + gr[GR::DQG + (size_t)r * D + c0 + c];
+                }
+            }
+        }
+        lds_barrier();
+        // element-wise: dK, dQ, and dG (into x2 after use); dG_n per channel
+        for (int idx = tid; idx < C * CB; idx += 256) {
+            const int r = idx / CB, c = idx % CB;
+            const float G = sm.G[r * LDB + c];
+            const float Gn = sm.G[(C - 1) * LDB + c];
+            const float kk = r < len ? to_f32(k[tok(r) + c0 + c]) : 0.f;
+            const float ga = exp_e(G), gi = exp_e(-G), e = exp_e(Gn - G);
+            const float dKG = sm.x1[r * LDB + c], dKI = sm.x2[r * LDB + c], dQG = sm.x3[r * LDB + c];
+            const float dKE = gr[GR::DKE + (size_t)r * D + c0 + c];
+            const float dK = dKG * ga + dKI * gi + dKE * e;
+            const float dQ = dQG * ga;
+            const float dG = dKG * sm.kg[r * LDB + c] + dQG * sm.qg[r * LDB + c] -
+                             dKI * sm.ki[r * LDB + c] - dKE * kk * e;
+            if (r < len) {
+                dk[tok(r) + c0 + c] = dK;
+                dq[tok(r) + c0 + c] = dQ;
+            }
+            sm.x1[r * LDB + c] = dG;
+            sm.x2[r * LDB + c] = dKE * kk * e;
+        }
+        lds_barrier();
+        if (tid < CB) {
+            const int c = tid;
+            const float Gn = sm.G[(C - 1) * LDB + c];
+            float dGn = gr[GR::DGN + c0 + c] * exp_e(Gn);
+            for (int r = 0; r < C; ++r) dGn += sm.x2[r * LDB + c];
+            float acc = dGn;
+            for (int r = C - 1; r >= 0; --r) {
+                acc += sm.x1[r * LDB + c];
+                if (r < len) dg[tok(r) + c0 + c] = acc;
+            }
+        }
+        lds_barrier();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side: planning and dispatch.
 // ---------------------------------------------------------------------------
@@ -1273,7 +1913,7 @@ static hipError_t launch_inter(const PrefillArgs& a, const PrefillPlan& plan, in
                                const int* chunk_off) {
     size_t smem;
     void (*kern)(int, int, int, int, int, const int*, const int*, float, const IT*, const float*,
-                 const char*, float*, float*);
+                 const char*, float*, float*, float*);
     if constexpr (KIND == 1) {
         smem = inter_dma_smem_bytes<D, C, BV, OT, IT>();
         kern = kda_inter_dma<D, C, BV, OT, IT, kProducers>;
@@ -1289,8 +1929,42 @@ static hipError_t launch_inter(const PrefillArgs& a, const PrefillPlan& plan, in
     const int threads = KIND == 0 ? 256 : 64 * (BV / 4 + kProducers);
     hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(threads), smem, a.stream, a.T, a.H,
                        a.N, nch_seq, (int)G8, a.cu_seqlens, chunk_off, a.scale, (const IT*)a.v,
-                       a.s0, (const char*)a.workspace + plan.off_records, a.o, a.sT);
+                       a.s0, (const char*)a.workspace + plan.off_records, a.o, a.sT,
+                       (float*)nullptr);
     return hipGetLastError();
+}
+
+// K0 (packed sequences) and K1: the chunk table and the chunk records.
+template <int D, int C, typename OT, typename IT>
+static hipError_t launch_records(const PrefillArgs& a, const PrefillPlan& plan, int nch_seq,
+                                 int** chunk_off, ChunkInfo** table) {
+    const bool varlen = a.cu_seqlens != nullptr;
+    char* ws = (char*)a.workspace;
+    *chunk_off = nullptr;
+    *table = nullptr;
+    if (varlen) {
+        *chunk_off = reinterpret_cast<int*>(ws + plan.off_table);
+        *table = reinterpret_cast<ChunkInfo*>(
+            ws + plan.off_table + ((size_t)(a.N + 1) * sizeof(int) + 255) / 256 * 256);
+        hipLaunchKernelGGL(kda_chunk_table, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, a.N,
+                           a.T, C, plan.nchunk_max, *chunk_off, *table);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (plan.nchunk_max > 0) {
+        const size_t smem = intra_smem_bytes<D, C, OT>();
+        auto kern = a.prep.active() ? kda_intra<D, C, OT, IT, true> : kda_intra<D, C, OT, IT, false>;
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)plan.nchunk_max, (unsigned)a.H), dim3(256), smem,
+                           a.stream, a.T, a.H, nch_seq, *table,
+                           varlen ? *chunk_off + a.N : nullptr, (const IT*)a.q, (const IT*)a.k,
+                           a.g, a.beta, ws + plan.off_records, a.prep);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int D, int C, typename OT, typename IT>
@@ -1300,31 +1974,10 @@ static hipError_t launch_dc(const PrefillArgs& a, const PrefillPlan& plan) {
     } else {
         const bool varlen = a.cu_seqlens != nullptr;
         const int nch_seq = varlen ? 0 : (a.T + C - 1) / C;
-        char* ws = (char*)a.workspace;
-        int* chunk_off = nullptr;
-        ChunkInfo* table = nullptr;
-        if (varlen) {
-            chunk_off = reinterpret_cast<int*>(ws + plan.off_table);
-            table = reinterpret_cast<ChunkInfo*>(
-                ws + plan.off_table + ((size_t)(a.N + 1) * sizeof(int) + 255) / 256 * 256);
-            hipLaunchKernelGGL(kda_chunk_table, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens,
-                               a.N, a.T, C, plan.nchunk_max, chunk_off, table);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-        if (plan.nchunk_max > 0) {
-            const size_t smem = intra_smem_bytes<D, C, OT>();
-            auto kern = a.prep.active() ? kda_intra<D, C, OT, IT, true> : kda_intra<D, C, OT, IT, false>;
-            hipError_t e = hipFuncSetAttribute(
-                (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(kern, dim3((unsigned)plan.nchunk_max, (unsigned)a.H), dim3(256),
-                               smem, a.stream, a.T, a.H, nch_seq, table,
-                               varlen ? chunk_off + a.N : nullptr, (const IT*)a.q,
-                               (const IT*)a.k, a.g, a.beta, ws + plan.off_records, a.prep);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
+        int* chunk_off;
+        ChunkInfo* table;
+        if (hipError_t e = launch_records<D, C, OT, IT>(a, plan, nch_seq, &chunk_off, &table))
+            return e;
         constexpr bool kBf = sizeof(OT) == 2;
         constexpr bool kDma16 = kBf && inter_dma_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
         constexpr bool kDma32 = kBf && D >= 32 && inter_dma_smem_bytes<D, C, 32, OT, IT>() <= kLdsLimit;
@@ -1359,6 +2012,149 @@ static hipError_t launch_d(const PrefillArgs& a, const PrefillPlan& plan) {
     }
     if (e != hipSuccess || !a.epi.on) return e;
     return launch_epilogue<D, IT>(a);
+}
+
+// ---- backward host side ----
+template <int D, int C, typename OT, typename IT>
+constexpr bool bwd_fits() {
+    return sizeof(BwdChainSmem<D, C, OT>) <= kLdsLimit && sizeof(BwdDvSmem<D, C, OT>) <= kLdsLimit &&
+           sizeof(BwdIntraSmem<C>) <= kLdsLimit && fits<D, C, OT>() &&
+           inter_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
+}
+
+bool backward_supported(int D, int C, bool bf16) {
+    if (!(D == 32 || D == 64 || D == 128) || !(C == 16 || C == 32 || C == 64)) return false;
+#define KDA_BFITS(DD, CC)                                                                      \
+    if (D == DD && C == CC)                                                                    \
+        return bf16 ? bwd_fits<DD, CC, float, bf16_t>() : bwd_fits<DD, CC, float, float>();
+    KDA_BFITS(32, 16) KDA_BFITS(32, 32) KDA_BFITS(32, 64)
+    KDA_BFITS(64, 16) KDA_BFITS(64, 32) KDA_BFITS(64, 64)
+    KDA_BFITS(128, 16) KDA_BFITS(128, 32) KDA_BFITS(128, 64)
+#undef KDA_BFITS
+    return false;
+}
+
+static size_t grad_rec_floats(int D, int C) {
+    return ((size_t)3 * C * D + 2 * (size_t)C * C + D + 63) / 64 * 64;
+}
+
+bool backward_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf16,
+                   BackwardPlan* plan) {
+    (void)bf16;   // the backward keeps fp32 records for either input type
+    if (!prefill_plan(B, T, H, D, C, N, varlen, false, &plan->f)) return false;
+    const size_t nch = (size_t)plan->f.nchunk_max;
+    const size_t hist = (nch * H * (size_t)D * D * sizeof(float) + 255) / 256 * 256;
+    plan->grec_floats = grad_rec_floats(D, C);
+    size_t off = plan->f.total;
+    plan->off_shist = off;
+    off += hist;
+    plan->off_dshist = off;
+    off += hist;
+    plan->off_grec = off;
+    off += (nch * H * plan->grec_floats * sizeof(float) + 255) / 256 * 256;
+    plan->total = off;
+    return true;
+}
+
+template <typename K>
+static hipError_t set_smem(K kern, size_t bytes) {
+    return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
+}
+
+template <int D, int C, typename OT, typename IT>
+static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan) {
+    if constexpr (!bwd_fits<D, C, OT, IT>()) {
+        return hipErrorInvalidValue;
+    } else {
+        static_assert(GradRec<D, C>::floats == ((size_t)3 * C * D + 2 * C * C + D + 63) / 64 * 64,
+                      "gradient record size");
+        const PrefillArgs& a = b.f;
+        const bool varlen = a.cu_seqlens != nullptr;
+        const int nch_seq = varlen ? 0 : (a.T + C - 1) / C;
+        char* ws = (char*)a.workspace;
+        float* s_hist = reinterpret_cast<float*>(ws + plan.off_shist);
+        float* ds_hist = reinterpret_cast<float*>(ws + plan.off_dshist);
+        float* grec = reinterpret_cast<float*>(ws + plan.off_grec);
+        int* chunk_off;
+        ChunkInfo* table;
+        if (hipError_t e = launch_records<D, C, OT, IT>(a, plan.f, nch_seq, &chunk_off, &table))
+            return e;
+        const long long chains = (long long)a.N * a.H;
+        const long long G8 = (chains + 7) / 8 * (D / 16);
+        // forward chain keeping the state at every chunk start
+        {
+            auto kern = kda_inter<D, C, 16, OT, IT>;
+            const size_t smem = inter_smem_bytes<D, C, 16, OT, IT>();
+            if (hipError_t e = set_smem(kern, smem)) return e;
+            hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(256), smem, a.stream, a.T, a.H, a.N,
+                               nch_seq, (int)G8, a.cu_seqlens, chunk_off, a.scale,
+                               (const IT*)a.v, a.s0, (const char*)ws + plan.f.off_records,
+                               (float*)nullptr, (float*)nullptr, s_hist);
+            if (hipError_t e = hipGetLastError()) return e;
+        }
+        // B3: reverse chain
+        {
+            auto kern = kda_bwd_chain<D, C, OT>;
+            if (hipError_t e = set_smem(kern, sizeof(BwdChainSmem<D, C, OT>))) return e;
+            hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(256),
+                               sizeof(BwdChainSmem<D, C, OT>), a.stream, a.T, a.H, a.N, nch_seq,
+                               (int)G8, a.cu_seqlens, chunk_off, a.scale,
+                               (const char*)ws + plan.f.off_records, b.d_o, b.dS_final, ds_hist,
+                               b.dS0);
+            if (hipError_t e = hipGetLastError()) return e;
+        }
+        if (plan.f.nchunk_max == 0) return hipSuccess;
+        const dim3 grid((unsigned)plan.f.nchunk_max, (unsigned)a.H);
+        const int* total = varlen ? chunk_off + a.N : nullptr;
+        // B4a: products over dv, and dv
+        {
+            auto kern = kda_bwd_dv<D, C, OT, IT>;
+            if (hipError_t e = set_smem(kern, sizeof(BwdDvSmem<D, C, OT>))) return e;
+            hipLaunchKernelGGL(kern, grid, dim3(256), sizeof(BwdDvSmem<D, C, OT>), a.stream, a.T,
+                               a.H, nch_seq, table, total, a.scale, (const IT*)a.v,
+                               (const char*)ws + plan.f.off_records, s_hist, ds_hist, b.d_o, grec,
+                               b.dv);
+            if (hipError_t e = hipGetLastError()) return e;
+        }
+        // B4b: intra-chunk part
+        {
+            auto kern = kda_bwd_intra<D, C, IT>;
+            if (hipError_t e = set_smem(kern, sizeof(BwdIntraSmem<C>))) return e;
+            hipLaunchKernelGGL(kern, grid, dim3(256), sizeof(BwdIntraSmem<C>), a.stream, a.T, a.H,
+                               nch_seq, table, total, (const IT*)a.q, (const IT*)a.k, a.g, a.beta,
+                               grec, b.dq, b.dk, b.dg, b.dbeta);
+            if (hipError_t e = hipGetLastError()) return e;
+        }
+        return hipSuccess;
+    }
+}
+
+template <int D, typename OT, typename IT>
+static hipError_t launch_bwd_d(const BackwardArgs& b, const BackwardPlan& plan) {
+    switch (b.f.C) {
+        case 16: return launch_bwd_dc<D, 16, OT, IT>(b, plan);
+        case 32: return launch_bwd_dc<D, 32, OT, IT>(b, plan);
+        case 64: return launch_bwd_dc<D, 64, OT, IT>(b, plan);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_backward(const BackwardArgs& b, const BackwardPlan& plan) {
+    if (b.f.bf16) {
+        switch (b.f.D) {
+            case 32: return launch_bwd_d<32, float, bf16_t>(b, plan);
+            case 64: return launch_bwd_d<64, float, bf16_t>(b, plan);
+            case 128: return launch_bwd_d<128, float, bf16_t>(b, plan);
+        }
+    } else {
+        switch (b.f.D) {
+            case 32: return launch_bwd_d<32, float, float>(b, plan);
+            case 64: return launch_bwd_d<64, float, float>(b, plan);
+            case 128: return launch_bwd_d<128, float, float>(b, plan);
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan) {

@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(lib):
     names = header_functions()
     assert set(names) == {"kda_status_string", "kda_version", "kda_chunk_fwd_workspace_bytes",
                           "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_decode_step",
-                          "kda_decode_step_ex"}
+                          "kda_decode_step_ex", "kda_chunk_bwd_workspace_bytes",
+                          "kda_chunk_bwd"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in kda.SIGNATURES, n
@@ -134,3 +135,39 @@ def test_prep_and_epilogue_validation(lib):
         assert call(epi=epi_inf_eps) == E["KDA_ERR_BAD_SHAPE"]
         assert call(epi=epi_odd_w) == E["KDA_ERR_NULL_ARG"]
         assert call(epi=epi_odd_gate) == E["KDA_ERR_NULL_ARG"]
+
+
+def test_backward_workspace_and_validation(lib):
+    """The backward's workspace holds fp32 chunk records plus two fp32 states
+    per (chunk, head) and a gradient record; bad arguments are rejected on the
+    host."""
+    E = {v: k for k, v in kda.STATUS_NAMES.items()}
+    wf = lib.kda_chunk_fwd_workspace_bytes
+    wb = lib.kda_chunk_bwd_workspace_bytes
+    nch, H, d, C = 512, 32, 128, 64
+    grec = (3 * C * d + 2 * C * C + d + 63) // 64 * 64
+    # fp32 chunk records for either input type
+    assert wb(1, 32768, H, d, d, C, 0, kda.KDA_BF16) == (
+        wf(1, 32768, H, d, d, C, 0, kda.KDA_F32) + 2 * nch * H * d * d * 4 + nch * H * grec * 4)
+    assert wb(1, 32768, H, d, d, C, 0, kda.KDA_BF16) == wb(1, 32768, H, d, d, C, 0, kda.KDA_F32)
+    assert wb(1, 100, 2, 64, 32, 64, 0, kda.KDA_BF16) == 0
+    assert wb(1, 100, 2, 64, 64, 48, 0, kda.KDA_BF16) == 0
+    assert wb(2, 100, 2, 64, 64, 64, 3, kda.KDA_BF16) == 0
+    p = ctypes.c_void_p(4096)
+
+    def bwd(B=1, T=64, H=2, dk=64, dv=64, chunk=64, dtype=kda.KDA_BF16, ptr=p, gb=p, dS0=None,
+            cu=None, nseq=0, ws=p, wsb=1 << 34):
+        return lib.kda_chunk_bwd(B, T, H, dk, dv, chunk, 1.0, dtype, ptr, ptr, ptr, ptr, ptr,
+                                 None, cu, nseq, ptr, None, ptr, ptr, ptr, ptr, gb, dS0, ws, wsb,
+                                 None)
+    assert bwd(B=0) == E["KDA_ERR_BAD_SHAPE"]
+    assert bwd(dtype=5) == E["KDA_ERR_BAD_DTYPE"]
+    assert bwd(dk=64, dv=128) == E["KDA_ERR_UNSUPPORTED"]
+    assert bwd(chunk=8) == E["KDA_ERR_UNSUPPORTED"]
+    assert bwd(ptr=None) == E["KDA_ERR_NULL_ARG"]
+    assert bwd(ptr=ctypes.c_void_p(4104)) == E["KDA_ERR_NULL_ARG"]
+    assert bwd(gb=ctypes.c_void_p(4098)) == E["KDA_ERR_NULL_ARG"]     # grad_beta: 4-byte
+    assert bwd(dS0=ctypes.c_void_p(4100)) == E["KDA_ERR_NULL_ARG"]
+    assert bwd(B=2, cu=p, nseq=2) == E["KDA_ERR_BAD_SHAPE"]
+    assert bwd(wsb=1024) == E["KDA_ERR_WORKSPACE"]
+    assert bwd(ws=ctypes.c_void_p(4096 + 64)) == E["KDA_ERR_WORKSPACE"]
