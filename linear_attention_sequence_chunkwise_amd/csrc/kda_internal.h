@@ -79,11 +79,12 @@ struct BackwardArgs {
     float* dS0;             // [N, H, dk, dv] or null
 };
 
-// Workspace of the backward: the forward's table and records, then the state
-// at every chunk start, dS after every chunk, and per-chunk gradient records.
+// Workspace of the backward: the forward's table and records (fp32), then
+// T and the strict-lower k Gram of every chunk, the state at every chunk
+// start, dS after every chunk, and per-chunk gradient records.
 struct BackwardPlan {
     PrefillPlan f;
-    size_t off_shist, off_dshist, off_grec;
+    size_t off_aux, off_shist, off_dshist, off_grec;
     size_t grec_floats;
     size_t total;
 };

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void kda_intra(
     int T, int H, int nch_seq, const ChunkInfo* __restrict__ table,
     const int* __restrict__ chunk_total, const IT* __restrict__ q, const IT* __restrict__ k,
     const float* __restrict__ g, const float* __restrict__ beta, char* __restrict__ records,
-    Prep pp) {
+    float* __restrict__ aux, Prep pp) {
     constexpr int NB = C / 16;
     constexpr int LDK = padded<OT>(D);
     constexpr int LDA = padded<OT>(C);
@@ -537,6 +537,9 @@ __global__ __launch_bounds__(256) void kda_intra(
                 const int row = 16 * Ib + 4 * lq + j;
                 if (!isM) sm.A[row * LDA + col] = to_ot<OT>(col < row ? sm.beta[row] * acc[j] : 0.f);
                 else macc[i][j] = col <= row ? acc[j] : 0.f;
+                if (aux && !isM)
+                    aux[((size_t)ch * H + h) * 2 * C * C + C * C + row * C + col] =
+                        col < row ? acc[j] : 0.f;
             }
         }
     }
@@ -619,7 +622,16 @@ __global__ __launch_bounds__(256) void kda_intra(
         lds_barrier();
     }
 
-    // ---- phase 5: Tb = T diag(beta) into the record (16-byte rows) ----
+    // ---- phase 5: Tb = T diag(beta) into the record (16-byte rows); T itself
+    // to aux when asked ----
+    if (aux) {
+        float* ta = aux + ((size_t)ch * H + h) * 2 * C * C;
+        for (int idx = tid; idx < C * C / 4; idx += 256) {
+            const int r = idx / (C / 4), c0 = (idx % (C / 4)) * 4;
+            *reinterpret_cast<float4*>(ta + r * C + c0) =
+                *reinterpret_cast<const float4*>(&sm.u.s.T[r * LDT + c0]);
+        }
+    }
     for (int idx = tid; idx < C * C / EPV; idx += 256) {
         const int r = idx / (C / EPV), c0 = (idx % (C / EPV)) * EPV;
         float tv[EPV];
@@ -684,8 +696,8 @@ struct ChainScratch {
 // O = scale (QS + M U), S <- Diag(Gamma_n) S + KPt U.  Ends with the new
 // state published to LDS; a barrier separates the last reads of the chunk
 // tiles and of the old state from that write, so on return the chunk's tiles
-// may be overwritten.
-template <int D, int C, int BV, typename OT, typename IT, int NWC = 4>
+// may be overwritten.  OUT = false: state only (QS and O are skipped).
+template <int D, int C, int BV, typename OT, typename IT, int NWC = 4, bool OUT = true>
 __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
                                             ChainScratch<D, C, BV, OT>& cs,
                                             float4v (&st)[((D / 16) * (BV / 16) + NWC - 1) / NWC],
@@ -721,7 +733,8 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
                 const int kk = ks + lq * mm::KPL;
                 const typename mm::frag bs = mm::load(cs.s, LDK, 16 * vt + l16, kk);
                 xk = mm::mma(load_swz<OT, D>(t.kg, 16 * rt + l16, kk), bs, xk);
-                qs[i] = mm::mma(load_swz<OT, D>(t.qg, 16 * rt + l16, kk), bs, qs[i]);
+                if constexpr (OUT)
+                    qs[i] = mm::mma(load_swz<OT, D>(t.qg, 16 * rt + l16, kk), bs, qs[i]);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -757,7 +770,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
         const int tt = wave + NWC * i;
-        if (tt < OTILES) {
+        if (OUT && tt < OTILES) {
             const int rt = tt / VT, vt = tt % VT;
             float4v acc = qs[i];
             const int kend = 16 * (rt + 1);
@@ -769,7 +782,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * rt + 4 * lq + j;
-                if (o && r < len)
+                if (r < len)
                     o[((size_t)(tok0 + r) * H + h) * D + v0 + 16 * vt + l16] = scale * acc[j];
             }
         }
@@ -907,14 +920,12 @@ struct InterSmem {
     ChainScratch<D, C, BV, OT> cs;
 };
 
-// s_hist (optional): the state at the start of every chunk, [chunk][H][D][D]
-// fp32 (the backward pass reads it); o may then be NULL.
 template <int D, int C, int BV, typename OT, typename IT>
 __global__ __launch_bounds__(256) void kda_inter(
     int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
     const int* __restrict__ chunk_off, float scale, const IT* __restrict__ v,
     const float* __restrict__ s0, const char* __restrict__ records, float* __restrict__ o,
-    float* __restrict__ sT, float* __restrict__ s_hist) {
+    float* __restrict__ sT) {
     constexpr int ST = (D / 16) * (BV / 16);
     constexpr int SPW = (ST + 3) / 4;
     typedef Rec<D, C, OT> R;
@@ -955,12 +966,81 @@ __global__ __launch_bounds__(256) void kda_inter(
         for (int i = 0; i < VPT; ++i)
             if (tid + 256 * i < NVV) reinterpret_cast<vec*>(sm.vraw)[tid + 256 * i] = vb[i];
         lds_barrier();
-        if (s_hist)
-            chain_store_state<D, BV>(st, s_hist, ((size_t)(cp.first + c) * H + cp.h) * (size_t)D * D,
-                                     cp.v0);
         inter_chunk<D, C, BV, OT, IT>(tiles, sm.cs, st, tok0, len, H, cp.h, cp.v0, scale, o);
     }
     if (sT) chain_store_state<D, BV>(st, sT, sbase, cp.v0);
+}
+
+// Forward chain of the backward pass: the state at the start of every chunk
+// into s_hist ([chunk][H][D][D] fp32), no output.  Only the record parts the
+// state update reads are loaded (KG, KPt, Tb, Gamma_n), and the next chunk's
+// parts are fetched into registers while the current chunk computes.
+template <int D, int C, int BV, typename OT, typename IT>
+__global__ __launch_bounds__(256) void kda_state_chain(
+    int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
+    const int* __restrict__ chunk_off, const IT* __restrict__ v, const float* __restrict__ s0,
+    const char* __restrict__ records, float* __restrict__ s_hist) {
+    constexpr int ST = (D / 16) * (BV / 16);
+    constexpr int SPW = (ST + 3) / 4;
+    typedef Rec<D, C, OT> R;
+    typedef u32x4 vec;
+    // needed 16-byte units: KG, then KPt and Tb, then Gamma_n
+    constexpr int A_END = (int)(R::QG * sizeof(OT) / 16);
+    constexpr int B_BEG = (int)(R::KPt * sizeof(OT) / 16), B_END = (int)(R::M * sizeof(OT) / 16);
+    constexpr int G_BEG = (int)(R::gn_byte / 16), G_END = (int)((R::gn_byte + 4 * D) / 16);
+    constexpr int NNEED = A_END + (B_END - B_BEG) + (G_END - G_BEG);
+    constexpr int RPT = (NNEED + 255) / 256;
+    constexpr int VPR = BV * (int)sizeof(IT) / 16;
+    constexpr int NVV = C * VPR;
+    constexpr int VPT = (NVV + 255) / 256;
+    static_assert(R::gn_byte % 16 == 0 && (4 * D) % 16 == 0, "record unit alignment");
+    extern __shared__ __align__(16) char smem_raw[];
+    InterSmem<D, C, BV, OT, IT>& sm = *reinterpret_cast<InterSmem<D, C, BV, OT, IT>*>(smem_raw);
+
+    const ChainPos cp = chain_pos<D, BV>(T, H, N_seq, nch_seq, G8, cu, chunk_off);
+    if (!cp.valid) return;
+    const int tid = threadIdx.x;
+    const size_t sbase = ((size_t)cp.n * H + cp.h) * (size_t)D * D;
+    float4v st[SPW];
+    chain_load_state<D, C, BV, OT>(st, sm.cs, s0, sbase, cp.v0);
+    const ChunkTiles<D, C, OT, IT> tiles(sm.img, sm.vraw);
+    auto unit = [](int j) {
+        return j < A_END ? j : j < A_END + (B_END - B_BEG) ? B_BEG + (j - A_END)
+                                                           : G_BEG + (j - A_END - (B_END - B_BEG));
+    };
+
+    vec rb[RPT], vb[VPT];
+    auto fetch = [&](int c) {
+        const int tok0 = cp.seq_tok0 + c * C;
+        const int len = min(C, cp.seq_len - c * C);
+        const vec* rec = reinterpret_cast<const vec*>(records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) rb[i] = rec[unit(min(tid + 256 * i, NNEED - 1))];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int idx = min(tid + 256 * i, NVV - 1);
+            const int r = min(idx / VPR, len - 1), cv = (idx % VPR) * (16 / (int)sizeof(IT));
+            vb[i] = *reinterpret_cast<const vec*>(v + ((size_t)(tok0 + r) * H + cp.h) * D + cp.v0 + cv);
+        }
+    };
+    if (cp.nch > 0) fetch(0);
+    for (int c = 0; c < cp.nch; ++c) {
+        const int tok0 = cp.seq_tok0 + c * C;
+        const int len = min(C, cp.seq_len - c * C);
+        // the previous chunk's tiles are free: inter_chunk ends with a barrier
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            if (tid + 256 * i < NNEED) reinterpret_cast<vec*>(sm.img)[unit(tid + 256 * i)] = rb[i];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+            if (tid + 256 * i < NVV) reinterpret_cast<vec*>(sm.vraw)[tid + 256 * i] = vb[i];
+        lds_barrier();
+        if (c + 1 < cp.nch) fetch(c + 1);
+        chain_store_state<D, BV>(st, s_hist, ((size_t)(cp.first + c) * H + cp.h) * (size_t)D * D,
+                                 cp.v0);
+        inter_chunk<D, C, BV, OT, IT, 4, false>(tiles, sm.cs, st, tok0, len, H, cp.h, cp.v0, 0.f,
+                                                nullptr);
+    }
 }
 
 // ---- K2b: double-buffered direct global-to-LDS variant ----
@@ -1039,7 +1119,7 @@ __global__ __launch_bounds__(64 * (BV / 4 + NP)) void kda_inter_dma(
     int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
     const int* __restrict__ chunk_off, float scale, const IT* __restrict__ v,
     const float* __restrict__ s0, const char* __restrict__ records, float* __restrict__ o,
-    float* __restrict__ sT, float* __restrict__ /*s_hist: not supported here*/) {
+    float* __restrict__ sT) {
     constexpr int NWC = BV / 4;                    // compute wavefronts (one tile each per phase)
     static_assert(64 * (NWC + NP) <= 1024, "workgroup too large");
     constexpr int ST = (D / 16) * (BV / 16);
@@ -1215,7 +1295,9 @@ static hipError_t launch_epilogue(const PrefillArgs& a) {
 // state at every chunk start; B3 the reverse chain per (sequence, head,
 // 16-column slice), keeping dSn of every chunk; B4a the products that
 // contract over dv, per (chunk, head), looping over 16-column blocks; B4b the
-// intra-chunk part per (chunk, head) in fp32, looping over 32-channel blocks.
+// intra-chunk part per (chunk, head) in fp32, looping over 16-channel blocks.
+// Only the lower-triangular parts of dT and dM matter: T and M are lower
+// triangular, so a perturbation of A or M never reaches their upper parts.
 // All products use fp32 matrix-core tiles (v_mfma_f32_16x16x4f32), whose
 // one-element-per-lane operands make transposed reads plain element loads.
 // ===========================================================================
@@ -1223,13 +1305,33 @@ static hipError_t launch_epilogue(const PrefillArgs& a) {
 // acc += sum_{k in [k0, k1)} A(m, k) B(k, n) for one 16x16 tile; a(m, k) and
 // b(k, n) take the row / column inside the tile.  Lane l supplies
 // A(l % 16, k + l / 16) and B(k + l / 16, l % 16); the result holds rows
-// 4 (l / 16) + j, column l % 16.  (k1 - k0) % 4 == 0.
+// 4 (l / 16) + j, column l % 16.  (k1 - k0) % 16 == 0.  Steps of 16: all
+// eight operand loads first, then four instructions on two interleaved
+// accumulators, so neither the loads nor the accumulation serialise.
 template <typename FA, typename FB>
 __device__ __forceinline__ float4v tile_mma(float4v acc, int k0, int k1, FA a, FB b) {
     const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
-    for (int k = k0; k < k1; k += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, k + lq), b(k + lq, l16), acc, 0, 0, 0);
-    return acc;
+    float4v acc2 = {0.f, 0.f, 0.f, 0.f};
+    for (int k = k0; k < k1; k += 16) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            av[s] = a(l16, k + 4 * s + lq);
+            bv[s] = b(k + 4 * s + lq, l16);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bv[0], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bv[1], acc2, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bv[2], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[3], bv[3], acc2, 0, 0, 0);
+    }
+    return acc + acc2;
+}
+
+// Lower 16x16 tiles (ct <= rt) of a C x C matrix, enumerated row by row.
+__device__ __forceinline__ void lower_tile(int t, int& rt, int& ct) {
+    rt = 0;
+    while ((rt + 1) * (rt + 2) / 2 <= t) ++rt;
+    ct = t - rt * (rt + 1) / 2;
 }
 
 // Per-chunk gradient record that B4a hands to B4b (fp32).
@@ -1238,36 +1340,42 @@ struct GradRec {
     static constexpr size_t DQG = 0;                   // [C][D]  scale dO S^T
     static constexpr size_t DKG = (size_t)C * D;       // [C][D]  -dX S^T
     static constexpr size_t DKE = 2 * (size_t)C * D;   // [C][D]  U dSn^T
-    static constexpr size_t DM = 3 * (size_t)C * D;    // [C][C]  scale dO U^T (lower)
-    static constexpr size_t DTB = DM + (size_t)C * C;  // [C][C]  dU X^T
+    static constexpr size_t DM = 3 * (size_t)C * D;    // [C][C]  scale dO U^T (lower tiles)
+    static constexpr size_t DTB = DM + (size_t)C * C;  // [C][C]  dU X^T (lower tiles)
     static constexpr size_t DGN = DTB + (size_t)C * C; // [D]     rowsum(dSn * S)
     static constexpr size_t floats = (DGN + D + 63) / 64 * 64;
 };
 
 // ---- B3: reverse chain ----
+// Eight wavefronts per (sequence, head, 16-column slice).  The next (earlier)
+// chunk's record and dO columns are fetched into registers while the current
+// chunk computes; the two products of dU run on separate wavefronts.
 template <int D, int C, typename OT>
 struct BwdChainSmem {
     static constexpr int LDV = 17;
     alignas(16) char img[Rec<D, C, OT>::bytes];
     float dO[C * LDV];
     float dS[D * LDV];
-    float dU[C * LDV];
+    float dUa[C * LDV], dUb[C * LDV];   // scale M^T dO and KE dSn
     float dX[C * LDV];
 };
 
+constexpr int kBwdChainWaves = 8;
+
 template <int D, int C, typename OT>
-__global__ __launch_bounds__(256) void kda_bwd_chain(
+__global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
     int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
     const int* __restrict__ chunk_off, float scale, const char* __restrict__ records,
     const float* __restrict__ d_o, const float* __restrict__ dS_final,
     float* __restrict__ ds_hist, float* __restrict__ dS0) {
+    constexpr int NW = kBwdChainWaves, NT = 64 * NW;
     constexpr int BV = 16, LDV = 17;
     typedef Rec<D, C, OT> R;
     constexpr int CK = R::CK;
     constexpr int NREC = (int)(R::bytes / 16);
-    constexpr int RPT = (NREC + 255) / 256;
-    constexpr int NDO = (C * BV + 255) / 256;
-    constexpr int RT = C / 16, DT = D / 16, SPW = (DT + 3) / 4;
+    constexpr int RPT = (NREC + NT - 1) / NT;
+    constexpr int NDO = (C * BV + NT - 1) / NT;
+    constexpr int RT = C / 16, DT = D / 16, SPW = (DT + NW - 1) / NW;
     typedef u32x4 vec;
     extern __shared__ __align__(16) char smem_raw[];
     BwdChainSmem<D, C, OT>& sm = *reinterpret_cast<BwdChainSmem<D, C, OT>*>(smem_raw);
@@ -1283,34 +1391,38 @@ __global__ __launch_bounds__(256) void kda_bwd_chain(
     float4v ds[SPW];
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-        const int s = wave + 4 * i;
+        const int s = wave + NW * i;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             ds[i][j] = (dS_final && s < DT)
                            ? dS_final[sbase + (size_t)(16 * s + 4 * lq + j) * D + cp.v0 + l16]
                            : 0.f;
     }
-    for (int c = cp.nch - 1; c >= 0; --c) {
-        const int chunk = cp.first + c;
+    vec rb[RPT];
+    float dov[NDO];
+    auto fetch = [&](int c) {
         const int tok0 = cp.seq_tok0 + c * C;
         const int len = min(C, cp.seq_len - c * C);
-        const vec* rec = reinterpret_cast<const vec*>(records + ((size_t)chunk * H + cp.h) * R::bytes);
-        vec rb[RPT];
+        const vec* rec = reinterpret_cast<const vec*>(records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) rb[i] = rec[min(tid + 256 * i, NREC - 1)];
-        float dov[NDO];
+        for (int i = 0; i < RPT; ++i) rb[i] = rec[min(tid + NT * i, NREC - 1)];
 #pragma unroll
         for (int i = 0; i < NDO; ++i) {
-            const int idx = min(tid + 256 * i, C * BV - 1);
+            const int idx = min(tid + NT * i, C * BV - 1);
             const int r = idx / BV, col = idx % BV;
             const float x = d_o[((size_t)(tok0 + min(r, len - 1)) * H + cp.h) * D + cp.v0 + col];
             dov[i] = r < len ? x : 0.f;
         }
+    };
+    if (cp.nch > 0) fetch(cp.nch - 1);
+    const float4v z = {0.f, 0.f, 0.f, 0.f};
+    for (int c = cp.nch - 1; c >= 0; --c) {
+        const int chunk = cp.first + c;
         // dSn of this chunk, for B4a
         float* dh = ds_hist + ((size_t)chunk * H + cp.h) * (size_t)D * D;
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int s = wave + 4 * i;
+            const int s = wave + NW * i;
             if (s < DT) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) dh[(size_t)(16 * s + 4 * lq + j) * D + cp.v0 + l16] = ds[i][j];
@@ -1319,40 +1431,46 @@ __global__ __launch_bounds__(256) void kda_bwd_chain(
         lds_barrier();   // the previous chunk's reads of LDS are complete
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
-            if (tid + 256 * i < NREC) reinterpret_cast<vec*>(sm.img)[tid + 256 * i] = rb[i];
+            if (tid + NT * i < NREC) reinterpret_cast<vec*>(sm.img)[tid + NT * i] = rb[i];
 #pragma unroll
         for (int i = 0; i < NDO; ++i) {
-            const int idx = tid + 256 * i;
+            const int idx = tid + NT * i;
             if (idx < C * BV) sm.dO[(idx / BV) * LDV + idx % BV] = dov[i];
         }
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int s = wave + 4 * i;
+            const int s = wave + NW * i;
             if (s < DT) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) sm.dS[(16 * s + 4 * lq + j) * LDV + l16] = ds[i][j];
             }
         }
         lds_barrier();
-        // dU = scale M^T dO + KE dSn   (M[i][r] and Tb[i][r] vanish for i < r)
-        for (int rt = wave; rt < RT; rt += 4) {
-            const float4v z = {0.f, 0.f, 0.f, 0.f};
-            const float4v a = tile_mma(
-                z, 16 * rt, C, [&](int m, int k) { return (float)img[R::M + swz<OT, CK>(k, 16 * rt + m)]; },
-                [&](int k, int n) { return sm.dO[k * LDV + n]; });
-            const float4v b = tile_mma(
-                z, 0, D, [&](int m, int k) { return (float)img[R::KPt + swz<OT, CK>(k, 16 * rt + m)]; },
-                [&](int k, int n) { return sm.dS[k * LDV + n]; });
+        if (c > 0) fetch(c - 1);
+        // dU = scale M^T dO (jobs [0, RT)) + KE dSn (jobs [RT, 2 RT));
+        // M[i][r] vanishes for i < r
+        for (int jb = wave; jb < 2 * RT; jb += NW) {
+            const int rt = jb % RT;
+            float4v a;
+            if (jb < RT)
+                a = tile_mma(z, 16 * rt, C,
+                             [&](int m, int k) { return (float)img[R::M + swz<OT, CK>(k, 16 * rt + m)]; },
+                             [&](int k, int n) { return sm.dO[k * LDV + n]; });
+            else
+                a = tile_mma(z, 0, D,
+                             [&](int m, int k) { return (float)img[R::KPt + swz<OT, CK>(k, 16 * rt + m)]; },
+                             [&](int k, int n) { return sm.dS[k * LDV + n]; });
+            float* dst = jb < RT ? sm.dUa : sm.dUb;
+            const float f = jb < RT ? scale : 1.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sm.dU[(16 * rt + 4 * lq + j) * LDV + l16] = scale * a[j] + b[j];
+            for (int j = 0; j < 4; ++j) dst[(16 * rt + 4 * lq + j) * LDV + l16] = f * a[j];
         }
         lds_barrier();
-        // dX = Tb^T dU
-        for (int rt = wave; rt < RT; rt += 4) {
-            const float4v z = {0.f, 0.f, 0.f, 0.f};
+        // dX = Tb^T dU (Tb[i][r] vanishes for i < r)
+        for (int rt = wave; rt < RT; rt += NW) {
             const float4v x = tile_mma(
                 z, 16 * rt, C, [&](int m, int k) { return (float)img[R::Tb + swz<OT, CK>(k, 16 * rt + m)]; },
-                [&](int k, int n) { return sm.dU[k * LDV + n]; });
+                [&](int k, int n) { return sm.dUa[k * LDV + n] + sm.dUb[k * LDV + n]; });
 #pragma unroll
             for (int j = 0; j < 4; ++j) sm.dX[(16 * rt + 4 * lq + j) * LDV + l16] = x[j];
         }
@@ -1360,9 +1478,8 @@ __global__ __launch_bounds__(256) void kda_bwd_chain(
         // dS = Gamma_n dSn + scale QG^T dO - KG^T dX
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int s = wave + 4 * i;
+            const int s = wave + NW * i;
             if (s < DT) {
-                const float4v z = {0.f, 0.f, 0.f, 0.f};
                 const float4v a = tile_mma(
                     z, 0, C, [&](int m, int k) { return (float)img[R::QG + swz<OT, D>(k, 16 * s + m)]; },
                     [&](int k, int n) { return sm.dO[k * LDV + n]; });
@@ -1378,7 +1495,7 @@ __global__ __launch_bounds__(256) void kda_bwd_chain(
     if (dS0) {
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int s = wave + 4 * i;
+            const int s = wave + NW * i;
             if (s < DT) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -1389,6 +1506,11 @@ __global__ __launch_bounds__(256) void kda_bwd_chain(
 }
 
 // ---- B4a: products over dv, per (chunk, head), 16-column value blocks ----
+// Eight wavefronts: in each block the four C x 16 products split into two
+// independent pairs (X, dU then U, dX) that run on separate wavefronts, and the
+// accumulated C x D / C x C products spread over all eight.  The next block's
+// state, state-gradient, dO and V columns are fetched into registers while the
+// current block computes.
 template <int D, int C, typename OT>
 struct BwdDvSmem {
     static constexpr int LDV = 17;
@@ -1399,20 +1521,25 @@ struct BwdDvSmem {
     float dO[C * LDV], V[C * LDV], X[C * LDV], U[C * LDV], dU[C * LDV], dX[C * LDV];
 };
 
+constexpr int kBwdDvWaves = 8;
+
 template <int D, int C, typename OT, typename IT>
-__global__ __launch_bounds__(256) void kda_bwd_dv(
+__global__ __launch_bounds__(64 * kBwdDvWaves) void kda_bwd_dv(
     int T, int H, int nch_seq, const ChunkInfo* __restrict__ table,
     const int* __restrict__ chunk_total, float scale, const IT* __restrict__ v,
     const char* __restrict__ records, const float* __restrict__ s_hist,
     const float* __restrict__ ds_hist, const float* __restrict__ d_o,
     float* __restrict__ grec, float* __restrict__ dv_out) {
+    constexpr int NW = kBwdDvWaves, NT = 64 * NW;
     constexpr int BV = 16, LDV = 17;
     typedef Rec<D, C, OT> R;
     typedef GradRec<D, C> GR;
     constexpr int CK = R::CK;
     constexpr int RT = C / 16, DT = D / 16;
-    constexpr int NQ = RT * DT, QPW = (NQ + 3) / 4;     // C x D tiles per wavefront
-    constexpr int NM = RT * RT, MPW = (NM + 3) / 4;     // C x C tiles per wavefront
+    constexpr int NQ = RT * DT, QPW = (NQ + NW - 1) / NW;          // C x D tiles per wavefront
+    constexpr int NL = RT * (RT + 1) / 2, MPW = (NL + NW - 1) / NW; // lower C x C tiles
+    constexpr int SPT = D * BV / NT, OPT = (C * BV + NT - 1) / NT;   // prefetch per thread
+    static_assert(D * BV % NT == 0, "state slice split");
     typedef u32x4 vec;
     extern __shared__ __align__(16) char smem_raw[];
     BwdDvSmem<D, C, OT>& sm = *reinterpret_cast<BwdDvSmem<D, C, OT>*>(smem_raw);
@@ -1432,19 +1559,37 @@ __global__ __launch_bounds__(256) void kda_bwd_dv(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lq = lane >> 4;
     const char* recb = records + ((size_t)ch * H + h) * R::bytes;
+    const float* Sh = s_hist + ((size_t)ch * H + h) * (size_t)D * D;
+    const float* dSh = ds_hist + ((size_t)ch * H + h) * (size_t)D * D;
+
+    float ps[SPT], pd[SPT], po[OPT], pv[OPT];
+    auto fetch = [&](int vb) {
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const int idx = tid + NT * i, c = idx / BV, col = idx % BV;
+            ps[i] = Sh[(size_t)c * D + vb + col];
+            pd[i] = dSh[(size_t)c * D + vb + col];
+        }
+#pragma unroll
+        for (int i = 0; i < OPT; ++i) {
+            const int idx = min(tid + NT * i, C * BV - 1), r = idx / BV, col = idx % BV;
+            const size_t off = ((size_t)(tok0 + min(r, len - 1)) * H + h) * D + vb + col;
+            po[i] = d_o[off];
+            pv[i] = to_f32(v[off]);
+        }
+    };
+    fetch(0);
     {   // stage KG and the KPt / Tb / M tail of the record
         constexpr int NKG = (int)(C * D * sizeof(OT) / 16);
         constexpr int NTL = (int)((D * CK + 2 * C * CK) * sizeof(OT) / 16);
         const vec* a = reinterpret_cast<const vec*>(recb + R::KG * sizeof(OT));
         const vec* b = reinterpret_cast<const vec*>(recb + R::KPt * sizeof(OT));
-        for (int i = tid; i < NKG; i += 256) reinterpret_cast<vec*>(sm.kg)[i] = a[i];
-        for (int i = tid; i < NTL; i += 256) reinterpret_cast<vec*>(sm.tail)[i] = b[i];
+        for (int i = tid; i < NKG; i += NT) reinterpret_cast<vec*>(sm.kg)[i] = a[i];
+        for (int i = tid; i < NTL; i += NT) reinterpret_cast<vec*>(sm.tail)[i] = b[i];
     }
     const OT* kpt = sm.tail;
     const OT* tb = sm.tail + D * CK;
     const OT* mm = sm.tail + D * CK + C * CK;
-    const float* Sh = s_hist + ((size_t)ch * H + h) * (size_t)D * D;
-    const float* dSh = ds_hist + ((size_t)ch * H + h) * (size_t)D * D;
 
     float4v aq[QPW], ak[QPW], ae[QPW], am[MPW], at[MPW];
 #pragma unroll
@@ -1456,58 +1601,72 @@ __global__ __launch_bounds__(256) void kda_bwd_dv(
 
     for (int vb = 0; vb < D; vb += BV) {
         lds_barrier();   // previous block's reads complete (and, first time, staging visible)
-        for (int idx = tid; idx < D * BV; idx += 256) {
-            const int c = idx / BV, col = idx % BV;
-            sm.S[c * LDV + col] = Sh[(size_t)c * D + vb + col];
-            sm.dSn[c * LDV + col] = dSh[(size_t)c * D + vb + col];
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const int idx = tid + NT * i, c = idx / BV, col = idx % BV;
+            sm.S[c * LDV + col] = ps[i];
+            sm.dSn[c * LDV + col] = pd[i];
         }
-        for (int idx = tid; idx < C * BV; idx += 256) {
-            const int r = idx / BV, col = idx % BV;
-            const size_t off = ((size_t)(tok0 + min(r, len - 1)) * H + h) * D + vb + col;
-            sm.dO[r * LDV + col] = r < len ? d_o[off] : 0.f;
-            sm.V[r * LDV + col] = r < len ? to_f32(v[off]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < OPT; ++i) {
+            const int idx = tid + NT * i, r = idx / BV, col = idx % BV;
+            if (idx < C * BV) {
+                sm.dO[r * LDV + col] = r < len ? po[i] : 0.f;
+                sm.V[r * LDV + col] = r < len ? pv[i] : 0.f;
+            }
         }
+        if (vb + BV < D) fetch(vb + BV);
         lds_barrier();
-        // X = V - KG S ; dU = scale M^T dO + KE dSn
-        for (int rt = wave; rt < RT; rt += 4) {
-            const float4v x = tile_mma(
-                z, 0, D, [&](int m, int k) { return (float)sm.kg[swz<OT, D>(16 * rt + m, k)]; },
-                [&](int k, int n) { return sm.S[k * LDV + n]; });
-            const float4v a = tile_mma(
-                z, 16 * rt, C, [&](int m, int k) { return (float)mm[swz<OT, CK>(k, 16 * rt + m)]; },
-                [&](int k, int n) { return sm.dO[k * LDV + n]; });
-            const float4v b = tile_mma(
-                z, 0, D, [&](int m, int k) { return (float)kpt[swz<OT, CK>(k, 16 * rt + m)]; },
-                [&](int k, int n) { return sm.dSn[k * LDV + n]; });
+        // jobs [0, RT): X = V - KG S;  [RT, 2 RT): dU = scale M^T dO + KE dSn
+        for (int jb = wave; jb < 2 * RT; jb += NW) {
+            const int rt = jb % RT;
+            float4v x;
+            if (jb < RT) {
+                x = tile_mma(z, 0, D, [&](int m, int k) { return (float)sm.kg[swz<OT, D>(16 * rt + m, k)]; },
+                             [&](int k, int n) { return sm.S[k * LDV + n]; });
+            } else {
+                const float4v a = tile_mma(
+                    z, 16 * rt, C, [&](int m, int k) { return (float)mm[swz<OT, CK>(k, 16 * rt + m)]; },
+                    [&](int k, int n) { return sm.dO[k * LDV + n]; });
+                x = tile_mma(z, 0, D, [&](int m, int k) { return (float)kpt[swz<OT, CK>(k, 16 * rt + m)]; },
+                             [&](int k, int n) { return sm.dSn[k * LDV + n]; });
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] += scale * a[j];
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * rt + 4 * lq + j;
-                sm.X[r * LDV + l16] = sm.V[r * LDV + l16] - x[j];
-                sm.dU[r * LDV + l16] = scale * a[j] + b[j];
+                if (jb < RT) sm.X[r * LDV + l16] = sm.V[r * LDV + l16] - x[j];
+                else sm.dU[r * LDV + l16] = x[j];
             }
         }
         lds_barrier();
-        // U = Tb X (Tb[r][i] = 0 for i > r) ; dX = Tb^T dU ; dV = dX
-        for (int rt = wave; rt < RT; rt += 4) {
-            const float4v u = tile_mma(
-                z, 0, 16 * (rt + 1), [&](int m, int k) { return (float)tb[swz<OT, CK>(16 * rt + m, k)]; },
-                [&](int k, int n) { return sm.X[k * LDV + n]; });
-            const float4v x = tile_mma(
-                z, 16 * rt, C, [&](int m, int k) { return (float)tb[swz<OT, CK>(k, 16 * rt + m)]; },
-                [&](int k, int n) { return sm.dU[k * LDV + n]; });
+        // jobs [0, RT): U = Tb X (Tb[r][i] = 0 for i > r);  [RT, 2 RT): dX = Tb^T dU = dV
+        for (int jb = wave; jb < 2 * RT; jb += NW) {
+            const int rt = jb % RT;
+            if (jb < RT) {
+                const float4v u = tile_mma(
+                    z, 0, 16 * (rt + 1), [&](int m, int k) { return (float)tb[swz<OT, CK>(16 * rt + m, k)]; },
+                    [&](int k, int n) { return sm.X[k * LDV + n]; });
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * rt + 4 * lq + j;
-                sm.U[r * LDV + l16] = u[j];
-                sm.dX[r * LDV + l16] = x[j];
-                if (r < len) dv_out[((size_t)(tok0 + r) * H + h) * D + vb + l16] = x[j];
+                for (int j = 0; j < 4; ++j) sm.U[(16 * rt + 4 * lq + j) * LDV + l16] = u[j];
+            } else {
+                const float4v x = tile_mma(
+                    z, 16 * rt, C, [&](int m, int k) { return (float)tb[swz<OT, CK>(k, 16 * rt + m)]; },
+                    [&](int k, int n) { return sm.dU[k * LDV + n]; });
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j;
+                    sm.dX[r * LDV + l16] = x[j];
+                    if (r < len) dv_out[((size_t)(tok0 + r) * H + h) * D + vb + l16] = x[j];
+                }
             }
         }
         lds_barrier();
         // accumulate the products over this block's dv columns
 #pragma unroll
         for (int i = 0; i < QPW; ++i) {
-            const int t = wave + 4 * i;
+            const int t = wave + NW * i;
             if (t < NQ) {
                 const int rt = t / DT, ct = t % DT;
                 aq[i] = tile_mma(aq[i], 0, BV, [&](int m, int k) { return sm.dO[(16 * rt + m) * LDV + k]; },
@@ -1520,9 +1679,10 @@ __global__ __launch_bounds__(256) void kda_bwd_dv(
         }
 #pragma unroll
         for (int i = 0; i < MPW; ++i) {
-            const int t = wave + 4 * i;
-            if (t < NM) {
-                const int rt = t / RT, ct = t % RT;
+            const int t = wave + NW * i;
+            if (t < NL) {
+                int rt, ct;
+                lower_tile(t, rt, ct);
                 am[i] = tile_mma(am[i], 0, BV, [&](int m, int k) { return sm.dO[(16 * rt + m) * LDV + k]; },
                                  [&](int k, int n) { return sm.U[(16 * ct + n) * LDV + k]; });
                 at[i] = tile_mma(at[i], 0, BV, [&](int m, int k) { return sm.dU[(16 * rt + m) * LDV + k]; },
@@ -1537,7 +1697,7 @@ __global__ __launch_bounds__(256) void kda_bwd_dv(
     float* gr = grec + ((size_t)ch * H + h) * GR::floats;
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
-        const int t = wave + 4 * i;
+        const int t = wave + NW * i;
         if (t < NQ) {
             const int rt = t / DT, ct = t % DT;
 #pragma unroll
@@ -1551,9 +1711,10 @@ __global__ __launch_bounds__(256) void kda_bwd_dv(
     }
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
-        const int t = wave + 4 * i;
-        if (t < NM) {
-            const int rt = t / RT, ct = t % RT;
+        const int t = wave + NW * i;
+        if (t < NL) {   // lower tiles only: the upper parts are never read
+            int rt, ct;
+            lower_tile(t, rt, ct);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * rt + 4 * lq + j, c = 16 * ct + l16;
@@ -1566,31 +1727,46 @@ __global__ __launch_bounds__(256) void kda_bwd_dv(
 }
 
 // ---- B4b: intra-chunk backward, per (chunk, head), fp32 ----
+// T and the strict-lower Gram P = KG KI^T come from the records kernel (aux
+// buffer).  Phase 1 forms dbeta and dP = diag(beta) dA; phase 2 walks the
+// channels in blocks of 16: chunk-local cumulative gates by a segmented scan,
+// the three C x 16 products, the element-wise dq, dk, dG and the reverse
+// cumulative sum that turns dG into dg.  Only lower tiles of the C x C
+// matrices are formed or read.
 template <int C>
 struct BwdIntraSmem {
-    static constexpr int LDC = C + 1, CB = 32, LDB = CB + 1;
-    float P[C * LDC];      // KG KI^T
-    float Tm[C * LDC];     // T = (I + A)^-1
-    float dP[C * LDC];     // dTb, then dA / dP
-    float dM[C * LDC];
-    float Y[C * LDC];      // scratch product
-    float G[C * LDB], kg[C * LDB], ki[C * LDB], qg[C * LDB];
-    float x1[C * LDB], x2[C * LDB], x3[C * LDB];    // dKG, dKI, dQG of the channel block
-    float beta[C], dbeta[C];
+    static constexpr int LDC = C + 1, CB = 16, LDB = CB + 1;
+    static constexpr int NSEG = 256 / CB;    // row segments per channel in the scans
+    static constexpr int RS = C / NSEG;      // rows per segment
+    float dP[C * LDC];     // dTb (lower), then dT T^T, then diag(beta) dA
+    float dM[C * LDC];     // scale dO U^T (lower)
+    union {
+        struct {
+            float Tm[C * LDC], Y[C * LDC];
+        } b;
+        struct {
+            float G[C * LDB], kg[C * LDB], ki[C * LDB], qg[C * LDB];
+            float x1[C * LDB], x2[C * LDB], x3[C * LDB];   // dKG, dKI, dQG
+        } c;
+    } u;
+    float tot[256], tot2[256];    // scan totals / partial sums
+    float red[(C / 16) * C];      // row sums of dA * P per column tile
+    float beta[C];
 };
 
 template <int D, int C, typename IT>
 __global__ __launch_bounds__(256) void kda_bwd_intra(
     int T, int H, int nch_seq, const ChunkInfo* __restrict__ table,
     const int* __restrict__ chunk_total, const IT* __restrict__ q, const IT* __restrict__ k,
-    const float* __restrict__ g, const float* __restrict__ beta,
+    const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ aux,
     const float* __restrict__ grec, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dg, float* __restrict__ dbeta) {
     typedef GradRec<D, C> GR;
     typedef BwdIntraSmem<C> SM;
-    constexpr int LDC = SM::LDC, CB = SM::CB, LDB = SM::LDB;
-    constexpr int RT = C / 16, NM = RT * RT, MPW = (NM + 3) / 4;
-    constexpr int NBT = RT * (CB / 16), BPW = (NBT + 3) / 4;   // C x CB tiles per wavefront
+    constexpr int LDC = SM::LDC, CB = SM::CB, LDB = SM::LDB, NSEG = SM::NSEG, RS = SM::RS;
+    constexpr int RT = C / 16, NL = RT * (RT + 1) / 2, LPW = (NL + 3) / 4;
+    constexpr int EPT = C * CB / 256;    // elements per thread in a C x CB block
+    static_assert(C * CB % 256 == 0 && RS >= 1, "block shape");
     extern __shared__ __align__(16) char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
@@ -1609,223 +1785,232 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lq = lane >> 4;
     const float* gr = grec + ((size_t)ch * H + h) * GR::floats;
+    const float* Tg = aux + ((size_t)ch * H + h) * 2 * C * C;
+    const float* Pg = Tg + C * C;
     const float4v z = {0.f, 0.f, 0.f, 0.f};
     auto tok = [&](int r) { return ((size_t)(tok0 + min(r, len - 1)) * H + h) * D; };
+    const int sc = tid % CB, ss = tid / CB;      // scan mapping: channel, row segment
 
-    if (tid < C) {
-        sm.beta[tid] = tid < len ? beta[(size_t)(tok0 + min(tid, len - 1)) * H + h] : 0.f;
-        sm.dbeta[tid] = 0.f;
+    if (tid < C) sm.beta[tid] = tid < len ? beta[(size_t)(tok0 + min(tid, len - 1)) * H + h] : 0.f;
+    // T, dTb and dM (lower parts) into LDS
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int r = idx / C, c = idx % C;
+        sm.u.b.Tm[r * LDC + c] = Tg[idx];
+        sm.dP[r * LDC + c] = c <= r ? gr[GR::DTB + idx] : 0.f;
+        sm.dM[r * LDC + c] = c <= r ? gr[GR::DM + idx] : 0.f;
     }
-    // G, KG = K Gamma, KI = K / Gamma (and QG) of one 32-channel block
-    auto load_block = [&](int c0, bool with_q) {
-        for (int idx = tid; idx < C * CB; idx += 256) {
-            const int r = idx / CB, c = idx % CB;
-            const float x = g[tok(r) + c0 + c];
-            sm.G[r * LDB + c] = r < len ? x : 0.f;
-        }
-        lds_barrier();
-        if (tid < CB) {   // running sum over the chunk, per channel
-            float acc = 0.f;
-            for (int r = 0; r < C; ++r) {
-                acc += sm.G[r * LDB + tid];
-                sm.G[r * LDB + tid] = acc;
-            }
-        }
-        lds_barrier();
-        for (int idx = tid; idx < C * CB; idx += 256) {
-            const int r = idx / CB, c = idx % CB;
-            const float G = sm.G[r * LDB + c];
-            const float kk = r < len ? to_f32(k[tok(r) + c0 + c]) : 0.f;
-            sm.kg[r * LDB + c] = kk * exp_e(G);
-            sm.ki[r * LDB + c] = kk * exp_e(-G);
-            if (with_q) sm.qg[r * LDB + c] = (r < len ? to_f32(q[tok(r) + c0 + c]) : 0.f) * exp_e(G);
-        }
-        lds_barrier();
-    };
-
-    // ---- pass 1: P = KG KI^T over the channel blocks ----
-    float4v ap[MPW];
+    // P on this wave's lower tiles, in matrix-core output layout
+    float4v pv[LPW];
 #pragma unroll
-    for (int i = 0; i < MPW; ++i) ap[i] = z;
-    for (int c0 = 0; c0 < D; c0 += CB) {
-        load_block(c0, false);
-#pragma unroll
-        for (int i = 0; i < MPW; ++i) {
-            const int t = wave + 4 * i;
-            if (t < NM) {
-                const int rt = t / RT, ct = t % RT;
-                ap[i] = tile_mma(ap[i], 0, CB, [&](int m, int kk) { return sm.kg[(16 * rt + m) * LDB + kk]; },
-                                 [&](int kk, int n) { return sm.ki[(16 * ct + n) * LDB + kk]; });
-            }
-        }
-        lds_barrier();
-    }
-#pragma unroll
-    for (int i = 0; i < MPW; ++i) {
+    for (int i = 0; i < LPW; ++i) {
         const int t = wave + 4 * i;
-        if (t < NM) {
-            const int rt = t / RT, ct = t % RT;
+        pv[i] = z;
+        if (t < NL) {
+            int rt, ct;
+            lower_tile(t, rt, ct);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sm.P[(16 * rt + 4 * lq + j) * LDC + 16 * ct + l16] = ap[i][j];
-        }
-    }
-    for (int idx = tid; idx < C * C; idx += 256) {
-        const int r = idx / C, c = idx % C;
-        sm.dP[r * LDC + c] = gr[GR::DTB + idx];
-        sm.dM[r * LDC + c] = gr[GR::DM + idx];
-    }
-    lds_barrier();
-    // ---- T = (I + A)^-1, A = diag(beta) strict_lower(P): one column per lane ----
-    if (wave == 0 && lane < C) {
-        for (int i = 0; i < C; ++i) {
-            float acc = 0.f;
-            for (int m = 0; m < i; ++m) acc += sm.P[i * LDC + m] * sm.Tm[m * LDC + lane];
-            sm.Tm[i * LDC + lane] = (i == lane ? 1.f : 0.f) - sm.beta[i] * acc;
+            for (int j = 0; j < 4; ++j) pv[i][j] = Pg[(16 * rt + 4 * lq + j) * C + 16 * ct + l16];
         }
     }
     lds_barrier();
-    // dbeta (from Tb = T diag beta) = colsum(dTb * T); dT = dTb diag(beta) -> Y
-    if (tid < C) {
-        float acc = 0.f;
-        for (int i = 0; i < C; ++i) acc += sm.dP[i * LDC + tid] * sm.Tm[i * LDC + tid];
-        sm.dbeta[tid] = acc;
-    }
-    for (int idx = tid; idx < C * C; idx += 256) {
-        const int r = idx / C, c = idx % C;
-        sm.Y[r * LDC + c] = sm.dP[r * LDC + c] * sm.beta[c];
-    }
-    lds_barrier();
-    // dP <- dT T^T
+
+    // ---- phase 1: dbeta and dP ----
+    // dbeta (through Tb = T diag beta) = colsum(dTb * T); Y = dT = dTb diag(beta)
     {
-        float4v a[MPW];
+        constexpr int PARTS = 256 / C;
+        const int c = tid % C, p = tid / C;
+        float acc = 0.f;
+        for (int i = c + p; i < C; i += PARTS) acc += sm.dP[i * LDC + c] * sm.u.b.Tm[i * LDC + c];
+        sm.tot[p * C + c] = acc;
+    }
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int r = idx / C, c = idx % C;
+        sm.u.b.Y[r * LDC + c] = sm.dP[r * LDC + c] * sm.beta[c];
+    }
+    lds_barrier();
+    // Z = Y T^T on the lower tiles (Y, T lower: k < 16 (ct + 1))
+    {
+        float4v a[LPW];
 #pragma unroll
-        for (int i = 0; i < MPW; ++i) {
+        for (int i = 0; i < LPW; ++i) {
             const int t = wave + 4 * i;
             a[i] = z;
-            if (t < NM) {
-                const int rt = t / RT, ct = t % RT;
-                a[i] = tile_mma(z, 0, C, [&](int m, int kk) { return sm.Y[(16 * rt + m) * LDC + kk]; },
-                                [&](int kk, int n) { return sm.Tm[(16 * ct + n) * LDC + kk]; });
+            if (t < NL) {
+                int rt, ct;
+                lower_tile(t, rt, ct);
+                a[i] = tile_mma(z, 0, 16 * (ct + 1),
+                                [&](int m, int kk) { return sm.u.b.Y[(16 * rt + m) * LDC + kk]; },
+                                [&](int kk, int n) { return sm.u.b.Tm[(16 * ct + n) * LDC + kk]; });
             }
         }
-        lds_barrier();
+        lds_barrier();   // dTb reads (dbeta partials, Y) are done
 #pragma unroll
-        for (int i = 0; i < MPW; ++i) {
+        for (int i = 0; i < LPW; ++i) {
             const int t = wave + 4 * i;
-            if (t < NM) {
-                const int rt = t / RT, ct = t % RT;
+            if (t < NL) {
+                int rt, ct;
+                lower_tile(t, rt, ct);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) sm.dP[(16 * rt + 4 * lq + j) * LDC + 16 * ct + l16] = a[i][j];
             }
         }
         lds_barrier();
-        // dA = -T^T (dT T^T), strict lower; dbeta += rowsum(dA * P); dP = diag(beta) dA
+        // dA = -T^T Z (strict lower; T^T upper: k >= 16 rt); dbeta += rowsum(dA * P)
 #pragma unroll
-        for (int i = 0; i < MPW; ++i) {
+        for (int i = 0; i < LPW; ++i) {
             const int t = wave + 4 * i;
             a[i] = z;
-            if (t < NM) {
-                const int rt = t / RT, ct = t % RT;
-                a[i] = tile_mma(z, 0, C, [&](int m, int kk) { return sm.Tm[kk * LDC + 16 * rt + m]; },
+            if (t < NL) {
+                int rt, ct;
+                lower_tile(t, rt, ct);
+                a[i] = tile_mma(z, 16 * rt, C,
+                                [&](int m, int kk) { return sm.u.b.Tm[kk * LDC + 16 * rt + m]; },
                                 [&](int kk, int n) { return sm.dP[kk * LDC + 16 * ct + n]; });
-            }
-        }
-        lds_barrier();
-#pragma unroll
-        for (int i = 0; i < MPW; ++i) {
-            const int t = wave + 4 * i;
-            if (t < NM) {
-                const int rt = t / RT, ct = t % RT;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * rt + 4 * lq + j, c = 16 * ct + l16;
-                    sm.Y[r * LDC + c] = c < r ? -a[i][j] : 0.f;     // dA
+                    a[i][j] = c < r ? -a[i][j] : 0.f;
+                    const float rs = group_sum<16>(a[i][j] * pv[i][j]);
+                    if (l16 == 0) sm.red[ct * C + r] = rs;
                 }
             }
         }
-        lds_barrier();
-    }
-    if (tid < C) {
-        float acc = 0.f;
-        for (int c = 0; c < tid; ++c) acc += sm.Y[tid * LDC + c] * sm.P[tid * LDC + c];
-        sm.dbeta[tid] += acc;
-    }
-    for (int idx = tid; idx < C * C; idx += 256) {
-        const int r = idx / C, c = idx % C;
-        sm.dP[r * LDC + c] = sm.beta[r] * sm.Y[r * LDC + c];
+        lds_barrier();   // Z reads done
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int t = wave + 4 * i;
+            if (t < NL) {
+                int rt, ct;
+                lower_tile(t, rt, ct);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j;
+                    sm.dP[r * LDC + 16 * ct + l16] = sm.beta[r] * a[i][j];
+                }
+            }
+        }
     }
     lds_barrier();
-    if (tid < len) dbeta[(size_t)(tok0 + tid) * H + h] = sm.dbeta[tid];
+    if (tid < C) {
+        float acc = 0.f;
+        for (int p = 0; p < 256 / C; ++p) acc += sm.tot[p * C + tid];
+        for (int ct = 0; ct <= tid / 16; ++ct) acc += sm.red[ct * C + tid];
+        if (tid < len) dbeta[(size_t)(tok0 + tid) * H + h] = acc;
+    }
 
-    // ---- pass 2: per channel block, the K, Q and gate gradients ----
+    // ---- phase 2: per block of CB channels ----
+    float pg[EPT], pk[EPT], pq[EPT];
+    auto fetch = [&](int c0) {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int idx = tid + 256 * e, r = idx / CB, c = idx % CB;
+            pg[e] = g[tok(r) + c0 + c];
+            pk[e] = to_f32(k[tok(r) + c0 + c]);
+            pq[e] = to_f32(q[tok(r) + c0 + c]);
+        }
+    };
+    fetch(0);
     for (int c0 = 0; c0 < D; c0 += CB) {
-        load_block(c0, true);
-        // dKG += dP KI ; dKI = dP^T KG + dM^T QG ; dQG += dM KI  (C x CB tiles)
-        float4v b1[BPW], b2[BPW], b3[BPW];
+        lds_barrier();   // previous block's (or phase 1's) LDS reads are done
 #pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-            const int t = wave + 4 * i;
-            b1[i] = b2[i] = b3[i] = z;
-            if (t < NBT) {
-                const int rt = t / (CB / 16), ct = t % (CB / 16);
-                b1[i] = tile_mma(z, 0, C, [&](int m, int kk) { return sm.dP[(16 * rt + m) * LDC + kk]; },
-                                 [&](int kk, int n) { return sm.ki[kk * LDB + 16 * ct + n]; });
-                b2[i] = tile_mma(z, 0, C, [&](int m, int kk) { return sm.dP[kk * LDC + 16 * rt + m]; },
-                                 [&](int kk, int n) { return sm.kg[kk * LDB + 16 * ct + n]; });
-                b2[i] = tile_mma(b2[i], 0, C, [&](int m, int kk) { return sm.dM[kk * LDC + 16 * rt + m]; },
-                                 [&](int kk, int n) { return sm.qg[kk * LDB + 16 * ct + n]; });
-                b3[i] = tile_mma(z, 0, C, [&](int m, int kk) { return sm.dM[(16 * rt + m) * LDC + kk]; },
-                                 [&](int kk, int n) { return sm.ki[kk * LDB + 16 * ct + n]; });
-            }
+        for (int e = 0; e < EPT; ++e) {
+            const int idx = tid + 256 * e, r = idx / CB, c = idx % CB;
+            sm.u.c.G[r * LDB + c] = r < len ? pg[e] : 0.f;
+            sm.u.c.kg[r * LDB + c] = r < len ? pk[e] : 0.f;    // raw k for now
+            sm.u.c.qg[r * LDB + c] = r < len ? pq[e] : 0.f;    // raw q for now
         }
+        if (c0 + CB < D) fetch(c0 + CB);
+        lds_barrier();
+        // chunk-local cumulative gate: segmented inclusive scan down the rows
+        float gv[RS];
+        {
+            float run = 0.f;
 #pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-            const int t = wave + 4 * i;
-            if (t < NBT) {
-                const int rt = t / (CB / 16), ct = t % (CB / 16);
+            for (int j = 0; j < RS; ++j) {
+                run += sm.u.c.G[(RS * ss + j) * LDB + sc];
+                gv[j] = run;
+            }
+            sm.tot[ss * CB + sc] = run;
+        }
+        lds_barrier();
+        float off = 0.f, gnv = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * rt + 4 * lq + j, c = 16 * ct + l16;
-                    sm.x1[r * LDB + c] = b1[i][j] + gr[GR::DKG + (size_t)r * D + c0 + c];
-                    sm.x2[r * LDB + c] = b2[i][j];
-                    sm.x3[r * LDB + c] = b3[i][j] + gr[GR::DQG + (size_t)r * D + c0 + c];
-                }
+        for (int s2 = 0; s2 < NSEG; ++s2) {
+            const float t = sm.tot[s2 * CB + sc];
+            gnv += t;
+            off += s2 < ss ? t : 0.f;
+        }
+        const float egn = exp_e(gnv);
+#pragma unroll
+        for (int j = 0; j < RS; ++j) {
+            const int r = RS * ss + j;
+            gv[j] += off;
+            const float ga = exp_e(gv[j]), gi = exp_e(-gv[j]);
+            const float kk = sm.u.c.kg[r * LDB + sc];
+            sm.u.c.kg[r * LDB + sc] = kk * ga;
+            sm.u.c.ki[r * LDB + sc] = kk * gi;
+            sm.u.c.qg[r * LDB + sc] *= ga;
+        }
+        lds_barrier();
+        // dKG = dP KI + grec, dKI = dP^T KG + dM^T QG, dQG = dM KI + grec
+        for (int rt = wave; rt < RT; rt += 4) {
+            float4v b1 = tile_mma(z, 0, 16 * (rt + 1),
+                                  [&](int m, int kk) { return sm.dP[(16 * rt + m) * LDC + kk]; },
+                                  [&](int kk, int n) { return sm.u.c.ki[kk * LDB + n]; });
+            float4v b2 = tile_mma(z, 16 * rt, C,
+                                  [&](int m, int kk) { return sm.dP[kk * LDC + 16 * rt + m]; },
+                                  [&](int kk, int n) { return sm.u.c.kg[kk * LDB + n]; });
+            b2 = tile_mma(b2, 16 * rt, C,
+                          [&](int m, int kk) { return sm.dM[kk * LDC + 16 * rt + m]; },
+                          [&](int kk, int n) { return sm.u.c.qg[kk * LDB + n]; });
+            float4v b3 = tile_mma(z, 0, 16 * (rt + 1),
+                                  [&](int m, int kk) { return sm.dM[(16 * rt + m) * LDC + kk]; },
+                                  [&](int kk, int n) { return sm.u.c.ki[kk * LDB + n]; });
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * rt + 4 * lq + j;
+                sm.u.c.x1[r * LDB + l16] = b1[j] + gr[GR::DKG + (size_t)r * D + c0 + l16];
+                sm.u.c.x2[r * LDB + l16] = b2[j];
+                sm.u.c.x3[r * LDB + l16] = b3[j] + gr[GR::DQG + (size_t)r * D + c0 + l16];
             }
         }
         lds_barrier();
-        // element-wise: dK, dQ, and dG (into x2 after use); dG_n per channel
-        for (int idx = tid; idx < C * CB; idx += 256) {
-            const int r = idx / CB, c = idx % CB;
-            const float G = sm.G[r * LDB + c];
-            const float Gn = sm.G[(C - 1) * LDB + c];
-            const float kk = r < len ? to_f32(k[tok(r) + c0 + c]) : 0.f;
-            const float ga = exp_e(G), gi = exp_e(-G), e = exp_e(Gn - G);
-            const float dKG = sm.x1[r * LDB + c], dKI = sm.x2[r * LDB + c], dQG = sm.x3[r * LDB + c];
-            const float dKE = gr[GR::DKE + (size_t)r * D + c0 + c];
-            const float dK = dKG * ga + dKI * gi + dKE * e;
-            const float dQ = dQG * ga;
-            const float dG = dKG * sm.kg[r * LDB + c] + dQG * sm.qg[r * LDB + c] -
-                             dKI * sm.ki[r * LDB + c] - dKE * kk * e;
+        // element-wise dk, dq, dG (scan mapping); dG_n partial sums
+        float dgv[RS];
+        float suf = 0.f, kes = 0.f;
+#pragma unroll
+        for (int j = RS - 1; j >= 0; --j) {
+            const int r = RS * ss + j;
+            const float ga = exp_e(gv[j]), gi = exp_e(-gv[j]);
+            const float dKG = sm.u.c.x1[r * LDB + sc], dKI = sm.u.c.x2[r * LDB + sc];
+            const float dQG = sm.u.c.x3[r * LDB + sc];
+            const float dKE = gr[GR::DKE + (size_t)r * D + c0 + sc];
+            const float ki = sm.u.c.ki[r * LDB + sc];
+            const float ke = ki * egn;                       // k exp(G_n - G)
             if (r < len) {
-                dk[tok(r) + c0 + c] = dK;
-                dq[tok(r) + c0 + c] = dQ;
+                dk[tok(r) + c0 + sc] = dKG * ga + dKI * gi + dKE * egn * gi;
+                dq[tok(r) + c0 + sc] = dQG * ga;
             }
-            sm.x1[r * LDB + c] = dG;
-            sm.x2[r * LDB + c] = dKE * kk * e;
+            suf += dKG * sm.u.c.kg[r * LDB + sc] + dQG * sm.u.c.qg[r * LDB + sc] - dKI * ki -
+                   dKE * ke;
+            dgv[j] = suf;
+            kes += dKE * ke;
         }
+        sm.tot[ss * CB + sc] = suf;
+        sm.tot2[ss * CB + sc] = kes;
         lds_barrier();
-        if (tid < CB) {
-            const int c = tid;
-            const float Gn = sm.G[(C - 1) * LDB + c];
-            float dGn = gr[GR::DGN + c0 + c] * exp_e(Gn);
-            for (int r = 0; r < C; ++r) dGn += sm.x2[r * LDB + c];
-            float acc = dGn;
-            for (int r = C - 1; r >= 0; --r) {
-                acc += sm.x1[r * LDB + c];
-                if (r < len) dg[tok(r) + c0 + c] = acc;
-            }
+        float after = 0.f, ke_all = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < NSEG; ++s2) {
+            after += s2 > ss ? sm.tot[s2 * CB + sc] : 0.f;
+            ke_all += sm.tot2[s2 * CB + sc];
         }
-        lds_barrier();
+        const float dgn = ke_all + gr[GR::DGN + c0 + sc] * egn;
+#pragma unroll
+        for (int j = 0; j < RS; ++j) {
+            const int r = RS * ss + j;
+            if (r < len) dg[tok(r) + c0 + sc] = dgv[j] + after + dgn;
+        }
     }
 }
 
@@ -1913,7 +2098,7 @@ static hipError_t launch_inter(const PrefillArgs& a, const PrefillPlan& plan, in
                                const int* chunk_off) {
     size_t smem;
     void (*kern)(int, int, int, int, int, const int*, const int*, float, const IT*, const float*,
-                 const char*, float*, float*, float*);
+                 const char*, float*, float*);
     if constexpr (KIND == 1) {
         smem = inter_dma_smem_bytes<D, C, BV, OT, IT>();
         kern = kda_inter_dma<D, C, BV, OT, IT, kProducers>;
@@ -1929,15 +2114,14 @@ static hipError_t launch_inter(const PrefillArgs& a, const PrefillPlan& plan, in
     const int threads = KIND == 0 ? 256 : 64 * (BV / 4 + kProducers);
     hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(threads), smem, a.stream, a.T, a.H,
                        a.N, nch_seq, (int)G8, a.cu_seqlens, chunk_off, a.scale, (const IT*)a.v,
-                       a.s0, (const char*)a.workspace + plan.off_records, a.o, a.sT,
-                       (float*)nullptr);
+                       a.s0, (const char*)a.workspace + plan.off_records, a.o, a.sT);
     return hipGetLastError();
 }
 
 // K0 (packed sequences) and K1: the chunk table and the chunk records.
 template <int D, int C, typename OT, typename IT>
 static hipError_t launch_records(const PrefillArgs& a, const PrefillPlan& plan, int nch_seq,
-                                 int** chunk_off, ChunkInfo** table) {
+                                 int** chunk_off, ChunkInfo** table, float* aux = nullptr) {
     const bool varlen = a.cu_seqlens != nullptr;
     char* ws = (char*)a.workspace;
     *chunk_off = nullptr;
@@ -1960,7 +2144,7 @@ static hipError_t launch_records(const PrefillArgs& a, const PrefillPlan& plan, 
         hipLaunchKernelGGL(kern, dim3((unsigned)plan.nchunk_max, (unsigned)a.H), dim3(256), smem,
                            a.stream, a.T, a.H, nch_seq, *table,
                            varlen ? *chunk_off + a.N : nullptr, (const IT*)a.q, (const IT*)a.k,
-                           a.g, a.beta, ws + plan.off_records, a.prep);
+                           a.g, a.beta, ws + plan.off_records, aux, a.prep);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -2046,6 +2230,8 @@ bool backward_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool b
     const size_t hist = (nch * H * (size_t)D * D * sizeof(float) + 255) / 256 * 256;
     plan->grec_floats = grad_rec_floats(D, C);
     size_t off = plan->f.total;
+    plan->off_aux = off;
+    off += (nch * H * 2 * (size_t)C * C * sizeof(float) + 255) / 256 * 256;
     plan->off_shist = off;
     off += hist;
     plan->off_dshist = off;
@@ -2076,28 +2262,28 @@ static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan)
         float* s_hist = reinterpret_cast<float*>(ws + plan.off_shist);
         float* ds_hist = reinterpret_cast<float*>(ws + plan.off_dshist);
         float* grec = reinterpret_cast<float*>(ws + plan.off_grec);
+        float* aux = reinterpret_cast<float*>(ws + plan.off_aux);
         int* chunk_off;
         ChunkInfo* table;
-        if (hipError_t e = launch_records<D, C, OT, IT>(a, plan.f, nch_seq, &chunk_off, &table))
+        if (hipError_t e = launch_records<D, C, OT, IT>(a, plan.f, nch_seq, &chunk_off, &table, aux))
             return e;
         const long long chains = (long long)a.N * a.H;
         const long long G8 = (chains + 7) / 8 * (D / 16);
         // forward chain keeping the state at every chunk start
         {
-            auto kern = kda_inter<D, C, 16, OT, IT>;
+            auto kern = kda_state_chain<D, C, 16, OT, IT>;
             const size_t smem = inter_smem_bytes<D, C, 16, OT, IT>();
             if (hipError_t e = set_smem(kern, smem)) return e;
             hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(256), smem, a.stream, a.T, a.H, a.N,
-                               nch_seq, (int)G8, a.cu_seqlens, chunk_off, a.scale,
-                               (const IT*)a.v, a.s0, (const char*)ws + plan.f.off_records,
-                               (float*)nullptr, (float*)nullptr, s_hist);
+                               nch_seq, (int)G8, a.cu_seqlens, chunk_off, (const IT*)a.v, a.s0,
+                               (const char*)ws + plan.f.off_records, s_hist);
             if (hipError_t e = hipGetLastError()) return e;
         }
         // B3: reverse chain
         {
             auto kern = kda_bwd_chain<D, C, OT>;
             if (hipError_t e = set_smem(kern, sizeof(BwdChainSmem<D, C, OT>))) return e;
-            hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(256),
+            hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(64 * kBwdChainWaves),
                                sizeof(BwdChainSmem<D, C, OT>), a.stream, a.T, a.H, a.N, nch_seq,
                                (int)G8, a.cu_seqlens, chunk_off, a.scale,
                                (const char*)ws + plan.f.off_records, b.d_o, b.dS_final, ds_hist,
@@ -2111,7 +2297,7 @@ static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan)
         {
             auto kern = kda_bwd_dv<D, C, OT, IT>;
             if (hipError_t e = set_smem(kern, sizeof(BwdDvSmem<D, C, OT>))) return e;
-            hipLaunchKernelGGL(kern, grid, dim3(256), sizeof(BwdDvSmem<D, C, OT>), a.stream, a.T,
+            hipLaunchKernelGGL(kern, grid, dim3(64 * kBwdDvWaves), sizeof(BwdDvSmem<D, C, OT>), a.stream, a.T,
                                a.H, nch_seq, table, total, a.scale, (const IT*)a.v,
                                (const char*)ws + plan.f.off_records, s_hist, ds_hist, b.d_o, grec,
                                b.dv);
@@ -2123,7 +2309,7 @@ static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan)
             if (hipError_t e = set_smem(kern, sizeof(BwdIntraSmem<C>))) return e;
             hipLaunchKernelGGL(kern, grid, dim3(256), sizeof(BwdIntraSmem<C>), a.stream, a.T, a.H,
                                nch_seq, table, total, (const IT*)a.q, (const IT*)a.k, a.g, a.beta,
-                               grec, b.dq, b.dk, b.dg, b.dbeta);
+                               aux, grec, b.dq, b.dk, b.dg, b.dbeta);
             if (hipError_t e = hipGetLastError()) return e;
         }
         return hipSuccess;

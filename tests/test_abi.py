@@ -138,9 +138,9 @@ def test_prep_and_epilogue_validation(lib):
 
 
 def test_backward_workspace_and_validation(lib):
-    """The backward's workspace holds fp32 chunk records plus two fp32 states
-    per (chunk, head) and a gradient record; bad arguments are rejected on the
-    host."""
+    """The backward's workspace holds fp32 chunk records plus, per (chunk,
+    head), T and the k Gram (C x C each), two fp32 states and a gradient
+    record; bad arguments are rejected on the host."""
     E = {v: k for k, v in kda.STATUS_NAMES.items()}
     wf = lib.kda_chunk_fwd_workspace_bytes
     wb = lib.kda_chunk_bwd_workspace_bytes
@@ -148,7 +148,8 @@ def test_backward_workspace_and_validation(lib):
     grec = (3 * C * d + 2 * C * C + d + 63) // 64 * 64
     # fp32 chunk records for either input type
     assert wb(1, 32768, H, d, d, C, 0, kda.KDA_BF16) == (
-        wf(1, 32768, H, d, d, C, 0, kda.KDA_F32) + 2 * nch * H * d * d * 4 + nch * H * grec * 4)
+        wf(1, 32768, H, d, d, C, 0, kda.KDA_F32) + nch * H * 2 * C * C * 4 +
+        2 * nch * H * d * d * 4 + nch * H * grec * 4)
     assert wb(1, 32768, H, d, d, C, 0, kda.KDA_BF16) == wb(1, 32768, H, d, d, C, 0, kda.KDA_F32)
     assert wb(1, 100, 2, 64, 32, 64, 0, kda.KDA_BF16) == 0
     assert wb(1, 100, 2, 64, 64, 48, 0, kda.KDA_BF16) == 0
