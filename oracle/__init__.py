@@ -10,6 +10,10 @@ Contents
 * ``kda_fwd`` / ``kda_decode_step``: the token-by-token fp64 recurrence in C
   (``kda_oracle.c``, OpenMP over independent (sequence, head) chains) -- the
   reference every GPU result is compared with.
+* ``kda_bwd``: exact gradients by reverse mode through the same token loop.
+* ``dplr_fwd``: the general diagonal-plus-low-rank recurrence
+  S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T, of which KDA is the
+  case a = beta k, b = alpha * k with write key beta k.
 * NumPy fp64 forms for one (sequence, head) chain, used only to pin the C
   oracle to something other than itself (see ``tests/test_oracle_pins.py``):
 
@@ -81,6 +85,8 @@ def _load():
         lib.oracle_kda_bwd.argtypes = [I, I, I, I, I, D, P, P, P, P, P, P, P, I, P, P, P, P, P, P,
                                        P, P]
         lib.oracle_kda_bwd.restype = I
+        lib.oracle_dplr_fwd.argtypes = [I, I, I, I, I, D, P, P, P, P, P, P, P, P, I, P, P]
+        lib.oracle_dplr_fwd.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         _lib = lib
@@ -357,4 +363,36 @@ def scalar_gated_deltanet_np(q, k, v, a, beta, scale, S0=None):
         kS = k[t] @ S
         S = a[t] * (S - beta[t] * np.outer(k[t], kS)) + beta[t] * np.outer(k[t], v[t])
         o[t] = scale * (q[t] @ S)
+    return o, S
+
+
+def dplr_fwd(q, k, v, a, b, g, scale, S0=None, cu_seqlens=None):
+    """Exact forward of the general diagonal-plus-low-rank recurrence in fp64:
+    S_t = (Diag(exp(g_t)) - a_t b_t^T) S_{t-1} + k_t v_t^T, o_t = scale S_t^T q_t.
+    q, k, a, b, g: [B, T, H, dk]; v: [B, T, H, dv] (float32 values).  S0 and
+    cu_seqlens as in kda_fwd.  Returns (o [B, T, H, dv], S [N, H, dk, dv]),
+    float64."""
+    q, k, v, a, b, g = (_f32(x) for x in (q, k, v, a, b, g))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for x in (k, a, b, g):
+        assert x.shape == q.shape
+    assert v.shape[:3] == (B, T, H)
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.shape[0] - 1
+    else:
+        cu = None
+        N = B
+    s0 = None
+    if S0 is not None:
+        s0 = np.ascontiguousarray(np.asarray(S0, dtype=np.float64))
+        assert s0.shape == (N, H, dk, dv)
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    S = np.zeros((N, H, dk, dv), dtype=np.float64)
+    rc = _load().oracle_dplr_fwd(B, T, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(a), _ptr(b), _ptr(g), _ptr(s0), _ptr(cu), N, _ptr(o),
+                                 _ptr(S))
+    if rc != 0:
+        raise ValueError("oracle_dplr_fwd rejected its arguments (code %d)" % rc)
     return o, S

@@ -497,3 +497,92 @@ int oracle_kda_bwd(int B, int T, int H, int dk, int dv, double scale,
     }
     return err;
 }
+
+/* ------------------------------------------------------------------------
+ * General diagonal-plus-low-rank (DPLR) transition, the family KDA belongs to
+ * (summary page, "Menor cantidad de operaciones que DPLR general": both allow
+ * fine-grained decay, and KDA ties both low-rank vectors of the transition to
+ * the key).  The page gives no formula; the form used here is
+ *
+ *     S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,                  alpha_t = exp(g_t),
+ *
+ * so that KDA is the case a_t = beta_t k_t, b_t = alpha_t * k_t with the
+ * write key beta_t k_t.  Token by token:
+ *     u = S^T b_t                 (read through b, before the step)
+ *     S <- Diag(alpha_t) S - a_t u^T + k_t v_t^T
+ *     o_t = scale * S^T q_t
+ * Layouts as for the KDA forward, with a, b [B, T, H, dk] (float32).
+ * ------------------------------------------------------------------------ */
+int oracle_dplr_fwd(int B, int T, int H, int dk, int dv, double scale,
+                    const float *q, const float *k, const float *v,
+                    const float *a, const float *b, const float *g,
+                    const double *S0, const int32_t *cu_seqlens, int N,
+                    double *o, double *S_final)
+{
+    if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return 1;
+    if (cu_seqlens) {
+        if (B != 1 || N <= 0) return 2;
+        if (cu_seqlens[0] != 0 || cu_seqlens[N] != T) return 3;
+        for (int n = 0; n < N; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return 4;
+    } else {
+        N = B;
+    }
+    const size_t tok_k = (size_t)H * dk, tok_v = (size_t)H * dv, SZ = (size_t)dk * dv;
+    const long chains = (long)N * H;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *S = (double *)malloc(sizeof(double) * SZ);
+        double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !u) {
+#pragma omp atomic write
+            err = 5;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long c = 0; c < chains; ++c) {
+                const int n = (int)(c / H), h = (int)(c % H);
+                long t0, t1, base;
+                if (cu_seqlens) { t0 = cu_seqlens[n]; t1 = cu_seqlens[n + 1]; base = 0; }
+                else { t0 = 0; t1 = T; base = (long)n * T; }
+                const size_t sidx = ((size_t)n * H + h) * SZ;
+                if (S0) memcpy(S, S0 + sidx, sizeof(double) * SZ);
+                else memset(S, 0, sizeof(double) * SZ);
+                for (long t = t0; t < t1; ++t) {
+                    const size_t tk = (size_t)(base + t) * tok_k + (size_t)h * dk;
+                    const size_t tv = (size_t)(base + t) * tok_v + (size_t)h * dv;
+                    /* u = S^T b (old state) */
+                    for (int j = 0; j < dv; ++j) u[j] = 0.0;
+                    for (int i = 0; i < dk; ++i) {
+                        const double bi = (double)b[tk + i];
+                        const double *row = S + (size_t)i * dv;
+                        for (int j = 0; j < dv; ++j) u[j] += bi * row[j];
+                    }
+                    /* S <- Diag(alpha) S - a u^T + k v^T */
+                    for (int i = 0; i < dk; ++i) {
+                        const double al = exp((double)g[tk + i]);
+                        const double ai = (double)a[tk + i], ki = (double)k[tk + i];
+                        double *row = S + (size_t)i * dv;
+                        for (int j = 0; j < dv; ++j)
+                            row[j] = al * row[j] - ai * u[j] + ki * (double)v[tv + j];
+                    }
+                    if (o) {
+                        double *orow = o + tv;
+                        for (int j = 0; j < dv; ++j) orow[j] = 0.0;
+                        for (int i = 0; i < dk; ++i) {
+                            const double qi = (double)q[tk + i];
+                            const double *row = S + (size_t)i * dv;
+                            for (int j = 0; j < dv; ++j) orow[j] += qi * row[j];
+                        }
+                        for (int j = 0; j < dv; ++j) orow[j] *= scale;
+                    }
+                }
+                if (S_final) memcpy(S_final + sidx, S, sizeof(double) * SZ);
+            }
+        }
+        free(S);
+        free(u);
+    }
+    return err;
+}
