@@ -264,6 +264,40 @@ kda_status kda_chunk_bwd(int B, int T, int H, int dk, int dv, int chunk,
                          void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* Bytes of device workspace kda_dplr_chunk_fwd needs (0 if the sizes are
+ * invalid or unsupported); arguments as for kda_chunk_fwd_workspace_bytes. */
+size_t kda_dplr_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv,
+                                          int chunk, int num_seqs,
+                                          kda_dtype qkv_dtype);
+
+/* Chunkwise forward of the general diagonal-plus-low-rank (DPLR) recurrence,
+ * the family KDA belongs to (same page, "Menor cantidad de operaciones que
+ * DPLR general": KDA ties both low-rank vectors of the transition to the key;
+ * the page gives no formula, the form used is the plainest one with KDA as a
+ * member):
+ *
+ *     S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,        alpha_t = exp(g_t),
+ *
+ * KDA being a_t = beta_t k_t, b_t = alpha_t * k_t with write key beta_t k_t.
+ * It is built with the same kernel machinery as kda_chunk_fwd, for comparing
+ * the two; the chunk form needs four decayed Gram blocks where KDA needs two.
+ *
+ *   a, b         [B, T, H, dk] in qkv_dtype (16-byte aligned).
+ *   Everything else exactly as in kda_chunk_fwd (q, k, v, g, initial_state,
+ *   cu_seqlens, num_seqs, o, final_state, workspace, errors).  The fp32 path
+ *   supports chunk 16 and 32 at dk = 128 (the chunk-64 tiles exceed LDS).
+ *   Domain as for kda_chunk_fwd, with |a|, |b| entries <= 1. */
+kda_status kda_dplr_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk,
+                              float scale, kda_dtype qkv_dtype,
+                              const void *q, const void *k, const void *v,
+                              const void *a, const void *b, const float *g,
+                              const float *initial_state,
+                              const int32_t *cu_seqlens, int num_seqs,
+                              float *o, float *final_state,
+                              void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -132,3 +132,30 @@ def config_inputs(cfg: int, device="cpu"):
                        s0_std=c["s0_std"])
     d["cu_seqlens"] = None
     return d
+
+
+def dplr_inputs(seed, B, T, H, dk, dv, dtype=torch.bfloat16, device="cpu", s0_std=None,
+                n_states=None, g_range=(0.001, 0.1)):
+    """Inputs of the general diagonal-plus-low-rank recurrence: q, k unit rows,
+    v ~ N(0, 1), g as in prefill_inputs, and untied low-rank vectors drawn as
+    independent perturbations of the key direction,
+        a = beta * unit(k + 0.5 n1),   b = unit(k + 0.5 n2),   beta ~ sigmoid(N(0, 1)),
+    so the transitions stay near the contractive KDA ones over long sequences.
+    q, k, v, a, b in ``dtype``; g [B, T, H, dk] and S0 float32."""
+    gen = _gen(seed, device)
+    f = dict(device=device, dtype=torch.float32, generator=gen)
+    q = _unit(torch.randn(B, T, H, dk, **f))
+    k = _unit(torch.randn(B, T, H, dk, **f))
+    v = torch.randn(B, T, H, dv, **f)
+    a = _unit(k + 0.5 * torch.randn(B, T, H, dk, **f))
+    b = _unit(k + 0.5 * torch.randn(B, T, H, dk, **f))
+    beta = torch.sigmoid(torch.randn(B, T, H, 1, **f))
+    lo, hi = g_range
+    g = -(lo + (hi - lo) * torch.rand(B, T, H, dk, **f))
+    out = dict(q=q, k=k, v=v, a=beta * a, b=b)
+    out = {n: t.to(dtype).contiguous() for n, t in out.items()}
+    out["g"] = g.contiguous()
+    out["S0"] = None
+    if s0_std is not None:
+        out["S0"] = (s0_std * torch.randn(n_states or B, H, dk, dv, **f)).contiguous()
+    return out

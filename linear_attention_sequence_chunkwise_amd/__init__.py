@@ -51,6 +51,9 @@ SIGNATURES = {
     "kda_chunk_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "kda_chunk_bwd": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "kda_dplr_chunk_fwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "kda_dplr_chunk_fwd": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                _I, _P, _P, _P, _SZ, _P]),
     "kda_decode_step": (_I, [_I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P]),
     "kda_decode_step_ex": (_I, [_I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                 _PREP, _EPI, _P]),
@@ -266,6 +269,50 @@ def kda_chunk_bwd(q, k, v, g, beta, grad_o, scale=None, chunk=64, initial_state=
     if rc != KDA_OK:
         raise KDAError("kda_chunk_bwd", rc)
     return dq, dk_, dv_, dg, db, dS0
+
+
+def kda_dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs=0,
+                                       dtype=torch.bfloat16):
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load_library().kda_dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk,
+                                                                  num_seqs, code))
+
+
+def kda_dplr_chunk_fwd(q, k, v, a, b, g, scale=None, chunk=64, initial_state=None,
+                       cu_seqlens=None, output_final_state=True, o=None, final_state=None,
+                       workspace=None, stream=None):
+    """Chunkwise forward of the general diagonal-plus-low-rank recurrence
+    S_t = (Diag(exp(g_t)) - a_t b_t^T) S_{t-1} + k_t v_t^T, o_t = scale S_t^T q_t.
+    q, k, a, b: [B, T, H, dk]; v: [B, T, H, dv] (all bf16 or all fp32); g:
+    [B, T, H, dk] fp32; the rest as in kda_chunk_fwd.  Returns (o, final_state)."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (a, "a"), (b, "b")):
+        _check(t, n, q.dtype, dev)
+    _check(g, "g", torch.float32, dev)
+    _check(initial_state, "initial_state", torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if scale is None:
+        scale = dk ** -0.5
+    if o is None:
+        o = torch.empty(B, T, H, dv, dtype=torch.float32, device=dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    code = _dtype_code(q)
+    nseq = N if cu_seqlens is not None else 0
+    need = lib.kda_dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, nseq, code)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+    rc = lib.kda_dplr_chunk_fwd(B, T, H, dk, dv, chunk, float(scale), code, _ptr(q), _ptr(k),
+                                _ptr(v), _ptr(a), _ptr(b), _ptr(g), _ptr(initial_state),
+                                _ptr(cu_seqlens), nseq, _ptr(o), _ptr(final_state),
+                                _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != KDA_OK:
+        raise KDAError("kda_dplr_chunk_fwd", rc)
+    return o, final_state
 
 
 def kda_decode_step(q, k, v, g, beta, state_cache, scale=None, slot_idx=None, o=None,

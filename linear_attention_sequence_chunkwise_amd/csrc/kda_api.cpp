@@ -213,6 +213,63 @@ kda_status kda_chunk_bwd(int B, int T, int H, int dk, int dv, int chunk, float s
     return from_hip(kda::launch_backward(b, plan));
 }
 
+size_t kda_dplr_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                          int num_seqs, kda_dtype qkv_dtype) {
+    if (B < 1 || T < 0 || H < 1 || num_seqs < 0) return 0;
+    if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return 0;
+    if (dk != dv || !kda::dplr_supported(dk, chunk, qkv_dtype == KDA_BF16)) return 0;
+    const bool varlen = num_seqs > 0;
+    if (varlen && B != 1) return 0;
+    kda::PrefillPlan plan;
+    if (!kda::dplr_plan(B, T, H, dk, chunk, varlen ? num_seqs : B, varlen, qkv_dtype == KDA_BF16,
+                        &plan))
+        return 0;
+    return plan.total;
+}
+
+kda_status kda_dplr_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk, float scale,
+                              kda_dtype qkv_dtype, const void* q, const void* k, const void* v,
+                              const void* a, const void* b, const float* g,
+                              const float* initial_state, const int32_t* cu_seqlens, int num_seqs,
+                              float* o, float* final_state, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_BAD_SHAPE;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen && (B != 1 || num_seqs < 1)) return KDA_ERR_BAD_SHAPE;
+    const int N = varlen ? num_seqs : B;
+    if ((long long)B * T * H * (long long)(dk > dv ? dk : dv) >= (1LL << 40)) return KDA_ERR_BAD_SHAPE;
+    if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+    if (dk != dv || !kda::dplr_supported(dk, chunk, qkv_dtype == KDA_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * T > 0) {
+        if (!q || !k || !v || !a || !b || !g || !o) return KDA_ERR_NULL_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(a) || !aligned16(b) ||
+            !aligned16(g) || !aligned16(o))
+            return KDA_ERR_NULL_ARG;
+    }
+    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+        return KDA_ERR_NULL_ARG;
+
+    kda::PrefillPlan plan;
+    if (!kda::dplr_plan(B, T, H, dk, chunk, N, varlen, qkv_dtype == KDA_BF16, &plan))
+        return KDA_ERR_BAD_SHAPE;
+    if (plan.total > 0 && (!workspace || workspace_bytes < plan.total || ((uintptr_t)workspace & 255u)))
+        return KDA_ERR_WORKSPACE;
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+
+    kda::DplrArgs d;
+    d.B = B; d.T = T; d.H = H; d.D = dk; d.C = chunk; d.scale = scale;
+    d.bf16 = qkv_dtype == KDA_BF16;
+    d.q = q; d.k = k; d.v = v; d.a = a; d.b = b; d.g = g;
+    d.s0 = initial_state; d.cu_seqlens = cu_seqlens; d.N = N;
+    d.o = o; d.sT = final_state;
+    d.workspace = workspace; d.workspace_bytes = workspace_bytes;
+    d.stream = stream;
+    return from_hip(kda::launch_dplr(d, plan));
+}
+
 kda_status kda_decode_step_ex(int N, int H, int dk, int dv, float scale, kda_dtype qkv_dtype,
                               const void* q, const void* k, const void* v, const float* g,
                               const float* beta, float* state_cache, int num_slots,

@@ -89,6 +89,23 @@ struct BackwardPlan {
     size_t total;
 };
 
+// Forward of the general diagonal-plus-low-rank recurrence (kda_dplr_chunk_fwd).
+struct DplrArgs {
+    int B, T, H, D, C;
+    float scale;
+    bool bf16;
+    const void *q, *k, *v, *a, *b;
+    const float* g;
+    const float* s0;
+    const int32_t* cu_seqlens;
+    int N;
+    float* o;
+    float* sT;
+    void* workspace;
+    size_t workspace_bytes;
+    hipStream_t stream;
+};
+
 // True when (D, C, dtype) has a built prefill kernel that fits in LDS.
 bool prefill_supported(int D, int C, bool bf16);
 bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf16,
@@ -100,5 +117,9 @@ bool backward_supported(int D, int C, bool bf16);
 bool backward_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf16,
                    BackwardPlan* plan);
 hipError_t launch_backward(const BackwardArgs& a, const BackwardPlan& plan);
+bool dplr_supported(int D, int C, bool bf16);
+bool dplr_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf16,
+               PrefillPlan* plan);
+hipError_t launch_dplr(const DplrArgs& a, const PrefillPlan& plan);
 
 }  // namespace kda

@@ -46,99 +46,12 @@
 
 #include <type_traits>
 
+#include "kda_chunk.h"
 #include "kda_common.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-// ---------------------------------------------------------------------------
-// Matrix-core fragment helpers.  Operands are staged in LDS as row-major
-// [row][k] tiles (for B = X^T that means X stored as [n][k]); every lane
-// loads KPL consecutive k of one row.  Output (16 x 16 fp32): lane l holds
-// rows 4*(l/16) + j, j = 0..3, of column l % 16.
-// ---------------------------------------------------------------------------
-template <typename OT>
-struct MM;
-
-template <>
-struct MM<_Float16> {
-    static constexpr int KS = 32;   // k per instruction
-    static constexpr int KPL = 8;   // k per lane
-    typedef half8 frag;
-    __device__ static __forceinline__ frag load(const _Float16* tile, int ld, int row, int k) {
-        return *reinterpret_cast<const half8*>(tile + row * ld + k);
-    }
-    __device__ static __forceinline__ float4v mma(frag a, frag b, float4v c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-    }
-};
-
-template <>
-struct MM<float> {
-    static constexpr int KS = 4;
-    static constexpr int KPL = 1;
-    typedef float frag;
-    __device__ static __forceinline__ frag load(const float* tile, int ld, int row, int k) {
-        return tile[row * ld + k];
-    }
-    __device__ static __forceinline__ float4v mma(frag a, frag b, float4v c) {
-        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-    }
-};
-
-template <typename OT>
-__device__ __forceinline__ OT to_ot(float x) { return (OT)x; }
-
-// 16 bytes of inputs -> floats (8 bf16 or 4 fp32), without taking addresses
-// (keeps the prefetch buffers in registers).
-// Two consecutive inputs as floats (bf16 pair from one 32-bit load).
-__device__ __forceinline__ float2 load2(const float* p) {
-    return *reinterpret_cast<const float2*>(p);
-}
-__device__ __forceinline__ float2 load2(const bf16_t* p) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-    return float2{__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u)};
-}
-__device__ __forceinline__ void unpack16(const u32x4& w, float (&e)[8]) {
-    const uint32_t u[4] = {w[0], w[1], w[2], w[3]};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        e[2 * i] = __builtin_bit_cast(float, u[i] << 16);
-        e[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xffff0000u);
-    }
-}
-// floats -> 16 bytes of OT (8 fp16 or 4 fp32), rounded once, built without
-// type punning through memory.
-__device__ __forceinline__ u32x4 pack16(const float (&x)[8]) {
-    u32x4 w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)x[2 * i]);
-        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)x[2 * i + 1]);
-        w[i] = lo | (hi << 16);
-    }
-    return w;
-}
-__device__ __forceinline__ u32x4 pack16(const float (&x)[4]) {
-    return __builtin_bit_cast(u32x4, float4v{x[0], x[1], x[2], x[3]});
-}
-__device__ __forceinline__ void unpack16(const u32x4& w, float (&e)[4]) {
-    const float4v f = __builtin_bit_cast(float4v, w);
-    e[0] = f[0];
-    e[1] = f[1];
-    e[2] = f[2];
-    e[3] = f[3];
-}
-
-// Padded leading dimension: +16 bytes per row spreads the rows of a 16-row
-// fragment over distinct LDS banks.
-template <typename OT>
-constexpr int padded(int k) { return k + 16 / (int)sizeof(OT); }
-
-// k extent of the chunk-indexed operands: at least one instruction's k (the
-// columns beyond C are kept at zero).
-template <int C, typename OT>
-constexpr int chunk_k() { return C > MM<OT>::KS ? C : MM<OT>::KS; }
 
 // ---------------------------------------------------------------------------
 // Workspace record of one (chunk, head).  It is stored as the exact LDS image
@@ -168,18 +81,6 @@ struct Rec {
     static constexpr size_t bytes = (gn_byte + 4 * (size_t)D + 1023) / 1024 * 1024;
 };
 
-// Element offset of (row, k) in a swizzled [rows][LD] tile of OT.
-template <typename OT, int LD>
-__device__ __forceinline__ int swz(int row, int k) {
-    constexpr int EPV = 16 / (int)sizeof(OT);
-    constexpr int NG = LD / EPV;
-    static_assert((NG & (NG - 1)) == 0, "groups per row must be a power of two");
-    return row * LD + ((((k / EPV) ^ row) & (NG - 1)) * EPV) + (k % EPV);
-}
-template <typename OT, int LD>
-__device__ __forceinline__ typename MM<OT>::frag load_swz(const OT* tile, int row, int k) {
-    return MM<OT>::load(tile + swz<OT, LD>(row, k) - k, 0, 0, k);
-}
 
 static size_t rec_bytes(int D, int C, bool bf16) {
     const size_t es = bf16 ? 2 : 4;
@@ -189,11 +90,6 @@ static size_t rec_bytes(int D, int C, bool bf16) {
     return (gn + 4 * (size_t)D + 1023) / 1024 * 1024;
 }
 
-struct ChunkInfo {
-    int tok0;   // first token (index into the flattened [B*T] token axis)
-    int len;    // valid rows, 1..C
-    int pad0, pad1;
-};
 
 // ---------------------------------------------------------------------------
 // K0: chunk table for packed sequences.  One workgroup.
@@ -295,30 +191,6 @@ struct IntraSmem {
     float beta[C];
 };
 
-// acc += X (16x16 at x, row-major ld ldx) * Y (16x16 at y, row-major [k][n]
-// ld ldy), operands rounded to OT: one fp16 16x16x16 instruction, or four
-// fp32 16x16x4 instructions.
-template <typename OT, typename XT, typename YT>
-__device__ __forceinline__ float4v mma16(float4v acc, const XT* x, int ldx, const YT* y, int ldy,
-                                         int lane) {
-    const int l16 = lane & 15, lq = lane >> 4;
-    if constexpr (sizeof(OT) == 2) {
-        half4 a, b;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            a[j] = (_Float16)(float)x[l16 * ldx + 4 * lq + j];
-            b[j] = (_Float16)(float)y[(4 * lq + j) * ldy + l16];
-        }
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, acc, 0, 0, 0);
-    } else {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32((float)x[l16 * ldx + 4 * s4 + lq],
-                                                       (float)y[(4 * s4 + lq) * ldy + l16], acc,
-                                                       0, 0, 0);
-        return acc;
-    }
-}
 
 // PREP: apply the optional input preparation (kda_prep) while loading.
 template <int D, int C, typename OT, typename IT, bool PREP>
@@ -682,15 +554,6 @@ struct ChunkTiles {
     }
 };
 
-// Per-workgroup state operand and scratch of the chain.
-template <int D, int C, int BV, typename OT>
-struct ChainScratch {
-    static constexpr int LDK = padded<OT>(D);
-    static constexpr int LDC = padded<OT>(chunk_k<C, OT>());
-    OT s[BV * LDK];      // state operand, [v][c]
-    OT x[BV * LDC];      // V - KG S, [v][i]
-    OT u[BV * LDC];      // U, [v][i]
-};
 
 // One chunk of the chain: X = V - KG S, QS = QG S, U = Tb X,
 // O = scale (QS + M U), S <- Diag(Gamma_n) S + KPt U.  Ends with the new
@@ -817,99 +680,6 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
     }
 }
 
-// Chain bounds of workgroup `L` (logical index after the XCD remap).
-struct ChainPos {
-    int n, h, v0, first, nch, seq_tok0, seq_len;
-    bool valid;
-};
-template <int D, int BV>
-__device__ __forceinline__ ChainPos chain_pos(int T, int H, int N_seq, int nch_seq, int G8,
-                                              const int32_t* __restrict__ cu,
-                                              const int* __restrict__ chunk_off) {
-    constexpr int P = D / BV;
-    ChainPos c;
-    const int b = blockIdx.x;
-    const int L = (b & 7) * G8 + (b >> 3);
-    const int p = L % P;
-    const int nh = L / P;
-    c.valid = nh < N_seq * H;
-    if (!c.valid) return c;
-    c.h = nh % H;
-    c.n = nh / H;
-    c.v0 = p * BV;
-    if (cu) {
-        c.first = chunk_off[c.n];
-        c.nch = min(chunk_off[c.n + 1], chunk_off[N_seq]) - c.first;
-        if (c.nch < 0) c.nch = 0;
-        c.seq_tok0 = cu[c.n];
-        c.seq_len = cu[c.n + 1] - c.seq_tok0;
-    } else {
-        c.first = c.n * nch_seq;
-        c.nch = nch_seq;
-        c.seq_tok0 = c.n * T;
-        c.seq_len = T;
-    }
-    return c;
-}
-
-// State tiles owned by this wave (fp32, MFMA output layout) from s0 or zero,
-// and the fp16/fp32 state operand in LDS.
-template <int D, int C, int BV, typename OT, int NWC = 4>
-__device__ __forceinline__ void chain_load_state(float4v (&st)[((D / 16) * (BV / 16) + NWC - 1) / NWC],
-                                                 ChainScratch<D, C, BV, OT>& cs,
-                                                 const float* __restrict__ s0, size_t sbase,
-                                                 int v0) {
-    constexpr int VT = BV / 16, ST = (D / 16) * VT, SPW = (ST + NWC - 1) / NWC;
-    constexpr int LDK = padded<OT>(D);
-    constexpr int CK = chunk_k<C, OT>();
-    constexpr int LDC = padded<OT>(CK);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lq = lane >> 4;
-    if constexpr (CK > C) {   // k-padding of X and U stays zero for the whole chain
-        for (int idx = threadIdx.x; idx < 2 * BV * (CK - C); idx += 64 * NWC) {
-            const int row = idx / (CK - C), col = C + idx % (CK - C);
-            (row < BV ? cs.x : cs.u)[(row % BV) * LDC + col] = to_ot<OT>(0.f);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int s = wave + NWC * i;
-        st[i] = float4v{0.f, 0.f, 0.f, 0.f};
-        if (s < ST && s0) {
-            const int ct = s / VT, vt = s % VT;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                st[i][j] = s0[sbase + (size_t)(16 * ct + 4 * lq + j) * D + v0 + 16 * vt + l16];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int s = wave + NWC * i;
-        if (s < ST) {
-            const int ct = s / VT, vt = s % VT;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                cs.s[(16 * vt + l16) * LDK + 16 * ct + 4 * lq + j] = to_ot<OT>(st[i][j]);
-        }
-    }
-}
-
-template <int D, int BV, int NWC = 4>
-__device__ __forceinline__ void chain_store_state(
-    const float4v (&st)[((D / 16) * (BV / 16) + NWC - 1) / NWC], float* __restrict__ sT,
-    size_t sbase, int v0) {
-    constexpr int VT = BV / 16, ST = (D / 16) * VT, SPW = (ST + NWC - 1) / NWC;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lq = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int s = wave + NWC * i;
-        if (s < ST) {
-            const int ct = s / VT, vt = s % VT;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                sT[sbase + (size_t)(16 * ct + 4 * lq + j) * D + v0 + 16 * vt + l16] = st[i][j];
-        }
-    }
-}
 
 // ---- K2a: register-staged variant (any dtype / slice width) ----
 template <int D, int C, int BV, typename OT, typename IT>
@@ -2017,7 +1787,6 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
 // ---------------------------------------------------------------------------
 // Host side: planning and dispatch.
 // ---------------------------------------------------------------------------
-constexpr size_t kLdsLimit = 160 * 1024;
 constexpr int kProducers = 8;   // producer wavefronts of the direct-copy chain kernel
 
 template <int D, int C, typename OT>
@@ -2027,8 +1796,6 @@ constexpr size_t inter_smem_bytes() { return sizeof(InterSmem<D, C, BV, OT, IT>)
 template <int D, int C, int BV, typename OT, typename IT>
 constexpr size_t inter_dma_smem_bytes() { return sizeof(InterDmaSmem<D, C, BV, OT, IT>); }
 
-template <typename OT>
-using InputOf = typename std::conditional<sizeof(OT) == 2, bf16_t, float>::type;
 
 template <int D, int C, typename OT>
 constexpr bool fits() {
@@ -2118,6 +1885,13 @@ static hipError_t launch_inter(const PrefillArgs& a, const PrefillPlan& plan, in
     return hipGetLastError();
 }
 
+hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int C, int cap, int* chunk_off,
+                              ChunkInfo* table, hipStream_t stream) {
+    hipLaunchKernelGGL(kda_chunk_table, dim3(1), dim3(256), 0, stream, cu, N, T, C, cap, chunk_off,
+                       table);
+    return hipGetLastError();
+}
+
 // K0 (packed sequences) and K1: the chunk table and the chunk records.
 template <int D, int C, typename OT, typename IT>
 static hipError_t launch_records(const PrefillArgs& a, const PrefillPlan& plan, int nch_seq,
@@ -2130,10 +1904,9 @@ static hipError_t launch_records(const PrefillArgs& a, const PrefillPlan& plan, 
         *chunk_off = reinterpret_cast<int*>(ws + plan.off_table);
         *table = reinterpret_cast<ChunkInfo*>(
             ws + plan.off_table + ((size_t)(a.N + 1) * sizeof(int) + 255) / 256 * 256);
-        hipLaunchKernelGGL(kda_chunk_table, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, a.N,
-                           a.T, C, plan.nchunk_max, *chunk_off, *table);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (hipError_t e = launch_chunk_table(a.cu_seqlens, a.N, a.T, C, plan.nchunk_max,
+                                              *chunk_off, *table, a.stream))
+            return e;
     }
     if (plan.nchunk_max > 0) {
         const size_t smem = intra_smem_bytes<D, C, OT>();

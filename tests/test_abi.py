@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"kda_status_string", "kda_version", "kda_chunk_fwd_workspace_bytes",
                           "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_decode_step",
                           "kda_decode_step_ex", "kda_chunk_bwd_workspace_bytes",
-                          "kda_chunk_bwd"}
+                          "kda_chunk_bwd", "kda_dplr_chunk_fwd_workspace_bytes",
+                          "kda_dplr_chunk_fwd"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in kda.SIGNATURES, n
@@ -172,3 +173,28 @@ def test_backward_workspace_and_validation(lib):
     assert bwd(B=2, cu=p, nseq=2) == E["KDA_ERR_BAD_SHAPE"]
     assert bwd(wsb=1024) == E["KDA_ERR_WORKSPACE"]
     assert bwd(ws=ctypes.c_void_p(4096 + 64)) == E["KDA_ERR_WORKSPACE"]
+
+
+def test_dplr_workspace_and_validation(lib):
+    """The DPLR record holds two C x d and two d x C tiles, three C x C tiles and
+    d fp32 decays; the fp32 chunk-64 tiles at d = 128 do not fit LDS."""
+    E = {v: k for k, v in kda.STATUS_NAMES.items()}
+    ws = lib.kda_dplr_chunk_fwd_workspace_bytes
+    rec = (2 * 64 * 128 + 2 * 128 * 64 + 3 * 64 * 64) * 2 + 4 * 128
+    rec = (rec + 1023) // 1024 * 1024
+    assert ws(1, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 512 * 32 * rec
+    assert ws(1, 100, 2, 128, 128, 64, 0, kda.KDA_F32) == 0
+    assert ws(1, 100, 2, 128, 128, 32, 0, kda.KDA_F32) > 0
+    assert ws(1, 100, 2, 64, 32, 64, 0, kda.KDA_BF16) == 0
+    p = ctypes.c_void_p(4096)
+
+    def fwd(B=1, T=64, H=2, dk=64, dv=64, chunk=64, dtype=kda.KDA_BF16, ptr=p, ab=p, wsb=1 << 30):
+        return lib.kda_dplr_chunk_fwd(B, T, H, dk, dv, chunk, 1.0, dtype, ptr, ptr, ptr, ab, ab,
+                                      ptr, None, None, 0, ptr, None, p, wsb, None)
+    assert fwd(B=0) == E["KDA_ERR_BAD_SHAPE"]
+    assert fwd(dtype=3) == E["KDA_ERR_BAD_DTYPE"]
+    assert fwd(chunk=48) == E["KDA_ERR_UNSUPPORTED"]
+    assert fwd(dk=128, dv=128, dtype=kda.KDA_F32) == E["KDA_ERR_UNSUPPORTED"]
+    assert fwd(ab=None) == E["KDA_ERR_NULL_ARG"]
+    assert fwd(ab=ctypes.c_void_p(4104)) == E["KDA_ERR_NULL_ARG"]
+    assert fwd(wsb=64) == E["KDA_ERR_WORKSPACE"]

@@ -1,0 +1,100 @@
+"""GPU parity of kda_dplr_chunk_fwd (general diagonal-plus-low-rank forward)
+against the fp64 oracle's token recurrence, with the bounds of the KDA
+forward (max |gpu - ref| / RMS(ref) below 1e-4 for float32 inputs, 2e-2 for
+bfloat16, for outputs and final states)."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import linear_attention_sequence_chunkwise_amd as kda
+import oracle
+from kda_testlib import TOL, np32, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run(d, chunk, cu=None):
+    o, S = kda.kda_dplr_chunk_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["g"], chunk=chunk,
+                                  initial_state=d["S0"], cu_seqlens=cu)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), S.cpu().numpy()
+
+
+def ref(d, cu=None, heads=None):
+    sel = (lambda t: t) if heads is None else (lambda t: t[:, :, heads])
+    D = d["q"].shape[-1]
+    S0 = None if d["S0"] is None else d["S0"].double().cpu().numpy()
+    if S0 is not None and heads is not None:
+        S0 = S0[:, heads]
+    return oracle.dplr_fwd(*(np32(sel(d[n])) for n in ("q", "k", "v", "a", "b", "g")), D ** -0.5,
+                           S0=S0, cu_seqlens=None if cu is None else cu.cpu().numpy())
+
+
+def supported(D, chunk, dtype):
+    return kda.kda_dplr_chunk_fwd_workspace_bytes(1, 64, 1, D, D, chunk, 0, dtype) > 0
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_dplr_forward(dtype, D, chunk):
+    if not supported(D, chunk, dtype):
+        pytest.skip("fp32 tiles of this size exceed LDS (KDA_ERR_UNSUPPORTED)")
+    d = kda_inputs.dplr_inputs(700 + D + chunk, 2, 150, 2, D, D, dtype, "cuda", s0_std=0.1)
+    o, S = run(d, chunk)
+    ro, rS = ref(d)
+    assert rel_err(o, ro) < TOL[dtype] and rel_err(S, rS) < TOL[dtype], (rel_err(o, ro),
+                                                                         rel_err(S, rS))
+
+
+@pytest.mark.parametrize("dtype,D,chunk", [(torch.bfloat16, 128, 64), (torch.float32, 64, 16)])
+def test_dplr_varlen(dtype, D, chunk):
+    lens = [1, 63, 64, 65, 130, 7, 0]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    d = kda_inputs.dplr_inputs(71, 1, int(sum(lens)), 3, D, D, dtype, "cuda", s0_std=0.1,
+                               n_states=len(lens))
+    o, S = run(d, chunk, cu)
+    ro, rS = ref(d, cu)
+    assert rel_err(o, ro) < TOL[dtype] and rel_err(S, rS) < TOL[dtype]
+    assert np.array_equal(S[-1], d["S0"][-1].cpu().numpy())      # empty sequence
+
+
+def test_dplr_reduces_to_kda():
+    """a = beta k, b = alpha * k, write key beta k: the DPLR kernels give the
+    KDA kernels' result (fp32, within rounding)."""
+    B, T, H, D = 1, 200, 2, 64
+    d = kda_inputs.prefill_inputs(72, B, T, H, D, D, torch.float32, "cuda", s0_std=0.1)
+    bk = (d["beta"][..., None] * d["k"]).contiguous()
+    ak = (torch.exp(d["g"]) * d["k"]).contiguous()
+    o1, S1 = kda.kda_dplr_chunk_fwd(d["q"], bk, d["v"], bk, ak, d["g"], chunk=32,
+                                    initial_state=d["S0"])
+    o2, S2 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=32,
+                               initial_state=d["S0"])
+    torch.cuda.synchronize()
+    assert rel_err(o1.cpu().numpy(), o2.double().cpu().numpy()) < 1e-4
+    assert rel_err(S1.cpu().numpy(), S2.double().cpu().numpy()) < 1e-4
+
+
+def test_dplr_zero_tokens_keeps_state():
+    d = kda_inputs.dplr_inputs(73, 1, 0, 2, 64, 64, torch.bfloat16, "cuda", s0_std=0.1)
+    o, S = run(d, 64)
+    assert o.size == 0 and np.array_equal(S, d["S0"].cpu().numpy())
+
+
+def test_dplr_config2_sampled():
+    """The 32K-token layer shape (B 1, H 32, d 128, bf16, chunk 64) as the
+    benchmark runs it; sampled heads checked against the oracle."""
+    d = kda_inputs.dplr_inputs(74, 1, 32768, 32, 128, 128, torch.bfloat16, "cuda")
+    o, S = run(d, 64)
+    heads = [0, 13, 31]
+    ro, rS = ref(d, heads=heads)
+    for i, h in enumerate(heads):
+        assert rel_err(o[:, :, h], ro[:, :, i]) < TOL[torch.bfloat16], h
+        assert rel_err(S[:, h], rS[:, i]) < TOL[torch.bfloat16], h
