@@ -24,6 +24,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2500.0      # dense fp16/bf16 matrix cores, TFLOP/s
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4   # q,k,v bf16; g; beta; o fp32
 DECODE_BYTES_PER_TOKEN_HEAD = 2 * 128 * 128 * 4 + 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4
+# general DPLR forward: q,k,v,a,b bf16, g in; o fp32 out
+DPLR_BYTES_PER_TOKEN_HEAD = 5 * 128 * 2 + 128 * 4 + 128 * 4
 # backward: q,k,v bf16, g, beta, grad_o in; grad q,k,v,g fp32 and grad beta out
 BACKWARD_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4 + 4 * 128 * 4 + 4
 
@@ -41,7 +43,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--profile-target", choices=["prefill", "decode", "backward", "copy"],
+    ap.add_argument("--no-dplr", action="store_true")
+    ap.add_argument("--profile-target", choices=["prefill", "decode", "backward", "dplr", "copy"],
                     help="run only this workload a few times (target for rocprofv3) and exit")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="read rocprofv3 FETCH_SIZE/WRITE_SIZE runs of the three profile "
@@ -74,12 +77,14 @@ def measured_traffic(leg):
     return rec["bytes_per_call"]
 
 
-LEG_SOURCES = {"prefill": ["kda_prefill.hip", "kda_common.h", "kda_internal.h"],
+LEG_SOURCES = {"prefill": ["kda_prefill.hip", "kda_chunk.h", "kda_common.h", "kda_internal.h"],
                "decode": ["kda_decode.hip", "kda_common.h", "kda_internal.h"],
-               "backward": ["kda_prefill.hip", "kda_common.h", "kda_internal.h"]}
+               "backward": ["kda_prefill.hip", "kda_chunk.h", "kda_common.h", "kda_internal.h"],
+               "dplr": ["kda_dplr.hip", "kda_chunk.h", "kda_common.h", "kda_internal.h"]}
 LEG_KERNELS = {"prefill": ("kda_intra", "kda_inter"), "decode": ("decode_step_kernel",),
-               "backward": ("kda_intra", "kda_inter", "kda_bwd_chain", "kda_bwd_dv",
-                            "kda_bwd_intra")}
+               "backward": ("kda_intra", "kda_state_chain", "kda_bwd_chain", "kda_bwd_dv",
+                            "kda_bwd_intra"),
+               "dplr": ("kda_dplr_intra", "kda_dplr_inter")}
 COPY_BYTES = 1 << 30   # the copy target reads and writes 1 GiB per dispatch
 
 
@@ -109,7 +114,7 @@ def traffic_from(d):
     1 GiB elementwise copy (torch.mul(x, 1.0, out=y)), so that 1.0 means the
     bytes actually moved."""
     out = {"method": "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE in separate runs of "
-                     "python bench.py --profile-target {copy,prefill,decode}; per-dispatch "
+                     "python bench.py --profile-target {copy,prefill,decode,backward,dplr}; per-dispatch "
                      "means, scaled by the copy kernel's reading of a 1 GiB read + 1 GiB write"}
     scale = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -158,6 +163,16 @@ def profile_target(kind):
         for _ in range(3):
             kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64, o=o,
                               final_state=S, workspace=ws)
+    elif kind == "dplr":
+        c = kda_inputs.CONFIGS[2]
+        B, T, H, D = c["B"], c["T"], c["H"], c["dk"]
+        d = kda_inputs.dplr_inputs(kda_inputs.CFG_SEED[2] + 70, B, T, H, D, D, torch.bfloat16,
+                                   "cuda")
+        ws = torch.empty(kda.kda_dplr_chunk_fwd_workspace_bytes(B, T, H, D, D, 64),
+                         dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            kda.kda_dplr_chunk_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["g"], chunk=64,
+                                   workspace=ws)
     elif kind == "backward":
         d = kda_inputs.config_inputs(2, "cuda")
         B, T, H, D = d["q"].shape
@@ -286,6 +301,61 @@ def bench_backward(kda, kda_inputs, d, steps, warmup, stream):
     ms = tm.stop() / steps
     torch.cuda.synchronize()
     return dict(ms=ms, workspace_bytes=ws.numel())
+
+
+def bench_dplr(kda, kda_inputs, kda_in, steps, warmup, stream):
+    """The general-DPLR forward on the same layer shape, next to KDA: KDA's
+    production path, and KDA with the register-staged chain kernel that the
+    DPLR forward also uses (same machinery, like for like)."""
+    c = kda_inputs.CONFIGS[2]
+    B, T, H, D, C = c["B"], c["T"], c["H"], c["dk"], c["chunk"]
+    d = kda_inputs.dplr_inputs(kda_inputs.CFG_SEED[2] + 70, B, T, H, D, D, torch.bfloat16, "cuda")
+    o = torch.empty(B, T, H, D, device="cuda")
+    S = torch.empty(B, H, D, D, device="cuda")
+    ws = torch.empty(max(kda.kda_dplr_chunk_fwd_workspace_bytes(B, T, H, D, D, C),
+                         kda.kda_chunk_fwd_workspace_bytes(B, T, H, D, D, C)),
+                     dtype=torch.uint8, device="cuda")
+
+    def timed(call):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        tm = StreamTimer(stream)
+        tm.start()
+        for _ in range(steps):
+            call()
+        ms = tm.stop() / steps
+        torch.cuda.synchronize()
+        return ms
+
+    dplr_ms = timed(lambda: kda.kda_dplr_chunk_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["g"],
+                                                   chunk=C, o=o, final_state=S, workspace=ws,
+                                                   stream=stream))
+    kcall = lambda: kda.kda_chunk_fwd(kda_in["q"], kda_in["k"], kda_in["v"], kda_in["g"],
+                                      kda_in["beta"], chunk=C, o=o, final_state=S, workspace=ws,
+                                      stream=stream)
+    kda_ms = timed(kcall)
+    prev = os.environ.get("KDA_INTER_VARIANT")
+    os.environ["KDA_INTER_VARIANT"] = "reg16"
+    try:
+        kda_reg_ms = timed(kcall)
+    finally:
+        if prev is None:
+            del os.environ["KDA_INTER_VARIANT"]
+        else:
+            os.environ["KDA_INTER_VARIANT"] = prev
+    db = DPLR_BYTES_PER_TOKEN_HEAD * B * T * H
+    roof = dict(bound="hbm", achieved=db / (dplr_ms / 1e3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                algorithmic_bytes=db, traffic=measured_traffic("dplr"),
+                kernel="kda_dplr_chunk_fwd call (kda_dplr_intra + kda_dplr_inter)")
+    roof["frac"] = roof["achieved"] / HBM_PEAK_GBS
+    return dict(ms_per_step=dplr_ms, value=B * T / (dplr_ms / 1e3), unit="tokens/s", roofline=roof,
+                kda_ms_per_step=kda_ms, kda_register_staged_chain_ms_per_step=kda_reg_ms,
+                kda_speedup=dplr_ms / kda_ms, kda_speedup_same_chain_kernel=dplr_ms / kda_reg_ms,
+                workload="general-DPLR forward (kda_dplr_chunk_fwd), B=1 H=32 T=32768 "
+                         "dk=dv=128 chunk=64 bf16 q/k/v/a/b, a and b independent "
+                         "perturbations of the key direction; KDA on its own inputs of the "
+                         "same shape")
 
 
 def decode_setup(kda, kda_inputs, n_steps, stream):
@@ -485,6 +555,13 @@ def main():
                                         "history, kda_bwd_chain, kda_bwd_dv, kda_bwd_intra)"))
         bwd["roofline"]["frac"] = bwd["roofline"]["achieved"] / HBM_PEAK_GBS
 
+    dplr = None
+    if not args.no_dplr:
+        dplr = bench_dplr(kda, kda_inputs, pf["inputs"], args.steps, args.warmup, stream)
+        print("dplr %.4f ms/call (kda %.4f, kda register-staged chain %.4f)"
+              % (dplr["ms_per_step"], dplr["kda_ms_per_step"],
+                 dplr["kda_register_staged_chain_ms_per_step"]), file=sys.stderr, flush=True)
+
     dec = None
     if not args.no_decode:
         dc = bench_decode(kda, kda_inputs, args.decode_steps, args.warmup, stream)
@@ -545,6 +622,7 @@ def main():
                      "gate; one extra pass over o inside the call)"),
         "cpu_baseline": cpu,
         "backward": bwd,
+        "general_dplr": dplr,
         "decode": dec,
     }
     print(json.dumps(out))
