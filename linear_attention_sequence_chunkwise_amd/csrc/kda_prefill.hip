@@ -1499,14 +1499,19 @@ __global__ __launch_bounds__(64 * kBwdDvWaves) void kda_bwd_dv(
 // ---- B4b: intra-chunk backward, per (chunk, head), fp32 ----
 // T and the strict-lower Gram P = KG KI^T come from the records kernel (aux
 // buffer).  Phase 1 forms dbeta and dP = diag(beta) dA; phase 2 walks the
-// channels in blocks of 16: chunk-local cumulative gates by a segmented scan,
-// the three C x 16 products, the element-wise dq, dk, dG and the reverse
-// cumulative sum that turns dG into dg.  Only lower tiles of the C x C
-// matrices are formed or read.
+// channels in blocks of 32: chunk-local cumulative gates by a segmented scan,
+// the three C x 32 products (one 16x16 tile per wavefront), the element-wise
+// dq, dk, dG and the reverse cumulative sum that turns dG into dg.  The next
+// block's inputs and gradient-record values are fetched into registers while
+// the current block computes.  Only lower tiles of the C x C matrices are
+// formed or read.
+constexpr int kBwdIntraWaves = 8;
+
 template <int C>
 struct BwdIntraSmem {
-    static constexpr int LDC = C + 1, CB = 16, LDB = CB + 1;
-    static constexpr int NSEG = 256 / CB;    // row segments per channel in the scans
+    static constexpr int NT = 64 * kBwdIntraWaves;
+    static constexpr int LDC = C + 1, CB = 32, LDB = CB + 1;
+    static constexpr int NSEG = NT / CB;     // row segments per channel in the scans
     static constexpr int RS = C / NSEG;      // rows per segment
     float dP[C * LDC];     // dTb (lower), then dT T^T, then diag(beta) dA
     float dM[C * LDC];     // scale dO U^T (lower)
@@ -1515,17 +1520,18 @@ struct BwdIntraSmem {
             float Tm[C * LDC], Y[C * LDC];
         } b;
         struct {
-            float G[C * LDB], kg[C * LDB], ki[C * LDB], qg[C * LDB];
+            float kg[C * LDB], ki[C * LDB], qg[C * LDB];
             float x1[C * LDB], x2[C * LDB], x3[C * LDB];   // dKG, dKI, dQG
+            float G[C * LDB];
         } c;
     } u;
-    float tot[256], tot2[256];    // scan totals / partial sums
+    float tot[NT], tot2[NT];      // scan totals / partial sums
     float red[(C / 16) * C];      // row sums of dA * P per column tile
     float beta[C];
 };
 
 template <int D, int C, typename IT>
-__global__ __launch_bounds__(256) void kda_bwd_intra(
+__global__ __launch_bounds__(64 * kBwdIntraWaves) void kda_bwd_intra(
     int T, int H, int nch_seq, const ChunkInfo* __restrict__ table,
     const int* __restrict__ chunk_total, const IT* __restrict__ q, const IT* __restrict__ k,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ aux,
@@ -1533,10 +1539,12 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
     float* __restrict__ dg, float* __restrict__ dbeta) {
     typedef GradRec<D, C> GR;
     typedef BwdIntraSmem<C> SM;
+    constexpr int NW = kBwdIntraWaves, NT = SM::NT;
     constexpr int LDC = SM::LDC, CB = SM::CB, LDB = SM::LDB, NSEG = SM::NSEG, RS = SM::RS;
-    constexpr int RT = C / 16, NL = RT * (RT + 1) / 2, LPW = (NL + 3) / 4;
-    constexpr int EPT = C * CB / 256;    // elements per thread in a C x CB block
-    static_assert(C * CB % 256 == 0 && RS >= 1, "block shape");
+    constexpr int RT = C / 16, NL = RT * (RT + 1) / 2, LPW = (NL + NW - 1) / NW;
+    constexpr int CT = CB / 16, NBT = RT * CT, BPW = (NBT + NW - 1) / NW;
+    constexpr int EPT = C * CB / NT;     // elements per thread in a C x CB block
+    static_assert(C * CB % NT == 0 && RS >= 1 && D % CB == 0, "block shape");
     extern __shared__ __align__(16) char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
@@ -1563,7 +1571,7 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
 
     if (tid < C) sm.beta[tid] = tid < len ? beta[(size_t)(tok0 + min(tid, len - 1)) * H + h] : 0.f;
     // T, dTb and dM (lower parts) into LDS
-    for (int idx = tid; idx < C * C; idx += 256) {
+    for (int idx = tid; idx < C * C; idx += NT) {
         const int r = idx / C, c = idx % C;
         sm.u.b.Tm[r * LDC + c] = Tg[idx];
         sm.dP[r * LDC + c] = c <= r ? gr[GR::DTB + idx] : 0.f;
@@ -1573,7 +1581,7 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
     float4v pv[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-        const int t = wave + 4 * i;
+        const int t = wave + NW * i;
         pv[i] = z;
         if (t < NL) {
             int rt, ct;
@@ -1582,18 +1590,44 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
             for (int j = 0; j < 4; ++j) pv[i][j] = Pg[(16 * rt + 4 * lq + j) * C + 16 * ct + l16];
         }
     }
+    // phase 2 inputs of the first block, fetched early
+    float pg[EPT], pk[EPT], pq[EPT];
+    float pdkg[BPW][4], pdqg[BPW][4], pdke[RS];
+    auto fetch = [&](int c0) {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int idx = tid + NT * e, r = idx / CB, c = idx % CB;
+            pg[e] = g[tok(r) + c0 + c];
+            pk[e] = to_f32(k[tok(r) + c0 + c]);
+            pq[e] = to_f32(q[tok(r) + c0 + c]);
+        }
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) {
+            const int t = min(wave + NW * i, NBT - 1);
+            const int rt = t / CT, ct = t % CT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const size_t e = (size_t)(16 * rt + 4 * lq + j) * D + c0 + 16 * ct + l16;
+                pdkg[i][j] = gr[GR::DKG + e];
+                pdqg[i][j] = gr[GR::DQG + e];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RS; ++j) pdke[j] = gr[GR::DKE + (size_t)(RS * ss + j) * D + c0 + sc];
+    };
+    fetch(0);
     lds_barrier();
 
     // ---- phase 1: dbeta and dP ----
     // dbeta (through Tb = T diag beta) = colsum(dTb * T); Y = dT = dTb diag(beta)
     {
-        constexpr int PARTS = 256 / C;
+        constexpr int PARTS = NT / C;
         const int c = tid % C, p = tid / C;
         float acc = 0.f;
         for (int i = c + p; i < C; i += PARTS) acc += sm.dP[i * LDC + c] * sm.u.b.Tm[i * LDC + c];
         sm.tot[p * C + c] = acc;
     }
-    for (int idx = tid; idx < C * C; idx += 256) {
+    for (int idx = tid; idx < C * C; idx += NT) {
         const int r = idx / C, c = idx % C;
         sm.u.b.Y[r * LDC + c] = sm.dP[r * LDC + c] * sm.beta[c];
     }
@@ -1603,7 +1637,7 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
         float4v a[LPW];
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            const int t = wave + 4 * i;
+            const int t = wave + NW * i;
             a[i] = z;
             if (t < NL) {
                 int rt, ct;
@@ -1616,7 +1650,7 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
         lds_barrier();   // dTb reads (dbeta partials, Y) are done
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            const int t = wave + 4 * i;
+            const int t = wave + NW * i;
             if (t < NL) {
                 int rt, ct;
                 lower_tile(t, rt, ct);
@@ -1628,7 +1662,7 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
         // dA = -T^T Z (strict lower; T^T upper: k >= 16 rt); dbeta += rowsum(dA * P)
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            const int t = wave + 4 * i;
+            const int t = wave + NW * i;
             a[i] = z;
             if (t < NL) {
                 int rt, ct;
@@ -1648,7 +1682,7 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
         lds_barrier();   // Z reads done
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            const int t = wave + 4 * i;
+            const int t = wave + NW * i;
             if (t < NL) {
                 int rt, ct;
                 lower_tile(t, rt, ct);
@@ -1663,32 +1697,31 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
     lds_barrier();
     if (tid < C) {
         float acc = 0.f;
-        for (int p = 0; p < 256 / C; ++p) acc += sm.tot[p * C + tid];
+        for (int p = 0; p < NT / C; ++p) acc += sm.tot[p * C + tid];
         for (int ct = 0; ct <= tid / 16; ++ct) acc += sm.red[ct * C + tid];
         if (tid < len) dbeta[(size_t)(tok0 + tid) * H + h] = acc;
     }
 
     // ---- phase 2: per block of CB channels ----
-    float pg[EPT], pk[EPT], pq[EPT];
-    auto fetch = [&](int c0) {
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const int idx = tid + 256 * e, r = idx / CB, c = idx % CB;
-            pg[e] = g[tok(r) + c0 + c];
-            pk[e] = to_f32(k[tok(r) + c0 + c]);
-            pq[e] = to_f32(q[tok(r) + c0 + c]);
-        }
-    };
-    fetch(0);
     for (int c0 = 0; c0 < D; c0 += CB) {
         lds_barrier();   // previous block's (or phase 1's) LDS reads are done
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            const int idx = tid + 256 * e, r = idx / CB, c = idx % CB;
+            const int idx = tid + NT * e, r = idx / CB, c = idx % CB;
             sm.u.c.G[r * LDB + c] = r < len ? pg[e] : 0.f;
             sm.u.c.kg[r * LDB + c] = r < len ? pk[e] : 0.f;    // raw k for now
             sm.u.c.qg[r * LDB + c] = r < len ? pq[e] : 0.f;    // raw q for now
         }
+        float dkg[BPW][4], dqg[BPW][4], dke[RS];
+#pragma unroll
+        for (int i = 0; i < BPW; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                dkg[i][j] = pdkg[i][j];
+                dqg[i][j] = pdqg[i][j];
+            }
+#pragma unroll
+        for (int j = 0; j < RS; ++j) dke[j] = pdke[j];
         if (c0 + CB < D) fetch(c0 + CB);
         lds_barrier();
         // chunk-local cumulative gate: segmented inclusive scan down the rows
@@ -1711,37 +1744,44 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
             off += s2 < ss ? t : 0.f;
         }
         const float egn = exp_e(gnv);
+        float ga[RS], gi[RS];
 #pragma unroll
         for (int j = 0; j < RS; ++j) {
             const int r = RS * ss + j;
             gv[j] += off;
-            const float ga = exp_e(gv[j]), gi = exp_e(-gv[j]);
+            ga[j] = exp_e(gv[j]);
+            gi[j] = exp_e(-gv[j]);
             const float kk = sm.u.c.kg[r * LDB + sc];
-            sm.u.c.kg[r * LDB + sc] = kk * ga;
-            sm.u.c.ki[r * LDB + sc] = kk * gi;
-            sm.u.c.qg[r * LDB + sc] *= ga;
+            sm.u.c.kg[r * LDB + sc] = kk * ga[j];
+            sm.u.c.ki[r * LDB + sc] = kk * gi[j];
+            sm.u.c.qg[r * LDB + sc] *= ga[j];
         }
         lds_barrier();
         // dKG = dP KI + grec, dKI = dP^T KG + dM^T QG, dQG = dM KI + grec
-        for (int rt = wave; rt < RT; rt += 4) {
-            float4v b1 = tile_mma(z, 0, 16 * (rt + 1),
-                                  [&](int m, int kk) { return sm.dP[(16 * rt + m) * LDC + kk]; },
-                                  [&](int kk, int n) { return sm.u.c.ki[kk * LDB + n]; });
-            float4v b2 = tile_mma(z, 16 * rt, C,
-                                  [&](int m, int kk) { return sm.dP[kk * LDC + 16 * rt + m]; },
-                                  [&](int kk, int n) { return sm.u.c.kg[kk * LDB + n]; });
-            b2 = tile_mma(b2, 16 * rt, C,
-                          [&](int m, int kk) { return sm.dM[kk * LDC + 16 * rt + m]; },
-                          [&](int kk, int n) { return sm.u.c.qg[kk * LDB + n]; });
-            float4v b3 = tile_mma(z, 0, 16 * (rt + 1),
-                                  [&](int m, int kk) { return sm.dM[(16 * rt + m) * LDC + kk]; },
-                                  [&](int kk, int n) { return sm.u.c.ki[kk * LDB + n]; });
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * rt + 4 * lq + j;
-                sm.u.c.x1[r * LDB + l16] = b1[j] + gr[GR::DKG + (size_t)r * D + c0 + l16];
-                sm.u.c.x2[r * LDB + l16] = b2[j];
-                sm.u.c.x3[r * LDB + l16] = b3[j] + gr[GR::DQG + (size_t)r * D + c0 + l16];
+        for (int i = 0; i < BPW; ++i) {
+            const int t = wave + NW * i;
+            if (t < NBT) {
+                const int rt = t / CT, ct = t % CT;
+                float4v b1 = tile_mma(z, 0, 16 * (rt + 1),
+                                      [&](int m, int kk) { return sm.dP[(16 * rt + m) * LDC + kk]; },
+                                      [&](int kk, int n) { return sm.u.c.ki[kk * LDB + 16 * ct + n]; });
+                float4v b2 = tile_mma(z, 16 * rt, C,
+                                      [&](int m, int kk) { return sm.dP[kk * LDC + 16 * rt + m]; },
+                                      [&](int kk, int n) { return sm.u.c.kg[kk * LDB + 16 * ct + n]; });
+                b2 = tile_mma(b2, 16 * rt, C,
+                              [&](int m, int kk) { return sm.dM[kk * LDC + 16 * rt + m]; },
+                              [&](int kk, int n) { return sm.u.c.qg[kk * LDB + 16 * ct + n]; });
+                float4v b3 = tile_mma(z, 0, 16 * (rt + 1),
+                                      [&](int m, int kk) { return sm.dM[(16 * rt + m) * LDC + kk]; },
+                                      [&](int kk, int n) { return sm.u.c.ki[kk * LDB + 16 * ct + n]; });
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j, c = 16 * ct + l16;
+                    sm.u.c.x1[r * LDB + c] = b1[j] + dkg[i][j];
+                    sm.u.c.x2[r * LDB + c] = b2[j];
+                    sm.u.c.x3[r * LDB + c] = b3[j] + dqg[i][j];
+                }
             }
         }
         lds_barrier();
@@ -1751,20 +1791,18 @@ __global__ __launch_bounds__(256) void kda_bwd_intra(
 #pragma unroll
         for (int j = RS - 1; j >= 0; --j) {
             const int r = RS * ss + j;
-            const float ga = exp_e(gv[j]), gi = exp_e(-gv[j]);
             const float dKG = sm.u.c.x1[r * LDB + sc], dKI = sm.u.c.x2[r * LDB + sc];
             const float dQG = sm.u.c.x3[r * LDB + sc];
-            const float dKE = gr[GR::DKE + (size_t)r * D + c0 + sc];
             const float ki = sm.u.c.ki[r * LDB + sc];
             const float ke = ki * egn;                       // k exp(G_n - G)
             if (r < len) {
-                dk[tok(r) + c0 + sc] = dKG * ga + dKI * gi + dKE * egn * gi;
-                dq[tok(r) + c0 + sc] = dQG * ga;
+                dk[tok(r) + c0 + sc] = dKG * ga[j] + dKI * gi[j] + dke[j] * egn * gi[j];
+                dq[tok(r) + c0 + sc] = dQG * ga[j];
             }
             suf += dKG * sm.u.c.kg[r * LDB + sc] + dQG * sm.u.c.qg[r * LDB + sc] - dKI * ki -
-                   dKE * ke;
+                   dke[j] * ke;
             dgv[j] = suf;
-            kes += dKE * ke;
+            kes += dke[j] * ke;
         }
         sm.tot[ss * CB + sc] = suf;
         sm.tot2[ss * CB + sc] = kes;
@@ -2080,7 +2118,7 @@ static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan)
         {
             auto kern = kda_bwd_intra<D, C, IT>;
             if (hipError_t e = set_smem(kern, sizeof(BwdIntraSmem<C>))) return e;
-            hipLaunchKernelGGL(kern, grid, dim3(256), sizeof(BwdIntraSmem<C>), a.stream, a.T, a.H,
+            hipLaunchKernelGGL(kern, grid, dim3(64 * kBwdIntraWaves), sizeof(BwdIntraSmem<C>), a.stream, a.T, a.H,
                                nch_seq, table, total, (const IT*)a.q, (const IT*)a.k, a.g, a.beta,
                                aux, grec, b.dq, b.dk, b.dg, b.dbeta);
             if (hipError_t e = hipGetLastError()) return e;

@@ -131,3 +131,40 @@ def test_empty_input_copies_state():
     d = make_prefill(13, 2, 0, 2, 64, torch.bfloat16, s0_std=0.1)
     o, S = run(d, 64)
     assert o.numel() == 0 and torch.equal(S, d["S0"])
+
+
+
+def test_prefill_under_graph_capture():
+    """A long prefill captured into a HIP graph replays correctly, several
+    times, with other work in between."""
+    B, T, H, D = 1, 16384, 8, 128
+    d = kda_inputs.prefill_inputs(83, B, T, H, D, D, torch.bfloat16, "cuda", s0_std=0.1)
+    ref_o, ref_S = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64,
+                                     initial_state=d["S0"])
+    torch.cuda.synchronize()
+    ref_o, ref_S = ref_o.cpu().numpy(), ref_S.cpu().numpy()
+    o = torch.empty(B, T, H, D, device="cuda")
+    S = torch.empty(B, H, D, D, device="cuda")
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(B, T, H, D, D, 64), dtype=torch.uint8,
+                     device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up outside the capture
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64,
+                          initial_state=d["S0"], o=o, final_state=S, workspace=ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64,
+                          initial_state=d["S0"], o=o, final_state=S, workspace=ws, stream=s)
+    for rep in range(3):
+        o.fill_(0.0)
+        S.fill_(0.0)
+        junk = torch.randn(1 << 20, device="cuda").sum()   # unrelated eager work in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(o.cpu().numpy(), ref_o), rep
+        assert np.array_equal(S.cpu().numpy(), ref_S), rep
+        del junk
