@@ -82,7 +82,7 @@ LEG_SOURCES = {"prefill": ["kda_prefill.hip", "kda_chunk.h", "kda_common.h", "kd
                "backward": ["kda_prefill.hip", "kda_chunk.h", "kda_common.h", "kda_internal.h"],
                "dplr": ["kda_dplr.hip", "kda_chunk.h", "kda_common.h", "kda_internal.h"]}
 LEG_KERNELS = {"prefill": ("kda_intra", "kda_inter"), "decode": ("decode_step_kernel",),
-               "backward": ("kda_intra", "kda_state_chain", "kda_bwd_chain", "kda_bwd_dv",
+               "backward": ("kda_intra", "kda_state_chain", "kda_bwd_chain", "kda_bwd_vprod",
                             "kda_bwd_intra"),
                "dplr": ("kda_dplr_intra", "kda_dplr_inter")}
 COPY_BYTES = 1 << 30   # the copy target reads and writes 1 GiB per dispatch
@@ -551,8 +551,8 @@ def main():
                    roofline=dict(bound="hbm", achieved=bb / (bw["ms"] / 1e3) / 1e9,
                                  peak=HBM_PEAK_GBS, unit="GB/s", algorithmic_bytes=bb,
                                  traffic=measured_traffic("backward"),
-                                 kernel="kda_chunk_bwd call (kda_intra, kda_inter with state "
-                                        "history, kda_bwd_chain, kda_bwd_dv, kda_bwd_intra)"))
+                                 kernel="kda_chunk_bwd call (kda_intra, kda_state_chain, "
+                                        "kda_bwd_chain, kda_bwd_vprod, kda_bwd_intra)"))
         bwd["roofline"]["frac"] = bwd["roofline"]["achieved"] / HBM_PEAK_GBS
 
     dplr = None

@@ -223,8 +223,9 @@ kda_status kda_decode_step_ex(int N, int H, int dk, int dv, float scale,
  * kda_chunk_fwd_workspace_bytes.  It holds the chunk records in fp32 (the
  * size kda_chunk_fwd_workspace_bytes gives for KDA_F32, for either input
  * type) plus, per (chunk, head), the UT factor and the k Gram (C x C each),
- * the state at the chunk start, the state gradient after it and a gradient
- * record: (2 dk dv + 3 C dk + 4 C^2 + dk) * 4 bytes, rounded. */
+ * the state at the chunk start, the state gradient after it, four C x dv
+ * intermediate tiles and a gradient record:
+ * (2 dk dv + 4 C dv + 3 C dk + 4 C^2 + dk) * 4 bytes, rounded. */
 size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv,
                                      int chunk, int num_seqs,
                                      kda_dtype qkv_dtype);

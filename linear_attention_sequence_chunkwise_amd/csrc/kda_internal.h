@@ -81,10 +81,11 @@ struct BackwardArgs {
 
 // Workspace of the backward: the forward's table and records (fp32), then
 // T and the strict-lower k Gram of every chunk, the state at every chunk
-// start, dS after every chunk, and per-chunk gradient records.
+// start, dS after every chunk, the chunk tiles X, U, dU, dX ([C][D] fp32
+// each), and per-chunk gradient records.
 struct BackwardPlan {
     PrefillPlan f;
-    size_t off_aux, off_shist, off_dshist, off_grec;
+    size_t off_aux, off_shist, off_dshist, off_xh, off_uh, off_duh, off_dxh, off_grec;
     size_t grec_floats;
     size_t total;
 };

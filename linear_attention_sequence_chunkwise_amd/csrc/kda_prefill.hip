@@ -560,12 +560,16 @@ struct ChunkTiles {
 // state published to LDS; a barrier separates the last reads of the chunk
 // tiles and of the old state from that write, so on return the chunk's tiles
 // may be overwritten.  OUT = false: state only (QS and O are skipped).
+// xh, uh (optional): this chunk's [C][D] fp32 tiles of X and U, of which the
+// slice's columns are written (the backward pass reads them).
 template <int D, int C, int BV, typename OT, typename IT, int NWC = 4, bool OUT = true>
 __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
                                             ChainScratch<D, C, BV, OT>& cs,
                                             float4v (&st)[((D / 16) * (BV / 16) + NWC - 1) / NWC],
                                             int tok0, int len, int H, int h, int v0,
-                                            float scale, float* __restrict__ o) {
+                                            float scale, float* __restrict__ o,
+                                            float* __restrict__ xh = nullptr,
+                                            float* __restrict__ uh = nullptr) {
     constexpr int LDK = padded<OT>(D);
     constexpr int CK = chunk_k<C, OT>();
     constexpr int LDC = padded<OT>(CK);
@@ -604,6 +608,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
                 const int r = 16 * rt + 4 * lq + j;
                 const float vv = r < len ? to_f32(t.v[r * BV + 16 * vt + l16]) : 0.f;
                 cs.x[(16 * vt + l16) * LDC + r] = to_ot<OT>(vv - xk[j]);
+                if (xh) xh[(size_t)r * D + v0 + 16 * vt + l16] = vv - xk[j];
             }
         }
     }
@@ -623,8 +628,10 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
                                mm::load(cs.x, LDC, 16 * vt + l16, kk), uacc);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
                 cs.u[(16 * vt + l16) * LDC + 16 * rt + 4 * lq + j] = to_ot<OT>(uacc[j]);
+                if (uh) uh[(size_t)(16 * rt + 4 * lq + j) * D + v0 + 16 * vt + l16] = uacc[j];
+            }
         }
     }
     lds_barrier();
@@ -742,14 +749,16 @@ __global__ __launch_bounds__(256) void kda_inter(
 }
 
 // Forward chain of the backward pass: the state at the start of every chunk
-// into s_hist ([chunk][H][D][D] fp32), no output.  Only the record parts the
+// into s_hist ([chunk][H][D][D] fp32) and the chunk's X and U into xh, uh
+// ([chunk][H][C][D] fp32), no output.  Only the record parts the
 // state update reads are loaded (KG, KPt, Tb, Gamma_n), and the next chunk's
 // parts are fetched into registers while the current chunk computes.
 template <int D, int C, int BV, typename OT, typename IT>
 __global__ __launch_bounds__(256) void kda_state_chain(
     int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
     const int* __restrict__ chunk_off, const IT* __restrict__ v, const float* __restrict__ s0,
-    const char* __restrict__ records, float* __restrict__ s_hist) {
+    const char* __restrict__ records, float* __restrict__ s_hist, float* __restrict__ xh,
+    float* __restrict__ uh) {
     constexpr int ST = (D / 16) * (BV / 16);
     constexpr int SPW = (ST + 3) / 4;
     typedef Rec<D, C, OT> R;
@@ -808,8 +817,9 @@ __global__ __launch_bounds__(256) void kda_state_chain(
         if (c + 1 < cp.nch) fetch(c + 1);
         chain_store_state<D, BV>(st, s_hist, ((size_t)(cp.first + c) * H + cp.h) * (size_t)D * D,
                                  cp.v0);
+        const size_t xo = ((size_t)(cp.first + c) * H + cp.h) * (size_t)C * D;
         inter_chunk<D, C, BV, OT, IT, 4, false>(tiles, sm.cs, st, tok0, len, H, cp.h, cp.v0, 0.f,
-                                                nullptr);
+                                                nullptr, xh + xo, uh + xo);
     }
 }
 
@@ -1062,9 +1072,9 @@ static hipError_t launch_epilogue(const PrefillArgs& a) {
 //   dG = dKG KG + dQG QG - dKI KI - dKE KE;  dG_n = colsum(dKE KE) + dGamma_n Gamma_n
 //   dg_r = sum_{r' >= r} dG_r' + dG_n
 // Kernels: the forward records (K0/K1) and a forward chain that keeps the
-// state at every chunk start; B3 the reverse chain per (sequence, head,
-// 16-column slice), keeping dSn of every chunk; B4a the products that
-// contract over dv, per (chunk, head), looping over 16-column blocks; B4b the
+// state at every chunk start (and X, U); B3 the reverse chain per (sequence,
+// head, 16-column slice), keeping dSn (and dU, dX = dV) of every chunk; B4a the
+// products that contract over dv, per (chunk, head), over 16-column blocks; B4b the
 // intra-chunk part per (chunk, head) in fp32, looping over 16-channel blocks.
 // Only the lower-triangular parts of dT and dM matter: T and M are lower
 // triangular, so a perturbation of A or M never reaches their upper parts.
@@ -1119,7 +1129,8 @@ struct GradRec {
 // ---- B3: reverse chain ----
 // Eight wavefronts per (sequence, head, 16-column slice).  The next (earlier)
 // chunk's record and dO columns are fetched into registers while the current
-// chunk computes; the two products of dU run on separate wavefronts.
+// chunk computes; the two products of dU run on separate wavefronts.  Writes
+// dV (= dX) and the chunk's dU and dX ([chunk][H][C][D] fp32) for B4a.
 template <int D, int C, typename OT>
 struct BwdChainSmem {
     static constexpr int LDV = 17;
@@ -1137,7 +1148,8 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
     int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
     const int* __restrict__ chunk_off, float scale, const char* __restrict__ records,
     const float* __restrict__ d_o, const float* __restrict__ dS_final,
-    float* __restrict__ ds_hist, float* __restrict__ dS0) {
+    float* __restrict__ ds_hist, float* __restrict__ dS0, float* __restrict__ duh,
+    float* __restrict__ dxh, float* __restrict__ dv_out) {
     constexpr int NW = kBwdChainWaves, NT = 64 * NW;
     constexpr int BV = 16, LDV = 17;
     typedef Rec<D, C, OT> R;
@@ -1188,6 +1200,9 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
     const float4v z = {0.f, 0.f, 0.f, 0.f};
     for (int c = cp.nch - 1; c >= 0; --c) {
         const int chunk = cp.first + c;
+        const int tok0 = cp.seq_tok0 + c * C;
+        const int len = min(C, cp.seq_len - c * C);
+        const size_t xo = ((size_t)chunk * H + cp.h) * (size_t)C * D;
         // dSn of this chunk, for B4a
         float* dh = ds_hist + ((size_t)chunk * H + cp.h) * (size_t)D * D;
 #pragma unroll
@@ -1236,13 +1251,22 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
             for (int j = 0; j < 4; ++j) dst[(16 * rt + 4 * lq + j) * LDV + l16] = f * a[j];
         }
         lds_barrier();
-        // dX = Tb^T dU (Tb[i][r] vanishes for i < r)
+        for (int idx = tid; idx < C * BV; idx += NT) {
+            const int r = idx / BV, col = idx % BV;
+            duh[xo + (size_t)r * D + cp.v0 + col] = sm.dUa[r * LDV + col] + sm.dUb[r * LDV + col];
+        }
+        // dX = Tb^T dU (Tb[i][r] vanishes for i < r) = dV
         for (int rt = wave; rt < RT; rt += NW) {
             const float4v x = tile_mma(
                 z, 16 * rt, C, [&](int m, int k) { return (float)img[R::Tb + swz<OT, CK>(k, 16 * rt + m)]; },
                 [&](int k, int n) { return sm.dUa[k * LDV + n] + sm.dUb[k * LDV + n]; });
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sm.dX[(16 * rt + 4 * lq + j) * LDV + l16] = x[j];
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * rt + 4 * lq + j;
+                sm.dX[r * LDV + l16] = x[j];
+                dxh[xo + (size_t)r * D + cp.v0 + l16] = x[j];
+                if (r < len) dv_out[((size_t)(tok0 + r) * H + cp.h) * D + cp.v0 + l16] = x[j];
+            }
         }
         lds_barrier();
         // dS = Gamma_n dSn + scale QG^T dO - KG^T dX
@@ -1276,43 +1300,38 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
 }
 
 // ---- B4a: products over dv, per (chunk, head), 16-column value blocks ----
-// Eight wavefronts: in each block the four C x 16 products split into two
-// independent pairs (X, dU then U, dX) that run on separate wavefronts, and the
-// accumulated C x D / C x C products spread over all eight.  The next block's
-// state, state-gradient, dO and V columns are fetched into registers while the
-// current block computes.
-template <int D, int C, typename OT>
+// The chains hand over X, U (forward) and dU, dX (reverse) of every chunk, so
+// this kernel only accumulates the five products that contract over dv:
+//   d(Q Gamma) = scale dO S^T,  d(K Gamma) = -dX S^T,  dKE = U dSn^T   (C x dk)
+//   dM = scale dO U^T,  dTb = dU X^T                                      (lower C x C)
+// and dGamma_n = rowsum(dSn * S).  Eight wavefronts; the next block's columns
+// are fetched into registers while the current block computes.
+template <int D, int C>
 struct BwdDvSmem {
     static constexpr int LDV = 17;
-    static constexpr int CK = chunk_k<C, OT>();
-    OT kg[C * D];                      // record KG (swizzled)
-    OT tail[D * CK + 2 * C * CK];      // record KPt, Tb, M (swizzled)
     float S[D * LDV], dSn[D * LDV];
-    float dO[C * LDV], V[C * LDV], X[C * LDV], U[C * LDV], dU[C * LDV], dX[C * LDV];
+    float dO[C * LDV], X[C * LDV], U[C * LDV], dU[C * LDV], dX[C * LDV];
 };
 
 constexpr int kBwdDvWaves = 8;
 
-template <int D, int C, typename OT, typename IT>
-__global__ __launch_bounds__(64 * kBwdDvWaves) void kda_bwd_dv(
+template <int D, int C>
+__global__ __launch_bounds__(64 * kBwdDvWaves) void kda_bwd_vprod(
     int T, int H, int nch_seq, const ChunkInfo* __restrict__ table,
-    const int* __restrict__ chunk_total, float scale, const IT* __restrict__ v,
-    const char* __restrict__ records, const float* __restrict__ s_hist,
-    const float* __restrict__ ds_hist, const float* __restrict__ d_o,
-    float* __restrict__ grec, float* __restrict__ dv_out) {
+    const int* __restrict__ chunk_total, float scale, const float* __restrict__ s_hist,
+    const float* __restrict__ ds_hist, const float* __restrict__ xh, const float* __restrict__ uh,
+    const float* __restrict__ duh, const float* __restrict__ dxh, const float* __restrict__ d_o,
+    float* __restrict__ grec) {
     constexpr int NW = kBwdDvWaves, NT = 64 * NW;
     constexpr int BV = 16, LDV = 17;
-    typedef Rec<D, C, OT> R;
     typedef GradRec<D, C> GR;
-    constexpr int CK = R::CK;
     constexpr int RT = C / 16, DT = D / 16;
     constexpr int NQ = RT * DT, QPW = (NQ + NW - 1) / NW;          // C x D tiles per wavefront
     constexpr int NL = RT * (RT + 1) / 2, MPW = (NL + NW - 1) / NW; // lower C x C tiles
     constexpr int SPT = D * BV / NT, OPT = (C * BV + NT - 1) / NT;   // prefetch per thread
     static_assert(D * BV % NT == 0, "state slice split");
-    typedef u32x4 vec;
     extern __shared__ __align__(16) char smem_raw[];
-    BwdDvSmem<D, C, OT>& sm = *reinterpret_cast<BwdDvSmem<D, C, OT>*>(smem_raw);
+    BwdDvSmem<D, C>& sm = *reinterpret_cast<BwdDvSmem<D, C>*>(smem_raw);
 
     const int ch = blockIdx.x, h = blockIdx.y;
     int tok0, len;
@@ -1328,38 +1347,29 @@ __global__ __launch_bounds__(64 * kBwdDvWaves) void kda_bwd_dv(
     }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lq = lane >> 4;
-    const char* recb = records + ((size_t)ch * H + h) * R::bytes;
-    const float* Sh = s_hist + ((size_t)ch * H + h) * (size_t)D * D;
-    const float* dSh = ds_hist + ((size_t)ch * H + h) * (size_t)D * D;
+    const size_t hbase = ((size_t)ch * H + h) * (size_t)D * D;
+    const size_t tbase = ((size_t)ch * H + h) * (size_t)C * D;
 
-    float ps[SPT], pd[SPT], po[OPT], pv[OPT];
+    float ps[SPT], pd[SPT], po[OPT], px[OPT], pu[OPT], pdu[OPT], pdx[OPT];
     auto fetch = [&](int vb) {
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
             const int idx = tid + NT * i, c = idx / BV, col = idx % BV;
-            ps[i] = Sh[(size_t)c * D + vb + col];
-            pd[i] = dSh[(size_t)c * D + vb + col];
+            ps[i] = s_hist[hbase + (size_t)c * D + vb + col];
+            pd[i] = ds_hist[hbase + (size_t)c * D + vb + col];
         }
 #pragma unroll
         for (int i = 0; i < OPT; ++i) {
             const int idx = min(tid + NT * i, C * BV - 1), r = idx / BV, col = idx % BV;
-            const size_t off = ((size_t)(tok0 + min(r, len - 1)) * H + h) * D + vb + col;
-            po[i] = d_o[off];
-            pv[i] = to_f32(v[off]);
+            const size_t e = tbase + (size_t)r * D + vb + col;
+            po[i] = d_o[((size_t)(tok0 + min(r, len - 1)) * H + h) * D + vb + col];
+            px[i] = xh[e];
+            pu[i] = uh[e];
+            pdu[i] = duh[e];
+            pdx[i] = dxh[e];
         }
     };
     fetch(0);
-    {   // stage KG and the KPt / Tb / M tail of the record
-        constexpr int NKG = (int)(C * D * sizeof(OT) / 16);
-        constexpr int NTL = (int)((D * CK + 2 * C * CK) * sizeof(OT) / 16);
-        const vec* a = reinterpret_cast<const vec*>(recb + R::KG * sizeof(OT));
-        const vec* b = reinterpret_cast<const vec*>(recb + R::KPt * sizeof(OT));
-        for (int i = tid; i < NKG; i += NT) reinterpret_cast<vec*>(sm.kg)[i] = a[i];
-        for (int i = tid; i < NTL; i += NT) reinterpret_cast<vec*>(sm.tail)[i] = b[i];
-    }
-    const OT* kpt = sm.tail;
-    const OT* tb = sm.tail + D * CK;
-    const OT* mm = sm.tail + D * CK + C * CK;
 
     float4v aq[QPW], ak[QPW], ae[QPW], am[MPW], at[MPW];
 #pragma unroll
@@ -1367,10 +1377,9 @@ __global__ __launch_bounds__(64 * kBwdDvWaves) void kda_bwd_dv(
 #pragma unroll
     for (int i = 0; i < MPW; ++i) am[i] = at[i] = float4v{0.f, 0.f, 0.f, 0.f};
     float agn = 0.f;
-    const float4v z = {0.f, 0.f, 0.f, 0.f};
 
     for (int vb = 0; vb < D; vb += BV) {
-        lds_barrier();   // previous block's reads complete (and, first time, staging visible)
+        lds_barrier();   // previous block's reads complete
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
             const int idx = tid + NT * i, c = idx / BV, col = idx % BV;
@@ -1382,58 +1391,14 @@ __global__ __launch_bounds__(64 * kBwdDvWaves) void kda_bwd_dv(
             const int idx = tid + NT * i, r = idx / BV, col = idx % BV;
             if (idx < C * BV) {
                 sm.dO[r * LDV + col] = r < len ? po[i] : 0.f;
-                sm.V[r * LDV + col] = r < len ? pv[i] : 0.f;
+                sm.X[r * LDV + col] = px[i];
+                sm.U[r * LDV + col] = pu[i];
+                sm.dU[r * LDV + col] = pdu[i];
+                sm.dX[r * LDV + col] = pdx[i];
             }
         }
         if (vb + BV < D) fetch(vb + BV);
         lds_barrier();
-        // jobs [0, RT): X = V - KG S;  [RT, 2 RT): dU = scale M^T dO + KE dSn
-        for (int jb = wave; jb < 2 * RT; jb += NW) {
-            const int rt = jb % RT;
-            float4v x;
-            if (jb < RT) {
-                x = tile_mma(z, 0, D, [&](int m, int k) { return (float)sm.kg[swz<OT, D>(16 * rt + m, k)]; },
-                             [&](int k, int n) { return sm.S[k * LDV + n]; });
-            } else {
-                const float4v a = tile_mma(
-                    z, 16 * rt, C, [&](int m, int k) { return (float)mm[swz<OT, CK>(k, 16 * rt + m)]; },
-                    [&](int k, int n) { return sm.dO[k * LDV + n]; });
-                x = tile_mma(z, 0, D, [&](int m, int k) { return (float)kpt[swz<OT, CK>(k, 16 * rt + m)]; },
-                             [&](int k, int n) { return sm.dSn[k * LDV + n]; });
-#pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] += scale * a[j];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * rt + 4 * lq + j;
-                if (jb < RT) sm.X[r * LDV + l16] = sm.V[r * LDV + l16] - x[j];
-                else sm.dU[r * LDV + l16] = x[j];
-            }
-        }
-        lds_barrier();
-        // jobs [0, RT): U = Tb X (Tb[r][i] = 0 for i > r);  [RT, 2 RT): dX = Tb^T dU = dV
-        for (int jb = wave; jb < 2 * RT; jb += NW) {
-            const int rt = jb % RT;
-            if (jb < RT) {
-                const float4v u = tile_mma(
-                    z, 0, 16 * (rt + 1), [&](int m, int k) { return (float)tb[swz<OT, CK>(16 * rt + m, k)]; },
-                    [&](int k, int n) { return sm.X[k * LDV + n]; });
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sm.U[(16 * rt + 4 * lq + j) * LDV + l16] = u[j];
-            } else {
-                const float4v x = tile_mma(
-                    z, 16 * rt, C, [&](int m, int k) { return (float)tb[swz<OT, CK>(k, 16 * rt + m)]; },
-                    [&](int k, int n) { return sm.dU[k * LDV + n]; });
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * rt + 4 * lq + j;
-                    sm.dX[r * LDV + l16] = x[j];
-                    if (r < len) dv_out[((size_t)(tok0 + r) * H + h) * D + vb + l16] = x[j];
-                }
-            }
-        }
-        lds_barrier();
-        // accumulate the products over this block's dv columns
 #pragma unroll
         for (int i = 0; i < QPW; ++i) {
             const int t = wave + NW * i;
@@ -2012,7 +1977,7 @@ static hipError_t launch_d(const PrefillArgs& a, const PrefillPlan& plan) {
 // ---- backward host side ----
 template <int D, int C, typename OT, typename IT>
 constexpr bool bwd_fits() {
-    return sizeof(BwdChainSmem<D, C, OT>) <= kLdsLimit && sizeof(BwdDvSmem<D, C, OT>) <= kLdsLimit &&
+    return sizeof(BwdChainSmem<D, C, OT>) <= kLdsLimit && sizeof(BwdDvSmem<D, C>) <= kLdsLimit &&
            sizeof(BwdIntraSmem<C>) <= kLdsLimit && fits<D, C, OT>() &&
            inter_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
 }
@@ -2047,6 +2012,15 @@ bool backward_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool b
     off += hist;
     plan->off_dshist = off;
     off += hist;
+    const size_t tile = (nch * H * (size_t)C * D * sizeof(float) + 255) / 256 * 256;
+    plan->off_xh = off;
+    off += tile;
+    plan->off_uh = off;
+    off += tile;
+    plan->off_duh = off;
+    off += tile;
+    plan->off_dxh = off;
+    off += tile;
     plan->off_grec = off;
     off += (nch * H * plan->grec_floats * sizeof(float) + 255) / 256 * 256;
     plan->total = off;
@@ -2074,6 +2048,10 @@ static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan)
         float* ds_hist = reinterpret_cast<float*>(ws + plan.off_dshist);
         float* grec = reinterpret_cast<float*>(ws + plan.off_grec);
         float* aux = reinterpret_cast<float*>(ws + plan.off_aux);
+        float* xh = reinterpret_cast<float*>(ws + plan.off_xh);
+        float* uh = reinterpret_cast<float*>(ws + plan.off_uh);
+        float* duh = reinterpret_cast<float*>(ws + plan.off_duh);
+        float* dxh = reinterpret_cast<float*>(ws + plan.off_dxh);
         int* chunk_off;
         ChunkInfo* table;
         if (hipError_t e = launch_records<D, C, OT, IT>(a, plan.f, nch_seq, &chunk_off, &table, aux))
@@ -2087,7 +2065,7 @@ static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan)
             if (hipError_t e = set_smem(kern, smem)) return e;
             hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(256), smem, a.stream, a.T, a.H, a.N,
                                nch_seq, (int)G8, a.cu_seqlens, chunk_off, (const IT*)a.v, a.s0,
-                               (const char*)ws + plan.f.off_records, s_hist);
+                               (const char*)ws + plan.f.off_records, s_hist, xh, uh);
             if (hipError_t e = hipGetLastError()) return e;
         }
         // B3: reverse chain
@@ -2098,20 +2076,19 @@ static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan)
                                sizeof(BwdChainSmem<D, C, OT>), a.stream, a.T, a.H, a.N, nch_seq,
                                (int)G8, a.cu_seqlens, chunk_off, a.scale,
                                (const char*)ws + plan.f.off_records, b.d_o, b.dS_final, ds_hist,
-                               b.dS0);
+                               b.dS0, duh, dxh, b.dv);
             if (hipError_t e = hipGetLastError()) return e;
         }
         if (plan.f.nchunk_max == 0) return hipSuccess;
         const dim3 grid((unsigned)plan.f.nchunk_max, (unsigned)a.H);
         const int* total = varlen ? chunk_off + a.N : nullptr;
-        // B4a: products over dv, and dv
+        // B4a: products over dv
         {
-            auto kern = kda_bwd_dv<D, C, OT, IT>;
-            if (hipError_t e = set_smem(kern, sizeof(BwdDvSmem<D, C, OT>))) return e;
-            hipLaunchKernelGGL(kern, grid, dim3(64 * kBwdDvWaves), sizeof(BwdDvSmem<D, C, OT>), a.stream, a.T,
-                               a.H, nch_seq, table, total, a.scale, (const IT*)a.v,
-                               (const char*)ws + plan.f.off_records, s_hist, ds_hist, b.d_o, grec,
-                               b.dv);
+            auto kern = kda_bwd_vprod<D, C>;
+            const size_t smem = sizeof(BwdDvSmem<D, C>);
+            if (hipError_t e = set_smem(kern, smem)) return e;
+            hipLaunchKernelGGL(kern, grid, dim3(64 * kBwdDvWaves), smem, a.stream, a.T, a.H, nch_seq,
+                               table, total, a.scale, s_hist, ds_hist, xh, uh, duh, dxh, b.d_o, grec);
             if (hipError_t e = hipGetLastError()) return e;
         }
         // B4b: intra-chunk part

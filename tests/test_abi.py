@@ -140,8 +140,9 @@ def test_prep_and_epilogue_validation(lib):
 
 def test_backward_workspace_and_validation(lib):
     """The backward's workspace holds fp32 chunk records plus, per (chunk,
-    head), T and the k Gram (C x C each), two fp32 states and a gradient
-    record; bad arguments are rejected on the host."""
+    head), T and the k Gram (C x C each), two fp32 states, four C x d tiles
+    (X, U, dU, dX) and a gradient record; bad arguments are rejected on the
+    host."""
     E = {v: k for k, v in kda.STATUS_NAMES.items()}
     wf = lib.kda_chunk_fwd_workspace_bytes
     wb = lib.kda_chunk_bwd_workspace_bytes
@@ -150,7 +151,7 @@ def test_backward_workspace_and_validation(lib):
     # fp32 chunk records for either input type
     assert wb(1, 32768, H, d, d, C, 0, kda.KDA_BF16) == (
         wf(1, 32768, H, d, d, C, 0, kda.KDA_F32) + nch * H * 2 * C * C * 4 +
-        2 * nch * H * d * d * 4 + nch * H * grec * 4)
+        2 * nch * H * d * d * 4 + 4 * nch * H * C * d * 4 + nch * H * grec * 4)
     assert wb(1, 32768, H, d, d, C, 0, kda.KDA_BF16) == wb(1, 32768, H, d, d, C, 0, kda.KDA_F32)
     assert wb(1, 100, 2, 64, 32, 64, 0, kda.KDA_BF16) == 0
     assert wb(1, 100, 2, 64, 64, 48, 0, kda.KDA_BF16) == 0
