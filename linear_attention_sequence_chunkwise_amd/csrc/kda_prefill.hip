@@ -168,11 +168,12 @@ struct IntraSmem {
     static constexpr int LDA = padded<OT>(C);
     static constexpr int LDT = C + 4;
     // Gram operands while the Gram runs; afterwards the same bytes hold the
-    // triangular solve's fp32 T, the staged M tile and per-wave scratch.
+    // triangular solve's fp32 T, the staged M tile and per-wave scratch.  The
+    // left operand is k_r a_r for the k.k^T Gram, then q_r a_r for the q.k^T
+    // Gram (one buffer, so that three workgroups fit a CU's LDS).
     struct Gram {
-        OT kl[C * LDK];        // k_r a_r       (Gram left, k)
-        OT ql[C * LDK];        // q_r a_r       (Gram left, q)
-        OT kr[C * LDK];        // k_i b_i       (Gram right)
+        OT kl[C * LDK];        // k_r a_r, then q_r a_r   (Gram left)
+        OT kr[C * LDK];        // k_i b_i                 (Gram right)
     };
     struct Solve {
         float T[C * LDT];      // (I + A)^-1, fp32
@@ -187,7 +188,6 @@ struct IntraSmem {
     OT F[NB * NB * D];         // F_IJ per channel
     float sig[NB * D];         // per sub-block sum of g
     float egs[NB * D];         // exp(Gs_I): block start relative to the chunk start
-    float egn[NB * D];         // exp(G_n - Ge_I)
     float beta[C];
 };
 
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256) void kda_intra(
             const int c = c0 + e;
             float* gv = e ? g1 : g0;
             const float* kv = e ? k1v : k0v;
-            const float* qv = e ? q1v : q0v;
+            float* qv = e ? q1v : q0v;
             float Gs = 0.f, Gn = 0.f;
 #pragma unroll
             for (int m = 0; m < NB; ++m) {
@@ -319,7 +319,6 @@ __global__ __launch_bounds__(256) void kda_intra(
             }
             const float sigI = sm.sig[I * D + c];
             sm.egs[I * D + c] = exp_e(Gs);                // exp(G before block I) <= 1
-            sm.egn[I * D + c] = exp_e(Gn - Gs - sigI);    // exp(G_n - Ge_I) <= 1
             float GsJ = 0.f;
             for (int J = 0; J <= I; ++J) {
                 const float sgJ = sm.sig[J * D + c];
@@ -337,7 +336,7 @@ __global__ __launch_bounds__(256) void kda_intra(
                 a *= gv[j];
                 const int r = 16 * I + j;
                 sm.u.g.kl[r * LDK + c] = to_ot<OT>(kv[j] * a);
-                sm.u.g.ql[r * LDK + c] = to_ot<OT>(qv[j] * a);
+                qv[j] *= a;            // q_r a_r, written to LDS after the k.k^T Gram
             }
             float bb = 1.f;
 #pragma unroll
@@ -350,24 +349,22 @@ __global__ __launch_bounds__(256) void kda_intra(
     }
     lds_barrier();
 
-    // ---- phase 3a: record tiles KG, QG, KPt from the LDS operands ----
-    // KG_r = (k_r a_r) exp(Gs_I), QG_r = (q_r a_r) exp(Gs_I) : rows of 16 bytes
+    // ---- phase 3a: record tiles KG, KPt from the LDS operands ----
+    // KG_r = (k_r a_r) exp(Gs_I) : rows of 16 bytes
     for (int idx = tid; idx < C * D / EPV; idx += 256) {
         const int r = idx / (D / EPV), c0 = (idx % (D / EPV)) * EPV;
         const float* eg = &sm.egs[(r >> 4) * D + c0];
-        float kk[EPV], qq[EPV];
+        float kk[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-            kk[e] = (float)sm.u.g.kl[r * LDK + c0 + e] * eg[e];
-            qq[e] = (float)sm.u.g.ql[r * LDK + c0 + e] * eg[e];
-        }
+        for (int e = 0; e < EPV; ++e) kk[e] = (float)sm.u.g.kl[r * LDK + c0 + e] * eg[e];
         *reinterpret_cast<vec*>(rec + R::KG + swz<OT, D>(r, c0)) = pack16(kk);
-        *reinterpret_cast<vec*>(rec + R::QG + swz<OT, D>(r, c0)) = pack16(qq);
     }
     // KPt[c][i] = (k_i b_i) exp(G_n - Ge_J), transposed: 16 bytes of one channel row
     for (int idx = tid; idx < D * C / EPV; idx += 256) {
         const int c = idx / (C / EPV), i0 = (idx % (C / EPV)) * EPV;
-        const float f = sm.egn[(i0 >> 4) * D + c];
+        float tail = 0.f;   // G_n - Ge_J: the gate sums of the later sub-blocks
+        for (int m = (i0 >> 4) + 1; m < NB; ++m) tail += sm.sig[m * D + c];
+        const float f = exp_e(tail);
         float kk[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) kk[e] = (float)sm.u.g.kr[(i0 + e) * LDK + c] * f;
@@ -375,41 +372,40 @@ __global__ __launch_bounds__(256) void kda_intra(
     }
 
     // ---- phase 3b: Gram blocks on the matrix cores ----
-    // tiles t in [0, 2 NT): first NT are A (k.k^T), the rest M (q.k^T).  A goes
-    // to LDS now; M stays in registers until the Gram operands are dead.
+    // First the NT lower blocks of A (k.k^T), straight to LDS; then the left
+    // operand becomes q_r a_r and the NT blocks of M (q.k^T) stay in registers
+    // until the Gram operands are dead.
     constexpr int NT = NB * (NB + 1) / 2;
-    constexpr int TPW = (2 * NT + 3) / 4;
+    constexpr int TPW = (NT + 3) / 4;
     const int l16 = lane & 15;
     const int lq = lane >> 4;
-    float4v macc[TPW];
+    auto gram = [&](int Ib, int Jb) {
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D; ks += mm::KS) {
+            const int kk = ks + lq * mm::KPL;
+            typename mm::frag af = mm::load(sm.u.g.kl, LDK, 16 * Ib + l16, kk);
+            typename mm::frag bf = mm::load(sm.u.g.kr, LDK, 16 * Jb + l16, kk);
+            const typename mm::frag ff = mm::load(sm.F + (Ib * NB + Jb) * D, 0, 0, kk);
+            bf = bf * ff;
+            acc = mm::mma(af, bf, acc);
+        }
+        return acc;
+    };
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         const int t = wave + 4 * i;
-        macc[i] = float4v{0.f, 0.f, 0.f, 0.f};
-        if (t < 2 * NT) {
-            const bool isM = t >= NT;
-            int tt = isM ? t - NT : t;
-            int Ib = 0;
+        if (t < NT) {
+            int tt = t, Ib = 0;
             while (tt > Ib) { tt -= Ib + 1; ++Ib; }
             const int Jb = tt;
-            const OT* left = isM ? sm.u.g.ql : sm.u.g.kl;
-            float4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < D; ks += mm::KS) {
-                const int kk = ks + lq * mm::KPL;
-                typename mm::frag af = mm::load(left, LDK, 16 * Ib + l16, kk);
-                typename mm::frag bf = mm::load(sm.u.g.kr, LDK, 16 * Jb + l16, kk);
-                const typename mm::frag ff = mm::load(sm.F + (Ib * NB + Jb) * D, 0, 0, kk);
-                bf = bf * ff;
-                acc = mm::mma(af, bf, acc);
-            }
+            const float4v acc = gram(Ib, Jb);
             const int col = 16 * Jb + l16;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * Ib + 4 * lq + j;
-                if (!isM) sm.A[row * LDA + col] = to_ot<OT>(col < row ? sm.beta[row] * acc[j] : 0.f);
-                else macc[i][j] = col <= row ? acc[j] : 0.f;
-                if (aux && !isM)
+                sm.A[row * LDA + col] = to_ot<OT>(col < row ? sm.beta[row] * acc[j] : 0.f);
+                if (aux)
                     aux[((size_t)ch * H + h) * 2 * C * C + C * C + row * C + col] =
                         col < row ? acc[j] : 0.f;
             }
@@ -420,6 +416,40 @@ __global__ __launch_bounds__(256) void kda_intra(
         const int r = idx / C, col = idx - r * C;
         if ((col >> 4) > (r >> 4)) sm.A[r * LDA + col] = to_ot<OT>(0.f);
     }
+    lds_barrier();   // the k.k^T Gram's reads of kl are done
+    if (task) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int r = 16 * I + j;
+            sm.u.g.kl[r * LDK + c0] = to_ot<OT>(q0v[j]);
+            sm.u.g.kl[r * LDK + c0 + 1] = to_ot<OT>(q1v[j]);
+        }
+    }
+    lds_barrier();
+    // QG_r = (q_r a_r) exp(Gs_I) : rows of 16 bytes
+    for (int idx = tid; idx < C * D / EPV; idx += 256) {
+        const int r = idx / (D / EPV), c0 = (idx % (D / EPV)) * EPV;
+        const float* eg = &sm.egs[(r >> 4) * D + c0];
+        float qq[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) qq[e] = (float)sm.u.g.kl[r * LDK + c0 + e] * eg[e];
+        *reinterpret_cast<vec*>(rec + R::QG + swz<OT, D>(r, c0)) = pack16(qq);
+    }
+    float4v macc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int t = wave + 4 * i;
+        macc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+        if (t < NT) {
+            int tt = t, Ib = 0;
+            while (tt > Ib) { tt -= Ib + 1; ++Ib; }
+            const int Jb = tt;
+            const float4v acc = gram(Ib, Jb);
+            const int col = 16 * Jb + l16;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) macc[i][j] = col <= 16 * Ib + 4 * lq + j ? acc[j] : 0.f;
+        }
+    }
     lds_barrier();   // Gram operands dead from here on
 
     // ---- phase 4a: stage M; invert the diagonal 16x16 blocks of I + A ----
@@ -427,9 +457,8 @@ __global__ __launch_bounds__(256) void kda_intra(
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         const int t = wave + 4 * i;
-        if (t >= NT && t < 2 * NT) {
-            int tt = t - NT;
-            int Ib = 0;
+        if (t < NT) {
+            int tt = t, Ib = 0;
             while (tt > Ib) { tt -= Ib + 1; ++Ib; }
             const int Jb = tt;
 #pragma unroll
