@@ -168,3 +168,25 @@ def test_prefill_under_graph_capture():
         assert np.array_equal(o.cpu().numpy(), ref_o), rep
         assert np.array_equal(S.cpu().numpy(), ref_S), rep
         del junk
+
+
+def test_concurrent_streams():
+    """Two prefills on two streams at once give the results of running them one
+    after the other (the library keeps no state between calls)."""
+    B, T, H, D = 1, 4096, 8, 128
+    da = kda_inputs.prefill_inputs(84, B, T, H, D, D, torch.bfloat16, "cuda", s0_std=0.1)
+    db = kda_inputs.prefill_inputs(85, B, T, H, D, D, torch.bfloat16, "cuda", s0_std=0.1)
+    run = lambda d, st=None: kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                               chunk=64, initial_state=d["S0"], stream=st)
+    ra, rb = run(da), run(db)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        ca = run(da, s1)
+    with torch.cuda.stream(s2):
+        cb = run(db, s2)
+    torch.cuda.synchronize()
+    for x, y in zip(ra + rb, ca + cb):
+        assert torch.equal(x, y)
