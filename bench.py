@@ -81,7 +81,8 @@ LEG_SOURCES = {"prefill": ["kda_prefill.hip", "kda_chunk.h", "kda_common.h", "kd
                "decode": ["kda_decode.hip", "kda_common.h", "kda_internal.h"],
                "backward": ["kda_prefill.hip", "kda_chunk.h", "kda_common.h", "kda_internal.h"],
                "dplr": ["kda_dplr.hip", "kda_chunk.h", "kda_common.h", "kda_internal.h"]}
-LEG_KERNELS = {"prefill": ("kda_intra", "kda_inter"), "decode": ("decode_step_kernel",),
+LEG_KERNELS = {"prefill": ("kda_intra", "kda_seg_chain", "kda_seg_combine", "kda_inter"),
+               "decode": ("decode_step_kernel",),
                "backward": ("kda_intra", "kda_state_chain", "kda_bwd_chain", "kda_bwd_vprod",
                             "kda_bwd_intra"),
                "dplr": ("kda_dplr_intra", "kda_dplr_inter")}
@@ -132,6 +133,8 @@ def traffic_from(d):
                 short = next((x for x in kern if x in k), None)
                 if short is None:
                     continue
+                if short == "kda_seg_chain":   # pass 1 (state runs) and pass 3 (outputs)
+                    short += " pass 3" if ("true>" in k or "Lb1E" in k) else " pass 1"
                 per_kernel.setdefault(short, {})[ctr] = v * 1024.0 / scale[ctr]
         total = sum(v.get("FETCH_SIZE", 0.0) + v.get("WRITE_SIZE", 0.0)
                     for v in per_kernel.values())
@@ -234,7 +237,8 @@ def bench_prefill(kda, kda_inputs, steps, warmup, stream):
         call()
     ms = tm.stop() / steps
     torch.cuda.synchronize()
-    return dict(ms=ms, tokens=B * T, token_heads=B * T * H, inputs=d)
+    return dict(ms=ms, tokens=B * T, token_heads=B * T * H, inputs=d,
+                segments=kda.kda_chunk_fwd_segments(B, T, H, D, D, C))
 
 
 def bench_prefill_prep(kda, kda_inputs, steps, warmup, stream, with_epilogue=False):
@@ -533,7 +537,9 @@ def main():
     tok_s = pf["tokens"] / (pf["ms"] / 1e3)
     roof = dict(bound="hbm", achieved=pf_bytes / (pf["ms"] / 1e3) / 1e9, peak=HBM_PEAK_GBS,
                 unit="GB/s", traffic=measured_traffic("prefill"),
-                kernel="kda_chunk_fwd call (kda_intra + kda_inter_dma)",
+                kernel="kda_chunk_fwd call (kda_intra, then the segment-parallel chain: "
+                       "kda_seg_chain state runs, kda_seg_combine, kda_seg_chain with outputs)",
+                chain_segments=pf["segments"],
                 algorithmic_bytes=pf_bytes,
                 mfma_tflops=pf_flops / (pf["ms"] / 1e3) / 1e12)
     roof["frac"] = roof["achieved"] / roof["peak"]

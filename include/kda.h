@@ -125,11 +125,24 @@ int kda_version(void);
 /* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if the
  * sizes are invalid or unsupported).  num_seqs: the number of packed
  * sequences when cu_seqlens will be passed (then B must be 1), or 0 for
- * B equal-length rows.  The size grows with T and num_seqs only, so a
- * workspace sized for the largest call serves all smaller ones. */
+ * B equal-length rows.  With B, H, dk, dv, chunk and dtype fixed, the size
+ * never shrinks as T or num_seqs grow, so a workspace sized for the longest
+ * call serves all shorter ones. */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv,
                                      int chunk, int num_seqs,
                                      kda_dtype qkv_dtype);
+
+/* How kda_chunk_fwd runs the sequential part of the chunk form (the state
+ * carried from chunk to chunk) for these sizes: 1 = one chain per (sequence,
+ * head), split over dv columns; n > 1 = each sequence cut into n segments,
+ * the segments' local end states and transition products computed in
+ * parallel, combined, and every segment then run from its true starting
+ * state (only for B equal-length rows, when B*H is small against the CU
+ * count).  Both give the chunk form's result; they differ by rounding only.
+ * 0 if the sizes are invalid or unsupported.  Informational: nothing needs
+ * it to make a call. */
+int kda_chunk_fwd_segments(int B, int T, int H, int dk, int dv, int chunk,
+                           int num_seqs, kda_dtype qkv_dtype);
 
 /* Chunkwise-parallel KDA prefill.
  *

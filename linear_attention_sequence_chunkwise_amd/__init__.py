@@ -44,6 +44,7 @@ SIGNATURES = {
     "kda_status_string": (ctypes.c_char_p, [_I]),
     "kda_version": (_I, []),
     "kda_chunk_fwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "kda_chunk_fwd_segments": (_I, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "kda_chunk_fwd": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                            _P, _P, _P, _SZ, _P]),
     "kda_chunk_fwd_ex": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
@@ -163,6 +164,12 @@ def kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torc
     code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
     return int(load_library().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs,
                                                              code))
+
+
+def kda_chunk_fwd_segments(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torch.bfloat16):
+    """Segments per sequence of the prefill's chain for these sizes (1: none)."""
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load_library().kda_chunk_fwd_segments(B, T, H, dk, dv, chunk, num_seqs, code))
 
 
 def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu_seqlens=None,

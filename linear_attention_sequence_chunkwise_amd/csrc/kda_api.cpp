@@ -82,6 +82,16 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
     return plan.total;
 }
 
+int kda_chunk_fwd_segments(int B, int T, int H, int dk, int dv, int chunk, int num_seqs,
+                           kda_dtype qkv_dtype) {
+    if (kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs, qkv_dtype) == 0) return 0;
+    const bool varlen = num_seqs > 0;
+    kda::PrefillPlan plan;
+    kda::prefill_plan(B, T, H, dk, chunk, varlen ? num_seqs : B, varlen, qkv_dtype == KDA_BF16,
+                      &plan);
+    return kda::prefill_chain_segments(plan);
+}
+
 kda_status kda_chunk_fwd_ex(int B, int T, int H, int dk, int dv, int chunk, float scale,
                             kda_dtype qkv_dtype, const void* q, const void* k, const void* v,
                             const float* g, const float* beta, const float* initial_state,

@@ -66,6 +66,8 @@ struct PrefillPlan {
     size_t chunk_rec_bytes;    // bytes of one chunk-head record
     size_t off_table;      // chunk table (varlen only)
     size_t off_records;    // chunk-head records
+    int nseg, seg_len;     // segments per sequence of the chain, chunks per segment
+    size_t off_seg;        // segment states (nseg > 1 only)
     size_t total;
 };
 
@@ -112,6 +114,8 @@ bool prefill_supported(int D, int C, bool bf16);
 bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf16,
                   PrefillPlan* plan);
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan);
+// Segments per sequence launch_prefill's chain uses with this plan (1: none).
+int prefill_chain_segments(const PrefillPlan& plan);
 hipError_t launch_decode(const DecodeArgs& a);
 // True when (D, C, dtype) has built backward kernels that fit in LDS.
 bool backward_supported(int D, int C, bool bf16);

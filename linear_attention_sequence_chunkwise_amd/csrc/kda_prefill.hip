@@ -44,6 +44,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "kda_chunk.h"
@@ -852,6 +853,495 @@ __global__ __launch_bounds__(256) void kda_state_chain(
     }
 }
 
+// Direct global-to-LDS copy (global_load_lds_dwordx4): every lane's 16 bytes
+// land at consecutive LDS addresses from the wave-uniform base in M0, with no
+// register destination; the copy counts in vmcnt like a load.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+// ---- K2s: segment-parallel chain for few long sequences ----
+//
+// Over one chunk the state moves as S <- A_c S + B_c, with
+// A_c S = Diag(Gamma_n) S - KPt Tb KG S and B_c = KPt Tb V (the chunk form of
+// the delta rule).  A run of several chunks from a state Z therefore ends at
+// P Z + E, where P is the product of the A_c (the run applied to the identity
+// with V = 0) and E is the run from zero.  A fixed-length sequence of nch
+// chunks is cut into nseg segments of L chunks:
+//   pass 1 (kda_seg_chain, OUT = false), for each segment s < nseg - 1: the
+//          run of V from S0 (s = 0) or from zero (E_s); for 0 < s < nseg - 1
+//          also the run of the identity with V = 0 (P_s), in a second
+//          workgroup on the same XCD, which reads the same records;
+//   pass 2 (kda_seg_combine): Sin_0 = S0, Sin_1 = E_0, and
+//          Sin_{s+1} = P_s Sin_s + E_s, in fp32;
+//   pass 3 (kda_seg_chain, OUT = true): every segment from Sin_s with
+//          outputs; the last one writes the final state.
+// Each workgroup owns all dv columns of its (sequence, head, segment): it
+// reads a chunk record once for D columns, where the per-slice chains read it
+// once per 16 columns, and sequences x heads x segments workgroups cover the
+// CUs even when sequences x heads is small.  State buffer `seg`, in planes of
+// [N*H][D][D] fp32: E_s at plane s (s < nseg - 1), P_s at plane nseg - 2 + s
+// (0 < s < nseg - 1), Sin_s at plane 2 nseg - 3 + s.
+__host__ __device__ constexpr int seg_planes(int nseg) { return 3 * nseg - 3; }
+__host__ __device__ constexpr int seg_plane_e(int s) { return s; }
+__host__ __device__ constexpr int seg_plane_p(int nseg, int s) { return nseg - 2 + s; }
+__host__ __device__ constexpr int seg_plane_in(int nseg, int s) { return 2 * nseg - 3 + s; }
+
+// Register-resident chain step.  Every 16 x 16 tile lives in the matrix-core
+// output layout (lane l holds rows 4*(l/16)+j, j = 0..3, of column l%16).
+// Rounded to the operand type, such a tile is directly the B operand of a
+// product that contracts over its rows, provided the contraction order inside
+// the instruction is permuted to match; the A operand (a record tile in LDS)
+// is read in the same order.  fp16: one 16x16x32 instruction contracts over
+// rows 4(l/16)..+3 of two tiles a, b; fp32: four 16x16x4 instructions per
+// tile, step s over rows 4m+s (m = 0..3).  So a wave that owns whole 16-column
+// blocks of the state runs X = V - KG S, U = Tb X, O = scale (QG S + M U) and
+// S <- Diag(Gamma_n) S + KPt U on its own registers, with no barrier and no
+// LDS round trip of S, X or U.
+//
+// B operands made once from NKT register tiles: fp16 pairs (tile 2p in
+// k-slots 0..3 of each lane, tile 2p+1 in 4..7; a missing last tile is zero),
+// or the fp32 tiles themselves.
+template <typename OT, int NKT>
+struct BOps {
+    static constexpr bool kHalf = sizeof(OT) == 2;
+    static constexpr int N = kHalf ? (NKT + 1) / 2 : NKT;
+    typename std::conditional<kHalf, half8, float4v>::type f[N];
+    __device__ __forceinline__ void from(const float4v (&t)[NKT]) {
+#pragma unroll
+        for (int p = 0; p < N; ++p) {
+            if constexpr (kHalf) {
+                const float4v a = t[2 * p];
+                const float4v b = 2 * p + 1 < NKT ? t[2 * p + 1] : float4v{0.f, 0.f, 0.f, 0.f};
+                f[p] = half8{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3],
+                             (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
+            } else {
+                f[p] = t[p];
+            }
+        }
+    }
+};
+
+// acc[nb] += A[16 ra + (0..15)][k-tiles 0 .. kend) * B over the tiles of
+// b[nb], for NB column blocks at once: every A fragment read from LDS feeds NB
+// instructions.  A: a swizzled [rows][LD] record tile in LDS.  fp16: pair p is
+// one 16x16x32 instruction, taken when 2p < kend (the A tile paired beyond
+// kend is zero: the triangular tiles' upper part or the record's k-padding).
+template <typename OT, int LD, int NKT, int NB>
+__device__ __forceinline__ void tile_chain_mma_nb(float4v (&acc)[NB], const OT* A, int ra,
+                                                  int kend, const BOps<OT, NKT> (&b)[NB]) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
+    const int row = 16 * ra + l16;
+    if constexpr (sizeof(OT) == 2) {
+#pragma unroll
+        for (int p = 0; p < BOps<OT, NKT>::N; ++p) {
+            if (2 * p < kend) {
+                const half4 x = *reinterpret_cast<const half4*>(A + swz<OT, LD>(row, 32 * p + 4 * lq));
+                const half4 y = *reinterpret_cast<const half4*>(A + swz<OT, LD>(row, 32 * p + 16 + 4 * lq));
+                const half8 af = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b[nb].f[p], acc[nb], 0, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+            if (kt < kend) {
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const float a = A[swz<OT, LD>(row, 16 * kt + 4 * lq + st)];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b[nb].f[kt][st], acc[nb], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// Record tiles of one chunk in LDS: the whole record (FULL), or packed, the
+// parts the state update reads: KG, then KPt and Tb, then Gamma_n.  Every
+// region is whole KiB (the record is, and Gamma_n ends it), so the image is
+// filled by 1 KiB direct global-to-LDS copies.
+template <int D, int C, typename OT, bool FULL>
+struct WideTiles {
+    typedef Rec<D, C, OT> R;
+    static constexpr int K_KPT = (int)(R::KPt * sizeof(OT) / 1024);   // KiB of KG (+ QG)
+    static constexpr int K_TB = (int)(R::Tb * sizeof(OT) / 1024);
+    static constexpr int K_M = (int)(R::M * sizeof(OT) / 1024);
+    static constexpr int K_QG = (int)(R::QG * sizeof(OT) / 1024);
+    static constexpr int K_REC = (int)(R::bytes / 1024);
+    static constexpr int K_GN = (int)(R::gn_byte / 1024);
+    static_assert(R::bytes % 1024 == 0 && (R::QG * sizeof(OT)) % 1024 == 0 &&
+                      (R::KPt * sizeof(OT)) % 1024 == 0 && (R::M * sizeof(OT)) % 1024 == 0 &&
+                      R::gn_byte % 1024 == 0 && K_REC == K_GN + 1,
+                  "record regions must be whole KiB, Gamma_n in the last one");
+    // copies (KiB) per image and the record KiB of image KiB j
+    static constexpr int KIB = FULL ? K_REC : K_QG + (K_M - K_KPT) + 1;
+    __device__ static int rec_kib(int j) {
+        if constexpr (FULL) return j;
+        return j < K_QG ? j : j < K_QG + (K_M - K_KPT) ? K_KPT + (j - K_QG) : K_GN;
+    }
+    const OT *kg, *qg, *kpt, *tb, *m;
+    const float* gn;
+    __device__ explicit WideTiles(const char* img) {
+        const OT* base = reinterpret_cast<const OT*>(img);
+        kg = base + R::KG;
+        if constexpr (FULL) {
+            qg = base + R::QG;
+            kpt = base + R::KPt;
+            tb = base + R::Tb;
+            m = base + R::M;
+            gn = reinterpret_cast<const float*>(img + R::gn_byte);
+        } else {
+            qg = m = nullptr;
+            kpt = reinterpret_cast<const OT*>(img + 1024 * (size_t)K_QG);
+            tb = kpt + (R::Tb - R::KPt);
+            gn = reinterpret_cast<const float*>(img + 1024 * (size_t)(K_QG + K_M - K_KPT));
+        }
+    }
+};
+
+// Value rows of one chunk for one wave's 16 * NVB columns, copied into the
+// wave's own LDS region ([C][16 NVB] of IT) by direct global-to-LDS loads:
+// LPR lanes per row, 64 / LPR rows per copy; rows past the chunk repeat its
+// last row.
+template <int C, typename IT, int NVB>
+struct ValueCopy {
+    static constexpr int LPR = 16 * NVB * (int)sizeof(IT) / 16;
+    static constexpr int ROWS = 64 / LPR;
+    static constexpr int NI = (C + ROWS - 1) / ROWS;
+    static constexpr int BYTES = C * 16 * NVB * (int)sizeof(IT);
+    static_assert(64 % LPR == 0, "value rows must be whole lanes of a copy");
+    // src: row 0, first column of this wave's columns; stride between rows
+    __device__ static __forceinline__ void issue(const IT* src, size_t stride, int len,
+                                                 uint32_t dst) {
+        const int lane = threadIdx.x & 63;
+        // this wave's reads of the region are complete before it is refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int r = i * ROWS + lane / LPR;
+            if (r < C)
+                dma16(src + (size_t)min(r, len - 1) * stride + (lane % LPR) * (16 / (int)sizeof(IT)),
+                      dst + i * 1024);
+        }
+    }
+};
+
+// One chunk for NB 16-column blocks of this wave: st[b] = block b's state
+// tiles (rows 16 ct.., ct = 0..D/16-1), its columns cbase + 16 b.  Blocks
+// b < NVB carry values, read from vl ([C][16 NVB] in LDS, rows < len count);
+// the others are runs of the identity (V = 0).  Once X is formed the value
+// region is refilled from vnext (the next chunk's rows, vlen of them; null:
+// nothing to fetch).  OUT: also O = scale (QG S + M U) into o for rows < len.
+template <int D, int C, typename OT, typename IT, bool OUT, int NB, int NVB>
+__device__ __forceinline__ void wide_chunk(const WideTiles<D, C, OT, OUT>& t,
+                                           float4v (&st)[NB][D / 16], const IT* vl,
+                                           uint32_t vl_lds, const IT* vnext, size_t vstride,
+                                           int vlen, int cbase, int tok0, int len, int H, int h,
+                                           float scale, float* __restrict__ o) {
+    constexpr int RT = C / 16, KT = D / 16;
+    constexpr int CK = chunk_k<C, OT>();
+    const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
+    const float4v zero = {0.f, 0.f, 0.f, 0.f};
+    // scheduling fences between row blocks and phases: without them the
+    // scheduler hoists the LDS operand loads of the whole chunk and spills
+    BOps<OT, KT> sb[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sb[nb].from(st[nb]);
+    float4v x[NB][RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        float4v acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = zero;
+        tile_chain_mma_nb<OT, D, KT, NB>(acc, t.kg, rt, KT, sb);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float4v vv = zero;
+            if (nb < NVB) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j;
+                    vv[j] = r < len ? to_f32(vl[r * 16 * NVB + 16 * nb + l16]) : 0.f;
+                }
+            }
+            x[nb][rt] = vv - acc[nb];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (NVB > 0 && vnext) ValueCopy<C, IT, NVB>::issue(vnext, vstride, vlen, vl_lds);
+    BOps<OT, RT> xb[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) xb[nb].from(x[nb]);
+    float4v u[NB][RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {   // Tb is lower triangular: k-tiles 0..rt
+        float4v acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = zero;
+        tile_chain_mma_nb<OT, CK, RT, NB>(acc, t.tb, rt, rt + 1, xb);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) u[nb][rt] = acc[nb];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    BOps<OT, RT> ub[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) ub[nb].from(u[nb]);
+    if constexpr (OUT) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float4v acc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = zero;
+            tile_chain_mma_nb<OT, D, KT, NB>(acc, t.qg, rt, KT, sb);
+            tile_chain_mma_nb<OT, CK, RT, NB>(acc, t.m, rt, rt + 1, ub);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j;
+                    if (r < len)
+                        o[((size_t)(tok0 + r) * H + h) * D + cbase + 16 * nb + l16] = scale * acc[nb][j];
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < KT; ++ct) {
+        float4v acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[nb][j] = st[nb][ct][j] * t.gn[16 * ct + 4 * lq + j];
+        }
+        tile_chain_mma_nb<OT, CK, RT, NB>(acc, t.kpt, ct, RT, ub);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) st[nb][ct] = acc[nb];
+        if (ct % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Waves and 16-column blocks per wave of the segment kernels.  Pass 1: one
+// wave per 16 columns of D, carrying those columns of the run of V (block 0)
+// and of the run of the identity (block 1).  Pass 3: kSegOutBlocks blocks of
+// the run of V per wave.
+constexpr int kSegOutBlocks = 1;
+template <int D, bool OUT>
+struct SegShape {
+    static constexpr int NCB = OUT ? (D / 16 >= kSegOutBlocks ? kSegOutBlocks : 1) : 2;
+    static constexpr int NVB = OUT ? NCB : 1;           // blocks with values
+    static constexpr int NW = OUT ? D / 16 / NCB : D / 16;
+};
+
+template <int D, int C, typename OT, typename IT, bool OUT>
+struct SegSmem {
+    alignas(1024) char img[2][WideTiles<D, C, OT, OUT>::KIB * 1024];
+    alignas(1024) char vals[SegShape<D, OUT>::NW]
+                           [(ValueCopy<C, IT, SegShape<D, OUT>::NVB>::BYTES + 1023) / 1024 * 1024];
+};
+
+template <int D, int C, typename OT, typename IT, bool OUT>
+__global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
+    int T, int H, int N_seq, int nch_seq, int L, int nseg, float scale,
+    const IT* __restrict__ v, const float* __restrict__ s0, const char* __restrict__ records,
+    float* __restrict__ o, float* __restrict__ sT, float* __restrict__ seg) {
+    typedef SegShape<D, OUT> SS;
+    typedef WideTiles<D, C, OT, OUT> WT;
+    typedef Rec<D, C, OT> R;
+    constexpr int KT = D / 16, RT = C / 16;
+    extern __shared__ __align__(1024) char smem_raw[];
+    SegSmem<D, C, OT, IT, OUT>& sm = *reinterpret_cast<SegSmem<D, C, OT, IT, OUT>*>(smem_raw);
+
+    const int lg = blockIdx.x;
+    const int nsp = OUT ? nseg : nseg - 1;   // segments this pass runs
+    const int s = lg % nsp, nh = lg / nsp;
+    if (nh >= N_seq * H) return;
+    const int n = nh / H, h = nh % H;
+    const int c0 = s * L, c1 = min(c0 + L, nch_seq);
+    const size_t plane = (size_t)N_seq * H * D * D;
+    const size_t sbase = (size_t)nh * D * D;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
+
+    // this wave's column blocks: pass 1, columns 16 wave.. of the run of V
+    // (block 0) and of the run of the identity (block 1; unused in segment 0);
+    // pass 3, columns 16 (NCB wave + b) of the run of V
+    const int cbase = 16 * SS::NVB * wave;
+    float4v st[SS::NCB][KT];
+#pragma unroll
+    for (int b = 0; b < SS::NCB; ++b) {
+        const bool ident = b >= SS::NVB;
+        const int col = (ident ? 16 * wave : cbase + 16 * b) + l16;
+        const float* src = OUT ? seg + seg_plane_in(nseg, s) * plane : (!ident && s == 0 ? s0 : nullptr);
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * ct + 4 * lq + j;
+                st[b][ct][j] = src ? src[sbase + (size_t)row * D + col]
+                                   : (ident && row == col ? 1.f : 0.f);
+            }
+    }
+
+    // record KiB copies of chunk c into image buffer bi, spread over the waves
+    auto copy_record = [&](int c, int bi) {
+        const char* rec = records + ((size_t)(n * nch_seq + c) * H + h) * R::bytes;
+        const uint32_t base = lds_addr(sm.img[bi]);
+        for (int j = wave; j < WT::KIB; j += SS::NW)
+            dma16(rec + (size_t)WT::rec_kib(j) * 1024 + lane * 16, base + j * 1024);
+    };
+    // this wave's value columns of chunk c (row 0) in global memory
+    auto vsrc = [&](int c) -> const IT* {
+        return v + ((size_t)(n * T + c * C) * H + h) * D + cbase;
+    };
+    const size_t vstride = (size_t)H * D;
+    const IT* vl = reinterpret_cast<const IT*>(sm.vals[wave]);
+    const uint32_t vl_lds = lds_addr(sm.vals[wave]);
+    // Compiler-visible vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt at their
+    // maxima): the state loads are complete before the copies start.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (c0 < c1) {
+        copy_record(c0, 0);
+        ValueCopy<C, IT, SS::NVB>::issue(vsrc(c0), vstride, min(C, T - c0 * C), vl_lds);
+    }
+    for (int c = c0; c < c1; ++c) {
+        const int bi = (c - c0) & 1;
+        const int tok0 = n * T + c * C, len = min(C, T - c * C);
+        // this wave's copies of chunk c have landed; after the barrier every
+        // wave's have, and every wave is done with chunk c - 1, whose record
+        // buffer the copies of chunk c + 1 then refill
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+        lds_barrier();
+        if (c + 1 < c1) copy_record(c + 1, bi ^ 1);
+        const WT tiles(sm.img[bi]);
+        wide_chunk<D, C, OT, IT, OUT, SS::NCB, SS::NVB>(
+            tiles, st, vl, vl_lds, c + 1 < c1 ? vsrc(c + 1) : nullptr, vstride,
+            min(C, T - (c + 1) * C), cbase, tok0, len, H, h, scale, o);
+    }
+#pragma unroll
+    for (int b = 0; b < SS::NCB; ++b) {
+        const bool ident = b >= SS::NVB;
+        float* dst = OUT ? (s == nseg - 1 ? sT : nullptr)
+                         : seg + (ident ? seg_plane_p(nseg, s) : seg_plane_e(s)) * plane;
+        if (!dst || (ident && s == 0)) continue;
+        const int col = (ident ? 16 * wave : cbase + 16 * b) + l16;
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dst[sbase + (size_t)(16 * ct + 4 * lq + j) * D + col] = st[b][ct][j];
+    }
+}
+
+// Pass 2: the state entering every segment, Sin_{s+1} = P_s Sin_s + E_s in
+// fp32, for 16 value columns of one (sequence, head) per workgroup.  P_s and
+// the E_s columns stream into two LDS buffers by direct copies, the next
+// segment's while the current product runs.  P rows are stored with their
+// 16-byte groups XOR-permuted by the row (the copy's source addresses do the
+// permutation), so the rows that one read instruction touches fall in
+// different banks.
+template <int D>
+struct CombineSmem {
+    static constexpr int NG = D / 4;   // 16-byte groups per P row
+    alignas(1024) float p[2][D * D];
+    alignas(1024) float e[2][D * 16];
+    float cur[D][16];
+};
+template <int D>
+constexpr size_t seg_combine_smem() { return sizeof(CombineSmem<D>); }
+
+template <int D>
+__global__ __launch_bounds__(256) void kda_seg_combine(int NH, int nseg,
+                                                       const float* __restrict__ s0,
+                                                       float* __restrict__ seg) {
+    typedef CombineSmem<D> SM;
+    constexpr int NG = SM::NG;
+    constexpr int RPC = 64 / NG;      // P rows per 1 KiB copy
+    constexpr int PCOPIES = D * D * 4 / 1024;
+    constexpr int ECOPIES = D * 64 / 1024;   // 16 columns = 4 lanes per row
+    constexpr int RT = D / 16;               // 16-row output tiles
+    constexpr int TPW = RT > 4 ? RT / 4 : 1; // tiles per wave (waves >= RT idle)
+    extern __shared__ __align__(1024) char smem_raw[];
+    SM& sm = *reinterpret_cast<SM*>(smem_raw);
+    const int nh = blockIdx.x, v0 = 16 * blockIdx.y, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
+    const size_t plane = (size_t)NH * D * D, base = (size_t)nh * D * D;
+
+    auto copy = [&](int s, int bi) {
+        const float* P = seg + seg_plane_p(nseg, s) * plane + base;
+        const float* E = seg + seg_plane_e(s) * plane + base + v0;
+        for (int i = wave; i < PCOPIES + ECOPIES; i += 4) {
+            if (i < PCOPIES) {
+                const int r = i * RPC + lane / NG, g = lane % NG;
+                dma16(P + (size_t)r * D + 4 * (g ^ (r % NG)), lds_addr(sm.p[bi]) + i * 1024);
+            } else {
+                const int ie = i - PCOPIES, r = ie * 16 + lane / 4;
+                dma16(E + (size_t)r * D + 4 * (lane % 4), lds_addr(sm.e[bi]) + ie * 1024);
+            }
+        }
+    };
+    for (int idx = tid; idx < D * 16; idx += 256) {
+        const int k = idx / 16, j = idx % 16;
+        const size_t at = (size_t)k * D + v0 + j;
+        seg[seg_plane_in(nseg, 0) * plane + base + at] = s0 ? s0[base + at] : 0.f;
+        const float e = seg[seg_plane_e(0) * plane + base + at];
+        seg[seg_plane_in(nseg, 1) * plane + base + at] = e;
+        sm.cur[k][j] = e;
+    }
+    // Compiler-visible vmcnt(0): the loads above are complete before the
+    // copies start (gfx9 encoding, expcnt and lgkmcnt at their maxima).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (nseg > 2) copy(1, 0);
+    for (int s = 1; s + 1 < nseg; ++s) {
+        const int bi = (s - 1) & 1;
+        // P_s and E_s have landed (this wave's copies; the barrier: all of
+        // them), cur holds Sin_s, and the other buffers are free
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+        lds_barrier();
+        if (s + 2 < nseg) copy(s + 1, bi ^ 1);
+        // out tile (rows 16 rt..) = E + P cur on fp32 matrix cores, k in steps of 4
+        float4v acc[TPW];
+        const bool live = wave * TPW < RT;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[t][j] = live ? sm.e[bi][(16 * (wave * TPW + t) + 4 * lq + j) * 16 + l16] : 0.f;
+        if (live) {
+#pragma unroll 8
+            for (int kt = 0; kt < D / 4; ++kt) {
+                const float b = sm.cur[4 * kt + lq][l16];
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const int r = 16 * (wave * TPW + t) + l16;
+                    const float a = sm.p[bi][r * D + 4 * (kt ^ (r % NG)) + lq];
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[t], 0, 0, 0);
+                }
+            }
+        }
+        lds_barrier();   // every wave's reads of cur are done
+        if (live) {
+            float* out = seg + seg_plane_in(nseg, s + 1) * plane + base;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * (wave * TPW + t) + 4 * lq + j;
+                    sm.cur[r][l16] = acc[t][j];
+                    out[(size_t)r * D + v0 + l16] = acc[t][j];
+                }
+        }
+    }
+}
+
 // ---- K2b: double-buffered direct global-to-LDS variant ----
 //
 // The chunk records (already in LDS-image form) and value rows are moved by
@@ -878,16 +1368,6 @@ __global__ __launch_bounds__(256) void kda_state_chain(
 // Every copy has at least one chunk of compute to land.  Before barrier 1 of
 // chunk c+1 a producer waits until at most its own count of chunk c+2 copies
 // is outstanding: the counter completes in order, so chunk c+1 is complete.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
-}
-
 template <int D, int C, int BV, typename OT, typename IT>
 struct InterDmaSmem {
     typedef Rec<D, C, OT> R;
@@ -1846,6 +2326,42 @@ bool prefill_supported(int D, int C, bool bf16) {
     return false;
 }
 
+template <int D, int C, typename OT>
+constexpr bool seg_fits_t() {
+    return sizeof(SegSmem<D, C, OT, InputOf<OT>, true>) <= kLdsLimit &&
+           sizeof(SegSmem<D, C, OT, InputOf<OT>, false>) <= kLdsLimit;
+}
+static bool seg_fits(int D, int C, bool bf16) {
+#define KDA_SFITS(DD, CC)                                                              \
+    if (D == DD && C == CC) return bf16 ? seg_fits_t<DD, CC, _Float16>() : seg_fits_t<DD, CC, float>();
+    KDA_SFITS(32, 16) KDA_SFITS(32, 32) KDA_SFITS(32, 64)
+    KDA_SFITS(64, 16) KDA_SFITS(64, 32) KDA_SFITS(64, 64)
+    KDA_SFITS(128, 16) KDA_SFITS(128, 32) KDA_SFITS(128, 64)
+#undef KDA_SFITS
+    return false;
+}
+
+// Segments per sequence for the segment-parallel chain (fixed-length batches):
+// enough that sequences x heads x segments covers the 256 CUs of an MI355X
+// with one workgroup each, with at least kSegMinChunks chunks per segment.
+// nseg = 1: the per-slice chain kernels run instead.
+constexpr int kSegCUs = 256, kSegMinChunks = 4;
+// Returns the segment count the state planes are reserved for: the count
+// asked for before rounding the segment length, which never falls as nch
+// grows (the count used, nseg, can: 32 chunks make 8 segments of 4, 33 make
+// 7 of 5), so the workspace size stays monotone in T.
+static int seg_split(long long chains, int nch, bool ok, int* nseg, int* seg_len) {
+    *nseg = 1;
+    *seg_len = nch;
+    if (!ok || chains < 1 || nch < 1) return 1;
+    const long long ns = std::min<long long>(kSegCUs / chains, nch / kSegMinChunks);
+    if (ns < 2) return 1;
+    const int l = (int)((nch + ns - 1) / ns);
+    *seg_len = l;
+    *nseg = (nch + l - 1) / l;
+    return (int)ns;
+}
+
 bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf16,
                   PrefillPlan* plan) {
     if (B < 1 || T < 0 || H < 1 || N < 1) return false;
@@ -1863,7 +2379,15 @@ bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf
         off += ((size_t)nchunk * sizeof(ChunkInfo) + 255) / 256 * 256;
     }
     plan->off_records = off;
-    off += (size_t)nchunk * H * plan->chunk_rec_bytes;
+    off += ((size_t)nchunk * H * plan->chunk_rec_bytes + 255) / 256 * 256;
+    plan->nseg = 1;
+    plan->seg_len = 0;
+    int reserve = 1;
+    if (!varlen)
+        reserve = seg_split((long long)N * H, (T + C - 1) / C, seg_fits(D, C, bf16), &plan->nseg,
+                            &plan->seg_len);
+    plan->off_seg = off;
+    if (reserve > 1) off += (size_t)seg_planes(reserve) * N * H * D * D * sizeof(float);
     plan->total = off;
     return true;
 }
@@ -1875,6 +2399,13 @@ bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf
 // KDA_INTER_VARIANT = dma16 / dma32 / reg16 / reg32 / reg64 overrides the
 // choice (benchmarking).
 enum class InterVariant { Dma16, Dma32, Reg16, Reg32, Reg64 };
+// True when KDA_INTER_VARIANT names one of the per-slice chain kernels (the
+// segment-parallel chain is then not used).
+static bool inter_override() {
+    const char* e = getenv("KDA_INTER_VARIANT");
+    return e && (!strcmp(e, "dma16") || !strcmp(e, "dma32") || !strcmp(e, "reg16") ||
+                 !strcmp(e, "reg32") || !strcmp(e, "reg64"));
+}
 static InterVariant choose_inter(int D, long long chains, bool bf16, bool dma16_ok,
                                  bool dma32_ok) {
     if (const char* e = getenv("KDA_INTER_VARIANT")) {
@@ -1956,6 +2487,42 @@ static hipError_t launch_records(const PrefillArgs& a, const PrefillPlan& plan, 
     return hipSuccess;
 }
 
+int prefill_chain_segments(const PrefillPlan& plan) {
+    return plan.nseg > 1 && !inter_override() ? plan.nseg : 1;
+}
+
+// Passes 1-3 of the segment-parallel chain (plan.nseg > 1).
+template <int D, int C, typename OT, typename IT>
+static hipError_t launch_segmented(const PrefillArgs& a, const PrefillPlan& plan, int nch_seq) {
+    const int nseg = plan.nseg, L = plan.seg_len;
+    const long long NH = (long long)a.N * a.H;
+    float* seg = reinterpret_cast<float*>((char*)a.workspace + plan.off_seg);
+    const char* rec = (const char*)a.workspace + plan.off_records;
+    const int smem1 = (int)sizeof(SegSmem<D, C, OT, IT, false>);
+    const int smem3 = (int)sizeof(SegSmem<D, C, OT, IT, true>);
+    auto k1 = kda_seg_chain<D, C, OT, IT, false>;
+    auto k3 = kda_seg_chain<D, C, OT, IT, true>;
+    hipError_t e = hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, smem1);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)k3, hipFuncAttributeMaxDynamicSharedMemorySize, smem3);
+    if (e != hipSuccess) return e;
+    // pass 1: one workgroup per (sequence, head, segment < nseg - 1)
+    hipLaunchKernelGGL(k1, dim3((unsigned)(NH * (nseg - 1))), dim3(64 * SegShape<D, false>::NW),
+                       smem1, a.stream, a.T, a.H, a.N, nch_seq, L, nseg, a.scale, (const IT*)a.v,
+                       a.s0, rec, (float*)nullptr, (float*)nullptr, seg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)kda_seg_combine<D>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)seg_combine_smem<D>());
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_seg_combine<D>, dim3((unsigned)NH, D / 16), dim3(256),
+                       seg_combine_smem<D>(), a.stream, (int)NH, nseg, a.s0, seg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k3, dim3((unsigned)(NH * nseg)), dim3(64 * SegShape<D, true>::NW), smem3,
+                       a.stream, a.T, a.H, a.N, nch_seq, L, nseg, a.scale, (const IT*)a.v, a.s0,
+                       rec, a.o, a.sT, seg);
+    return hipGetLastError();
+}
+
 template <int D, int C, typename OT, typename IT>
 static hipError_t launch_dc(const PrefillArgs& a, const PrefillPlan& plan) {
     if constexpr (!fits<D, C, OT>()) {
@@ -1967,6 +2534,10 @@ static hipError_t launch_dc(const PrefillArgs& a, const PrefillPlan& plan) {
         ChunkInfo* table;
         if (hipError_t e = launch_records<D, C, OT, IT>(a, plan, nch_seq, &chunk_off, &table))
             return e;
+        if constexpr (seg_fits_t<D, C, OT>()) {
+            if (plan.nseg > 1 && !inter_override())
+                return launch_segmented<D, C, OT, IT>(a, plan, nch_seq);
+        }
         constexpr bool kBf = sizeof(OT) == 2;
         constexpr bool kDma16 = kBf && inter_dma_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
         constexpr bool kDma32 = kBf && D >= 32 && inter_dma_smem_bytes<D, C, 32, OT, IT>() <= kLdsLimit;
@@ -2031,6 +2602,8 @@ bool backward_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool b
                    BackwardPlan* plan) {
     (void)bf16;   // the backward keeps fp32 records for either input type
     if (!prefill_plan(B, T, H, D, C, N, varlen, false, &plan->f)) return false;
+    plan->f.nseg = 1;   // the backward runs its own chains: no segment states
+    plan->f.total = plan->f.off_seg;
     const size_t nch = (size_t)plan->f.nchunk_max;
     const size_t hist = (nch * H * (size_t)D * D * sizeof(float) + 255) / 256 * 256;
     plan->grec_floats = grad_rec_floats(D, C);

@@ -29,6 +29,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
     assert set(names) == {"kda_status_string", "kda_version", "kda_chunk_fwd_workspace_bytes",
+                          "kda_chunk_fwd_segments",
                           "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_decode_step",
                           "kda_decode_step_ex", "kda_chunk_bwd_workspace_bytes",
                           "kda_chunk_bwd", "kda_dplr_chunk_fwd_workspace_bytes",
@@ -50,7 +51,10 @@ def test_workspace_size(lib):
     # holds three C x d and two C x C fp16 tiles plus d fp32 decays, in whole KiB
     rec = (3 * 64 * 128 + 2 * 64 * 64) * 2 + 4 * 128
     rec = (rec + 1023) // 1024 * 1024
-    assert ws(1, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 512 * 32 * rec
+    # plus, with 32 (sequence, head) chains cut into 8 segments, 3 * 8 - 3 fp32
+    # d x d state planes per chain (end states, transition products, entering
+    # states)
+    assert ws(1, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 512 * 32 * rec + 21 * 32 * 128 * 128 * 4
     assert ws(1, 100, 2, 64, 64, 16, 0, kda.KDA_F32) > ws(1, 100, 2, 64, 64, 16, 0, kda.KDA_BF16)
     # packed sequences add a chunk table and one partial chunk per sequence
     assert ws(1, 1000, 2, 64, 64, 64, 5, kda.KDA_BF16) > ws(1, 1000, 2, 64, 64, 64, 0, kda.KDA_BF16)
@@ -59,6 +63,29 @@ def test_workspace_size(lib):
     assert ws(1, 100, 2, 64, 64, 48, 0, kda.KDA_BF16) == 0      # unsupported chunk
     assert ws(2, 100, 2, 64, 64, 64, 3, kda.KDA_BF16) == 0      # packed needs B == 1
     assert ws(1, 100, 2, 64, 64, 64, 0, 7) == 0                 # bad dtype
+
+
+def test_chain_segments(lib):
+    seg = lib.kda_chunk_fwd_segments
+    # 32 chains, 512 chunks: 8 segments of 64 chunks cover 256 CUs
+    assert seg(1, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 8
+    # at least 4 chunks per segment: 40 chunks allow 10, the CUs ask for 64
+    assert seg(1, 40 * 64, 4, 64, 64, 64, 0, kda.KDA_BF16) == 10
+    assert seg(2, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 4
+    assert seg(8, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 1     # 256 chains already
+    assert seg(1, 32768, 32, 128, 128, 64, 3, kda.KDA_BF16) == 1     # packed sequences
+    assert seg(1, 7 * 64, 32, 128, 128, 64, 0, kda.KDA_BF16) == 1    # too short to split
+    assert seg(1, 32768, 32, 128, 128, 64, 0, kda.KDA_F32) == 1      # fp32 d=128 C=64: LDS
+    assert seg(1, 32768, 32, 64, 64, 64, 0, kda.KDA_F32) == 1        # fp32 d=64 C=64: LDS
+    assert seg(1, 32768, 32, 64, 64, 32, 0, kda.KDA_F32) == 8
+    assert seg(1, 32768, 32, 96, 96, 64, 0, kda.KDA_BF16) == 0       # unsupported
+
+
+def test_workspace_monotone_in_T(lib):
+    ws = lib.kda_chunk_fwd_workspace_bytes
+    for B, H, d, c in ((1, 32, 128, 64), (1, 4, 64, 16), (3, 2, 32, 32)):
+        sizes = [ws(B, T, H, d, d, c, 0, kda.KDA_BF16) for T in range(0, 4000, 37)]
+        assert all(a <= b for a, b in zip(sizes, sizes[1:])), (B, H, d, c)
 
 
 def _fwd(lib, B=1, T=64, H=2, dk=64, dv=64, chunk=64, dtype=kda.KDA_BF16, ptr=4096, cu=None,

@@ -190,3 +190,68 @@ def test_concurrent_streams():
     torch.cuda.synchronize()
     for x, y in zip(ra + rb, ca + cb):
         assert torch.equal(x, y)
+
+
+# Shapes where the chain is cut into segments (B*H small, many chunks), each
+# with a ragged last chunk: (B, T, H, d, chunk, dtype).
+SEG_CASES = [
+    (2, 1000, 2, 64, 64, torch.bfloat16),
+    (1, 1100, 3, 128, 64, torch.bfloat16),
+    (1, 700, 2, 32, 16, torch.float32),
+    (2, 1050, 2, 64, 32, torch.float32),
+    (1, 1000, 4, 128, 16, torch.float32),
+]
+
+
+def _segments(B, T, H, D, chunk, dtype):
+    return kda.kda_chunk_fwd_segments(B, T, H, D, D, chunk, 0, dtype)
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: "B%dT%dH%dd%dC%d%s" % (
+    c[0], c[1], c[2], c[3], c[4], "bf16" if c[5] == torch.bfloat16 else "f32"))
+@pytest.mark.parametrize("s0", [None, 0.1])
+def test_segmented_chain(case, s0):
+    """Segment-parallel chain (local runs, transition products, combine, rerun)
+    against the oracle, element by element."""
+    B, T, H, D, chunk, dtype = case
+    assert _segments(*case) > 2, case
+    d = make_prefill(B * 7 + T + D + chunk, B, T, H, D, dtype, s0_std=s0)
+    check(d, chunk)
+
+
+def test_two_segments():
+    """Two segments: the second starts from the first's end state, no
+    transition product is formed."""
+    B, T, H, D = 1, 8 * 64, 32, 128
+    assert kda.kda_chunk_fwd_segments(B, T, H, D, D, 64) == 2
+    d = make_prefill(81, B, T, H, D, torch.bfloat16, s0_std=0.1)
+    check(d, 64)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_segmented_equals_slice_chain(dtype, monkeypatch):
+    """The segment-parallel chain and the per-slice chain agree to rounding."""
+    B, T, H, D, chunk = 1, 2000, 2, 64, 32
+    assert kda.kda_chunk_fwd_segments(B, T, H, D, D, chunk, 0, dtype) > 1
+    d = make_prefill(82, B, T, H, D, dtype, s0_std=0.1)
+    o1, S1 = run(d, chunk)
+    monkeypatch.setenv("KDA_INTER_VARIANT", "reg16")
+    assert kda.kda_chunk_fwd_segments(B, T, H, D, D, chunk, 0, dtype) == 1
+    o2, S2 = run(d, chunk)
+    tol = TOL[dtype]
+    assert rel_err(o1.cpu().numpy(), o2.double().cpu().numpy()) < tol
+    assert rel_err(S1.cpu().numpy(), S2.double().cpu().numpy()) < tol
+
+
+def test_segmented_in_place_state():
+    """final_state aliasing initial_state: the first segment reads its copy of
+    S0, so the last segment's write cannot race with it."""
+    B, T, H, D = 1, 4096, 8, 128
+    assert kda.kda_chunk_fwd_segments(B, T, H, D, D, 64) > 1
+    d = make_prefill(83, B, T, H, D, torch.bfloat16, s0_std=0.1)
+    o1, S1 = run(d, 64)
+    st = d["S0"].clone()
+    o2, _ = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64,
+                              initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, st)
