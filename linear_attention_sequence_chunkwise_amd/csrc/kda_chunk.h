@@ -124,6 +124,36 @@ __device__ __forceinline__ typename MM<OT>::frag load_swz(const OT* tile, int ro
     return MM<OT>::load(tile + swz<OT, LD>(row, k) - k, 0, 0, k);
 }
 
+// Order of the contraction index in KDA's fp16 chunk records and chain
+// operands.  Within every 32 entries, logical k = 16 h + 4 q + e (h = 0..1,
+// q = 0..3, e = 0..3) is stored at 8 q + 4 h + e.  A 16x16x32 fp16 instruction
+// whose lanes supply k = 4 (l/16) + 0..3 of two 16-row tiles (the order in
+// which matrix-core output tiles serve as B operands) then reads each A
+// fragment as one 16-byte group.  Products whose operands both use the order
+// (a whole 16-byte group per lane on each side) are unaffected by it.  fp32
+// operands keep the natural order.
+template <typename OT>
+__host__ __device__ constexpr int kperm(int k) {
+    if constexpr (sizeof(OT) == 2) {
+        const int l = k & 31;
+        return (k & ~31) + 8 * ((l & 15) >> 2) + 4 * (l >> 4) + (l & 3);
+    } else {
+        return k;
+    }
+}
+template <typename OT>
+__host__ __device__ constexpr int kperm_inv(int t) {
+    if constexpr (sizeof(OT) == 2) {
+        const int l = t & 31;
+        return (t & ~31) + 16 * ((l & 7) >> 2) + 4 * (l >> 3) + (l & 3);
+    } else {
+        return t;
+    }
+}
+static_assert(kperm<_Float16>(kperm_inv<_Float16>(21)) == 21 && kperm<_Float16>(19) == 7 &&
+                  kperm<_Float16>(4) == 8 && kperm<_Float16>(36) == 40,
+              "contraction order");
+
 struct ChunkInfo {
     int tok0;   // first token (index into the flattened [B*T] token axis)
     int len;    // valid rows, 1..C
@@ -201,8 +231,9 @@ __device__ __forceinline__ ChainPos chain_pos(int T, int H, int N_seq, int nch_s
 }
 
 // State tiles owned by this wave (fp32, MFMA output layout) from s0 or zero,
-// and the fp16/fp32 state operand in LDS.
-template <int D, int C, int BV, typename OT, int NWC = 4>
+// and the fp16/fp32 state operand in LDS (contraction index in the kperm order
+// when PERM).
+template <int D, int C, int BV, typename OT, int NWC = 4, bool PERM = false>
 __device__ __forceinline__ void chain_load_state(float4v (&st)[((D / 16) * (BV / 16) + NWC - 1) / NWC],
                                                  ChainScratch<D, C, BV, OT>& cs,
                                                  const float* __restrict__ s0, size_t sbase,
@@ -215,7 +246,7 @@ __device__ __forceinline__ void chain_load_state(float4v (&st)[((D / 16) * (BV /
     if constexpr (CK > C) {   // k-padding of X and U stays zero for the whole chain
         for (int idx = threadIdx.x; idx < 2 * BV * (CK - C); idx += 64 * NWC) {
             const int row = idx / (CK - C), col = C + idx % (CK - C);
-            (row < BV ? cs.x : cs.u)[(row % BV) * LDC + col] = to_ot<OT>(0.f);
+            (row < BV ? cs.x : cs.u)[(row % BV) * LDC + (PERM ? kperm<OT>(col) : col)] = to_ot<OT>(0.f);
         }
     }
 #pragma unroll
@@ -235,8 +266,10 @@ __device__ __forceinline__ void chain_load_state(float4v (&st)[((D / 16) * (BV /
         if (s < ST) {
             const int ct = s / VT, vt = s % VT;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                cs.s[(16 * vt + l16) * LDK + 16 * ct + 4 * lq + j] = to_ot<OT>(st[i][j]);
+            for (int j = 0; j < 4; ++j) {
+                const int k = 16 * ct + 4 * lq + j;
+                cs.s[(16 * vt + l16) * LDK + (PERM ? kperm<OT>(k) : k)] = to_ot<OT>(st[i][j]);
+            }
         }
     }
 }

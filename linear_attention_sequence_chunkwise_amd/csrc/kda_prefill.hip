@@ -83,6 +83,14 @@ struct Rec {
 };
 
 
+// Logical column of element e of the stored 16-byte group at column c0 (a
+// multiple of the group size) in the kperm order: fp16 groups hold two runs of
+// four consecutive logical columns, 16 apart; fp32 groups one run of four.
+template <typename OT>
+__device__ __forceinline__ int group_col(int c0, int e) {
+    return sizeof(OT) == 2 ? kperm_inv<OT>(c0) + (e & 3) + 16 * (e >> 2) : c0 + e;
+}
+
 static size_t rec_bytes(int D, int C, bool bf16) {
     const size_t es = bf16 ? 2 : 4;
     const size_t ks = bf16 ? 32 : 4;
@@ -352,23 +360,34 @@ __global__ __launch_bounds__(256) void kda_intra(
 
     // ---- phase 3a: record tiles KG, KPt from the LDS operands ----
     // KG_r = (k_r a_r) exp(Gs_I) : rows of 16 bytes
+    // (record columns in the kperm order: stored column c0 + e holds channel
+    // kperm_inv(c0 + e))
     for (int idx = tid; idx < C * D / EPV; idx += 256) {
         const int r = idx / (D / EPV), c0 = (idx % (D / EPV)) * EPV;
-        const float* eg = &sm.egs[(r >> 4) * D + c0];
         float kk[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) kk[e] = (float)sm.u.g.kl[r * LDK + c0 + e] * eg[e];
+        for (int e = 0; e < EPV; ++e) {
+            const int c = group_col<OT>(c0, e);
+            kk[e] = (float)sm.u.g.kl[r * LDK + c] * sm.egs[(r >> 4) * D + c];
+        }
         *reinterpret_cast<vec*>(rec + R::KG + swz<OT, D>(r, c0)) = pack16(kk);
     }
-    // KPt[c][i] = (k_i b_i) exp(G_n - Ge_J), transposed: 16 bytes of one channel row
-    for (int idx = tid; idx < D * C / EPV; idx += 256) {
-        const int c = idx / (C / EPV), i0 = (idx % (C / EPV)) * EPV;
+    // KPt[c][i] = (k_i b_i) exp(G_n - Ge_J), transposed: 16 bytes of one channel
+    // row; token columns in the kperm order, zero past C (k-padding)
+    for (int idx = tid; idx < D * R::CK / EPV; idx += 256) {
+        const int c = idx / (R::CK / EPV), i0 = (idx % (R::CK / EPV)) * EPV;
+        // the group's runs of four tokens lie in sub-blocks J and (fp16) J + 1
+        const int J = group_col<OT>(i0, 0) >> 4;
         float tail = 0.f;   // G_n - Ge_J: the gate sums of the later sub-blocks
-        for (int m = (i0 >> 4) + 1; m < NB; ++m) tail += sm.sig[m * D + c];
-        const float f = exp_e(tail);
+        for (int m = J + 1; m < NB; ++m) tail += sm.sig[m * D + c];
+        const float f0 = exp_e(tail);
+        const float f1 = J + 1 < NB ? exp_e(tail - sm.sig[(J + 1) * D + c]) : 0.f;
         float kk[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) kk[e] = (float)sm.u.g.kr[(i0 + e) * LDK + c] * f;
+        for (int e = 0; e < EPV; ++e) {
+            const int i = group_col<OT>(i0, e);
+            kk[e] = i < C ? (float)sm.u.g.kr[i * LDK + c] * (e < 4 ? f0 : f1) : 0.f;
+        }
         *reinterpret_cast<vec*>(rec + R::KPt + swz<OT, R::CK>(c, i0)) = pack16(kk);
     }
 
@@ -430,10 +449,12 @@ __global__ __launch_bounds__(256) void kda_intra(
     // QG_r = (q_r a_r) exp(Gs_I) : rows of 16 bytes
     for (int idx = tid; idx < C * D / EPV; idx += 256) {
         const int r = idx / (D / EPV), c0 = (idx % (D / EPV)) * EPV;
-        const float* eg = &sm.egs[(r >> 4) * D + c0];
         float qq[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) qq[e] = (float)sm.u.g.kl[r * LDK + c0 + e] * eg[e];
+        for (int e = 0; e < EPV; ++e) {
+            const int c = group_col<OT>(c0, e);
+            qq[e] = (float)sm.u.g.kl[r * LDK + c] * sm.egs[(r >> 4) * D + c];
+        }
         *reinterpret_cast<vec*>(rec + R::QG + swz<OT, D>(r, c0)) = pack16(qq);
     }
     float4v macc[TPW];
@@ -499,10 +520,16 @@ __global__ __launch_bounds__(256) void kda_intra(
 
     // ---- phase 4b: store M; off-diagonal blocks of T level by level:
     //      T_IJ = -T_II * sum_{m=J}^{I-1} A_Im T_mJ ----
-    for (int idx = tid; idx < C * C / EPV; idx += 256) {
-        const int r = idx / (C / EPV), c0 = (idx % (C / EPV)) * EPV;
-        *reinterpret_cast<vec*>(rec + R::M + swz<OT, R::CK>(r, c0)) =
-            *reinterpret_cast<const vec*>(&sm.u.s.M[r * LDA + c0]);
+    // (token columns in the kperm order, zero past C)
+    for (int idx = tid; idx < C * R::CK / EPV; idx += 256) {
+        const int r = idx / (R::CK / EPV), c0 = (idx % (R::CK / EPV)) * EPV;
+        float mv[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const int col = group_col<OT>(c0, e);
+            mv[e] = col < C ? (float)sm.u.s.M[r * LDA + col] : 0.f;
+        }
+        *reinterpret_cast<vec*>(rec + R::M + swz<OT, R::CK>(r, c0)) = pack16(mv);
     }
     for (int d = 1; d < NB; ++d) {
         if (wave < NB - d) {
@@ -534,22 +561,16 @@ __global__ __launch_bounds__(256) void kda_intra(
                 *reinterpret_cast<const float4*>(&sm.u.s.T[r * LDT + c0]);
         }
     }
-    for (int idx = tid; idx < C * C / EPV; idx += 256) {
-        const int r = idx / (C / EPV), c0 = (idx % (C / EPV)) * EPV;
+    // (token columns in the kperm order, zero past C)
+    for (int idx = tid; idx < C * R::CK / EPV; idx += 256) {
+        const int r = idx / (R::CK / EPV), c0 = (idx % (R::CK / EPV)) * EPV;
         float tv[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) tv[e] = sm.u.s.T[r * LDT + c0 + e] * sm.beta[c0 + e];
-        *reinterpret_cast<vec*>(rec + R::Tb + swz<OT, R::CK>(r, c0)) = pack16(tv);
-    }
-    if constexpr (R::CK > C) {   // zero k-padding of the chunk-indexed tiles
-        constexpr int PV = (R::CK - C) / EPV;
-        for (int idx = tid; idx < (D + 2 * C) * PV; idx += 256) {
-            const int row = idx / PV, c0 = C + (idx % PV) * EPV;
-            const size_t off = row < D ? R::KPt + swz<OT, R::CK>(row, c0)
-                             : row < D + C ? R::Tb + swz<OT, R::CK>(row - D, c0)
-                                           : R::M + swz<OT, R::CK>(row - D - C, c0);
-            *reinterpret_cast<vec*>(rec + off) = vec{0u, 0u, 0u, 0u};
+        for (int e = 0; e < EPV; ++e) {
+            const int col = group_col<OT>(c0, e);
+            tv[e] = col < C ? sm.u.s.T[r * LDT + col] * sm.beta[col] : 0.f;
         }
+        *reinterpret_cast<vec*>(rec + R::Tb + swz<OT, R::CK>(r, c0)) = pack16(tv);
     }
 }
 
@@ -637,7 +658,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * rt + 4 * lq + j;
                 const float vv = r < len ? to_f32(t.v[r * BV + 16 * vt + l16]) : 0.f;
-                cs.x[(16 * vt + l16) * LDC + r] = to_ot<OT>(vv - xk[j]);
+                cs.x[(16 * vt + l16) * LDC + kperm<OT>(r)] = to_ot<OT>(vv - xk[j]);
                 if (xh) xh[(size_t)r * D + v0 + 16 * vt + l16] = vv - xk[j];
             }
         }
@@ -659,7 +680,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                cs.u[(16 * vt + l16) * LDC + 16 * rt + 4 * lq + j] = to_ot<OT>(uacc[j]);
+                cs.u[(16 * vt + l16) * LDC + kperm<OT>(16 * rt + 4 * lq + j)] = to_ot<OT>(uacc[j]);
                 if (uh) uh[(size_t)(16 * rt + 4 * lq + j) * D + v0 + 16 * vt + l16] = uacc[j];
             }
         }
@@ -712,7 +733,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
             const int ct = s / VT, vt = s % VT;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                cs.s[(16 * vt + l16) * LDK + 16 * ct + 4 * lq + j] = to_ot<OT>(st[i][j]);
+                cs.s[(16 * vt + l16) * LDK + kperm<OT>(16 * ct + 4 * lq + j)] = to_ot<OT>(st[i][j]);
         }
     }
 }
@@ -750,7 +771,7 @@ __global__ __launch_bounds__(256) void kda_inter(
     const int tid = threadIdx.x;
     const size_t sbase = ((size_t)cp.n * H + cp.h) * (size_t)D * D;
     float4v st[SPW];
-    chain_load_state<D, C, BV, OT>(st, sm.cs, s0, sbase, cp.v0);
+    chain_load_state<D, C, BV, OT, 4, true>(st, sm.cs, s0, sbase, cp.v0);
     const ChunkTiles<D, C, OT, IT> tiles(sm.img, sm.vraw);
 
     vec rb[RPT], vb[VPT];
@@ -811,7 +832,7 @@ __global__ __launch_bounds__(256) void kda_state_chain(
     const int tid = threadIdx.x;
     const size_t sbase = ((size_t)cp.n * H + cp.h) * (size_t)D * D;
     float4v st[SPW];
-    chain_load_state<D, C, BV, OT>(st, sm.cs, s0, sbase, cp.v0);
+    chain_load_state<D, C, BV, OT, 4, true>(st, sm.cs, s0, sbase, cp.v0);
     const ChunkTiles<D, C, OT, IT> tiles(sm.img, sm.vraw);
     auto unit = [](int j) {
         return j < A_END ? j : j < A_END + (B_END - B_BEG) ? B_BEG + (j - A_END)
@@ -942,9 +963,9 @@ __device__ __forceinline__ void tile_chain_mma_nb(float4v (&acc)[NB], const OT* 
 #pragma unroll
         for (int p = 0; p < BOps<OT, NKT>::N; ++p) {
             if (2 * p < kend) {
-                const half4 x = *reinterpret_cast<const half4*>(A + swz<OT, LD>(row, 32 * p + 4 * lq));
-                const half4 y = *reinterpret_cast<const half4*>(A + swz<OT, LD>(row, 32 * p + 16 + 4 * lq));
-                const half8 af = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+                // k = 32p + 4 lq + 0..3 and 32p + 16 + 4 lq + 0..3: one 16-byte group
+                // in the records' kperm order
+                const half8 af = *reinterpret_cast<const half8*>(A + swz<OT, LD>(row, 32 * p + 8 * lq));
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
                     acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b[nb].f[p], acc[nb], 0, 0, 0);
@@ -1505,7 +1526,7 @@ __global__ __launch_bounds__(64 * (BV / 4 + NP)) void kda_inter_dma(
     }
 
     float4v st[SPW];
-    chain_load_state<D, C, BV, OT, NWC>(st, sm.cs, s0, sbase, cp.v0);
+    chain_load_state<D, C, BV, OT, NWC, true>(st, sm.cs, s0, sbase, cp.v0);
     // Compiler-visible vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at
     // their maxima): the initial-state loads are complete, so the compiler's
     // wait-count bookkeeping carries nothing pending into the loop.
