@@ -1182,9 +1182,21 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
     extern __shared__ __align__(1024) char smem_raw[];
     SegSmem<D, C, OT, IT, OUT>& sm = *reinterpret_cast<SegSmem<D, C, OT, IT, OUT>*>(smem_raw);
 
+    // pass 3: workgroup (sequence-head, segment) in order.  Pass 1: dispatch
+    // is round-robin over the 8 XCDs, and every segment of sequence-head nh
+    // runs on XCD nh % 8, where the combine's workgroups of nh run next and
+    // find the segment states in that XCD's L2.
     const int lg = blockIdx.x;
     const int nsp = OUT ? nseg : nseg - 1;   // segments this pass runs
-    const int s = lg % nsp, nh = lg / nsp;
+    int s, nh;
+    if constexpr (OUT) {
+        s = lg % nsp;
+        nh = lg / nsp;
+    } else {
+        const int j = lg >> 3;
+        s = j % nsp;
+        nh = 8 * (j / nsp) + (lg & 7);
+    }
     if (nh >= N_seq * H) return;
     const int n = nh / H, h = nh % H;
     const int c0 = s * L, c1 = min(c0 + L, nch_seq);
@@ -1328,7 +1340,9 @@ __global__ __launch_bounds__(256) void kda_seg_combine(int NH, int nseg,
         asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
         lds_barrier();
         if (s + 2 < nseg) copy(s + 1, bi ^ 1);
-        // out tile (rows 16 rt..) = E + P cur on fp32 matrix cores, k in steps of 4
+        // out tile (rows 16 rt..) = E + P cur on fp32 matrix cores, k in steps of
+        // 4, over KS interleaved partial sums per tile (independent chains)
+        constexpr int KS = 4;
         float4v acc[TPW];
         const bool live = wave * TPW < RT;
 #pragma unroll
@@ -1337,16 +1351,23 @@ __global__ __launch_bounds__(256) void kda_seg_combine(int NH, int nseg,
             for (int j = 0; j < 4; ++j)
                 acc[t][j] = live ? sm.e[bi][(16 * (wave * TPW + t) + 4 * lq + j) * 16 + l16] : 0.f;
         if (live) {
-#pragma unroll 8
+            float4v part[TPW][KS];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int q = 0; q < KS; ++q) part[t][q] = q ? float4v{0.f, 0.f, 0.f, 0.f} : acc[t];
+#pragma unroll
             for (int kt = 0; kt < D / 4; ++kt) {
                 const float b = sm.cur[4 * kt + lq][l16];
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     const int r = 16 * (wave * TPW + t) + l16;
                     const float a = sm.p[bi][r * D + 4 * (kt ^ (r % NG)) + lq];
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[t], 0, 0, 0);
+                    part[t][kt % KS] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, part[t][kt % KS], 0, 0, 0);
                 }
             }
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) acc[t] = (part[t][0] + part[t][1]) + (part[t][2] + part[t][3]);
         }
         lds_barrier();   // every wave's reads of cur are done
         if (live) {
@@ -2527,8 +2548,9 @@ static hipError_t launch_segmented(const PrefillArgs& a, const PrefillPlan& plan
     if (e == hipSuccess)
         e = hipFuncSetAttribute((const void*)k3, hipFuncAttributeMaxDynamicSharedMemorySize, smem3);
     if (e != hipSuccess) return e;
-    // pass 1: one workgroup per (sequence, head, segment < nseg - 1)
-    hipLaunchKernelGGL(k1, dim3((unsigned)(NH * (nseg - 1))), dim3(64 * SegShape<D, false>::NW),
+    // pass 1: one workgroup per (sequence, head, segment < nseg - 1), grouped
+    // by XCD (the sequence-head count rounded up to a multiple of 8)
+    hipLaunchKernelGGL(k1, dim3((unsigned)((NH + 7) / 8 * 8 * (nseg - 1))), dim3(64 * SegShape<D, false>::NW),
                        smem1, a.stream, a.T, a.H, a.N, nch_seq, L, nseg, a.scale, (const IT*)a.v,
                        a.s0, rec, (float*)nullptr, (float*)nullptr, seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
