@@ -1062,13 +1062,15 @@ struct ValueCopy {
 // b < NVB carry values, read from vl ([C][16 NVB] in LDS, rows < len count);
 // the others are runs of the identity (V = 0).  Once X is formed the value
 // region is refilled from vnext (the next chunk's rows, vlen of them; null:
-// nothing to fetch).  OUT: also O = scale (QG S + M U) into o for rows < len.
-template <int D, int C, typename OT, typename IT, bool OUT, int NB, int NVB>
+// nothing to fetch).  OUT: also O = scale (QG S + M U) into o for rows < len,
+// or, with EPI, into oo (this lane's tile entries) for the caller's epilogue.
+template <int D, int C, typename OT, typename IT, bool OUT, int NB, int NVB, bool EPI = false>
 __device__ __forceinline__ void wide_chunk(const WideTiles<D, C, OT, OUT>& t,
                                            float4v (&st)[NB][D / 16], const IT* vl,
                                            uint32_t vl_lds, const IT* vnext, size_t vstride,
                                            int vlen, int cbase, int tok0, int len, int H, int h,
-                                           float scale, float* __restrict__ o) {
+                                           float scale, float* __restrict__ o,
+                                           float4v (&oo)[NB][C / 16]) {
     constexpr int RT = C / 16, KT = D / 16;
     constexpr int CK = chunk_k<C, OT>();
     const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
@@ -1126,13 +1128,18 @@ __device__ __forceinline__ void wide_chunk(const WideTiles<D, C, OT, OUT>& t,
             tile_chain_mma_nb<OT, D, KT, NB>(acc, t.qg, rt, KT, sb);
             tile_chain_mma_nb<OT, CK, RT, NB>(acc, t.m, rt, rt + 1, ub);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int nb = 0; nb < NB; ++nb) {
+                if constexpr (EPI) {
+                    oo[nb][rt] = scale * acc[nb];
+                } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * rt + 4 * lq + j;
-                    if (r < len)
-                        o[((size_t)(tok0 + r) * H + h) * D + cbase + 16 * nb + l16] = scale * acc[nb][j];
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 16 * rt + 4 * lq + j;
+                        if (r < len)
+                            o[((size_t)(tok0 + r) * H + h) * D + cbase + 16 * nb + l16] = scale * acc[nb][j];
+                    }
                 }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -1168,13 +1175,21 @@ struct SegSmem {
     alignas(1024) char img[2][WideTiles<D, C, OT, OUT>::KIB * 1024];
     alignas(1024) char vals[SegShape<D, OUT>::NW]
                            [(ValueCopy<C, IT, SegShape<D, OUT>::NVB>::BYTES + 1023) / 1024 * 1024];
+    float part[OUT ? C : 1][SegShape<D, OUT>::NW];   // fused epilogue: per-wave row sums of o^2
 };
 
-template <int D, int C, typename OT, typename IT, bool OUT>
+// EPI (pass 3 only): the output epilogue (per-row RMS norm over dv, weight,
+// sigmoid gate) fused: a workgroup owns whole output rows, so each wave sums
+// the squares of its columns per row, the partial sums meet in LDS, and the
+// finished rows are written once.
+template <int D, int C, typename OT, typename IT, bool OUT, bool EPI = false>
 __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
     int T, int H, int N_seq, int nch_seq, int L, int nseg, float scale,
     const IT* __restrict__ v, const float* __restrict__ s0, const char* __restrict__ records,
-    float* __restrict__ o, float* __restrict__ sT, float* __restrict__ seg) {
+    float* __restrict__ o, float* __restrict__ sT, float* __restrict__ seg,
+    const IT* __restrict__ gate = nullptr, const float* __restrict__ weight = nullptr,
+    float eps = 0.f) {
+    static_assert(!EPI || OUT, "the epilogue belongs to the pass with outputs");
     typedef SegShape<D, OUT> SS;
     typedef WideTiles<D, C, OT, OUT> WT;
     typedef Rec<D, C, OT> R;
@@ -1231,6 +1246,9 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
         for (int j = wave; j < WT::KIB; j += SS::NW)
             dma16(rec + (size_t)WT::rec_kib(j) * 1024 + lane * 16, base + j * 1024);
     };
+    float wt[SS::NCB];   // fused epilogue: this lane's weight entries
+#pragma unroll
+    for (int b = 0; b < SS::NCB; ++b) wt[b] = (EPI && weight) ? weight[cbase + 16 * b + l16] : 1.f;
     // this wave's value columns of chunk c (row 0) in global memory
     auto vsrc = [&](int c) -> const IT* {
         return v + ((size_t)(n * T + c * C) * H + h) * D + cbase;
@@ -1253,11 +1271,70 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
         // buffer the copies of chunk c + 1 then refill
         asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
         lds_barrier();
+        // fused epilogue: this lane's gate entries of the chunk (rows clamped
+        // to the chunk; used after the products, so the loads have the chunk's
+        // compute to land).  Issued before the next chunk's copies: the memory
+        // counter retires in order, so waiting for the gate then does not wait
+        // for those copies.
+        uint32_t zr[EPI ? SS::NCB : 1][EPI ? RT : 1][4];
+        if constexpr (EPI) {
+            if (gate) {
+#pragma unroll
+                for (int b = 0; b < SS::NCB; ++b)
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int r = min(16 * rt + 4 * lq + j, len - 1);
+                            const IT* zp = gate + ((size_t)(tok0 + r) * H + h) * D + cbase + 16 * b + l16;
+                            if constexpr (sizeof(IT) == 2)
+                                zr[b][rt][j] = reinterpret_cast<const bf16_t*>(zp)->bits;
+                            else
+                                zr[b][rt][j] = __builtin_bit_cast(uint32_t, *reinterpret_cast<const float*>(zp));
+                        }
+            }
+        }
         if (c + 1 < c1) copy_record(c + 1, bi ^ 1);
+        float4v oo[SS::NCB][RT];
         const WT tiles(sm.img[bi]);
-        wide_chunk<D, C, OT, IT, OUT, SS::NCB, SS::NVB>(
+        wide_chunk<D, C, OT, IT, OUT, SS::NCB, SS::NVB, EPI>(
             tiles, st, vl, vl_lds, c + 1 < c1 ? vsrc(c + 1) : nullptr, vstride,
-            min(C, T - (c + 1) * C), cbase, tok0, len, H, h, scale, o);
+            min(C, T - (c + 1) * C), cbase, tok0, len, H, h, scale, o, oo);
+        if constexpr (EPI) {
+            // y = o / sqrt(mean over dv of o^2 + eps) * weight * sigmoid(gate)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int b = 0; b < SS::NCB; ++b) ss += oo[b][rt][j] * oo[b][rt][j];
+                    ss = group_sum<16>(ss);
+                    if (l16 == 0) sm.part[16 * rt + 4 * lq + j][wave] = ss;
+                }
+            lds_barrier();
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j;
+                    float tot = 0.f;
+#pragma unroll
+                    for (int w = 0; w < SS::NW; ++w) tot += sm.part[r][w];
+                    const float rs = rnorm(tot * (1.f / D) + eps);
+#pragma unroll
+                    for (int b = 0; b < SS::NCB; ++b) {
+                        const int col = cbase + 16 * b + l16;
+                        float y = oo[b][rt][j] * rs * wt[b];
+                        if (gate) {
+                            const float z = sizeof(IT) == 2 ? __builtin_bit_cast(float, zr[b][rt][j] << 16)
+                                                            : __builtin_bit_cast(float, zr[b][rt][j]);
+                            y *= sigmoid_f(z);
+                        }
+                        if (r < len) o[((size_t)(tok0 + r) * H + h) * D + col] = y;
+                    }
+                }
+        }
     }
 #pragma unroll
     for (int b = 0; b < SS::NCB; ++b) {
@@ -2533,7 +2610,8 @@ int prefill_chain_segments(const PrefillPlan& plan) {
     return plan.nseg > 1 && !inter_override() ? plan.nseg : 1;
 }
 
-// Passes 1-3 of the segment-parallel chain (plan.nseg > 1).
+// Passes 1-3 of the segment-parallel chain (plan.nseg > 1), with the output
+// epilogue, when asked for, fused into pass 3.
 template <int D, int C, typename OT, typename IT>
 static hipError_t launch_segmented(const PrefillArgs& a, const PrefillPlan& plan, int nch_seq) {
     const int nseg = plan.nseg, L = plan.seg_len;
@@ -2543,7 +2621,8 @@ static hipError_t launch_segmented(const PrefillArgs& a, const PrefillPlan& plan
     const int smem1 = (int)sizeof(SegSmem<D, C, OT, IT, false>);
     const int smem3 = (int)sizeof(SegSmem<D, C, OT, IT, true>);
     auto k1 = kda_seg_chain<D, C, OT, IT, false>;
-    auto k3 = kda_seg_chain<D, C, OT, IT, true>;
+    // pass 3 with the output epilogue fused when one is asked for
+    auto k3 = a.epi.on ? kda_seg_chain<D, C, OT, IT, true, true> : kda_seg_chain<D, C, OT, IT, true>;
     hipError_t e = hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, smem1);
     if (e == hipSuccess)
         e = hipFuncSetAttribute((const void*)k3, hipFuncAttributeMaxDynamicSharedMemorySize, smem3);
@@ -2552,7 +2631,8 @@ static hipError_t launch_segmented(const PrefillArgs& a, const PrefillPlan& plan
     // by XCD (the sequence-head count rounded up to a multiple of 8)
     hipLaunchKernelGGL(k1, dim3((unsigned)((NH + 7) / 8 * 8 * (nseg - 1))), dim3(64 * SegShape<D, false>::NW),
                        smem1, a.stream, a.T, a.H, a.N, nch_seq, L, nseg, a.scale, (const IT*)a.v,
-                       a.s0, rec, (float*)nullptr, (float*)nullptr, seg);
+                       a.s0, rec, (float*)nullptr, (float*)nullptr, seg, (const IT*)nullptr,
+                       (const float*)nullptr, 0.f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = hipFuncSetAttribute((const void*)kda_seg_combine<D>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)seg_combine_smem<D>());
@@ -2562,8 +2642,35 @@ static hipError_t launch_segmented(const PrefillArgs& a, const PrefillPlan& plan
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k3, dim3((unsigned)(NH * nseg)), dim3(64 * SegShape<D, true>::NW), smem3,
                        a.stream, a.T, a.H, a.N, nch_seq, L, nseg, a.scale, (const IT*)a.v, a.s0,
-                       rec, a.o, a.sT, seg);
+                       rec, a.o, a.sT, seg, (const IT*)a.epi.gate, a.epi.weight, a.epi.eps);
     return hipGetLastError();
+}
+
+// The per-slice chain kernels (segment count 1, packed sequences, or shapes
+// whose segment kernels do not fit LDS).
+template <int D, int C, typename OT, typename IT>
+static hipError_t launch_slices(const PrefillArgs& a, const PrefillPlan& plan, int nch_seq,
+                                const int* chunk_off) {
+    constexpr bool kBf = sizeof(OT) == 2;
+    constexpr bool kDma16 = kBf && inter_dma_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
+    constexpr bool kDma32 = kBf && D >= 32 && inter_dma_smem_bytes<D, C, 32, OT, IT>() <= kLdsLimit;
+    switch (choose_inter(D, (long long)a.N * a.H, kBf, kDma16, kDma32)) {
+        case InterVariant::Dma16:
+            if constexpr (kDma16) return launch_inter<D, C, 16, OT, IT, 1>(a, plan, nch_seq, chunk_off);
+            break;
+        case InterVariant::Dma32:
+            if constexpr (kDma32) return launch_inter<D, C, 32, OT, IT, 1>(a, plan, nch_seq, chunk_off);
+            break;
+        case InterVariant::Reg64:
+            if constexpr (kBf && D >= 64) return launch_inter<D, C, 64, OT, IT, 0>(a, plan, nch_seq, chunk_off);
+            break;
+        case InterVariant::Reg32:
+            if constexpr (kBf && D >= 32) return launch_inter<D, C, 32, OT, IT, 0>(a, plan, nch_seq, chunk_off);
+            break;
+        default:
+            break;
+    }
+    return launch_inter<D, C, 16, OT, IT, 0>(a, plan, nch_seq, chunk_off);
 }
 
 template <int D, int C, typename OT, typename IT>
@@ -2581,26 +2688,8 @@ static hipError_t launch_dc(const PrefillArgs& a, const PrefillPlan& plan) {
             if (plan.nseg > 1 && !inter_override())
                 return launch_segmented<D, C, OT, IT>(a, plan, nch_seq);
         }
-        constexpr bool kBf = sizeof(OT) == 2;
-        constexpr bool kDma16 = kBf && inter_dma_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
-        constexpr bool kDma32 = kBf && D >= 32 && inter_dma_smem_bytes<D, C, 32, OT, IT>() <= kLdsLimit;
-        switch (choose_inter(D, (long long)a.N * a.H, kBf, kDma16, kDma32)) {
-            case InterVariant::Dma16:
-                if constexpr (kDma16) return launch_inter<D, C, 16, OT, IT, 1>(a, plan, nch_seq, chunk_off);
-                break;
-            case InterVariant::Dma32:
-                if constexpr (kDma32) return launch_inter<D, C, 32, OT, IT, 1>(a, plan, nch_seq, chunk_off);
-                break;
-            case InterVariant::Reg64:
-                if constexpr (kBf && D >= 64) return launch_inter<D, C, 64, OT, IT, 0>(a, plan, nch_seq, chunk_off);
-                break;
-            case InterVariant::Reg32:
-                if constexpr (kBf && D >= 32) return launch_inter<D, C, 32, OT, IT, 0>(a, plan, nch_seq, chunk_off);
-                break;
-            default:
-                break;
-        }
-        return launch_inter<D, C, 16, OT, IT, 0>(a, plan, nch_seq, chunk_off);
+        if (hipError_t e = launch_slices<D, C, OT, IT>(a, plan, nch_seq, chunk_off)) return e;
+        return a.epi.on ? launch_epilogue<D, IT>(a) : hipSuccess;
     }
 }
 
@@ -2613,8 +2702,7 @@ static hipError_t launch_d(const PrefillArgs& a, const PrefillPlan& plan) {
         case 64: e = launch_dc<D, 64, OT, IT>(a, plan); break;
         default: return hipErrorInvalidValue;
     }
-    if (e != hipSuccess || !a.epi.on) return e;
-    return launch_epilogue<D, IT>(a);
+    return e;
 }
 
 // ---- backward host side ----

@@ -132,3 +132,33 @@ def test_decode_epilogue(dtype, D, with_prep):
     assert rel_err(o.cpu().numpy()[valid], ro[valid]) < 1e-5
     assert np.all(o.cpu().numpy()[4] == 7.0)
     assert rel_err(state.cpu().numpy(), ref_state) < 1e-5
+
+
+@pytest.mark.parametrize("dtype,D,chunk", [(torch.bfloat16, 128, 64), (torch.float32, 64, 32),
+                                           (torch.bfloat16, 32, 16)])
+@pytest.mark.parametrize("weight,gate", [(True, True), (False, False), (True, False),
+                                         (False, True)])
+def test_prefill_epilogue_fused_in_segments(dtype, D, chunk, weight, gate):
+    """Epilogue fused into the segment-parallel chain's pass with outputs
+    (several segments, ragged last chunk), against the oracle."""
+    B, T, H = 1, 1100, 2
+    assert kda.kda_chunk_fwd_segments(B, T, H, D, D, chunk, 0, dtype) > 2
+    d = kda_inputs.prefill_inputs(500 + D + chunk, B, T, H, D, D, dtype, "cuda", s0_std=0.1)
+    check_prefill(d, chunk, epi_params(6, (B, T, H, D), dtype, weight, gate))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_epilogue_fused_equals_separate_pass(dtype, monkeypatch):
+    """Fused epilogue (segment chain) and the separate epilogue pass after the
+    per-slice chain agree to rounding."""
+    B, T, H, D, chunk = 1, 2000, 2, 64, 32
+    d = kda_inputs.prefill_inputs(77, B, T, H, D, D, dtype, "cuda", s0_std=0.1)
+    epi = epi_params(8, (B, T, H, D), dtype)
+    run = lambda: kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=chunk,
+                                    initial_state=d["S0"], epilogue=epi)
+    assert kda.kda_chunk_fwd_segments(B, T, H, D, D, chunk, 0, dtype) > 1
+    o1, _ = run()
+    monkeypatch.setenv("KDA_INTER_VARIANT", "reg16")
+    o2, _ = run()
+    torch.cuda.synchronize()
+    assert rel_err(o1.cpu().numpy(), o2.double().cpu().numpy()) < TOL[dtype]
