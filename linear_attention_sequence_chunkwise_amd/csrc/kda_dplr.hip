@@ -116,8 +116,9 @@ __global__ __launch_bounds__(256) void kda_dplr_intra(
     extern __shared__ __align__(16) char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
-    const int ch = blockIdx.x;
-    const int h = blockIdx.y;
+    // heads fastest: the workgroups in flight read whole token rows
+    const int ch = blockIdx.x / H;
+    const int h = blockIdx.x - ch * H;
     int tok0, len;
     if (table) {
         if (ch >= *chunk_total) return;
@@ -610,7 +611,7 @@ bool dplr_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf16,
     if (B < 1 || T < 0 || H < 1 || N < 1) return false;
     if (varlen && B != 1) return false;
     long long nchunk = varlen ? (long long)T / C + N : (long long)B * ((T + C - 1) / C);
-    if (nchunk > (1LL << 31) - 1) return false;
+    if (nchunk * H >= (1LL << 24)) return false;   // 1-D grid of 256-thread workgroups
     plan->nchunk_max = (int)nchunk;
     plan->chunk_rec_bytes = dplr_rec_bytes(D, C, bf16);
     size_t off = 0;
@@ -654,7 +655,7 @@ static hipError_t launch_dplr_dc(const DplrArgs& a, const PrefillPlan& plan) {
             auto kern = kda_dplr_intra<D, C, OT, IT>;
             const size_t smem = sizeof(DIntraSmem<D, C, OT>);
             if (hipError_t e = dplr_set_smem(kern, smem)) return e;
-            hipLaunchKernelGGL(kern, dim3((unsigned)plan.nchunk_max, (unsigned)a.H), dim3(256), smem,
+            hipLaunchKernelGGL(kern, dim3((unsigned)((long long)plan.nchunk_max * a.H)), dim3(256), smem,
                                a.stream, a.T, a.H, nch_seq, table, varlen ? chunk_off + a.N : nullptr,
                                (const IT*)a.q, (const IT*)a.k, (const IT*)a.a, (const IT*)a.b, a.g,
                                ws + plan.off_records);

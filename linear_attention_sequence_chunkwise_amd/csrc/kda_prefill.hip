@@ -218,8 +218,10 @@ __global__ __launch_bounds__(256) void kda_intra(
     extern __shared__ __align__(16) char smem_raw[];
     IntraSmem<D, C, OT>& sm = *reinterpret_cast<IntraSmem<D, C, OT>*>(smem_raw);
 
-    const int ch = blockIdx.x;
-    const int h = blockIdx.y;
+    // heads fastest: the workgroups in flight read whole token rows of q, k, g
+    // (all heads) and write consecutive records
+    const int ch = blockIdx.x / H;
+    const int h = blockIdx.x - ch * H;
     int tok0, len;
     if (table) {
         if (ch >= *chunk_total) return;
@@ -2488,7 +2490,9 @@ bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf
     long long nchunk;
     if (varlen) nchunk = (long long)T / C + N;
     else nchunk = (long long)B * ((T + C - 1) / C);
-    if (nchunk > (1LL << 31) - 1) return false;
+    // one 256-thread workgroup per (chunk, head) in a 1-D grid: the dispatch's
+    // work-item count must stay below 2^32
+    if (nchunk * H >= (1LL << 24)) return false;
     plan->nchunk_max = (int)nchunk;
     plan->chunk_rec_bytes = rec_bytes(D, C, bf16);
     size_t off = 0;
@@ -2596,7 +2600,7 @@ static hipError_t launch_records(const PrefillArgs& a, const PrefillPlan& plan, 
         hipError_t e = hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3((unsigned)plan.nchunk_max, (unsigned)a.H), dim3(256), smem,
+        hipLaunchKernelGGL(kern, dim3((unsigned)((long long)plan.nchunk_max * a.H)), dim3(256), smem,
                            a.stream, a.T, a.H, nch_seq, *table,
                            varlen ? *chunk_off + a.N : nullptr, (const IT*)a.q, (const IT*)a.k,
                            a.g, a.beta, ws + plan.off_records, aux, a.prep);

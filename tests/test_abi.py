@@ -63,6 +63,9 @@ def test_workspace_size(lib):
     assert ws(1, 100, 2, 64, 64, 48, 0, kda.KDA_BF16) == 0      # unsupported chunk
     assert ws(2, 100, 2, 64, 64, 64, 3, kda.KDA_BF16) == 0      # packed needs B == 1
     assert ws(1, 100, 2, 64, 64, 64, 0, 7) == 0                 # bad dtype
+    # at most 2^24 - 1 (chunk, head) pairs: one workgroup each in a 1-D grid
+    assert ws(1, 64 * ((1 << 22) - 1), 4, 64, 64, 64, 0, kda.KDA_BF16) > 0
+    assert ws(1, 64 * (1 << 22), 4, 64, 64, 64, 0, kda.KDA_BF16) == 0
 
 
 def test_chain_segments(lib):
