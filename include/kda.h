@@ -263,9 +263,10 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv,
  *                  alias grad_final_state; no other aliasing is allowed.
  *   workspace      at least kda_chunk_bwd_workspace_bytes(...) bytes,
  *                  256-byte aligned; contents on entry are ignored.
- * Errors as for kda_chunk_fwd.  Domain: that of kda_chunk_fwd, and within a
- * chunk the per-channel sum of -g stays below 80 (the intra-chunk gradient is
- * formed with exp(+-G) relative to the chunk start in fp32). */
+ * Errors as for kda_chunk_fwd, with KDA_ERR_BAD_SHAPE from 2^23 (chunk, head)
+ * pairs on.  Domain: that of kda_chunk_fwd, and within a chunk the
+ * per-channel sum of -g stays below 80 (the intra-chunk gradient is formed
+ * with exp(+-G) relative to the chunk start in fp32). */
 kda_status kda_chunk_bwd(int B, int T, int H, int dk, int dv, int chunk,
                          float scale, kda_dtype qkv_dtype,
                          const void *q, const void *k, const void *v,

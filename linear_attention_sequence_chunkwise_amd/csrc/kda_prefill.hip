@@ -1963,7 +1963,7 @@ __global__ __launch_bounds__(64 * kBwdDvWaves) void kda_bwd_vprod(
     extern __shared__ __align__(16) char smem_raw[];
     BwdDvSmem<D, C>& sm = *reinterpret_cast<BwdDvSmem<D, C>*>(smem_raw);
 
-    const int ch = blockIdx.x, h = blockIdx.y;
+    const int ch = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;   // heads fastest
     int tok0, len;
     if (table) {
         if (ch >= *chunk_total) return;
@@ -2143,7 +2143,7 @@ __global__ __launch_bounds__(64 * kBwdIntraWaves) void kda_bwd_intra(
     extern __shared__ __align__(16) char smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
-    const int ch = blockIdx.x, h = blockIdx.y;
+    const int ch = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;   // heads fastest
     int tok0, len;
     if (table) {
         if (ch >= *chunk_total) return;
@@ -2737,6 +2737,9 @@ bool backward_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool b
                    BackwardPlan* plan) {
     (void)bf16;   // the backward keeps fp32 records for either input type
     if (!prefill_plan(B, T, H, D, C, N, varlen, false, &plan->f)) return false;
+    // the per-(chunk, head) kernels run 512-thread workgroups in a 1-D grid:
+    // the dispatch's work-item count must stay below 2^32
+    if ((long long)plan->f.nchunk_max * H >= (1LL << 23)) return false;
     plan->f.nseg = 1;   // the backward runs its own chains: no segment states
     plan->f.total = plan->f.off_seg;
     const size_t nch = (size_t)plan->f.nchunk_max;
@@ -2817,7 +2820,8 @@ static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan)
             if (hipError_t e = hipGetLastError()) return e;
         }
         if (plan.f.nchunk_max == 0) return hipSuccess;
-        const dim3 grid((unsigned)plan.f.nchunk_max, (unsigned)a.H);
+        // one workgroup per (chunk, head), heads fastest (1-D grid)
+        const dim3 grid((unsigned)((long long)plan.f.nchunk_max * a.H));
         const int* total = varlen ? chunk_off + a.N : nullptr;
         // B4a: products over dv
         {

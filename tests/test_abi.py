@@ -186,6 +186,9 @@ def test_backward_workspace_and_validation(lib):
     assert wb(1, 100, 2, 64, 32, 64, 0, kda.KDA_BF16) == 0
     assert wb(1, 100, 2, 64, 64, 48, 0, kda.KDA_BF16) == 0
     assert wb(2, 100, 2, 64, 64, 64, 3, kda.KDA_BF16) == 0
+    # at most 2^23 - 1 (chunk, head) pairs (512-thread workgroups in a 1-D grid)
+    assert wb(1, 64 * ((1 << 21) - 1), 4, 64, 64, 64, 0, kda.KDA_BF16) > 0
+    assert wb(1, 64 * (1 << 21), 4, 64, 64, 64, 0, kda.KDA_BF16) == 0
     p = ctypes.c_void_p(4096)
 
     def bwd(B=1, T=64, H=2, dk=64, dv=64, chunk=64, dtype=kda.KDA_BF16, ptr=p, gb=p, dS0=None,
