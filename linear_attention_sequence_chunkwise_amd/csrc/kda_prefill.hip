@@ -1177,13 +1177,16 @@ struct SegSmem {
     alignas(1024) char img[2][WideTiles<D, C, OT, OUT>::KIB * 1024];
     alignas(1024) char vals[SegShape<D, OUT>::NW]
                            [(ValueCopy<C, IT, SegShape<D, OUT>::NVB>::BYTES + 1023) / 1024 * 1024];
-    float part[OUT ? C : 1][SegShape<D, OUT>::NW];   // fused epilogue: per-wave row sums of o^2
+    float part[2][OUT ? C : 1][SegShape<D, OUT>::NW];   // fused epilogue: per-wave row sums of o^2
 };
 
 // EPI (pass 3 only): the output epilogue (per-row RMS norm over dv, weight,
 // sigmoid gate) fused: a workgroup owns whole output rows, so each wave sums
-// the squares of its columns per row, the partial sums meet in LDS, and the
-// finished rows are written once.
+// the squares of its columns per row into LDS (two buffers, by chunk parity),
+// and a chunk's rows are finished at the end of the next chunk: the barrier
+// at that chunk's start has published every wave's sums, and the gate
+// entries, loaded at that start, have had the chunk's compute to land.  The
+// last chunk is finished after one more barrier.
 template <int D, int C, typename OT, typename IT, bool OUT, bool EPI = false>
 __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
     int T, int H, int N_seq, int nch_seq, int L, int nseg, float scale,
@@ -1251,6 +1254,58 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
     float wt[SS::NCB];   // fused epilogue: this lane's weight entries
 #pragma unroll
     for (int b = 0; b < SS::NCB; ++b) wt[b] = (EPI && weight) ? weight[cbase + 16 * b + l16] : 1.f;
+    // fused epilogue state: the previous chunk's output tiles and rows
+    float4v oprev[EPI ? SS::NCB : 1][EPI ? RT : 1];
+    bool have_prev = false;
+    int ptok0 = 0, plen = 0;
+    // this lane's gate entries of the rows of the chunk at tok0 (len rows)
+    auto load_gate = [&](uint32_t (&zr)[EPI ? SS::NCB : 1][EPI ? RT : 1][4], int tok0, int len) {
+        if constexpr (EPI) {
+            if (!gate) return;
+#pragma unroll
+            for (int b = 0; b < SS::NCB; ++b)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = min(16 * rt + 4 * lq + j, len - 1);
+                        const IT* zp = gate + ((size_t)(tok0 + r) * H + h) * D + cbase + 16 * b + l16;
+                        if constexpr (sizeof(IT) == 2)
+                            zr[b][rt][j] = reinterpret_cast<const bf16_t*>(zp)->bits;
+                        else
+                            zr[b][rt][j] = __builtin_bit_cast(uint32_t, *reinterpret_cast<const float*>(zp));
+                    }
+        }
+    };
+    // y = o / sqrt(mean over dv of o^2 + eps) * weight * sigmoid(gate) for
+    // the rows of a finished chunk; part: every wave's row sums of that chunk
+    auto finish = [&](const float4v (&ov)[EPI ? SS::NCB : 1][EPI ? RT : 1],
+                      const uint32_t (&zr)[EPI ? SS::NCB : 1][EPI ? RT : 1][4],
+                      const float (&part)[OUT ? C : 1][SS::NW], int tok0, int len) {
+        if constexpr (EPI) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * lq + j;
+                    float tot = 0.f;
+#pragma unroll
+                    for (int w = 0; w < SS::NW; ++w) tot += part[r][w];
+                    const float rs = rnorm(tot * (1.f / D) + eps);
+#pragma unroll
+                    for (int b = 0; b < SS::NCB; ++b) {
+                        const int col = cbase + 16 * b + l16;
+                        float y = ov[b][rt][j] * rs * wt[b];
+                        if (gate) {
+                            const float z = sizeof(IT) == 2 ? __builtin_bit_cast(float, zr[b][rt][j] << 16)
+                                                            : __builtin_bit_cast(float, zr[b][rt][j]);
+                            y *= sigmoid_f(z);
+                        }
+                        if (r < len) o[((size_t)(tok0 + r) * H + h) * D + col] = y;
+                    }
+                }
+        }
+    };
     // this wave's value columns of chunk c (row 0) in global memory
     auto vsrc = [&](int c) -> const IT* {
         return v + ((size_t)(n * T + c * C) * H + h) * D + cbase;
@@ -1273,28 +1328,13 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
         // buffer the copies of chunk c + 1 then refill
         asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
         lds_barrier();
-        // fused epilogue: this lane's gate entries of the chunk (rows clamped
-        // to the chunk; used after the products, so the loads have the chunk's
-        // compute to land).  Issued before the next chunk's copies: the memory
-        // counter retires in order, so waiting for the gate then does not wait
-        // for those copies.
+        // fused epilogue: this lane's gate entries of the previous chunk's rows
+        // (rows clamped to that chunk), finished at the end of this chunk.
+        // Issued before the next chunk's copies: the memory counter retires in
+        // order, so waiting for the gate then does not wait for those copies.
         uint32_t zr[EPI ? SS::NCB : 1][EPI ? RT : 1][4];
         if constexpr (EPI) {
-            if (gate) {
-#pragma unroll
-                for (int b = 0; b < SS::NCB; ++b)
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int r = min(16 * rt + 4 * lq + j, len - 1);
-                            const IT* zp = gate + ((size_t)(tok0 + r) * H + h) * D + cbase + 16 * b + l16;
-                            if constexpr (sizeof(IT) == 2)
-                                zr[b][rt][j] = reinterpret_cast<const bf16_t*>(zp)->bits;
-                            else
-                                zr[b][rt][j] = __builtin_bit_cast(uint32_t, *reinterpret_cast<const float*>(zp));
-                        }
-            }
+            if (have_prev) load_gate(zr, ptok0, plen);
         }
         if (c + 1 < c1) copy_record(c + 1, bi ^ 1);
         float4v oo[SS::NCB][RT];
@@ -1303,7 +1343,10 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
             tiles, st, vl, vl_lds, c + 1 < c1 ? vsrc(c + 1) : nullptr, vstride,
             min(C, T - (c + 1) * C), cbase, tok0, len, H, h, scale, o, oo);
         if constexpr (EPI) {
-            // y = o / sqrt(mean over dv of o^2 + eps) * weight * sigmoid(gate)
+            // the previous chunk's rows: every wave's sums were published by
+            // the barrier at this chunk's start
+            if (have_prev) finish(oprev, zr, sm.part[bi ^ 1], ptok0, plen);
+            // this wave's sums of squares per row of the chunk, into the parity buffer
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -1312,30 +1355,23 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
 #pragma unroll
                     for (int b = 0; b < SS::NCB; ++b) ss += oo[b][rt][j] * oo[b][rt][j];
                     ss = group_sum<16>(ss);
-                    if (l16 == 0) sm.part[16 * rt + 4 * lq + j][wave] = ss;
+                    if (l16 == 0) sm.part[bi][16 * rt + 4 * lq + j][wave] = ss;
                 }
+#pragma unroll
+            for (int b = 0; b < SS::NCB; ++b)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) oprev[b][rt] = oo[b][rt];
+            have_prev = true;
+            ptok0 = tok0;
+            plen = len;
+        }
+    }
+    if constexpr (EPI) {
+        if (have_prev) {   // the last chunk: every wave's sums, then its rows
+            uint32_t zr[SS::NCB][RT][4];
+            load_gate(zr, ptok0, plen);
             lds_barrier();
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * rt + 4 * lq + j;
-                    float tot = 0.f;
-#pragma unroll
-                    for (int w = 0; w < SS::NW; ++w) tot += sm.part[r][w];
-                    const float rs = rnorm(tot * (1.f / D) + eps);
-#pragma unroll
-                    for (int b = 0; b < SS::NCB; ++b) {
-                        const int col = cbase + 16 * b + l16;
-                        float y = oo[b][rt][j] * rs * wt[b];
-                        if (gate) {
-                            const float z = sizeof(IT) == 2 ? __builtin_bit_cast(float, zr[b][rt][j] << 16)
-                                                            : __builtin_bit_cast(float, zr[b][rt][j]);
-                            y *= sigmoid_f(z);
-                        }
-                        if (r < len) o[((size_t)(tok0 + r) * H + h) * D + col] = y;
-                    }
-                }
+            finish(oprev, zr, sm.part[(c1 - 1 - c0) & 1], ptok0, plen);
         }
     }
 #pragma unroll
