@@ -898,9 +898,9 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
 // with V = 0) and E is the run from zero.  A fixed-length sequence of nch
 // chunks is cut into nseg segments of L chunks:
 //   pass 1 (kda_seg_chain, OUT = false), for each segment s < nseg - 1: the
-//          run of V from S0 (s = 0) or from zero (E_s); for 0 < s < nseg - 1
-//          also the run of the identity with V = 0 (P_s), in a second
-//          workgroup on the same XCD, which reads the same records;
+//          run of V from S0 (s = 0) or from zero (E_s) and, for s > 0, the
+//          run of the identity with V = 0 (P_s), as two column blocks of every
+//          wave, which share the record's operand reads;
 //   pass 2 (kda_seg_combine): Sin_0 = S0, Sin_1 = E_0, and
 //          Sin_{s+1} = P_s Sin_s + E_s, in fp32;
 //   pass 3 (kda_seg_chain, OUT = true): every segment from Sin_s with
@@ -997,7 +997,6 @@ template <int D, int C, typename OT, bool FULL>
 struct WideTiles {
     typedef Rec<D, C, OT> R;
     static constexpr int K_KPT = (int)(R::KPt * sizeof(OT) / 1024);   // KiB of KG (+ QG)
-    static constexpr int K_TB = (int)(R::Tb * sizeof(OT) / 1024);
     static constexpr int K_M = (int)(R::M * sizeof(OT) / 1024);
     static constexpr int K_QG = (int)(R::QG * sizeof(OT) / 1024);
     static constexpr int K_REC = (int)(R::bytes / 1024);
@@ -1163,7 +1162,8 @@ __device__ __forceinline__ void wide_chunk(const WideTiles<D, C, OT, OUT>& t,
 // Waves and 16-column blocks per wave of the segment kernels.  Pass 1: one
 // wave per 16 columns of D, carrying those columns of the run of V (block 0)
 // and of the run of the identity (block 1).  Pass 3: kSegOutBlocks blocks of
-// the run of V per wave.
+// the run of V per wave (two blocks halve the LDS operand reads but leave one
+// wave per SIMD; at d = 128 that measured slower).
 constexpr int kSegOutBlocks = 1;
 template <int D, bool OUT>
 struct SegShape {
