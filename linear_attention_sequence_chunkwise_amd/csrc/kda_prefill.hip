@@ -2500,9 +2500,10 @@ static bool seg_fits(int D, int C, bool bf16) {
 
 // Segments per sequence for the segment-parallel chain (fixed-length batches):
 // enough that sequences x heads x segments covers the 256 CUs of an MI355X
-// with one workgroup each, with at least kSegMinChunks chunks per segment.
+// with one workgroup each, with at least kSegMinChunks chunks per segment and
+// at most kSegMax segments (the combine is nseg - 2 dependent steps).
 // nseg = 1: the per-slice chain kernels run instead.
-constexpr int kSegCUs = 256, kSegMinChunks = 4;
+constexpr int kSegCUs = 256, kSegMinChunks = 4, kSegMax = 32;
 // Returns the segment count the state planes are reserved for: the count
 // asked for before rounding the segment length, which never falls as nch
 // grows (the count used, nseg, can: 32 chunks make 8 segments of 4, 33 make
@@ -2511,7 +2512,8 @@ static int seg_split(long long chains, int nch, bool ok, int* nseg, int* seg_len
     *nseg = 1;
     *seg_len = nch;
     if (!ok || chains < 1 || nch < 1) return 1;
-    const long long ns = std::min<long long>(kSegCUs / chains, nch / kSegMinChunks);
+    const long long ns = std::min<long long>(std::min<long long>(kSegCUs / chains, kSegMax),
+                                             nch / kSegMinChunks);
     if (ns < 2) return 1;
     const int l = (int)((nch + ns - 1) / ns);
     *seg_len = l;

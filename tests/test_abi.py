@@ -82,6 +82,8 @@ def test_chain_segments(lib):
     assert seg(1, 32768, 32, 64, 64, 64, 0, kda.KDA_F32) == 1        # fp32 d=64 C=64: LDS
     assert seg(1, 32768, 32, 64, 64, 32, 0, kda.KDA_F32) == 8
     assert seg(1, 32768, 32, 96, 96, 64, 0, kda.KDA_BF16) == 0       # unsupported
+    # one chain: the CUs would take 256 segments, the combine's depth caps it at 32
+    assert seg(1, 32768, 1, 128, 128, 64, 0, kda.KDA_BF16) == 32
 
 
 def test_workspace_monotone_in_T(lib):

@@ -255,3 +255,12 @@ def test_segmented_in_place_state():
                               initial_state=st, final_state=st)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, st)
+
+
+def test_single_chain_many_segments():
+    """One (sequence, head) chain cut into 32 segments (the cap): 30 combine
+    steps, each segment rerun from its combined state."""
+    B, T, H, D = 1, 32 * 4 * 64 - 20, 1, 128
+    assert kda.kda_chunk_fwd_segments(B, T, H, D, D, 64) == 32
+    d = make_prefill(90, B, T, H, D, torch.bfloat16, s0_std=0.1)
+    check(d, 64)
