@@ -364,7 +364,10 @@ __global__ __launch_bounds__(256) void kda_intra(
     // KG_r = (k_r a_r) exp(Gs_I) : rows of 16 bytes
     // (record columns in the kperm order: stored column c0 + e holds channel
     // kperm_inv(c0 + e))
-    for (int idx = tid; idx < C * D / EPV; idx += 256) {
+    #pragma unroll
+    for (int it_ = 0; it_ < (C * D / EPV + 255) / 256; ++it_) {   // compile-time trip count
+        const int idx = tid + 256 * it_;
+        if (idx >= C * D / EPV) break;
         const int r = idx / (D / EPV), c0 = (idx % (D / EPV)) * EPV;
         float kk[EPV];
 #pragma unroll
@@ -376,7 +379,10 @@ __global__ __launch_bounds__(256) void kda_intra(
     }
     // KPt[c][i] = (k_i b_i) exp(G_n - Ge_J), transposed: 16 bytes of one channel
     // row; token columns in the kperm order, zero past C (k-padding)
-    for (int idx = tid; idx < D * R::CK / EPV; idx += 256) {
+    #pragma unroll
+    for (int it_ = 0; it_ < (D * R::CK / EPV + 255) / 256; ++it_) {   // compile-time trip count
+        const int idx = tid + 256 * it_;
+        if (idx >= D * R::CK / EPV) break;
         const int c = idx / (R::CK / EPV), i0 = (idx % (R::CK / EPV)) * EPV;
         // the group's runs of four tokens lie in sub-blocks J and (fp16) J + 1
         const int J = group_col<OT>(i0, 0) >> 4;
@@ -434,7 +440,10 @@ __global__ __launch_bounds__(256) void kda_intra(
         }
     }
     // zero A above the diagonal blocks
-    for (int idx = tid; idx < C * C; idx += 256) {
+    #pragma unroll
+    for (int it_ = 0; it_ < (C * C + 255) / 256; ++it_) {   // compile-time trip count
+        const int idx = tid + 256 * it_;
+        if (idx >= C * C) break;
         const int r = idx / C, col = idx - r * C;
         if ((col >> 4) > (r >> 4)) sm.A[r * LDA + col] = to_ot<OT>(0.f);
     }
@@ -449,7 +458,10 @@ __global__ __launch_bounds__(256) void kda_intra(
     }
     lds_barrier();
     // QG_r = (q_r a_r) exp(Gs_I) : rows of 16 bytes
-    for (int idx = tid; idx < C * D / EPV; idx += 256) {
+    #pragma unroll
+    for (int it_ = 0; it_ < (C * D / EPV + 255) / 256; ++it_) {   // compile-time trip count
+        const int idx = tid + 256 * it_;
+        if (idx >= C * D / EPV) break;
         const int r = idx / (D / EPV), c0 = (idx % (D / EPV)) * EPV;
         float qq[EPV];
 #pragma unroll
@@ -490,7 +502,10 @@ __global__ __launch_bounds__(256) void kda_intra(
                 sm.u.s.M[(16 * Ib + 4 * lq + j) * LDA + 16 * Jb + l16] = to_ot<OT>(macc[i][j]);
         }
     }
-    for (int idx = tid; idx < C * C; idx += 256) {   // zero the upper blocks of M and T
+    #pragma unroll
+    for (int it_ = 0; it_ < (C * C + 255) / 256; ++it_) {   // compile-time trip count
+        const int idx = tid + 256 * it_;
+        if (idx >= C * C) break;   // zero the upper blocks of M and T
         const int r = idx / C, col = idx - r * C;
         if ((col >> 4) > (r >> 4)) {
             sm.u.s.M[r * LDA + col] = to_ot<OT>(0.f);
@@ -523,7 +538,10 @@ __global__ __launch_bounds__(256) void kda_intra(
     // ---- phase 4b: store M; off-diagonal blocks of T level by level:
     //      T_IJ = -T_II * sum_{m=J}^{I-1} A_Im T_mJ ----
     // (token columns in the kperm order, zero past C)
-    for (int idx = tid; idx < C * R::CK / EPV; idx += 256) {
+    #pragma unroll
+    for (int it_ = 0; it_ < (C * R::CK / EPV + 255) / 256; ++it_) {   // compile-time trip count
+        const int idx = tid + 256 * it_;
+        if (idx >= C * R::CK / EPV) break;
         const int r = idx / (R::CK / EPV), c0 = (idx % (R::CK / EPV)) * EPV;
         float mv[EPV];
 #pragma unroll
@@ -557,14 +575,20 @@ __global__ __launch_bounds__(256) void kda_intra(
     // to aux when asked ----
     if (aux) {
         float* ta = aux + ((size_t)ch * H + h) * 2 * C * C;
-        for (int idx = tid; idx < C * C / 4; idx += 256) {
+        #pragma unroll
+        for (int it_ = 0; it_ < (C * C / 4 + 255) / 256; ++it_) {   // compile-time trip count
+            const int idx = tid + 256 * it_;
+            if (idx >= C * C / 4) break;
             const int r = idx / (C / 4), c0 = (idx % (C / 4)) * 4;
             *reinterpret_cast<float4*>(ta + r * C + c0) =
                 *reinterpret_cast<const float4*>(&sm.u.s.T[r * LDT + c0]);
         }
     }
     // (token columns in the kperm order, zero past C)
-    for (int idx = tid; idx < C * R::CK / EPV; idx += 256) {
+    #pragma unroll
+    for (int it_ = 0; it_ < (C * R::CK / EPV + 255) / 256; ++it_) {   // compile-time trip count
+        const int idx = tid + 256 * it_;
+        if (idx >= C * R::CK / EPV) break;
         const int r = idx / (R::CK / EPV), c0 = (idx % (R::CK / EPV)) * EPV;
         float tv[EPV];
 #pragma unroll
