@@ -319,8 +319,6 @@ __global__ __launch_bounds__(256) void kda_intra(
         for (int e = 0; e < 2; ++e) {
             const int c = c0 + e;
             float* gv = e ? g1 : g0;
-            const float* kv = e ? k1v : k0v;
-            float* qv = e ? q1v : q0v;
             float Gs = 0.f, Gn = 0.f;
 #pragma unroll
             for (int m = 0; m < NB; ++m) {
@@ -331,31 +329,46 @@ __global__ __launch_bounds__(256) void kda_intra(
             const float sigI = sm.sig[I * D + c];
             sm.egs[I * D + c] = exp_e(Gs);                // exp(G before block I) <= 1
             float GsJ = 0.f;
-            for (int J = 0; J <= I; ++J) {
-                const float sgJ = sm.sig[J * D + c];
-                const float f = (J < I) ? exp_e(Gs - (GsJ + sgJ)) : exp_e(-sigI);
-                sm.F[(I * NB + J) * D + c] = to_ot<OT>(f);
-                GsJ += sgJ;
+#pragma unroll
+            for (int J = 0; J < NB; ++J) {
+                if (J <= I) {
+                    const float sgJ = sm.sig[J * D + c];
+                    const float f = (J < I) ? exp_e(Gs - (GsJ + sgJ)) : exp_e(-sigI);
+                    sm.F[(I * NB + J) * D + c] = to_ot<OT>(f);
+                    GsJ += sgJ;
+                }
             }
             if (I == 0) gn_out[c] = exp_e(Gn);
-            // alpha_j = exp(g_j); a_j = prod_{j'<=j} alpha, b_j = prod_{j'>j} alpha
+            // alpha_j = exp(g_j)
 #pragma unroll
             for (int j = 0; j < 16; ++j) gv[j] = exp_e(gv[j]);
-            float a = 1.f;
+        }
+        // a_j = prod_{j'<=j} alpha, b_j = prod_{j'>j} alpha, both channels of the
+        // pair at once: one 4-byte (fp16) or 8-byte (fp32) LDS store per row
+        auto store2 = [](OT* p, float x0, float x1) {
+            if constexpr (sizeof(OT) == 2)
+                *reinterpret_cast<uint32_t*>(p) = __builtin_bit_cast(uint16_t, (_Float16)x0) |
+                                                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x1) << 16);
+            else
+                *reinterpret_cast<float2*>(p) = float2{x0, x1};
+        };
+        float a0 = 1.f, a1 = 1.f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                a *= gv[j];
-                const int r = 16 * I + j;
-                sm.u.g.kl[r * LDK + c] = to_ot<OT>(kv[j] * a);
-                qv[j] *= a;            // q_r a_r, written to LDS after the k.k^T Gram
-            }
-            float bb = 1.f;
+        for (int j = 0; j < 16; ++j) {
+            a0 *= g0[j];
+            a1 *= g1[j];
+            const int r = 16 * I + j;
+            store2(&sm.u.g.kl[r * LDK + c0], k0v[j] * a0, k1v[j] * a1);
+            q0v[j] *= a0;          // q_r a_r, written to LDS after the k.k^T Gram
+            q1v[j] *= a1;
+        }
+        float b0 = 1.f, b1 = 1.f;
 #pragma unroll
-            for (int j = 15; j >= 0; --j) {
-                const int r = 16 * I + j;
-                sm.u.g.kr[r * LDK + c] = to_ot<OT>(kv[j] * bb);
-                bb *= gv[j];
-            }
+        for (int j = 15; j >= 0; --j) {
+            const int r = 16 * I + j;
+            store2(&sm.u.g.kr[r * LDK + c0], k0v[j] * b0, k1v[j] * b1);
+            b0 *= g0[j];
+            b1 *= g1[j];
         }
     }
     lds_barrier();
@@ -387,7 +400,9 @@ __global__ __launch_bounds__(256) void kda_intra(
         // the group's runs of four tokens lie in sub-blocks J and (fp16) J + 1
         const int J = group_col<OT>(i0, 0) >> 4;
         float tail = 0.f;   // G_n - Ge_J: the gate sums of the later sub-blocks
-        for (int m = J + 1; m < NB; ++m) tail += sm.sig[m * D + c];
+#pragma unroll
+        for (int m = 1; m < NB; ++m)
+            if (m > J) tail += sm.sig[m * D + c];
         const float f0 = exp_e(tail);
         const float f1 = J + 1 < NB ? exp_e(tail - sm.sig[(J + 1) * D + c]) : 0.f;
         float kk[EPV];
