@@ -69,15 +69,22 @@ namespace kda {
 //   Gn  [D]        exp(G_n), fp32, at byte gn_byte
 // CK = max(C, one instruction's k); columns C..CK-1 are zero.  The record is
 // rounded up to whole KiB.
+//
+// fp16 records (FOLD) carry the two products with Tb instead of Tb itself:
+// the KPt slot holds W = KPt Tb and the M slot M Tb (still lower triangular),
+// and there is no Tb slot.  The chain then needs no U = Tb X step:
+// KPt U = W X and M U = (M Tb) X.  The backward keeps the plain fp32 record,
+// whose T, M and KPt it differentiates through.
 // ---------------------------------------------------------------------------
 template <int D, int C, typename OT>
 struct Rec {
+    static constexpr bool FOLD = sizeof(OT) == 2;
     static constexpr int CK = chunk_k<C, OT>();
     static constexpr size_t KG = 0;
     static constexpr size_t QG = (size_t)C * D;
     static constexpr size_t KPt = 2 * (size_t)C * D;
     static constexpr size_t Tb = KPt + (size_t)D * CK;
-    static constexpr size_t M = Tb + (size_t)C * CK;
+    static constexpr size_t M = Tb + (FOLD ? 0 : (size_t)C * CK);
     static constexpr size_t gn_byte = (M + (size_t)C * CK) * sizeof(OT);
     static constexpr size_t bytes = (gn_byte + 4 * (size_t)D + 1023) / 1024 * 1024;
 };
@@ -95,7 +102,7 @@ static size_t rec_bytes(int D, int C, bool bf16) {
     const size_t es = bf16 ? 2 : 4;
     const size_t ks = bf16 ? 32 : 4;
     const size_t ck = (size_t)C > ks ? C : ks;
-    const size_t gn = (2 * (size_t)C * D + (size_t)D * ck + 2 * (size_t)C * ck) * es;
+    const size_t gn = (2 * (size_t)C * D + (size_t)D * ck + (bf16 ? 1 : 2) * (size_t)C * ck) * es;
     return (gn + 4 * (size_t)D + 1023) / 1024 * 1024;
 }
 
@@ -392,11 +399,7 @@ __global__ __launch_bounds__(256) void kda_intra(
     }
     // KPt[c][i] = (k_i b_i) exp(G_n - Ge_J), transposed: 16 bytes of one channel
     // row; token columns in the kperm order, zero past C (k-padding)
-    #pragma unroll
-    for (int it_ = 0; it_ < (D * R::CK / EPV + 255) / 256; ++it_) {   // compile-time trip count
-        const int idx = tid + 256 * it_;
-        if (idx >= D * R::CK / EPV) break;
-        const int c = idx / (R::CK / EPV), i0 = (idx % (R::CK / EPV)) * EPV;
+    auto kpt_group = [&](int c, int i0, float (&kk)[EPV]) {
         // the group's runs of four tokens lie in sub-blocks J and (fp16) J + 1
         const int J = group_col<OT>(i0, 0) >> 4;
         float tail = 0.f;   // G_n - Ge_J: the gate sums of the later sub-blocks
@@ -405,13 +408,42 @@ __global__ __launch_bounds__(256) void kda_intra(
             if (m > J) tail += sm.sig[m * D + c];
         const float f0 = exp_e(tail);
         const float f1 = J + 1 < NB ? exp_e(tail - sm.sig[(J + 1) * D + c]) : 0.f;
-        float kk[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const int i = group_col<OT>(i0, e);
             kk[e] = i < C ? (float)sm.u.g.kr[i * LDK + c] * (e < 4 ? f0 : f1) : 0.f;
         }
-        *reinterpret_cast<vec*>(rec + R::KPt + swz<OT, R::CK>(c, i0)) = pack16(kk);
+    };
+    const int l16 = lane & 15;
+    const int lq = lane >> 4;
+    // FOLD: KPt stays in registers as the B fragments of W^T = Tb^T KPt^T
+    // (channel blocks wave, wave + 4, ..; lane: channel l16 of the block and
+    // the 16-byte token group 8 lq of each 32-token step), for phase 5
+    constexpr int NCB = D / 16, CPW = (NCB + 3) / 4, NKS = R::CK / 32;
+    half8 kpf[R::FOLD ? CPW : 1][R::FOLD ? NKS : 1];
+    if constexpr (R::FOLD) {
+#pragma unroll
+        for (int x = 0; x < CPW; ++x) {
+            const int cb = wave + 4 * x;
+            if (cb < NCB) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    float kk[EPV];
+                    kpt_group(16 * cb + l16, 32 * ks + 8 * lq, kk);
+                    kpf[x][ks] = __builtin_bit_cast(half8, pack16(kk));
+                }
+            }
+        }
+    } else {
+        #pragma unroll
+        for (int it_ = 0; it_ < (D * R::CK / EPV + 255) / 256; ++it_) {   // compile-time trip count
+            const int idx = tid + 256 * it_;
+            if (idx >= D * R::CK / EPV) break;
+            const int c = idx / (R::CK / EPV), i0 = (idx % (R::CK / EPV)) * EPV;
+            float kk[EPV];
+            kpt_group(c, i0, kk);
+            *reinterpret_cast<vec*>(rec + R::KPt + swz<OT, R::CK>(c, i0)) = pack16(kk);
+        }
     }
 
     // ---- phase 3b: Gram blocks on the matrix cores ----
@@ -420,8 +452,6 @@ __global__ __launch_bounds__(256) void kda_intra(
     // until the Gram operands are dead.
     constexpr int NT = NB * (NB + 1) / 2;
     constexpr int TPW = (NT + 3) / 4;
-    const int l16 = lane & 15;
-    const int lq = lane >> 4;
     auto gram = [&](int Ib, int Jb) {
         float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -550,21 +580,23 @@ __global__ __launch_bounds__(256) void kda_intra(
     }
     lds_barrier();
 
-    // ---- phase 4b: store M; off-diagonal blocks of T level by level:
-    //      T_IJ = -T_II * sum_{m=J}^{I-1} A_Im T_mJ ----
+    // ---- phase 4b: store M (FOLD: M Tb, in phase 5); off-diagonal blocks of
+    //      T level by level: T_IJ = -T_II * sum_{m=J}^{I-1} A_Im T_mJ ----
     // (token columns in the kperm order, zero past C)
-    #pragma unroll
-    for (int it_ = 0; it_ < (C * R::CK / EPV + 255) / 256; ++it_) {   // compile-time trip count
-        const int idx = tid + 256 * it_;
-        if (idx >= C * R::CK / EPV) break;
-        const int r = idx / (R::CK / EPV), c0 = (idx % (R::CK / EPV)) * EPV;
-        float mv[EPV];
+    if constexpr (!R::FOLD) {
+        #pragma unroll
+        for (int it_ = 0; it_ < (C * R::CK / EPV + 255) / 256; ++it_) {   // compile-time trip count
+            const int idx = tid + 256 * it_;
+            if (idx >= C * R::CK / EPV) break;
+            const int r = idx / (R::CK / EPV), c0 = (idx % (R::CK / EPV)) * EPV;
+            float mv[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-            const int col = group_col<OT>(c0, e);
-            mv[e] = col < C ? (float)sm.u.s.M[r * LDA + col] : 0.f;
+            for (int e = 0; e < EPV; ++e) {
+                const int col = group_col<OT>(c0, e);
+                mv[e] = col < C ? (float)sm.u.s.M[r * LDA + col] : 0.f;
+            }
+            *reinterpret_cast<vec*>(rec + R::M + swz<OT, R::CK>(r, c0)) = pack16(mv);
         }
-        *reinterpret_cast<vec*>(rec + R::M + swz<OT, R::CK>(r, c0)) = pack16(mv);
     }
     for (int d = 1; d < NB; ++d) {
         if (wave < NB - d) {
@@ -600,18 +632,107 @@ __global__ __launch_bounds__(256) void kda_intra(
         }
     }
     // (token columns in the kperm order, zero past C)
-    #pragma unroll
-    for (int it_ = 0; it_ < (C * R::CK / EPV + 255) / 256; ++it_) {   // compile-time trip count
-        const int idx = tid + 256 * it_;
-        if (idx >= C * R::CK / EPV) break;
-        const int r = idx / (R::CK / EPV), c0 = (idx % (R::CK / EPV)) * EPV;
-        float tv[EPV];
+    if constexpr (!R::FOLD) {
+        #pragma unroll
+        for (int it_ = 0; it_ < (C * R::CK / EPV + 255) / 256; ++it_) {   // compile-time trip count
+            const int idx = tid + 256 * it_;
+            if (idx >= C * R::CK / EPV) break;
+            const int r = idx / (R::CK / EPV), c0 = (idx % (R::CK / EPV)) * EPV;
+            float tv[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-            const int col = group_col<OT>(c0, e);
-            tv[e] = col < C ? sm.u.s.T[r * LDT + col] * sm.beta[col] : 0.f;
+            for (int e = 0; e < EPV; ++e) {
+                const int col = group_col<OT>(c0, e);
+                tv[e] = col < C ? sm.u.s.T[r * LDT + col] * sm.beta[col] : 0.f;
+            }
+            *reinterpret_cast<vec*>(rec + R::Tb + swz<OT, R::CK>(r, c0)) = pack16(tv);
         }
-        *reinterpret_cast<vec*>(rec + R::Tb + swz<OT, R::CK>(r, c0)) = pack16(tv);
+    } else {
+        // FOLD: W = KPt Tb and M Tb, computed transposed (W^T = Tb^T KPt^T,
+        // (M Tb)^T = Tb^T M^T) so that an output lane holds four consecutive
+        // tokens j of one row: with the tiles of tokens 32 b + 0..15 and
+        // 32 b + 16..31 side by side that is one 16-byte group of the kperm
+        // order (stored 32 b + 8 lq .. + 7).  A fragments of Tb^T: rows j of
+        // tile jt, the tokens i of k-step ks in the kperm order (Tb_ij = 0 for
+        // i < j: steps below jt / 2 are zero).
+        half8 ta[NB][NKS];
+#pragma unroll
+        for (int jt = 0; jt < NB; ++jt)
+#pragma unroll
+            for (int ks = jt / 2; ks < NKS; ++ks) {
+                const int j = 16 * jt + l16;
+                const float bj = sm.beta[j];
+                float a[EPV];
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    const int i = group_col<OT>(32 * ks + 8 * lq, e);
+                    a[e] = i < C ? sm.u.s.T[i * LDT + j] * bj : 0.f;
+                }
+                ta[jt][ks] = __builtin_bit_cast(half8, pack16(a));
+            }
+        const float4v zero = {0.f, 0.f, 0.f, 0.f};
+        // W rows: this wave's channel blocks
+#pragma unroll
+        for (int x = 0; x < CPW; ++x) {
+            const int cb = wave + 4 * x;
+            if (cb < NCB) {
+#pragma unroll
+                for (int b = 0; b < NKS; ++b) {
+                    float w[EPV];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int jt = 2 * b + hh;
+                        float4v acc = zero;
+                        if (jt < NB) {
+#pragma unroll
+                            for (int ks = jt / 2; ks < NKS; ++ks) acc = mm::mma(ta[jt][ks], kpf[x][ks], acc);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[4 * hh + e] = acc[e];
+                    }
+                    *reinterpret_cast<vec*>(rec + R::KPt + swz<OT, R::CK>(16 * cb + l16, 32 * b + 8 * lq)) =
+                        pack16(w);
+                }
+            }
+        }
+        // M Tb rows: row tiles rt = wave, wave + 4, ..; every 32-token block b
+        // (compile-time, so that the fragments stay in registers);
+        // (M Tb)_rj = sum_{j <= i <= r} M_ri Tb_ij, zero for j > r
+#pragma unroll
+        for (int z = 0; z < (NB + 3) / 4; ++z) {
+            const int rt = wave + 4 * z;
+            if (rt < NB) {
+                const int r = 16 * rt + l16;
+                // B fragments of M^T: row r, the k-step's tokens in the kperm order
+                half8 bm[NKS];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    float mv[EPV];
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        const int i = group_col<OT>(32 * ks + 8 * lq, e);
+                        mv[e] = i < C ? (float)sm.u.s.M[r * LDA + i] : 0.f;
+                    }
+                    bm[ks] = __builtin_bit_cast(half8, pack16(mv));
+                }
+#pragma unroll
+                for (int b = 0; b < NKS; ++b) {
+                    float w[EPV];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int jt = 2 * b + hh;
+                        float4v acc = zero;
+                        if (jt < NB && jt <= rt) {
+#pragma unroll
+                            for (int ks = jt / 2; ks < NKS; ++ks)
+                                if (ks <= rt / 2) acc = mm::mma(ta[jt][ks], bm[ks], acc);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[4 * hh + e] = acc[e];
+                    }
+                    *reinterpret_cast<vec*>(rec + R::M + swz<OT, R::CK>(r, 32 * b + 8 * lq)) = pack16(w);
+                }
+            }
+        }
     }
 }
 
@@ -639,7 +760,7 @@ struct ChunkTiles {
         kg = base + R::KG;
         qg = base + R::QG;
         kpt = base + R::KPt;
-        tb = base + R::Tb;
+        tb = R::FOLD ? nullptr : base + R::Tb;
         m = base + R::M;
         gn = reinterpret_cast<const float*>(img + R::gn_byte);
         v = vraw;
@@ -654,6 +775,8 @@ struct ChunkTiles {
 // may be overwritten.  OUT = false: state only (QS and O are skipped).
 // xh, uh (optional): this chunk's [C][D] fp32 tiles of X and U, of which the
 // slice's columns are written (the backward pass reads them).
+// Folded (fp16) records: O = scale (QS + (M Tb) X), S <- Diag(Gamma_n) S + W X
+// with no U step; its barrier stays, so every chunk has the same barriers.
 template <int D, int C, int BV, typename OT, typename IT, int NWC = 4, bool OUT = true>
 __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
                                             ChainScratch<D, C, BV, OT>& cs,
@@ -707,10 +830,12 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
     lds_barrier();
 
     // ---- U = Tb X (Tb lower triangular: k only up to the diagonal block) ----
+    constexpr bool FOLD = Rec<D, C, OT>::FOLD;
+    const OT* ub_tile = FOLD ? cs.x : cs.u;   // B operand of the output and state products
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
         const int tt = wave + NWC * i;
-        if (tt < OTILES) {
+        if (!FOLD && tt < OTILES) {
             const int rt = tt / VT, vt = tt % VT;
             float4v uacc = {0.f, 0.f, 0.f, 0.f};
             const int kend = 16 * (rt + 1);
@@ -739,7 +864,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
             for (int ks = 0; ks < kend; ks += mm::KS) {
                 const int kk = ks + lq * mm::KPL;
                 acc = mm::mma(load_swz<OT, CK>(t.m, 16 * rt + l16, kk),
-                              mm::load(cs.u, LDC, 16 * vt + l16, kk), acc);
+                              mm::load(ub_tile, LDC, 16 * vt + l16, kk), acc);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -762,7 +887,7 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
             for (int ks = 0; ks < CK; ks += mm::KS) {
                 const int kk = ks + lq * mm::KPL;
                 st[i] = mm::mma(load_swz<OT, CK>(t.kpt, 16 * ct + l16, kk),
-                                mm::load(cs.u, LDC, 16 * vt + l16, kk), st[i]);
+                                mm::load(ub_tile, LDC, 16 * vt + l16, kk), st[i]);
             }
         }
     }
@@ -1058,13 +1183,13 @@ struct WideTiles {
         if constexpr (FULL) {
             qg = base + R::QG;
             kpt = base + R::KPt;
-            tb = base + R::Tb;
+            tb = R::FOLD ? nullptr : base + R::Tb;
             m = base + R::M;
             gn = reinterpret_cast<const float*>(img + R::gn_byte);
         } else {
             qg = m = nullptr;
             kpt = reinterpret_cast<const OT*>(img + 1024 * (size_t)K_QG);
-            tb = kpt + (R::Tb - R::KPt);
+            tb = R::FOLD ? nullptr : kpt + (R::Tb - R::KPt);
             gn = reinterpret_cast<const float*>(img + 1024 * (size_t)(K_QG + K_M - K_KPT));
         }
     }
@@ -1145,20 +1270,27 @@ __device__ __forceinline__ void wide_chunk(const WideTiles<D, C, OT, OUT>& t,
     BOps<OT, RT> xb[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) xb[nb].from(x[nb]);
-    float4v u[NB][RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {   // Tb is lower triangular: k-tiles 0..rt
-        float4v acc[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = zero;
-        tile_chain_mma_nb<OT, CK, RT, NB>(acc, t.tb, rt, rt + 1, xb);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) u[nb][rt] = acc[nb];
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    // B operand of the output and state products: U = Tb X, or X itself with
+    // folded records (whose M and KPt slots hold M Tb and KPt Tb)
     BOps<OT, RT> ub[NB];
+    if constexpr (Rec<D, C, OT>::FOLD) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) ub[nb].from(u[nb]);
+        for (int nb = 0; nb < NB; ++nb) ub[nb] = xb[nb];
+    } else {
+        float4v u[NB][RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {   // Tb is lower triangular: k-tiles 0..rt
+            float4v acc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = zero;
+            tile_chain_mma_nb<OT, CK, RT, NB>(acc, t.tb, rt, rt + 1, xb);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) u[nb][rt] = acc[nb];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) ub[nb].from(u[nb]);
+    }
     if constexpr (OUT) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {

@@ -47,17 +47,18 @@ def test_status_strings(lib):
 
 def test_workspace_size(lib):
     ws = lib.kda_chunk_fwd_workspace_bytes
-    # B=1 T=32768 H=32 d=128 C=64 bf16: 512 chunks x 32 heads x record; a record
-    # holds three C x d and two C x C fp16 tiles plus d fp32 decays, in whole KiB
-    rec = (3 * 64 * 128 + 2 * 64 * 64) * 2 + 4 * 128
+    # B=1 T=32768 H=32 d=128 C=64 bf16: 512 chunks x 32 heads x record; a bf16
+    # record holds three C x d and one C x C fp16 tiles (the products with T diag
+    # beta folded in) plus d fp32 decays, in whole KiB
+    rec = (3 * 64 * 128 + 64 * 64) * 2 + 4 * 128
     rec = (rec + 1023) // 1024 * 1024
     # plus, with 32 (sequence, head) chains cut into 8 segments, 3 * 8 - 3 fp32
     # d x d state planes per chain (end states, transition products, entering
     # states)
     assert ws(1, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 512 * 32 * rec + 21 * 32 * 128 * 128 * 4
     assert ws(1, 100, 2, 64, 64, 16, 0, kda.KDA_F32) > ws(1, 100, 2, 64, 64, 16, 0, kda.KDA_BF16)
-    # packed sequences add a chunk table and one partial chunk per sequence
-    assert ws(1, 1000, 2, 64, 64, 64, 5, kda.KDA_BF16) > ws(1, 1000, 2, 64, 64, 64, 0, kda.KDA_BF16)
+    # packed sequences add a chunk table and room for one partial chunk per sequence
+    assert ws(1, 1000, 2, 64, 64, 64, 5, kda.KDA_BF16) > ws(1, 1000, 2, 64, 64, 64, 1, kda.KDA_BF16)
     assert ws(1, 100, 2, 64, 32, 64, 0, kda.KDA_BF16) == 0      # dk != dv
     assert ws(1, 100, 2, 96, 96, 64, 0, kda.KDA_BF16) == 0      # unsupported d
     assert ws(1, 100, 2, 64, 64, 48, 0, kda.KDA_BF16) == 0      # unsupported chunk
