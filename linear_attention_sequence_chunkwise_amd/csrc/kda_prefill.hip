@@ -268,13 +268,18 @@ __global__ __launch_bounds__(256) void kda_intra(
     const int c0 = 2 * cp;
     float g0[16], g1[16], k0v[16], k1v[16], q0v[16], q1v[16];
     if (task) {
+        // With NP >= 64 a wave holds one sub-block, so its row offsets are
+        // wave-uniform: scalar registers, and every load is a scalar row base
+        // plus this lane's fixed column offset.
+        const int Ir = NP >= 64 ? __builtin_amdgcn_readfirstlane(I) : I;
+        const size_t head0 = ((size_t)tok0 * H + h) * D;
+        const unsigned lc = (unsigned)c0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const int r = min(16 * I + j, len - 1);
-            const size_t off = ((size_t)(tok0 + r) * H + h) * D + c0;
-            const float2 gg = *reinterpret_cast<const float2*>(g + off);
-            const float2 kk = load2(k + off);
-            const float2 qq = load2(q + off);
+            const size_t ro = head0 + (size_t)min(16 * Ir + j, len - 1) * ((size_t)H * D);
+            const float2 gg = *reinterpret_cast<const float2*>(g + ro + lc);
+            const float2 kk = load2(k + ro + lc);
+            const float2 qq = load2(q + ro + lc);
             g0[j] = gg.x; g1[j] = gg.y;
             k0v[j] = kk.x; k1v[j] = kk.y;
             q0v[j] = qq.x; q1v[j] = qq.y;
@@ -292,12 +297,17 @@ __global__ __launch_bounds__(256) void kda_intra(
                 }
             }
         }
+        if (len < C) {   // a partial chunk: the rows past its end (copies of its last row) are zeroed
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (16 * I + j >= len) {
+                    g0[j] = g1[j] = k0v[j] = k1v[j] = q0v[j] = q1v[j] = 0.f;
+                }
+            }
+        }
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            if (16 * I + j >= len) {
-                g0[j] = g1[j] = k0v[j] = k1v[j] = q0v[j] = q1v[j] = 0.f;
-            }
             s0 += g0[j];
             s1 += g1[j];
         }
@@ -484,14 +494,8 @@ __global__ __launch_bounds__(256) void kda_intra(
             }
         }
     }
-    // zero A above the diagonal blocks
-    #pragma unroll
-    for (int it_ = 0; it_ < (C * C + 255) / 256; ++it_) {   // compile-time trip count
-        const int idx = tid + 256 * it_;
-        if (idx >= C * C) break;
-        const int r = idx / C, col = idx - r * C;
-        if ((col >> 4) > (r >> 4)) sm.A[r * LDA + col] = to_ot<OT>(0.f);
-    }
+    // (A above the diagonal blocks is never read: the solve takes the diagonal
+    // blocks' lower parts and the blocks below them)
     lds_barrier();   // the k.k^T Gram's reads of kl are done
     if (task) {
 #pragma unroll
@@ -547,14 +551,16 @@ __global__ __launch_bounds__(256) void kda_intra(
                 sm.u.s.M[(16 * Ib + 4 * lq + j) * LDA + 16 * Jb + l16] = to_ot<OT>(macc[i][j]);
         }
     }
-    #pragma unroll
-    for (int it_ = 0; it_ < (C * C + 255) / 256; ++it_) {   // compile-time trip count
-        const int idx = tid + 256 * it_;
-        if (idx >= C * C) break;   // zero the upper blocks of M and T
-        const int r = idx / C, col = idx - r * C;
-        if ((col >> 4) > (r >> 4)) {
-            sm.u.s.M[r * LDA + col] = to_ot<OT>(0.f);
-            sm.u.s.T[r * LDT + col] = 0.f;
+    if constexpr (!R::FOLD) {   // whole rows of M and T are stored: zero their upper blocks
+        #pragma unroll
+        for (int it_ = 0; it_ < (C * C + 255) / 256; ++it_) {   // compile-time trip count
+            const int idx = tid + 256 * it_;
+            if (idx >= C * C) break;
+            const int r = idx / C, col = idx - r * C;
+            if ((col >> 4) > (r >> 4)) {
+                sm.u.s.M[r * LDA + col] = to_ot<OT>(0.f);
+                sm.u.s.T[r * LDT + col] = 0.f;
+            }
         }
     }
     if (wave < NB && lane < 16) {
@@ -653,7 +659,8 @@ __global__ __launch_bounds__(256) void kda_intra(
         // 32 b + 16..31 side by side that is one 16-byte group of the kperm
         // order (stored 32 b + 8 lq .. + 7).  A fragments of Tb^T: rows j of
         // tile jt, the tokens i of k-step ks in the kperm order (Tb_ij = 0 for
-        // i < j: steps below jt / 2 are zero).
+        // i < j: steps below jt / 2 are zero).  The upper blocks of T and M in
+        // LDS hold stale Gram operands: reads of them are masked to zero.
         half8 ta[NB][NKS];
 #pragma unroll
         for (int jt = 0; jt < NB; ++jt)
@@ -665,7 +672,7 @@ __global__ __launch_bounds__(256) void kda_intra(
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) {
                     const int i = group_col<OT>(32 * ks + 8 * lq, e);
-                    a[e] = i < C ? sm.u.s.T[i * LDT + j] * bj : 0.f;
+                    a[e] = i < C && (i >> 4) >= jt ? sm.u.s.T[i * LDT + j] * bj : 0.f;
                 }
                 ta[jt][ks] = __builtin_bit_cast(half8, pack16(a));
             }
@@ -710,7 +717,7 @@ __global__ __launch_bounds__(256) void kda_intra(
 #pragma unroll
                     for (int e = 0; e < EPV; ++e) {
                         const int i = group_col<OT>(32 * ks + 8 * lq, e);
-                        mv[e] = i < C ? (float)sm.u.s.M[r * LDA + i] : 0.f;
+                        mv[e] = i < C && (i >> 4) <= rt ? (float)sm.u.s.M[r * LDA + i] : 0.f;
                     }
                     bm[ks] = __builtin_bit_cast(half8, pack16(mv));
                 }
@@ -1256,10 +1263,14 @@ __device__ __forceinline__ void wide_chunk(const WideTiles<D, C, OT, OUT>& t,
         for (int nb = 0; nb < NB; ++nb) {
             float4v vv = zero;
             if (nb < NVB) {
+                // every row of the region holds data (rows past the chunk repeat
+                // its last row): read unconditionally, then select, so that the
+                // reads are not split into branches that each wait for LDS
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * rt + 4 * lq + j;
-                    vv[j] = r < len ? to_f32(vl[r * 16 * NVB + 16 * nb + l16]) : 0.f;
+                    const float x = to_f32(vl[r * 16 * NVB + 16 * nb + l16]);
+                    vv[j] = r < len ? x : 0.f;
                 }
             }
             x[nb][rt] = vv - acc[nb];
