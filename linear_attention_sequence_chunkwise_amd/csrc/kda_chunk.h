@@ -70,6 +70,28 @@ __device__ __forceinline__ float2 load2(const bf16_t* p) {
     const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
     return float2{__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u)};
 }
+// Raw buffer view of a tensor region: loads at a scalar byte offset (a row,
+// the same for the whole wave) plus this lane's byte offset, with no vector
+// address arithmetic.  Every offset used must stay below 2^31 bytes.
+struct BufView {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ explicit BufView(const void* base)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                              0x00020000)) {}
+    // two consecutive inputs as floats (fp32 pair, or bf16 pair from 32 bits)
+    __device__ __forceinline__ float2 pair(float*, unsigned lane_off, int row_off) const {
+        // taken whole as 64 bits: indexing the builtin's two-element result
+        // directly compiled to a single 32-bit load with both elements equal
+        const unsigned long long w =
+            __builtin_bit_cast(unsigned long long, __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, row_off, 0));
+        return float2{__builtin_bit_cast(float, (uint32_t)w), __builtin_bit_cast(float, (uint32_t)(w >> 32))};
+    }
+    __device__ __forceinline__ float2 pair(bf16_t*, unsigned lane_off, int row_off) const {
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, row_off, 0);
+        return float2{__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u)};
+    }
+};
+
 __device__ __forceinline__ void unpack16(const u32x4& w, float (&e)[8]) {
     const uint32_t u[4] = {w[0], w[1], w[2], w[3]};
 #pragma unroll
@@ -90,6 +112,7 @@ __device__ __forceinline__ u32x4 pack16(const float (&x)[8]) {
     }
     return w;
 }
+
 __device__ __forceinline__ u32x4 pack16(const float (&x)[4]) {
     return __builtin_bit_cast(u32x4, float4v{x[0], x[1], x[2], x[3]});
 }

@@ -264,22 +264,32 @@ __global__ __launch_bounds__(256) void kda_intra(
     constexpr int NP = D / 2;
     const int cp = tid % NP;
     const int I = tid / NP;
-    const bool task = I < NB;
+    const bool task = NP * NB >= 256 || I < NB;   // every thread has a task when NP NB >= 256
     const int c0 = 2 * cp;
     float g0[16], g1[16], k0v[16], k1v[16], q0v[16], q1v[16];
     if (task) {
         // With NP >= 64 a wave holds one sub-block, so its row offsets are
         // wave-uniform: scalar registers, and every load is a scalar row base
         // plus this lane's fixed column offset.
+        // buffer views from the chunk's first row of this head; a row lies
+        // H D elements further (the plan keeps C H D fp32 below 2^31 bytes)
         const int Ir = NP >= 64 ? __builtin_amdgcn_readfirstlane(I) : I;
         const size_t head0 = ((size_t)tok0 * H + h) * D;
-        const unsigned lc = (unsigned)c0;
+        const BufView bg(g + head0), bk(k + head0), bq(q + head0);
+        const unsigned lg = (unsigned)c0 * (unsigned)sizeof(float);
+        const unsigned li = (unsigned)c0 * (unsigned)sizeof(IT);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const size_t ro = head0 + (size_t)min(16 * Ir + j, len - 1) * ((size_t)H * D);
-            const float2 gg = *reinterpret_cast<const float2*>(g + ro + lc);
-            const float2 kk = load2(k + ro + lc);
-            const float2 qq = load2(q + ro + lc);
+            const int ro = min(16 * Ir + j, len - 1) * H * D;
+            // the row offset is a scalar offset when wave-uniform, else part
+            // of the lane's offset (a vector scalar offset would be serialised)
+            const int sg = NP >= 64 ? ro * (int)sizeof(float) : 0;
+            const int si = NP >= 64 ? ro * (int)sizeof(IT) : 0;
+            const unsigned vg = NP >= 64 ? lg : lg + (unsigned)(ro * (int)sizeof(float));
+            const unsigned vi = NP >= 64 ? li : li + (unsigned)(ro * (int)sizeof(IT));
+            const float2 gg = bg.pair((float*)nullptr, vg, sg);
+            const float2 kk = bk.pair((IT*)nullptr, vi, si);
+            const float2 qq = bq.pair((IT*)nullptr, vi, si);
             g0[j] = gg.x; g1[j] = gg.y;
             k0v[j] = kk.x; k1v[j] = kk.y;
             q0v[j] = qq.x; q1v[j] = qq.y;
@@ -363,11 +373,11 @@ __global__ __launch_bounds__(256) void kda_intra(
         // a_j = prod_{j'<=j} alpha, b_j = prod_{j'>j} alpha, both channels of the
         // pair at once: one 4-byte (fp16) or 8-byte (fp32) LDS store per row
         auto store2 = [](OT* p, float x0, float x1) {
-            if constexpr (sizeof(OT) == 2)
-                *reinterpret_cast<uint32_t*>(p) = __builtin_bit_cast(uint16_t, (_Float16)x0) |
-                                                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x1) << 16);
-            else
+            if constexpr (sizeof(OT) == 2) {
+                *reinterpret_cast<half2v*>(p) = half2v{(_Float16)x0, (_Float16)x1};   // one packed conversion
+            } else {
                 *reinterpret_cast<float2*>(p) = float2{x0, x1};
+            }
         };
         float a0 = 1.f, a1 = 1.f;
 #pragma unroll
@@ -563,9 +573,10 @@ __global__ __launch_bounds__(256) void kda_intra(
             }
         }
     }
-    if (wave < NB && lane < 16) {
-        // column `lane` of (I + A_II)^-1 by forward substitution (4 partial sums)
-        const int I = wave, jc = lane;
+    if (wave == 0 && lane < 16 * NB) {
+        // column jc of (I + A_II)^-1 by forward substitution (4 partial sums);
+        // one wave takes all diagonal blocks, 16 lanes each
+        const int I = lane >> 4, jc = lane & 15;
         const OT* Ab = &sm.A[(16 * I) * LDA + 16 * I];
         float x[16];
 #pragma unroll
@@ -2713,6 +2724,8 @@ bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf
     // one 256-thread workgroup per (chunk, head) in a 1-D grid: the dispatch's
     // work-item count must stay below 2^32
     if (nchunk * H >= (1LL << 24)) return false;
+    // K1 addresses a chunk's rows of g by 32-bit byte offsets from its first row
+    if ((long long)C * H * D * (long long)sizeof(float) >= (1LL << 31)) return false;
     plan->nchunk_max = (int)nchunk;
     plan->chunk_rec_bytes = rec_bytes(D, C, bf16);
     size_t off = 0;
