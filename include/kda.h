@@ -59,8 +59,9 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL_ARG = 1,     /* a required pointer is NULL or misaligned   */
     KDA_ERR_BAD_SHAPE = 2,    /* a size is negative/zero where it may not be,
-                                 sizes are inconsistent, or a prefill has
-                                 2^24 or more (chunk, head) pairs            */
+                                 sizes are inconsistent, a prefill has 2^24
+                                 or more (chunk, head) pairs, or
+                                 chunk * H * dk * 4 reaches 2^31 bytes       */
     KDA_ERR_UNSUPPORTED = 3,  /* dk, dv, chunk or dtype outside the built set */
     KDA_ERR_BAD_DTYPE = 4,    /* dtype code not in kda_dtype                 */
     KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required     */

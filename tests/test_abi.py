@@ -67,6 +67,9 @@ def test_workspace_size(lib):
     # at most 2^24 - 1 (chunk, head) pairs: one workgroup each in a 1-D grid
     assert ws(1, 64 * ((1 << 22) - 1), 4, 64, 64, 64, 0, kda.KDA_BF16) > 0
     assert ws(1, 64 * (1 << 22), 4, 64, 64, 64, 0, kda.KDA_BF16) == 0
+    # K1 reads a chunk's rows through 32-bit byte offsets: chunk * H * dk * 4 < 2^31
+    assert ws(1, 64, (1 << 16) - 1, 128, 128, 64, 0, kda.KDA_BF16) > 0
+    assert ws(1, 64, 1 << 16, 128, 128, 64, 0, kda.KDA_BF16) == 0
 
 
 def test_chain_segments(lib):
