@@ -8,7 +8,7 @@ fp32 gates, zero initial state.  The decode leg (reported under "decode") is
 fresh inputs per step.  All inputs are synthetic (seeded) and resident in HBM
 before timing starts.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 20]
 """
 from __future__ import annotations
 
@@ -38,7 +38,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

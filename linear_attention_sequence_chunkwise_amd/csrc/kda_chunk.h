@@ -113,6 +113,13 @@ __device__ __forceinline__ u32x4 pack16(const float (&x)[8]) {
     return w;
 }
 
+// The same rounding for plain fp32 values (matrix-core results): built as a
+// vector, one packed conversion per pair.
+__device__ __forceinline__ u32x4 pack16_acc(const float (&x)[8]) {
+    const half8 h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3],
+                     (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]};
+    return __builtin_bit_cast(u32x4, h);
+}
 __device__ __forceinline__ u32x4 pack16(const float (&x)[4]) {
     return __builtin_bit_cast(u32x4, float4v{x[0], x[1], x[2], x[3]});
 }

@@ -472,18 +472,21 @@ __global__ __launch_bounds__(256) void kda_intra(
     // until the Gram operands are dead.
     constexpr int NT = NB * (NB + 1) / 2;
     constexpr int TPW = (NT + 3) / 4;
-    auto gram = [&](int Ib, int Jb) {
+    // F_IJ is exactly one for adjacent sub-blocks (J = I - 1): no factor there
+    auto gram_f = [&](int Ib, int Jb, auto scaled) {
         float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D; ks += mm::KS) {
             const int kk = ks + lq * mm::KPL;
             typename mm::frag af = mm::load(sm.u.g.kl, LDK, 16 * Ib + l16, kk);
             typename mm::frag bf = mm::load(sm.u.g.kr, LDK, 16 * Jb + l16, kk);
-            const typename mm::frag ff = mm::load(sm.F + (Ib * NB + Jb) * D, 0, 0, kk);
-            bf = bf * ff;
+            if constexpr (decltype(scaled)::value) bf = bf * mm::load(sm.F + (Ib * NB + Jb) * D, 0, 0, kk);
             acc = mm::mma(af, bf, acc);
         }
         return acc;
+    };
+    auto gram = [&](int Ib, int Jb) {
+        return Jb + 1 == Ib ? gram_f(Ib, Jb, std::false_type()) : gram_f(Ib, Jb, std::true_type());
     };
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -708,7 +711,7 @@ __global__ __launch_bounds__(256) void kda_intra(
                         for (int e = 0; e < 4; ++e) w[4 * hh + e] = acc[e];
                     }
                     *reinterpret_cast<vec*>(rec + R::KPt + swz<OT, R::CK>(16 * cb + l16, 32 * b + 8 * lq)) =
-                        pack16(w);
+                        pack16_acc(w);
                 }
             }
         }
@@ -747,7 +750,7 @@ __global__ __launch_bounds__(256) void kda_intra(
 #pragma unroll
                         for (int e = 0; e < 4; ++e) w[4 * hh + e] = acc[e];
                     }
-                    *reinterpret_cast<vec*>(rec + R::M + swz<OT, R::CK>(r, 32 * b + 8 * lq)) = pack16(w);
+                    *reinterpret_cast<vec*>(rec + R::M + swz<OT, R::CK>(r, 32 * b + 8 * lq)) = pack16_acc(w);
                 }
             }
         }
