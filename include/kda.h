@@ -140,9 +140,11 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv,
  * the segments' local end states and transition products computed in
  * parallel, combined, and every segment then run from its true starting
  * state (only for B equal-length rows, when B*H is small against the CU
- * count).  Both give the chunk form's result; they differ by rounding only.
- * 0 if the sizes are invalid or unsupported.  Informational: nothing needs
- * it to make a call. */
+ * count); -1 = one workgroup per (sequence, head) runs its whole chain over
+ * all dv columns (when there are at least 128 chains, packed sequences
+ * included, longest sequences first).  All give the chunk form's result; they
+ * differ by rounding only.  0 if the sizes are invalid or unsupported.
+ * Informational: nothing needs it to make a call. */
 int kda_chunk_fwd_segments(int B, int T, int H, int dk, int dv, int chunk,
                            int num_seqs, kda_dtype qkv_dtype);
 

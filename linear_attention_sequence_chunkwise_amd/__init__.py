@@ -167,7 +167,9 @@ def kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torc
 
 
 def kda_chunk_fwd_segments(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torch.bfloat16):
-    """Segments per sequence of the prefill's chain for these sizes (1: none)."""
+    """How the prefill's chain runs for these sizes: n > 1 segments per
+    sequence, 1 the per-slice chain, -1 one workgroup per whole (sequence,
+    head) chain, 0 unsupported sizes."""
     code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
     return int(load_library().kda_chunk_fwd_segments(B, T, H, dk, dv, chunk, num_seqs, code))
 

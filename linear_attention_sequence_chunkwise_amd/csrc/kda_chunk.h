@@ -17,10 +17,11 @@ template <typename OT>
 using InputOf = typename std::conditional<sizeof(OT) == 2, bf16_t, float>::type;
 
 // K0 launcher (packed sequences): chunk offsets per sequence and one
-// ChunkInfo per chunk, at most cap entries.
+// ChunkInfo per chunk, at most cap entries; order (or null): the sequences by
+// chunk count, longest first.
 struct ChunkInfo;
 hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int C, int cap, int* chunk_off,
-                              ChunkInfo* table, hipStream_t stream);
+                              ChunkInfo* table, int* order, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Matrix-core fragment helpers.  Operands are staged in LDS as row-major

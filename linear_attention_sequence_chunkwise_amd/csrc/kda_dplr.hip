@@ -648,7 +648,7 @@ static hipError_t launch_dplr_dc(const DplrArgs& a, const PrefillPlan& plan) {
             table = reinterpret_cast<ChunkInfo*>(ws + plan.off_table +
                                                  ((size_t)(a.N + 1) * sizeof(int) + 255) / 256 * 256);
             if (hipError_t e = launch_chunk_table(a.cu_seqlens, a.N, a.T, C, plan.nchunk_max,
-                                                  chunk_off, table, a.stream))
+                                                  chunk_off, table, nullptr, a.stream))
                 return e;
         }
         if (plan.nchunk_max > 0) {

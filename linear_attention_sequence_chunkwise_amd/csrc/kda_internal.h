@@ -67,6 +67,8 @@ struct PrefillPlan {
     size_t off_table;      // chunk table (varlen only)
     size_t off_records;    // chunk-head records
     int nseg, seg_len;     // segments per sequence of the chain, chunks per segment
+    bool whole;            // chain: one workgroup per (sequence, head) over all columns
+    size_t off_order;      // sequences by length, longest first (varlen only)
     size_t off_seg;        // segment states (nseg > 1 only)
     size_t total;
 };

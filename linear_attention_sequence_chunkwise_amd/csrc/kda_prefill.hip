@@ -110,15 +110,20 @@ static size_t rec_bytes(int D, int C, bool bf16) {
 // ---------------------------------------------------------------------------
 // K0: chunk table for packed sequences.  One workgroup.
 //   chunk_off[n] = sum_{m<n} ceil(len_m / C),  chunk_off[N] = total chunks;
-//   table[chunk_off[n] + c] = {cu[n] + c*C, min(C, len_n - c*C)}.
+//   table[chunk_off[n] + c] = {cu[n] + c*C, min(C, len_n - c*C)};
+//   order (optional): the sequences by chunk count, longest first (ties by
+//   index; the identity beyond kOrderMax sequences or for malformed cu).
 // ---------------------------------------------------------------------------
+constexpr int kOrderMax = 1024;
 __global__ __launch_bounds__(256) void kda_chunk_table(const int32_t* __restrict__ cu, int N,
                                                        int T, int C, int cap,
                                                        int* __restrict__ chunk_off,
-                                                       ChunkInfo* __restrict__ table) {
+                                                       ChunkInfo* __restrict__ table,
+                                                       int* __restrict__ order) {
     __shared__ int s_scan[256];
     __shared__ int s_base;
     __shared__ int s_bad;
+    __shared__ int s_nch[kOrderMax];
     const int tid = threadIdx.x;
     if (tid == 0) {
         s_base = 0;
@@ -132,6 +137,8 @@ __global__ __launch_bounds__(256) void kda_chunk_table(const int32_t* __restrict
     __syncthreads();
     if (s_bad) {
         for (int n = tid; n <= N; n += 256) chunk_off[n] = 0;
+        if (order)
+            for (int n = tid; n < N; n += 256) order[n] = n;
         return;
     }
     for (int base = 0; base < N; base += 256) {
@@ -168,6 +175,20 @@ __global__ __launch_bounds__(256) void kda_chunk_table(const int32_t* __restrict
         __syncthreads();
     }
     if (tid == 0) chunk_off[N] = min(s_base, cap);
+    if (order) {
+        if (N > kOrderMax) {
+            for (int n = tid; n < N; n += 256) order[n] = n;
+            return;
+        }
+        for (int n = tid; n < N; n += 256) s_nch[n] = (max(cu[n + 1] - cu[n], 0) + C - 1) / C;
+        __syncthreads();
+        for (int n = tid; n < N; n += 256) {
+            const int mine = s_nch[n];
+            int rank = 0;
+            for (int m = 0; m < N; ++m) rank += s_nch[m] > mine || (s_nch[m] == mine && m < n);
+            order[rank] = n;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1383,13 +1404,19 @@ struct SegSmem {
 // at that chunk's start has published every wave's sums, and the gate
 // entries, loaded at that start, have had the chunk's compute to land.  The
 // last chunk is finished after one more barrier.
+//
+// With nseg = 1 (pass 3 only) a workgroup runs its (sequence, head) from S0 to
+// the end: the form for chains too many to split.  cu / chunk_off (or null):
+// packed sequences, in the order given by order (longest first, so that the
+// longest chains start first).
 template <int D, int C, typename OT, typename IT, bool OUT, bool EPI = false>
 __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
     int T, int H, int N_seq, int nch_seq, int L, int nseg, float scale,
     const IT* __restrict__ v, const float* __restrict__ s0, const char* __restrict__ records,
     float* __restrict__ o, float* __restrict__ sT, float* __restrict__ seg,
-    const IT* __restrict__ gate = nullptr, const float* __restrict__ weight = nullptr,
-    float eps = 0.f) {
+    const IT* __restrict__ gate, const float* __restrict__ weight, float eps,
+    const int32_t* __restrict__ cu, const int* __restrict__ chunk_off,
+    const int* __restrict__ order) {
     static_assert(!EPI || OUT, "the epilogue belongs to the pass with outputs");
     typedef SegShape<D, OUT> SS;
     typedef WideTiles<D, C, OT, OUT> WT;
@@ -1414,10 +1441,23 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
         nh = 8 * (j / nsp) + (lg & 7);
     }
     if (nh >= N_seq * H) return;
-    const int n = nh / H, h = nh % H;
-    const int c0 = s * L, c1 = min(c0 + L, nch_seq);
+    const int n = order ? order[nh / H] : nh / H, h = nh % H;
+    // this sequence's tokens and chunk records
+    int seq_tok0, seq_len, first, nch;
+    if (cu) {
+        seq_tok0 = cu[n];
+        seq_len = cu[n + 1] - seq_tok0;
+        first = chunk_off[n];
+        nch = max(min(chunk_off[n + 1], chunk_off[N_seq]) - first, 0);
+    } else {
+        seq_tok0 = n * T;
+        seq_len = T;
+        first = n * nch_seq;
+        nch = nch_seq;
+    }
+    const int c0 = s * L, c1 = min(c0 + L, nch);
     const size_t plane = (size_t)N_seq * H * D * D;
-    const size_t sbase = (size_t)nh * D * D;
+    const size_t sbase = ((size_t)n * H + h) * D * D;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
 
     // this wave's column blocks: pass 1, columns 16 wave.. of the run of V
@@ -1429,7 +1469,8 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
     for (int b = 0; b < SS::NCB; ++b) {
         const bool ident = b >= SS::NVB;
         const int col = (ident ? 16 * wave : cbase + 16 * b) + l16;
-        const float* src = OUT ? seg + seg_plane_in(nseg, s) * plane : (!ident && s == 0 ? s0 : nullptr);
+        const float* src = OUT ? (nseg == 1 ? s0 : seg + seg_plane_in(nseg, s) * plane)
+                               : (!ident && s == 0 ? s0 : nullptr);
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
@@ -1442,7 +1483,7 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
 
     // record KiB copies of chunk c into image buffer bi, spread over the waves
     auto copy_record = [&](int c, int bi) {
-        const char* rec = records + ((size_t)(n * nch_seq + c) * H + h) * R::bytes;
+        const char* rec = records + ((size_t)(first + c) * H + h) * R::bytes;
         const uint32_t base = lds_addr(sm.img[bi]);
         for (int j = wave; j < WT::KIB; j += SS::NW)
             dma16(rec + (size_t)WT::rec_kib(j) * 1024 + lane * 16, base + j * 1024);
@@ -1504,7 +1545,7 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
     };
     // this wave's value columns of chunk c (row 0) in global memory
     auto vsrc = [&](int c) -> const IT* {
-        return v + ((size_t)(n * T + c * C) * H + h) * D + cbase;
+        return v + ((size_t)(seq_tok0 + c * C) * H + h) * D + cbase;
     };
     const size_t vstride = (size_t)H * D;
     const IT* vl = reinterpret_cast<const IT*>(sm.vals[wave]);
@@ -1514,11 +1555,11 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
     __builtin_amdgcn_s_waitcnt(0x0F70);
     if (c0 < c1) {
         copy_record(c0, 0);
-        ValueCopy<C, IT, SS::NVB>::issue(vsrc(c0), vstride, min(C, T - c0 * C), vl_lds);
+        ValueCopy<C, IT, SS::NVB>::issue(vsrc(c0), vstride, min(C, seq_len - c0 * C), vl_lds);
     }
     for (int c = c0; c < c1; ++c) {
         const int bi = (c - c0) & 1;
-        const int tok0 = n * T + c * C, len = min(C, T - c * C);
+        const int tok0 = seq_tok0 + c * C, len = min(C, seq_len - c * C);
         // this wave's copies of chunk c have landed; after the barrier every
         // wave's have, and every wave is done with chunk c - 1, whose record
         // buffer the copies of chunk c + 1 then refill
@@ -1537,7 +1578,7 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
         const WT tiles(sm.img[bi]);
         wide_chunk<D, C, OT, IT, OUT, SS::NCB, SS::NVB, EPI>(
             tiles, st, vl, vl_lds, c + 1 < c1 ? vsrc(c + 1) : nullptr, vstride,
-            min(C, T - (c + 1) * C), cbase, tok0, len, H, h, scale, o, oo);
+            min(C, seq_len - (c + 1) * C), cbase, tok0, len, H, h, scale, o, oo);
         if constexpr (EPI) {
             // the previous chunk's rows: every wave's sums were published by
             // the barrier at this chunk's start
@@ -2700,6 +2741,7 @@ static bool seg_fits(int D, int C, bool bf16) {
 // at most kSegMax segments (the combine is nseg - 2 dependent steps).
 // nseg = 1: the per-slice chain kernels run instead.
 constexpr int kSegCUs = 256, kSegMinChunks = 4, kSegMax = 32;
+constexpr int kWholeMinChains = 128;   // (sequence, head) chains for the one-workgroup-per-chain form
 // Returns the segment count the state planes are reserved for: the count
 // asked for before rounding the segment length, which never falls as nch
 // grows (the count used, nseg, can: 32 chunks make 8 segments of 4, 33 make
@@ -2733,18 +2775,25 @@ bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf
     plan->chunk_rec_bytes = rec_bytes(D, C, bf16);
     size_t off = 0;
     plan->off_table = off;
+    plan->off_order = off;
     if (varlen) {
         off += ((size_t)(N + 1) * sizeof(int) + 255) / 256 * 256;
         off += ((size_t)nchunk * sizeof(ChunkInfo) + 255) / 256 * 256;
+        plan->off_order = off;
+        off += ((size_t)N * sizeof(int) + 255) / 256 * 256;
     }
     plan->off_records = off;
     off += ((size_t)nchunk * H * plan->chunk_rec_bytes + 255) / 256 * 256;
     plan->nseg = 1;
     plan->seg_len = 0;
+    const bool fits = seg_fits(D, C, bf16);
     int reserve = 1;
     if (!varlen)
-        reserve = seg_split((long long)N * H, (T + C - 1) / C, seg_fits(D, C, bf16), &plan->nseg,
-                            &plan->seg_len);
+        reserve = seg_split((long long)N * H, (T + C - 1) / C, fits, &plan->nseg, &plan->seg_len);
+    // chains that cannot be cut into segments (too many to share the CUs, or
+    // packed sequences) but still fill half the chip run one workgroup per
+    // (sequence, head) over all columns
+    plan->whole = fits && plan->nseg == 1 && (long long)N * H >= kWholeMinChains;
     plan->off_seg = off;
     if (reserve > 1) off += (size_t)seg_planes(reserve) * N * H * D * D * sizeof(float);
     plan->total = off;
@@ -2808,9 +2857,9 @@ static hipError_t launch_inter(const PrefillArgs& a, const PrefillPlan& plan, in
 }
 
 hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int C, int cap, int* chunk_off,
-                              ChunkInfo* table, hipStream_t stream) {
+                              ChunkInfo* table, int* order, hipStream_t stream) {
     hipLaunchKernelGGL(kda_chunk_table, dim3(1), dim3(256), 0, stream, cu, N, T, C, cap, chunk_off,
-                       table);
+                       table, order);
     return hipGetLastError();
 }
 
@@ -2826,8 +2875,9 @@ static hipError_t launch_records(const PrefillArgs& a, const PrefillPlan& plan, 
         *chunk_off = reinterpret_cast<int*>(ws + plan.off_table);
         *table = reinterpret_cast<ChunkInfo*>(
             ws + plan.off_table + ((size_t)(a.N + 1) * sizeof(int) + 255) / 256 * 256);
+        int* order = plan.whole ? reinterpret_cast<int*>(ws + plan.off_order) : nullptr;
         if (hipError_t e = launch_chunk_table(a.cu_seqlens, a.N, a.T, C, plan.nchunk_max,
-                                              *chunk_off, *table, a.stream))
+                                              *chunk_off, *table, order, a.stream))
             return e;
     }
     if (plan.nchunk_max > 0) {
@@ -2847,7 +2897,9 @@ static hipError_t launch_records(const PrefillArgs& a, const PrefillPlan& plan, 
 }
 
 int prefill_chain_segments(const PrefillPlan& plan) {
-    return plan.nseg > 1 && !inter_override() ? plan.nseg : 1;
+    if (inter_override()) return 1;
+    if (plan.nseg > 1) return plan.nseg;
+    return plan.whole ? -1 : 1;
 }
 
 // Passes 1-3 of the segment-parallel chain (plan.nseg > 1), with the output
@@ -2872,7 +2924,8 @@ static hipError_t launch_segmented(const PrefillArgs& a, const PrefillPlan& plan
     hipLaunchKernelGGL(k1, dim3((unsigned)((NH + 7) / 8 * 8 * (nseg - 1))), dim3(64 * SegShape<D, false>::NW),
                        smem1, a.stream, a.T, a.H, a.N, nch_seq, L, nseg, a.scale, (const IT*)a.v,
                        a.s0, rec, (float*)nullptr, (float*)nullptr, seg, (const IT*)nullptr,
-                       (const float*)nullptr, 0.f);
+                       (const float*)nullptr, 0.f, (const int32_t*)nullptr, (const int*)nullptr,
+                       (const int*)nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = hipFuncSetAttribute((const void*)kda_seg_combine<D>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)seg_combine_smem<D>());
@@ -2882,7 +2935,28 @@ static hipError_t launch_segmented(const PrefillArgs& a, const PrefillPlan& plan
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k3, dim3((unsigned)(NH * nseg)), dim3(64 * SegShape<D, true>::NW), smem3,
                        a.stream, a.T, a.H, a.N, nch_seq, L, nseg, a.scale, (const IT*)a.v, a.s0,
-                       rec, a.o, a.sT, seg, (const IT*)a.epi.gate, a.epi.weight, a.epi.eps);
+                       rec, a.o, a.sT, seg, (const IT*)a.epi.gate, a.epi.weight, a.epi.eps,
+                       (const int32_t*)nullptr, (const int*)nullptr, (const int*)nullptr);
+    return hipGetLastError();
+}
+
+// One workgroup per (sequence, head) over all columns: the segment kernel's
+// pass with outputs run as a single segment from S0 (packed sequences in the
+// order K0 gives, longest first), with the epilogue fused when asked for.
+template <int D, int C, typename OT, typename IT>
+static hipError_t launch_whole(const PrefillArgs& a, const PrefillPlan& plan, int nch_seq,
+                               const int* chunk_off, const int* order) {
+    const bool varlen = a.cu_seqlens != nullptr;
+    const char* rec = (const char*)a.workspace + plan.off_records;
+    const int smem3 = (int)sizeof(SegSmem<D, C, OT, IT, true>);
+    auto k3 = a.epi.on ? kda_seg_chain<D, C, OT, IT, true, true> : kda_seg_chain<D, C, OT, IT, true>;
+    hipError_t e = hipFuncSetAttribute((const void*)k3, hipFuncAttributeMaxDynamicSharedMemorySize, smem3);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k3, dim3((unsigned)((long long)a.N * a.H)), dim3(64 * SegShape<D, true>::NW), smem3,
+                       a.stream, a.T, a.H, a.N, nch_seq, varlen ? plan.nchunk_max : nch_seq, 1, a.scale,
+                       (const IT*)a.v, a.s0, rec, a.o, a.sT, (float*)nullptr, (const IT*)a.epi.gate,
+                       a.epi.weight, a.epi.eps, varlen ? a.cu_seqlens : (const int32_t*)nullptr,
+                       varlen ? chunk_off : (const int*)nullptr, varlen ? order : (const int*)nullptr);
     return hipGetLastError();
 }
 
@@ -2927,6 +3001,10 @@ static hipError_t launch_dc(const PrefillArgs& a, const PrefillPlan& plan) {
         if constexpr (seg_fits_t<D, C, OT>()) {
             if (plan.nseg > 1 && !inter_override())
                 return launch_segmented<D, C, OT, IT>(a, plan, nch_seq);
+            if (plan.whole && !inter_override())
+                return launch_whole<D, C, OT, IT>(
+                    a, plan, nch_seq, chunk_off,
+                    reinterpret_cast<const int*>((const char*)a.workspace + plan.off_order));
         }
         if (hipError_t e = launch_slices<D, C, OT, IT>(a, plan, nch_seq, chunk_off)) return e;
         return a.epi.on ? launch_epilogue<D, IT>(a) : hipSuccess;
@@ -2977,6 +3055,7 @@ bool backward_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool b
     // the dispatch's work-item count must stay below 2^32
     if ((long long)plan->f.nchunk_max * H >= (1LL << 23)) return false;
     plan->f.nseg = 1;   // the backward runs its own chains: no segment states
+    plan->f.whole = false;
     plan->f.total = plan->f.off_seg;
     const size_t nch = (size_t)plan->f.nchunk_max;
     const size_t hist = (nch * H * (size_t)D * D * sizeof(float) + 255) / 256 * 256;

@@ -79,8 +79,14 @@ def test_chain_segments(lib):
     # at least 4 chunks per segment: 40 chunks allow 10, the CUs ask for 64
     assert seg(1, 40 * 64, 4, 64, 64, 64, 0, kda.KDA_BF16) == 10
     assert seg(2, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 4
-    assert seg(8, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 1     # 256 chains already
-    assert seg(1, 32768, 32, 128, 128, 64, 3, kda.KDA_BF16) == 1     # packed sequences
+    # 256 chains already: one workgroup per whole chain; also from 128 chains on
+    assert seg(8, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == -1
+    assert seg(4, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == 2
+    assert seg(5, 32768, 32, 128, 128, 64, 0, kda.KDA_BF16) == -1
+    assert seg(1, 32768, 127, 128, 128, 64, 0, kda.KDA_BF16) == 2
+    # packed sequences: the per-slice chain below 128 chains, whole chains from there
+    assert seg(1, 32768, 32, 128, 128, 64, 3, kda.KDA_BF16) == 1
+    assert seg(1, 32768, 32, 128, 128, 64, 4, kda.KDA_BF16) == -1
     assert seg(1, 7 * 64, 32, 128, 128, 64, 0, kda.KDA_BF16) == 1    # too short to split
     assert seg(1, 32768, 32, 128, 128, 64, 0, kda.KDA_F32) == 1      # fp32 d=128 C=64: LDS
     assert seg(1, 32768, 32, 64, 64, 64, 0, kda.KDA_F32) == 1        # fp32 d=64 C=64: LDS

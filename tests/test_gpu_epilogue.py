@@ -162,3 +162,21 @@ def test_prefill_epilogue_fused_equals_separate_pass(dtype, monkeypatch):
     o2, _ = run()
     torch.cuda.synchronize()
     assert rel_err(o1.cpu().numpy(), o2.double().cpu().numpy()) < TOL[dtype]
+
+
+@pytest.mark.parametrize("varlen", [False, True])
+def test_prefill_epilogue_fused_in_whole_chains(varlen):
+    """Epilogue fused into the one-workgroup-per-chain form (>= 128 chains),
+    fixed-length rows and packed sequences, against the oracle."""
+    H, D, chunk = 40, 64, 64
+    if varlen:
+        lens = [150, 0, 64, 1, 300, 77]
+        cu = kda_inputs.cu_seqlens_of(lens).cuda()
+        B, T, nseq = 1, sum(lens), len(lens)
+        d = kda_inputs.prefill_inputs(610, 1, T, H, D, D, torch.bfloat16, "cuda", s0_std=0.1,
+                                      n_states=nseq)
+    else:
+        cu, B, T, nseq = None, 4, 150, 0
+        d = kda_inputs.prefill_inputs(611, B, T, H, D, D, torch.bfloat16, "cuda", s0_std=0.1)
+    assert kda.kda_chunk_fwd_segments(B, T, H, D, D, chunk, nseq) == -1
+    check_prefill(d, chunk, epi_params(7, (B, T, H, D), torch.bfloat16), cu=cu)

@@ -264,3 +264,55 @@ def test_single_chain_many_segments():
     assert kda.kda_chunk_fwd_segments(B, T, H, D, D, 64) == 32
     d = make_prefill(90, B, T, H, D, torch.bfloat16, s0_std=0.1)
     check(d, 64)
+
+
+# ---- one workgroup per whole (sequence, head) chain ----
+
+@pytest.mark.parametrize("D,chunk,dtype", [(128, 64, torch.bfloat16), (64, 32, torch.bfloat16),
+                                           (32, 16, torch.float32)])
+@pytest.mark.parametrize("s0", [None, 0.1])
+def test_whole_chain(D, chunk, dtype, s0):
+    """B*H >= 128 chains too many to split: each runs whole in one workgroup
+    over all columns; every output and state against the oracle."""
+    B, T, H = 4, 3 * chunk + 7, 40
+    assert kda.kda_chunk_fwd_segments(B, T, H, D, D, chunk, 0, dtype) == -1
+    d = make_prefill(91 + D + chunk, B, T, H, D, dtype, s0_std=s0)
+    check(d, chunk)
+
+
+def _varlen_many(seed, H, D, dtype, lens):
+    cu = kda_inputs.cu_seqlens_of(lens).cuda()
+    d = make_prefill(seed, 1, sum(lens), H, D, dtype, s0_std=0.1, n_states=len(lens))
+    return d, cu
+
+
+def test_whole_chain_varlen():
+    """Packed sequences with >= 128 chains: whole chains, longest first, with
+    empty, one-token, partial-chunk and multi-chunk sequences."""
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(0, 300, size=37)] + [0, 1, 63, 64, 65, 700]
+    H, D = 4, 64
+    assert kda.kda_chunk_fwd_segments(1, sum(lens), H, D, D, 64, len(lens)) == -1
+    d, cu = _varlen_many(92, H, D, torch.bfloat16, lens)
+    check(d, 64, cu=cu)
+
+
+def test_whole_chain_equals_slice_chain(monkeypatch):
+    """The whole-chain form and the per-slice chain agree to rounding, for
+    packed sequences and in place (final_state aliasing initial_state)."""
+    lens = [200, 0, 64, 1000, 17, 333, 64 * 5, 90] * 5
+    H, D = 4, 128
+    d, cu = _varlen_many(93, H, D, torch.bfloat16, lens)
+    assert kda.kda_chunk_fwd_segments(1, sum(lens), H, D, D, 64, len(lens)) == -1
+    o1, S1 = run(d, 64, cu=cu)
+    st = d["S0"].clone()
+    o3, _ = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64,
+                              initial_state=st, final_state=st, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(S1, st)
+    monkeypatch.setenv("KDA_INTER_VARIANT", "reg16")
+    assert kda.kda_chunk_fwd_segments(1, sum(lens), H, D, D, 64, len(lens)) == 1
+    o2, S2 = run(d, 64, cu=cu)
+    tol = TOL[torch.bfloat16]
+    assert rel_err(o1.cpu().numpy(), o2.double().cpu().numpy()) < tol
+    assert rel_err(S1.cpu().numpy(), S2.double().cpu().numpy()) < tol
