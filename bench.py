@@ -241,6 +241,41 @@ def bench_prefill(kda, kda_inputs, steps, warmup, stream):
                 segments=kda.kda_chunk_fwd_segments(B, T, H, D, D, C))
 
 
+def bench_prefill_varlen(kda, kda_inputs, steps, warmup, stream):
+    """The packed-sequence layer: 16 sequences of seeded lengths U[256, 8192],
+    H=32, d=128, chunk 64, bf16, states reset at each boundary, per-sequence
+    final states out."""
+    d = kda_inputs.config_inputs(3, "cuda")
+    cu = d["cu_seqlens"]
+    B, T, H, D = d["q"].shape
+    N = cu.numel() - 1
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(B, T, H, D, D, 64, N), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty(B, T, H, D, device="cuda")
+    S = torch.empty(N, H, D, D, device="cuda")
+    torch.cuda.synchronize()
+
+    def call():
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64, cu_seqlens=cu,
+                          o=o, final_state=S, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    tm = StreamTimer(stream)
+    tm.start()
+    for _ in range(steps):
+        call()
+    ms = tm.stop() / steps
+    torch.cuda.synchronize()
+    nbytes = PREFILL_BYTES_PER_TOKEN_HEAD * T * H + N * H * D * D * 4   # + final states
+    return dict(ms_per_step=ms, value=T / (ms / 1e3), unit="tokens/s",
+                hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, algorithmic_bytes=nbytes,
+                chain_form=kda.kda_chunk_fwd_segments(B, T, H, D, D, 64, N),
+                workload="packed prefill: %d sequences, %d tokens (lengths U[256, 8192], seeded), "
+                         "H=32 dk=dv=128 chunk=64 bf16, per-sequence final states" % (N, T))
+
+
 def bench_prefill_prep(kda, kda_inputs, steps, warmup, stream, with_epilogue=False):
     """The prefill layer on raw inputs with the in-kernel preparation (q/k L2
     normalisation, beta from logits, gate activation) and optionally the
@@ -531,6 +566,8 @@ def main():
     pf_full_ms = bench_prefill_prep(kda, kda_inputs, args.steps, args.warmup, stream, True)
     print("prefill with preparation and epilogue %.4f ms/call" % pf_full_ms, file=sys.stderr,
           flush=True)
+    pf_var = bench_prefill_varlen(kda, kda_inputs, args.steps, args.warmup, stream)
+    print("packed prefill %.4f ms/call" % pf_var["ms_per_step"], file=sys.stderr, flush=True)
     th = pf["token_heads"]
     pf_bytes = PREFILL_BYTES_PER_TOKEN_HEAD * th
     pf_flops = prefill_flops_per_token_head() * th
@@ -625,7 +662,8 @@ def main():
             ms_per_step=pf_full_ms, value=pf["tokens"] / (pf_full_ms / 1e3), unit="tokens/s",
             overhead=pf_full_ms / pf["ms"] - 1.0,
             workload="as above plus the output epilogue (per-head RMSNorm, weight, sigmoid "
-                     "gate; one extra pass over o inside the call)"),
+                     "gate), fused into the chain's pass with outputs"),
+        "prefill_packed": pf_var,
         "cpu_baseline": cpu,
         "backward": bwd,
         "general_dplr": dplr,
