@@ -44,7 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-dplr", action="store_true")
-    ap.add_argument("--profile-target", choices=["prefill", "decode", "backward", "dplr", "copy"],
+    ap.add_argument("--no-packed", action="store_true")
+    ap.add_argument("--profile-target",
+                    choices=["prefill", "packed", "decode", "backward", "dplr", "copy"],
                     help="run only this workload a few times (target for rocprofv3) and exit")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="read rocprofv3 FETCH_SIZE/WRITE_SIZE runs of the three profile "
@@ -78,10 +80,12 @@ def measured_traffic(leg):
 
 
 LEG_SOURCES = {"prefill": ["kda_prefill.hip", "kda_chunk.h", "kda_common.h", "kda_internal.h"],
+               "packed": ["kda_prefill.hip", "kda_chunk.h", "kda_common.h", "kda_internal.h"],
                "decode": ["kda_decode.hip", "kda_common.h", "kda_internal.h"],
                "backward": ["kda_prefill.hip", "kda_chunk.h", "kda_common.h", "kda_internal.h"],
                "dplr": ["kda_dplr.hip", "kda_chunk.h", "kda_common.h", "kda_internal.h"]}
 LEG_KERNELS = {"prefill": ("kda_intra", "kda_seg_chain", "kda_seg_combine", "kda_inter"),
+               "packed": ("kda_chunk_table", "kda_intra", "kda_seg_chain", "kda_inter"),
                "decode": ("decode_step_kernel",),
                "backward": ("kda_intra", "kda_state_chain", "kda_bwd_chain", "kda_bwd_vprod",
                             "kda_bwd_intra"),
@@ -133,7 +137,9 @@ def traffic_from(d):
                 short = next((x for x in kern if x in k), None)
                 if short is None:
                     continue
-                if short == "kda_seg_chain":   # pass 1 (state runs) and pass 3 (outputs)
+                if short == "kda_seg_chain" and leg == "packed":
+                    short += " whole chains"
+                elif short == "kda_seg_chain":   # pass 1 (state runs) and pass 3 (outputs)
                     short += " pass 3" if ("true>" in k or "Lb1E" in k) else " pass 1"
                 per_kernel.setdefault(short, {})[ctr] = v * 1024.0 / scale[ctr]
         total = sum(v.get("FETCH_SIZE", 0.0) + v.get("WRITE_SIZE", 0.0)
@@ -166,6 +172,16 @@ def profile_target(kind):
         for _ in range(3):
             kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64, o=o,
                               final_state=S, workspace=ws)
+    elif kind == "packed":
+        d = kda_inputs.config_inputs(3, "cuda")
+        cu = d["cu_seqlens"]
+        B, T, H, D = d["q"].shape
+        N = cu.numel() - 1
+        ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(B, T, H, D, D, 64, N),
+                         dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64, cu_seqlens=cu,
+                              workspace=ws)
     elif kind == "dplr":
         c = kda_inputs.CONFIGS[2]
         B, T, H, D = c["B"], c["T"], c["H"], c["dk"]
@@ -566,8 +582,11 @@ def main():
     pf_full_ms = bench_prefill_prep(kda, kda_inputs, args.steps, args.warmup, stream, True)
     print("prefill with preparation and epilogue %.4f ms/call" % pf_full_ms, file=sys.stderr,
           flush=True)
-    pf_var = bench_prefill_varlen(kda, kda_inputs, args.steps, args.warmup, stream)
-    print("packed prefill %.4f ms/call" % pf_var["ms_per_step"], file=sys.stderr, flush=True)
+    pf_var = None
+    if not args.no_packed:
+        pf_var = bench_prefill_varlen(kda, kda_inputs, args.steps, args.warmup, stream)
+        pf_var["traffic"] = measured_traffic("packed")
+        print("packed prefill %.4f ms/call" % pf_var["ms_per_step"], file=sys.stderr, flush=True)
     th = pf["token_heads"]
     pf_bytes = PREFILL_BYTES_PER_TOKEN_HEAD * th
     pf_flops = prefill_flops_per_token_head() * th
