@@ -488,12 +488,15 @@ def bench_decode_prep(kda, kda_inputs, cache, n_steps, stream):
 
 def bench_decode(kda, kda_inputs, n_steps, warmup, stream):
     cache, steps, o = decode_setup(kda, kda_inputs, n_steps, stream)
-    scratch = cache.clone()
+    # warm-up steps on the cache itself (its pages then are the ones in the
+    # translation caches), then the cache restored to its initialised state
+    saved = cache.clone()
     for s in range(warmup):
         x = steps[s % n_steps]
-        kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], scratch, o=o[0],
+        kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], cache, o=o[0],
                             stream=stream)
-    del scratch
+    cache.copy_(saved)
+    del saved
     torch.cuda.synchronize()
     tm = StreamTimer(stream)
     tm.start()
