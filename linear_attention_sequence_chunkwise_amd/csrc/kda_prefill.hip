@@ -493,21 +493,18 @@ __global__ __launch_bounds__(256) void kda_intra(
     // until the Gram operands are dead.
     constexpr int NT = NB * (NB + 1) / 2;
     constexpr int TPW = (NT + 3) / 4;
-    // F_IJ is exactly one for adjacent sub-blocks (J = I - 1): no factor there
-    auto gram_f = [&](int Ib, int Jb, auto scaled) {
+    auto gram = [&](int Ib, int Jb) {
         float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D; ks += mm::KS) {
             const int kk = ks + lq * mm::KPL;
             typename mm::frag af = mm::load(sm.u.g.kl, LDK, 16 * Ib + l16, kk);
             typename mm::frag bf = mm::load(sm.u.g.kr, LDK, 16 * Jb + l16, kk);
-            if constexpr (decltype(scaled)::value) bf = bf * mm::load(sm.F + (Ib * NB + Jb) * D, 0, 0, kk);
+            const typename mm::frag ff = mm::load(sm.F + (Ib * NB + Jb) * D, 0, 0, kk);
+            bf = bf * ff;
             acc = mm::mma(af, bf, acc);
         }
         return acc;
-    };
-    auto gram = [&](int Ib, int Jb) {
-        return Jb + 1 == Ib ? gram_f(Ib, Jb, std::false_type()) : gram_f(Ib, Jb, std::true_type());
     };
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
