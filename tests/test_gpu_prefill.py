@@ -316,3 +316,15 @@ def test_whole_chain_equals_slice_chain(monkeypatch):
     tol = TOL[torch.bfloat16]
     assert rel_err(o1.cpu().numpy(), o2.double().cpu().numpy()) < tol
     assert rel_err(S1.cpu().numpy(), S2.double().cpu().numpy()) < tol
+
+
+def test_whole_chain_many_sequences_unordered():
+    """More packed sequences than the length ranking covers (1100 > 1024): the
+    whole-chain form runs them in the given order, still every output and
+    state against the oracle."""
+    rng = np.random.default_rng(6)
+    lens = [int(x) for x in rng.integers(0, 40, size=1100)]
+    H, D = 1, 32
+    assert kda.kda_chunk_fwd_segments(1, sum(lens), H, D, D, 16, len(lens)) == -1
+    d, cu = _varlen_many(94, H, D, torch.bfloat16, lens)
+    check(d, 16, cu=cu)
