@@ -27,11 +27,15 @@
 //                        decay factors, the two Gram blocks on the matrix
 //                        cores, the triangular solve, and a record
 //                        {K*Gamma, Q*Gamma, (K*exp(G_n-G))^T, T diag(beta), M,
-//                        Gamma_n} written to the workspace.
-//   K2 kda_inter         one workgroup per (sequence, head, dv-slice),
-//                        sequential over the sequence's chunks: fp32 state in
-//                        registers, the four state/output products on the
-//                        matrix cores, output written directly.
+//                        Gamma_n} written to the workspace (fp16 records carry
+//                        the products (K*exp(G_n-G))^T T diag(beta) and
+//                        M T diag(beta) instead of the last three: see Rec).
+//   K2 the chain,        sequential over each sequence's chunks, fp32 state
+//                        in registers, products on the matrix cores:
+//      kda_seg_chain     segment-parallel (few chains: state runs of every
+//      kda_seg_combine   segment, their combination, a rerun with outputs),
+//                        or one workgroup per whole chain (many chains);
+//      kda_inter(_dma)   one workgroup per (sequence, head, dv-slice).
 //
 // Division-free decay factors.  K/Gamma overflows for strong gates, so the
 // Gram blocks are formed on 16-token sub-blocks with reference points: for
@@ -1128,8 +1132,9 @@ __host__ __device__ constexpr int seg_plane_in(int nseg, int s) { return 2 * nse
 // rows 4(l/16)..+3 of two tiles a, b; fp32: four 16x16x4 instructions per
 // tile, step s over rows 4m+s (m = 0..3).  So a wave that owns whole 16-column
 // blocks of the state runs X = V - KG S, U = Tb X, O = scale (QG S + M U) and
-// S <- Diag(Gamma_n) S + KPt U on its own registers, with no barrier and no
-// LDS round trip of S, X or U.
+// S <- Diag(Gamma_n) S + KPt U (folded fp16 records: no U, the M and KPt
+// slots applied to X) on its own registers, with no barrier and no LDS round
+// trip of S, X or U.
 //
 // B operands made once from NKT register tiles: fp16 pairs (tile 2p in
 // k-slots 0..3 of each lane, tile 2p+1 in 4..7; a missing last tile is zero),
@@ -1268,6 +1273,8 @@ struct ValueCopy {
 // region is refilled from vnext (the next chunk's rows, vlen of them; null:
 // nothing to fetch).  OUT: also O = scale (QG S + M U) into o for rows < len,
 // or, with EPI, into oo (this lane's tile entries) for the caller's epilogue.
+// Folded (fp16) records: U is X, the record's M and KPt slots holding M Tb and
+// KPt Tb.
 template <int D, int C, typename OT, typename IT, bool OUT, int NB, int NVB, bool EPI = false>
 __device__ __forceinline__ void wide_chunk(const WideTiles<D, C, OT, OUT>& t,
                                            float4v (&st)[NB][D / 16], const IT* vl,
@@ -1742,7 +1749,7 @@ __global__ __launch_bounds__(256) void kda_seg_combine(int NH, int nseg,
 // wavefronts never touch the memory pipeline except for their output stores.
 //
 // A CU only keeps a limited number of cache-line misses in flight, so issuing
-// a whole 65 KiB chunk stalls the issuing wavefront for about as long as the
+// a whole chunk record stalls the issuing wavefront for about as long as the
 // chunk's compute takes.  The producers take part in every workgroup barrier,
 // so one long burst would hold the compute wavefronts at the next barrier.
 // Instead each region of the two buffers is refilled as soon as the phase
