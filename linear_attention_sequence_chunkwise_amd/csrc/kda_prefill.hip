@@ -1239,10 +1239,14 @@ struct WideTiles {
     }
 };
 
+// A zero row for the value copies' rows past a chunk's end (64 bf16 or 32
+// fp32 values: up to two 16-column blocks per wave).
+__device__ __attribute__((aligned(16))) const uint32_t kZeroRow[32] = {};
+
 // Value rows of one chunk for one wave's 16 * NVB columns, copied into the
 // wave's own LDS region ([C][16 NVB] of IT) by direct global-to-LDS loads:
-// LPR lanes per row, 64 / LPR rows per copy; rows past the chunk repeat its
-// last row.
+// LPR lanes per row, 64 / LPR rows per copy; rows past the chunk are copied
+// from a zero row, so that readers need not mask them.
 template <int C, typename IT, int NVB>
 struct ValueCopy {
     static constexpr int LPR = 16 * NVB * (int)sizeof(IT) / 16;
@@ -1250,18 +1254,19 @@ struct ValueCopy {
     static constexpr int NI = (C + ROWS - 1) / ROWS;
     static constexpr int BYTES = C * 16 * NVB * (int)sizeof(IT);
     static_assert(64 % LPR == 0, "value rows must be whole lanes of a copy");
+    static_assert(LPR * 16 <= (int)sizeof(kZeroRow), "zero row too short");
     // src: row 0, first column of this wave's columns; stride between rows
     __device__ static __forceinline__ void issue(const IT* src, size_t stride, int len,
                                                  uint32_t dst) {
         const int lane = threadIdx.x & 63;
+        const IT* zero = reinterpret_cast<const IT*>(kZeroRow);
         // this wave's reads of the region are complete before it is refilled
         asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int r = i * ROWS + lane / LPR;
-            if (r < C)
-                dma16(src + (size_t)min(r, len - 1) * stride + (lane % LPR) * (16 / (int)sizeof(IT)),
-                      dst + i * 1024);
+            const int part = (lane % LPR) * (16 / (int)sizeof(IT));
+            if (r < C) dma16(r < len ? src + (size_t)r * stride + part : zero + part, dst + i * 1024);
         }
     }
 };
@@ -1302,15 +1307,11 @@ __device__ __forceinline__ void wide_chunk(const WideTiles<D, C, OT, OUT>& t,
         for (int nb = 0; nb < NB; ++nb) {
             float4v vv = zero;
             if (nb < NVB) {
-                // every row of the region holds data (rows past the chunk repeat
-                // its last row): read unconditionally, then select, so that the
-                // reads are not split into branches that each wait for LDS
+                // rows past the chunk hold zeros (see ValueCopy): no masking,
+                // so the reads are not split into branches that wait for LDS
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * rt + 4 * lq + j;
-                    const float x = to_f32(vl[r * 16 * NVB + 16 * nb + l16]);
-                    vv[j] = r < len ? x : 0.f;
-                }
+                for (int j = 0; j < 4; ++j)
+                    vv[j] = to_f32(vl[(16 * rt + 4 * lq + j) * 16 * NVB + 16 * nb + l16]);
             }
             x[nb][rt] = vv - acc[nb];
         }
