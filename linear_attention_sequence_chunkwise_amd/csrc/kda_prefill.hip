@@ -2221,16 +2221,20 @@ struct BwdDvSmem {
     float dO[C * LDV], X[C * LDV], U[C * LDV], dU[C * LDV], dX[C * LDV];
 };
 
-constexpr int kBwdDvWaves = 8;
+// Sixteen wavefronts (four per SIMD; the accumulators of two C x D tiles and
+// one lower C x C tile per wavefront keep it within 128 registers), or fewer
+// when a 16-column state slice has fewer elements than threads.
+template <int D>
+constexpr int bwd_dv_waves() { return D * 16 / 64 < 16 ? D * 16 / 64 : 16; }
 
 template <int D, int C>
-__global__ __launch_bounds__(64 * kBwdDvWaves) void kda_bwd_vprod(
+__global__ __launch_bounds__(64 * bwd_dv_waves<D>()) void kda_bwd_vprod(
     int T, int H, int nch_seq, const ChunkInfo* __restrict__ table,
     const int* __restrict__ chunk_total, float scale, const float* __restrict__ s_hist,
     const float* __restrict__ ds_hist, const float* __restrict__ xh, const float* __restrict__ uh,
     const float* __restrict__ duh, const float* __restrict__ dxh, const float* __restrict__ d_o,
     float* __restrict__ grec) {
-    constexpr int NW = kBwdDvWaves, NT = 64 * NW;
+    constexpr int NW = bwd_dv_waves<D>(), NT = 64 * NW;
     constexpr int BV = 16, LDV = 17;
     typedef GradRec<D, C> GR;
     constexpr int RT = C / 16, DT = D / 16;
@@ -3148,7 +3152,7 @@ static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan)
             auto kern = kda_bwd_vprod<D, C>;
             const size_t smem = sizeof(BwdDvSmem<D, C>);
             if (hipError_t e = set_smem(kern, smem)) return e;
-            hipLaunchKernelGGL(kern, grid, dim3(64 * kBwdDvWaves), smem, a.stream, a.T, a.H, nch_seq,
+            hipLaunchKernelGGL(kern, grid, dim3(64 * bwd_dv_waves<D>()), smem, a.stream, a.T, a.H, nch_seq,
                                table, total, a.scale, s_hist, ds_hist, xh, uh, duh, dxh, b.d_o, grec);
             if (hipError_t e = hipGetLastError()) return e;
         }
