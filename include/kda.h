@@ -39,10 +39,16 @@
  *     and o are fp32.  The bf16 path feeds the matrix cores with fp16 operands
  *     (exact for bf16 inputs of magnitude >= 2^-14) and accumulates in fp32;
  *     the fp32 path uses fp32 matrix-core products throughout.
- *   - Domain of the fast path (not checked): finite inputs; g <= 0; q and k
- *     L2-normalised (|entries| <= 1); |v| and the state entries < 6e4; within
- *     any 16-token block of a chunk the per-channel sum of -g stays below 10
- *     (per-token gates down to about -0.6 on average).
+ *   - Domain (not checked): finite inputs; g <= 0, of any magnitude; q and k
+ *     L2-normalised (|entries| <= 1); |v| and the state entries < 6e4.  The
+ *     chunk form builds its decay factors from products of per-token gates
+ *     and from sums of whole sub-block gate sums, never from differences, so
+ *     strong or huge gates lose nothing to cancellation.  A 16-token sub-block
+ *     whose per-channel gate sum falls below -8 (bf16 inputs) or -40 (fp32)
+ *     gets its diagonal Gram tiles from an exact fp32 path instead of the
+ *     matrix cores; this costs time only for such sub-blocks.
+ *     kda_chunk_bwd and kda_dplr_chunk_fwd keep narrower domains, stated at
+ *     their declarations.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -109,9 +115,11 @@ typedef struct {
  *   gate     device pointer to the gate logits, laid out like o ([B, T, H, dv]
  *            for the prefill, [N, H, dv] for decode) in qkv_dtype, or NULL
  *            (no gate).
- * The decode step applies it in the same kernel; the prefill applies it in
- * one extra pass over o inside the same call (an output row is spread over
- * several workgroups of the chain kernel). */
+ * The decode step applies it in the same kernel.  The prefill applies it in
+ * the chain kernel's pass that writes o when one workgroup owns whole output
+ * rows (the segment-parallel and whole-chain forms); with the per-slice form
+ * (an output row spread over several workgroups) it runs one extra pass over
+ * o inside the same call. */
 typedef struct {
     float eps;
     const float *weight;
@@ -306,7 +314,9 @@ size_t kda_dplr_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv,
  *   Everything else exactly as in kda_chunk_fwd (q, k, v, g, initial_state,
  *   cu_seqlens, num_seqs, o, final_state, workspace, errors).  The fp32 path
  *   supports chunk 16 and 32 at dk = 128 (the chunk-64 tiles exceed LDS).
- *   Domain as for kda_chunk_fwd, with |a|, |b| entries <= 1. */
+ *   Domain: that of kda_chunk_fwd, with |a|, |b| entries <= 1, except that
+ *   there is no exact path for strong decay: within any 16-token sub-block
+ *   the per-channel sum of -g stays below 10 (bf16 inputs) or 80 (fp32). */
 kda_status kda_dplr_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk,
                               float scale, kda_dtype qkv_dtype,
                               const void *q, const void *k, const void *v,

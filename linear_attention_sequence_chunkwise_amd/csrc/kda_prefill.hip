@@ -202,6 +202,125 @@ __global__ __launch_bounds__(256) void kda_chunk_table(const int32_t* __restrict
 // channels of one sub-block, so its loads of g, k, q rows are contiguous.
 // Record tiles leave the workgroup through LDS as 16-byte coalesced stores.
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Strong decay inside one 16-token sub-block.  The factor F_II = exp(-sum of g
+// over sub-block I) grows without bound as the gates get stronger, and a_r,
+// b_i shrink towards the bottom of the operand type's range.  A sub-block
+// whose per-channel gate sum falls below kStrongSum (fp16 operands: F <= e^8
+// and a_r, b_i >= e^-8; fp32: e^40) takes the exact path below for its
+// diagonal Gram tiles instead of the matrix cores; all other tiles only ever
+// use factors <= 1 and need nothing.
+// ---------------------------------------------------------------------------
+template <typename OT>
+constexpr float kStrongSum() { return sizeof(OT) == 2 ? -8.f : -40.f; }
+
+// Sum over aligned groups of NP lanes, scattered.  On entry every lane holds
+// NV partial values (NV <= NP, powers of two); on return lane l holds the
+// group sum of value (l % NP) / (NP / NV) in v[0].  Recursive halving: at
+// the step with stride s the lane whose bit s is set keeps the upper half of
+// its values and receives its partner's upper half (the partner keeps the
+// lower halves); once one value is left the remaining strides sum it whole.
+template <int NP, int NV, int S = NP / 2, int CNT = NV>
+__device__ __forceinline__ void reduce_scatter(float (&v)[NV], int lane) {
+    if constexpr (S >= 1) {
+        if constexpr (CNT > 1) {
+            constexpr int H = CNT / 2;
+            const bool up = (lane & S) != 0;
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                const float keep = up ? v[H + j] : v[j];
+                const float send = up ? v[j] : v[H + j];
+                v[j] = keep + __shfl_xor(send, S);
+            }
+            reduce_scatter<NP, NV, S / 2, H>(v, lane);
+        } else {
+            v[0] += __shfl_xor(v[0], S);
+            reduce_scatter<NP, NV, S / 2, 1>(v, lane);
+        }
+    }
+}
+
+// Row r and column i (i <= r) of the p-th entry of a 16 x 16 lower triangle
+// enumerated row by row, each row from its diagonal down to column 0:
+// p = r (r + 1) / 2 + (r - i).
+__device__ __forceinline__ void tri_entry(int p, int& r, int& i) {
+    int rr = (int)((sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
+    if ((rr + 1) * (rr + 2) / 2 <= p) ++rr;
+    if (rr * (rr + 1) / 2 > p) --rr;
+    r = rr;
+    i = rr - (p - rr * (rr + 1) / 2);
+}
+
+// Exact diagonal Gram tiles of one 16-token sub-block, evaluated in fp32 from
+// the per-token gates (no factor above one anywhere):
+//   A_ri = sum_c k_r[c] k_i[c] P_ir[c]   (i < r),
+//   M_ri = sum_c q_r[c] k_i[c] P_ir[c]   (i <= r),
+//   P_ir[c] = prod_{j=i+1..r} alpha_j[c]  (P_rr = 1).
+// Layout of the intra-chunk kernel's first phases: NP lanes hold the
+// sub-block, each lane two channels (al*, k*, q* hold alpha, k and q of the
+// sub-block's 16 rows for those channels).  Each lane forms the partial sums
+// over its two channels; a scattered sum over the NP lanes completes them,
+// NV values at a time.  Every lane of the wave must call this (the sums cross
+// lanes); only lanes with `store` write.  Results go to the A tile in LDS:
+// A_ri * beta_r at (r, i) of the diagonal block, M_ri at the transposed
+// position (i, r) -- the upper triangle with its diagonal, which the
+// triangular solve never reads -- from where the M tile is staged later; the
+// unscaled A_ri also goes to kk (row stride C) when it is not null.
+template <int C, int NP, typename OT>
+__device__ __forceinline__ void diag_exact(bool store, int lane, const float (&al0)[16],
+                                           const float (&al1)[16], const float (&k0)[16],
+                                           const float (&k1)[16], const float (&q0)[16],
+                                           const float (&q1)[16], OT* Ablk, int lda,
+                                           const float* beta, float* kk) {
+    constexpr int NV = NP < 16 ? NP : 16;   // values per scattered sum
+    constexpr int NE = 2 * 136;             // (M, A) per entry of the lower triangle
+    const int mine = (lane % NP) / (NP / NV);
+    const bool writer = store && (lane % (NP / NV)) == 0;
+    float buf[NV];
+    float P0 = 1.f, P1 = 1.f;
+    auto flush = [&](int b) {
+        reduce_scatter<NP, NV>(buf, lane);
+        const int s = b * NV + mine;
+        if (writer && s < NE) {
+            int r, i;
+            tri_entry(s >> 1, r, i);
+            const float x = buf[0];
+            if (s & 1) {
+                if (i < r) {
+                    Ablk[r * lda + i] = to_ot<OT>(beta[r] * x);
+                    if (kk) kk[r * C + i] = x;
+                }
+            } else {
+                Ablk[i * lda + r] = to_ot<OT>(x);
+            }
+        }
+    };
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int i = r; i >= 0; --i) {
+            if (i < r) {
+                P0 *= al0[i + 1];
+                P1 *= al1[i + 1];
+            } else {
+                P0 = 1.f;
+                P1 = 1.f;
+            }
+            const float t0 = k0[i] * P0, t1 = k1[i] * P1;
+            const int s = 2 * (r * (r + 1) / 2 + (r - i));   // compile-time after unrolling
+            buf[s % NV] = q0[r] * t0 + q1[r] * t1;
+            buf[(s + 1) % NV] = i < r ? k0[r] * t0 + k1[r] * t1 : 0.f;
+            if ((s + 2) % NV == 0) flush(s / NV);
+        }
+    }
+    if (NE % NV != 0) {
+#pragma unroll
+        for (int j = NE % NV; j < NV; ++j) buf[j] = 0.f;
+        flush(NE / NV);
+    }
+}
+
+
 template <int D, int C, typename OT>
 struct IntraSmem {
     static constexpr int NB = C / 16;
@@ -230,6 +349,7 @@ struct IntraSmem {
     float sig[NB * D];         // per sub-block sum of g
     float egs[NB * D];         // exp(Gs_I): block start relative to the chunk start
     float beta[C];
+    int strong[NB];            // sub-block I takes the exact diagonal path
 };
 
 
@@ -366,6 +486,7 @@ __global__ __launch_bounds__(256) void kda_intra(
     lds_barrier();
 
     // ---- phase 2: decay factors (one exp per element) and Gram operands ----
+    bool strong = false;
     if (task) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -380,21 +501,45 @@ __global__ __launch_bounds__(256) void kda_intra(
             }
             const float sigI = sm.sig[I * D + c];
             sm.egs[I * D + c] = exp_e(Gs);                // exp(G before block I) <= 1
-            float GsJ = 0.f;
+            // F_IJ = exp(sum of the gate sums strictly between J and I), summed
+            // directly (a difference of running sums would cancel for huge
+            // gates); F_II = exp(-sigI) is only used below kStrongSum
 #pragma unroll
             for (int J = 0; J < NB; ++J) {
                 if (J <= I) {
-                    const float sgJ = sm.sig[J * D + c];
-                    const float f = (J < I) ? exp_e(Gs - (GsJ + sgJ)) : exp_e(-sigI);
+                    float mid = 0.f;
+#pragma unroll
+                    for (int m = 0; m < NB; ++m)
+                        if (m > J && m < I) mid += sm.sig[m * D + c];
+                    const float f = (J < I) ? exp_e(mid) : exp_e(-sigI);
                     sm.F[(I * NB + J) * D + c] = to_ot<OT>(f);
-                    GsJ += sgJ;
                 }
             }
             if (I == 0) gn_out[c] = exp_e(Gn);
+            if (sigI < kStrongSum<OT>()) strong = true;
             // alpha_j = exp(g_j)
 #pragma unroll
             for (int j = 0; j < 16; ++j) gv[j] = exp_e(gv[j]);
         }
+    }
+    // Strong decay: the diagonal Gram tiles of the flagged sub-blocks, exactly
+    // (every lane of the wave takes part in the sums across lanes)
+    {
+        const unsigned long long sb = __ballot(strong);
+        // the NP lanes of this sub-block (aligned within the wave)
+        unsigned long long gmask = ~0ull;
+        if constexpr (NP < 64) gmask = ((1ull << NP) - 1) << (lane & ~(NP - 1) & 63);
+        const bool mine = task && (sb & gmask) != 0;
+        if (task && (lane % NP) == 0) sm.strong[I] = mine ? 1 : 0;
+        if (sb != 0) {
+            diag_exact<C, NP, OT>(mine, lane, g0, g1, k0v, k1v, q0v, q1v,
+                                  &sm.A[(16 * I) * LDA + 16 * I], LDA, &sm.beta[16 * I],
+                                  aux ? aux + ((size_t)ch * H + h) * 2 * C * C + C * C +
+                                            (16 * I) * C + 16 * I
+                                      : nullptr);
+        }
+    }
+    if (task) {
         // a_j = prod_{j'<=j} alpha, b_j = prod_{j'>j} alpha, both channels of the
         // pair at once: one 4-byte (fp16) or 8-byte (fp32) LDS store per row
         auto store2 = [](OT* p, float x0, float x1) {
@@ -447,12 +592,16 @@ __global__ __launch_bounds__(256) void kda_intra(
     auto kpt_group = [&](int c, int i0, float (&kk)[EPV]) {
         // the group's runs of four tokens lie in sub-blocks J and (fp16) J + 1
         const int J = group_col<OT>(i0, 0) >> 4;
-        float tail = 0.f;   // G_n - Ge_J: the gate sums of the later sub-blocks
+        // G_n - Ge_J and G_n - Ge_{J+1}: the gate sums of the later sub-blocks,
+        // each summed directly (no difference of sums)
+        float tail0 = 0.f, tail1 = 0.f;
 #pragma unroll
-        for (int m = 1; m < NB; ++m)
-            if (m > J) tail += sm.sig[m * D + c];
-        const float f0 = exp_e(tail);
-        const float f1 = J + 1 < NB ? exp_e(tail - sm.sig[(J + 1) * D + c]) : 0.f;
+        for (int m = 1; m < NB; ++m) {
+            if (m > J) tail0 += sm.sig[m * D + c];
+            if (m > J + 1) tail1 += sm.sig[m * D + c];
+        }
+        const float f0 = exp_e(tail0);
+        const float f1 = J + 1 < NB ? exp_e(tail1) : 0.f;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const int i = group_col<OT>(i0, e);
@@ -517,13 +666,16 @@ __global__ __launch_bounds__(256) void kda_intra(
             int tt = t, Ib = 0;
             while (tt > Ib) { tt -= Ib + 1; ++Ib; }
             const int Jb = tt;
-            const float4v acc = gram(Ib, Jb);
+            // a strong sub-block's diagonal tile came from the exact path (its
+            // upper triangle holds that path's M tile)
+            const bool exact = Ib == Jb && sm.strong[Ib];
+            const float4v acc = exact ? float4v{0.f, 0.f, 0.f, 0.f} : gram(Ib, Jb);
             const int col = 16 * Jb + l16;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * Ib + 4 * lq + j;
-                sm.A[row * LDA + col] = to_ot<OT>(col < row ? sm.beta[row] * acc[j] : 0.f);
-                if (aux)
+                if (!exact) sm.A[row * LDA + col] = to_ot<OT>(col < row ? sm.beta[row] * acc[j] : 0.f);
+                if (aux && (!exact || col >= row))
                     aux[((size_t)ch * H + h) * 2 * C * C + C * C + row * C + col] =
                         col < row ? acc[j] : 0.f;
             }
@@ -564,6 +716,7 @@ __global__ __launch_bounds__(256) void kda_intra(
             int tt = t, Ib = 0;
             while (tt > Ib) { tt -= Ib + 1; ++Ib; }
             const int Jb = tt;
+            if (Ib == Jb && sm.strong[Ib]) continue;   // staged from the exact path
             const float4v acc = gram(Ib, Jb);
             const int col = 16 * Jb + l16;
 #pragma unroll
@@ -581,9 +734,14 @@ __global__ __launch_bounds__(256) void kda_intra(
             int tt = t, Ib = 0;
             while (tt > Ib) { tt -= Ib + 1; ++Ib; }
             const int Jb = tt;
+            const bool exact = Ib == Jb && sm.strong[Ib];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                sm.u.s.M[(16 * Ib + 4 * lq + j) * LDA + 16 * Jb + l16] = to_ot<OT>(macc[i][j]);
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * Ib + 4 * lq + j, col = 16 * Jb + l16;
+                // the exact path left M_rc at the transposed place (c, r)
+                sm.u.s.M[row * LDA + col] =
+                    exact ? (col <= row ? sm.A[col * LDA + row] : to_ot<OT>(0.f)) : to_ot<OT>(macc[i][j]);
+            }
         }
     }
     if constexpr (!R::FOLD) {   // whole rows of M and T are stored: zero their upper blocks

@@ -134,6 +134,22 @@ def test_backward_strong_decay():
     assert_close(run_gpu(d, 64, do, dSf), run_oracle(d, do, dSf), TOL_BWD)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_backward_one_strong_subblock(dtype):
+    """One 16-token sub-block per chunk with gates -U(2.6, 3.0) (sub-block sums
+    near -45, so its diagonal Gram tiles take the exact path of the records
+    kernel) and the usual gates elsewhere: chunk sums stay above -80."""
+    B, T, H, D = 1, 200, 2, 128
+    d = make_prefill(69, B, T, H, D, dtype, s0_std=0.1)
+    gen = torch.Generator(device="cuda").manual_seed(70)
+    strong = -(2.6 + 0.4 * torch.rand(d["g"].shape, device="cuda", generator=gen))
+    pos = torch.arange(T, device="cuda") % 64
+    sel = ((pos >= 16) & (pos < 32)).view(1, T, 1, 1)
+    d["g"] = torch.where(sel, strong, d["g"]).contiguous()
+    do, dSf = cotangents(10, B, T, H, D, B)
+    assert_close(run_gpu(d, 64, do, dSf), run_oracle(d, do, dSf), TOL_BWD)
+
+
 def test_backward_chunk_invariance():
     """The gradients do not depend on the chunk length beyond rounding."""
     B, T, H, D = 2, 100, 2, 64

@@ -121,9 +121,47 @@ def test_in_place_state_and_determinism():
 
 
 def test_strong_decay():
-    """Per-token log gates down to -0.6: each 16-token sub-block decays by up
-    to exp(-9.6), the documented edge of the fast path."""
+    """Per-token log gates down to -0.6: 16-token sub-block sums around -5.4,
+    near the edge where sub-blocks start to take the exact diagonal path."""
     d = make_prefill(12, 1, 512, 4, 128, torch.bfloat16, s0_std=0.1, g_range=(0.05, 0.6))
+    check(d, 64)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_strong_decay_any_gate(dtype):
+    """log alpha ~ -U(0.1, 5) per token and channel (16-token sums around -41):
+    every sub-block's diagonal Gram tiles take the exact path; the state of a
+    chunk is forgotten within a few tokens, so the outputs are dominated by
+    the most recent tokens.  d = 128, chunk 64, with an initial state."""
+    d = make_prefill(40, 2, 700, 4, 128, dtype, s0_std=0.1, g_range=(0.1, 5.0))
+    check(d, 64)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_mixed_decay(dtype, D, chunk):
+    """Gates whose 16-token sums straddle the exact-path threshold (-8 for
+    bf16 inputs, -40 for fp32): within one chunk some sub-blocks take the
+    matrix-core diagonal tiles and others the exact path."""
+    gr = (0.001, 1.0) if dtype == torch.bfloat16 else (1.5, 3.5)
+    d = make_prefill(41 + D + chunk, 2, 3 * chunk + 9, 3, D, dtype, s0_std=0.1, g_range=gr)
+    check(d, chunk)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_huge_gates(dtype):
+    """Most gates in the usual range, with scattered per-channel gates of -1e6
+    and whole tokens at -1e30 (alpha = 0): the decay factors between
+    sub-blocks are summed directly, so a huge gate sum in one sub-block does
+    not swamp the factors of its neighbours."""
+    d = make_prefill(42, 1, 400, 4, 128, dtype, s0_std=0.1)
+    gen = torch.Generator(device="cuda").manual_seed(43)
+    u = torch.rand(d["g"].shape, device="cuda", generator=gen)
+    g = torch.where(u < 0.03, torch.full_like(d["g"], -1e6), d["g"])
+    tok = torch.rand(d["g"].shape[:3], device="cuda", generator=gen) < 0.02
+    g = torch.where(tok[..., None], torch.full_like(g, -1e30), g)
+    d["g"] = g.contiguous()
     check(d, 64)
 
 

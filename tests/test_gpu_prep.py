@@ -3,8 +3,10 @@ kda_decode_step_prep) against the fp64 oracle with the same preparation.
 
 Raw inputs, as a model layer would hand them over: q and k un-normalised (rows
 of random length), beta as logits, g as the gate pre-activation with per-head
-A_log and per-channel dt_bias.  The gate parameters keep log alpha within
-[-0.5, 0) so every case stays inside the kernels' documented domain.
+A_log and per-channel dt_bias.  The default gate parameters keep log alpha
+within [-0.5, 0); the wide ones (A_log up to 1.5, dt_bias up to 3) give
+per-token log gates down to about -20, where the chunk form's strong-decay
+path takes over.
 """
 import numpy as np
 import pytest
@@ -23,7 +25,7 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def raw_inputs(seed, B, T, H, D, dtype, s0=True, n_states=None):
+def raw_inputs(seed, B, T, H, D, dtype, s0=True, n_states=None, wide_gate=False):
     gen = torch.Generator(device="cuda").manual_seed(seed)
     f = dict(device="cuda", dtype=torch.float32, generator=gen)
     q = torch.randn(B, T, H, D, **f) * (0.3 + 3 * torch.rand(B, T, H, 1, **f))
@@ -33,6 +35,9 @@ def raw_inputs(seed, B, T, H, D, dtype, s0=True, n_states=None):
     g = 0.5 * torch.randn(B, T, H, D, **f)
     A_log = -1.0 + 1.5 * torch.rand(H, **f)
     dt_bias = -5.0 + 3.0 * torch.rand(H, D, **f)
+    if wide_gate:
+        A_log = 1.5 * torch.rand(H, **f)
+        dt_bias = -1.0 + 4.0 * torch.rand(H, D, **f)
     S0 = None
     if s0:
         S0 = 0.1 * torch.randn(n_states or B, H, D, D, **f)
@@ -70,6 +75,15 @@ def run_prefill(d, chunk, prep, cu=None):
 def test_prefill_prep_all_steps(dtype, D, chunk):
     d = raw_inputs(100 + D + chunk, 2, 150, 2, D, dtype)
     eo, es = run_prefill(d, chunk, prep_of(d))
+    assert eo < TOL[dtype] and es < TOL[dtype], (eo, es)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_prep_wide_gate(dtype):
+    """The Mamba/GDN gate with un-narrowed A_log and dt_bias, d = 128, chunk
+    64: prepared log gates reach about -20 per token."""
+    d = raw_inputs(150, 2, 300, 4, 128, dtype, wide_gate=True)
+    eo, es = run_prefill(d, 64, prep_of(d))
     assert eo < TOL[dtype] and es < TOL[dtype], (eo, es)
 
 
