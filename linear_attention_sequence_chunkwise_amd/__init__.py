@@ -7,6 +7,7 @@ every call raises ``RuntimeError`` -- there is no fallback of any kind.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -110,7 +111,20 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _check(t, name, dtype=None, device=None):
+def _alloc_stream(stream):
+    """Context under which the binding allocates: the launch stream, so that
+    the caching allocator orders any reuse of a block after the kernels that
+    use it (a block freed while other streams still run work on it could
+    otherwise be handed out again too early)."""
+    if stream is None:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(stream)
+
+
+def _check(t, name, dtype=None, device=None, shape=None):
+    """Contiguity, dtype, device and exact shape of a tensor argument.  The C
+    ABI sees only pointers, so this is the only place a mis-shaped buffer
+    (one the kernels would read or write past) can be caught."""
     if t is None:
         return
     if not t.is_contiguous():
@@ -119,6 +133,20 @@ def _check(t, name, dtype=None, device=None):
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if device is not None and t.device != device:
         raise ValueError("%s must be on %s" % (name, device))
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _on_gpu(t, name):
+    """Host tensors would hand host pointers to the kernels."""
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor, got device %s" % (name, t.device))
+
+
+def _dims(t, name, n):
+    if t.dim() != n:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, n, tuple(t.shape)))
+    return t.shape
 
 
 def make_prep(prep, H, dk, device):
@@ -129,12 +157,8 @@ def make_prep(prep, H, dk, device):
         return None, ()
     a = prep.get("A_log")
     b = prep.get("dt_bias")
-    _check(a, "A_log", torch.float32, device)
-    _check(b, "dt_bias", torch.float32, device)
-    if a is not None and a.numel() != H:
-        raise ValueError("A_log must hold H values")
-    if b is not None and b.numel() != H * dk:
-        raise ValueError("dt_bias must hold H * dk values")
+    _check(a, "A_log", torch.float32, device, (H,))
+    _check(b, "dt_bias", torch.float32, device, (H, dk))
     st = KdaPrep(1 if prep.get("normalize_qk") else 0, float(prep.get("eps", 1e-6)),
                  1 if prep.get("beta_logit") else 0,
                  None if a is None else a.data_ptr(), None if b is None else b.data_ptr())
@@ -149,15 +173,35 @@ def make_epilogue(epilogue, dv, o_shape, qkv_dtype, device):
         return None, ()
     w = epilogue.get("weight")
     z = epilogue.get("gate")
-    _check(w, "weight", torch.float32, device)
-    _check(z, "gate", qkv_dtype, device)
-    if w is not None and w.numel() != dv:
-        raise ValueError("weight must hold dv values")
-    if z is not None and tuple(z.shape) != tuple(o_shape):
-        raise ValueError("gate must be shaped like o")
+    _check(w, "weight", torch.float32, device, (dv,))
+    _check(z, "gate", qkv_dtype, device, o_shape)
     st = KdaEpilogue(float(epilogue.get("eps", 1e-6)), None if w is None else w.data_ptr(),
                      None if z is None else z.data_ptr())
     return st, (w, z)
+
+
+def _prefill_shapes(q, k, v, g, beta, initial_state, cu_seqlens):
+    """Sizes of a prefill-shaped call, every token tensor checked against q:
+    q, k, g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H]; initial_state
+    [N, H, dk, dv]; cu_seqlens [N + 1] int32 with B = 1.  (beta None: not
+    part of the call, or missing -- the C ABI reports the latter.)"""
+    B, T, H, dk = _dims(q, "q", 4)
+    dv = _dims(v, "v", 4)[-1]
+    dev = q.device
+    _check(q, "q", None, dev)
+    for t, n in ((k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev, (B, T, H, dk if n == "k" else dv))
+    _check(g, "g", torch.float32, dev, (B, T, H, dk))
+    _check(beta, "beta", torch.float32, dev, (B, T, H))
+    N = B
+    if cu_seqlens is not None:
+        _dims(cu_seqlens, "cu_seqlens", 1)
+        _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        if B != 1:
+            raise ValueError("cu_seqlens needs B == 1, got B = %d" % B)
+        N = cu_seqlens.numel() - 1
+    _check(initial_state, "initial_state", torch.float32, dev, (N, H, dk, dv))
+    return B, T, H, dk, dv, N, dev
 
 
 def kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torch.bfloat16):
@@ -188,27 +232,23 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu
     None).
     """
     lib = load_library()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dev = q.device
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, q.dtype, dev)
-    _check(g, "g", torch.float32, dev)
-    _check(beta, "beta", torch.float32, dev)
-    _check(initial_state, "initial_state", torch.float32, dev)
-    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    B, T, H, dk, dv, N, dev = _prefill_shapes(q, k, v, g, beta, initial_state, cu_seqlens)
     if scale is None:
         scale = dk ** -0.5
-    if o is None:
-        o = torch.empty(B, T, H, dv, dtype=torch.float32, device=dev)
-    if output_final_state and final_state is None:
-        final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    _check(o, "o", torch.float32, dev, (B, T, H, dv))
+    _check(final_state, "final_state", torch.float32, dev, (N, H, dk, dv))
     code = _dtype_code(q)
     need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk,
                                              N if cu_seqlens is not None else 0, code)
-    if workspace is None:
-        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, dev)
+    _on_gpu(q, "q")
+    with _alloc_stream(stream):
+        if o is None:
+            o = torch.empty(B, T, H, dv, dtype=torch.float32, device=dev)
+        if output_final_state and final_state is None:
+            final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
     args = (B, T, H, dk, dv, chunk, float(scale), code, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
             _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
             N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), _ptr(workspace),
@@ -244,32 +284,26 @@ def kda_chunk_bwd(q, k, v, g, beta, grad_o, scale=None, chunk=64, initial_state=
     dg, dbeta, d_initial_state), all fp32, the last None when not wanted.
     """
     lib = load_library()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dev = q.device
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, q.dtype, dev)
-    _check(g, "g", torch.float32, dev)
-    _check(beta, "beta", torch.float32, dev)
-    _check(initial_state, "initial_state", torch.float32, dev)
-    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
-    _check(grad_o, "grad_o", torch.float32, dev)
-    _check(grad_final_state, "grad_final_state", torch.float32, dev)
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    B, T, H, dk, dv, N, dev = _prefill_shapes(q, k, v, g, beta, initial_state, cu_seqlens)
+    _check(grad_o, "grad_o", torch.float32, dev, (B, T, H, dv))
+    _check(grad_final_state, "grad_final_state", torch.float32, dev, (N, H, dk, dv))
+    _check(workspace, "workspace", torch.uint8, dev)
+    _on_gpu(q, "q")
     if scale is None:
         scale = dk ** -0.5
-    f = dict(dtype=torch.float32, device=dev)
-    dq = torch.empty(B, T, H, dk, **f)
-    dk_ = torch.empty(B, T, H, dk, **f)
-    dv_ = torch.empty(B, T, H, dv, **f)
-    dg = torch.empty(B, T, H, dk, **f)
-    db = torch.empty(B, T, H, **f)
-    dS0 = torch.empty(N, H, dk, dv, **f) if want_grad_initial_state else None
     code = _dtype_code(q)
     nseq = N if cu_seqlens is not None else 0
     need = lib.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk, nseq, code)
-    if workspace is None:
-        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+    f = dict(dtype=torch.float32, device=dev)
+    with _alloc_stream(stream):
+        dq = torch.empty(B, T, H, dk, **f)
+        dk_ = torch.empty(B, T, H, dk, **f)
+        dv_ = torch.empty(B, T, H, dv, **f)
+        dg = torch.empty(B, T, H, dk, **f)
+        db = torch.empty(B, T, H, **f)
+        dS0 = torch.empty(N, H, dk, dv, **f) if want_grad_initial_state else None
+        if workspace is None:
+            workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
     rc = lib.kda_chunk_bwd(B, T, H, dk, dv, chunk, float(scale), code, _ptr(q), _ptr(k),
                            _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
                            nseq, _ptr(grad_o), _ptr(grad_final_state), _ptr(dq), _ptr(dk_),
@@ -295,26 +329,25 @@ def kda_dplr_chunk_fwd(q, k, v, a, b, g, scale=None, chunk=64, initial_state=Non
     q, k, a, b: [B, T, H, dk]; v: [B, T, H, dv] (all bf16 or all fp32); g:
     [B, T, H, dk] fp32; the rest as in kda_chunk_fwd.  Returns (o, final_state)."""
     lib = load_library()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dev = q.device
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (a, "a"), (b, "b")):
-        _check(t, n, q.dtype, dev)
-    _check(g, "g", torch.float32, dev)
-    _check(initial_state, "initial_state", torch.float32, dev)
-    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    B, T, H, dk, dv, N, dev = _prefill_shapes(q, k, v, g, None, initial_state, cu_seqlens)
+    for t, n in ((a, "a"), (b, "b")):
+        _check(t, n, q.dtype, dev, (B, T, H, dk))
+    _check(o, "o", torch.float32, dev, (B, T, H, dv))
+    _check(final_state, "final_state", torch.float32, dev, (N, H, dk, dv))
+    _check(workspace, "workspace", torch.uint8, dev)
+    _on_gpu(q, "q")
     if scale is None:
         scale = dk ** -0.5
-    if o is None:
-        o = torch.empty(B, T, H, dv, dtype=torch.float32, device=dev)
-    if output_final_state and final_state is None:
-        final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
     code = _dtype_code(q)
     nseq = N if cu_seqlens is not None else 0
     need = lib.kda_dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, nseq, code)
-    if workspace is None:
-        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+    with _alloc_stream(stream):
+        if o is None:
+            o = torch.empty(B, T, H, dv, dtype=torch.float32, device=dev)
+        if output_final_state and final_state is None:
+            final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
     rc = lib.kda_dplr_chunk_fwd(B, T, H, dk, dv, chunk, float(scale), code, _ptr(q), _ptr(k),
                                 _ptr(v), _ptr(a), _ptr(b), _ptr(g), _ptr(initial_state),
                                 _ptr(cu_seqlens), nseq, _ptr(o), _ptr(final_state),
@@ -331,19 +364,24 @@ def kda_decode_step(q, k, v, g, beta, state_cache, scale=None, slot_idx=None, o=
     int32 [N] or None; prep and epilogue as in kda_chunk_fwd.  Returns
     o [N, H, dv] fp32."""
     lib = load_library()
-    N, H, dk = q.shape
-    dv = v.shape[-1]
+    N, H, dk = _dims(q, "q", 3)
+    dv = _dims(v, "v", 3)[-1]
     dev = q.device
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, q.dtype, dev)
-    _check(g, "g", torch.float32, dev)
-    _check(beta, "beta", torch.float32, dev)
-    _check(state_cache, "state_cache", torch.float32, dev)
-    _check(slot_idx, "slot_idx", torch.int32, dev)
+    _check(q, "q", None, dev)
+    _check(k, "k", q.dtype, dev, (N, H, dk))
+    _check(v, "v", q.dtype, dev, (N, H, dv))
+    _check(g, "g", torch.float32, dev, (N, H, dk))
+    _check(beta, "beta", torch.float32, dev, (N, H))
+    slots = _dims(state_cache, "state_cache", 4)[0]
+    _check(state_cache, "state_cache", torch.float32, dev, (slots, H, dk, dv))
+    _check(slot_idx, "slot_idx", torch.int32, dev, (N,))
+    _check(o, "o", torch.float32, dev, (N, H, dv))
+    _on_gpu(q, "q")
     if scale is None:
         scale = dk ** -0.5
     if o is None:
-        o = torch.empty(N, H, dv, dtype=torch.float32, device=dev)
+        with _alloc_stream(stream):
+            o = torch.empty(N, H, dv, dtype=torch.float32, device=dev)
     args = (N, H, dk, dv, float(scale), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
             _ptr(beta), _ptr(state_cache), state_cache.shape[0], _ptr(slot_idx), _ptr(o))
     if prep is None and epilogue is None:

@@ -230,6 +230,28 @@ def test_concurrent_streams():
         assert torch.equal(x, y)
 
 
+def test_side_stream_not_current():
+    """stream= a side stream that is not made current: the binding allocates
+    the outputs and the workspace on that stream, and a burst of allocations
+    on the current stream meanwhile (which would reuse a block freed on the
+    wrong stream) does not disturb the result."""
+    B, T, H, D = 1, 8192, 8, 128
+    d = kda_inputs.prefill_inputs(86, B, T, H, D, D, torch.bfloat16, "cuda", s0_std=0.1)
+    ref_o, ref_S = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64,
+                                     initial_state=d["S0"])
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        o, S = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64,
+                                 initial_state=d["S0"], stream=s)
+        junk = [torch.full((1 << 20,), float(i), device="cuda") for i in range(64)]
+        s.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(S, ref_S), rep
+        del junk, o, S
+
+
 # Shapes where the chain is cut into segments (B*H small, many chunks), each
 # with a ragged last chunk: (B, T, H, d, chunk, dtype).
 SEG_CASES = [
