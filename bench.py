@@ -390,15 +390,9 @@ def bench_dplr(kda, kda_inputs, kda_in, steps, warmup, stream):
                                       kda_in["beta"], chunk=C, o=o, final_state=S, workspace=ws,
                                       stream=stream)
     kda_ms = timed(kcall)
-    prev = os.environ.get("KDA_INTER_VARIANT")
-    os.environ["KDA_INTER_VARIANT"] = "reg16"
-    try:
-        kda_reg_ms = timed(kcall)
-    finally:
-        if prev is None:
-            del os.environ["KDA_INTER_VARIANT"]
-        else:
-            os.environ["KDA_INTER_VARIANT"] = prev
+    kda_reg_ms = timed(lambda: kda.kda_chunk_fwd(kda_in["q"], kda_in["k"], kda_in["v"], kda_in["g"],
+                                                 kda_in["beta"], chunk=C, o=o, final_state=S,
+                                                 workspace=ws, stream=stream, chain_form="reg16"))
     db = DPLR_BYTES_PER_TOKEN_HEAD * B * T * H
     roof = dict(bound="hbm", achieved=db / (dplr_ms / 1e3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
                 algorithmic_bytes=db, traffic=measured_traffic("dplr"),

@@ -243,6 +243,40 @@ kda_status kda_decode_step_ex(int N, int H, int dk, int dv, float scale,
                               const kda_prep *prep, const kda_epilogue *epilogue,
                               hipStream_t stream);
 
+/* Chain forms, for comparing them in tests and benchmarks (every form gives
+ * the result of the chunk form up to rounding order).  The per-slice forms
+ * run one workgroup per (sequence, head, dv-slice), sequential over the
+ * sequence's chunks: register-staged with 16-, 32- or 64-column slices, or
+ * with direct global-to-LDS copies of the chunk records and 16- or
+ * 32-column slices.  kda_chunk_fwd and kda_chunk_fwd_ex use KDA_CHAIN_AUTO:
+ * the segment-parallel form for few long sequences, one workgroup per whole
+ * (sequence, head) chain for many, the per-slice forms otherwise. */
+typedef enum {
+    KDA_CHAIN_AUTO = 0,
+    KDA_CHAIN_SLICE_REG16 = 1,   /* any dtype                                  */
+    KDA_CHAIN_SLICE_REG32 = 2,   /* bf16 inputs                               */
+    KDA_CHAIN_SLICE_REG64 = 3,   /* bf16 inputs, dk >= 64                     */
+    KDA_CHAIN_SLICE_DMA16 = 4,   /* bf16 inputs, where two records fit LDS    */
+    KDA_CHAIN_SLICE_DMA32 = 5    /* bf16 inputs, where two records fit LDS    */
+} kda_chain_form;
+
+/* kda_chunk_fwd_ex with the chain form chosen by the caller (a testing and
+ * benchmarking entry point: the result does not depend on the form beyond
+ * rounding).  A form outside kda_chain_form, or one not built for (dk, chunk,
+ * dtype), returns KDA_ERR_UNSUPPORTED.  With a per-slice form and an
+ * epilogue, the epilogue runs as one extra pass over o.  The workspace is
+ * sized by kda_chunk_fwd_workspace_bytes as for kda_chunk_fwd. */
+kda_status kda_chunk_fwd_chain(int B, int T, int H, int dk, int dv, int chunk,
+                               float scale, kda_dtype qkv_dtype,
+                               const void *q, const void *k, const void *v,
+                               const float *g, const float *beta,
+                               const float *initial_state,
+                               const int32_t *cu_seqlens, int num_seqs,
+                               float *o, float *final_state,
+                               void *workspace, size_t workspace_bytes,
+                               const kda_prep *prep, const kda_epilogue *epilogue,
+                               kda_chain_form form, hipStream_t stream);
+
 /* Bytes of device workspace kda_chunk_bwd needs for these sizes (0 if the
  * sizes are invalid or unsupported); arguments as for
  * kda_chunk_fwd_workspace_bytes.  It holds the chunk records in fp32 (the

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 KDA_F32 = 0
 KDA_BF16 = 1
 KDA_OK = 0
+# kda_chain_form codes (kda_chunk_fwd_chain)
+CHAIN_FORMS = {"auto": 0, "reg16": 1, "reg32": 2, "reg64": 3, "dma16": 4, "dma32": 5}
 STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL_ARG", 2: "KDA_ERR_BAD_SHAPE",
                 3: "KDA_ERR_UNSUPPORTED", 4: "KDA_ERR_BAD_DTYPE", 5: "KDA_ERR_WORKSPACE",
                 6: "KDA_ERR_HIP"}
@@ -50,6 +52,8 @@ SIGNATURES = {
                            _P, _P, _P, _SZ, _P]),
     "kda_chunk_fwd_ex": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                               _P, _P, _P, _SZ, _PREP, _EPI, _P]),
+    "kda_chunk_fwd_chain": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
+                                 _P, _P, _P, _SZ, _PREP, _EPI, _I, _P]),
     "kda_chunk_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "kda_chunk_bwd": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -220,7 +224,7 @@ def kda_chunk_fwd_segments(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torch.bfloa
 
 def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu_seqlens=None,
                   output_final_state=True, o=None, final_state=None, workspace=None,
-                  stream=None, prep=None, epilogue=None):
+                  stream=None, prep=None, epilogue=None, chain_form=None):
     """Chunkwise KDA prefill.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32); g: [B, T, H, dk] fp32
@@ -228,8 +232,9 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu
     None; cu_seqlens: int32 [N + 1] (B must be 1) or None; prep: optional
     in-kernel input preparation (see make_prep); epilogue: optional output
     RMSNorm + gate (see make_epilogue).  With either, kda_chunk_fwd_ex is
-    called.  Returns (o [B, T, H, dv] fp32, final_state [N, H, dk, dv] fp32 or
-    None).
+    called.  chain_form: None, or a key of CHAIN_FORMS to force how the chain
+    runs (kda_chunk_fwd_chain; for comparing forms).  Returns (o [B, T, H, dv]
+    fp32, final_state [N, H, dk, dv] fp32 or None).
     """
     lib = load_library()
     B, T, H, dk, dv, N, dev = _prefill_shapes(q, k, v, g, beta, initial_state, cu_seqlens)
@@ -253,15 +258,21 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu
             _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
             N if cu_seqlens is not None else 0, _ptr(o), _ptr(final_state), _ptr(workspace),
             workspace.numel())
-    if prep is None and epilogue is None:
+    if prep is None and epilogue is None and chain_form is None:
         rc = lib.kda_chunk_fwd(*args, _stream(stream))
         fn = "kda_chunk_fwd"
     else:
         st, _keep = make_prep(prep, H, dk, dev)
         et, _keep2 = make_epilogue(epilogue, dv, (B, T, H, dv), q.dtype, dev)
-        rc = lib.kda_chunk_fwd_ex(*args, None if st is None else ctypes.byref(st),
-                                  None if et is None else ctypes.byref(et), _stream(stream))
-        fn = "kda_chunk_fwd_ex"
+        pst = None if st is None else ctypes.byref(st)
+        pet = None if et is None else ctypes.byref(et)
+        if chain_form is None:
+            rc = lib.kda_chunk_fwd_ex(*args, pst, pet, _stream(stream))
+            fn = "kda_chunk_fwd_ex"
+        else:
+            rc = lib.kda_chunk_fwd_chain(*args, pst, pet, CHAIN_FORMS[chain_form],
+                                         _stream(stream))
+            fn = "kda_chunk_fwd_chain"
     if rc != KDA_OK:
         raise KDAError(fn, rc)
     return o, final_state

@@ -92,13 +92,17 @@ int kda_chunk_fwd_segments(int B, int T, int H, int dk, int dv, int chunk, int n
     return kda::prefill_chain_segments(plan);
 }
 
-kda_status kda_chunk_fwd_ex(int B, int T, int H, int dk, int dv, int chunk, float scale,
-                            kda_dtype qkv_dtype, const void* q, const void* k, const void* v,
-                            const float* g, const float* beta, const float* initial_state,
-                            const int32_t* cu_seqlens, int num_seqs, float* o,
-                            float* final_state, void* workspace, size_t workspace_bytes,
-                            const kda_prep* prep, const kda_epilogue* epilogue,
-                            hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// kda_chunk_fwd_ex with a chain form (kda_chain_form code; 0 = automatic).
+kda_status chunk_fwd(int B, int T, int H, int dk, int dv, int chunk, float scale,
+                     kda_dtype qkv_dtype, const void* q, const void* k, const void* v,
+                     const float* g, const float* beta, const float* initial_state,
+                     const int32_t* cu_seqlens, int num_seqs, float* o, float* final_state,
+                     void* workspace, size_t workspace_bytes, const kda_prep* prep,
+                     const kda_epilogue* epilogue, int form, hipStream_t stream) {
     if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_BAD_SHAPE;
     kda::Prep pr;
     if (kda_status e = read_prep(prep, &pr)) return e;
@@ -110,6 +114,9 @@ kda_status kda_chunk_fwd_ex(int B, int T, int H, int dk, int dv, int chunk, floa
     if ((long long)B * T * H * (long long)(dk > dv ? dk : dv) >= (1LL << 40)) return KDA_ERR_BAD_SHAPE;
     if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
     if (dk != dv || !kda::prefill_supported(dk, chunk, qkv_dtype == KDA_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    if (form < KDA_CHAIN_AUTO || form > KDA_CHAIN_SLICE_DMA32 ||
+        !kda::prefill_chain_form_ok(dk, chunk, qkv_dtype == KDA_BF16, form))
         return KDA_ERR_UNSUPPORTED;
     const bool has_tokens = (long long)B * T > 0;
     if (has_tokens) {
@@ -139,8 +146,37 @@ kda_status kda_chunk_fwd_ex(int B, int T, int H, int dk, int dv, int chunk, floa
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.prep = pr;
     a.epi = ep;
+    a.chain = form;
     a.stream = stream;
     return from_hip(kda::launch_prefill(a, plan));
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd_ex(int B, int T, int H, int dk, int dv, int chunk, float scale,
+                            kda_dtype qkv_dtype, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, const float* initial_state,
+                            const int32_t* cu_seqlens, int num_seqs, float* o,
+                            float* final_state, void* workspace, size_t workspace_bytes,
+                            const kda_prep* prep, const kda_epilogue* epilogue,
+                            hipStream_t stream) {
+    return chunk_fwd(B, T, H, dk, dv, chunk, scale, qkv_dtype, q, k, v, g, beta, initial_state,
+                     cu_seqlens, num_seqs, o, final_state, workspace, workspace_bytes, prep,
+                     epilogue, KDA_CHAIN_AUTO, stream);
+}
+
+kda_status kda_chunk_fwd_chain(int B, int T, int H, int dk, int dv, int chunk, float scale,
+                               kda_dtype qkv_dtype, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const float* initial_state,
+                               const int32_t* cu_seqlens, int num_seqs, float* o,
+                               float* final_state, void* workspace, size_t workspace_bytes,
+                               const kda_prep* prep, const kda_epilogue* epilogue,
+                               kda_chain_form form, hipStream_t stream) {
+    return chunk_fwd(B, T, H, dk, dv, chunk, scale, qkv_dtype, q, k, v, g, beta, initial_state,
+                     cu_seqlens, num_seqs, o, final_state, workspace, workspace_bytes, prep,
+                     epilogue, (int)form, stream);
 }
 
 kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk, float scale,

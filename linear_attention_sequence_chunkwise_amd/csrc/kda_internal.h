@@ -57,6 +57,7 @@ struct PrefillArgs {
     size_t workspace_bytes;
     Prep prep;
     Epilogue epi;
+    int chain = 0;         // 0: the automatic chain form; 1..5: a forced per-slice kernel
     hipStream_t stream;
 };
 
@@ -118,6 +119,8 @@ bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan);
 // Segments per sequence launch_prefill's chain uses with this plan (1: none).
 int prefill_chain_segments(const PrefillPlan& plan);
+// Whether chain form `form` (a kda_chain_form code) is built for (D, C, dtype).
+bool prefill_chain_form_ok(int D, int C, bool bf16, int form);
 hipError_t launch_decode(const DecodeArgs& a);
 // True when (D, C, dtype) has built backward kernels that fit in LDS.
 bool backward_supported(int D, int C, bool bf16);

@@ -1241,17 +1241,18 @@ __global__ __launch_bounds__(256) void kda_state_chain(
     }
 }
 
-// Direct global-to-LDS copy (global_load_lds_dwordx4): every lane's 16 bytes
-// land at consecutive LDS addresses from the wave-uniform base in M0, with no
-// register destination; the copy counts in vmcnt like a load.
+// Direct global-to-LDS copy (global_load_lds_dwordx4 through the compiler's
+// builtin, which sets M0 itself): every lane's 16 bytes land at consecutive
+// LDS addresses from the wave-uniform base, with no register destination; the
+// copy counts in vmcnt like a load, and the compiler sees it in its own waits.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
+    __builtin_amdgcn_global_load_lds(
+        (__attribute__((address_space(1))) void*)const_cast<void*>(g),
+        (__attribute__((address_space(3))) void*)(uintptr_t)__builtin_amdgcn_readfirstlane(lds_base),
+        16, 0, 0);
 }
 
 // ---- K2s: segment-parallel chain for few long sequences ----
@@ -2971,24 +2972,18 @@ bool prefill_plan(int B, int T, int H, int D, int C, int N, bool varlen, bool bf
 // record, so slices are made as wide as still covers the chip: few chains
 // (each must span many CUs) use 32- or 16-column slices with double-buffered
 // direct-to-LDS copies; many chains use 64-column slices, register-staged.
-// KDA_INTER_VARIANT = dma16 / dma32 / reg16 / reg32 / reg64 overrides the
-// choice (benchmarking).
+// A caller of kda_chunk_fwd_chain may force one of them (PrefillArgs::chain,
+// the kda_chain_form codes; 0 = this choice).
 enum class InterVariant { Dma16, Dma32, Reg16, Reg32, Reg64 };
-// True when KDA_INTER_VARIANT names one of the per-slice chain kernels (the
-// segment-parallel chain is then not used).
-static bool inter_override() {
-    const char* e = getenv("KDA_INTER_VARIANT");
-    return e && (!strcmp(e, "dma16") || !strcmp(e, "dma32") || !strcmp(e, "reg16") ||
-                 !strcmp(e, "reg32") || !strcmp(e, "reg64"));
-}
 static InterVariant choose_inter(int D, long long chains, bool bf16, bool dma16_ok,
-                                 bool dma32_ok) {
-    if (const char* e = getenv("KDA_INTER_VARIANT")) {
-        if (!strcmp(e, "dma16") && dma16_ok) return InterVariant::Dma16;
-        if (!strcmp(e, "dma32") && dma32_ok) return InterVariant::Dma32;
-        if (!strcmp(e, "reg16")) return InterVariant::Reg16;
-        if (!strcmp(e, "reg32") && bf16 && D >= 32) return InterVariant::Reg32;
-        if (!strcmp(e, "reg64") && bf16 && D >= 64) return InterVariant::Reg64;
+                                 bool dma32_ok, int forced) {
+    switch (forced) {
+        case 1: return InterVariant::Reg16;
+        case 2: return InterVariant::Reg32;
+        case 3: return InterVariant::Reg64;
+        case 4: return InterVariant::Dma16;
+        case 5: return InterVariant::Dma32;
+        default: break;
     }
     if (!bf16) return InterVariant::Reg16;
     if (D >= 64 && chains * (D / 64) >= 512) return InterVariant::Reg64;
@@ -3064,7 +3059,6 @@ static hipError_t launch_records(const PrefillArgs& a, const PrefillPlan& plan, 
 }
 
 int prefill_chain_segments(const PrefillPlan& plan) {
-    if (inter_override()) return 1;
     if (plan.nseg > 1) return plan.nseg;
     return plan.whole ? -1 : 1;
 }
@@ -3135,7 +3129,7 @@ static hipError_t launch_slices(const PrefillArgs& a, const PrefillPlan& plan, i
     constexpr bool kBf = sizeof(OT) == 2;
     constexpr bool kDma16 = kBf && inter_dma_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
     constexpr bool kDma32 = kBf && D >= 32 && inter_dma_smem_bytes<D, C, 32, OT, IT>() <= kLdsLimit;
-    switch (choose_inter(D, (long long)a.N * a.H, kBf, kDma16, kDma32)) {
+    switch (choose_inter(D, (long long)a.N * a.H, kBf, kDma16, kDma32, a.chain)) {
         case InterVariant::Dma16:
             if constexpr (kDma16) return launch_inter<D, C, 16, OT, IT, 1>(a, plan, nch_seq, chunk_off);
             break;
@@ -3166,9 +3160,9 @@ static hipError_t launch_dc(const PrefillArgs& a, const PrefillPlan& plan) {
         if (hipError_t e = launch_records<D, C, OT, IT>(a, plan, nch_seq, &chunk_off, &table))
             return e;
         if constexpr (seg_fits_t<D, C, OT>()) {
-            if (plan.nseg > 1 && !inter_override())
+            if (plan.nseg > 1 && a.chain == 0)
                 return launch_segmented<D, C, OT, IT>(a, plan, nch_seq);
-            if (plan.whole && !inter_override())
+            if (plan.whole && a.chain == 0)
                 return launch_whole<D, C, OT, IT>(
                     a, plan, nch_seq, chunk_off,
                     reinterpret_cast<const int*>((const char*)a.workspace + plan.off_order));
@@ -3188,6 +3182,44 @@ static hipError_t launch_d(const PrefillArgs& a, const PrefillPlan& plan) {
         default: return hipErrorInvalidValue;
     }
     return e;
+}
+
+// Whether the per-slice chain kernel `form` (kda_chain_form code, 1..5) is
+// built for (D, C, dtype).
+template <int D, int C, typename OT, typename IT>
+static bool chain_form_dc(int form) {
+    if constexpr (!fits<D, C, OT>()) {
+        return false;
+    } else {
+        constexpr bool kBf = sizeof(OT) == 2;
+        switch (form) {
+            case 1: return true;
+            case 2: return kBf;
+            case 3: return kBf && D >= 64;
+            case 4: return kBf && inter_dma_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
+            case 5: return kBf && inter_dma_smem_bytes<D, C, 32, OT, IT>() <= kLdsLimit;
+            default: return false;
+        }
+    }
+}
+template <typename OT, typename IT, int D>
+static bool chain_form_d(int C, int form) {
+    switch (C) {
+        case 16: return chain_form_dc<D, 16, OT, IT>(form);
+        case 32: return chain_form_dc<D, 32, OT, IT>(form);
+        case 64: return chain_form_dc<D, 64, OT, IT>(form);
+        default: return false;
+    }
+}
+bool prefill_chain_form_ok(int D, int C, bool bf16, int form) {
+    if (form == 0) return prefill_supported(D, C, bf16);
+    if (!prefill_supported(D, C, bf16)) return false;
+    switch (D) {
+        case 32: return bf16 ? chain_form_d<_Float16, bf16_t, 32>(C, form) : chain_form_d<float, float, 32>(C, form);
+        case 64: return bf16 ? chain_form_d<_Float16, bf16_t, 64>(C, form) : chain_form_d<float, float, 64>(C, form);
+        case 128: return bf16 ? chain_form_d<_Float16, bf16_t, 128>(C, form) : chain_form_d<float, float, 128>(C, form);
+        default: return false;
+    }
 }
 
 // ---- backward host side ----

@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(lib):
     names = header_functions()
     assert set(names) == {"kda_status_string", "kda_version", "kda_chunk_fwd_workspace_bytes",
                           "kda_chunk_fwd_segments",
-                          "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_decode_step",
+                          "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_fwd_chain",
+                          "kda_decode_step",
                           "kda_decode_step_ex", "kda_chunk_bwd_workspace_bytes",
                           "kda_chunk_bwd", "kda_dplr_chunk_fwd_workspace_bytes",
                           "kda_dplr_chunk_fwd"}
@@ -125,6 +126,45 @@ def test_prefill_validation(lib):
     assert _fwd(lib, cu=ctypes.c_void_p(4096), nseq=0) == E["KDA_ERR_BAD_SHAPE"]
     assert _fwd(lib, wsb=16) == E["KDA_ERR_WORKSPACE"]
     assert _fwd(lib, ws=ctypes.c_void_p(4096 + 16)) == E["KDA_ERR_WORKSPACE"]  # not 256-aligned
+
+
+def _fwd_chain(lib, form, dtype=kda.KDA_BF16, dk=64, chunk=64):
+    p = ctypes.c_void_p(4096)
+    return lib.kda_chunk_fwd_chain(1, 0, 2, dk, dk, chunk, 1.0, dtype, p, p, p, p, p, None, None,
+                                   0, p, None, p, 1 << 30, None, None, form, None)
+
+
+def test_chain_form_validation(lib):
+    """Forms outside kda_chain_form, or not built for the sizes, are rejected
+    on the host (T = 0 keeps valid calls from reaching the device)."""
+    E = {v: k for k, v in kda.STATUS_NAMES.items()}
+    assert _fwd_chain(lib, -1) == E["KDA_ERR_UNSUPPORTED"]
+    assert _fwd_chain(lib, 6) == E["KDA_ERR_UNSUPPORTED"]
+    assert _fwd_chain(lib, kda.CHAIN_FORMS["reg32"], dtype=kda.KDA_F32) == E["KDA_ERR_UNSUPPORTED"]
+    assert _fwd_chain(lib, kda.CHAIN_FORMS["reg64"], dk=32, chunk=16) == E["KDA_ERR_UNSUPPORTED"]
+    assert _fwd_chain(lib, kda.CHAIN_FORMS["dma16"], dtype=kda.KDA_F32) == E["KDA_ERR_UNSUPPORTED"]
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+def test_no_device_reports_hip_error(lib):
+    """Valid arguments with no usable GPU: every entry point returns
+    KDA_ERR_HIP from its device query instead of crashing (the pointers are
+    never touched)."""
+    if _gpu_visible():
+        pytest.skip("a GPU is visible: valid calls would launch kernels")
+    E = {v: k for k, v in kda.STATUS_NAMES.items()}
+    p = ctypes.c_void_p(4096)
+    assert _fwd(lib) == E["KDA_ERR_HIP"]
+    assert lib.kda_decode_step(2, 2, 64, 64, 1.0, kda.KDA_BF16, p, p, p, p, p, p, 2, None, p,
+                               None) == E["KDA_ERR_HIP"]
+    assert lib.kda_chunk_bwd(1, 64, 2, 64, 64, 64, 1.0, kda.KDA_BF16, p, p, p, p, p, None, None,
+                             0, p, None, p, p, p, p, p, None, p, 1 << 34, None) == E["KDA_ERR_HIP"]
+    assert lib.kda_dplr_chunk_fwd(1, 64, 2, 64, 64, 64, 1.0, kda.KDA_BF16, p, p, p, p, p, p, None,
+                                  None, 0, p, None, p, 1 << 30, None) == E["KDA_ERR_HIP"]
 
 
 def test_decode_validation(lib):

@@ -148,18 +148,18 @@ def test_prefill_epilogue_fused_in_segments(dtype, D, chunk, weight, gate):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_prefill_epilogue_fused_equals_separate_pass(dtype, monkeypatch):
+def test_prefill_epilogue_fused_equals_separate_pass(dtype):
     """Fused epilogue (segment chain) and the separate epilogue pass after the
     per-slice chain agree to rounding."""
     B, T, H, D, chunk = 1, 2000, 2, 64, 32
     d = kda_inputs.prefill_inputs(77, B, T, H, D, D, dtype, "cuda", s0_std=0.1)
     epi = epi_params(8, (B, T, H, D), dtype)
-    run = lambda: kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=chunk,
-                                    initial_state=d["S0"], epilogue=epi)
+    run = lambda form=None: kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                              chunk=chunk, initial_state=d["S0"], epilogue=epi,
+                                              chain_form=form)
     assert kda.kda_chunk_fwd_segments(B, T, H, D, D, chunk, 0, dtype) > 1
     o1, _ = run()
-    monkeypatch.setenv("KDA_INTER_VARIANT", "reg16")
-    o2, _ = run()
+    o2, _ = run("reg16")
     torch.cuda.synchronize()
     assert rel_err(o1.cpu().numpy(), o2.double().cpu().numpy()) < TOL[dtype]
 

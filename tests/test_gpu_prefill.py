@@ -289,15 +289,15 @@ def test_two_segments():
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_segmented_equals_slice_chain(dtype, monkeypatch):
+def test_segmented_equals_slice_chain(dtype):
     """The segment-parallel chain and the per-slice chain agree to rounding."""
     B, T, H, D, chunk = 1, 2000, 2, 64, 32
     assert kda.kda_chunk_fwd_segments(B, T, H, D, D, chunk, 0, dtype) > 1
     d = make_prefill(82, B, T, H, D, dtype, s0_std=0.1)
     o1, S1 = run(d, chunk)
-    monkeypatch.setenv("KDA_INTER_VARIANT", "reg16")
-    assert kda.kda_chunk_fwd_segments(B, T, H, D, D, chunk, 0, dtype) == 1
-    o2, S2 = run(d, chunk)
+    o2, S2 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=chunk,
+                               initial_state=d["S0"], chain_form="reg16")
+    torch.cuda.synchronize()
     tol = TOL[dtype]
     assert rel_err(o1.cpu().numpy(), o2.double().cpu().numpy()) < tol
     assert rel_err(S1.cpu().numpy(), S2.double().cpu().numpy()) < tol
@@ -357,7 +357,7 @@ def test_whole_chain_varlen():
     check(d, 64, cu=cu)
 
 
-def test_whole_chain_equals_slice_chain(monkeypatch):
+def test_whole_chain_equals_slice_chain():
     """The whole-chain form and the per-slice chain agree to rounding, for
     packed sequences and in place (final_state aliasing initial_state)."""
     lens = [200, 0, 64, 1000, 17, 333, 64 * 5, 90] * 5
@@ -370,9 +370,9 @@ def test_whole_chain_equals_slice_chain(monkeypatch):
                               initial_state=st, final_state=st, cu_seqlens=cu)
     torch.cuda.synchronize()
     assert torch.equal(o1, o3) and torch.equal(S1, st)
-    monkeypatch.setenv("KDA_INTER_VARIANT", "reg16")
-    assert kda.kda_chunk_fwd_segments(1, sum(lens), H, D, D, 64, len(lens)) == 1
-    o2, S2 = run(d, 64, cu=cu)
+    o2, S2 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=64,
+                               initial_state=d["S0"], cu_seqlens=cu, chain_form="reg16")
+    torch.cuda.synchronize()
     tol = TOL[torch.bfloat16]
     assert rel_err(o1.cpu().numpy(), o2.double().cpu().numpy()) < tol
     assert rel_err(S1.cpu().numpy(), S2.double().cpu().numpy()) < tol
