@@ -170,16 +170,22 @@ def test_backward_repeatable():
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
 
 
-def test_backward_config2_sampled():
+def test_backward_config2_all_heads():
     """The 32K-token layer (B 1, H 32, d 128, bf16, chunk 64) as the benchmark
-    runs it; sampled heads checked against the oracle."""
+    runs it; every gradient of every head against the oracle.  The oracle's
+    reverse mode keeps each chain's whole state history (4 GiB at 32K
+    tokens), so it runs eight heads at a time; the error is taken over all
+    heads jointly."""
     B, T, H, D = 1, 32768, 32, 128
     d = make_prefill(68, B, T, H, D, torch.bfloat16, s0_std=0.1)
     do, dSf = cotangents(9, B, T, H, D, B)
     got = run_gpu(d, 64, do, dSf)
-    heads = [0, 19, 31]
-    ref = run_oracle(d, do, dSf, heads=heads)
-    for i, h in enumerate(heads):
-        one = [x[:, :, h] for x in got[:5]] + [got[5][:, h]]
-        e = errors(one, [x[:, :, i] for x in ref[:5]] + [ref[5][:, i]])
-        assert all(v < TOL_BWD for v in e.values()), (h, e)
+    ref = [np.empty_like(x) for x in got]
+    for h0 in range(0, H, 8):
+        heads = list(range(h0, h0 + 8))
+        r = run_oracle(d, do, dSf, heads=heads)
+        for i in range(5):
+            ref[i][:, :, h0:h0 + 8] = r[i]
+        ref[5][:, h0:h0 + 8] = r[5]
+        print("heads %d..%d done" % (h0, h0 + 7), flush=True)
+    assert_close(got, ref, TOL_BWD)

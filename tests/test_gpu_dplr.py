@@ -88,13 +88,11 @@ def test_dplr_zero_tokens_keeps_state():
     assert o.size == 0 and np.array_equal(S, d["S0"].cpu().numpy())
 
 
-def test_dplr_config2_sampled():
+def test_dplr_config2_all_heads():
     """The 32K-token layer shape (B 1, H 32, d 128, bf16, chunk 64) as the
-    benchmark runs it; sampled heads checked against the oracle."""
+    benchmark runs it; every output and final state against the oracle."""
     d = kda_inputs.dplr_inputs(74, 1, 32768, 32, 128, 128, torch.bfloat16, "cuda")
     o, S = run(d, 64)
-    heads = [0, 13, 31]
-    ro, rS = ref(d, heads=heads)
-    for i, h in enumerate(heads):
-        assert rel_err(o[:, :, h], ro[:, :, i]) < TOL[torch.bfloat16], h
-        assert rel_err(S[:, h], rS[:, i]) < TOL[torch.bfloat16], h
+    ro, rS = ref(d)
+    assert rel_err(o, ro) < TOL[torch.bfloat16]
+    assert rel_err(S, rS) < TOL[torch.bfloat16]
