@@ -71,7 +71,9 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = 3,  /* dk, dv, chunk or dtype outside the built set */
     KDA_ERR_BAD_DTYPE = 4,    /* dtype code not in kda_dtype                 */
     KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required     */
-    KDA_ERR_HIP = 6           /* the HIP runtime reported an error           */
+    KDA_ERR_HIP = 6,          /* the HIP runtime reported an error           */
+    KDA_ERR_SCRATCH = 7       /* kda_chunk_fwd_noalloc: the call's workspace
+                                 exceeds KDA_NOALLOC_SCRATCH_BYTES           */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -190,6 +192,29 @@ kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk,
                          float *o, float *final_state,
                          void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* kda_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument, and no allocation of any kind.  The workspace is a
+ * fixed device array of KDA_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU, held from the first call on that GPU until the process ends.
+ *   - Arguments, layouts and errors as kda_chunk_fwd, plus KDA_ERR_SCRATCH
+ *     when kda_chunk_fwd_workspace_bytes(...) for the same sizes exceeds
+ *     KDA_NOALLOC_SCRATCH_BYTES (e.g. at dk = dv = 128, chunk 64, bf16 and
+ *     32 heads: about 4 500 tokens).
+ *   - Every call on one GPU uses that GPU's single array, whose contents
+ *     persist from the previous call; nothing in it needs to start at zero.
+ *     Calls that overlap in time on one GPU (several streams or threads)
+ *     race on it: the caller serialises them, e.g. on one stream. */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
+kda_status kda_chunk_fwd_noalloc(int B, int T, int H, int dk, int dv, int chunk,
+                                 float scale, kda_dtype qkv_dtype,
+                                 const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta,
+                                 const float *initial_state,
+                                 const int32_t *cu_seqlens, int num_seqs,
+                                 float *o, float *final_state,
+                                 hipStream_t stream);
 
 /* kda_chunk_fwd with the optional input preparation and output epilogue
  * above (either pointer may be NULL).  Same arguments, layouts, workspace and

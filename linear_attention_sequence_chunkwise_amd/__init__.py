@@ -23,7 +23,7 @@ KDA_OK = 0
 CHAIN_FORMS = {"auto": 0, "reg16": 1, "reg32": 2, "reg64": 3, "dma16": 4, "dma32": 5}
 STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL_ARG", 2: "KDA_ERR_BAD_SHAPE",
                 3: "KDA_ERR_UNSUPPORTED", 4: "KDA_ERR_BAD_DTYPE", 5: "KDA_ERR_WORKSPACE",
-                6: "KDA_ERR_HIP"}
+                6: "KDA_ERR_HIP", 7: "KDA_ERR_SCRATCH"}
 
 # name -> (restype, argtypes), mirroring include/kda.h
 _P, _I, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -54,6 +54,8 @@ SIGNATURES = {
                               _P, _P, _P, _SZ, _PREP, _EPI, _P]),
     "kda_chunk_fwd_chain": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                                  _P, _P, _P, _SZ, _PREP, _EPI, _I, _P]),
+    "kda_chunk_fwd_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P,
+                                   _I, _P, _P, _P]),
     "kda_chunk_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "kda_chunk_bwd": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -275,6 +277,34 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, chunk=64, initial_state=None, cu
             fn = "kda_chunk_fwd_chain"
     if rc != KDA_OK:
         raise KDAError(fn, rc)
+    return o, final_state
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # KDA_NOALLOC_SCRATCH_BYTES
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, o, final_state=None, scale=None, chunk=64,
+                          initial_state=None, cu_seqlens=None, stream=None):
+    """kda_chunk_fwd through the entry point that allocates nothing: the
+    library's fixed per-GPU scratch replaces the workspace, and the caller
+    passes the outputs (o [B, T, H, dv] fp32, final_state [N, H, dk, dv] fp32
+    or None).  Calls that overlap on one GPU race on that scratch.  Returns
+    (o, final_state)."""
+    lib = load_library()
+    B, T, H, dk, dv, N, dev = _prefill_shapes(q, k, v, g, beta, initial_state, cu_seqlens)
+    if o is None:
+        raise ValueError("o must be given (this entry point allocates nothing)")
+    _check(o, "o", torch.float32, dev, (B, T, H, dv))
+    _check(final_state, "final_state", torch.float32, dev, (N, H, dk, dv))
+    _on_gpu(q, "q")
+    if scale is None:
+        scale = dk ** -0.5
+    rc = lib.kda_chunk_fwd_noalloc(B, T, H, dk, dv, chunk, float(scale), _dtype_code(q), _ptr(q),
+                                   _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                   _ptr(cu_seqlens), N if cu_seqlens is not None else 0, _ptr(o),
+                                   _ptr(final_state), _stream(stream))
+    if rc != KDA_OK:
+        raise KDAError("kda_chunk_fwd_noalloc", rc)
     return o, final_state
 
 

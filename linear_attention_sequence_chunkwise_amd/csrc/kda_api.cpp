@@ -7,9 +7,39 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kda_internal.h"
 
 namespace {
+
+// Scratch of kda_chunk_fwd_noalloc: a fixed device array, one copy per GPU,
+// held until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host that name is only a stand-in); it uses the device
+// address hipGetSymbolAddress reports for the current device, looked up once
+// per device.
+constexpr size_t kScratchBytes = (size_t)KDA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's copy of `scratch` (nullptr if the runtime cannot report it).
+void* scratch_of(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -62,6 +92,9 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE: unknown dtype code";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
+        case KDA_ERR_SCRATCH:
+            return "KDA_ERR_SCRATCH: the call needs more workspace than the fixed scratch of "
+                   "kda_chunk_fwd_noalloc";
     }
     return "KDA_ERR_UNKNOWN";
 }
@@ -177,6 +210,29 @@ kda_status kda_chunk_fwd_chain(int B, int T, int H, int dk, int dv, int chunk, f
     return chunk_fwd(B, T, H, dk, dv, chunk, scale, qkv_dtype, q, k, v, g, beta, initial_state,
                      cu_seqlens, num_seqs, o, final_state, workspace, workspace_bytes, prep,
                      epilogue, (int)form, stream);
+}
+
+kda_status kda_chunk_fwd_noalloc(int B, int T, int H, int dk, int dv, int chunk, float scale,
+                                 kda_dtype qkv_dtype, const void* q, const void* k,
+                                 const void* v, const float* g, const float* beta,
+                                 const float* initial_state, const int32_t* cu_seqlens,
+                                 int num_seqs, float* o, float* final_state, hipStream_t stream) {
+    // size check first: a call whose workspace would not fit the fixed
+    // scratch is refused before any device work
+    const size_t need = kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk,
+                                                      cu_seqlens ? num_seqs : 0, qkv_dtype);
+    if (need > kScratchBytes) return KDA_ERR_SCRATCH;
+    if (need == 0)   // invalid sizes (reported by the checks) or no workspace needed
+        return chunk_fwd(B, T, H, dk, dv, chunk, scale, qkv_dtype, q, k, v, g, beta,
+                         initial_state, cu_seqlens, num_seqs, o, final_state, nullptr, 0, nullptr,
+                         nullptr, KDA_CHAIN_AUTO, stream);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+    void* ws = scratch_of(dev);
+    if (!ws) return KDA_ERR_HIP;
+    return chunk_fwd(B, T, H, dk, dv, chunk, scale, qkv_dtype, q, k, v, g, beta, initial_state,
+                     cu_seqlens, num_seqs, o, final_state, ws, kScratchBytes, nullptr, nullptr,
+                     KDA_CHAIN_AUTO, stream);
 }
 
 kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk, float scale,

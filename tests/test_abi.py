@@ -31,6 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"kda_status_string", "kda_version", "kda_chunk_fwd_workspace_bytes",
                           "kda_chunk_fwd_segments",
                           "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_fwd_chain",
+                          "kda_chunk_fwd_noalloc",
                           "kda_decode_step",
                           "kda_decode_step_ex", "kda_chunk_bwd_workspace_bytes",
                           "kda_chunk_bwd", "kda_dplr_chunk_fwd_workspace_bytes",
@@ -165,6 +166,22 @@ def test_no_device_reports_hip_error(lib):
                              0, p, None, p, p, p, p, p, None, p, 1 << 34, None) == E["KDA_ERR_HIP"]
     assert lib.kda_dplr_chunk_fwd(1, 64, 2, 64, 64, 64, 1.0, kda.KDA_BF16, p, p, p, p, p, p, None,
                                   None, 0, p, None, p, 1 << 30, None) == E["KDA_ERR_HIP"]
+    assert lib.kda_chunk_fwd_noalloc(1, 64, 2, 64, 64, 64, 1.0, kda.KDA_BF16, p, p, p, p, p, None,
+                                     None, 0, p, None, None) == E["KDA_ERR_HIP"]
+
+
+def test_noalloc_validation(lib):
+    """The no-allocation entry point refuses calls whose workspace would not
+    fit its fixed scratch, on the host, with KDA_ERR_SCRATCH."""
+    E = {v: k for k, v in kda.STATUS_NAMES.items()}
+    p = ctypes.c_void_p(4096)
+    big = lib.kda_chunk_fwd_noalloc(1, 8192, 32, 128, 128, 64, 1.0, kda.KDA_BF16, p, p, p, p, p,
+                                    None, None, 0, p, None, None)
+    assert big == E["KDA_ERR_SCRATCH"]
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 32, 128, 128, 64, 0, kda.KDA_BF16) > \
+        kda.NOALLOC_SCRATCH_BYTES
+    assert lib.kda_chunk_fwd_noalloc(1, 64, 2, 48, 48, 64, 1.0, kda.KDA_BF16, p, p, p, p, p,
+                                     None, None, 0, p, None, None) == E["KDA_ERR_UNSUPPORTED"]
 
 
 def test_decode_validation(lib):
