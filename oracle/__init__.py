@@ -19,7 +19,8 @@ Contents
 
   - ``recurrence_np``    the delta-rule token loop, written out again in NumPy;
   - ``bruteforce_np``    the literal matrix product (I - b k k^T) Diag(a) S + b k v^T;
-  - ``chunked_np``       the chunkwise WY/UT form, derived from the recurrence;
+  - ``chunked_np``       the chunkwise WY/UT form, derived from the recurrence
+    (its per-chunk quantities from ``chunk_terms_np``);
   - ``linear_attention_closed_form``, ``scalar_gated_deltanet_np``: the textbook
     special cases the method reduces to.
 
@@ -285,6 +286,27 @@ def bruteforce_np(q, k, v, g, beta, scale, S0=None):
     return o, S
 
 
+def chunk_terms_np(Q, K, Gl, b):
+    """The intra-chunk quantities of the chunkwise form for one chunk of n
+    tokens (summary page, "Algoritmo paralelo por chunks": the two decayed
+    Gram blocks, the UT transform by forward substitution), with G_r =
+    sum_{j<=r} g_j per channel and Gamma = exp(G):
+        KG = K*Gamma,  QG = Q*Gamma,  KE = K*exp(G_n - G)          (n x dk)
+        A  = strict_lower(diag(beta) (K*Gamma) (K/Gamma)^T)        (n x n)
+        M  = lower_incl_diag((Q*Gamma) (K/Gamma)^T)                 (n x n)
+        T  = (I + A)^-1,   Gn = exp(G_n)                            (dk)
+    Returned as a dict.  The division by Gamma is done in fp64 with the chunk
+    start as reference; for cross-checks on gates whose chunk sums stay above
+    about -700."""
+    G = np.cumsum(Gl, axis=0)
+    Gam = np.exp(G)
+    Kp, Km, Qp = K * Gam, K * np.exp(-G), Q * Gam
+    A = np.tril(b[:, None] * (Kp @ Km.T), -1)
+    M = np.tril(Qp @ Km.T, 0)
+    Tm = forward_substitution_inverse(np.eye(Q.shape[0]) + A)
+    return dict(KG=Kp, QG=Qp, KE=K * np.exp(G[-1] - G), A=A, M=M, T=Tm, Gn=np.exp(G[-1]))
+
+
 def chunked_np(q, k, v, g, beta, scale, S0=None, chunk=64):
     """Chunkwise form (summary page, "Algoritmo paralelo por chunks"): fixed
     chunks, each starting from the previous chunk's final state; inside a chunk
@@ -292,36 +314,25 @@ def chunked_np(q, k, v, g, beta, scale, S0=None, chunk=64):
     T = (I + A)^-1, obtained by forward substitution, and the output joins the
     inter-chunk (state) and intra-chunk (masked Gram) parts.
 
-    Within a chunk of n tokens starting from state S, with G_r = sum_{j<=r} g_j
-    (per channel) and Gamma = exp(G):
-        A = strict_lower(diag(beta) (K*Gamma) (K/Gamma)^T)
-        M = lower_incl_diag((Q*Gamma) (K/Gamma)^T)
-        T = (I + A)^-1
-        W = T diag(beta) (K*Gamma),   Ut = T diag(beta) V
+    Within a chunk of n tokens starting from state S, with the quantities of
+    chunk_terms_np:
+        W = T diag(beta) KG,   Ut = T diag(beta) V
         U = Ut - W S
-        O = scale ((Q*Gamma) S + M U)
-        S <- Diag(Gamma_n) S + (K * exp(G_n - G))^T U
-    The division by Gamma is done here in fp64 with a per-chunk reference; this
-    form is for cross-checks on tame gates only.
+        O = scale (QG S + M U)
+        S <- Diag(Gn) S + KE^T U
     """
     q, k, v, g, beta, S = _chain(q, k, v, g, beta, S0)
     T_len = q.shape[0]
     o = np.zeros((T_len, v.shape[1]))
     for c0 in range(0, T_len, chunk):
         c1 = min(c0 + chunk, T_len)
-        n = c1 - c0
-        Q, K, V, Gl, b = q[c0:c1], k[c0:c1], v[c0:c1], g[c0:c1], beta[c0:c1]
-        G = np.cumsum(Gl, axis=0)
-        Gam = np.exp(G)
-        Kp, Km, Qp = K * Gam, K * np.exp(-G), Q * Gam
-        A = np.tril(b[:, None] * (Kp @ Km.T), -1)
-        M = np.tril(Qp @ Km.T, 0)
-        Tm = forward_substitution_inverse(np.eye(n) + A)
-        W = Tm @ (b[:, None] * Kp)
-        Ut = Tm @ (b[:, None] * V)
+        b, V = beta[c0:c1], v[c0:c1]
+        t = chunk_terms_np(q[c0:c1], k[c0:c1], g[c0:c1], b)
+        W = t["T"] @ (b[:, None] * t["KG"])
+        Ut = t["T"] @ (b[:, None] * V)
         U = Ut - W @ S
-        o[c0:c1] = scale * (Qp @ S + M @ U)
-        S = np.exp(G[-1])[:, None] * S + (K * np.exp(G[-1] - G)).T @ U
+        o[c0:c1] = scale * (t["QG"] @ S + t["M"] @ U)
+        S = t["Gn"][:, None] * S + t["KE"].T @ U
     return o, S
 
 

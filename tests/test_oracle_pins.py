@@ -311,3 +311,37 @@ def test_pins_detect_planted_mistakes(kind):
     ob, Sb = oracle.bruteforce_np(q, k, v, g, beta, 0.5, S0)
     om, Sm = _mutant(q, k, v, g, beta, 0.5, S0, kind)
     assert np.max(np.abs(om - ob)) > 1e-3
+
+
+def test_chunk_terms_against_direct_sums():
+    """The per-chunk quantities of the chunked form, against sums written out
+    entry by entry with the decay between tokens as a product of per-token
+    gates (no division), on a tiny chunk: A_ri = beta_r sum_c k_r k_i
+    prod_{i<j<=r} alpha_j, M_ri likewise with q_r and i <= r, T (I + A) = I,
+    KE = k * prod_{j>i} alpha_j, Gn = prod_j alpha_j."""
+    rng = np.random.default_rng(77)
+    n, dk = 6, 3
+    Q, K = rng.standard_normal((n, dk)), rng.standard_normal((n, dk))
+    g = -rng.uniform(0.05, 2.0, (n, dk))
+    b = rng.uniform(0.1, 1.0, n)
+    t = oracle.chunk_terms_np(Q, K, g, b)
+    al = np.exp(g)
+    A = np.zeros((n, n))
+    M = np.zeros((n, n))
+    for r in range(n):
+        for i in range(r + 1):
+            for c in range(dk):
+                p = 1.0
+                for j in range(i + 1, r + 1):
+                    p *= al[j, c]
+                M[r, i] += Q[r, c] * K[i, c] * p
+                if i < r:
+                    A[r, i] += b[r] * K[r, c] * K[i, c] * p
+    assert np.allclose(t["A"], A, rtol=1e-12, atol=1e-14)
+    assert np.allclose(t["M"], M, rtol=1e-12, atol=1e-14)
+    assert np.allclose(t["T"] @ (np.eye(n) + A), np.eye(n), atol=1e-12)
+    KE = K * np.array([[np.prod(al[i + 1:, c]) for c in range(dk)] for i in range(n)])
+    assert np.allclose(t["KE"], KE, rtol=1e-12)
+    assert np.allclose(t["Gn"], np.prod(al, axis=0), rtol=1e-12)
+    assert np.allclose(t["KG"], K * np.cumprod(al, axis=0), rtol=1e-12)
+    assert np.allclose(t["QG"], Q * np.cumprod(al, axis=0), rtol=1e-12)
