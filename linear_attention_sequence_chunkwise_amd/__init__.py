@@ -56,6 +56,9 @@ SIGNATURES = {
                                  _P, _P, _P, _SZ, _PREP, _EPI, _I, _P]),
     "kda_chunk_fwd_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P,
                                    _I, _P, _P, _P]),
+    "kda_debug_chunk_intra_floats": (_SZ, [_I, _I]),
+    "kda_debug_chunk_intra_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "kda_debug_chunk_intra": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "kda_chunk_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "kda_chunk_bwd": (_I, [_I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P, _I,
                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -306,6 +309,45 @@ def kda_chunk_fwd_noalloc(q, k, v, g, beta, o, final_state=None, scale=None, chu
     if rc != KDA_OK:
         raise KDAError("kda_chunk_fwd_noalloc", rc)
     return o, final_state
+
+
+def kda_debug_chunk_intra(q, k, g, beta, chunk=64, stream=None):
+    """Diagnostics (include/kda_debug.h): the intra-chunk kernel alone, its
+    per-(chunk, head) results unpacked to fp32.  q, k, g [B, T, H, dk]; beta
+    [B, T, H].  Returns a dict of tensors shaped [B, nchunk, H, ...]: KG, QG
+    [C, dk]; KP [dk, C]; TB, MM, T, P [C, C]; GN [dk]."""
+    lib = load_library()
+    B, T, H, dk = _dims(q, "q", 4)
+    dev = q.device
+    _check(q, "q", None, dev)
+    _check(k, "k", q.dtype, dev, (B, T, H, dk))
+    _check(g, "g", torch.float32, dev, (B, T, H, dk))
+    _check(beta, "beta", torch.float32, dev, (B, T, H))
+    _on_gpu(q, "q")
+    C = chunk
+    code = _dtype_code(q)
+    per = int(lib.kda_debug_chunk_intra_floats(dk, C))
+    need = int(lib.kda_debug_chunk_intra_workspace_bytes(B, T, H, dk, C, code))
+    if per == 0 or (need == 0 and T > 0):
+        raise KDAError("kda_debug_chunk_intra", 3)
+    nch = (T + C - 1) // C
+    with _alloc_stream(stream):
+        out = torch.zeros(B * nch * H * per, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    rc = lib.kda_debug_chunk_intra(B, T, H, dk, C, code, _ptr(q), _ptr(k), _ptr(g), _ptr(beta),
+                                   _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+    if rc != KDA_OK:
+        raise KDAError("kda_debug_chunk_intra", rc)
+    out = out.view(B, nch, H, per)
+    res, off = {}, 0
+    for name, shape in (("KG", (C, dk)), ("QG", (C, dk)), ("KP", (dk, C)), ("TB", (C, C)),
+                        ("MM", (C, C)), ("GN", (dk,)), ("T", (C, C)), ("P", (C, C))):
+        n = 1
+        for x in shape:
+            n *= x
+        res[name] = out[..., off:off + n].reshape(B, nch, H, *shape)
+        off += n
+    return res
 
 
 def kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk, num_seqs=0, dtype=torch.bfloat16):

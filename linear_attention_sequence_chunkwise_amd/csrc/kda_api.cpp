@@ -3,6 +3,7 @@
 // the first HIP call, so a rejected call touches neither the device nor the
 // caller's buffers.
 #include "kda.h"
+#include "kda_debug.h"
 
 #include <math.h>
 #include <stdint.h>
@@ -233,6 +234,46 @@ kda_status kda_chunk_fwd_noalloc(int B, int T, int H, int dk, int dv, int chunk,
     return chunk_fwd(B, T, H, dk, dv, chunk, scale, qkv_dtype, q, k, v, g, beta, initial_state,
                      cu_seqlens, num_seqs, o, final_state, ws, kScratchBytes, nullptr, nullptr,
                      KDA_CHAIN_AUTO, stream);
+}
+
+size_t kda_debug_chunk_intra_floats(int dk, int chunk) {
+    if (!kda::prefill_supported(dk, chunk, true)) return 0;
+    return kda::debug_intra_out_floats(dk, chunk);
+}
+
+size_t kda_debug_chunk_intra_workspace_bytes(int B, int T, int H, int dk, int chunk,
+                                             kda_dtype qkv_dtype) {
+    if (B < 1 || T < 0 || H < 1) return 0;
+    if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return 0;
+    if (!kda::prefill_supported(dk, chunk, qkv_dtype == KDA_BF16)) return 0;
+    return kda::debug_intra_workspace(B, T, H, dk, chunk, qkv_dtype == KDA_BF16);
+}
+
+kda_status kda_debug_chunk_intra(int B, int T, int H, int dk, int chunk, kda_dtype qkv_dtype,
+                                 const void* q, const void* k, const float* g,
+                                 const float* beta, float* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    if (B < 1 || T < 0 || H < 1 || dk < 1) return KDA_ERR_BAD_SHAPE;
+    if ((long long)B * T * H * (long long)dk >= (1LL << 40)) return KDA_ERR_BAD_SHAPE;
+    if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+    if (!kda::prefill_supported(dk, chunk, qkv_dtype == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+    if ((long long)chunk * H * dk * 4 >= (1LL << 31)) return KDA_ERR_BAD_SHAPE;
+    if ((long long)B * ((T + chunk - 1) / chunk) * H >= (1LL << 24)) return KDA_ERR_BAD_SHAPE;
+    if ((long long)B * T == 0) return KDA_OK;
+    if (!q || !k || !g || !beta || !out) return KDA_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(g) || !aligned16(out)) return KDA_ERR_NULL_ARG;
+    const size_t need = kda::debug_intra_workspace(B, T, H, dk, chunk, qkv_dtype == KDA_BF16);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return KDA_ERR_WORKSPACE;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+    kda::PrefillArgs a = {};
+    a.B = B; a.T = T; a.H = H; a.D = dk; a.C = chunk; a.scale = 1.f;
+    a.bf16 = qkv_dtype == KDA_BF16;
+    a.q = q; a.k = k; a.v = nullptr; a.g = g; a.beta = beta;
+    a.N = B;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.stream = stream;
+    return from_hip(kda::launch_debug_intra(a, out));
 }
 
 kda_status kda_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk, float scale,

@@ -121,6 +121,10 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan);
 int prefill_chain_segments(const PrefillPlan& plan);
 // Whether chain form `form` (a kda_chain_form code) is built for (D, C, dtype).
 bool prefill_chain_form_ok(int D, int C, bool bf16, int form);
+// Diagnostics (kda_debug.h): the records kernel alone, its results unpacked.
+size_t debug_intra_workspace(int B, int T, int H, int D, int C, bool bf16);
+size_t debug_intra_out_floats(int D, int C);
+hipError_t launch_debug_intra(const PrefillArgs& a, float* out);
 hipError_t launch_decode(const DecodeArgs& a);
 // True when (D, C, dtype) has built backward kernels that fit in LDS.
 bool backward_supported(int D, int C, bool bf16);

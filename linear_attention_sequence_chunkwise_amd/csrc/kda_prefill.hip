@@ -3386,6 +3386,124 @@ hipError_t launch_backward(const BackwardArgs& b, const BackwardPlan& plan) {
     return hipErrorInvalidValue;
 }
 
+// ---- diagnostics: the records kernel's results in plain layouts ----
+// Per (chunk, head), fp32: KG [C][D], QG [C][D], the KPt slot [D][C] (KPt, or
+// W = KPt Tb for fp16 records), the Tb slot [C][C] (zero for fp16 records),
+// the M slot [C][C] (M, or M Tb), Gamma_n [D], then T [C][C] and the
+// unscaled strict-lower k.k^T Gram P [C][C] from the kernel's side output.
+// Record columns come back in logical order; T and P above the diagonal are
+// written as zero.
+constexpr size_t debug_intra_floats(int D, int C) {
+    return 3 * (size_t)C * D + 4 * (size_t)C * C + D;
+}
+
+template <int D, int C, typename OT>
+__global__ __launch_bounds__(256) void kda_debug_unpack(const char* __restrict__ records,
+                                                        const float* __restrict__ aux,
+                                                        float* __restrict__ out) {
+    typedef Rec<D, C, OT> R;
+    constexpr int EPV = 16 / (int)sizeof(OT);
+    constexpr int CK = R::CK;
+    const size_t i = blockIdx.x;
+    const OT* rec = reinterpret_cast<const OT*>(records + i * R::bytes);
+    const float* ax = aux + i * 2 * C * C;
+    float* dst = out + i * debug_intra_floats(D, C);
+    float* kg = dst;
+    float* qg = kg + C * D;
+    float* kp = qg + C * D;
+    float* tb = kp + D * C;
+    float* mm = tb + C * C;
+    float* gn = mm + C * C;
+    float* tt = gn + D;
+    float* pp = tt + C * C;
+    for (int idx = threadIdx.x; idx < C * D; idx += 256) {
+        const int r = idx / D, s = idx % D;
+        const int c = group_col<OT>(s - s % EPV, s % EPV);
+        kg[r * D + c] = (float)rec[R::KG + swz<OT, D>(r, s)];
+        qg[r * D + c] = (float)rec[R::QG + swz<OT, D>(r, s)];
+    }
+    for (int idx = threadIdx.x; idx < D * CK; idx += 256) {
+        const int r = idx / CK, s = idx % CK;
+        const int t = group_col<OT>(s - s % EPV, s % EPV);
+        if (t < C) kp[r * C + t] = (float)rec[R::KPt + swz<OT, CK>(r, s)];
+    }
+    for (int idx = threadIdx.x; idx < C * CK; idx += 256) {
+        const int r = idx / CK, s = idx % CK;
+        const int t = group_col<OT>(s - s % EPV, s % EPV);
+        if (t < C) {
+            tb[r * C + t] = R::FOLD ? 0.f : (float)rec[R::Tb + swz<OT, CK>(r, s)];
+            mm[r * C + t] = (float)rec[R::M + swz<OT, CK>(r, s)];
+        }
+    }
+    const float* gr = reinterpret_cast<const float*>(reinterpret_cast<const char*>(rec) + R::gn_byte);
+    for (int c = threadIdx.x; c < D; c += 256) gn[c] = gr[c];
+    for (int idx = threadIdx.x; idx < C * C; idx += 256) {
+        const int r = idx / C, c = idx % C;
+        tt[idx] = c <= r ? ax[idx] : 0.f;
+        pp[idx] = c < r ? ax[C * C + idx] : 0.f;
+    }
+}
+
+template <int D, int C, typename OT, typename IT>
+static hipError_t launch_debug_dc(const PrefillArgs& a, float* out) {
+    if constexpr (!fits<D, C, OT>()) {
+        return hipErrorInvalidValue;
+    } else {
+        const int nch_seq = (a.T + C - 1) / C;
+        const long long n = (long long)a.B * nch_seq * a.H;
+        if (n == 0) return hipSuccess;
+        char* rec = (char*)a.workspace;
+        float* aux = reinterpret_cast<float*>(rec + (size_t)n * Rec<D, C, OT>::bytes);
+        const size_t smem = intra_smem_bytes<D, C, OT>();
+        auto kern = kda_intra<D, C, OT, IT, false>;
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(256), smem, a.stream, a.T, a.H, nch_seq,
+                           (const ChunkInfo*)nullptr, (const int*)nullptr, (const IT*)a.q,
+                           (const IT*)a.k, a.g, a.beta, rec, aux, Prep());
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        auto unpack = kda_debug_unpack<D, C, OT>;
+        hipLaunchKernelGGL(unpack, dim3((unsigned)n), dim3(256), 0, a.stream, (const char*)rec,
+                           (const float*)aux, out);
+        return hipGetLastError();
+    }
+}
+
+template <int D, typename OT, typename IT>
+static hipError_t launch_debug_d(const PrefillArgs& a, float* out) {
+    switch (a.C) {
+        case 16: return launch_debug_dc<D, 16, OT, IT>(a, out);
+        case 32: return launch_debug_dc<D, 32, OT, IT>(a, out);
+        case 64: return launch_debug_dc<D, 64, OT, IT>(a, out);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+size_t debug_intra_workspace(int B, int T, int H, int D, int C, bool bf16) {
+    const size_t n = (size_t)B * ((T + C - 1) / C) * H;
+    return n * (rec_bytes(D, C, bf16) + 2 * (size_t)C * C * sizeof(float));
+}
+
+size_t debug_intra_out_floats(int D, int C) { return debug_intra_floats(D, C); }
+
+hipError_t launch_debug_intra(const PrefillArgs& a, float* out) {
+    if (a.bf16) {
+        switch (a.D) {
+            case 32: return launch_debug_d<32, _Float16, bf16_t>(a, out);
+            case 64: return launch_debug_d<64, _Float16, bf16_t>(a, out);
+            case 128: return launch_debug_d<128, _Float16, bf16_t>(a, out);
+        }
+    } else {
+        switch (a.D) {
+            case 32: return launch_debug_d<32, float, float>(a, out);
+            case 64: return launch_debug_d<64, float, float>(a, out);
+            case 128: return launch_debug_d<128, float, float>(a, out);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan) {
     if (a.bf16) {
         switch (a.D) {

@@ -11,10 +11,11 @@ import linear_attention_sequence_chunkwise_amd as kda
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
+DEBUG_HEADER = os.path.join(ROOT, "include", "kda_debug.h")
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
 
@@ -39,6 +40,23 @@ def test_exports_every_declared_symbol(lib):
     for n in names:
         assert hasattr(lib, n), n
         assert n in kda.SIGNATURES, n
+
+
+def test_exports_debug_symbols(lib):
+    names = header_functions(DEBUG_HEADER)
+    assert set(names) == {"kda_debug_chunk_intra_floats", "kda_debug_chunk_intra_workspace_bytes",
+                          "kda_debug_chunk_intra"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in kda.SIGNATURES, n
+    assert lib.kda_debug_chunk_intra_floats(128, 64) == 3 * 64 * 128 + 4 * 64 * 64 + 128
+    assert lib.kda_debug_chunk_intra_floats(48, 64) == 0
+    E = {v: k for k, v in kda.STATUS_NAMES.items()}
+    p = ctypes.c_void_p(4096)
+    assert lib.kda_debug_chunk_intra(1, 64, 2, 64, 128, kda.KDA_BF16, p, p, p, p, p, p, 1 << 30,
+                                     None) == E["KDA_ERR_UNSUPPORTED"]
+    assert lib.kda_debug_chunk_intra(1, 64, 2, 64, 64, kda.KDA_BF16, p, p, p, p, p, p, 16,
+                                     None) == E["KDA_ERR_WORKSPACE"]
 
 
 def test_status_strings(lib):
