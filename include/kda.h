@@ -72,11 +72,21 @@ typedef enum {
     KDA_ERR_BAD_DTYPE = 4,    /* dtype code not in kda_dtype                 */
     KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required     */
     KDA_ERR_HIP = 6,          /* the HIP runtime reported an error           */
-    KDA_ERR_SCRATCH = 7       /* kda_chunk_fwd_noalloc: the call's workspace
+    KDA_ERR_SCRATCH = 7,      /* kda_chunk_fwd_noalloc: the call's workspace
                                  exceeds KDA_NOALLOC_SCRATCH_BYTES           */
+    KDA_STATUS_INT_MIN_ = -2147483647 - 1,
+    KDA_STATUS_INT_MAX_ = 2147483647
 } kda_status;
 
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+/* The enums below span the whole int range (the _INT_MIN/_INT_MAX members are
+ * never valid arguments): a C caller may pass any int, and the library's
+ * range checks of such a value stay well defined in C++. */
+typedef enum {
+    KDA_F32 = 0,
+    KDA_BF16 = 1,
+    KDA_DTYPE_INT_MIN_ = -2147483647 - 1,
+    KDA_DTYPE_INT_MAX_ = 2147483647
+} kda_dtype;
 
 /* Optional input preparation done inside the kernels -- the per-token steps
  * a Kimi Linear layer applies to the operator's inputs (GeekNews summary of
@@ -282,7 +292,9 @@ typedef enum {
     KDA_CHAIN_SLICE_REG32 = 2,   /* bf16 inputs                               */
     KDA_CHAIN_SLICE_REG64 = 3,   /* bf16 inputs, dk >= 64                     */
     KDA_CHAIN_SLICE_DMA16 = 4,   /* bf16 inputs, where two records fit LDS    */
-    KDA_CHAIN_SLICE_DMA32 = 5    /* bf16 inputs, where two records fit LDS    */
+    KDA_CHAIN_SLICE_DMA32 = 5,   /* bf16 inputs, where two records fit LDS    */
+    KDA_CHAIN_INT_MIN_ = -2147483647 - 1,
+    KDA_CHAIN_INT_MAX_ = 2147483647
 } kda_chain_form;
 
 /* kda_chunk_fwd_ex with the chain form chosen by the caller (a testing and

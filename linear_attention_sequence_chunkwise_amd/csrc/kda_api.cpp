@@ -96,6 +96,8 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_SCRATCH:
             return "KDA_ERR_SCRATCH: the call needs more workspace than the fixed scratch of "
                    "kda_chunk_fwd_noalloc";
+        default:
+            break;
     }
     return "KDA_ERR_UNKNOWN";
 }
