@@ -45,7 +45,11 @@ __device__ __forceinline__ float exp_e(float x) {
 __device__ __forceinline__ float softplus_f(float x) {
     return fmaxf(x, 0.f) + 0.6931471805599453f * __builtin_amdgcn_logf(1.f + exp_e(-fabsf(x)));
 }
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + exp_e(-x)); }
+// 1 / (1 + e^-x) with the hardware reciprocal (about 1 ulp; 0 when e^-x
+// overflows, 1 when it underflows).
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return __builtin_amdgcn_rcpf(1.f + exp_e(-x));
+}
 // 1 / sqrt(s) for s > 0 and 0 for s == 0, so that a zero vector stays zero.
 __device__ __forceinline__ float rnorm(float s) { return s > 0.f ? rsqrtf(s) : 0.f; }
 

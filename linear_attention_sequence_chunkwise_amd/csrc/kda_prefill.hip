@@ -240,6 +240,31 @@ __device__ __forceinline__ void reduce_scatter(float (&v)[NV], int lane) {
     }
 }
 
+// The same scattered sum within each 16-lane DPP row (NV <= 16 values, a
+// power of two), partners from mirror permutes (each pairs lanes with the
+// opposite stride bit and the same higher bits): on return lane l of the row
+// holds in v[0] the row sum of value l / (16 / NV).
+template <int NV, int S = 8, int CNT = NV>
+__device__ __forceinline__ void row16_reduce_scatter(float (&v)[NV], int l16) {
+    if constexpr (S >= 1) {
+        constexpr int CTRL = S == 8 ? 0x140 : S == 4 ? 0x141 : S == 2 ? 0x1B : 0xB1;
+        if constexpr (CNT > 1) {
+            constexpr int H = CNT / 2;
+            const bool up = (l16 & S) != 0;
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                const float keep = up ? v[H + j] : v[j];
+                const float send = up ? v[j] : v[H + j];
+                v[j] = keep + dpp_f<CTRL>(send);
+            }
+            row16_reduce_scatter<NV, S / 2, H>(v, l16);
+        } else {
+            v[0] += dpp_f<CTRL>(v[0]);
+            row16_reduce_scatter<NV, S / 2, 1>(v, l16);
+        }
+    }
+}
+
 // Row r and column i (i <= r) of the p-th entry of a 16 x 16 lower triangle
 // enumerated row by row, each row from its diagonal down to column 0:
 // p = r (r + 1) / 2 + (r - i).
@@ -1555,10 +1580,14 @@ struct SegShape {
 
 template <int D, int C, typename OT, typename IT, bool OUT>
 struct SegSmem {
+    static constexpr int VBYTES = (ValueCopy<C, IT, SegShape<D, OUT>::NVB>::BYTES + 1023) / 1024 * 1024;
     alignas(1024) char img[2][WideTiles<D, C, OT, OUT>::KIB * 1024];
-    alignas(1024) char vals[SegShape<D, OUT>::NW]
-                           [(ValueCopy<C, IT, SegShape<D, OUT>::NVB>::BYTES + 1023) / 1024 * 1024];
-    float part[2][OUT ? C : 1][SegShape<D, OUT>::NW];   // fused epilogue: per-wave row sums of o^2
+    alignas(1024) char vals[SegShape<D, OUT>::NW][VBYTES];
+    // fused epilogue: each wave's gate columns of the chunk being finished
+    // (laid out like its value columns), and per-wave row sums of o^2
+    alignas(1024) char gates[OUT ? SegShape<D, OUT>::NW : 1][OUT ? VBYTES : 16];
+    float part[2][OUT ? C : 1][SegShape<D, OUT>::NW];
+    float rsc[OUT ? SegShape<D, OUT>::NW : 1][OUT ? C : 1];   // per-wave row scales
 };
 
 // EPI (pass 3 only): the output epilogue (per-row RMS norm over dv, weight,
@@ -1659,49 +1688,44 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
     float4v oprev[EPI ? SS::NCB : 1][EPI ? RT : 1];
     bool have_prev = false;
     int ptok0 = 0, plen = 0;
-    // this lane's gate entries of the rows of the chunk at tok0 (len rows)
-    auto load_gate = [&](uint32_t (&zr)[EPI ? SS::NCB : 1][EPI ? RT : 1][4], int tok0, int len) {
+    // the gate columns of this wave for the rows of the chunk at tok0 (len
+    // rows), copied into its gate region like its value columns
+    const IT* gl = reinterpret_cast<const IT*>(sm.gates[OUT ? wave : 0]);
+    auto load_gate = [&](int tok0, int len) {
         if constexpr (EPI) {
             if (!gate) return;
-#pragma unroll
-            for (int b = 0; b < SS::NCB; ++b)
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r = min(16 * rt + 4 * lq + j, len - 1);
-                        const IT* zp = gate + ((size_t)(tok0 + r) * H + h) * D + cbase + 16 * b + l16;
-                        if constexpr (sizeof(IT) == 2)
-                            zr[b][rt][j] = reinterpret_cast<const bf16_t*>(zp)->bits;
-                        else
-                            zr[b][rt][j] = __builtin_bit_cast(uint32_t, *reinterpret_cast<const float*>(zp));
-                    }
+            ValueCopy<C, IT, SS::NVB>::issue(gate + ((size_t)tok0 * H + h) * D + cbase,
+                                             (size_t)H * D, len, lds_addr(sm.gates[wave]));
         }
     };
     // y = o / sqrt(mean over dv of o^2 + eps) * weight * sigmoid(gate) for
     // the rows of a finished chunk; part: every wave's row sums of that chunk
     auto finish = [&](const float4v (&ov)[EPI ? SS::NCB : 1][EPI ? RT : 1],
-                      const uint32_t (&zr)[EPI ? SS::NCB : 1][EPI ? RT : 1][4],
                       const float (&part)[OUT ? C : 1][SS::NW], int tok0, int len) {
         if constexpr (EPI) {
+            // lane r totals row r over the waves' sums (every wave does this
+            // for all C rows: 64 lanes, C <= 64) and leaves the row's scale in
+            // its own table, from which each lane reads the scales of its rows
+            if (lane < C) {
+                float tot = 0.f;
+#pragma unroll
+                for (int w = 0; w < SS::NW; ++w) tot += part[lane][w];
+                sm.rsc[wave][lane] = rnorm(tot * (1.f / D) + eps);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * rt + 4 * lq + j;
-                    float tot = 0.f;
-#pragma unroll
-                    for (int w = 0; w < SS::NW; ++w) tot += part[r][w];
-                    const float rs = rnorm(tot * (1.f / D) + eps);
+                    const float rs = sm.rsc[wave][r];
 #pragma unroll
                     for (int b = 0; b < SS::NCB; ++b) {
                         const int col = cbase + 16 * b + l16;
                         float y = ov[b][rt][j] * rs * wt[b];
-                        if (gate) {
-                            const float z = sizeof(IT) == 2 ? __builtin_bit_cast(float, zr[b][rt][j] << 16)
-                                                            : __builtin_bit_cast(float, zr[b][rt][j]);
-                            y *= sigmoid_f(z);
-                        }
+                        if (gate) y *= sigmoid_f(to_f32(gl[r * 16 * SS::NVB + 16 * b + l16]));
                         if (r < len) o[((size_t)(tok0 + r) * H + h) * D + col] = y;
                     }
                 }
@@ -1729,13 +1753,12 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
         // buffer the copies of chunk c + 1 then refill
         asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
         lds_barrier();
-        // fused epilogue: this lane's gate entries of the previous chunk's rows
-        // (rows clamped to that chunk), finished at the end of this chunk.
-        // Issued before the next chunk's copies: the memory counter retires in
-        // order, so waiting for the gate then does not wait for those copies.
-        uint32_t zr[EPI ? SS::NCB : 1][EPI ? RT : 1][4];
+        // fused epilogue: this wave's gate columns of the previous chunk's
+        // rows, finished at the end of this chunk (its own reads of the gate
+        // region, at the end of the previous chunk, are done: the barrier
+        // waited for them)
         if constexpr (EPI) {
-            if (have_prev) load_gate(zr, ptok0, plen);
+            if (have_prev) load_gate(ptok0, plen);
         }
         if (c + 1 < c1) copy_record(c + 1, bi ^ 1);
         float4v oo[SS::NCB][RT];
@@ -1746,18 +1769,32 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
         if constexpr (EPI) {
             // the previous chunk's rows: every wave's sums were published by
             // the barrier at this chunk's start
-            if (have_prev) finish(oprev, zr, sm.part[bi ^ 1], ptok0, plen);
-            // this wave's sums of squares per row of the chunk, into the parity buffer
+            if (have_prev) {
+                // this wave's gate copies (issued at the chunk's start, before
+                // the record and value copies) have landed; those later copies
+                // are due by now as well
+                asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+                finish(oprev, sm.part[bi ^ 1], ptok0, plen);
+            }
+            // this wave's sums of squares per row of the chunk, into the parity
+            // buffer: the 16 lanes of a DPP row hold the same 4 RT rows, one
+            // column each; a scattered sum leaves lane l16 with row entry l16
+            float ss[4 * RT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    float ss = 0.f;
+                    float x = 0.f;
 #pragma unroll
-                    for (int b = 0; b < SS::NCB; ++b) ss += oo[b][rt][j] * oo[b][rt][j];
-                    ss = group_sum<16>(ss);
-                    if (l16 == 0) sm.part[bi][16 * rt + 4 * lq + j][wave] = ss;
+                    for (int b = 0; b < SS::NCB; ++b) x += oo[b][rt][j] * oo[b][rt][j];
+                    ss[4 * rt + j] = x;
                 }
+            row16_reduce_scatter<4 * RT>(ss, l16);
+            constexpr int SPAN = 16 / (4 * RT);   // lanes holding the same entry
+            if (l16 % SPAN == 0) {
+                const int e = l16 / SPAN;          // entry 4 rt + j
+                sm.part[bi][16 * (e / 4) + 4 * lq + (e % 4)][wave] = ss[0];
+            }
 #pragma unroll
             for (int b = 0; b < SS::NCB; ++b)
 #pragma unroll
@@ -1769,10 +1806,10 @@ __global__ __launch_bounds__((64 * SegShape<D, OUT>::NW)) void kda_seg_chain(
     }
     if constexpr (EPI) {
         if (have_prev) {   // the last chunk: every wave's sums, then its rows
-            uint32_t zr[SS::NCB][RT][4];
-            load_gate(zr, ptok0, plen);
+            load_gate(ptok0, plen);
+            asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // the gate copies have landed
             lds_barrier();
-            finish(oprev, zr, sm.part[(c1 - 1 - c0) & 1], ptok0, plen);
+            finish(oprev, sm.part[(c1 - 1 - c0) & 1], ptok0, plen);
         }
     }
 #pragma unroll
