@@ -297,7 +297,8 @@ def bench_prefill_varlen(kda, kda_inputs, steps, warmup, stream):
                 hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, algorithmic_bytes=nbytes,
                 chain_form=kda.kda_chunk_fwd_segments(B, T, H, D, D, 64, N),
                 workload="packed prefill: %d sequences, %d tokens (lengths U[256, 8192], seeded), "
-                         "H=32 dk=dv=128 chunk=64 bf16, per-sequence final states" % (N, T))
+                         "H=32 dk=dv=128 chunk=64 bf16, per-sequence final states" % (N, T),
+                inputs=d)
 
 
 def bench_prefill_prep(kda, kda_inputs, steps, warmup, stream, with_epilogue=False):
@@ -540,6 +541,24 @@ def cpu_baseline_prefill(d, target_s=10.0):
                        "%.2f s" % (Ts, T, reps, dt))
 
 
+def cpu_baseline_packed(d, target_s=5.0):
+    """The fp64 oracle on the packed 16-sequence layer, whole (all sequences
+    and heads), repeated until about target_s seconds have run."""
+    import oracle
+    cu = d["cu_seqlens"].cpu().numpy()
+    q, k, v, g, b = (d[n].float().cpu().numpy() for n in ("q", "k", "v", "g", "beta"))
+    T = q.shape[1]
+    dt, reps = 0.0, 0
+    while dt < target_s:
+        t0 = time.perf_counter()
+        oracle.kda_fwd(q, k, v, g, b, 128 ** -0.5, cu_seqlens=cu)
+        dt += time.perf_counter() - t0
+        reps += 1
+    return dict(value=T * reps / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample="packed prefill, all %d sequences x 32 heads (%d tokens), %d run(s), %.2f s"
+                       % (cu.shape[0] - 1, T, reps, dt))
+
+
 def cpu_baseline_decode(kda_inputs, target_s=6.0):
     import numpy as np
     import oracle
@@ -665,10 +684,14 @@ def main():
                      "(kda_decode_step_ex)")
 
     cpu = None
+    packed_inputs = pf_var.pop("inputs") if pf_var is not None else None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_prefill(pf["inputs"])
+        if pf_var is not None:
+            pf_var["cpu_baseline"] = cpu_baseline_packed(packed_inputs)
         if dec is not None:
             dec["cpu_baseline"] = cpu_baseline_decode(kda_inputs)
+    del packed_inputs
 
     out = {
         "metric": "KDA prefill tokens/s (H=32, d=128)",

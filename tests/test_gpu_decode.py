@@ -93,14 +93,29 @@ def test_config4_decode_workload():
     x 128 x 128 cache filled by a 4096-token prefill per sequence (32 per call),
     then 512 decode steps with fresh inputs.  Every chain (8192) is recomputed
     by the oracle -- prefill over the same 4096 tokens, then the 512 steps --
-    and compared at every step's output and in the final state, jointly."""
+    and compared at every step's output and in the final state, jointly.  To
+    separate the decode's own error from the prefill's, the oracle's steps are
+    also run from the GPU's prefill states for the first 32 sequences, held to
+    the fp32 bound."""
     import bench
     stream = torch.cuda.current_stream()
     n_steps = 512
     cache, steps, o = bench.decode_setup(kda, kda_inputs, n_steps, stream)
+    nd = 32   # decode-only check: the oracle's steps restarted from the GPU's prefill states
+    gpu_init = cache[:nd].double().cpu().numpy()
     bench.decode_run(kda, cache, steps, o, stream)
     torch.cuda.synchronize()
     N, D = cache.shape[0], cache.shape[-1]
+    st = gpu_init.copy()
+    o_dec = np.empty((n_steps, nd) + tuple(o.shape[2:]))
+    for s in range(n_steps):
+        x = {name: np32(steps[s][name][:nd]) for name in ("q", "k", "v", "g", "beta")}
+        o_dec[s] = oracle.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], D ** -0.5, st)
+    e_dec = rel_err(o[:, :nd].cpu().numpy(), o_dec)
+    e_dst = rel_err(cache[:nd].cpu().numpy(), st)
+    print("decode alone (from the GPU's prefill states): err_o %.2e err_S %.2e" % (e_dec, e_dst),
+          flush=True)
+    assert e_dec < 1e-5 and e_dst < 1e-5
     NB = bench.DECODE_INIT_BATCH
     ref_state = []
     for b0 in range(0, N, NB):
