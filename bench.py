@@ -51,6 +51,11 @@ def parse():
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="read rocprofv3 FETCH_SIZE/WRITE_SIZE runs of the three profile "
                          "targets from DIR/<target>_<counter>/ and write profiles/traffic.json")
+    ap.add_argument("--stats-from", metavar="CSV",
+                    help="print a rocprofv3 --stats kernel_stats.csv as a table and exit")
+    ap.add_argument("--mfma-from", metavar="CSV",
+                    help="print a rocprofv3 --pmc run of matrix-core counters "
+                         "(counter_collection.csv) as a per-kernel table and exit")
     return ap.parse_args()
 
 
@@ -150,6 +155,84 @@ def traffic_from(d):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def kernel_label(name):
+    """Readable label of a KDA kernel from its (mangled) name: base name,
+    <dk,chunk>, record type and the variant flags."""
+    import re
+    m = re.search(r"(kda_[a-z_]+?|decode_step_kernel)(?:I|\(|<|$)", name)
+    if m is None:
+        return name[:60]
+    base = m.group(1)
+    targs = re.search(re.escape(base) + r"<([^>(]*)>", name)
+    if targs:   # demangled: <128, 64, float, kda::bf16_t, false>
+        args = [a.strip() for a in targs.group(1).split(",")]
+        dims = [a for a in args if a.isdigit()][:2]
+        ot = ("fp16 records" if "_Float16" in args else
+              "fp32 records" if "float" in args and base not in ("kda_seg_combine",) else "")
+        flags = ["1" if a == "true" else "0" for a in args if a in ("true", "false")]
+    else:       # mangled: ILi128ELi64EDF16_...Lb1E
+        dims = re.findall(r"Li(\d+)E", name)
+        ot = "fp16 records" if "DF16_" in name else ("fp32 records" if "Eff" in name else "")
+        flags = re.findall(r"Lb([01])E", name)
+    extra = []
+    if base == "kda_intra" and flags and flags[0] == "1":
+        extra.append("with preparation")
+    if base == "kda_seg_chain" and flags:
+        extra.append("with outputs (pass 3)" if flags[0] == "1" else "state runs (pass 1)")
+        if len(flags) > 1 and flags[1] == "1":
+            extra.append("fused epilogue")
+    parts = ", ".join([x for x in [ot] + extra if x])
+    return "%s<%s>%s" % (base, ",".join(dims[:2]), " (" + parts + ")" if parts else "")
+
+
+def stats_table(path):
+    """Markdown table of a rocprofv3 kernel_stats.csv (KDA kernels first)."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    print("| kernel | calls | avg us | min us | max us | % of GPU time |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        kda_k = "kda" in r["Name"] or "decode_step" in r["Name"]
+        name = kernel_label(r["Name"]) if kda_k else r["Name"][:50] + " (torch)"
+        if not kda_k and float(r["Percentage"]) < 1.0:
+            continue
+        print("| %s | %s | %.1f | %.1f | %.1f | %.2f |" % (
+            name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+
+
+def mfma_table(path, xcds=8, simds=1024):
+    """Per-kernel matrix-core table from a rocprofv3 --pmc counter_collection.csv
+    with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_F16/_F32,
+    SQ_INSTS_MFMA, SQ_INSTS_VALU, SQ_WAVES, GRBM_GUI_ACTIVE.  MFMA busy % =
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) (the CSV's
+    GRBM_GUI_ACTIVE sums the 8 XCDs' counters); TFLOP/s = 512 x MOPS / duration
+    (dense-tile flops, masked tiles included); VALU/wave = SQ_INSTS_VALU / SQ_WAVES."""
+    import collections
+    import csv
+    ctr = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for r in csv.DictReader(open(path)):
+        if "kda" not in r["Kernel_Name"]:
+            continue
+        key = kernel_label(r["Kernel_Name"])
+        ctr[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        dur[key][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    print("| kernel | dispatches | avg us | MFMA busy % | f16 TFLOP/s | f32 TFLOP/s | "
+          "MFMA instr | VALU/wave |")
+    print("|---|---|---|---|---|---|---|---|")
+    for key, c in ctr.items():
+        avg = {k: sum(v) / len(v) for k, v in c.items()}
+        us = sum(dur[key].values()) / len(dur[key])
+        busy = 100 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] / xcds * simds)
+        f16 = 512 * avg["SQ_INSTS_VALU_MFMA_MOPS_F16"] / us / 1e6
+        f32 = 512 * avg["SQ_INSTS_VALU_MFMA_MOPS_F32"] / us / 1e6
+        vpw = avg["SQ_INSTS_VALU"] / max(avg["SQ_WAVES"], 1)
+        print("| %s | %d | %.1f | %.1f | %.1f | %.1f | %.3g | %.0f |" % (
+            key, len(dur[key]), us, busy, f16, f32, avg["SQ_INSTS_MFMA"], vpw))
 
 
 def profile_target(kind):
@@ -590,6 +673,12 @@ def main():
         sys.exit(2)
     if args.traffic_from:
         traffic_from(args.traffic_from)
+        return
+    if args.stats_from:
+        stats_table(args.stats_from)
+        return
+    if args.mfma_from:
+        mfma_table(args.mfma_from)
         return
     if args.profile_target:
         profile_target(args.profile_target)
