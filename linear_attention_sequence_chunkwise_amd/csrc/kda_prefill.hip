@@ -2286,6 +2286,10 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
     }
     vec rb[RPT];
     float dov[NDO];
+    // rows of the fetched chunk: rows past it are zeroed when the fetched dO
+    // reaches LDS, not at the fetch (a select there would wait for the loads,
+    // and with them, in issue order, for the whole record fetch)
+    int dlen = 0;
     auto fetch = [&](int c) {
         const int tok0 = cp.seq_tok0 + c * C;
         const int len = min(C, cp.seq_len - c * C);
@@ -2296,9 +2300,9 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
         for (int i = 0; i < NDO; ++i) {
             const int idx = min(tid + NT * i, C * BV - 1);
             const int r = idx / BV, col = idx % BV;
-            const float x = d_o[((size_t)(tok0 + min(r, len - 1)) * H + cp.h) * D + cp.v0 + col];
-            dov[i] = r < len ? x : 0.f;
+            dov[i] = d_o[((size_t)(tok0 + min(r, len - 1)) * H + cp.h) * D + cp.v0 + col];
         }
+        dlen = len;
     };
     if (cp.nch > 0) fetch(cp.nch - 1);
     const float4v z = {0.f, 0.f, 0.f, 0.f};
@@ -2324,7 +2328,7 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
 #pragma unroll
         for (int i = 0; i < NDO; ++i) {
             const int idx = tid + NT * i;
-            if (idx < C * BV) sm.dO[(idx / BV) * LDV + idx % BV] = dov[i];
+            if (idx < C * BV) sm.dO[(idx / BV) * LDV + idx % BV] = idx / BV < dlen ? dov[i] : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
@@ -2664,15 +2668,18 @@ __global__ __launch_bounds__(64 * kBwdIntraWaves) void kda_bwd_intra(
         }
     }
     // phase 2 inputs of the first block, fetched early
-    float pg[EPT], pk[EPT], pq[EPT];
+    // (q and k stay in their input type until they reach LDS: converting
+    // them here would wait for the loads, and with them for the whole fetch)
+    float pg[EPT];
+    IT pk[EPT], pq[EPT];
     float pdkg[BPW][4], pdqg[BPW][4], pdke[RS];
     auto fetch = [&](int c0) {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const int idx = tid + NT * e, r = idx / CB, c = idx % CB;
             pg[e] = g[tok(r) + c0 + c];
-            pk[e] = to_f32(k[tok(r) + c0 + c]);
-            pq[e] = to_f32(q[tok(r) + c0 + c]);
+            pk[e] = k[tok(r) + c0 + c];
+            pq[e] = q[tok(r) + c0 + c];
         }
 #pragma unroll
         for (int i = 0; i < BPW; ++i) {
@@ -2782,8 +2789,8 @@ __global__ __launch_bounds__(64 * kBwdIntraWaves) void kda_bwd_intra(
         for (int e = 0; e < EPT; ++e) {
             const int idx = tid + NT * e, r = idx / CB, c = idx % CB;
             sm.u.c.G[r * LDB + c] = r < len ? pg[e] : 0.f;
-            sm.u.c.kg[r * LDB + c] = r < len ? pk[e] : 0.f;    // raw k for now
-            sm.u.c.qg[r * LDB + c] = r < len ? pq[e] : 0.f;    // raw q for now
+            sm.u.c.kg[r * LDB + c] = r < len ? to_f32(pk[e]) : 0.f;    // raw k for now
+            sm.u.c.qg[r * LDB + c] = r < len ? to_f32(pq[e]) : 0.f;    // raw q for now
         }
         float dkg[BPW][4], dqg[BPW][4], dke[RS];
 #pragma unroll
