@@ -1064,8 +1064,11 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
         if (!FOLD && tt < OTILES) {
             const int rt = tt / VT, vt = tt % VT;
             float4v uacc = {0.f, 0.f, 0.f, 0.f};
-            const int kend = 16 * (rt + 1);
-            for (int ks = 0; ks < kend; ks += mm::KS) {
+            // Tb is lower triangular and its upper part is stored as zeros:
+            // the whole k range, unrolled, so that the operand reads run ahead
+            // (a loop to the diagonal block exposes each read's latency)
+#pragma unroll
+            for (int ks = 0; ks < CK; ks += mm::KS) {
                 const int kk = ks + lq * mm::KPL;
                 uacc = mm::mma(load_swz<OT, CK>(t.tb, 16 * rt + l16, kk),
                                mm::load(cs.x, LDC, 16 * vt + l16, kk), uacc);
@@ -1086,8 +1089,10 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
         if (OUT && tt < OTILES) {
             const int rt = tt / VT, vt = tt % VT;
             float4v acc = qs[i];
-            const int kend = 16 * (rt + 1);
-            for (int ks = 0; ks < kend; ks += mm::KS) {
+            // (M, or M Tb, lower triangular with zeros stored above: the whole
+            // k range, unrolled, as for U)
+#pragma unroll
+            for (int ks = 0; ks < CK; ks += mm::KS) {
                 const int kk = ks + lq * mm::KPL;
                 acc = mm::mma(load_swz<OT, CK>(t.m, 16 * rt + l16, kk),
                               mm::load(ub_tile, LDC, 16 * vt + l16, kk), acc);
@@ -2346,12 +2351,10 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
             const int rt = jb % RT;
             float4v a;
             if (jb < RT)
-                a = tile_mma(z, 16 * rt, C,
-                             [&](int m, int k) { return (float)img[R::M + swz<OT, CK>(k, 16 * rt + m)]; },
+                a = tile_mma(z, 16 * rt, C, [&](int m, int k) { return (float)img[R::M + swz<OT, CK>(k, 16 * rt + m)]; },
                              [&](int k, int n) { return sm.dO[k * LDV + n]; });
             else
-                a = tile_mma(z, 0, D,
-                             [&](int m, int k) { return (float)img[R::KPt + swz<OT, CK>(k, 16 * rt + m)]; },
+                a = tile_mma(z, 0, D, [&](int m, int k) { return (float)img[R::KPt + swz<OT, CK>(k, 16 * rt + m)]; },
                              [&](int k, int n) { return sm.dS[k * LDV + n]; });
             float* dst = jb < RT ? sm.dUa : sm.dUb;
             const float f = jb < RT ? scale : 1.f;
