@@ -1089,13 +1089,23 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
         if (OUT && tt < OTILES) {
             const int rt = tt / VT, vt = tt % VT;
             float4v acc = qs[i];
-            // (M, or M Tb, lower triangular with zeros stored above: the whole
-            // k range, unrolled, as for U)
+            if constexpr (!FOLD) {
+                // (M lower triangular with zeros stored above: the whole k
+                // range, unrolled, as for U)
 #pragma unroll
-            for (int ks = 0; ks < CK; ks += mm::KS) {
-                const int kk = ks + lq * mm::KPL;
-                acc = mm::mma(load_swz<OT, CK>(t.m, 16 * rt + l16, kk),
-                              mm::load(ub_tile, LDC, 16 * vt + l16, kk), acc);
+                for (int ks = 0; ks < CK; ks += mm::KS) {
+                    const int kk = ks + lq * mm::KPL;
+                    acc = mm::mma(load_swz<OT, CK>(t.m, 16 * rt + l16, kk),
+                                  mm::load(ub_tile, LDC, 16 * vt + l16, kk), acc);
+                }
+            } else {
+                // (fp16: one or two 32-wide steps, up to the diagonal block)
+                const int kend = 16 * (rt + 1);
+                for (int ks = 0; ks < kend; ks += mm::KS) {
+                    const int kk = ks + lq * mm::KPL;
+                    acc = mm::mma(load_swz<OT, CK>(t.m, 16 * rt + l16, kk),
+                                  mm::load(ub_tile, LDC, 16 * vt + l16, kk), acc);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
