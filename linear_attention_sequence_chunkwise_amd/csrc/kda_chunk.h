@@ -221,7 +221,7 @@ template <int D, int C, int BV, typename OT>
 struct ChainScratch {
     static constexpr int LDK = padded<OT>(D);
     static constexpr int LDC = padded<OT>(chunk_k<C, OT>());
-    OT s[BV * LDK];      // state operand, [v][c]
+    alignas(16) OT s[BV * LDK];   // state operand, [v][c] (16-byte rows: fp32 reads four k at once)
     OT x[BV * LDC];      // V - KG S, [v][i]
     OT u[BV * LDC];      // U, [v][i]
 };

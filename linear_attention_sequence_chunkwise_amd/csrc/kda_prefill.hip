@@ -994,6 +994,28 @@ struct ChunkTiles {
 };
 
 
+// fp32 operands: acc += A[ra + (0..15)][0 .. NK) * B[rb + (0..15)][0 .. NK)^T
+// for one 16x16 output tile, A a swizzled [rows][LDA] record tile and B an
+// [n][ldb] operand in LDS, both with the contraction index along the row.
+// Each lane reads one 16-byte group of four consecutive k from each side per
+// 16 k, and the four 16x16x4 steps take k = 16 g + 4 (lane / 16) + s
+// (s = 0..3): a permutation of the contraction, one read per four products
+// instead of one per product.
+template <int LDA, int NK>
+__device__ __forceinline__ float4v chain_prod_f32(float4v acc, const float* A, int ra, const float* B,
+                                                  int ldb, int rb) {
+    static_assert(NK % 16 == 0, "k range");
+    const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
+#pragma unroll
+    for (int g = 0; g < NK / 16; ++g) {
+        const float4v a = *reinterpret_cast<const float4v*>(A + swz<float, LDA>(ra + l16, 16 * g + 4 * lq));
+        const float4v b = *reinterpret_cast<const float4v*>(B + (rb + l16) * ldb + 16 * g + 4 * lq);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b[st], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
 // One chunk of the chain: X = V - KG S, QS = QG S, U = Tb X,
 // O = scale (QS + M U), S <- Diag(Gamma_n) S + KPt U.  Ends with the new
 // state published to LDS; a barrier separates the last reads of the chunk
@@ -1036,13 +1058,18 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
         if (tt < OTILES) {
             const int rt = tt / VT, vt = tt % VT;
             float4v xk = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (sizeof(OT) == 4) {
+                xk = chain_prod_f32<D, D>(xk, t.kg, 16 * rt, cs.s, LDK, 16 * vt);
+                if constexpr (OUT) qs[i] = chain_prod_f32<D, D>(qs[i], t.qg, 16 * rt, cs.s, LDK, 16 * vt);
+            } else {
 #pragma unroll
-            for (int ks = 0; ks < D; ks += mm::KS) {
-                const int kk = ks + lq * mm::KPL;
-                const typename mm::frag bs = mm::load(cs.s, LDK, 16 * vt + l16, kk);
-                xk = mm::mma(load_swz<OT, D>(t.kg, 16 * rt + l16, kk), bs, xk);
-                if constexpr (OUT)
-                    qs[i] = mm::mma(load_swz<OT, D>(t.qg, 16 * rt + l16, kk), bs, qs[i]);
+                for (int ks = 0; ks < D; ks += mm::KS) {
+                    const int kk = ks + lq * mm::KPL;
+                    const typename mm::frag bs = mm::load(cs.s, LDK, 16 * vt + l16, kk);
+                    xk = mm::mma(load_swz<OT, D>(t.kg, 16 * rt + l16, kk), bs, xk);
+                    if constexpr (OUT)
+                        qs[i] = mm::mma(load_swz<OT, D>(t.qg, 16 * rt + l16, kk), bs, qs[i]);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -1067,11 +1094,15 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
             // Tb is lower triangular and its upper part is stored as zeros:
             // the whole k range, unrolled, so that the operand reads run ahead
             // (a loop to the diagonal block exposes each read's latency)
+            if constexpr (sizeof(OT) == 4) {
+                uacc = chain_prod_f32<CK, CK>(uacc, t.tb, 16 * rt, cs.x, LDC, 16 * vt);
+            } else {
 #pragma unroll
-            for (int ks = 0; ks < CK; ks += mm::KS) {
-                const int kk = ks + lq * mm::KPL;
-                uacc = mm::mma(load_swz<OT, CK>(t.tb, 16 * rt + l16, kk),
-                               mm::load(cs.x, LDC, 16 * vt + l16, kk), uacc);
+                for (int ks = 0; ks < CK; ks += mm::KS) {
+                    const int kk = ks + lq * mm::KPL;
+                    uacc = mm::mma(load_swz<OT, CK>(t.tb, 16 * rt + l16, kk),
+                                   mm::load(cs.x, LDC, 16 * vt + l16, kk), uacc);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -1089,9 +1120,12 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
         if (OUT && tt < OTILES) {
             const int rt = tt / VT, vt = tt % VT;
             float4v acc = qs[i];
-            if constexpr (!FOLD) {
+            if constexpr (sizeof(OT) == 4) {
                 // (M lower triangular with zeros stored above: the whole k
                 // range, unrolled, as for U)
+                acc = chain_prod_f32<CK, CK>(acc, reinterpret_cast<const float*>(t.m), 16 * rt,
+                                             reinterpret_cast<const float*>(ub_tile), LDC, 16 * vt);
+            } else if constexpr (!FOLD) {
 #pragma unroll
                 for (int ks = 0; ks < CK; ks += mm::KS) {
                     const int kk = ks + lq * mm::KPL;
@@ -1124,11 +1158,16 @@ __device__ __forceinline__ void inter_chunk(const ChunkTiles<D, C, OT, IT>& t,
             const int ct = s / VT, vt = s % VT;
 #pragma unroll
             for (int j = 0; j < 4; ++j) st[i][j] *= t.gn[16 * ct + 4 * lq + j];
+            if constexpr (sizeof(OT) == 4) {
+                st[i] = chain_prod_f32<CK, CK>(st[i], reinterpret_cast<const float*>(t.kpt), 16 * ct,
+                                               reinterpret_cast<const float*>(ub_tile), LDC, 16 * vt);
+            } else {
 #pragma unroll
-            for (int ks = 0; ks < CK; ks += mm::KS) {
-                const int kk = ks + lq * mm::KPL;
-                st[i] = mm::mma(load_swz<OT, CK>(t.kpt, 16 * ct + l16, kk),
-                                mm::load(ub_tile, LDC, 16 * vt + l16, kk), st[i]);
+                for (int ks = 0; ks < CK; ks += mm::KS) {
+                    const int kk = ks + lq * mm::KPL;
+                    st[i] = mm::mma(load_swz<OT, CK>(t.kpt, 16 * ct + l16, kk),
+                                    mm::load(ub_tile, LDC, 16 * vt + l16, kk), st[i]);
+                }
             }
         }
     }
