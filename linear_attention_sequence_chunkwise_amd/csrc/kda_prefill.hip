@@ -2289,17 +2289,40 @@ struct GradRec {
 // chunk's record and dO columns are fetched into registers while the current
 // chunk computes; the two products of dU run on separate wavefronts.  Writes
 // dV (= dX) and the chunk's dU and dX ([chunk][H][C][D] fp32) for B4a.
+// The products' right operands (dO, dS, dU, dX) are kept as [column][k]
+// rows of 16-byte groups: a lane reads four consecutive k at once (and a
+// matrix-core output tile is stored as one 16-byte write per lane).
 template <int D, int C, typename OT>
 struct BwdChainSmem {
-    static constexpr int LDV = 17;
+    static constexpr int LDO = C + 4, LDD = D + 4;   // row strides (floats), 16-byte multiples
     alignas(16) char img[Rec<D, C, OT>::bytes];
-    float dO[C * LDV];
-    float dS[D * LDV];
-    float dUa[C * LDV], dUb[C * LDV];   // scale M^T dO and KE dSn
-    float dX[C * LDV];
+    alignas(16) float dO[16 * LDO];                  // [n][token]
+    alignas(16) float dS[16 * LDD];                  // [n][channel]
+    alignas(16) float dUa[16 * LDO], dUb[16 * LDO];  // scale M^T dO and KE dSn, [n][token]
+    alignas(16) float dX[16 * LDO];                  // [n][token]
 };
 
 constexpr int kBwdChainWaves = 8;
+
+// acc += A(m, k) B[n][k] over k = 16 g0 .. NK for one 16x16 tile: A read
+// element-wise through `a`, B an [n][ldb] fp32 array in LDS read as 16-byte
+// groups (`b(g)` returns lane's four k of group g).  The four 16x16x4 steps of
+// group g take k = 16 g + 4 (lane / 16) + s, s = 0..3 (a permutation of the
+// contraction), alternating between two accumulators.
+template <int NK, typename FA, typename FB>
+__device__ __forceinline__ float4v tile_mma_bv(float4v acc, int g0, FA a, FB b) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
+    float4v acc2 = {0.f, 0.f, 0.f, 0.f};
+    for (int g = g0; g < NK / 16; ++g) {
+        const float4v bv = b(g);
+        const int k = 16 * g + 4 * lq;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, k), bv[0], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, k + 1), bv[1], acc2, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, k + 2), bv[2], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, k + 3), bv[3], acc2, 0, 0, 0);
+    }
+    return acc + acc2;
+}
 
 template <int D, int C, typename OT>
 __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
@@ -2309,7 +2332,8 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
     float* __restrict__ ds_hist, float* __restrict__ dS0, float* __restrict__ duh,
     float* __restrict__ dxh, float* __restrict__ dv_out) {
     constexpr int NW = kBwdChainWaves, NT = 64 * NW;
-    constexpr int BV = 16, LDV = 17;
+    constexpr int BV = 16;
+    constexpr int LDO = BwdChainSmem<D, C, OT>::LDO, LDD = BwdChainSmem<D, C, OT>::LDD;
     typedef Rec<D, C, OT> R;
     constexpr int CK = R::CK;
     constexpr int NREC = (int)(R::bytes / 16);
@@ -2382,15 +2406,12 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
 #pragma unroll
         for (int i = 0; i < NDO; ++i) {
             const int idx = tid + NT * i;
-            if (idx < C * BV) sm.dO[(idx / BV) * LDV + idx % BV] = idx / BV < dlen ? dov[i] : 0.f;
+            if (idx < C * BV) sm.dO[(idx % BV) * LDO + idx / BV] = idx / BV < dlen ? dov[i] : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int s = wave + NW * i;
-            if (s < DT) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sm.dS[(16 * s + 4 * lq + j) * LDV + l16] = ds[i][j];
-            }
+            if (s < DT) *reinterpret_cast<float4v*>(&sm.dS[l16 * LDD + 16 * s + 4 * lq]) = ds[i];
         }
         lds_barrier();
         if (c > 0) fetch(c - 1);
@@ -2400,30 +2421,32 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
             const int rt = jb % RT;
             float4v a;
             if (jb < RT)
-                a = tile_mma(z, 16 * rt, C, [&](int m, int k) { return (float)img[R::M + swz<OT, CK>(k, 16 * rt + m)]; },
-                             [&](int k, int n) { return sm.dO[k * LDV + n]; });
+                a = tile_mma_bv<C>(z, rt, [&](int m, int k) { return (float)img[R::M + swz<OT, CK>(k, 16 * rt + m)]; },
+                                   [&](int g) { return *reinterpret_cast<const float4v*>(&sm.dO[l16 * LDO + 16 * g + 4 * lq]); });
             else
-                a = tile_mma(z, 0, D, [&](int m, int k) { return (float)img[R::KPt + swz<OT, CK>(k, 16 * rt + m)]; },
-                             [&](int k, int n) { return sm.dS[k * LDV + n]; });
+                a = tile_mma_bv<D>(z, 0, [&](int m, int k) { return (float)img[R::KPt + swz<OT, CK>(k, 16 * rt + m)]; },
+                                   [&](int g) { return *reinterpret_cast<const float4v*>(&sm.dS[l16 * LDD + 16 * g + 4 * lq]); });
             float* dst = jb < RT ? sm.dUa : sm.dUb;
             const float f = jb < RT ? scale : 1.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dst[(16 * rt + 4 * lq + j) * LDV + l16] = f * a[j];
+            *reinterpret_cast<float4v*>(&dst[l16 * LDO + 16 * rt + 4 * lq]) = f * a;
         }
         lds_barrier();
         for (int idx = tid; idx < C * BV; idx += NT) {
             const int r = idx / BV, col = idx % BV;
-            duh[xo + (size_t)r * D + cp.v0 + col] = sm.dUa[r * LDV + col] + sm.dUb[r * LDV + col];
+            duh[xo + (size_t)r * D + cp.v0 + col] = sm.dUa[col * LDO + r] + sm.dUb[col * LDO + r];
         }
         // dX = Tb^T dU (Tb[i][r] vanishes for i < r) = dV
         for (int rt = wave; rt < RT; rt += NW) {
-            const float4v x = tile_mma(
-                z, 16 * rt, C, [&](int m, int k) { return (float)img[R::Tb + swz<OT, CK>(k, 16 * rt + m)]; },
-                [&](int k, int n) { return sm.dUa[k * LDV + n] + sm.dUb[k * LDV + n]; });
+            const float4v x = tile_mma_bv<C>(
+                z, rt, [&](int m, int k) { return (float)img[R::Tb + swz<OT, CK>(k, 16 * rt + m)]; },
+                [&](int g) {
+                    return *reinterpret_cast<const float4v*>(&sm.dUa[l16 * LDO + 16 * g + 4 * lq]) +
+                           *reinterpret_cast<const float4v*>(&sm.dUb[l16 * LDO + 16 * g + 4 * lq]);
+                });
+            *reinterpret_cast<float4v*>(&sm.dX[l16 * LDO + 16 * rt + 4 * lq]) = x;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * rt + 4 * lq + j;
-                sm.dX[r * LDV + l16] = x[j];
                 dxh[xo + (size_t)r * D + cp.v0 + l16] = x[j];
                 if (r < len) dv_out[((size_t)(tok0 + r) * H + cp.h) * D + cp.v0 + l16] = x[j];
             }
@@ -2434,12 +2457,12 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
         for (int i = 0; i < SPW; ++i) {
             const int s = wave + NW * i;
             if (s < DT) {
-                const float4v a = tile_mma(
-                    z, 0, C, [&](int m, int k) { return (float)img[R::QG + swz<OT, D>(k, 16 * s + m)]; },
-                    [&](int k, int n) { return sm.dO[k * LDV + n]; });
-                const float4v b = tile_mma(
-                    z, 0, C, [&](int m, int k) { return (float)img[R::KG + swz<OT, D>(k, 16 * s + m)]; },
-                    [&](int k, int n) { return sm.dX[k * LDV + n]; });
+                const float4v a = tile_mma_bv<C>(
+                    z, 0, [&](int m, int k) { return (float)img[R::QG + swz<OT, D>(k, 16 * s + m)]; },
+                    [&](int g) { return *reinterpret_cast<const float4v*>(&sm.dO[l16 * LDO + 16 * g + 4 * lq]); });
+                const float4v b = tile_mma_bv<C>(
+                    z, 0, [&](int m, int k) { return (float)img[R::KG + swz<OT, D>(k, 16 * s + m)]; },
+                    [&](int g) { return *reinterpret_cast<const float4v*>(&sm.dX[l16 * LDO + 16 * g + 4 * lq]); });
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     ds[i][j] = gn[16 * s + 4 * lq + j] * ds[i][j] + scale * a[j] - b[j];
