@@ -2491,10 +2491,34 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
 // are fetched into registers while the current block computes.
 template <int D, int C>
 struct BwdDvSmem {
-    static constexpr int LDV = 17;
-    float S[D * LDV], dSn[D * LDV];
-    float dO[C * LDV], X[C * LDV], U[C * LDV], dU[C * LDV], dX[C * LDV];
+    // rows of the 16-column block padded to 20 floats: 16-byte aligned, so
+    // that a lane reads four consecutive columns at once, and conflict-free
+    // for 16 rows read at the same column group
+    static constexpr int LDV = 20;
+    alignas(16) float S[D * LDV];
+    alignas(16) float dSn[D * LDV];
+    alignas(16) float dO[C * LDV];
+    alignas(16) float X[C * LDV];
+    alignas(16) float U[C * LDV];
+    alignas(16) float dU[C * LDV];
+    alignas(16) float dX[C * LDV];
 };
+
+// acc += A[16 ra + (0..15)][0..16) * B[16 rb + (0..15)][0..16)^T for [row][16]
+// fp32 operands in LDS (row stride ld, 16-byte aligned): one 16-byte read per
+// lane and side; the four 16x16x4 steps take k = 4 (lane / 16) + s.
+__device__ __forceinline__ float4v block_mma16(float4v acc, const float* A, int ra, const float* B, int rb,
+                                               int ld) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
+    const float4v a = *reinterpret_cast<const float4v*>(A + (16 * ra + l16) * ld + 4 * lq);
+    const float4v b = *reinterpret_cast<const float4v*>(B + (16 * rb + l16) * ld + 4 * lq);
+    float4v acc2 = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc2, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc2, 0, 0, 0);
+    return acc + acc2;
+}
 
 // Sixteen wavefronts (four per SIMD; the accumulators of two C x D tiles and
 // one lower C x C tile per wavefront keep it within 128 registers), or fewer
@@ -2510,7 +2534,7 @@ __global__ __launch_bounds__(64 * bwd_dv_waves<D>()) void kda_bwd_vprod(
     const float* __restrict__ duh, const float* __restrict__ dxh, const float* __restrict__ d_o,
     float* __restrict__ grec) {
     constexpr int NW = bwd_dv_waves<D>(), NT = 64 * NW;
-    constexpr int BV = 16, LDV = 17;
+    constexpr int BV = 16, LDV = BwdDvSmem<D, C>::LDV;
     typedef GradRec<D, C> GR;
     constexpr int RT = C / 16, DT = D / 16;
     constexpr int NQ = RT * DT, QPW = (NQ + NW - 1) / NW;          // C x D tiles per wavefront
@@ -2591,12 +2615,9 @@ __global__ __launch_bounds__(64 * bwd_dv_waves<D>()) void kda_bwd_vprod(
             const int t = wave + NW * i;
             if (t < NQ) {
                 const int rt = t / DT, ct = t % DT;
-                aq[i] = tile_mma(aq[i], 0, BV, [&](int m, int k) { return sm.dO[(16 * rt + m) * LDV + k]; },
-                                 [&](int k, int n) { return sm.S[(16 * ct + n) * LDV + k]; });
-                ak[i] = tile_mma(ak[i], 0, BV, [&](int m, int k) { return sm.dX[(16 * rt + m) * LDV + k]; },
-                                 [&](int k, int n) { return sm.S[(16 * ct + n) * LDV + k]; });
-                ae[i] = tile_mma(ae[i], 0, BV, [&](int m, int k) { return sm.U[(16 * rt + m) * LDV + k]; },
-                                 [&](int k, int n) { return sm.dSn[(16 * ct + n) * LDV + k]; });
+                aq[i] = block_mma16(aq[i], sm.dO, rt, sm.S, ct, LDV);
+                ak[i] = block_mma16(ak[i], sm.dX, rt, sm.S, ct, LDV);
+                ae[i] = block_mma16(ae[i], sm.U, rt, sm.dSn, ct, LDV);
             }
         }
 #pragma unroll
@@ -2605,10 +2626,8 @@ __global__ __launch_bounds__(64 * bwd_dv_waves<D>()) void kda_bwd_vprod(
             if (t < NL) {
                 int rt, ct;
                 lower_tile(t, rt, ct);
-                am[i] = tile_mma(am[i], 0, BV, [&](int m, int k) { return sm.dO[(16 * rt + m) * LDV + k]; },
-                                 [&](int k, int n) { return sm.U[(16 * ct + n) * LDV + k]; });
-                at[i] = tile_mma(at[i], 0, BV, [&](int m, int k) { return sm.dU[(16 * rt + m) * LDV + k]; },
-                                 [&](int k, int n) { return sm.X[(16 * ct + n) * LDV + k]; });
+                am[i] = block_mma16(am[i], sm.dO, rt, sm.U, ct, LDV);
+                at[i] = block_mma16(at[i], sm.dU, rt, sm.X, ct, LDV);
             }
         }
         if (tid < D) {
