@@ -355,10 +355,14 @@ struct IntraSmem {
     // Gram operands while the Gram runs; afterwards the same bytes hold the
     // triangular solve's fp32 T, the staged M tile and per-wave scratch.  The
     // left operand is k_r a_r for the k.k^T Gram, then q_r a_r for the q.k^T
-    // Gram (one buffer, so that three workgroups fit a CU's LDS).
+    // Gram (one buffer, so that three workgroups fit a CU's LDS).  fp32 at
+    // d = 128 stages them half the channels at a time (DH = 2), so that two
+    // workgroups fit.
+    static constexpr int DH = (sizeof(OT) == 4 && D == 128) ? 2 : 1;
+    static constexpr int LDKG = padded<OT>(D / DH);
     struct Gram {
-        OT kl[C * LDK];        // k_r a_r, then q_r a_r   (Gram left)
-        OT kr[C * LDK];        // k_i b_i                 (Gram right)
+        OT kl[C * LDKG];       // k_r a_r, then q_r a_r   (Gram left)
+        OT kr[C * LDKG];       // k_i b_i                 (Gram right)
     };
     struct Solve {
         float T[C * LDT];      // (I + A)^-1, fp32
@@ -564,75 +568,6 @@ __global__ __launch_bounds__(256) void kda_intra(
                                       : nullptr);
         }
     }
-    if (task) {
-        // a_j = prod_{j'<=j} alpha, b_j = prod_{j'>j} alpha, both channels of the
-        // pair at once: one 4-byte (fp16) or 8-byte (fp32) LDS store per row
-        auto store2 = [](OT* p, float x0, float x1) {
-            if constexpr (sizeof(OT) == 2) {
-                *reinterpret_cast<half2v*>(p) = half2v{(_Float16)x0, (_Float16)x1};   // one packed conversion
-            } else {
-                *reinterpret_cast<float2*>(p) = float2{x0, x1};
-            }
-        };
-        float a0 = 1.f, a1 = 1.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            a0 *= g0[j];
-            a1 *= g1[j];
-            const int r = 16 * I + j;
-            store2(&sm.u.g.kl[r * LDK + c0], k0v[j] * a0, k1v[j] * a1);
-            q0v[j] *= a0;          // q_r a_r, written to LDS after the k.k^T Gram
-            q1v[j] *= a1;
-        }
-        float b0 = 1.f, b1 = 1.f;
-#pragma unroll
-        for (int j = 15; j >= 0; --j) {
-            const int r = 16 * I + j;
-            store2(&sm.u.g.kr[r * LDK + c0], k0v[j] * b0, k1v[j] * b1);
-            b0 *= g0[j];
-            b1 *= g1[j];
-        }
-    }
-    lds_barrier();
-
-    // ---- phase 3a: record tiles KG, KPt from the LDS operands ----
-    // KG_r = (k_r a_r) exp(Gs_I) : rows of 16 bytes
-    // (record columns in the kperm order: stored column c0 + e holds channel
-    // kperm_inv(c0 + e))
-    #pragma unroll
-    for (int it_ = 0; it_ < (C * D / EPV + 255) / 256; ++it_) {   // compile-time trip count
-        const int idx = tid + 256 * it_;
-        if (idx >= C * D / EPV) break;
-        const int r = idx / (D / EPV), c0 = (idx % (D / EPV)) * EPV;
-        float kk[EPV];
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-            const int c = group_col<OT>(c0, e);
-            kk[e] = (float)sm.u.g.kl[r * LDK + c] * sm.egs[(r >> 4) * D + c];
-        }
-        *reinterpret_cast<vec*>(rec + R::KG + swz<OT, D>(r, c0)) = pack16(kk);
-    }
-    // KPt[c][i] = (k_i b_i) exp(G_n - Ge_J), transposed: 16 bytes of one channel
-    // row; token columns in the kperm order, zero past C (k-padding)
-    auto kpt_group = [&](int c, int i0, float (&kk)[EPV]) {
-        // the group's runs of four tokens lie in sub-blocks J and (fp16) J + 1
-        const int J = group_col<OT>(i0, 0) >> 4;
-        // G_n - Ge_J and G_n - Ge_{J+1}: the gate sums of the later sub-blocks,
-        // each summed directly (no difference of sums)
-        float tail0 = 0.f, tail1 = 0.f;
-#pragma unroll
-        for (int m = 1; m < NB; ++m) {
-            if (m > J) tail0 += sm.sig[m * D + c];
-            if (m > J + 1) tail1 += sm.sig[m * D + c];
-        }
-        const float f0 = exp_e(tail0);
-        const float f1 = J + 1 < NB ? exp_e(tail1) : 0.f;
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-            const int i = group_col<OT>(i0, e);
-            kk[e] = i < C ? (float)sm.u.g.kr[i * LDK + c] * (e < 4 ? f0 : f1) : 0.f;
-        }
-    };
     const int l16 = lane & 15;
     const int lq = lane >> 4;
     // FOLD: KPt stays in registers as the B fragments of W^T = Tb^T KPt^T
@@ -640,115 +575,334 @@ __global__ __launch_bounds__(256) void kda_intra(
     // the 16-byte token group 8 lq of each 32-token step), for phase 5
     constexpr int NCB = D / 16, CPW = (NCB + 3) / 4, NKS = R::CK / 32;
     half8 kpf[R::FOLD ? CPW : 1][R::FOLD ? NKS : 1];
-    if constexpr (R::FOLD) {
+    constexpr int NT = NB * (NB + 1) / 2;
+    constexpr int TPW = (NT + 3) / 4;
+    float4v macc[TPW];
+    if constexpr (IntraSmem<D, C, OT>::DH == 1) {
+        if (task) {
+            // a_j = prod_{j'<=j} alpha, b_j = prod_{j'>j} alpha, both channels of the
+            // pair at once: one 4-byte (fp16) or 8-byte (fp32) LDS store per row
+            auto store2 = [](OT* p, float x0, float x1) {
+                if constexpr (sizeof(OT) == 2) {
+                    *reinterpret_cast<half2v*>(p) = half2v{(_Float16)x0, (_Float16)x1};   // one packed conversion
+                } else {
+                    *reinterpret_cast<float2*>(p) = float2{x0, x1};
+                }
+            };
+            float a0 = 1.f, a1 = 1.f;
 #pragma unroll
-        for (int x = 0; x < CPW; ++x) {
-            const int cb = wave + 4 * x;
-            if (cb < NCB) {
+            for (int j = 0; j < 16; ++j) {
+                a0 *= g0[j];
+                a1 *= g1[j];
+                const int r = 16 * I + j;
+                store2(&sm.u.g.kl[r * LDK + c0], k0v[j] * a0, k1v[j] * a1);
+                q0v[j] *= a0;          // q_r a_r, written to LDS after the k.k^T Gram
+                q1v[j] *= a1;
+            }
+            float b0 = 1.f, b1 = 1.f;
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    float kk[EPV];
-                    kpt_group(16 * cb + l16, 32 * ks + 8 * lq, kk);
-                    kpf[x][ks] = __builtin_bit_cast(half8, pack16(kk));
+            for (int j = 15; j >= 0; --j) {
+                const int r = 16 * I + j;
+                store2(&sm.u.g.kr[r * LDK + c0], k0v[j] * b0, k1v[j] * b1);
+                b0 *= g0[j];
+                b1 *= g1[j];
+            }
+        }
+        lds_barrier();
+
+        // ---- phase 3a: record tiles KG, KPt from the LDS operands ----
+        // KG_r = (k_r a_r) exp(Gs_I) : rows of 16 bytes
+        // (record columns in the kperm order: stored column c0 + e holds channel
+        // kperm_inv(c0 + e))
+        #pragma unroll
+        for (int it_ = 0; it_ < (C * D / EPV + 255) / 256; ++it_) {   // compile-time trip count
+            const int idx = tid + 256 * it_;
+            if (idx >= C * D / EPV) break;
+            const int r = idx / (D / EPV), c0 = (idx % (D / EPV)) * EPV;
+            float kk[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const int c = group_col<OT>(c0, e);
+                kk[e] = (float)sm.u.g.kl[r * LDK + c] * sm.egs[(r >> 4) * D + c];
+            }
+            *reinterpret_cast<vec*>(rec + R::KG + swz<OT, D>(r, c0)) = pack16(kk);
+        }
+        // KPt[c][i] = (k_i b_i) exp(G_n - Ge_J), transposed: 16 bytes of one channel
+        // row; token columns in the kperm order, zero past C (k-padding)
+        auto kpt_group = [&](int c, int i0, float (&kk)[EPV]) {
+            // the group's runs of four tokens lie in sub-blocks J and (fp16) J + 1
+            const int J = group_col<OT>(i0, 0) >> 4;
+            // G_n - Ge_J and G_n - Ge_{J+1}: the gate sums of the later sub-blocks,
+            // each summed directly (no difference of sums)
+            float tail0 = 0.f, tail1 = 0.f;
+#pragma unroll
+            for (int m = 1; m < NB; ++m) {
+                if (m > J) tail0 += sm.sig[m * D + c];
+                if (m > J + 1) tail1 += sm.sig[m * D + c];
+            }
+            const float f0 = exp_e(tail0);
+            const float f1 = J + 1 < NB ? exp_e(tail1) : 0.f;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const int i = group_col<OT>(i0, e);
+                kk[e] = i < C ? (float)sm.u.g.kr[i * LDK + c] * (e < 4 ? f0 : f1) : 0.f;
+            }
+        };
+        if constexpr (R::FOLD) {
+#pragma unroll
+            for (int x = 0; x < CPW; ++x) {
+                const int cb = wave + 4 * x;
+                if (cb < NCB) {
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        float kk[EPV];
+                        kpt_group(16 * cb + l16, 32 * ks + 8 * lq, kk);
+                        kpf[x][ks] = __builtin_bit_cast(half8, pack16(kk));
+                    }
+                }
+            }
+        } else {
+            #pragma unroll
+            for (int it_ = 0; it_ < (D * R::CK / EPV + 255) / 256; ++it_) {   // compile-time trip count
+                const int idx = tid + 256 * it_;
+                if (idx >= D * R::CK / EPV) break;
+                const int c = idx / (R::CK / EPV), i0 = (idx % (R::CK / EPV)) * EPV;
+                float kk[EPV];
+                kpt_group(c, i0, kk);
+                *reinterpret_cast<vec*>(rec + R::KPt + swz<OT, R::CK>(c, i0)) = pack16(kk);
+            }
+        }
+
+        // ---- phase 3b: Gram blocks on the matrix cores ----
+        // First the NT lower blocks of A (k.k^T), straight to LDS; then the left
+        // operand becomes q_r a_r and the NT blocks of M (q.k^T) stay in registers
+        // until the Gram operands are dead.
+        auto gram = [&](int Ib, int Jb) {
+            float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < D; ks += mm::KS) {
+                const int kk = ks + lq * mm::KPL;
+                typename mm::frag af = mm::load(sm.u.g.kl, LDK, 16 * Ib + l16, kk);
+                typename mm::frag bf = mm::load(sm.u.g.kr, LDK, 16 * Jb + l16, kk);
+                const typename mm::frag ff = mm::load(sm.F + (Ib * NB + Jb) * D, 0, 0, kk);
+                bf = bf * ff;
+                acc = mm::mma(af, bf, acc);
+            }
+            return acc;
+        };
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int t = wave + 4 * i;
+            if (t < NT) {
+                int tt = t, Ib = 0;
+                while (tt > Ib) { tt -= Ib + 1; ++Ib; }
+                const int Jb = tt;
+                // a strong sub-block's diagonal tile came from the exact path (its
+                // upper triangle holds that path's M tile)
+                const bool exact = Ib == Jb && sm.strong[Ib];
+                const float4v acc = exact ? float4v{0.f, 0.f, 0.f, 0.f} : gram(Ib, Jb);
+                const int col = 16 * Jb + l16;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = 16 * Ib + 4 * lq + j;
+                    if (!exact) sm.A[row * LDA + col] = to_ot<OT>(col < row ? sm.beta[row] * acc[j] : 0.f);
+                    if (aux && (!exact || col >= row))
+                        aux[((size_t)ch * H + h) * 2 * C * C + C * C + row * C + col] =
+                            col < row ? acc[j] : 0.f;
                 }
             }
         }
-    } else {
-        #pragma unroll
-        for (int it_ = 0; it_ < (D * R::CK / EPV + 255) / 256; ++it_) {   // compile-time trip count
-            const int idx = tid + 256 * it_;
-            if (idx >= D * R::CK / EPV) break;
-            const int c = idx / (R::CK / EPV), i0 = (idx % (R::CK / EPV)) * EPV;
-            float kk[EPV];
-            kpt_group(c, i0, kk);
-            *reinterpret_cast<vec*>(rec + R::KPt + swz<OT, R::CK>(c, i0)) = pack16(kk);
-        }
-    }
-
-    // ---- phase 3b: Gram blocks on the matrix cores ----
-    // First the NT lower blocks of A (k.k^T), straight to LDS; then the left
-    // operand becomes q_r a_r and the NT blocks of M (q.k^T) stay in registers
-    // until the Gram operands are dead.
-    constexpr int NT = NB * (NB + 1) / 2;
-    constexpr int TPW = (NT + 3) / 4;
-    auto gram = [&](int Ib, int Jb) {
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
+        // (A above the diagonal blocks is never read: the solve takes the diagonal
+        // blocks' lower parts and the blocks below them)
+        lds_barrier();   // the k.k^T Gram's reads of kl are done
+        if (task) {
 #pragma unroll
-        for (int ks = 0; ks < D; ks += mm::KS) {
-            const int kk = ks + lq * mm::KPL;
-            typename mm::frag af = mm::load(sm.u.g.kl, LDK, 16 * Ib + l16, kk);
-            typename mm::frag bf = mm::load(sm.u.g.kr, LDK, 16 * Jb + l16, kk);
-            const typename mm::frag ff = mm::load(sm.F + (Ib * NB + Jb) * D, 0, 0, kk);
-            bf = bf * ff;
-            acc = mm::mma(af, bf, acc);
-        }
-        return acc;
-    };
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int t = wave + 4 * i;
-        if (t < NT) {
-            int tt = t, Ib = 0;
-            while (tt > Ib) { tt -= Ib + 1; ++Ib; }
-            const int Jb = tt;
-            // a strong sub-block's diagonal tile came from the exact path (its
-            // upper triangle holds that path's M tile)
-            const bool exact = Ib == Jb && sm.strong[Ib];
-            const float4v acc = exact ? float4v{0.f, 0.f, 0.f, 0.f} : gram(Ib, Jb);
-            const int col = 16 * Jb + l16;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * Ib + 4 * lq + j;
-                if (!exact) sm.A[row * LDA + col] = to_ot<OT>(col < row ? sm.beta[row] * acc[j] : 0.f);
-                if (aux && (!exact || col >= row))
-                    aux[((size_t)ch * H + h) * 2 * C * C + C * C + row * C + col] =
-                        col < row ? acc[j] : 0.f;
+            for (int j = 0; j < 16; ++j) {
+                const int r = 16 * I + j;
+                sm.u.g.kl[r * LDK + c0] = to_ot<OT>(q0v[j]);
+                sm.u.g.kl[r * LDK + c0 + 1] = to_ot<OT>(q1v[j]);
             }
         }
-    }
-    // (A above the diagonal blocks is never read: the solve takes the diagonal
-    // blocks' lower parts and the blocks below them)
-    lds_barrier();   // the k.k^T Gram's reads of kl are done
-    if (task) {
+        lds_barrier();
+        // QG_r = (q_r a_r) exp(Gs_I) : rows of 16 bytes
+        #pragma unroll
+        for (int it_ = 0; it_ < (C * D / EPV + 255) / 256; ++it_) {   // compile-time trip count
+            const int idx = tid + 256 * it_;
+            if (idx >= C * D / EPV) break;
+            const int r = idx / (D / EPV), c0 = (idx % (D / EPV)) * EPV;
+            float qq[EPV];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int r = 16 * I + j;
-            sm.u.g.kl[r * LDK + c0] = to_ot<OT>(q0v[j]);
-            sm.u.g.kl[r * LDK + c0 + 1] = to_ot<OT>(q1v[j]);
+            for (int e = 0; e < EPV; ++e) {
+                const int c = group_col<OT>(c0, e);
+                qq[e] = (float)sm.u.g.kl[r * LDK + c] * sm.egs[(r >> 4) * D + c];
+            }
+            *reinterpret_cast<vec*>(rec + R::QG + swz<OT, D>(r, c0)) = pack16(qq);
         }
-    }
-    lds_barrier();
-    // QG_r = (q_r a_r) exp(Gs_I) : rows of 16 bytes
-    #pragma unroll
-    for (int it_ = 0; it_ < (C * D / EPV + 255) / 256; ++it_) {   // compile-time trip count
-        const int idx = tid + 256 * it_;
-        if (idx >= C * D / EPV) break;
-        const int r = idx / (D / EPV), c0 = (idx % (D / EPV)) * EPV;
-        float qq[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-            const int c = group_col<OT>(c0, e);
-            qq[e] = (float)sm.u.g.kl[r * LDK + c] * sm.egs[(r >> 4) * D + c];
+        for (int i = 0; i < TPW; ++i) {
+            const int t = wave + 4 * i;
+            macc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+            if (t < NT) {
+                int tt = t, Ib = 0;
+                while (tt > Ib) { tt -= Ib + 1; ++Ib; }
+                const int Jb = tt;
+                if (Ib == Jb && sm.strong[Ib]) continue;   // staged from the exact path
+                const float4v acc = gram(Ib, Jb);
+                const int col = 16 * Jb + l16;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) macc[i][j] = col <= 16 * Ib + 4 * lq + j ? acc[j] : 0.f;
+            }
         }
-        *reinterpret_cast<vec*>(rec + R::QG + swz<OT, D>(r, c0)) = pack16(qq);
-    }
-    float4v macc[TPW];
+        lds_barrier();   // Gram operands dead from here on
+    } else {
+        // fp32 at d = 128: the Gram operands (k_r a_r, k_i b_i, then q_r a_r) are
+        // staged half the channels at a time, so that the kernel's LDS allows
+        // two workgroups per CU (one would hold 95 KiB).  Per half: the
+        // operands of its channels, their KG and KPt record rows and the k.k^T
+        // Gram's partial sums; then q_r a_r and its QG rows and the q.k^T
+        // Gram's partial sums.  Both Grams accumulate in registers.
+        constexpr int DHALF = D / 2, LDKH = IntraSmem<D, C, OT>::LDKG;
+        float4v aacc[TPW];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int t = wave + 4 * i;
-        macc[i] = float4v{0.f, 0.f, 0.f, 0.f};
-        if (t < NT) {
-            int tt = t, Ib = 0;
+        for (int i = 0; i < TPW; ++i) aacc[i] = macc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+        auto tile_of = [](int t, int& Ib, int& Jb) {
+            int tt = t;
+            Ib = 0;
             while (tt > Ib) { tt -= Ib + 1; ++Ib; }
-            const int Jb = tt;
-            if (Ib == Jb && sm.strong[Ib]) continue;   // staged from the exact path
-            const float4v acc = gram(Ib, Jb);
-            const int col = 16 * Jb + l16;
+            Jb = tt;
+        };
+        // partial Gram over this half's channels: left operand in kl
+        auto gram_half = [&](int Ib, int Jb, int hf, float4v acc) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) macc[i][j] = col <= 16 * Ib + 4 * lq + j ? acc[j] : 0.f;
+            for (int ks = 0; ks < DHALF; ks += mm::KS) {
+                const int kk = ks + lq * mm::KPL;
+                typename mm::frag af = mm::load(sm.u.g.kl, LDKH, 16 * Ib + l16, kk);
+                typename mm::frag bf = mm::load(sm.u.g.kr, LDKH, 16 * Jb + l16, kk);
+                const typename mm::frag ff = mm::load(sm.F + (Ib * NB + Jb) * D + hf * DHALF, 0, 0, kk);
+                bf = bf * ff;
+                acc = mm::mma(af, bf, acc);
+            }
+            return acc;
+        };
+        const bool my_task = task;
+        const int my_half = c0 / DHALF, lc0 = c0 - my_half * DHALF;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            if (hf > 0) lds_barrier();   // the previous half's reads of kl and kr are done
+            if (my_task && my_half == hf) {
+                float a0 = 1.f, a1 = 1.f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    a0 *= g0[j];
+                    a1 *= g1[j];
+                    const int r = 16 * I + j;
+                    *reinterpret_cast<float2*>(&sm.u.g.kl[r * LDKH + lc0]) = float2{k0v[j] * a0, k1v[j] * a1};
+                    q0v[j] *= a0;
+                    q1v[j] *= a1;
+                }
+                float b0 = 1.f, b1 = 1.f;
+#pragma unroll
+                for (int j = 15; j >= 0; --j) {
+                    const int r = 16 * I + j;
+                    *reinterpret_cast<float2*>(&sm.u.g.kr[r * LDKH + lc0]) = float2{k0v[j] * b0, k1v[j] * b1};
+                    b0 *= g0[j];
+                    b1 *= g1[j];
+                }
+            }
+            lds_barrier();
+            // KG rows of this half's channels
+#pragma unroll
+            for (int it_ = 0; it_ < (C * DHALF / EPV + 255) / 256; ++it_) {
+                const int idx = tid + 256 * it_;
+                if (idx >= C * DHALF / EPV) break;
+                const int r = idx / (DHALF / EPV), lc = (idx % (DHALF / EPV)) * EPV, cg = hf * DHALF + lc;
+                float kk[EPV];
+#pragma unroll
+                for (int e = 0; e < EPV; ++e)
+                    kk[e] = sm.u.g.kl[r * LDKH + lc + e] * sm.egs[(r >> 4) * D + cg + e];
+                *reinterpret_cast<vec*>(rec + R::KG + swz<OT, D>(r, cg)) = pack16(kk);
+            }
+            // KPt rows of this half's channels: (k_i b_i) exp(G_n - Ge_J)
+#pragma unroll
+            for (int it_ = 0; it_ < (DHALF * R::CK / EPV + 255) / 256; ++it_) {
+                const int idx = tid + 256 * it_;
+                if (idx >= DHALF * R::CK / EPV) break;
+                const int lc = idx / (R::CK / EPV), i0 = (idx % (R::CK / EPV)) * EPV, cg = hf * DHALF + lc;
+                const int J = i0 >> 4;   // fp32 groups: four tokens of one sub-block
+                float tail = 0.f;
+#pragma unroll
+                for (int m = 1; m < NB; ++m)
+                    if (m > J) tail += sm.sig[m * D + cg];
+                const float f = exp_e(tail);
+                float kk[EPV];
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) kk[e] = i0 + e < C ? sm.u.g.kr[(i0 + e) * LDKH + lc] * f : 0.f;
+                *reinterpret_cast<vec*>(rec + R::KPt + swz<OT, R::CK>(cg, i0)) = pack16(kk);
+            }
+            // k.k^T Gram, partial
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int t = wave + 4 * i;
+                if (t < NT) {
+                    int Ib, Jb;
+                    tile_of(t, Ib, Jb);
+                    if (!(Ib == Jb && sm.strong[Ib])) aacc[i] = gram_half(Ib, Jb, hf, aacc[i]);
+                }
+            }
+            lds_barrier();   // this half's k.k^T Gram has read kl
+            if (my_task && my_half == hf) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int r = 16 * I + j;
+                    *reinterpret_cast<float2*>(&sm.u.g.kl[r * LDKH + lc0]) = float2{q0v[j], q1v[j]};
+                }
+            }
+            lds_barrier();
+            // QG rows of this half's channels
+#pragma unroll
+            for (int it_ = 0; it_ < (C * DHALF / EPV + 255) / 256; ++it_) {
+                const int idx = tid + 256 * it_;
+                if (idx >= C * DHALF / EPV) break;
+                const int r = idx / (DHALF / EPV), lc = (idx % (DHALF / EPV)) * EPV, cg = hf * DHALF + lc;
+                float qq[EPV];
+#pragma unroll
+                for (int e = 0; e < EPV; ++e)
+                    qq[e] = sm.u.g.kl[r * LDKH + lc + e] * sm.egs[(r >> 4) * D + cg + e];
+                *reinterpret_cast<vec*>(rec + R::QG + swz<OT, D>(r, cg)) = pack16(qq);
+            }
+            // q.k^T Gram, partial
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int t = wave + 4 * i;
+                if (t < NT) {
+                    int Ib, Jb;
+                    tile_of(t, Ib, Jb);
+                    if (!(Ib == Jb && sm.strong[Ib])) macc[i] = gram_half(Ib, Jb, hf, macc[i]);
+                }
+            }
         }
+        // the Grams complete: A to LDS (and aux), M masked to its lower part
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int t = wave + 4 * i;
+            if (t < NT) {
+                int Ib, Jb;
+                tile_of(t, Ib, Jb);
+                const bool exact = Ib == Jb && sm.strong[Ib];
+                const int col = 16 * Jb + l16;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = 16 * Ib + 4 * lq + j;
+                    if (!exact) sm.A[row * LDA + col] = col < row ? sm.beta[row] * aacc[i][j] : 0.f;
+                    if (aux && (!exact || col >= row))
+                        aux[((size_t)ch * H + h) * 2 * C * C + C * C + row * C + col] =
+                            col < row ? aacc[i][j] : 0.f;
+                    macc[i][j] = !exact && col <= row ? macc[i][j] : 0.f;
+                }
+            }
+        }
+        lds_barrier();   // Gram operands dead from here on
     }
-    lds_barrier();   // Gram operands dead from here on
 
     // ---- phase 4a: stage M; invert the diagonal 16x16 blocks of I + A ----
     constexpr int LDT = C + 4;
