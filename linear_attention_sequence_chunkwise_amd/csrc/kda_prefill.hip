@@ -1403,15 +1403,19 @@ __global__ __launch_bounds__(256) void kda_inter(
 // into s_hist ([chunk][H][D][D] fp32) and the chunk's X and U into xh, uh
 // ([chunk][H][C][D] fp32), no output.  Only the record parts the
 // state update reads are loaded (KG, KPt, Tb, Gamma_n), and the next chunk's
-// parts are fetched into registers while the current chunk computes.
+// parts are fetched into registers while the current chunk computes.  Eight
+// wavefronts: the state update (eight 16x16 tiles per slice) takes one tile
+// per wavefront.
+constexpr int kStateChainWaves = 8;
 template <int D, int C, int BV, typename OT, typename IT>
-__global__ __launch_bounds__(256) void kda_state_chain(
+__global__ __launch_bounds__(64 * kStateChainWaves) void kda_state_chain(
     int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
     const int* __restrict__ chunk_off, const IT* __restrict__ v, const float* __restrict__ s0,
     const char* __restrict__ records, float* __restrict__ s_hist, float* __restrict__ xh,
     float* __restrict__ uh) {
+    constexpr int NWC = kStateChainWaves, NT = 64 * NWC;
     constexpr int ST = (D / 16) * (BV / 16);
-    constexpr int SPW = (ST + 3) / 4;
+    constexpr int SPW = (ST + NWC - 1) / NWC;
     typedef Rec<D, C, OT> R;
     typedef u32x4 vec;
     // needed 16-byte units: KG, then KPt and Tb, then Gamma_n
@@ -1419,10 +1423,10 @@ __global__ __launch_bounds__(256) void kda_state_chain(
     constexpr int B_BEG = (int)(R::KPt * sizeof(OT) / 16), B_END = (int)(R::M * sizeof(OT) / 16);
     constexpr int G_BEG = (int)(R::gn_byte / 16), G_END = (int)((R::gn_byte + 4 * D) / 16);
     constexpr int NNEED = A_END + (B_END - B_BEG) + (G_END - G_BEG);
-    constexpr int RPT = (NNEED + 255) / 256;
+    constexpr int RPT = (NNEED + NT - 1) / NT;
     constexpr int VPR = BV * (int)sizeof(IT) / 16;
     constexpr int NVV = C * VPR;
-    constexpr int VPT = (NVV + 255) / 256;
+    constexpr int VPT = (NVV + NT - 1) / NT;
     static_assert(R::gn_byte % 16 == 0 && (4 * D) % 16 == 0, "record unit alignment");
     extern __shared__ __align__(16) char smem_raw[];
     InterSmem<D, C, BV, OT, IT>& sm = *reinterpret_cast<InterSmem<D, C, BV, OT, IT>*>(smem_raw);
@@ -1432,7 +1436,7 @@ __global__ __launch_bounds__(256) void kda_state_chain(
     const int tid = threadIdx.x;
     const size_t sbase = ((size_t)cp.n * H + cp.h) * (size_t)D * D;
     float4v st[SPW];
-    chain_load_state<D, C, BV, OT, 4, true>(st, sm.cs, s0, sbase, cp.v0);
+    chain_load_state<D, C, BV, OT, NWC, true>(st, sm.cs, s0, sbase, cp.v0);
     const ChunkTiles<D, C, OT, IT> tiles(sm.img, sm.vraw);
     auto unit = [](int j) {
         return j < A_END ? j : j < A_END + (B_END - B_BEG) ? B_BEG + (j - A_END)
@@ -1445,10 +1449,10 @@ __global__ __launch_bounds__(256) void kda_state_chain(
         const int len = min(C, cp.seq_len - c * C);
         const vec* rec = reinterpret_cast<const vec*>(records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) rb[i] = rec[unit(min(tid + 256 * i, NNEED - 1))];
+        for (int i = 0; i < RPT; ++i) rb[i] = rec[unit(min(tid + NT * i, NNEED - 1))];
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int idx = min(tid + 256 * i, NVV - 1);
+            const int idx = min(tid + NT * i, NVV - 1);
             const int r = min(idx / VPR, len - 1), cv = (idx % VPR) * (16 / (int)sizeof(IT));
             vb[i] = *reinterpret_cast<const vec*>(v + ((size_t)(tok0 + r) * H + cp.h) * D + cp.v0 + cv);
         }
@@ -1460,16 +1464,16 @@ __global__ __launch_bounds__(256) void kda_state_chain(
         // the previous chunk's tiles are free: inter_chunk ends with a barrier
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
-            if (tid + 256 * i < NNEED) reinterpret_cast<vec*>(sm.img)[unit(tid + 256 * i)] = rb[i];
+            if (tid + NT * i < NNEED) reinterpret_cast<vec*>(sm.img)[unit(tid + NT * i)] = rb[i];
 #pragma unroll
         for (int i = 0; i < VPT; ++i)
-            if (tid + 256 * i < NVV) reinterpret_cast<vec*>(sm.vraw)[tid + 256 * i] = vb[i];
+            if (tid + NT * i < NVV) reinterpret_cast<vec*>(sm.vraw)[tid + NT * i] = vb[i];
         lds_barrier();
         if (c + 1 < cp.nch) fetch(c + 1);
-        chain_store_state<D, BV>(st, s_hist, ((size_t)(cp.first + c) * H + cp.h) * (size_t)D * D,
+        chain_store_state<D, BV, NWC>(st, s_hist, ((size_t)(cp.first + c) * H + cp.h) * (size_t)D * D,
                                  cp.v0);
         const size_t xo = ((size_t)(cp.first + c) * H + cp.h) * (size_t)C * D;
-        inter_chunk<D, C, BV, OT, IT, 4, false>(tiles, sm.cs, st, tok0, len, H, cp.h, cp.v0, 0.f,
+        inter_chunk<D, C, BV, OT, IT, NWC, false>(tiles, sm.cs, st, tok0, len, H, cp.h, cp.v0, 0.f,
                                                 nullptr, xh + xo, uh + xo);
     }
 }
@@ -3609,8 +3613,8 @@ static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan)
             auto kern = kda_state_chain<D, C, 16, OT, IT>;
             const size_t smem = inter_smem_bytes<D, C, 16, OT, IT>();
             if (hipError_t e = set_smem(kern, smem)) return e;
-            hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(256), smem, a.stream, a.T, a.H, a.N,
-                               nch_seq, (int)G8, a.cu_seqlens, chunk_off, (const IT*)a.v, a.s0,
+            hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(64 * kStateChainWaves), smem, a.stream, a.T,
+                               a.H, a.N, nch_seq, (int)G8, a.cu_seqlens, chunk_off, (const IT*)a.v, a.s0,
                                (const char*)ws + plan.f.off_records, s_hist, xh, uh);
             if (hipError_t e = hipGetLastError()) return e;
         }
