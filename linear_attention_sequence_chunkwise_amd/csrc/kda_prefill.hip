@@ -2834,12 +2834,12 @@ __global__ __launch_bounds__(64 * bwd_dv_waves<D>()) void kda_bwd_vprod(
 // block's inputs and gradient-record values are fetched into registers while
 // the current block computes.  Only lower tiles of the C x C matrices are
 // formed or read.
-constexpr int kBwdIntraWaves = 8;
+constexpr int kBwdIntraWaves = 4;
 
 template <int C>
 struct BwdIntraSmem {
     static constexpr int NT = 64 * kBwdIntraWaves;
-    static constexpr int LDC = C + 1, CB = 32, LDB = CB + 1;
+    static constexpr int LDC = C + 1, CB = 16, LDB = CB + 1;
     static constexpr int NSEG = NT / CB;     // row segments per channel in the scans
     static constexpr int RS = C / NSEG;      // rows per segment
     float dP[C * LDC];     // dTb (lower), then dT T^T, then diag(beta) dA
