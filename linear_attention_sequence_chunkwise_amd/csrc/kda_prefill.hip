@@ -2645,8 +2645,9 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
 // this kernel only accumulates the five products that contract over dv:
 //   d(Q Gamma) = scale dO S^T,  d(K Gamma) = -dX S^T,  dKE = U dSn^T   (C x dk)
 //   dM = scale dO U^T,  dTb = dU X^T                                      (lower C x C)
-// and dGamma_n = rowsum(dSn * S).  Eight wavefronts; the next block's columns
-// are fetched into registers while the current block computes.
+// and dGamma_n = rowsum(dSn * S).  Sixteen wavefronts (eight at d = 32; see
+// bwd_dv_waves); the next block's columns are fetched into registers while
+// the current block computes.
 template <int D, int C>
 struct BwdDvSmem {
     // rows of the 16-column block padded to 20 floats: 16-byte aligned, so
@@ -2828,12 +2829,13 @@ __global__ __launch_bounds__(64 * bwd_dv_waves<D>()) void kda_bwd_vprod(
 // ---- B4b: intra-chunk backward, per (chunk, head), fp32 ----
 // T and the strict-lower Gram P = KG KI^T come from the records kernel (aux
 // buffer).  Phase 1 forms dbeta and dP = diag(beta) dA; phase 2 walks the
-// channels in blocks of 32: chunk-local cumulative gates by a segmented scan,
-// the three C x 32 products (one 16x16 tile per wavefront), the element-wise
+// channels in blocks of 16: chunk-local cumulative gates by a segmented scan,
+// the three C x 16 products (one 16x16 tile per wavefront), the element-wise
 // dq, dk, dG and the reverse cumulative sum that turns dG into dg.  The next
 // block's inputs and gradient-record values are fetched into registers while
 // the current block computes.  Only lower tiles of the C x C matrices are
-// formed or read.
+// formed or read.  Four wavefronts and 16-channel blocks keep the LDS at
+// about 70 KiB (C = 64): two workgroups share a CU.
 constexpr int kBwdIntraWaves = 4;
 
 template <int C>
