@@ -1401,80 +1401,174 @@ __global__ __launch_bounds__(256) void kda_inter(
 
 // Forward chain of the backward pass: the state at the start of every chunk
 // into s_hist ([chunk][H][D][D] fp32) and the chunk's X and U into xh, uh
-// ([chunk][H][C][D] fp32), no output.  Only the record parts the
-// state update reads are loaded (KG, KPt, Tb, Gamma_n), and the next chunk's
-// parts are fetched into registers while the current chunk computes.  Eight
-// wavefronts: the state update (eight 16x16 tiles per slice) takes one tile
-// per wavefront.
+// ([chunk][H][C][D] fp32), no output.  Eight wavefronts per (sequence, head,
+// 16-column slice).  Every record element is an operand of exactly one
+// wavefront (the X and U row tiles, one state tile each), so the record never
+// goes through LDS: each wavefront loads its own operand fragments (16-byte
+// groups of four consecutive k along a record row) into registers, one chunk
+// ahead, each right after the phase that consumed the previous ones.  Only
+// the B operands (S, X, U, [column][k] rows) pass through LDS.
 constexpr int kStateChainWaves = 8;
+template <int D, int C>
+struct StateChainSmem {
+    static constexpr int LDK = D + 4, LDC = C + 4;   // 16-byte multiples
+    alignas(16) float s[16 * LDK];                   // state, [n][channel]
+    alignas(16) float x[16 * LDC];                   // X, [n][token]
+    alignas(16) float u[16 * LDC];                   // U, [n][token]
+};
+
+// acc += A B for one 16x16 tile over NG groups of 16 k: A fragments in
+// registers, a[g] = A(lane % 16, 16 g + 4 (lane / 16) + 0..3), B read through
+// b(g) as the lane's four k of group g (a permutation of the contraction).
+// Two accumulators alternate.
+template <int NG, int NA, typename FB>
+__device__ __forceinline__ float4v frag_mma4(float4v acc, const float4v (&a)[NA], FB b) {
+    static_assert(NG <= NA, "fragment count");
+    float4v acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const float4v bv = b(g);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][0], bv[0], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][1], bv[1], acc2, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][2], bv[2], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][3], bv[3], acc2, 0, 0, 0);
+    }
+    return acc + acc2;
+}
+
+// Row fragments of a swizzled fp32 record tile P ([rows][LD]): f[g] = the
+// lane's 16-byte group of row 16 t + lane % 16 at k = 16 g + 4 (lane / 16).
+template <int LD, int NG, int NA>
+__device__ __forceinline__ void load_frag_rows(float4v (&f)[NA], const float* P, int t) {
+    static_assert(NG <= NA, "fragment count");
+    const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        f[g] = *reinterpret_cast<const float4v*>(P + swz<float, LD>(16 * t + l16, 16 * g + 4 * lq));
+}
+
 template <int D, int C, int BV, typename OT, typename IT>
 __global__ __launch_bounds__(64 * kStateChainWaves) void kda_state_chain(
     int T, int H, int N_seq, int nch_seq, int G8, const int32_t* __restrict__ cu,
     const int* __restrict__ chunk_off, const IT* __restrict__ v, const float* __restrict__ s0,
     const char* __restrict__ records, float* __restrict__ s_hist, float* __restrict__ xh,
     float* __restrict__ uh) {
-    constexpr int NWC = kStateChainWaves, NT = 64 * NWC;
-    constexpr int ST = (D / 16) * (BV / 16);
-    constexpr int SPW = (ST + NWC - 1) / NWC;
+    static_assert(sizeof(OT) == 4 && BV == 16, "fp32 records, 16-column slices");
     typedef Rec<D, C, OT> R;
-    typedef u32x4 vec;
-    // needed 16-byte units: KG, then KPt and Tb, then Gamma_n
-    constexpr int A_END = (int)(R::QG * sizeof(OT) / 16);
-    constexpr int B_BEG = (int)(R::KPt * sizeof(OT) / 16), B_END = (int)(R::M * sizeof(OT) / 16);
-    constexpr int G_BEG = (int)(R::gn_byte / 16), G_END = (int)((R::gn_byte + 4 * D) / 16);
-    constexpr int NNEED = A_END + (B_END - B_BEG) + (G_END - G_BEG);
-    constexpr int RPT = (NNEED + NT - 1) / NT;
-    constexpr int VPR = BV * (int)sizeof(IT) / 16;
-    constexpr int NVV = C * VPR;
-    constexpr int VPT = (NVV + NT - 1) / NT;
-    static_assert(R::gn_byte % 16 == 0 && (4 * D) % 16 == 0, "record unit alignment");
+    typedef StateChainSmem<D, C> SM;
+    constexpr int NW = kStateChainWaves;
+    constexpr int CK = R::CK, LDK = SM::LDK, LDC = SM::LDC;
+    constexpr int RT = C / 16, DT = D / 16;
+    static_assert(CK == C && RT <= NW && DT <= NW, "one tile per wavefront and phase");
     extern __shared__ __align__(16) char smem_raw[];
-    InterSmem<D, C, BV, OT, IT>& sm = *reinterpret_cast<InterSmem<D, C, BV, OT, IT>*>(smem_raw);
+    SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
     const ChainPos cp = chain_pos<D, BV>(T, H, N_seq, nch_seq, G8, cu, chunk_off);
     if (!cp.valid) return;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, lq = lane >> 4;
+    const bool xu = wave < RT;              // X and U row tile rt = wave
+    const bool sj = DT >= NW || wave < DT;  // state tile: channels 16 wave ..
+    // Every wavefront issues the same global loads and stores in every
+    // chunk (wavefronts without a tile load a neighbour's fragments, the last
+    // chunk reloads itself): the compiler's wait counts, merged over all
+    // paths, then let the next chunk's fragments stay in flight.
+    const int rtl = min(wave, RT - 1), stl = min(wave, DT - 1);
     const size_t sbase = ((size_t)cp.n * H + cp.h) * (size_t)D * D;
-    float4v st[SPW];
-    chain_load_state<D, C, BV, OT, NWC, true>(st, sm.cs, s0, sbase, cp.v0);
-    const ChunkTiles<D, C, OT, IT> tiles(sm.img, sm.vraw);
-    auto unit = [](int j) {
-        return j < A_END ? j : j < A_END + (B_END - B_BEG) ? B_BEG + (j - A_END)
-                                                           : G_BEG + (j - A_END - (B_END - B_BEG));
-    };
 
-    vec rb[RPT], vb[VPT];
-    auto fetch = [&](int c) {
-        const int tok0 = cp.seq_tok0 + c * C;
-        const int len = min(C, cp.seq_len - c * C);
-        const vec* rec = reinterpret_cast<const vec*>(records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes);
+    float4v st = {0.f, 0.f, 0.f, 0.f};
+    if (sj && s0) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) rb[i] = rec[unit(min(tid + NT * i, NNEED - 1))];
+        for (int j = 0; j < 4; ++j) st[j] = s0[sbase + (size_t)(16 * wave + 4 * lq + j) * D + cp.v0 + l16];
+    }
+    if (sj) *reinterpret_cast<float4v*>(&sm.s[l16 * LDK + 16 * wave + 4 * lq]) = st;
+
+    float4v fx[DT], fu[RT], fs[RT];
+    float fg[4], fv[4];
+    auto rec_of = [&](int c) {
+        return reinterpret_cast<const float*>(records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes);
+    };
+    // KG rows and the value rows of X (rows past the chunk are masked at use)
+    auto load_x = [&](int c) {
+        load_frag_rows<D, DT>(fx, rec_of(c) + R::KG, rtl);
+        const int tok0 = cp.seq_tok0 + c * C, len = min(C, cp.seq_len - c * C);
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = min(tid + NT * i, NVV - 1);
-            const int r = min(idx / VPR, len - 1), cv = (idx % VPR) * (16 / (int)sizeof(IT));
-            vb[i] = *reinterpret_cast<const vec*>(v + ((size_t)(tok0 + r) * H + cp.h) * D + cp.v0 + cv);
+        for (int j = 0; j < 4; ++j) {
+            const int r = min(16 * rtl + 4 * lq + j, len - 1);
+            fv[j] = to_f32(v[((size_t)(tok0 + r) * H + cp.h) * D + cp.v0 + l16]);
         }
     };
-    if (cp.nch > 0) fetch(0);
+    auto load_u = [&](int c) { load_frag_rows<CK, RT>(fu, rec_of(c) + R::Tb, rtl); };
+    auto load_s = [&](int c) {
+        const float* rp = rec_of(c);
+        load_frag_rows<CK, RT>(fs, rp + R::KPt, stl);
+        const float* gp = reinterpret_cast<const float*>(reinterpret_cast<const char*>(rp) + R::gn_byte);
+        const float4v g4 = *reinterpret_cast<const float4v*>(gp + 16 * stl + 4 * lq);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fg[j] = g4[j];
+    };
+    if (cp.nch > 0) {
+        load_x(0);
+        load_u(0);
+        load_s(0);
+    }
+    // Compiler-visible vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt at their
+    // maxima): nothing pending enters the loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();   // initial state published
     for (int c = 0; c < cp.nch; ++c) {
-        const int tok0 = cp.seq_tok0 + c * C;
+        const int cn = min(c + 1, cp.nch - 1);
         const int len = min(C, cp.seq_len - c * C);
-        // the previous chunk's tiles are free: inter_chunk ends with a barrier
-#pragma unroll
-        for (int i = 0; i < RPT; ++i)
-            if (tid + NT * i < NNEED) reinterpret_cast<vec*>(sm.img)[unit(tid + NT * i)] = rb[i];
-#pragma unroll
-        for (int i = 0; i < VPT; ++i)
-            if (tid + NT * i < NVV) reinterpret_cast<vec*>(sm.vraw)[tid + NT * i] = vb[i];
-        lds_barrier();
-        if (c + 1 < cp.nch) fetch(c + 1);
-        chain_store_state<D, BV, NWC>(st, s_hist, ((size_t)(cp.first + c) * H + cp.h) * (size_t)D * D,
-                                 cp.v0);
         const size_t xo = ((size_t)(cp.first + c) * H + cp.h) * (size_t)C * D;
-        inter_chunk<D, C, BV, OT, IT, NWC, false>(tiles, sm.cs, st, tok0, len, H, cp.h, cp.v0, 0.f,
-                                                nullptr, xh + xo, uh + xo);
+        // the state at the chunk start
+        if (sj) {
+            float* sh = s_hist + ((size_t)(cp.first + c) * H + cp.h) * (size_t)D * D;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sh[(size_t)(16 * wave + 4 * lq + j) * D + cp.v0 + l16] = st[j];
+        }
+        // ---- X = V - KG S ----
+        if (xu) {
+            const float4v xk = frag_mma4<DT>(float4v{0.f, 0.f, 0.f, 0.f}, fx, [&](int g) {
+                return *reinterpret_cast<const float4v*>(&sm.s[l16 * LDK + 16 * g + 4 * lq]);
+            });
+            float4v x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = (16 * wave + 4 * lq + j < len ? fv[j] : 0.f) - xk[j];
+            *reinterpret_cast<float4v*>(&sm.x[l16 * LDC + 16 * wave + 4 * lq]) = x;
+        }
+        load_x(cn);
+        lds_barrier();
+        // X and U rows to xh, uh from LDS, by every thread
+        auto store_rows = [&](const float* src, float* dst) {
+#pragma unroll
+            for (int i = 0; i < (16 * C + 64 * NW - 1) / (64 * NW); ++i) {
+                const int idx = min((int)threadIdx.x + 64 * NW * i, 16 * C - 1);
+                const int r = idx / 16, col = idx % 16;
+                dst[xo + (size_t)r * D + cp.v0 + col] = src[col * LDC + r];
+            }
+        };
+        store_rows(sm.x, xh);
+        // ---- U = Tb X (Tb lower triangular, zeros stored above) ----
+        if (xu) {
+            const float4v u = frag_mma4<RT>(float4v{0.f, 0.f, 0.f, 0.f}, fu, [&](int g) {
+                return *reinterpret_cast<const float4v*>(&sm.x[l16 * LDC + 16 * g + 4 * lq]);
+            });
+            *reinterpret_cast<float4v*>(&sm.u[l16 * LDC + 16 * wave + 4 * lq]) = u;
+        }
+        load_u(cn);
+        lds_barrier();
+        store_rows(sm.u, uh);
+        // ---- S <- Diag(Gamma_n) S + KPt U ----
+        if (sj) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st[j] *= fg[j];
+            st = frag_mma4<RT>(st, fs, [&](int g) {
+                return *reinterpret_cast<const float4v*>(&sm.u[l16 * LDC + 16 * g + 4 * lq]);
+            });
+            // the old state's last reads (X) are behind the first barrier
+            *reinterpret_cast<float4v*>(&sm.s[l16 * LDK + 16 * wave + 4 * lq]) = st;
+        }
+        load_s(cn);
+        lds_barrier();
     }
 }
 
@@ -2443,18 +2537,21 @@ struct GradRec {
 };
 
 // ---- B3: reverse chain ----
-// Eight wavefronts per (sequence, head, 16-column slice).  The next (earlier)
-// chunk's record and dO columns are fetched into registers while the current
-// chunk computes; the two products of dU run on separate wavefronts.  Writes
-// dV (= dX) and the chunk's dU and dX ([chunk][H][C][D] fp32) for B4a.
-// The products' right operands (dO, dS, dU, dX) are kept as [column][k]
-// rows of 16-byte groups: a lane reads four consecutive k at once (and a
-// matrix-core output tile is stored as one 16-byte write per lane).
+// Eight wavefronts per (sequence, head, 16-column slice); writes dV (= dX)
+// and the chunk's dU and dX ([chunk][H][C][D] fp32) for B4a.  Every record
+// element is an operand of exactly one wavefront's tile: the record never
+// goes through LDS.  Each wavefront loads its own A fragments straight into
+// registers, one chunk ahead, each right after the phase that consumed the
+// previous ones; the record tiles enter transposed (the contraction runs
+// along their columns), so a fragment is one element per product.  The
+// right operands (dO, dS, dU, dX) are kept in LDS as [column][k] rows of
+// 16-byte groups: a lane reads four consecutive k at once, and the four
+// 16x16x4 steps of group g take k = 16 g + 4 (lane / 16) + s (a permutation
+// of the contraction).  dO is double-buffered, so a chunk has three barriers.
 template <int D, int C, typename OT>
 struct BwdChainSmem {
     static constexpr int LDO = C + 4, LDD = D + 4;   // row strides (floats), 16-byte multiples
-    alignas(16) char img[Rec<D, C, OT>::bytes];
-    alignas(16) float dO[16 * LDO];                  // [n][token]
+    alignas(16) float dO[2][16 * LDO];               // [n][token], chunks alternate
     alignas(16) float dS[16 * LDD];                  // [n][channel]
     alignas(16) float dUa[16 * LDO], dUb[16 * LDO];  // scale M^T dO and KE dSn, [n][token]
     alignas(16) float dX[16 * LDO];                  // [n][token]
@@ -2462,24 +2559,34 @@ struct BwdChainSmem {
 
 constexpr int kBwdChainWaves = 8;
 
-// acc += A(m, k) B[n][k] over k = 16 g0 .. NK for one 16x16 tile: A read
-// element-wise through `a`, B an [n][ldb] fp32 array in LDS read as 16-byte
-// groups (`b(g)` returns lane's four k of group g).  The four 16x16x4 steps of
-// group g take k = 16 g + 4 (lane / 16) + s, s = 0..3 (a permutation of the
-// contraction), alternating between two accumulators.
-template <int NK, typename FA, typename FB>
-__device__ __forceinline__ float4v tile_mma_bv(float4v acc, int g0, FA a, FB b) {
-    const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
-    float4v acc2 = {0.f, 0.f, 0.f, 0.f};
-    for (int g = g0; g < NK / 16; ++g) {
+// acc += A B for one 16x16 tile over NG groups of 16 k: A fragments in
+// registers, a[4 g + s] = A(lane % 16, 16 g + 4 (lane / 16) + s), B through
+// b(g) as the lane's four k of group g.  Two accumulators alternate.
+template <int NG, int NA, typename FB>
+__device__ __forceinline__ float4v frag_mma1(const float (&a)[NA], FB b) {
+    static_assert(4 * NG <= NA, "fragment count");
+    float4v acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
         const float4v bv = b(g);
-        const int k = 16 * g + 4 * lq;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, k), bv[0], acc, 0, 0, 0);
-        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, k + 1), bv[1], acc2, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, k + 2), bv[2], acc, 0, 0, 0);
-        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, k + 3), bv[3], acc2, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * g], bv[0], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * g + 1], bv[1], acc2, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * g + 2], bv[2], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * g + 3], bv[3], acc2, 0, 0, 0);
     }
     return acc + acc2;
+}
+
+// Transposed fragments of a swizzled fp32 record tile P ([rows][LD]):
+// f[4 g + s] = P[16 g + 4 (lane / 16) + s][16 t + lane % 16], g < NG.
+template <int LD, int NG, int NA>
+__device__ __forceinline__ void load_frag_cols(float (&f)[NA], const float* P, int t) {
+    static_assert(4 * NG <= NA, "fragment count");
+    const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) f[4 * g + s] = P[swz<float, LD>(16 * g + 4 * lq + s, 16 * t + l16)];
 }
 
 template <int D, int C, typename OT>
@@ -2489,16 +2596,16 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
     const float* __restrict__ d_o, const float* __restrict__ dS_final,
     float* __restrict__ ds_hist, float* __restrict__ dS0, float* __restrict__ duh,
     float* __restrict__ dxh, float* __restrict__ dv_out) {
+    static_assert(sizeof(OT) == 4, "the backward reads fp32 records");
     constexpr int NW = kBwdChainWaves, NT = 64 * NW;
     constexpr int BV = 16;
     constexpr int LDO = BwdChainSmem<D, C, OT>::LDO, LDD = BwdChainSmem<D, C, OT>::LDD;
     typedef Rec<D, C, OT> R;
     constexpr int CK = R::CK;
-    constexpr int NREC = (int)(R::bytes / 16);
-    constexpr int RPT = (NREC + NT - 1) / NT;
     constexpr int NDO = (C * BV + NT - 1) / NT;
-    constexpr int RT = C / 16, DT = D / 16, SPW = (DT + NW - 1) / NW;
-    typedef u32x4 vec;
+    constexpr int RT = C / 16, DT = D / 16;
+    constexpr int NA1 = (C > D ? C : D) / 4;
+    static_assert(CK == C && 2 * RT <= NW && DT <= NW, "one tile per wavefront and phase");
     extern __shared__ __align__(16) char smem_raw[];
     BwdChainSmem<D, C, OT>& sm = *reinterpret_cast<BwdChainSmem<D, C, OT>*>(smem_raw);
 
@@ -2506,32 +2613,55 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
     if (!cp.valid) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lq = lane >> 4;
+    // roles: dU job (scale M^T dO, rt = wave; KE dSn, rt = wave - RT), dX
+    // tile rt = wave, dS tile s = wave
+    const bool mj = wave < RT, kj = wave >= RT && wave < 2 * RT;
+    const int rt1 = mj ? wave : min(wave - RT, RT - 1);
+    const bool xj = wave < RT, sj = DT >= NW || wave < DT;
+    // Every wavefront issues the same global loads and stores in every chunk
+    // (wavefronts without a tile load a neighbour's fragments, the first
+    // chunk reloads itself): the compiler's wait counts, merged over all
+    // paths, then let the next chunk's fragments stay in flight.
+    const int xtl = min(wave, RT - 1), stl = min(wave, DT - 1);
     const size_t sbase = ((size_t)cp.n * H + cp.h) * (size_t)D * D;
-    const OT* img = reinterpret_cast<const OT*>(sm.img);
-    const float* gn = reinterpret_cast<const float*>(sm.img + R::gn_byte);
 
-    float4v ds[SPW];
+    float4v ds = {0.f, 0.f, 0.f, 0.f};
+    if (sj && dS_final) {
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int s = wave + NW * i;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            ds[i][j] = (dS_final && s < DT)
-                           ? dS_final[sbase + (size_t)(16 * s + 4 * lq + j) * D + cp.v0 + l16]
-                           : 0.f;
+        for (int j = 0; j < 4; ++j) ds[j] = dS_final[sbase + (size_t)(16 * wave + 4 * lq + j) * D + cp.v0 + l16];
     }
-    vec rb[RPT];
+    float f1[NA1], f2[C / 4], fq[C / 4], fk[C / 4], fg[4];
     float dov[NDO];
     // rows of the fetched chunk: rows past it are zeroed when the fetched dO
-    // reaches LDS, not at the fetch (a select there would wait for the loads,
-    // and with them, in issue order, for the whole record fetch)
+    // reaches LDS, not at the fetch (a select there would wait for the loads)
     int dlen = 0;
-    auto fetch = [&](int c) {
+    auto rec_of = [&](int c) {
+        return reinterpret_cast<const float*>(records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes);
+    };
+    // phase-1 fragments: NA1 / 4 groups for every wavefront (the M tile's
+    // C / 16 groups repeat)
+    auto load1 = [&](int c) {
+        const float* P = rec_of(c) + (mj ? R::M : R::KPt);
+        const int rows = mj ? C : D;
+#pragma unroll
+        for (int g = 0; g < NA1 / 4; ++g)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+                f1[4 * g + s4] = P[swz<float, CK>((16 * g + 4 * lq + s4) % rows, 16 * rt1 + l16)];
+    };
+    auto load2 = [&](int c) { load_frag_cols<CK, C / 16>(f2, rec_of(c) + R::Tb, xtl); };
+    auto load3 = [&](int c) {
+        const float* rp = rec_of(c);
+        load_frag_cols<D, C / 16>(fq, rp + R::QG, stl);
+        load_frag_cols<D, C / 16>(fk, rp + R::KG, stl);
+        const float* gp = reinterpret_cast<const float*>(reinterpret_cast<const char*>(rp) + R::gn_byte);
+        const float4v g4 = *reinterpret_cast<const float4v*>(gp + 16 * stl + 4 * lq);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fg[j] = g4[j];
+    };
+    auto fetch_do = [&](int c) {
         const int tok0 = cp.seq_tok0 + c * C;
         const int len = min(C, cp.seq_len - c * C);
-        const vec* rec = reinterpret_cast<const vec*>(records + ((size_t)(cp.first + c) * H + cp.h) * R::bytes);
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) rb[i] = rec[min(tid + NT * i, NREC - 1)];
 #pragma unroll
         for (int i = 0; i < NDO; ++i) {
             const int idx = min(tid + NT * i, C * BV - 1);
@@ -2540,103 +2670,90 @@ __global__ __launch_bounds__(64 * kBwdChainWaves) void kda_bwd_chain(
         }
         dlen = len;
     };
-    if (cp.nch > 0) fetch(cp.nch - 1);
-    const float4v z = {0.f, 0.f, 0.f, 0.f};
+    if (cp.nch > 0) {
+        load1(cp.nch - 1);
+        load2(cp.nch - 1);
+        load3(cp.nch - 1);
+        fetch_do(cp.nch - 1);
+    }
+    // Compiler-visible vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt at their
+    // maxima): nothing pending enters the loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     for (int c = cp.nch - 1; c >= 0; --c) {
+        const int cp1 = max(c - 1, 0);
         const int chunk = cp.first + c;
         const int tok0 = cp.seq_tok0 + c * C;
         const int len = min(C, cp.seq_len - c * C);
         const size_t xo = ((size_t)chunk * H + cp.h) * (size_t)C * D;
+        float* sdo = sm.dO[c & 1];
         // dSn of this chunk, for B4a
-        float* dh = ds_hist + ((size_t)chunk * H + cp.h) * (size_t)D * D;
+        if (sj) {
+            float* dh = ds_hist + ((size_t)chunk * H + cp.h) * (size_t)D * D;
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int s = wave + NW * i;
-            if (s < DT) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dh[(size_t)(16 * s + 4 * lq + j) * D + cp.v0 + l16] = ds[i][j];
-            }
+            for (int j = 0; j < 4; ++j) dh[(size_t)(16 * wave + 4 * lq + j) * D + cp.v0 + l16] = ds[j];
         }
-        lds_barrier();   // the previous chunk's reads of LDS are complete
-#pragma unroll
-        for (int i = 0; i < RPT; ++i)
-            if (tid + NT * i < NREC) reinterpret_cast<vec*>(sm.img)[tid + NT * i] = rb[i];
+        // dO into the buffer last read two chunks ago; dS, last read by the
+        // previous chunk's dU products (behind its second barrier)
 #pragma unroll
         for (int i = 0; i < NDO; ++i) {
             const int idx = tid + NT * i;
-            if (idx < C * BV) sm.dO[(idx % BV) * LDO + idx / BV] = idx / BV < dlen ? dov[i] : 0.f;
+            if (idx < C * BV) sdo[(idx % BV) * LDO + idx / BV] = idx / BV < dlen ? dov[i] : 0.f;
         }
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int s = wave + NW * i;
-            if (s < DT) *reinterpret_cast<float4v*>(&sm.dS[l16 * LDD + 16 * s + 4 * lq]) = ds[i];
-        }
+        if (sj) *reinterpret_cast<float4v*>(&sm.dS[l16 * LDD + 16 * wave + 4 * lq]) = ds;
         lds_barrier();
-        if (c > 0) fetch(c - 1);
-        // dU = scale M^T dO (jobs [0, RT)) + KE dSn (jobs [RT, 2 RT));
-        // M[i][r] vanishes for i < r
-        for (int jb = wave; jb < 2 * RT; jb += NW) {
-            const int rt = jb % RT;
+        fetch_do(cp1);
+        // ---- dU = scale M^T dO (M[i][r] = 0 for i < r, zeros stored) + KE dSn ----
+        if (mj || kj) {
             float4v a;
-            if (jb < RT)
-                a = tile_mma_bv<C>(z, rt, [&](int m, int k) { return (float)img[R::M + swz<OT, CK>(k, 16 * rt + m)]; },
-                                   [&](int g) { return *reinterpret_cast<const float4v*>(&sm.dO[l16 * LDO + 16 * g + 4 * lq]); });
+            if (mj)
+                a = scale * frag_mma1<C / 16>(f1, [&](int g) {
+                        return *reinterpret_cast<const float4v*>(&sdo[l16 * LDO + 16 * g + 4 * lq]);
+                    });
             else
-                a = tile_mma_bv<D>(z, 0, [&](int m, int k) { return (float)img[R::KPt + swz<OT, CK>(k, 16 * rt + m)]; },
-                                   [&](int g) { return *reinterpret_cast<const float4v*>(&sm.dS[l16 * LDD + 16 * g + 4 * lq]); });
-            float* dst = jb < RT ? sm.dUa : sm.dUb;
-            const float f = jb < RT ? scale : 1.f;
-            *reinterpret_cast<float4v*>(&dst[l16 * LDO + 16 * rt + 4 * lq]) = f * a;
+                a = frag_mma1<D / 16>(f1, [&](int g) {
+                    return *reinterpret_cast<const float4v*>(&sm.dS[l16 * LDD + 16 * g + 4 * lq]);
+                });
+            *reinterpret_cast<float4v*>(&(mj ? sm.dUa : sm.dUb)[l16 * LDO + 16 * rt1 + 4 * lq]) = a;
         }
         lds_barrier();
         for (int idx = tid; idx < C * BV; idx += NT) {
             const int r = idx / BV, col = idx % BV;
             duh[xo + (size_t)r * D + cp.v0 + col] = sm.dUa[col * LDO + r] + sm.dUb[col * LDO + r];
         }
-        // dX = Tb^T dU (Tb[i][r] vanishes for i < r) = dV
-        for (int rt = wave; rt < RT; rt += NW) {
-            const float4v x = tile_mma_bv<C>(
-                z, rt, [&](int m, int k) { return (float)img[R::Tb + swz<OT, CK>(k, 16 * rt + m)]; },
-                [&](int g) {
-                    return *reinterpret_cast<const float4v*>(&sm.dUa[l16 * LDO + 16 * g + 4 * lq]) +
-                           *reinterpret_cast<const float4v*>(&sm.dUb[l16 * LDO + 16 * g + 4 * lq]);
-                });
-            *reinterpret_cast<float4v*>(&sm.dX[l16 * LDO + 16 * rt + 4 * lq]) = x;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * rt + 4 * lq + j;
-                dxh[xo + (size_t)r * D + cp.v0 + l16] = x[j];
-                if (r < len) dv_out[((size_t)(tok0 + r) * H + cp.h) * D + cp.v0 + l16] = x[j];
-            }
+        load1(cp1);
+        // ---- dX = Tb^T dU (Tb[i][r] = 0 for i < r, zeros stored) = dV ----
+        if (xj) {
+            const float4v x = frag_mma1<C / 16>(f2, [&](int g) {
+                return *reinterpret_cast<const float4v*>(&sm.dUa[l16 * LDO + 16 * g + 4 * lq]) +
+                       *reinterpret_cast<const float4v*>(&sm.dUb[l16 * LDO + 16 * g + 4 * lq]);
+            });
+            *reinterpret_cast<float4v*>(&sm.dX[l16 * LDO + 16 * wave + 4 * lq]) = x;
         }
+        load2(cp1);
         lds_barrier();
-        // dS = Gamma_n dSn + scale QG^T dO - KG^T dX
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int s = wave + NW * i;
-            if (s < DT) {
-                const float4v a = tile_mma_bv<C>(
-                    z, 0, [&](int m, int k) { return (float)img[R::QG + swz<OT, D>(k, 16 * s + m)]; },
-                    [&](int g) { return *reinterpret_cast<const float4v*>(&sm.dO[l16 * LDO + 16 * g + 4 * lq]); });
-                const float4v b = tile_mma_bv<C>(
-                    z, 0, [&](int m, int k) { return (float)img[R::KG + swz<OT, D>(k, 16 * s + m)]; },
-                    [&](int g) { return *reinterpret_cast<const float4v*>(&sm.dX[l16 * LDO + 16 * g + 4 * lq]); });
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    ds[i][j] = gn[16 * s + 4 * lq + j] * ds[i][j] + scale * a[j] - b[j];
-            }
+        // dX rows to dxh and dv (rows of the chunk only), by every thread
+        for (int idx = tid; idx < C * BV; idx += NT) {
+            const int r = idx / BV, col = idx % BV;
+            const float x = sm.dX[col * LDO + r];
+            dxh[xo + (size_t)r * D + cp.v0 + col] = x;
+            if (r < len) dv_out[((size_t)(tok0 + r) * H + cp.h) * D + cp.v0 + col] = x;
         }
+        // ---- dS = Gamma_n dSn + scale QG^T dO - KG^T dX ----
+        if (sj) {
+            const float4v a = frag_mma1<C / 16>(fq, [&](int g) {
+                return *reinterpret_cast<const float4v*>(&sdo[l16 * LDO + 16 * g + 4 * lq]);
+            });
+            const float4v b = frag_mma1<C / 16>(fk, [&](int g) {
+                return *reinterpret_cast<const float4v*>(&sm.dX[l16 * LDO + 16 * g + 4 * lq]);
+            });
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ds[j] = fg[j] * ds[j] + scale * a[j] - b[j];
+        }
+        load3(cp1);
     }
-    if (dS0) {
+    if (dS0 && sj) {
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int s = wave + NW * i;
-            if (s < DT) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    dS0[sbase + (size_t)(16 * s + 4 * lq + j) * D + cp.v0 + l16] = ds[i][j];
-            }
-        }
+        for (int j = 0; j < 4; ++j) dS0[sbase + (size_t)(16 * wave + 4 * lq + j) * D + cp.v0 + l16] = ds[j];
     }
 }
 
@@ -3525,7 +3642,7 @@ template <int D, int C, typename OT, typename IT>
 constexpr bool bwd_fits() {
     return sizeof(BwdChainSmem<D, C, OT>) <= kLdsLimit && sizeof(BwdDvSmem<D, C>) <= kLdsLimit &&
            sizeof(BwdIntraSmem<C>) <= kLdsLimit && fits<D, C, OT>() &&
-           inter_smem_bytes<D, C, 16, OT, IT>() <= kLdsLimit;
+           sizeof(StateChainSmem<D, C>) <= kLdsLimit;
 }
 
 bool backward_supported(int D, int C, bool bf16) {
@@ -3613,7 +3730,7 @@ static hipError_t launch_bwd_dc(const BackwardArgs& b, const BackwardPlan& plan)
         // forward chain keeping the state at every chunk start
         {
             auto kern = kda_state_chain<D, C, 16, OT, IT>;
-            const size_t smem = inter_smem_bytes<D, C, 16, OT, IT>();
+            const size_t smem = sizeof(StateChainSmem<D, C>);
             if (hipError_t e = set_smem(kern, smem)) return e;
             hipLaunchKernelGGL(kern, dim3((unsigned)(8 * G8)), dim3(64 * kStateChainWaves), smem, a.stream, a.T,
                                a.H, a.N, nch_seq, (int)G8, a.cu_seqlens, chunk_off, (const IT*)a.v, a.s0,
