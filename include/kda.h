@@ -47,8 +47,8 @@
  *     whose per-channel gate sum falls below -8 (bf16 inputs) or -40 (fp32)
  *     gets its diagonal Gram tiles from an exact fp32 path instead of the
  *     matrix cores; this costs time only for such sub-blocks.
- *     kda_chunk_bwd and kda_dplr_chunk_fwd keep narrower domains, stated at
- *     their declarations.
+ *     kda_chunk_bwd has the same domain; kda_dplr_chunk_fwd keeps a narrower
+ *     one, stated at its declaration.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -346,9 +346,12 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv,
  *   workspace      at least kda_chunk_bwd_workspace_bytes(...) bytes,
  *                  256-byte aligned; contents on entry are ignored.
  * Errors as for kda_chunk_fwd, with KDA_ERR_BAD_SHAPE from 2^23 (chunk, head)
- * pairs on.  Domain: that of kda_chunk_fwd, and within a chunk the
- * per-channel sum of -g stays below 80 (the intra-chunk gradient is formed
- * with exp(+-G) relative to the chunk start in fp32). */
+ * pairs on.  Domain: that of kda_chunk_fwd (any g <= 0).  The intra-chunk
+ * gradient is formed with factors exp(+-G) relative to the chunk start while
+ * every per-channel chunk sum of g stays above -60; a 16-channel block of a
+ * chunk with a sum below that takes an exact path whose decay factors are
+ * running products of per-token gates (slower: about 1.4x the call time when
+ * every block takes it). */
 kda_status kda_chunk_bwd(int B, int T, int H, int dk, int dv, int chunk,
                          float scale, kda_dtype qkv_dtype,
                          const void *q, const void *k, const void *v,

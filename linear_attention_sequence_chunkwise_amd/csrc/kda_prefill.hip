@@ -2954,6 +2954,9 @@ __global__ __launch_bounds__(64 * bwd_dv_waves<D>()) void kda_bwd_vprod(
 // formed or read.  Four wavefronts and 16-channel blocks keep the LDS at
 // about 70 KiB (C = 64): two workgroups share a CU.
 constexpr int kBwdIntraWaves = 4;
+// A channel block whose chunk gate sum falls below this takes the exact path
+// of kda_bwd_intra (e^{+-60} keeps the fast path's factors well inside fp32).
+constexpr float kBwdExactChunk = -60.f;
 
 template <int C>
 struct BwdIntraSmem {
@@ -3187,73 +3190,150 @@ __global__ __launch_bounds__(64 * kBwdIntraWaves) void kda_bwd_intra(
             sm.tot[ss * CB + sc] = run;
         }
         lds_barrier();
-        float off = 0.f, gnv = 0.f;
+        // G_r = off + the segment's running sum; G_n (gnv) and the gate sum of
+        // the rows after this segment (aft) are sums of whole segments
+        float off = 0.f, gnv = 0.f, aft = 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < NSEG; ++s2) {
             const float t = sm.tot[s2 * CB + sc];
             gnv += t;
             off += s2 < ss ? t : 0.f;
+            aft += s2 > ss ? t : 0.f;
         }
+#pragma unroll
+        for (int j = 0; j < RS; ++j) gv[j] += off;
         const float egn = exp_e(gnv);
-        float ga[RS], gi[RS];
-#pragma unroll
-        for (int j = 0; j < RS; ++j) {
-            const int r = RS * ss + j;
-            gv[j] += off;
-            ga[j] = exp_e(gv[j]);
-            gi[j] = exp_e(-gv[j]);
-            const float kk = sm.u.c.kg[r * LDB + sc];
-            sm.u.c.kg[r * LDB + sc] = kk * ga[j];
-            sm.u.c.ki[r * LDB + sc] = kk * gi[j];
-            sm.u.c.qg[r * LDB + sc] *= ga[j];
-        }
-        lds_barrier();
-        // dKG = dP KI + grec, dKI = dP^T KG + dM^T QG, dQG = dM KI + grec
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-            const int t = wave + NW * i;
-            if (t < NBT) {
-                const int rt = t / CT, ct = t % CT;
-                float4v b1 = tile_mma(z, 0, 16 * (rt + 1),
-                                      [&](int m, int kk) { return sm.dP[(16 * rt + m) * LDC + kk]; },
-                                      [&](int kk, int n) { return sm.u.c.ki[kk * LDB + 16 * ct + n]; });
-                float4v b2 = tile_mma(z, 16 * rt, C,
-                                      [&](int m, int kk) { return sm.dP[kk * LDC + 16 * rt + m]; },
-                                      [&](int kk, int n) { return sm.u.c.kg[kk * LDB + 16 * ct + n]; });
-                b2 = tile_mma(b2, 16 * rt, C,
-                              [&](int m, int kk) { return sm.dM[kk * LDC + 16 * rt + m]; },
-                              [&](int kk, int n) { return sm.u.c.qg[kk * LDB + 16 * ct + n]; });
-                float4v b3 = tile_mma(z, 0, 16 * (rt + 1),
-                                      [&](int m, int kk) { return sm.dM[(16 * rt + m) * LDC + kk]; },
-                                      [&](int kk, int n) { return sm.u.c.ki[kk * LDB + 16 * ct + n]; });
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * rt + 4 * lq + j, c = 16 * ct + l16;
-                    sm.u.c.x1[r * LDB + c] = b1[j] + dkg[i][j];
-                    sm.u.c.x2[r * LDB + c] = b2[j];
-                    sm.u.c.x3[r * LDB + c] = b3[j] + dqg[i][j];
-                }
-            }
-        }
-        lds_barrier();
-        // element-wise dk, dq, dG (scan mapping); dG_n partial sums
+        // The products below use k e^{-G} and e^{G} relative to the chunk
+        // start, which overflow once a channel decays by more than about e^-88
+        // over the chunk.  A block with a channel below kBwdExactChunk takes
+        // the exact path instead, whose factors e^{G_r - G_i} (i <= r) are
+        // running products of per-token gates, none above one.  Every
+        // wavefront holds all CB channels of the block (ss spans the rows), so
+        // the ballot is the same in every wavefront.
+        const bool exact = __ballot(gnv < kBwdExactChunk) != 0ull;
         float dgv[RS];
         float suf = 0.f, kes = 0.f;
+        if (!exact) {
+            float ga[RS], gi[RS];
 #pragma unroll
-        for (int j = RS - 1; j >= 0; --j) {
-            const int r = RS * ss + j;
-            const float dKG = sm.u.c.x1[r * LDB + sc], dKI = sm.u.c.x2[r * LDB + sc];
-            const float dQG = sm.u.c.x3[r * LDB + sc];
-            const float ki = sm.u.c.ki[r * LDB + sc];
-            const float ke = ki * egn;                       // k exp(G_n - G)
-            if (r < len) {
-                dk[tok(r) + c0 + sc] = dKG * ga[j] + dKI * gi[j] + dke[j] * egn * gi[j];
-                dq[tok(r) + c0 + sc] = dQG * ga[j];
+            for (int j = 0; j < RS; ++j) {
+                const int r = RS * ss + j;
+                ga[j] = exp_e(gv[j]);
+                gi[j] = exp_e(-gv[j]);
+                const float kk = sm.u.c.kg[r * LDB + sc];
+                sm.u.c.kg[r * LDB + sc] = kk * ga[j];
+                sm.u.c.ki[r * LDB + sc] = kk * gi[j];
+                sm.u.c.qg[r * LDB + sc] *= ga[j];
             }
-            suf += dKG * sm.u.c.kg[r * LDB + sc] + dQG * sm.u.c.qg[r * LDB + sc] - dKI * ki -
-                   dke[j] * ke;
-            dgv[j] = suf;
-            kes += dke[j] * ke;
+            lds_barrier();
+            // dKG = dP KI + grec, dKI = dP^T KG + dM^T QG, dQG = dM KI + grec
+#pragma unroll
+            for (int i = 0; i < BPW; ++i) {
+                const int t = wave + NW * i;
+                if (t < NBT) {
+                    const int rt = t / CT, ct = t % CT;
+                    float4v b1 = tile_mma(z, 0, 16 * (rt + 1),
+                                          [&](int m, int kk) { return sm.dP[(16 * rt + m) * LDC + kk]; },
+                                          [&](int kk, int n) { return sm.u.c.ki[kk * LDB + 16 * ct + n]; });
+                    float4v b2 = tile_mma(z, 16 * rt, C,
+                                          [&](int m, int kk) { return sm.dP[kk * LDC + 16 * rt + m]; },
+                                          [&](int kk, int n) { return sm.u.c.kg[kk * LDB + 16 * ct + n]; });
+                    b2 = tile_mma(b2, 16 * rt, C,
+                                  [&](int m, int kk) { return sm.dM[kk * LDC + 16 * rt + m]; },
+                                  [&](int kk, int n) { return sm.u.c.qg[kk * LDB + 16 * ct + n]; });
+                    float4v b3 = tile_mma(z, 0, 16 * (rt + 1),
+                                          [&](int m, int kk) { return sm.dM[(16 * rt + m) * LDC + kk]; },
+                                          [&](int kk, int n) { return sm.u.c.ki[kk * LDB + 16 * ct + n]; });
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 16 * rt + 4 * lq + j, c = 16 * ct + l16;
+                        sm.u.c.x1[r * LDB + c] = b1[j] + dkg[i][j];
+                        sm.u.c.x2[r * LDB + c] = b2[j];
+                        sm.u.c.x3[r * LDB + c] = b3[j] + dqg[i][j];
+                    }
+                }
+            }
+            lds_barrier();
+            // element-wise dk, dq, dG (scan mapping); dG_n partial sums
+#pragma unroll
+            for (int j = RS - 1; j >= 0; --j) {
+                const int r = RS * ss + j;
+                const float dKG = sm.u.c.x1[r * LDB + sc], dKI = sm.u.c.x2[r * LDB + sc];
+                const float dQG = sm.u.c.x3[r * LDB + sc];
+                const float ki = sm.u.c.ki[r * LDB + sc];
+                const float ke = ki * egn;                       // k exp(G_n - G)
+                if (r < len) {
+                    dk[tok(r) + c0 + sc] = dKG * ga[j] + dKI * gi[j] + dke[j] * egn * gi[j];
+                    dq[tok(r) + c0 + sc] = dQG * ga[j];
+                }
+                suf += dKG * sm.u.c.kg[r * LDB + sc] + dQG * sm.u.c.qg[r * LDB + sc] - dKI * ki -
+                       dke[j] * ke;
+                dgv[j] = suf;
+                kes += dke[j] * ke;
+            }
+        } else {
+            // alpha = e^{g} per row (x2), the records' dKG and dQG tiles (x1,
+            // x3); kg and qg still hold the raw k and q of the block
+#pragma unroll
+            for (int j = 0; j < RS; ++j) {
+                const int r = RS * ss + j;
+                sm.u.c.x2[r * LDB + sc] = exp_e(sm.u.c.G[r * LDB + sc]);
+            }
+#pragma unroll
+            for (int i = 0; i < BPW; ++i) {
+                const int t = wave + NW * i;
+                if (t < NBT) {
+                    const int rt = t / CT, ct = t % CT;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 16 * rt + 4 * lq + j, c = 16 * ct + l16;
+                        sm.u.c.x1[r * LDB + c] = dkg[i][j];
+                        sm.u.c.x3[r * LDB + c] = dqg[i][j];
+                    }
+                }
+            }
+            lds_barrier();
+            // per row r of this thread (channel sc):
+            //   a = sum_{i<r} dP[r][i] k_i e^{G_r-G_i}       (= dKG_prod e^{G_r})
+            //   d = sum_{i<=r} dM[r][i] k_i e^{G_r-G_i}      (= dQG_prod e^{G_r})
+            //   b = sum_{i>r} dP[i][r] k_i e^{G_i-G_r} + sum_{i>=r} dM[i][r] q_i e^{G_i-G_r}
+            // e^{G_n - G_r} from the gate sum of the rows after r (a suffix
+            // sum, not a difference of running sums, which would cancel for
+            // huge gates)
+            float sfx = aft;
+#pragma unroll 1
+            for (int j = RS - 1; j >= 0; --j) {
+                const int r = RS * ss + j;
+                const float eke = exp_e(sfx);
+                sfx += sm.u.c.G[r * LDB + sc];
+                const float kr = sm.u.c.kg[r * LDB + sc], qr = sm.u.c.qg[r * LDB + sc];
+                float a = 0.f, d = sm.dM[r * LDC + r] * kr, f = 1.f;
+#pragma unroll 1
+                for (int i = r - 1; i >= 0; --i) {
+                    f *= sm.u.c.x2[(i + 1) * LDB + sc];
+                    const float kf = sm.u.c.kg[i * LDB + sc] * f;
+                    a += sm.dP[r * LDC + i] * kf;
+                    d += sm.dM[r * LDC + i] * kf;
+                }
+                float b = sm.dM[r * LDC + r] * qr;
+                f = 1.f;
+#pragma unroll 1
+                for (int i = r + 1; i < C; ++i) {
+                    f *= sm.u.c.x2[i * LDB + sc];
+                    b += (sm.dP[i * LDC + r] * sm.u.c.kg[i * LDB + sc] +
+                          sm.dM[i * LDC + r] * sm.u.c.qg[i * LDB + sc]) * f;
+                }
+                const float ga = exp_e(gv[j]);
+                const float A = a + sm.u.c.x1[r * LDB + sc] * ga;
+                const float Q = d + sm.u.c.x3[r * LDB + sc] * ga;
+                if (r < len) {
+                    dk[tok(r) + c0 + sc] = A + b + dke[j] * eke;
+                    dq[tok(r) + c0 + sc] = Q;
+                }
+                suf += kr * A + qr * Q - kr * b - dke[j] * kr * eke;
+                dgv[j] = suf;
+                kes += dke[j] * kr * eke;
+            }
         }
         sm.tot[ss * CB + sc] = suf;
         sm.tot2[ss * CB + sc] = kes;

@@ -126,8 +126,8 @@ def test_backward_zero_tokens():
 
 
 def test_backward_strong_decay():
-    """Gates down to -0.5 per token (chunk decay sums up to ~32), the edge of
-    the documented domain, fp32."""
+    """Gates down to -0.5 per token (chunk decay sums up to ~32, below the
+    exact path's threshold: the matrix-core products), fp32."""
     B, T, H, D = 1, 192, 2, 64
     d = make_prefill(65, B, T, H, D, torch.float32, s0_std=0.1, g_range=(0.05, 0.5))
     do, dSf = cotangents(6, B, T, H, D, B)
@@ -138,7 +138,8 @@ def test_backward_strong_decay():
 def test_backward_one_strong_subblock(dtype):
     """One 16-token sub-block per chunk with gates -U(2.6, 3.0) (sub-block sums
     near -45, so its diagonal Gram tiles take the exact path of the records
-    kernel) and the usual gates elsewhere: chunk sums stay above -80."""
+    kernel) and the usual gates elsewhere: chunk sums stay above -60, so the
+    intra-chunk gradient uses its matrix-core products."""
     B, T, H, D = 1, 200, 2, 128
     d = make_prefill(69, B, T, H, D, dtype, s0_std=0.1)
     gen = torch.Generator(device="cuda").manual_seed(70)
@@ -147,6 +148,51 @@ def test_backward_one_strong_subblock(dtype):
     sel = ((pos >= 16) & (pos < 32)).view(1, T, 1, 1)
     d["g"] = torch.where(sel, strong, d["g"]).contiguous()
     do, dSf = cotangents(10, B, T, H, D, B)
+    assert_close(run_gpu(d, 64, do, dSf), run_oracle(d, do, dSf), TOL_BWD)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_backward_any_gate(dtype):
+    """log alpha ~ -U(0.1, 5) per token and channel: chunk gate sums near -160,
+    far beyond e^{-88}.  Every channel block of the intra-chunk gradient takes
+    its exact path (decay factors as running products of gates); d = 128,
+    chunk 64, initial state and final-state gradient."""
+    B, T, H, D = 1, 200, 2, 128
+    d = make_prefill(71, B, T, H, D, dtype, s0_std=0.1, g_range=(0.1, 5.0))
+    do, dSf = cotangents(11, B, T, H, D, B)
+    assert_close(run_gpu(d, 64, do, dSf), run_oracle(d, do, dSf), TOL_BWD)
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_backward_exact_and_fast_blocks(chunk):
+    """Strong gates (-U(0.1, 5)) only in channels 16..31 and only in every
+    other 64-token span, the usual gates elsewhere: within one call, and
+    within one chunk, some channel blocks take the exact path and the others
+    the matrix-core products."""
+    B, T, H, D = 1, 260, 2, 64
+    d = make_prefill(72, B, T, H, D, torch.float32, s0_std=0.1)
+    gen = torch.Generator(device="cuda").manual_seed(73)
+    strong = -(0.1 + 4.9 * torch.rand(d["g"].shape, device="cuda", generator=gen))
+    ch = torch.arange(D, device="cuda")
+    tok = torch.arange(T, device="cuda")
+    sel = ((ch >= 16) & (ch < 32)).view(1, 1, 1, D) & ((tok // 64) % 2 == 1).view(1, T, 1, 1)
+    d["g"] = torch.where(sel, strong, d["g"]).contiguous()
+    do, dSf = cotangents(12, B, T, H, D, B)
+    assert_close(run_gpu(d, chunk, do, dSf), run_oracle(d, do, dSf), TOL_BWD)
+
+
+def test_backward_huge_gates():
+    """Most gates in the usual range, with scattered per-channel gates of -1e6
+    and whole tokens at -1e30 (alpha = 0), bf16 inputs, d = 128."""
+    B, T, H, D = 1, 300, 2, 128
+    d = make_prefill(74, B, T, H, D, torch.bfloat16, s0_std=0.1)
+    gen = torch.Generator(device="cuda").manual_seed(75)
+    u = torch.rand(d["g"].shape, device="cuda", generator=gen)
+    g = torch.where(u < 0.03, torch.full_like(d["g"], -1e6), d["g"])
+    tok = torch.rand(d["g"].shape[:3], device="cuda", generator=gen) < 0.02
+    g = torch.where(tok[..., None], torch.full_like(g, -1e30), g)
+    d["g"] = g.contiguous()
+    do, dSf = cotangents(13, B, T, H, D, B)
     assert_close(run_gpu(d, 64, do, dSf), run_oracle(d, do, dSf), TOL_BWD)
 
 
