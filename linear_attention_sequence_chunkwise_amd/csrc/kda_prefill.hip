@@ -3308,7 +3308,7 @@ __global__ __launch_bounds__(64 * kBwdIntraWaves) void kda_bwd_intra(
                 sfx += sm.u.c.G[r * LDB + sc];
                 const float kr = sm.u.c.kg[r * LDB + sc], qr = sm.u.c.qg[r * LDB + sc];
                 float a = 0.f, d = sm.dM[r * LDC + r] * kr, f = 1.f;
-#pragma unroll 1
+#pragma unroll 8
                 for (int i = r - 1; i >= 0; --i) {
                     f *= sm.u.c.x2[(i + 1) * LDB + sc];
                     const float kf = sm.u.c.kg[i * LDB + sc] * f;
@@ -3317,7 +3317,7 @@ __global__ __launch_bounds__(64 * kBwdIntraWaves) void kda_bwd_intra(
                 }
                 float b = sm.dM[r * LDC + r] * qr;
                 f = 1.f;
-#pragma unroll 1
+#pragma unroll 8
                 for (int i = r + 1; i < C; ++i) {
                     f *= sm.u.c.x2[i * LDB + sc];
                     b += (sm.dP[i * LDC + r] * sm.u.c.kg[i * LDB + sc] +
