@@ -47,8 +47,7 @@
  *     whose per-channel gate sum falls below -8 (bf16 inputs) or -40 (fp32)
  *     gets its diagonal Gram tiles from an exact fp32 path instead of the
  *     matrix cores; this costs time only for such sub-blocks.
- *     kda_chunk_bwd has the same domain; kda_dplr_chunk_fwd keeps a narrower
- *     one, stated at its declaration.
+ *     kda_chunk_bwd and kda_dplr_chunk_fwd have the same domain.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -388,9 +387,10 @@ size_t kda_dplr_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv,
  *   Everything else exactly as in kda_chunk_fwd (q, k, v, g, initial_state,
  *   cu_seqlens, num_seqs, o, final_state, workspace, errors).  The fp32 path
  *   supports chunk 16 and 32 at dk = 128 (the chunk-64 tiles exceed LDS).
- *   Domain: that of kda_chunk_fwd, with |a|, |b| entries <= 1, except that
- *   there is no exact path for strong decay: within any 16-token sub-block
- *   the per-channel sum of -g stays below 10 (bf16 inputs) or 80 (fp32). */
+ *   Domain: that of kda_chunk_fwd (any g <= 0), with |a|, |b| entries <= 1.
+ *   A 16-token sub-block whose per-channel gate sum falls below -8 (bf16
+ *   inputs) or -40 (fp32) gets its four diagonal Gram tiles from an exact
+ *   fp32 path, as in kda_chunk_fwd. */
 kda_status kda_dplr_chunk_fwd(int B, int T, int H, int dk, int dv, int chunk,
                               float scale, kda_dtype qkv_dtype,
                               const void *q, const void *k, const void *v,

@@ -323,4 +323,79 @@ __device__ __forceinline__ void chain_store_state(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Strong decay inside one 16-token sub-block (the intra-chunk kernels of KDA
+// and of general DPLR).  The factor F_II = exp(-sum of g over sub-block I)
+// grows without bound as the gates get stronger, and the within-block prefix
+// and suffix products shrink towards the bottom of the operand type's range.
+// A sub-block whose per-channel gate sum falls below kStrongSum (fp16
+// operands: F <= e^8 and the products >= e^-8; fp32: e^40) takes an exact path
+// for its diagonal Gram tiles instead of the matrix cores; all other tiles
+// only ever use factors <= 1 and need nothing.
+// ---------------------------------------------------------------------------
+template <typename OT>
+constexpr float kStrongSum() { return sizeof(OT) == 2 ? -8.f : -40.f; }
+
+// Sum over aligned groups of NP lanes, scattered.  On entry every lane holds
+// NV partial values (NV <= NP, powers of two); on return lane l holds the
+// group sum of value (l % NP) / (NP / NV) in v[0].  Recursive halving: at
+// the step with stride s the lane whose bit s is set keeps the upper half of
+// its values and receives its partner's upper half (the partner keeps the
+// lower halves); once one value is left the remaining strides sum it whole.
+template <int NP, int NV, int S = NP / 2, int CNT = NV>
+__device__ __forceinline__ void reduce_scatter(float (&v)[NV], int lane) {
+    if constexpr (S >= 1) {
+        if constexpr (CNT > 1) {
+            constexpr int H = CNT / 2;
+            const bool up = (lane & S) != 0;
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                const float keep = up ? v[H + j] : v[j];
+                const float send = up ? v[j] : v[H + j];
+                v[j] = keep + __shfl_xor(send, S);
+            }
+            reduce_scatter<NP, NV, S / 2, H>(v, lane);
+        } else {
+            v[0] += __shfl_xor(v[0], S);
+            reduce_scatter<NP, NV, S / 2, 1>(v, lane);
+        }
+    }
+}
+
+// The same scattered sum within each 16-lane DPP row (NV <= 16 values, a
+// power of two), partners from mirror permutes (each pairs lanes with the
+// opposite stride bit and the same higher bits): on return lane l of the row
+// holds in v[0] the row sum of value l / (16 / NV).
+template <int NV, int S = 8, int CNT = NV>
+__device__ __forceinline__ void row16_reduce_scatter(float (&v)[NV], int l16) {
+    if constexpr (S >= 1) {
+        constexpr int CTRL = S == 8 ? 0x140 : S == 4 ? 0x141 : S == 2 ? 0x1B : 0xB1;
+        if constexpr (CNT > 1) {
+            constexpr int H = CNT / 2;
+            const bool up = (l16 & S) != 0;
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                const float keep = up ? v[H + j] : v[j];
+                const float send = up ? v[j] : v[H + j];
+                v[j] = keep + dpp_f<CTRL>(send);
+            }
+            row16_reduce_scatter<NV, S / 2, H>(v, l16);
+        } else {
+            v[0] += dpp_f<CTRL>(v[0]);
+            row16_reduce_scatter<NV, S / 2, 1>(v, l16);
+        }
+    }
+}
+
+// Row r and column i (i <= r) of the p-th entry of a 16 x 16 lower triangle
+// enumerated row by row, each row from its diagonal down to column 0:
+// p = r (r + 1) / 2 + (r - i).
+__device__ __forceinline__ void tri_entry(int p, int& r, int& i) {
+    int rr = (int)((sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
+    if ((rr + 1) * (rr + 2) / 2 <= p) ++rr;
+    if (rr * (rr + 1) / 2 > p) --rr;
+    r = rr;
+    i = rr - (p - rr * (rr + 1) / 2);
+}
+
 }  // namespace kda

@@ -98,7 +98,102 @@ struct DIntraSmem {
     float sig[NB * D];                   // per sub-block sum of g
     float egs[NB * D];                   // exp(Gs_I)
     float egn[NB * D];                   // exp(G_n - Ge_I)
+    float xq[2][NB][256];                // exact diagonal tiles: -Pqa, Pqk (strong sub-blocks)
+    int strong[NB];                      // sub-block I takes the exact diagonal path
 };
+
+// Exact diagonal Gram tiles of one strong 16-token sub-block, evaluated in fp32
+// from the per-token gates with no factor above one anywhere: with
+// P_ir = prod_{j=i+1..r} alpha_j and Q_ir = prod_{j=i+1..r-1} alpha_j,
+//   Pqk_ri = sum_c q_r k_i P_ir,   Pqa_ri = sum_c q_r a_i P_ir    (i <= r)
+//   Pbk_ri = sum_c b_r k_i Q_ir,   Pba_ri = sum_c b_r a_i Q_ir    (i < r)
+// (b reads the state before its own token's decay, q the one after it).  NP
+// lanes hold the sub-block, two channels each; the lane loads the raw rows of
+// g, q, k, a, b for its channels (rows past the chunk as zero: alpha = 1), so
+// that nothing it needs is held in registers across the kernel's other
+// phases.  Each lane forms partial sums over its two
+// channels; a scattered sum over the NP lanes completes them, NV values at a
+// time.  Every lane of the wave calls this (the sums cross lanes); lanes with
+// `store` write Pba and Pbk into the diagonal tiles of A and pbk (zeros on and
+// above the diagonal), and -Pqa and Pqk into xqa and xqk (row-major 16 x 16).
+template <int NP, typename OT, typename IT>
+__device__ __forceinline__ void dplr_diag_exact(
+    bool store, bool task, int lane, const float* g, const IT* q, const IT* k, const IT* a,
+    const IT* b, size_t row0, size_t rs, int nrows, OT* Ablk, OT* Pbk, int lda, float* xqa,
+    float* xqk) {
+    constexpr int NV = NP < 16 ? NP : 16;   // values per scattered sum
+    constexpr int NE = 4 * 136;             // (Pqk, Pqa, Pbk, Pba) per lower-triangle entry
+    static_assert(NE % NV == 0, "whole flushes");
+    float al0[16], al1[16], q0[16], q1[16], k0[16], k1[16], a0[16], a1[16], b0[16], b1[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const size_t off = row0 + (size_t)max(min(r, nrows - 1), 0) * rs;
+        const bool ok = task && r < nrows;
+        const float2 gg = ok ? *reinterpret_cast<const float2*>(g + off) : float2{0.f, 0.f};
+        al0[r] = exp_e(gg.x);
+        al1[r] = exp_e(gg.y);
+        const float2 qq = ok ? load2(q + off) : float2{0.f, 0.f};
+        const float2 kk = ok ? load2(k + off) : float2{0.f, 0.f};
+        const float2 aa = ok ? load2(a + off) : float2{0.f, 0.f};
+        const float2 bb = ok ? load2(b + off) : float2{0.f, 0.f};
+        q0[r] = qq.x; q1[r] = qq.y; k0[r] = kk.x; k1[r] = kk.y;
+        a0[r] = aa.x; a1[r] = aa.y; b0[r] = bb.x; b1[r] = bb.y;
+    }
+    const int mine = (lane % NP) / (NP / NV);
+    const bool writer = store && (lane % (NP / NV)) == 0;
+    float buf[NV];
+    auto flush = [&](int bidx) {
+        reduce_scatter<NP, NV>(buf, lane);
+        const int s = bidx * NV + mine;
+        if (writer && s < NE) {
+            int r, i;
+            tri_entry(s >> 2, r, i);
+            const float x = buf[0];
+            const int kind = s & 3;
+            if (kind == 0) xqk[r * 16 + i] = x;
+            else if (kind == 1) xqa[r * 16 + i] = -x;
+            else if (kind == 2) Pbk[r * lda + i] = to_ot<OT>(i < r ? x : 0.f);
+            else Ablk[r * lda + i] = to_ot<OT>(i < r ? x : 0.f);
+        }
+    };
+    float P0 = 1.f, P1 = 1.f, Q0 = 1.f, Q1 = 1.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int i = r; i >= 0; --i) {
+            if (i == r) {
+                P0 = 1.f;
+                P1 = 1.f;
+            } else {
+                P0 *= al0[i + 1];
+                P1 *= al1[i + 1];
+                if (i == r - 1) {
+                    Q0 = 1.f;
+                    Q1 = 1.f;
+                } else {
+                    Q0 *= al0[i + 1];
+                    Q1 *= al1[i + 1];
+                }
+            }
+            const int s = 4 * (r * (r + 1) / 2 + (r - i));   // compile-time after unrolling
+            buf[s % NV] = q0[r] * k0[i] * P0 + q1[r] * k1[i] * P1;
+            buf[(s + 1) % NV] = q0[r] * a0[i] * P0 + q1[r] * a1[i] * P1;
+            buf[(s + 2) % NV] = i < r ? b0[r] * k0[i] * Q0 + b1[r] * k1[i] * Q1 : 0.f;
+            buf[(s + 3) % NV] = i < r ? b0[r] * a0[i] * Q0 + b1[r] * a1[i] * Q1 : 0.f;
+            if ((s + 4) % NV == 0) flush(s / NV);
+        }
+    }
+    // the strictly upper part of the A and pbk tiles
+    if (store) {
+        for (int idx = lane % NP; idx < 256; idx += NP) {
+            const int r = idx >> 4, i = idx & 15;
+            if (i > r) {
+                Ablk[r * lda + i] = to_ot<OT>(0.f);
+                Pbk[r * lda + i] = to_ot<OT>(0.f);
+            }
+        }
+    }
+}
 
 template <int D, int C, typename OT, typename IT>
 __global__ __launch_bounds__(256) void kda_dplr_intra(
@@ -162,28 +257,39 @@ __global__ __launch_bounds__(256) void kda_dplr_intra(
     lds_barrier();
 
     // ---- phase 2: decay factors and the four Gram operands ----
+    // The exponents of the bridges and of exp(G_n - Ge_I) are sums of whole
+    // sub-block gate sums, never differences of running sums (those cancel
+    // for huge gates).  F_II = exp(-sigI) is only used while sigI stays above
+    // kStrongSum; a sub-block below it takes the exact diagonal path.
+    bool strong = false;
     if (task) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int c = c0 + e;
             float* gv = e ? g1 : g0;
-            float Gs = 0.f, Gn = 0.f;
+            float Gs = 0.f, Gn = 0.f, tail = 0.f;
 #pragma unroll
             for (int m = 0; m < NB; ++m) {
                 const float sg = sm.sig[m * D + c];
                 if (m < I) Gs += sg;
+                if (m > I) tail += sg;
                 Gn += sg;
             }
             const float sigI = sm.sig[I * D + c];
             sm.egs[I * D + c] = exp_e(Gs);
-            sm.egn[I * D + c] = exp_e(Gn - Gs - sigI);
-            float GsJ = 0.f;
-            for (int J = 0; J <= I; ++J) {
-                const float sgJ = sm.sig[J * D + c];
-                const float f = (J < I) ? exp_e(Gs - (GsJ + sgJ)) : exp_e(-sigI);
-                sm.F[(I * NB + J) * D + c] = to_ot<OT>(f);
-                GsJ += sgJ;
+            sm.egn[I * D + c] = exp_e(tail);
+#pragma unroll
+            for (int J = 0; J < NB; ++J) {
+                if (J <= I) {
+                    float mid = 0.f;
+#pragma unroll
+                    for (int m = 0; m < NB; ++m)
+                        if (m > J && m < I) mid += sm.sig[m * D + c];
+                    const float f = (J < I) ? exp_e(mid) : exp_e(-sigI);
+                    sm.F[(I * NB + J) * D + c] = to_ot<OT>(f);
+                }
             }
+            if (sigI < kStrongSum<OT>()) strong = true;
             if (I == 0) gn_out[c] = exp_e(Gn);
 #pragma unroll
             for (int j = 0; j < 16; ++j) gv[j] = exp_e(gv[j]);
@@ -219,6 +325,14 @@ __global__ __launch_bounds__(256) void kda_dplr_intra(
             s1 *= g1[j];
         }
     }
+    // Strong sub-blocks (their diagonal Gram tiles come from the exact path,
+    // after the matrix-core phase): a ballot per wave, whose lanes of one
+    // sub-block are aligned
+    const unsigned long long sb = __ballot(strong);
+    unsigned long long gmask = ~0ull;
+    if constexpr (NP < 64) gmask = ((1ull << NP) - 1) << (lane & ~(NP - 1) & 63);
+    const bool mine = task && (sb & gmask) != 0;
+    if (task && (lane % NP) == 0) sm.strong[I] = mine ? 1 : 0;
     lds_barrier();
 
     // ---- phase 3a: record tiles QG, KEt, AEt from the operands ----
@@ -290,6 +404,23 @@ __global__ __launch_bounds__(256) void kda_dplr_intra(
         }
     }
     lds_barrier();   // Gram operands dead from here on (except bl)
+    // Strong sub-blocks: the exact diagonal tiles replace what the matrix cores
+    // wrote there (every lane of a flagged wave takes part in the sums across
+    // lanes; the barrier is taken by all waves or none)
+    bool any_strong = false;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) any_strong |= sm.strong[i] != 0;
+    if (any_strong) {
+        if (sb != 0) {
+            const int Ic = task ? I : 0;
+            dplr_diag_exact<NP, OT, IT>(mine, task, lane, g, q, k, a, b,
+                                        ((size_t)(tok0 + 16 * Ic) * H + h) * D + c0, (size_t)H * D,
+                                        len - 16 * Ic, &sm.A[(16 * Ic) * LDA + 16 * Ic],
+                                        &sm.pbk[(16 * Ic) * LDA + 16 * Ic], LDA, sm.xq[0][Ic],
+                                        sm.xq[1][Ic]);
+        }
+        lds_barrier();
+    }
 
     // ---- phase 4a: stage Pqa/Pqk; b e^Gx in place; diagonal blocks of T ----
 #pragma unroll
@@ -302,9 +433,14 @@ __global__ __launch_bounds__(256) void kda_dplr_intra(
             while (tt > Ib) { tt -= Ib + 1; ++Ib; }
             const int Jb = tt;
             OT* dst = kind == 2 ? sm.u.s.pqa : sm.u.s.pqk;
+            const bool exact = Ib == Jb && sm.strong[Ib];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                dst[(16 * Ib + 4 * lq + j) * LDA + 16 * Jb + l16] = to_ot<OT>(pacc[i][j]);
+            for (int j = 0; j < 4; ++j) {
+                const int row = 4 * lq + j;
+                const float x = exact ? (l16 <= row ? sm.xq[kind - 2][Ib][row * 16 + l16] : 0.f)
+                                      : pacc[i][j];
+                dst[(16 * Ib + row) * LDA + 16 * Jb + l16] = to_ot<OT>(x);
+            }
         }
     }
     for (int idx = tid; idx < C * C; idx += 256) {   // upper blocks of Pqa, Pqk, R and T

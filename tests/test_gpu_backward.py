@@ -181,6 +181,19 @@ def test_backward_exact_and_fast_blocks(chunk):
     assert_close(run_gpu(d, chunk, do, dSf), run_oracle(d, do, dSf), TOL_BWD)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_backward_varlen_any_gate(dtype):
+    """Packed sequences with partial chunks under log alpha ~ -U(0.1, 5): the
+    exact path's rows past a sequence's end carry no weight, and its suffix
+    sums stop at the sequence's last row."""
+    lens = [1, 63, 64, 65, 130, 7]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    T, H, D = int(sum(lens)), 2, 128
+    d = make_prefill(76, 1, T, H, D, dtype, s0_std=0.1, g_range=(0.1, 5.0), n_states=len(lens))
+    do, dSf = cotangents(14, 1, T, H, D, len(lens))
+    assert_close(run_gpu(d, 64, do, dSf, cu=cu), run_oracle(d, do, dSf, cu=cu), TOL_BWD)
+
+
 def test_backward_huge_gates():
     """Most gates in the usual range, with scattered per-channel gates of -1e6
     and whole tokens at -1e30 (alpha = 0), bf16 inputs, d = 128."""

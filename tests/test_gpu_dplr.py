@@ -66,6 +66,54 @@ def test_dplr_varlen(dtype, D, chunk):
     assert np.array_equal(S[-1], d["S0"][-1].cpu().numpy())      # empty sequence
 
 
+@pytest.mark.parametrize("dtype,D,chunk", [(torch.bfloat16, 128, 64), (torch.float32, 64, 64),
+                                           (torch.float32, 128, 32)])
+def test_dplr_any_gate(dtype, D, chunk):
+    """log alpha ~ -U(0.1, 5) per token and channel: every 16-token sub-block
+    takes the exact diagonal path for its four Gram tiles, and the bridges
+    between sub-blocks are products of factors below one."""
+    d = kda_inputs.dplr_inputs(720 + D + chunk, 2, 300, 2, D, D, dtype, "cuda", s0_std=0.1,
+                               g_range=(0.1, 5.0))
+    o, S = run(d, chunk)
+    ro, rS = ref(d)
+    assert rel_err(o, ro) < TOL[dtype] and rel_err(S, rS) < TOL[dtype], (rel_err(o, ro),
+                                                                         rel_err(S, rS))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_dplr_mixed_decay(dtype, D, chunk):
+    """Gates whose 16-token sums straddle the exact-path threshold (-8 for
+    bf16 inputs, -40 for fp32): within one chunk some sub-blocks take the
+    matrix-core diagonal tiles and others the exact path."""
+    if not supported(D, chunk, dtype):
+        pytest.skip("fp32 tiles of this size exceed LDS (KDA_ERR_UNSUPPORTED)")
+    gr = (0.001, 1.0) if dtype == torch.bfloat16 else (1.5, 3.5)
+    d = kda_inputs.dplr_inputs(740 + D + chunk, 2, 3 * chunk + 9, 2, D, D, dtype, "cuda",
+                               s0_std=0.1, g_range=gr)
+    o, S = run(d, chunk)
+    ro, rS = ref(d)
+    assert rel_err(o, ro) < TOL[dtype] and rel_err(S, rS) < TOL[dtype], (rel_err(o, ro),
+                                                                         rel_err(S, rS))
+
+
+def test_dplr_huge_gates():
+    """Scattered per-channel gates of -1e6 and whole tokens at -1e30 (alpha = 0)
+    among the usual ones, bf16, d = 128, chunk 64."""
+    d = kda_inputs.dplr_inputs(760, 1, 400, 2, 128, 128, torch.bfloat16, "cuda", s0_std=0.1)
+    gen = torch.Generator(device="cuda").manual_seed(761)
+    u = torch.rand(d["g"].shape, device="cuda", generator=gen)
+    g = torch.where(u < 0.03, torch.full_like(d["g"], -1e6), d["g"])
+    tok = torch.rand(d["g"].shape[:3], device="cuda", generator=gen) < 0.02
+    g = torch.where(tok[..., None], torch.full_like(g, -1e30), g)
+    d["g"] = g.contiguous()
+    o, S = run(d, 64)
+    ro, rS = ref(d)
+    tol = TOL[torch.bfloat16]
+    assert rel_err(o, ro) < tol and rel_err(S, rS) < tol, (rel_err(o, ro), rel_err(S, rS))
+
+
 def test_dplr_reduces_to_kda():
     """a = beta k, b = alpha * k, write key beta k: the DPLR kernels give the
     KDA kernels' result (fp32, within rounding)."""
