@@ -3116,30 +3116,41 @@ __global__ __launch_bounds__(64 * kBwdIntraWaves) void kda_bwd_intra(
             sm.tot[ss * CB + sc] = run;
         }
         lds_barrier();
-        // G_r = off + the segment's running sum; G_n (gnv) and the gate sum of
-        // the rows after this segment (aft) are sums of whole segments
-        float off = 0.f, gnv = 0.f, aft = 0.f;
+        // G_r = off + the segment's running sum; G_n (gnv), the gate sum of the
+        // rows after this segment (aft) and the lowest gate sum of a 16-row
+        // tile (tmin) are sums of whole segments
+        constexpr int SPT = 16 / RS;   // segments per 16-row tile
+        float off = 0.f, gnv = 0.f, aft = 0.f, tmin = 0.f, tcur = 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < NSEG; ++s2) {
             const float t = sm.tot[s2 * CB + sc];
             gnv += t;
             off += s2 < ss ? t : 0.f;
             aft += s2 > ss ? t : 0.f;
+            tcur += t;
+            if (s2 % SPT == SPT - 1) {
+                tmin = fminf(tmin, tcur);
+                tcur = 0.f;
+            }
         }
 #pragma unroll
         for (int j = 0; j < RS; ++j) gv[j] += off;
         const float egn = exp_e(gnv);
         // The products below use k e^{-G} and e^{G} relative to the chunk
         // start, which overflow once a channel decays by more than about e^-88
-        // over the chunk.  A block with a channel below kBwdExactChunk takes
-        // the exact path instead, whose factors e^{G_r - G_i} (i <= r) are
-        // running products of per-token gates, none above one.  Every
-        // wavefront holds all CB channels of the block (ss spans the rows), so
-        // the ballot is the same in every wavefront.
-        const bool exact = __ballot(gnv < kBwdExactChunk) != 0ull;
+        // over the chunk.  A block with a channel whose chunk sum falls below
+        // kBwdExactChunk takes the tiled path if every 16-row tile of it stays
+        // above that (the same products, each output tile's operands scaled
+        // relative to that tile's first and last rows), else the exact path,
+        // whose factors e^{G_r - G_i} (i <= r) are running products of
+        // per-token gates, none above one.  Every wavefront holds all CB
+        // channels of the block (ss spans the rows), so the ballots are the
+        // same in every wavefront.
+        const bool chunk_strong = __ballot(gnv < kBwdExactChunk) != 0ull;
+        const bool exact = __ballot(tmin < kBwdExactChunk) != 0ull;
         float dgv[RS];
         float suf = 0.f, kes = 0.f;
-        if (!exact) {
+        if (!chunk_strong) {
             float ga[RS], gi[RS];
 #pragma unroll
             for (int j = 0; j < RS; ++j) {
@@ -3196,6 +3207,78 @@ __global__ __launch_bounds__(64 * kBwdIntraWaves) void kda_bwd_intra(
                        dke[j] * ke;
                 dgv[j] = suf;
                 kes += dke[j] * ke;
+            }
+        } else if (!exact) {
+            // tiled path: G (from the chunk start) per row into ki; kg and qg
+            // hold the raw k and q of the block.  For output tile rt with Ls,
+            // Le = G before its first row and at its last row:
+            //   x1 = sum_i dP[r][i] k_i e^{Ls-G_i} + dKG_rec e^{Ls}   (A = x1 e^{G_r-Ls})
+            //   x3 = sum_i dM[r][i] k_i e^{Ls-G_i} + dQG_rec e^{Ls}   (Q = x3 e^{G_r-Ls})
+            //   x2 = sum_i (dP[i][r] k_i + dM[i][r] q_i) e^{G_i-Le}   (B = x2 e^{Le-G_r})
+            // every factor at most e^{-(a tile's gate sum)} < e^{-kBwdExactChunk}
+            float* Gc = sm.u.c.ki;
+#pragma unroll
+            for (int j = 0; j < RS; ++j) Gc[(RS * ss + j) * LDB + sc] = gv[j];
+            lds_barrier();
+#pragma unroll
+            for (int i = 0; i < BPW; ++i) {
+                const int t = wave + NW * i;
+                if (t < NBT) {
+                    const int rt = t / CT, ct = t % CT;
+                    const int cn = 16 * ct + l16;   // this lane's column of the B operands
+                    const float ls = rt > 0 ? Gc[(16 * rt - 1) * LDB + cn] : 0.f;
+                    const float le = Gc[(16 * rt + 15) * LDB + cn];
+                    auto kin = [&](int kk, int n) {
+                        return sm.u.c.kg[kk * LDB + 16 * ct + n] * exp_e(ls - Gc[kk * LDB + 16 * ct + n]);
+                    };
+                    const float4v b1 = tile_mma(z, 0, 16 * (rt + 1),
+                                                [&](int m, int kk) { return sm.dP[(16 * rt + m) * LDC + kk]; }, kin);
+                    const float4v b3 = tile_mma(z, 0, 16 * (rt + 1),
+                                                [&](int m, int kk) { return sm.dM[(16 * rt + m) * LDC + kk]; }, kin);
+                    float4v b2 = tile_mma(z, 16 * rt, C,
+                                          [&](int m, int kk) { return sm.dP[kk * LDC + 16 * rt + m]; },
+                                          [&](int kk, int n) {
+                                              return sm.u.c.kg[kk * LDB + 16 * ct + n] *
+                                                     exp_e(Gc[kk * LDB + 16 * ct + n] - le);
+                                          });
+                    b2 = tile_mma(b2, 16 * rt, C,
+                                  [&](int m, int kk) { return sm.dM[kk * LDC + 16 * rt + m]; },
+                                  [&](int kk, int n) {
+                                      return sm.u.c.qg[kk * LDB + 16 * ct + n] *
+                                             exp_e(Gc[kk * LDB + 16 * ct + n] - le);
+                                  });
+                    const float els = exp_e(ls);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 16 * rt + 4 * lq + j, c = 16 * ct + l16;
+                        sm.u.c.x1[r * LDB + c] = b1[j] + dkg[i][j] * els;
+                        sm.u.c.x2[r * LDB + c] = b2[j];
+                        sm.u.c.x3[r * LDB + c] = b3[j] + dqg[i][j] * els;
+                    }
+                }
+            }
+            lds_barrier();
+            // element-wise (scan mapping); e^{G_n - G_r} from a suffix sum
+            float sfx = aft;
+#pragma unroll
+            for (int j = RS - 1; j >= 0; --j) {
+                const int r = RS * ss + j, T = r >> 4;
+                const float ls = T > 0 ? Gc[(16 * T - 1) * LDB + sc] : 0.f;
+                const float le = Gc[(16 * T + 15) * LDB + sc];
+                const float eke = exp_e(sfx);
+                sfx += sm.u.c.G[r * LDB + sc];
+                const float kr = sm.u.c.kg[r * LDB + sc], qr = sm.u.c.qg[r * LDB + sc];
+                const float e1 = exp_e(gv[j] - ls);
+                const float A = sm.u.c.x1[r * LDB + sc] * e1;
+                const float Q = sm.u.c.x3[r * LDB + sc] * e1;
+                const float Bv = sm.u.c.x2[r * LDB + sc] * exp_e(le - gv[j]);
+                if (r < len) {
+                    dk[tok(r) + c0 + sc] = A + Bv + dke[j] * eke;
+                    dq[tok(r) + c0 + sc] = Q;
+                }
+                suf += kr * A + qr * Q - kr * Bv - dke[j] * kr * eke;
+                dgv[j] = suf;
+                kes += dke[j] * kr * eke;
             }
         } else {
             // alpha = e^{g} per row (x2), the records' dKG and dQG tiles (x1,
