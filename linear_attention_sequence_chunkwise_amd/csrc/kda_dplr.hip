@@ -23,7 +23,10 @@
 // use KDA's 16-token sub-block reference points: for row r in sub-block I and
 // column i in sub-block J <= I, exp(G_r - G_i) = pre_r F_IJ suf_i with the
 // within-block prefix pre_r <= 1 (exclusive for the b rows), suffix suf_i <= 1
-// and the bridge F_IJ (above one only across a single sub-block).
+// and the bridge F_IJ (above one only across a single sub-block, F_II; the
+// bridges' exponents are sums of whole sub-block gate sums).  A sub-block
+// whose gate sum falls below kStrongSum gets its diagonal tiles from an exact
+// fp32 path instead (dplr_diag_exact), so the form holds for any g <= 0.
 //
 // Kernels: K0 (chunk table, shared with KDA) for packed sequences; D1
 // kda_dplr_intra per (chunk, head): the four Grams, the solve, W and R into a

@@ -2878,10 +2878,13 @@ __global__ __launch_bounds__(64 * bwd_dv_waves<D>()) void kda_bwd_vprod(
 // block's inputs and gradient-record values are fetched into registers while
 // the current block computes.  Only lower tiles of the C x C matrices are
 // formed or read.  Four wavefronts and 16-channel blocks keep the LDS at
-// about 70 KiB (C = 64): two workgroups share a CU.
+// about 70 KiB (C = 64): two workgroups share a CU.  Strong decay: a channel
+// block takes the tiled path or the exact path (see the block loop) when its
+// gate sums pass kBwdExactChunk.
 constexpr int kBwdIntraWaves = 4;
-// A channel block whose chunk gate sum falls below this takes the exact path
-// of kda_bwd_intra (e^{+-60} keeps the fast path's factors well inside fp32).
+// Gate-sum threshold of kda_bwd_intra's paths: while a channel's chunk sum
+// (chunk-start products) or every 16-row tile sum (tiled path) stays above
+// it, the products' factors e^{+-G} stay within e^{60}, well inside fp32.
 constexpr float kBwdExactChunk = -60.f;
 
 template <int C>
