@@ -101,7 +101,6 @@ struct DIntraSmem {
     float sig[NB * D];                   // per sub-block sum of g
     float egs[NB * D];                   // exp(Gs_I)
     float egn[NB * D];                   // exp(G_n - Ge_I)
-    float xq[2][NB][256];                // exact diagonal tiles: -Pqa, Pqk (strong sub-blocks)
     int strong[NB];                      // sub-block I takes the exact diagonal path
 };
 
@@ -117,13 +116,14 @@ struct DIntraSmem {
 // phases.  Each lane forms partial sums over its two
 // channels; a scattered sum over the NP lanes completes them, NV values at a
 // time.  Every lane of the wave calls this (the sums cross lanes); lanes with
-// `store` write Pba and Pbk into the diagonal tiles of A and pbk (zeros on and
-// above the diagonal), and -Pqa and Pqk into xqa and xqk (row-major 16 x 16).
+// `store` write the diagonal tiles of A and pbk: Pba and Pbk below the
+// diagonal, and -Pqa and Pqk transposed, at (i, r) on and above it (the
+// triangular solve reads only below the diagonal; the Pqa and Pqk staging
+// takes them from there, and clears pbk's upper part for the R products).
 template <int NP, typename OT, typename IT>
 __device__ __forceinline__ void dplr_diag_exact(
     bool store, bool task, int lane, const float* g, const IT* q, const IT* k, const IT* a,
-    const IT* b, size_t row0, size_t rs, int nrows, OT* Ablk, OT* Pbk, int lda, float* xqa,
-    float* xqk) {
+    const IT* b, size_t row0, size_t rs, int nrows, OT* Ablk, OT* Pbk, int lda) {
     constexpr int NV = NP < 16 ? NP : 16;   // values per scattered sum
     constexpr int NE = 4 * 136;             // (Pqk, Pqa, Pbk, Pba) per lower-triangle entry
     static_assert(NE % NV == 0, "whole flushes");
@@ -153,10 +153,12 @@ __device__ __forceinline__ void dplr_diag_exact(
             tri_entry(s >> 2, r, i);
             const float x = buf[0];
             const int kind = s & 3;
-            if (kind == 0) xqk[r * 16 + i] = x;
-            else if (kind == 1) xqa[r * 16 + i] = -x;
-            else if (kind == 2) Pbk[r * lda + i] = to_ot<OT>(i < r ? x : 0.f);
-            else Ablk[r * lda + i] = to_ot<OT>(i < r ? x : 0.f);
+            if (kind == 0) Pbk[i * lda + r] = to_ot<OT>(x);
+            else if (kind == 1) Ablk[i * lda + r] = to_ot<OT>(-x);
+            else if (i < r) {
+                if (kind == 2) Pbk[r * lda + i] = to_ot<OT>(x);
+                else Ablk[r * lda + i] = to_ot<OT>(x);
+            }
         }
     };
     float P0 = 1.f, P1 = 1.f, Q0 = 1.f, Q1 = 1.f;
@@ -184,16 +186,6 @@ __device__ __forceinline__ void dplr_diag_exact(
             buf[(s + 2) % NV] = i < r ? b0[r] * k0[i] * Q0 + b1[r] * k1[i] * Q1 : 0.f;
             buf[(s + 3) % NV] = i < r ? b0[r] * a0[i] * Q0 + b1[r] * a1[i] * Q1 : 0.f;
             if ((s + 4) % NV == 0) flush(s / NV);
-        }
-    }
-    // the strictly upper part of the A and pbk tiles
-    if (store) {
-        for (int idx = lane % NP; idx < 256; idx += NP) {
-            const int r = idx >> 4, i = idx & 15;
-            if (i > r) {
-                Ablk[r * lda + i] = to_ot<OT>(0.f);
-                Pbk[r * lda + i] = to_ot<OT>(0.f);
-            }
         }
     }
 }
@@ -419,8 +411,7 @@ __global__ __launch_bounds__(256) void kda_dplr_intra(
             dplr_diag_exact<NP, OT, IT>(mine, task, lane, g, q, k, a, b,
                                         ((size_t)(tok0 + 16 * Ic) * H + h) * D + c0, (size_t)H * D,
                                         len - 16 * Ic, &sm.A[(16 * Ic) * LDA + 16 * Ic],
-                                        &sm.pbk[(16 * Ic) * LDA + 16 * Ic], LDA, sm.xq[0][Ic],
-                                        sm.xq[1][Ic]);
+                                        &sm.pbk[(16 * Ic) * LDA + 16 * Ic], LDA);
         }
         lds_barrier();
     }
@@ -436,12 +427,22 @@ __global__ __launch_bounds__(256) void kda_dplr_intra(
             while (tt > Ib) { tt -= Ib + 1; ++Ib; }
             const int Jb = tt;
             OT* dst = kind == 2 ? sm.u.s.pqa : sm.u.s.pqk;
+            // a strong sub-block's exact -Pqa / Pqk tile sits transposed on and
+            // above the diagonal of its A / pbk tile; pbk's is cleared once
+            // read (the R products read that tile whole)
             const bool exact = Ib == Jb && sm.strong[Ib];
+            OT* stash = (kind == 2 ? sm.A : sm.pbk) + (16 * Ib) * LDA + 16 * Ib;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 4 * lq + j;
-                const float x = exact ? (l16 <= row ? sm.xq[kind - 2][Ib][row * 16 + l16] : 0.f)
-                                      : pacc[i][j];
+                float x = pacc[i][j];
+                if (exact) {
+                    x = 0.f;
+                    if (l16 <= row) {
+                        x = (float)stash[l16 * LDA + row];
+                        if (kind == 3) stash[l16 * LDA + row] = to_ot<OT>(0.f);
+                    }
+                }
                 dst[(16 * Ib + row) * LDA + 16 * Jb + l16] = to_ot<OT>(x);
             }
         }
