@@ -144,3 +144,14 @@ def test_dplr_config2_all_heads():
     ro, rS = ref(d)
     assert rel_err(o, ro) < TOL[torch.bfloat16]
     assert rel_err(S, rS) < TOL[torch.bfloat16]
+
+
+def test_dplr_config2_strong_gates_all_heads():
+    """The 32K-token layer shape with log alpha ~ -U(0.1, 5): every sub-block
+    takes the exact diagonal path; every output and final state."""
+    d = kda_inputs.dplr_inputs(75, 1, 32768, 32, 128, 128, torch.bfloat16, "cuda",
+                               g_range=(0.1, 5.0))
+    o, S = run(d, 64)
+    ro, rS = ref(d)
+    assert rel_err(o, ro) < TOL[torch.bfloat16]
+    assert rel_err(S, rS) < TOL[torch.bfloat16]

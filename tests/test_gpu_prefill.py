@@ -69,6 +69,27 @@ def test_config2_all_heads():
     check(d, 64)
 
 
+def test_config2_strong_gates_all_heads():
+    """The 32K-token layer of the benchmark with log alpha ~ -U(0.1, 5): every
+    16-token sub-block of every head takes the exact diagonal path, in the
+    launch configuration bench.py times; every output and final state."""
+    d = make_prefill(13, 1, 32768, 32, 128, torch.bfloat16, s0_std=0.1, g_range=(0.1, 5.0))
+    check(d, 64)
+
+
+def test_config2_few_fast_channels_all_heads():
+    """The 32K-token layer with the usual gates except 5 % of each head's
+    channels at log alpha ~ -U(1, 2.5) (a gate with a few fast-decaying
+    channels): fast and exact sub-blocks side by side in every chunk; every
+    output and final state."""
+    d = make_prefill(14, 1, 32768, 32, 128, torch.bfloat16, s0_std=0.1)
+    gen = torch.Generator(device="cuda").manual_seed(15)
+    fast = torch.rand(32, 128, device="cuda", generator=gen) < 0.05
+    u = torch.rand(d["g"].shape, device="cuda", generator=gen)
+    d["g"] = torch.where(fast, -(1.0 + 1.5 * u), d["g"]).contiguous()
+    check(d, 64)
+
+
 def test_config3_varlen_all_chains():
     """The packed 16-sequence layer: every output and every per-sequence
     final state (512 chains)."""
