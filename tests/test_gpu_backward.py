@@ -258,8 +258,41 @@ def test_backward_config2_all_heads():
     reverse mode keeps each chain's whole state history (4 GiB at 32K
     tokens), so it runs eight heads at a time; the error is taken over all
     heads jointly."""
-    B, T, H, D = 1, 32768, 32, 128
-    d = make_prefill(68, B, T, H, D, torch.bfloat16, s0_std=0.1)
+    full_size_check(make_prefill(68, 1, 32768, 32, 128, torch.bfloat16, s0_std=0.1))
+
+
+# At 32K tokens under strong gates the gradients are heavy-tailed: the state
+# forgets within a few tokens, so the final-state cotangent reaches only the
+# last tokens, whose gradients stand up to several hundred times above the
+# RMS (measured: 400x for dk and dv, 800x for dg).  A bound on max|error| / RMS
+# would ask those elements for a relative accuracy of a few fp32 ulps after
+# the chain's products; each element is held instead to TOL_BWD times the
+# larger of the RMS and its own size (dg to TOL_DG_ALL_STRONG, as above).
+def assert_close_elementwise(got, ref, tol, tol_dg):
+    for n, a, b in zip(NAMES, got, ref):
+        if a is None:
+            continue
+        t = tol_dg if n == "dg" else tol
+        a = np.asarray(a, np.float64)
+        b = np.asarray(b, np.float64)
+        scale = np.sqrt((b ** 2).mean()) + np.abs(b)
+        worst = float((np.abs(a - b) / scale).max())
+        assert worst < t, (n, worst)
+
+
+def test_backward_config2_strong_gates_all_heads():
+    """The same layer with log alpha ~ -U(0.1, 5): every chunk takes the
+    backward's strong-decay paths (16-row tile sums around -41, so mostly the
+    tiled path, the exact one where a tile's sum falls below -60); every
+    gradient of every head, element by element."""
+    full_size_check(make_prefill(69, 1, 32768, 32, 128, torch.bfloat16, s0_std=0.1,
+                                 g_range=(0.1, 5.0)),
+                    lambda got, ref: assert_close_elementwise(got, ref, TOL_BWD,
+                                                              TOL_DG_ALL_STRONG))
+
+
+def full_size_check(d, check=lambda got, ref: assert_close(got, ref, TOL_BWD)):
+    B, T, H, D = d["q"].shape
     do, dSf = cotangents(9, B, T, H, D, B)
     got = run_gpu(d, 64, do, dSf)
     ref = [np.empty_like(x) for x in got]
@@ -270,4 +303,4 @@ def test_backward_config2_all_heads():
             ref[i][:, :, h0:h0 + 8] = r[i]
         ref[5][:, h0:h0 + 8] = r[5]
         print("heads %d..%d done" % (h0, h0 + 7), flush=True)
-    assert_close(got, ref, TOL_BWD)
+    check(got, ref)
